@@ -1,0 +1,6 @@
+"""CPU fp64 oracle for the GEMM-Residual-RMSNorm-GEMM chain.
+
+TEST INFRASTRUCTURE ONLY: imported by the test-suite, the smoke check and the
+benchmark's CPU-baseline leg, never by the library or its Python binding.
+"""
+from .chain import backward, forward  # noqa: F401
