@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused GEMM-Residual-PartialRMS-GEMM chain on one MI355X.
+
+One step = one pass of the fused forward chain over one batch of synthetic
+LLaMA-shaped input already resident in HBM:
+    coda_gemm_res_prms  (H = A W1 + R, Hg = H g, partial sums of squares)
+    coda_rms_combine    (r = 1/sqrt(mean(H^2) + eps))
+    coda_gemm_rowscale  (Y = diag(r) Hg W2)
+Default workload: 7B-style hidden size, M = 16384 tokens, K = D = 4096,
+N2 = 28672 (gate||up of F = 14336), bf16 storage, fp32 accumulation.
+
+Prints ONE JSON line: whole-job TFLOP/s (algorithmic GEMM flops
+2MKD + 2MDN2 per step), the roofline of the dominant kernel (the second GEMM)
+timed with HIP events on the launch stream, the unfused reference chain for
+A/B comparison, and the fp64 CPU oracle timed on a bounded row sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused GEMM-Res-PartialRMS-GEMM TFLOP/s at 7B hidden; % of bf16 MFMA peak"
+# MI355X dense bf16 MFMA peak: 256 CUs x 4096 flop/CU/clk x 2.4 GHz
+PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+PEAK_F32_TFLOPS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="7b-bf16")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU work budget of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ref-chain", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, x, budget_s: float):
+    """The fp64 oracle, as it stands, on a bounded sample of rows of the same workload."""
+    import threadpoolctl
+
+    import oracle
+
+    cores = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+    row_flops = 2.0 * wl.K * wl.D + 2.0 * wl.D * wl.N2
+    probe = min(wl.M, 256)
+    t0 = time.perf_counter()
+    oracle.forward(x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps, rows=np.arange(probe))
+    t_probe = time.perf_counter() - t0
+    n = int(min(wl.M, max(probe, probe * budget_s / max(t_probe, 1e-3))))
+    rows = np.arange(n)
+    t0 = time.perf_counter()
+    oracle.forward(x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps, rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": round(n * row_flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"rows 0..{n - 1} of the {wl.M}-row {wl.name} forward chain (rows are independent), "
+                      f"fp64 numpy, {dt:.2f} s, including the oracle's own fp64 weight conversion"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the chain is row-independent and would shard over M with no exchange in the forward)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import coda_inputs as ci
+    import transformer_gemm_epilogue_gemm1_amd as coda
+
+    wl = ci.WORKLOADS[args.workload]
+    if wl.backward:
+        raise SystemExit("use a forward workload")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = ci.make_inputs(wl, seed=args.seed)
+
+    def up(h):
+        if h.dtype == "bf16":
+            return torch.from_numpy(h.bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(h.bits).to(dev)
+
+    d = {k: up(v) for k, v in x.items()}
+    tdt = d["A"].dtype
+    M, K, D, N2 = wl.M, wl.K, wl.D, wl.N2
+    T = coda.coda_prms_num_partials(tdt, D)
+    H = torch.empty((M, D), device=dev, dtype=tdt)
+    Hg = torch.empty((M, D), device=dev, dtype=tdt)
+    P = torch.empty((T, M), device=dev, dtype=torch.float32)
+    r = torch.empty((M,), device=dev, dtype=torch.float32)
+    Y = torch.empty((M, N2), device=dev, dtype=tdt)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        coda.coda_gemm_res_prms(d["A"], d["W1"], d["R"], d["g"], H, Hg, P, stream)
+        if ev is not None:
+            ev[0].record(stream)
+        coda.coda_rms_combine(P, r, D, wl.eps, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        coda.coda_gemm_rowscale(Hg, d["W2"], r, Y, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    # per-kernel durations: GEMM1 from the previous step's end (or start) to ev0
+    g1_ms, comb_ms, g2_ms = [], [], []
+    for i in range(args.steps):
+        prev = start if i == 0 else evs[i - 1][2]
+        g1_ms.append(prev.elapsed_time(evs[i][0]))
+        comb_ms.append(evs[i][0].elapsed_time(evs[i][1]))
+        g2_ms.append(evs[i][1].elapsed_time(evs[i][2]))
+    g1_avg, comb_avg, g2_avg = (float(np.mean(v)) for v in (g1_ms, comb_ms, g2_ms))
+
+    flops = wl.fwd_flops
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    g2_flops = 2.0 * M * D * N2
+    g2_tflops = g2_flops / (g2_avg * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name} fused forward chain", "M": M, "K": K, "D": D, "N2": N2,
+                   "eps": wl.eps, "seed": args.seed},
+        "pct_of_peak": round(100.0 * tflops / peak, 2),
+        "roofline": {"bound": "mfma", "kernel": "coda_gemm_rowscale (second GEMM, row-scale epilogue)",
+                     "achieved": round(g2_tflops, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
+                     "frac": round(g2_tflops / peak, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": g2_flops},
+        "kernels_ms": {"coda_gemm_res_prms": round(g1_avg, 4), "coda_rms_combine": round(comb_avg, 4),
+                       "coda_gemm_rowscale": round(g2_avg, 4)},
+        "wall_s_timed_region": round(wall_s, 3),
+    }
+
+    if not args.no_ref_chain:
+        ws = torch.empty((coda.coda_ref_chain_workspace_bytes(tdt, M, D),), device=dev, dtype=torch.uint8)
+        Hr = torch.empty_like(H)
+        rr = torch.empty_like(r)
+        Yr = torch.empty_like(Y)
+        for _ in range(max(2, args.warmup // 2)):
+            coda.coda_ref_chain(d["A"], d["W1"], d["R"], d["g"], d["W2"], Hr, rr, Yr, ws, wl.eps, stream)
+        nref = max(5, args.steps // 2)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(nref):
+            coda.coda_ref_chain(d["A"], d["W1"], d["R"], d["g"], d["W2"], Hr, rr, Yr, ws, wl.eps, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ref_ms = a.elapsed_time(b) / nref
+        out["ref_chain_ms"] = round(ref_ms, 4)
+        out["speedup_vs_ref_chain"] = round(ref_ms / ms_step, 4)
+        out["h_bit_identical_to_ref_chain"] = bool(torch.equal(Hr.view(torch.int16) if tdt == torch.bfloat16
+                                                               else Hr, H.view(torch.int16)
+                                                               if tdt == torch.bfloat16 else H))
+        del ws, Hr, rr, Yr
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,132 @@
+/*
+ * libcoda - the fused GEMM-Residual-PartialRMS-GEMM chain on one AMD Instinct
+ * MI355X (CDNA4, gfx950).
+ *
+ * The chain (CODA news article by Synced / 机器之心, mirrored by KuCoin News,
+ * section "CODA：「尾声」里藏着宝藏", the GEMM-RMSNorm-GEMM example):
+ *
+ *     H = A W1 + R                      residual stream after a projection
+ *     Y = RMSNorm(H; g) W2              r_i = 1 / sqrt(mean_j H_ij^2 + eps)
+ *                                       RMSNorm(H; g)_ij = r_i H_ij g_j
+ *
+ * The per-row scale r commutes with the second GEMM, so it is applied in that
+ * GEMM's epilogue; the first GEMM's epilogue only emits per-tile partial sums
+ * of squares, and a small combine kernel merges them into r.  No standalone
+ * RMSNorm pass over H remains.  The epilogue building blocks used (section
+ * "五种「积木」和一套「乐高语言」") are: element-wise (residual add), vector
+ * load (broadcast of the RMSNorm weight g), tile store (H, kept for the
+ * backward) and tile reduction (the partial RMS).
+ *
+ * Conventions shared by every entry point
+ *   - Matrices are row-major with an explicit leading dimension `ld*`, counted
+ *     in elements.  Shapes use the article's orientation: A[M,K], W1[K,D],
+ *     R/H/Hg[M,D], W2[D,N2], Y[M,N2].
+ *   - Every data pointer is a device pointer on the current HIP device.  The
+ *     caller owns all memory; the library never allocates or frees.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream): they validate, enqueue kernels and return.  No host sync.
+ *   - Validation happens before anything is enqueued.  On error the status is
+ *     returned, nothing is enqueued, and coda_last_error() describes it.
+ *     CODA_ERR_HIP means a launch failed (hipGetLastError reported it).
+ *   - Requirements (CODA_ERR_SHAPE / CODA_ERR_ALIGN otherwise): M >= 0 (M = 0
+ *     is a no-op); K, D, N2 >= 1 and multiples of 8 (bf16) or 4 (f32);
+ *     ld >= row width and a multiple of 8 (bf16) or 4 (f32) elements; base
+ *     pointers 16-byte aligned; each matrix spans less than 4 GiB.
+ *   - Outputs must not overlap inputs (CODA_ERR_ALIAS), except where stated.
+ *   - Deterministic: the same inputs give the same bits on every call (fixed
+ *     reduction orders, no atomics).  Thread-safe: no mutable global state
+ *     except the per-thread last-error string.
+ *   - Rounding: every float32 -> bfloat16 conversion is round-to-nearest-even.
+ */
+#ifndef CODA_H
+#define CODA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CODA_OK = 0,
+  CODA_ERR_NULL = 1,      /* a required pointer is NULL                        */
+  CODA_ERR_SHAPE = 2,     /* a size or leading dimension is out of range       */
+  CODA_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned                  */
+  CODA_ERR_DTYPE = 4,     /* unknown dtype code                                */
+  CODA_ERR_ALIAS = 5,     /* an output overlaps an input or another output     */
+  CODA_ERR_WORKSPACE = 6, /* workspace missing or smaller than required        */
+  CODA_ERR_HIP = 7        /* a HIP launch failed                               */
+} coda_status;
+
+typedef enum {
+  CODA_BF16 = 0, /* A, W1, R, g, H, Hg, W2, Y stored as bfloat16, fp32 accumulation */
+  CODA_F32 = 1   /* everything stored and computed in float32                        */
+} coda_dtype;
+
+/* Number of partial-sum rows T that coda_gemm_res_prms writes for width D.
+ * The caller allocates partials as float[T * M].  Returns -1 for bad args. */
+int64_t coda_prms_num_partials(coda_dtype dt, int64_t D);
+
+/* First GEMM with the residual / partial-RMS epilogue.
+ *   H      = round(A W1 + R)                      [M,D]  (stored dtype)
+ *   Hg     = round(float(H) * g)                  [M,D]  (only if g != NULL)
+ *   partials[t*M + i] = sum over the columns j of tile t of float(H_ij)^2
+ * for t in [0, T), T = coda_prms_num_partials(dt, D).  Tile t covers columns
+ * [t*128, t*128+128) (clipped to D; an empty tile writes 0).  g and Hg are
+ * both NULL or both non-NULL; with g == NULL the caller folds g into W2
+ * itself.  A: lda >= K; W1: ldw1 >= D; R: ldr >= D; H, Hg: ldh, ldhg >= D. */
+coda_status coda_gemm_res_prms(coda_dtype dt, int64_t M, int64_t K, int64_t D,
+                               const void* A, int64_t lda,
+                               const void* W1, int64_t ldw1,
+                               const void* R, int64_t ldr,
+                               const void* g,
+                               void* H, int64_t ldh,
+                               void* Hg, int64_t ldhg,
+                               float* partials, void* stream);
+
+/* Combine: r_i = 1 / sqrt((sum_{t<T} partials[t*M + i]) / D + eps), summed in
+ * increasing t.  partials: float[T*M] as written above; r: float[M].
+ * T >= 1, D >= 1, eps >= 0. */
+coda_status coda_rms_combine(int64_t M, int64_t D, int64_t T, float eps,
+                             const float* partials, float* r, void* stream);
+
+/* Second GEMM with the deferred row-scale epilogue:
+ *   Y_ik = round(r_i * sum_j X_ij W2_jk)          [M,N2]
+ * X is Hg = H diag(g) (or H when g was folded into W2).  r may be NULL
+ * (then r_i = 1, a plain GEMM).  X: ldx >= D; W2: ldw2 >= N2; Y: ldy >= N2. */
+coda_status coda_gemm_rowscale(coda_dtype dt, int64_t M, int64_t D, int64_t N2,
+                               const void* X, int64_t ldx,
+                               const void* W2, int64_t ldw2,
+                               const float* r,
+                               void* Y, int64_t ldy, void* stream);
+
+/* Bytes of workspace coda_ref_chain needs: float C[M,D] + X_n[M,D]. */
+size_t coda_ref_chain_workspace_bytes(coda_dtype dt, int64_t M, int64_t D);
+
+/* Unfused reference chain (the operator-by-operator order: GEMM, residual add,
+ * RMSNorm, GEMM), for A/B comparison with the fused path.  Four kernels:
+ *   C  = A W1 (float32, same GEMM main loop as coda_gemm_res_prms)
+ *   H  = round(C + R)                 -> bit-identical to the fused H
+ *   r_i = 1/sqrt(mean_j float(H_ij)^2 + eps);  X_n = round(float(H) * r * g)
+ *   Y  = round(X_n W2)
+ * All matrices dense (ld = width).  ws: coda_ref_chain_workspace_bytes(). */
+coda_status coda_ref_chain(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64_t N2,
+                           float eps,
+                           const void* A, const void* W1, const void* R,
+                           const void* g, const void* W2,
+                           void* H, float* r, void* Y,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* coda_status_string(coda_status s);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if
+ * none).  Valid until the next libcoda call on that thread. */
+const char* coda_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CODA_H */

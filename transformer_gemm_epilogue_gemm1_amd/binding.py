@@ -1,0 +1,162 @@
+"""Thin torch-facing binding of libcoda: argument marshalling only.
+
+Each function takes torch tensors on the current HIP device, checks dtype,
+device and layout, and passes raw device pointers, leading dimensions and the
+current stream to the C entry point of the same name.  All arithmetic runs in
+libcoda's kernels; torch only supplies device memory and streams.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_DT = {torch.bfloat16: _lib.CODA_BF16, torch.float32: _lib.CODA_F32}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}: use bfloat16 or float32")
+    return _DT[t.dtype]
+
+
+def _mat(t: torch.Tensor, name: str, dtype: torch.dtype, shape) -> int:
+    """Row-major 2-D (or 1-D) device tensor with unit column stride -> leading dim."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dim() == 1:
+        if t.numel() > 1 and t.stride(0) != 1:
+            raise ValueError(f"{name} must be contiguous")
+        return t.shape[0]
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return max(t.stride(0), t.shape[1])
+
+
+def _dense(t: torch.Tensor, name: str) -> None:
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def coda_prms_num_partials(dtype: torch.dtype, D: int) -> int:
+    return int(_lib.load().coda_prms_num_partials(_DT[dtype], D))
+
+
+def coda_gemm_res_prms(A, W1, R, g: Optional[torch.Tensor], H, Hg: Optional[torch.Tensor], partials,
+                       stream=None) -> None:
+    """H = A W1 + R, Hg = H * g, partial sums of squares of H (see coda.h)."""
+    lib = _lib.load()
+    dt = A.dtype
+    M, K = A.shape
+    D = W1.shape[1]
+    T = coda_prms_num_partials(dt, D)
+    lda = _mat(A, "A", dt, (M, K))
+    ldw1 = _mat(W1, "W1", dt, (K, D))
+    ldr = _mat(R, "R", dt, (M, D))
+    ldh = _mat(H, "H", dt, (M, D))
+    ldhg = 0
+    if g is not None:
+        _mat(g, "g", dt, (D,))
+        ldhg = _mat(Hg, "Hg", dt, (M, D))
+    _mat(partials, "partials", torch.float32, (T, M))
+    _dense(partials, "partials")
+    st = lib.coda_gemm_res_prms(_dtype_code(A), M, K, D, A.data_ptr(), lda, W1.data_ptr(), ldw1,
+                                R.data_ptr(), ldr, g.data_ptr() if g is not None else None,
+                                H.data_ptr(), ldh, Hg.data_ptr() if Hg is not None else None, ldhg,
+                                partials.data_ptr(), _stream(stream))
+    _lib.check("coda_gemm_res_prms", st)
+
+
+def coda_rms_combine(partials, r, D: int, eps: float, stream=None) -> None:
+    """r_i = 1/sqrt(sum_t partials[t, i] / D + eps)."""
+    lib = _lib.load()
+    T, M = partials.shape
+    _mat(partials, "partials", torch.float32, (T, M))
+    _dense(partials, "partials")
+    _mat(r, "r", torch.float32, (M,))
+    st = lib.coda_rms_combine(M, D, T, float(eps), partials.data_ptr(), r.data_ptr(), _stream(stream))
+    _lib.check("coda_rms_combine", st)
+
+
+def coda_gemm_rowscale(X, W2, r: Optional[torch.Tensor], Y, stream=None) -> None:
+    """Y = diag(r) (X W2), the deferred RMSNorm row scale in the epilogue."""
+    lib = _lib.load()
+    dt = X.dtype
+    M, D = X.shape
+    N2 = W2.shape[1]
+    ldx = _mat(X, "X", dt, (M, D))
+    ldw2 = _mat(W2, "W2", dt, (D, N2))
+    ldy = _mat(Y, "Y", dt, (M, N2))
+    if r is not None:
+        _mat(r, "r", torch.float32, (M,))
+    st = lib.coda_gemm_rowscale(_dtype_code(X), M, D, N2, X.data_ptr(), ldx, W2.data_ptr(), ldw2,
+                                r.data_ptr() if r is not None else None, Y.data_ptr(), ldy,
+                                _stream(stream))
+    _lib.check("coda_gemm_rowscale", st)
+
+
+def coda_ref_chain_workspace_bytes(dtype: torch.dtype, M: int, D: int) -> int:
+    return int(_lib.load().coda_ref_chain_workspace_bytes(_DT[dtype], M, D))
+
+
+def coda_ref_chain(A, W1, R, g, W2, H, r, Y, ws, eps: float, stream=None) -> None:
+    """Unfused chain: GEMM, residual add, RMSNorm, GEMM (all dense tensors)."""
+    lib = _lib.load()
+    dt = A.dtype
+    M, K = A.shape
+    D = W1.shape[1]
+    N2 = W2.shape[1]
+    for t, n, dtp, shp in ((A, "A", dt, (M, K)), (W1, "W1", dt, (K, D)), (R, "R", dt, (M, D)),
+                           (g, "g", dt, (D,)), (W2, "W2", dt, (D, N2)), (H, "H", dt, (M, D)),
+                           (r, "r", torch.float32, (M,)), (Y, "Y", dt, (M, N2))):
+        _mat(t, n, dtp, shp)
+        _dense(t, n)
+    if ws.device.type != "cuda":
+        raise ValueError("workspace must be on a HIP device")
+    st = lib.coda_ref_chain(_dtype_code(A), M, K, D, N2, float(eps), A.data_ptr(), W1.data_ptr(),
+                            R.data_ptr(), g.data_ptr(), W2.data_ptr(), H.data_ptr(), r.data_ptr(),
+                            Y.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    _lib.check("coda_ref_chain", st)
+
+
+# ---- conveniences that allocate outputs with torch, then call the above ----
+
+def fused_forward(A, W1, R, g, W2, eps: float, stream=None):
+    """The fused chain: three launches, returns (H, Hg, r, Y)."""
+    M, D, N2 = A.shape[0], W1.shape[1], W2.shape[1]
+    dev, dt = A.device, A.dtype
+    H = torch.empty((M, D), device=dev, dtype=dt)
+    Hg = torch.empty((M, D), device=dev, dtype=dt)
+    P = torch.empty((coda_prms_num_partials(dt, D), M), device=dev, dtype=torch.float32)
+    r = torch.empty((M,), device=dev, dtype=torch.float32)
+    Y = torch.empty((M, N2), device=dev, dtype=dt)
+    coda_gemm_res_prms(A, W1, R, g, H, Hg, P, stream)
+    coda_rms_combine(P, r, D, eps, stream)
+    coda_gemm_rowscale(Hg, W2, r, Y, stream)
+    return H, Hg, r, Y, P
+
+
+def ref_chain(A, W1, R, g, W2, eps: float, stream=None):
+    """The unfused chain, returns (H, r, Y)."""
+    M, D, N2 = A.shape[0], W1.shape[1], W2.shape[1]
+    dev, dt = A.device, A.dtype
+    H = torch.empty((M, D), device=dev, dtype=dt)
+    r = torch.empty((M,), device=dev, dtype=torch.float32)
+    Y = torch.empty((M, N2), device=dev, dtype=dt)
+    ws = torch.empty((coda_ref_chain_workspace_bytes(dt, M, D),), device=dev, dtype=torch.uint8)
+    coda_ref_chain(A, W1, R, g, W2, H, r, Y, ws, eps, stream)
+    return H, r, Y

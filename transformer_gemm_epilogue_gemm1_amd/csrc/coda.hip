@@ -1,0 +1,293 @@
+// libcoda C ABI: argument validation and kernel launches.
+//
+// Every entry point validates all arguments on the host first and returns an
+// error without enqueuing anything (and without any HIP call) if one fails.
+// See include/coda.h for the contract of each call.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/coda.h"
+#include "epilogues.hpp"
+#include "rowops.hpp"
+
+using namespace coda;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+coda_status fail(coda_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+coda_status ok() {
+  g_last_error.clear();
+  return CODA_OK;
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+constexpr int64_t kMaxSpan = ((int64_t)1 << 32) - 16;  // 32-bit offsets inside one matrix
+
+int elem_size(coda_dtype dt) { return dt == CODA_BF16 ? 2 : 4; }
+int elems_per_chunk(coda_dtype dt) { return dt == CODA_BF16 ? 8 : 4; }
+
+struct Mat {
+  const void* p;
+  int64_t rows, cols, ld;
+  int es;  // element size in bytes
+  const char* name;
+  int64_t span() const { return rows <= 0 ? 0 : ((rows - 1) * ld + cols) * es; }
+};
+
+coda_status check_mat(const Mat& m, int E) {
+  if (m.p == nullptr) return fail(CODA_ERR_NULL, "%s is NULL", m.name);
+  if (m.ld < m.cols) return fail(CODA_ERR_SHAPE, "%s: ld %lld < width %lld", m.name, (long long)m.ld, (long long)m.cols);
+  if (m.ld % E != 0) return fail(CODA_ERR_ALIGN, "%s: ld %lld not a multiple of %d elements", m.name, (long long)m.ld, E);
+  if (((uintptr_t)m.p & 15) != 0) return fail(CODA_ERR_ALIGN, "%s is not 16-byte aligned", m.name);
+  if (m.span() > kMaxSpan) return fail(CODA_ERR_SHAPE, "%s spans %lld bytes (limit 4 GiB)", m.name, (long long)m.span());
+  return CODA_OK;
+}
+
+bool overlaps(const Mat& a, const Mat& b) {
+  if (a.p == nullptr || b.p == nullptr || a.span() == 0 || b.span() == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + a.span();
+  const uintptr_t b0 = (uintptr_t)b.p, b1 = b0 + b.span();
+  return a0 < b1 && b0 < a1;
+}
+
+// Each output against every input and every other output.
+coda_status check_alias(const Mat* outs, int nout, const Mat* ins, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlaps(outs[i], ins[j])) return fail(CODA_ERR_ALIAS, "%s overlaps input %s", outs[i].name, ins[j].name);
+    for (int j = i + 1; j < nout; ++j)
+      if (overlaps(outs[i], outs[j])) return fail(CODA_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+  return CODA_OK;
+}
+
+coda_status check_dims(coda_dtype dt, int64_t M, std::initializer_list<std::pair<const char*, int64_t>> dims) {
+  if (dt != CODA_BF16 && dt != CODA_F32) return fail(CODA_ERR_DTYPE, "unknown dtype %d", (int)dt);
+  if (M < 0 || M > kMaxDim) return fail(CODA_ERR_SHAPE, "M = %lld out of range", (long long)M);
+  for (auto& d : dims) {
+    if (d.second < 1 || d.second > kMaxDim) return fail(CODA_ERR_SHAPE, "%s = %lld out of range", d.first, (long long)d.second);
+    if (d.second % 8 != 0) return fail(CODA_ERR_SHAPE, "%s = %lld is not a multiple of 8", d.first, (long long)d.second);
+  }
+  return CODA_OK;
+}
+
+coda_status launch_status(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(CODA_ERR_HIP, "%s launch: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+constexpr int kGroupM = 8;
+
+template <typename T, bool AKC, bool BKC, class Epi>
+coda_status launch_gemm(const char* what, int M, int N, int K, const void* a, int64_t lda, const void* b,
+                        int64_t ldb, const typename Epi::Params& ep, hipStream_t s) {
+  GemmArgs g;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.tiles_m = (M + kTileM - 1) / kTileM;
+  g.tiles_n = (N + kTileN - 1) / kTileN;
+  g.group_m = kGroupM;
+  g.a = a;
+  g.lda = lda;
+  g.b = b;
+  g.ldb = ldb;
+  const int nblocks = g.tiles_m * g.tiles_n;
+  hipLaunchKernelGGL((gemm_kernel<T, AKC, BKC, Epi>), dim3(nblocks), dim3(kThreads), 0, s, g, ep);
+  return launch_status(what);
+}
+
+int64_t num_partials(int64_t D) { return 2 * ((D + kTileN - 1) / kTileN); }
+
+template <typename T>
+coda_status gemm_res_prms_impl(int M, int K, int D, const void* A, int64_t lda, const void* W1, int64_t ldw1,
+                               const void* R, int64_t ldr, const void* g, void* H, int64_t ldh, void* Hg,
+                               int64_t ldhg, float* partials, hipStream_t s) {
+  typename EpiResPrms<T>::Params ep{(const T*)R, ldr, (const T*)g, (T*)H, ldh, (T*)Hg, ldhg, partials};
+  return launch_gemm<T, true, false, EpiResPrms<T>>("coda_gemm_res_prms", M, D, K, A, lda, W1, ldw1, ep, s);
+}
+
+template <typename T>
+coda_status gemm_rowscale_impl(int M, int D, int N2, const void* X, int64_t ldx, const void* W2, int64_t ldw2,
+                               const float* r, void* Y, int64_t ldy, hipStream_t s) {
+  typename EpiRowScale<T>::Params ep{r, (T*)Y, ldy};
+  return launch_gemm<T, true, false, EpiRowScale<T>>("coda_gemm_rowscale", M, N2, D, X, ldx, W2, ldw2, ep, s);
+}
+
+coda_status combine_impl(int M, int D, int T, float eps, const float* partials, float* r, hipStream_t s) {
+  hipLaunchKernelGGL(rms_combine_kernel, dim3((M + 255) / 256), dim3(256), 0, s, partials, r, M, T, D, eps);
+  return launch_status("coda_rms_combine");
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t coda_prms_num_partials(coda_dtype dt, int64_t D) {
+  if (dt != CODA_BF16 && dt != CODA_F32) return -1;
+  if (D < 1 || D > kMaxDim) return -1;
+  return num_partials(D);
+}
+
+coda_status coda_gemm_res_prms(coda_dtype dt, int64_t M, int64_t K, int64_t D, const void* A, int64_t lda,
+                               const void* W1, int64_t ldw1, const void* R, int64_t ldr, const void* g, void* H,
+                               int64_t ldh, void* Hg, int64_t ldhg, float* partials, void* stream) {
+  coda_status st = check_dims(dt, M, {{"K", K}, {"D", D}});
+  if (st != CODA_OK) return st;
+  if (M == 0) return ok();
+  const int es = elem_size(dt), E = elems_per_chunk(dt);
+  const int64_t T = num_partials(D);
+  if ((g == nullptr) != (Hg == nullptr)) return fail(CODA_ERR_NULL, "g and Hg must be both NULL or both set");
+  const Mat mA{A, M, K, lda, es, "A"}, mW1{W1, K, D, ldw1, es, "W1"}, mR{R, M, D, ldr, es, "R"};
+  const Mat mg{g, 1, D, D, es, "g"}, mH{H, M, D, ldh, es, "H"}, mHg{Hg, M, D, ldhg, es, "Hg"};
+  const Mat mP{partials, T, M, M, 4, "partials"};
+  for (const Mat* m : {&mA, &mW1, &mR, &mH})
+    if ((st = check_mat(*m, E)) != CODA_OK) return st;
+  if (g != nullptr) {
+    if ((st = check_mat(mg, E)) != CODA_OK) return st;
+    if ((st = check_mat(mHg, E)) != CODA_OK) return st;
+  }
+  if (partials == nullptr) return fail(CODA_ERR_NULL, "partials is NULL");
+  if (((uintptr_t)partials & 3) != 0) return fail(CODA_ERR_ALIGN, "partials is not 4-byte aligned");
+  if (mP.span() > kMaxSpan) return fail(CODA_ERR_SHAPE, "partials span too large");
+  const Mat outs[3] = {mH, g ? mHg : Mat{nullptr, 0, 0, 0, es, "Hg"}, mP};
+  const Mat ins[4] = {mA, mW1, mR, g ? mg : Mat{nullptr, 0, 0, 0, es, "g"}};
+  if ((st = check_alias(outs, 3, ins, 4)) != CODA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == CODA_BF16)
+    return gemm_res_prms_impl<uint16_t>((int)M, (int)K, (int)D, A, lda, W1, ldw1, R, ldr, g, H, ldh, Hg, ldhg,
+                                        partials, s);
+  return gemm_res_prms_impl<float>((int)M, (int)K, (int)D, A, lda, W1, ldw1, R, ldr, g, H, ldh, Hg, ldhg, partials,
+                                   s);
+}
+
+coda_status coda_rms_combine(int64_t M, int64_t D, int64_t T, float eps, const float* partials, float* r,
+                             void* stream) {
+  if (M < 0 || M > kMaxDim) return fail(CODA_ERR_SHAPE, "M = %lld out of range", (long long)M);
+  if (D < 1 || D > kMaxDim) return fail(CODA_ERR_SHAPE, "D = %lld out of range", (long long)D);
+  if (T < 1 || T > 65536) return fail(CODA_ERR_SHAPE, "T = %lld out of range", (long long)T);
+  if (!(eps >= 0.f) || isinf(eps)) return fail(CODA_ERR_SHAPE, "eps must be finite and >= 0");
+  if (M == 0) return ok();
+  if (partials == nullptr || r == nullptr) return fail(CODA_ERR_NULL, "partials and r must be set");
+  if ((((uintptr_t)partials | (uintptr_t)r) & 3) != 0) return fail(CODA_ERR_ALIGN, "partials / r not 4-byte aligned");
+  const Mat mP{partials, T, M, M, 4, "partials"}, mr{r, 1, M, M, 4, "r"};
+  if (mP.span() > kMaxSpan) return fail(CODA_ERR_SHAPE, "partials span too large");
+  if (overlaps(mP, mr)) return fail(CODA_ERR_ALIAS, "r overlaps partials");
+  return combine_impl((int)M, (int)D, (int)T, eps, partials, r, (hipStream_t)stream);
+}
+
+coda_status coda_gemm_rowscale(coda_dtype dt, int64_t M, int64_t D, int64_t N2, const void* X, int64_t ldx,
+                               const void* W2, int64_t ldw2, const float* r, void* Y, int64_t ldy, void* stream) {
+  coda_status st = check_dims(dt, M, {{"D", D}, {"N2", N2}});
+  if (st != CODA_OK) return st;
+  if (M == 0) return ok();
+  const int es = elem_size(dt), E = elems_per_chunk(dt);
+  const Mat mX{X, M, D, ldx, es, "X"}, mW2{W2, D, N2, ldw2, es, "W2"}, mY{Y, M, N2, ldy, es, "Y"};
+  const Mat mr{r, 1, M, M, 4, "r"};
+  for (const Mat* m : {&mX, &mW2, &mY})
+    if ((st = check_mat(*m, E)) != CODA_OK) return st;
+  if (r != nullptr && ((uintptr_t)r & 3) != 0) return fail(CODA_ERR_ALIGN, "r is not 4-byte aligned");
+  const Mat ins[3] = {mX, mW2, r ? mr : Mat{nullptr, 0, 0, 0, 4, "r"}};
+  if ((st = check_alias(&mY, 1, ins, 3)) != CODA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == CODA_BF16) return gemm_rowscale_impl<uint16_t>((int)M, (int)D, (int)N2, X, ldx, W2, ldw2, r, Y, ldy, s);
+  return gemm_rowscale_impl<float>((int)M, (int)D, (int)N2, X, ldx, W2, ldw2, r, Y, ldy, s);
+}
+
+size_t coda_ref_chain_workspace_bytes(coda_dtype dt, int64_t M, int64_t D) {
+  if ((dt != CODA_BF16 && dt != CODA_F32) || M < 0 || D < 1) return 0;
+  const size_t c = (size_t)M * D * 4;
+  const size_t c_aligned = (c + 255) & ~(size_t)255;
+  return c_aligned + (size_t)M * D * elem_size(dt);
+}
+
+coda_status coda_ref_chain(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64_t N2, float eps, const void* A,
+                           const void* W1, const void* R, const void* g, const void* W2, void* H, float* r, void* Y,
+                           void* ws, size_t ws_bytes, void* stream) {
+  coda_status st = check_dims(dt, M, {{"K", K}, {"D", D}, {"N2", N2}});
+  if (st != CODA_OK) return st;
+  if (!(eps >= 0.f) || isinf(eps)) return fail(CODA_ERR_SHAPE, "eps must be finite and >= 0");
+  if (M == 0) return ok();
+  const int es = elem_size(dt), E = elems_per_chunk(dt);
+  const Mat mA{A, M, K, K, es, "A"}, mW1{W1, K, D, D, es, "W1"}, mR{R, M, D, D, es, "R"}, mg{g, 1, D, D, es, "g"};
+  const Mat mW2{W2, D, N2, N2, es, "W2"}, mH{H, M, D, D, es, "H"}, mY{Y, M, N2, N2, es, "Y"};
+  const Mat mr{r, 1, M, M, 4, "r"};
+  for (const Mat* m : {&mA, &mW1, &mR, &mg, &mW2, &mH, &mY})
+    if ((st = check_mat(*m, E)) != CODA_OK) return st;
+  if (r == nullptr) return fail(CODA_ERR_NULL, "r is NULL");
+  if (((uintptr_t)r & 3) != 0) return fail(CODA_ERR_ALIGN, "r is not 4-byte aligned");
+  const size_t need = coda_ref_chain_workspace_bytes(dt, M, D);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(CODA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  if (((uintptr_t)ws & 255) != 0) return fail(CODA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const size_t c_aligned = ((size_t)M * D * 4 + 255) & ~(size_t)255;
+  float* C = (float*)ws;
+  void* Xn = (char*)ws + c_aligned;
+  const Mat mC{C, M, D, D, 4, "workspace C"}, mXn{Xn, M, D, D, es, "workspace Xn"};
+  if (mC.span() > kMaxSpan) return fail(CODA_ERR_SHAPE, "workspace C spans more than 4 GiB");
+  const Mat outs[5] = {mH, mr, mY, mC, mXn};
+  const Mat ins[5] = {mA, mW1, mR, mg, mW2};
+  if ((st = check_alias(outs, 5, ins, 5)) != CODA_OK) return st;
+
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t nchunks = M * D / 8;
+  const int ew_blocks = (int)((nchunks + 255) / 256 < 16384 ? (nchunks + 255) / 256 : 16384);
+  if (dt == CODA_BF16) {
+    typedef uint16_t T;
+    if ((st = launch_gemm<T, true, false, EpiStoreF32>("coda_ref_chain gemm1", (int)M, (int)D, (int)K, A, K, W1, D,
+                                                        EpiStoreF32::Params{C, D}, s)) != CODA_OK)
+      return st;
+    hipLaunchKernelGGL(residual_add_kernel<T>, dim3(ew_blocks), dim3(256), 0, s, C, (const T*)R, (T*)H, nchunks);
+    if ((st = launch_status("coda_ref_chain residual")) != CODA_OK) return st;
+    hipLaunchKernelGGL(rmsnorm_rows_kernel<T>, dim3((unsigned)M), dim3(256), 0, s, (const T*)H, (const T*)g, r,
+                       (T*)Xn, (int)D, eps);
+    if ((st = launch_status("coda_ref_chain rmsnorm")) != CODA_OK) return st;
+    return gemm_rowscale_impl<T>((int)M, (int)D, (int)N2, Xn, D, W2, N2, nullptr, Y, N2, s);
+  } else {
+    typedef float T;
+    if ((st = launch_gemm<T, true, false, EpiStoreF32>("coda_ref_chain gemm1", (int)M, (int)D, (int)K, A, K, W1, D,
+                                                        EpiStoreF32::Params{C, D}, s)) != CODA_OK)
+      return st;
+    hipLaunchKernelGGL(residual_add_kernel<T>, dim3(ew_blocks), dim3(256), 0, s, C, (const T*)R, (T*)H, nchunks);
+    if ((st = launch_status("coda_ref_chain residual")) != CODA_OK) return st;
+    hipLaunchKernelGGL(rmsnorm_rows_kernel<T>, dim3((unsigned)M), dim3(256), 0, s, (const T*)H, (const T*)g, r,
+                       (T*)Xn, (int)D, eps);
+    if ((st = launch_status("coda_ref_chain rmsnorm")) != CODA_OK) return st;
+    return gemm_rowscale_impl<T>((int)M, (int)D, (int)N2, Xn, D, W2, N2, nullptr, Y, N2, s);
+  }
+}
+
+const char* coda_status_string(coda_status s) {
+  switch (s) {
+    case CODA_OK: return "CODA_OK";
+    case CODA_ERR_NULL: return "CODA_ERR_NULL";
+    case CODA_ERR_SHAPE: return "CODA_ERR_SHAPE";
+    case CODA_ERR_ALIGN: return "CODA_ERR_ALIGN";
+    case CODA_ERR_DTYPE: return "CODA_ERR_DTYPE";
+    case CODA_ERR_ALIAS: return "CODA_ERR_ALIAS";
+    case CODA_ERR_WORKSPACE: return "CODA_ERR_WORKSPACE";
+    case CODA_ERR_HIP: return "CODA_ERR_HIP";
+  }
+  return "CODA_ERR_UNKNOWN";
+}
+
+const char* coda_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Small row-wise kernels: the combine of the partial sums of squares, and the
+// unfused chain's residual-add and RMSNorm passes.
+#pragma once
+
+#include "gemm.hpp"
+
+namespace coda {
+
+// r_i = 1/sqrt(mean_j H_ij^2 + eps) from the per-tile partial sums of squares
+// (the light auxiliary reduction of the CODA news article by Synced, section
+// "CODA：「尾声」里藏着宝藏").  One thread per row; partials[t*M + i] are summed
+// in increasing t (fixed order: deterministic), the mean and reciprocal
+// square root are taken in double precision and rounded once to float.
+__global__ __launch_bounds__(256) void rms_combine_kernel(const float* __restrict__ partials,
+                                                          float* __restrict__ r, int M, int T, int D,
+                                                          float eps) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= M) return;
+  float s = 0.f;
+  for (int t = 0; t < T; ++t) s += partials[(int64_t)t * M + i];
+  r[i] = (float)(1.0 / sqrt((double)s / (double)D + (double)eps));
+}
+
+// Unfused chain, step 2: H = round(C + R), elementwise over dense [M, D].
+template <typename T>
+__global__ __launch_bounds__(256) void residual_add_kernel(const float* __restrict__ C, const T* __restrict__ R,
+                                                           T* __restrict__ H, int64_t nchunks) {
+  for (int64_t c = blockIdx.x * 256ll + threadIdx.x; c < nchunks; c += (int64_t)gridDim.x * 256) {
+    float cv[8], rv[8];
+    Chunk8<float>::load(C + c * 8, cv);
+    Chunk8<T>::load(R + c * 8, rv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cv[i] = cv[i] + rv[i];
+    Chunk8<T>::store(H + c * 8, cv);
+  }
+}
+
+// Unfused chain, step 3: standalone RMSNorm over dense [M, D], one workgroup
+// per row: r = 1/sqrt(mean(H^2) + eps), X_n = round(float(H) * r * g).
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const T* __restrict__ H, const T* __restrict__ g,
+                                                           float* __restrict__ r, T* __restrict__ Xn, int D,
+                                                           float eps) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const T* h = H + row * D;
+  const int nch = D / 8;
+  float s = 0.f;
+  for (int c = threadIdx.x; c < nch; c += 256) {
+    float v[8];
+    Chunk8<T>::load(h + c * 8, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += v[i] * v[i];
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float rr = (float)(1.0 / sqrt((double)tot / (double)D + (double)eps));
+  if (threadIdx.x == 0) r[row] = rr;
+  for (int c = threadIdx.x; c < nch; c += 256) {
+    float v[8], gv[8];
+    Chunk8<T>::load(h + c * 8, v);
+    Chunk8<T>::load(g + c * 8, gv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (v[i] * rr) * gv[i];
+    Chunk8<T>::store(Xn + row * D + c * 8, v);
+  }
+}
+
+}  // namespace coda
