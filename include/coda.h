@@ -31,7 +31,7 @@
  *   - Requirements (CODA_ERR_SHAPE / CODA_ERR_ALIGN otherwise): M >= 0 (M = 0
  *     is a no-op); K, D, N2 >= 1 and multiples of 8 (bf16) or 4 (f32);
  *     ld >= row width and a multiple of 8 (bf16) or 4 (f32) elements; base
- *     pointers 16-byte aligned; each matrix spans less than 4 GiB.
+ *     pointers 16-byte aligned; each matrix spans less than 2 GiB.
  *   - Outputs must not overlap inputs (CODA_ERR_ALIAS), except where stated.
  *   - Deterministic: the same inputs give the same bits on every call (fixed
  *     reduction orders, no atomics).  Thread-safe: no mutable global state

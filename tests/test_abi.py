@@ -92,7 +92,7 @@ def rowscale(lib, dt=BF16, M=512, D=256, N2=512, X=H_, ldx=None, W2=W2_, ldw2=No
     (dict(Hg=H_ + 64), ALIAS),
     (dict(part=R_ + 4096), ALIAS),
     (dict(M=1 << 31), SHAPE),
-    (dict(M=1 << 20, K=4096, lda=4096 * 1024), SHAPE),  # A spans more than 4 GiB
+    (dict(M=1 << 20, K=4096, lda=4096 * 1024), SHAPE),  # A spans more than 2 GiB
 ])
 def test_gemm_res_prms_rejects(lib, kw, status):
     assert prms(lib, **kw) == status

@@ -37,7 +37,7 @@ coda_status ok() {
 }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
-constexpr int64_t kMaxSpan = ((int64_t)1 << 32) - 16;  // 32-bit offsets inside one matrix
+constexpr int64_t kMaxSpan = ((int64_t)1 << 31) - 256;  // 32-bit buffer offsets inside one matrix
 
 int elem_size(coda_dtype dt) { return dt == CODA_BF16 ? 2 : 4; }
 int elems_per_chunk(coda_dtype dt) { return dt == CODA_BF16 ? 8 : 4; }
@@ -55,7 +55,7 @@ coda_status check_mat(const Mat& m, int E) {
   if (m.ld < m.cols) return fail(CODA_ERR_SHAPE, "%s: ld %lld < width %lld", m.name, (long long)m.ld, (long long)m.cols);
   if (m.ld % E != 0) return fail(CODA_ERR_ALIGN, "%s: ld %lld not a multiple of %d elements", m.name, (long long)m.ld, E);
   if (((uintptr_t)m.p & 15) != 0) return fail(CODA_ERR_ALIGN, "%s is not 16-byte aligned", m.name);
-  if (m.span() > kMaxSpan) return fail(CODA_ERR_SHAPE, "%s spans %lld bytes (limit 4 GiB)", m.name, (long long)m.span());
+  if (m.span() > kMaxSpan) return fail(CODA_ERR_SHAPE, "%s spans %lld bytes (limit 2 GiB)", m.name, (long long)m.span());
   return CODA_OK;
 }
 
@@ -95,6 +95,11 @@ coda_status launch_status(const char* what) {
 
 constexpr int kGroupM = 8;
 
+// Bytes spanned by an operand stored as `rows` rows of `cols` elements.
+uint32_t span_bytes(int64_t rows, int64_t cols, int64_t ld, int es) {
+  return (uint32_t)(rows <= 0 ? 0 : ((rows - 1) * ld + cols) * es);
+}
+
 template <typename T, bool AKC, bool BKC, class Epi>
 coda_status launch_gemm(const char* what, int M, int N, int K, const void* a, int64_t lda, const void* b,
                         int64_t ldb, const typename Epi::Params& ep, hipStream_t s) {
@@ -107,8 +112,10 @@ coda_status launch_gemm(const char* what, int M, int N, int K, const void* a, in
   g.group_m = kGroupM;
   g.a = a;
   g.lda = lda;
+  g.a_span = AKC ? span_bytes(M, K, lda, sizeof(T)) : span_bytes(K, M, lda, sizeof(T));
   g.b = b;
   g.ldb = ldb;
+  g.b_span = BKC ? span_bytes(N, K, ldb, sizeof(T)) : span_bytes(K, N, ldb, sizeof(T));
   const int nblocks = g.tiles_m * g.tiles_n;
   hipLaunchKernelGGL((gemm_kernel<T, AKC, BKC, Epi>), dim3(nblocks), dim3(kThreads), 0, s, g, ep);
   return launch_status(what);
@@ -241,7 +248,7 @@ coda_status coda_ref_chain(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64
   float* C = (float*)ws;
   void* Xn = (char*)ws + c_aligned;
   const Mat mC{C, M, D, D, 4, "workspace C"}, mXn{Xn, M, D, D, es, "workspace Xn"};
-  if (mC.span() > kMaxSpan) return fail(CODA_ERR_SHAPE, "workspace C spans more than 4 GiB");
+  if (mC.span() > kMaxSpan) return fail(CODA_ERR_SHAPE, "workspace C spans more than 2 GiB");
   const Mat outs[5] = {mH, mr, mY, mC, mXn};
   const Mat ins[5] = {mA, mW1, mR, mg, mW2};
   if ((st = check_alias(outs, 5, ins, 5)) != CODA_OK) return st;

@@ -100,26 +100,36 @@ struct Chunk8<float> {
 };
 
 // ---- operand staging: HBM -> registers -> LDS ---------------------------
+// Global reads go through a raw buffer descriptor spanning exactly the
+// operand's bytes.  A slot that falls outside the matrix (row >= rows,
+// contraction index >= K) gets an offset past the descriptor's extent, for
+// which the hardware returns zeros: no load ever leaves the operand and no
+// select has to wait for the load to land.
+constexpr uint32_t kOutOfRange = 0x80000000u;  // every operand spans < 2 GiB
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t span_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)span_bytes, 0x00020000);
+}
+
 template <typename T, bool KC>
 struct Stager {
   static constexpr int E = Elem<T>::E;
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t off[8];  // byte offset of each slot for the k-tile at k0 = 0 (kOutOfRange: row outside)
+  int kidx[8];      // contraction index of each slot's first element at k0 = 0
   u32x4 reg[8];
 
-  // Loads k-tile starting at contraction index k0 of rows [row0, row0+256).
-  // Out-of-range rows / contraction indices read as zero (the address is
-  // clamped to the base so no load leaves the matrix).
-  __device__ __forceinline__ void load(const T* __restrict__ base, int64_t ld, int row0, int nrows,
-                                       int k0, int K, int tid) {
+  __device__ __forceinline__ void init(const T* base, uint32_t span_bytes, int64_t ld, int row0, int nrows,
+                                       int tid) {
+    rsrc = make_rsrc(base, span_bytes);
     if constexpr (KC) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         int row, c;
         kc_slot(tid, i, &row, &c);
-        const int gr = row0 + row, gk = k0 + c * E;
-        const bool ok = (gr < nrows) && (gk < K);
-        const T* p = ok ? base + (int64_t)gr * ld + gk : base;
-        const u32x4 v = *(const u32x4*)p;
-        reg[i] = ok ? v : u32x4{0, 0, 0, 0};
+        const int gr = row0 + row;
+        kidx[i] = c * E;
+        off[i] = gr < nrows ? (uint32_t)(((int64_t)gr * ld + c * E) * (int64_t)sizeof(T)) : kOutOfRange;
       }
     } else {
       constexpr int NB = 8 / E;  // E x E blocks per thread (bf16: 1, fp32: 2)
@@ -130,13 +140,22 @@ struct Stager {
         const int gr = row0 + rb * E;
 #pragma unroll
         for (int j = 0; j < E; ++j) {
-          const int gk = k0 + kb * E + j;
-          const bool ok = (gr < nrows) && (gk < K);
-          const T* p = ok ? base + (int64_t)gk * ld + gr : base;
-          const u32x4 v = *(const u32x4*)p;
-          reg[bi * E + j] = ok ? v : u32x4{0, 0, 0, 0};
+          kidx[bi * E + j] = kb * E + j;
+          off[bi * E + j] =
+              gr < nrows ? (uint32_t)(((int64_t)(kb * E + j) * ld + gr) * (int64_t)sizeof(T)) : kOutOfRange;
         }
       }
+    }
+  }
+
+  // Loads the k-tile starting at contraction index k0 (a multiple of the
+  // k-tile width); k_step_bytes is the byte distance of k0 from k-tile 0.
+  __device__ __forceinline__ void load(int k0, uint32_t k_step_bytes, int K) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool ok = (off[i] != kOutOfRange) && (k0 + kidx[i] < K);
+      const uint32_t o = ok ? off[i] + k_step_bytes : kOutOfRange;
+      reg[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)o, 0, 0);
     }
   }
 
@@ -238,8 +257,10 @@ struct GemmArgs {
   int tiles_m, tiles_n, group_m;
   const void* a;
   int64_t lda;
+  uint32_t a_span;  // bytes the A operand spans (< 2 GiB)
   const void* b;
   int64_t ldb;
+  uint32_t b_span;
 };
 
 constexpr int kLdsBytes = 4 * kStageBytes;  // two stages x (A tile + B tile) = 128 KiB
@@ -261,10 +282,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   map_tile(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, &tm, &tn);
   const int m0 = tm * kTileM, n0 = tn * kTileN;
 
-  const T* A = (const T*)g.a;
-  const T* B = (const T*)g.b;
   Stager<T, A_KC> sa;
   Stager<T, B_KC> sb;
+  sa.init((const T*)g.a, g.a_span, g.lda, m0, g.M, tid);
+  sb.init((const T*)g.b, g.b_span, g.ldb, n0, g.N, tid);
+  // byte step per k-tile: along a row (contraction contiguous) or down rows
+  const uint32_t a_step = A_KC ? (uint32_t)kRowBytes : (uint32_t)(KT * g.lda * (int64_t)sizeof(T));
+  const uint32_t b_step = B_KC ? (uint32_t)kRowBytes : (uint32_t)(KT * g.ldb * (int64_t)sizeof(T));
   f32x4 acc[8][8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -272,8 +296,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = (g.K + KT - 1) / KT;
-  sa.load(A, g.lda, m0, g.M, 0, g.K, tid);
-  sb.load(B, g.ldb, n0, g.N, 0, g.K, tid);
+  sa.load(0, 0, g.K);
+  sb.load(0, 0, g.K);
   sa.store(lds, tid);
   sb.store(lds + kStageBytes, tid);
   __syncthreads();
@@ -282,8 +306,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const char* Bs = As + kStageBytes;
     const bool more = kt + 1 < nk;
     if (more) {
-      sa.load(A, g.lda, m0, g.M, (kt + 1) * KT, g.K, tid);
-      sb.load(B, g.ldb, n0, g.N, (kt + 1) * KT, g.K, tid);
+      sa.load((kt + 1) * KT, (uint32_t)(kt + 1) * a_step, g.K);
+      sb.load((kt + 1) * KT, (uint32_t)(kt + 1) * b_step, g.K);
     }
     Mma<T>::run(As, Bs, acc, lane, wm, wn);
     if (more) {
