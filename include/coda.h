@@ -73,7 +73,7 @@ int64_t coda_prms_num_partials(coda_dtype dt, int64_t D);
  *   Hg     = round(float(H) * g)                  [M,D]  (only if g != NULL)
  *   partials[t*M + i] = sum over the columns j of tile t of float(H_ij)^2
  * for t in [0, T), T = coda_prms_num_partials(dt, D).  Tile t covers columns
- * [t*128, t*128+128) (clipped to D; an empty tile writes 0).  g and Hg are
+ * [t*64, t*64+64) (clipped to D; an empty tile writes 0).  g and Hg are
  * both NULL or both non-NULL; with g == NULL the caller folds g into W2
  * itself.  A: lda >= K; W1: ldw1 >= D; R: ldr >= D; H, Hg: ldh, ldhg >= D. */
 coda_status coda_gemm_res_prms(coda_dtype dt, int64_t M, int64_t K, int64_t D,

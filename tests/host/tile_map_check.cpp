@@ -1,7 +1,16 @@
 // Host-side checks of the GEMM kernels' index maps (built with g++, no GPU):
-// every map is a bijection onto its buffer and never leaves it, the LDS
-// swizzle spreads MFMA fragment reads over distinct banks, and the register
-// transpose used for row-contiguous operands is a true transpose.
+//  - the workgroup -> tile map is a bijection,
+//  - every direct HBM->LDS load lands where the fragment reads expect the
+//    logical element (KC and RC layouts, bf16 and fp32), covering each LDS
+//    slot of a stage exactly once,
+//  - fragment reads stay inside their operand tile, return the right logical
+//    elements (the transposing read is emulated with the lane mapping the GPU
+//    probe established: within each 16-lane group, lane i receives the i-th
+//    16-bit value of every 16-lane stripe of the group's concatenated reads),
+//  - the address shortcuts the kernel uses hold (fragment t at +1 KiB for KC,
+//    at ^ 32 t for RC bf16, h = 1 at +2 KiB),
+//  - fragment reads are LDS-bank-conflict free (KC) or at most 2-way (RC),
+//  - the epilogue slabs stay inside their LDS region.
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -13,16 +22,16 @@
 using namespace coda;
 
 static int failures = 0;
-#define CHECK(cond, ...)                   \
-  do {                                     \
-    if (!(cond)) {                         \
-      if (failures < 20) {                 \
+#define CHECK(cond, ...)                                     \
+  do {                                                       \
+    if (!(cond)) {                                           \
+      if (failures < 20) {                                   \
         fprintf(stderr, "FAIL %s:%d: ", __FILE__, __LINE__); \
-        fprintf(stderr, __VA_ARGS__);      \
-        fprintf(stderr, "\n");             \
-      }                                    \
-      ++failures;                          \
-    }                                      \
+        fprintf(stderr, __VA_ARGS__);                        \
+        fprintf(stderr, "\n");                               \
+      }                                                      \
+      ++failures;                                            \
+    }                                                        \
   } while (0)
 
 static void check_map_tile() {
@@ -36,101 +45,135 @@ static void check_map_tile() {
       for (int b = 0; b < nb; ++b) {
         int tm = -1, tn = -1;
         map_tile(b, tm_n, tn_n, gm, &tm, &tn);
-        CHECK(tm >= 0 && tm < tm_n && tn >= 0 && tn < tn_n, "map_tile(%d,%d,%d,%d) -> (%d,%d) out of range", b, tm_n,
-              tn_n, gm, tm, tn);
+        CHECK(tm >= 0 && tm < tm_n && tn >= 0 && tn < tn_n, "map_tile(%d,%d,%d,%d) -> (%d,%d)", b, tm_n, tn_n, gm, tm,
+              tn);
         if (tm >= 0 && tm < tm_n && tn >= 0 && tn < tn_n) seen[tm * tn_n + tn]++;
       }
       for (int i = 0; i < nb; ++i) CHECK(seen[i] == 1, "tile %d of %dx%d (group %d) hit %d times", i, tm_n, tn_n, gm, seen[i]);
     }
 }
 
-static void check_lds_layout() {
-  std::vector<int> seen(kStageBytes / 16, 0);
-  for (int row = 0; row < kTileM; ++row)
-    for (int c = 0; c < kChunks; ++c) {
-      const int off = lds_offset(row, c);
-      CHECK(off >= 0 && off + 16 <= kStageBytes && off % 16 == 0, "lds_offset(%d,%d)=%d", row, c, off);
-      seen[off / 16]++;
-    }
-  for (size_t i = 0; i < seen.size(); ++i) CHECK(seen[i] == 1, "LDS slot %zu used %d times", i, seen[i]);
-  // fragment reads: 16 consecutive rows (one per lane) at one logical chunk;
-  // 16-byte reads use 4 consecutive 4-byte banks.
-  for (int r0 = 0; r0 < kTileM; r0 += 16)
-    for (int c = 0; c < kChunks; ++c) {
-      int used64[64] = {0};
-      for (int i = 0; i < 16; ++i) {
-        const int bank = (lds_offset(r0 + i, c) / 4) % 64;
-        for (int w = 0; w < 4; ++w) used64[(bank + w) % 64]++;
+// ---- contraction-contiguous layout --------------------------------------
+static void check_kc() {
+  // DMA placement == fragment-read placement, full coverage
+  std::vector<int> pos_of(kTileM * 4, -1), hits(kOperandBytes / 16, 0);
+  for (int s = 0; s < kDmaSlots; ++s)
+    for (int w = 0; w < kWaves; ++w)
+      for (int L = 0; L < 64; ++L) {
+        int r, c;
+        dma_kc(s, w, L, &r, &c);
+        CHECK(r >= 0 && r < kTileM && c >= 0 && c < 4, "dma_kc(%d,%d,%d) -> (%d,%d)", s, w, L, r, c);
+        const int pos = (s * kWaves + w) * 1024 + 16 * L;
+        CHECK(pos + 16 <= kOperandBytes, "KC DMA block out of tile");
+        CHECK(kc_offset(r, c) == pos, "KC: DMA writes (%d,%d) at %d, reads expect %d", r, c, pos, kc_offset(r, c));
+        hits[pos / 16]++;
+        pos_of[r * 4 + c] = pos;
+        // a lane's chunk is the same in every slot (the kernel keeps one index)
+        int r0, c0;
+        dma_kc(0, w, L, &r0, &c0);
+        CHECK(c0 == c, "KC chunk differs between slots");
       }
-      for (int b = 0; b < 64; ++b) CHECK(used64[b] == 1, "64-bank conflict rows %d.. chunk %d bank %d", r0, c, b);
-      for (int h = 0; h < 16; h += 8) {
-        int used32[32] = {0};
-        for (int i = h; i < h + 8; ++i) {
-          const int bank = (lds_offset(r0 + i, c) / 4) % 32;
-          for (int w = 0; w < 4; ++w) used32[(bank + w) % 32]++;
+  for (size_t i = 0; i < hits.size(); ++i) CHECK(hits[i] == 1, "KC LDS slot %zu written %d times", i, hits[i]);
+  for (size_t i = 0; i < pos_of.size(); ++i) CHECK(pos_of[i] >= 0, "KC element chunk %zu never loaded", i);
+  // fragment reads: the lane reads logical (base + 16 t + i, chunk g); +1 KiB per t; banks
+  for (int base = 0; base < kTileM; base += 64)
+    for (int t = 0; t < 8 && base + 16 * t < kTileM; ++t) {
+      for (int lane = 0; lane < 64; ++lane) {
+        const int off = kc_offset(base + 16 * t + (lane & 15), lane >> 4);
+        CHECK(off == kc_offset(base + (lane & 15), lane >> 4) + 1024 * t, "KC fragment stride");
+        CHECK(off >= 0 && off + 16 <= kOperandBytes, "KC fragment read out of tile");
+      }
+      for (int g = 0; g < 4; ++g) {  // one 16-lane group = one pass of a 16-byte read
+        int used[64] = {0};
+        for (int i = 0; i < 16; ++i) {
+          const int bank = (kc_offset(base + 16 * t + i, g) / 4) % 64;
+          for (int q = 0; q < 4; ++q) used[(bank + q) % 64]++;
         }
-        for (int b = 0; b < 32; ++b) CHECK(used32[b] == 1, "32-bank conflict rows %d.. chunk %d bank %d", r0 + h, c, b);
+        for (int b = 0; b < 64; ++b) CHECK(used[b] == 1, "KC fragment bank conflict base %d t %d g %d", base, t, g);
       }
     }
 }
 
-static void check_staging() {
-  // contraction-contiguous operand: 256 threads x 8 slots cover 256 rows x 8 chunks once
-  std::vector<int> seen(kTileM * kChunks, 0);
-  for (int t = 0; t < kThreads; ++t)
-    for (int i = 0; i < 8; ++i) {
-      int row, c;
-      kc_slot(t, i, &row, &c);
-      CHECK(row >= 0 && row < kTileM && c >= 0 && c < kChunks, "kc_slot(%d,%d)", t, i);
-      seen[row * kChunks + c]++;
-    }
-  for (size_t i = 0; i < seen.size(); ++i) CHECK(seen[i] == 1, "kc chunk %zu hit %d", i, seen[i]);
-  // row-contiguous operand: E x E blocks
-  for (int E : {8, 4}) {
-    std::fill(seen.begin(), seen.end(), 0);
-    const int nb = 8 / E;
-    for (int t = 0; t < kThreads; ++t)
-      for (int i = 0; i < nb; ++i) {
-        int rb, kb;
-        rc_block(t, i, E, &rb, &kb);
-        CHECK(rb >= 0 && rb < kTileM / E && kb >= 0 && kb < kChunks, "rc_block(%d,%d,E=%d)", t, i, E);
-        for (int c = 0; c < E; ++c) seen[(rb * E + c) * kChunks + kb]++;
+// ---- row-contiguous layout ----------------------------------------------
+static void check_rc(int E) {
+  const int KTE = kKTBytes / (16 / E);  // contraction rows per k-tile (32 bf16, 16 fp32)
+  const int cpr = rc_row_bytes(E) / 16;
+  std::vector<int> hits(kOperandBytes / 16, 0), loaded(KTE * cpr, 0);
+  // element id at each 2-byte (bf16) / 4-byte (fp32) LDS position: k * 256 + col
+  std::vector<int> lds(kOperandBytes / (16 / E) * 0 + kOperandBytes, -1);
+  const int es = 16 / E;
+  for (int s = 0; s < kDmaSlots; ++s)
+    for (int w = 0; w < kWaves; ++w)
+      for (int L = 0; L < 64; ++L) {
+        int k, c;
+        dma_rc(s, w, L, E, &k, &c);
+        CHECK(k >= 0 && k < KTE && c >= 0 && c < cpr, "dma_rc E=%d (%d,%d,%d) -> (%d,%d)", E, s, w, L, k, c);
+        const int pos = (s * kWaves + w) * 1024 + 16 * L;
+        CHECK(rc_offset(k, c, E) == pos, "RC E=%d: DMA writes (%d,%d) at %d, layout says %d", E, k, c, pos,
+              rc_offset(k, c, E));
+        hits[pos / 16]++;
+        loaded[k * cpr + c]++;
+        // the kernel derives slot s's contraction row as row(slot 0) + s * kslot
+        int k0, c0;
+        dma_rc(0, w, L, E, &k0, &c0);
+        CHECK(k == k0 + s * ((kWaves * 1024) / rc_row_bytes(E)), "RC E=%d slot row stride", E);
+        for (int e = 0; e < E; ++e) lds[pos + e * es] = k * kTileM + c * E + e;
       }
-    for (size_t i = 0; i < seen.size(); ++i) CHECK(seen[i] == 1, "rc E=%d chunk %zu hit %d", E, i, seen[i]);
-  }
-}
-
-static void check_transpose() {
-  uint32_t in[8][4], out[8][4];
-  uint16_t val[8][8];
-  srand(1);
-  for (int trial = 0; trial < 100; ++trial) {
-    for (int r = 0; r < 8; ++r)
-      for (int c = 0; c < 8; ++c) val[r][c] = (uint16_t)(rand() & 0xffff);
-    for (int r = 0; r < 8; ++r)
-      for (int p = 0; p < 4; ++p) in[r][p] = (uint32_t)val[r][2 * p] | ((uint32_t)val[r][2 * p + 1] << 16);
-    transpose8x8_b16(in, out);
-    for (int c = 0; c < 8; ++c)
-      for (int k = 0; k < 8; ++k) {
-        const uint16_t got = (uint16_t)(out[c][k / 2] >> (16 * (k & 1)));
-        CHECK(got == val[k][c], "transpose: out[%d] elem %d = %04x, want %04x", c, k, got, val[k][c]);
+  for (size_t i = 0; i < hits.size(); ++i) CHECK(hits[i] == 1, "RC E=%d LDS slot %zu written %d times", E, i, hits[i]);
+  for (size_t i = 0; i < loaded.size(); ++i) CHECK(loaded[i] == 1, "RC E=%d element chunk %zu loaded %d times", E, i,
+                                                   loaded[i]);
+  const int nfrag[2] = {kFragM, kFragN};
+  const int bases_step[2] = {kWaveM, kWaveN};
+  for (int which = 0; which < 2; ++which)
+    for (int base = 0; base < kTileM; base += bases_step[which])
+      for (int t = 0; t < nfrag[which]; ++t) {
+        if (E == 8) {
+          for (int h = 0; h < 2; ++h) {
+            int bank_hits[64] = {0};
+            int got[64][4];
+            for (int lane = 0; lane < 64; ++lane) {
+              const int off = rc_tr_offset(base, t, h, lane);
+              CHECK(off == (rc_tr_lane_base(base, 0, lane) ^ (32 * t)) + 2048 * h, "RC tr address shortcut base %d t %d h %d lane %d",
+                    base, t, h, lane);
+              CHECK(off >= 0 && off + 8 <= kOperandBytes && off % 8 == 0, "RC tr read out of tile");
+              for (int e = 0; e < 4; ++e) got[lane][e] = lds[off + 2 * e];
+              for (int q = 0; q < 2; ++q) bank_hits[(off / 4 + q) % 64]++;
+            }
+            for (int b = 0; b < 64; ++b) CHECK(bank_hits[b] <= 2, "RC tr read bank %d hit %d times", b, bank_hits[b]);
+            // emulate the transposing read and check the MFMA operand layout
+            for (int lane = 0; lane < 64; ++lane) {
+              const int g = lane >> 4, i = lane & 15;
+              for (int u = 0; u < 4; ++u) {
+                const int src = 16 * u + i;  // stripe index within the group's 64 values
+                const int v = got[16 * g + src / 4][src % 4];
+                const int want = (8 * g + 4 * h + u) * kTileM + base + 16 * t + i;
+                CHECK(v == want, "RC tr lane %d u %d: got %d want %d (base %d t %d h %d)", lane, u, v, want, base, t, h);
+              }
+            }
+          }
+        } else {
+          for (int u = 0; u < 4; ++u)
+            for (int lane = 0; lane < 64; ++lane) {
+              const int off = rc_f32_offset(base, t, u, lane);
+              CHECK(off >= 0 && off + 4 <= kOperandBytes, "RC f32 read out of tile");
+              const int want = (4 * (lane >> 4) + u) * kTileM + base + 16 * t + (lane & 15);
+              CHECK(lds[off] == want, "RC f32 lane %d u %d: got %d want %d", lane, u, lds[off], want);
+            }
+        }
       }
-  }
 }
 
 static void check_epilogue_slab() {
-  // each wavefront's 16 x kEpiPitch float slab stays inside its own region
-  // and inside the first LDS stage; lane writes and reads stay in the slab
   const int slab_floats = 16 * kEpiPitch;
-  CHECK(4 * slab_floats * 4 <= 2 * kStageBytes * 2, "slabs exceed LDS");
+  CHECK((kWaves / 4) * kEpiSlabBytes <= kStageBytes, "slabs exceed their stage");
   for (int lane = 0; lane < 64; ++lane) {
-    for (int nt = 0; nt < 8; ++nt)
+    for (int nt = 0; nt < kFragN; ++nt)
       for (int e = 0; e < 4; ++e) {
         const int idx = (4 * (lane >> 4) + e) * kEpiPitch + nt * 16 + (lane & 15);
         CHECK(idx >= 0 && idx < slab_floats, "slab write lane %d", lane);
       }
-    for (int q = 0; q < 4; ++q) {
-      const int idx = ((lane >> 4) + 4 * q) * kEpiPitch + (lane & 15) * 8;
+    for (int q = 0; q < 2; ++q) {
+      const int idx = ((lane >> 3) + 8 * q) * kEpiPitch + (lane & 7) * 8;
       CHECK(idx >= 0 && idx + 8 <= slab_floats && idx % 4 == 0, "slab read lane %d", lane);
     }
   }
@@ -138,9 +181,9 @@ static void check_epilogue_slab() {
 
 int main() {
   check_map_tile();
-  check_lds_layout();
-  check_staging();
-  check_transpose();
+  check_kc();
+  check_rc(8);
+  check_rc(4);
   check_epilogue_slab();
   if (failures) {
     fprintf(stderr, "%d failures\n", failures);

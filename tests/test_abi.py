@@ -50,10 +50,11 @@ def test_status_strings(lib):
 
 
 def test_num_partials_and_workspace(lib):
-    assert lib.coda_prms_num_partials(BF16, 4096) == 32
-    assert lib.coda_prms_num_partials(BF16, 2048) == 16
-    assert lib.coda_prms_num_partials(F32, 8) == 2
-    assert lib.coda_prms_num_partials(BF16, 264) == 4
+    # one partial per 64 columns, whole 256-column tiles
+    assert lib.coda_prms_num_partials(BF16, 4096) == 64
+    assert lib.coda_prms_num_partials(BF16, 2048) == 32
+    assert lib.coda_prms_num_partials(F32, 8) == 4
+    assert lib.coda_prms_num_partials(BF16, 264) == 8
     assert lib.coda_prms_num_partials(5, 64) == -1
     assert lib.coda_prms_num_partials(BF16, 0) == -1
     c = ((16384 * 4096 * 4 + 255) // 256) * 256

@@ -78,9 +78,9 @@ def _check_stages(wl, o):
     H64 = H.astype(np.float64)
     ss = np.sum(H64 * H64, axis=1)
     np.testing.assert_allclose(P.sum(0), ss, rtol=2e-6, atol=1e-6)
-    # each partial covers its own 128 columns
+    # each partial covers its own 64 columns
     for t in range(T):
-        cols = slice(128 * t, min(128 * t + 128, wl.D))
+        cols = slice(64 * t, min(64 * t + 64, wl.D))
         np.testing.assert_allclose(P[t], np.sum(H64[:, cols] ** 2, axis=1), rtol=2e-6, atol=1e-6)
     r_host = 1.0 / np.sqrt(P.sum(0) / wl.D + wl.eps)
     np.testing.assert_allclose(o["r"].cpu().numpy(), r_host, rtol=1e-6)

@@ -121,7 +121,7 @@ coda_status launch_gemm(const char* what, int M, int N, int K, const void* a, in
   return launch_status(what);
 }
 
-int64_t num_partials(int64_t D) { return 2 * ((D + kTileN - 1) / kTileN); }
+int64_t num_partials(int64_t D) { return (kTileN / kPartialCols) * ((D + kTileN - 1) / kTileN); }
 
 template <typename T>
 coda_status gemm_res_prms_impl(int M, int K, int D, const void* A, int64_t lda, const void* W1, int64_t ldw1,

@@ -6,10 +6,10 @@
 // H out), tile reduction (partial sums of squares per row).
 //
 // The GEMM kernel hands each lane 8 consecutive columns `col .. col+7` of one
-// row through apply(q, row, col, v) (q = which of the lane's 4 rows of the
+// row through apply(q, row, col, v) (q = which of the lane's 2 rows of the
 // current 16-row slab), and calls end_slab(slab_row0) on every lane once the
-// slab is done.  Lanes l and l' with l/16 == l'/16 hold the same rows; the 16
-// lanes of such a group together cover the wavefront's 128 columns.
+// slab is done.  Lanes l and l' with l/8 == l'/8 hold the same rows; the 8
+// lanes of such a group together cover the wavefront's 64 columns.
 #pragma once
 
 #include "gemm.hpp"
@@ -17,8 +17,8 @@
 namespace coda {
 
 // First GEMM of the chain: H = round(acc + R), Hg = round(float(H) * g),
-// partials[t][row] = sum over the 128 columns of partial tile t of float(H)^2
-// with t = 2 * (column tile) + (column half of the workgroup).  The squares
+// partials[t][row] = sum over the 64 columns of partial tile t of float(H)^2
+// with t = 4 * (column tile) + (column quarter of the workgroup).  The squares
 // use the stored (rounded) H so that r computed from them normalises exactly
 // the H that is kept for the backward.
 template <typename T>
@@ -35,20 +35,19 @@ struct EpiResPrms {
   };
   Params p;
   float gv[8];
-  float ss[4];
+  float ss[2];
   int lane, t, M;
 
   __device__ __forceinline__ EpiResPrms(const Params& p_, int lane_, int wm, int wn, int m0, int n0, int tn,
                                         int M_, int N)
-      : p(p_), lane(lane_), t(2 * tn + wn), M(M_) {
+      : p(p_), lane(lane_), t(4 * tn + wn), M(M_) {
     (void)wm;
     (void)m0;
-    const int col = n0 + wn * 128 + (lane & 15) * 8;
+    const int col = n0 + wn * kWaveN + (lane & 7) * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i) gv[i] = 1.f;
     if (p.g != nullptr && col < N) Chunk8<T>::load(p.g + col, gv);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) ss[q] = 0.f;
+    ss[0] = ss[1] = 0.f;
   }
 
   __device__ __forceinline__ void apply(int q, int row, int col, float v[8]) {
@@ -70,14 +69,13 @@ struct EpiResPrms {
 
   __device__ __forceinline__ void end_slab(int slab_row0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
       float s = ss[q];
       s += __shfl_xor(s, 1);
       s += __shfl_xor(s, 2);
       s += __shfl_xor(s, 4);
-      s += __shfl_xor(s, 8);
-      const int row = slab_row0 + (lane >> 4) + 4 * q;
-      if ((lane & 15) == 0 && row < M) p.partials[(int64_t)t * M + row] = s;
+      const int row = slab_row0 + (lane >> 3) + 8 * q;
+      if ((lane & 7) == 0 && row < M) p.partials[(int64_t)t * M + row] = s;
       ss[q] = 0.f;
     }
   }

@@ -14,19 +14,23 @@
 //   B_KC = true : B(k, n) at b[n * ldb + k]   (contraction contiguous)
 //   B_KC = false: B(k, n) at b[k * ldb + n]   (N contiguous: a [K, N] matrix)
 //
-// Workgroup: 256 threads = 4 wavefronts (2 x 2), a 256 x 256 output tile,
-// each wavefront a 128 x 128 sub-tile held as 8 x 8 MFMA 16x16 accumulators
-// (256 fp32 per lane).  Per k-tile (128 bytes of contraction = 64 bf16 or 32
-// fp32) both operand tiles are loaded from HBM into registers, written to a
-// double-buffered, XOR-swizzled LDS stage ([row][k], contraction contiguous;
-// row-contiguous operands are transposed in registers on the way), and read
-// back as MFMA fragments:
-//   bf16: v_mfma_f32_16x16x32_bf16, one 16-byte fragment per lane per operand
+// Workgroup: 512 threads = 8 wavefronts (2 x 4, two per SIMD), a 256 x 256
+// output tile, each wavefront a 128 x 64 sub-tile held as 8 x 4 MFMA 16x16
+// accumulators (128 fp32 per lane).  Two wavefronts per SIMD let one issue
+// MFMAs while the other waits on LDS or the barrier.  The contraction is cut
+// into k-tiles of 64 bytes per operand row (32 bf16 / 16 fp32).  Each k-tile
+// of both operands goes from HBM straight into one of four LDS stages
+// (buffer loads with an LDS destination; no registers, no LDS write
+// instructions), contraction-contiguous operands as [row][k] and
+// row-contiguous operands as they lie in memory ([k][row]), both XOR
+// swizzled.  Fragments are read back with 16-byte reads ([row][k]) or 8-byte
+// transposing reads ([k][row], bf16) and feed
+//   bf16: v_mfma_f32_16x16x32_bf16
 //   fp32: v_mfma_f32_16x16x4_f32, the 4 floats of a fragment feed 4 MFMAs
-// Lane l of a 16x16 fragment holds operand row (l % 16) and contraction chunk
-// (l / 16); accumulator element e of lane l is output (4*(l/16)+e, l%16).
-// The contraction order inside one MFMA is the same for A and B, so the
-// product does not depend on how the hardware orders the k values.
+// Lane l of a 16x16 fragment holds operand row (l % 16) and contraction
+// elements of group (l / 16); accumulator element e of lane l is output
+// (4*(l/16)+e, l%16).  The contraction order inside one MFMA is the same for
+// A and B, so the product does not depend on how the hardware orders k.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -99,158 +103,162 @@ struct Chunk8<float> {
   __device__ static float round(float x) { return x; }
 };
 
-// ---- operand staging: HBM -> registers -> LDS ---------------------------
+// ---- operand staging: HBM -> LDS directly --------------------------------
 // Global reads go through a raw buffer descriptor spanning exactly the
 // operand's bytes.  A slot that falls outside the matrix (row >= rows,
 // contraction index >= K) gets an offset past the descriptor's extent, for
-// which the hardware returns zeros: no load ever leaves the operand and no
-// select has to wait for the load to land.
+// which the hardware returns zeros: no load ever leaves the operand.
 constexpr uint32_t kOutOfRange = 0x80000000u;  // every operand spans < 2 GiB
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t span_bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)span_bytes, 0x00020000);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+
 template <typename T, bool KC>
-struct Stager {
+struct Dma {
   static constexpr int E = Elem<T>::E;
+  static constexpr int KTE = kKTBytes / (int)sizeof(T);  // contraction elements per k-tile
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t off[8];  // byte offset of each slot for the k-tile at k0 = 0 (kOutOfRange: row outside)
-  int kidx[8];      // contraction index of each slot's first element at k0 = 0
-  u32x4 reg[8];
+  uint32_t voff[kDmaSlots];  // byte offset of each slot at k-tile 0, or kOutOfRange (row outside)
+  int kidx0;                 // contraction index of slot 0 at k-tile 0
+  int kslot;                 // contraction index step between slots (KC: 0, RC: rows per slot)
+  uint32_t kstep;            // bytes between consecutive k-tiles
 
-  __device__ __forceinline__ void init(const T* base, uint32_t span_bytes, int64_t ld, int row0, int nrows,
-                                       int tid) {
-    rsrc = make_rsrc(base, span_bytes);
-    if constexpr (KC) {
+  __device__ __forceinline__ void init(const void* p, uint32_t span_bytes, int64_t ld, int row0, int nrows,
+                                       int wave, int lane) {
+    rsrc = make_rsrc(p, span_bytes);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        int row, c;
-        kc_slot(tid, i, &row, &c);
-        const int gr = row0 + row;
-        kidx[i] = c * E;
-        off[i] = gr < nrows ? (uint32_t)(((int64_t)gr * ld + c * E) * (int64_t)sizeof(T)) : kOutOfRange;
-      }
-    } else {
-      constexpr int NB = 8 / E;  // E x E blocks per thread (bf16: 1, fp32: 2)
-#pragma unroll
-      for (int bi = 0; bi < NB; ++bi) {
-        int rb, kb;
-        rc_block(tid, bi, E, &rb, &kb);
-        const int gr = row0 + rb * E;
-#pragma unroll
-        for (int j = 0; j < E; ++j) {
-          kidx[bi * E + j] = kb * E + j;
-          off[bi * E + j] =
-              gr < nrows ? (uint32_t)(((int64_t)(kb * E + j) * ld + gr) * (int64_t)sizeof(T)) : kOutOfRange;
-        }
+    for (int s = 0; s < kDmaSlots; ++s) {
+      if constexpr (KC) {
+        int r, c;
+        dma_kc(s, wave, lane, &r, &c);
+        const int gr = row0 + r;
+        if (s == 0) kidx0 = c * E;  // the chunk of a lane is the same in every slot
+        voff[s] = gr < nrows ? (uint32_t)(((int64_t)gr * ld + c * E) * (int64_t)sizeof(T)) : kOutOfRange;
+      } else {
+        int k, c;
+        dma_rc(s, wave, lane, E, &k, &c);
+        const int gr = row0 + c * E;
+        if (s == 0) kidx0 = k;  // slot s: contraction row k + s * kslot
+        voff[s] = gr < nrows ? (uint32_t)(((int64_t)k * ld + gr) * (int64_t)sizeof(T)) : kOutOfRange;
       }
     }
+    kslot = KC ? 0 : (kWaves * 1024) / rc_row_bytes(E);
+    kstep = KC ? (uint32_t)kKTBytes : (uint32_t)(KTE * ld * (int64_t)sizeof(T));
   }
 
-  // Loads the k-tile starting at contraction index k0 (a multiple of the
-  // k-tile width); k_step_bytes is the byte distance of k0 from k-tile 0.
-  __device__ __forceinline__ void load(int k0, uint32_t k_step_bytes, int K) {
+  // Loads k-tile kt into the operand tile at `dst`.  `wave` is wave-uniform;
+  // each slot fills the 1 KiB block (4 s + wave) of the tile.
+  __device__ __forceinline__ void issue(char* dst, int kt, int K, int wave) const {
+    const uint32_t kb = (uint32_t)kt * kstep;
+    const int k0 = kt * KTE + kidx0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool ok = (off[i] != kOutOfRange) && (k0 + kidx[i] < K);
-      const uint32_t o = ok ? off[i] + k_step_bytes : kOutOfRange;
-      reg[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)o, 0, 0);
-    }
-  }
-
-  __device__ __forceinline__ void store(char* lds, int tid) const {
-    if constexpr (KC) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        int row, c;
-        kc_slot(tid, i, &row, &c);
-        *(u32x4*)(lds + lds_offset(row, c)) = reg[i];
-      }
-    } else if constexpr (E == 8) {
-      // 8 x 8 bf16 transpose: reg[j] holds contraction index j for tile rows
-      // rb*8 .. rb*8+7 (two per dword); out[c] gathers tile row c's 8
-      // contraction values.
-      int rb, kb;
-      rc_block(tid, 0, E, &rb, &kb);
-      uint32_t in[8][4], out[8][4];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) in[j][p] = reg[j][p];
-      transpose8x8_b16(in, out);
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        *(u32x4*)(lds + lds_offset(rb * 8 + c, kb)) = u32x4{out[c][0], out[c][1], out[c][2], out[c][3]};
-    } else {
-      // 4 x 4 fp32 transpose, two blocks per thread
-#pragma unroll
-      for (int bi = 0; bi < 2; ++bi) {
-        int rb, kb;
-        rc_block(tid, bi, E, &rb, &kb);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const u32x4 o{reg[bi * 4 + 0][c], reg[bi * 4 + 1][c], reg[bi * 4 + 2][c], reg[bi * 4 + 3][c]};
-          *(u32x4*)(lds + lds_offset(rb * 4 + c, kb)) = o;
-        }
-      }
+    for (int s = 0; s < kDmaSlots; ++s) {
+      const bool ok = (voff[s] != kOutOfRange) & (k0 + s * kslot < K);
+      const uint32_t o = ok ? voff[s] + kb : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + (s * kWaves + wave) * 1024), 16, o, 0, 0,
+                                               0);
     }
   }
 };
 
-// ---- one k-tile of MFMAs from an LDS stage ------------------------------
+// ---- MFMA fragments ----------------------------------------------------
+// Eight fragments (t = 0..7) of the wavefront's 128 operand rows for one
+// k-tile, 16 bytes per lane each (fragment maps in tile_map.hpp).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Keeps the compiler from treating v as loop-invariant, so addresses derived
+// from it are recomputed where used instead of all being hoisted into
+// registers (four stages x eight fragments would not fit).
+__device__ __forceinline__ void opaque(int& v) { asm volatile("" : "+v"(v)); }
+
+template <typename T, bool KC, int NF>
+struct FragReader {
+  int off0;  // lane's byte offset of fragment 0 in the operand tile (RC bf16: h = 0 base)
+  int base, lane;
+  __device__ __forceinline__ FragReader(int base_, int lane_) : base(base_), lane(lane_) {
+    off0 = KC ? kc_offset(base_ + (lane_ & 15), lane_ >> 4)
+              : (sizeof(T) == 2 ? rc_tr_lane_base(base_, 0, lane_) : 0);
+  }
+  __device__ __forceinline__ void read(const char* tile, u32x4 (&f)[NF]) {
+    opaque(off0);
+    if constexpr (KC) {
+      // the swizzle depends on row % 16 only: fragment t lies 16 rows (1 KiB) further
+      const char* p = tile + off0;
+#pragma unroll
+      for (int t = 0; t < NF; ++t) f[t] = *(const u32x4*)(p + t * 1024);
+    } else if constexpr (sizeof(T) == 2) {
+      // fragment t at (tile + lane base) ^ 32 t, computed on the 32-bit LDS
+      // address (stage bases are 1 KiB aligned, so the XOR stays inside the
+      // tile); h = 1 is 4 contraction rows (2 KiB) further
+      const uint32_t p = (uint32_t)(uintptr_t)((const lds_char*)tile + off0);
+#pragma unroll
+      for (int t = 0; t < NF; ++t) {
+        const uint32_t q = p ^ (uint32_t)(32 * t);
+        const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)q));
+        const u32x2 hi =
+            __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(q + 2048)));
+        f[t] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NF; ++t)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) f[t][u] = *(const uint32_t*)(tile + rc_f32_offset(base, t, u, lane));
+    }
+  }
+};
+
 template <typename T>
 struct Mma;
 
 template <>
 struct Mma<uint16_t> {
-  __device__ __forceinline__ static void run(const char* As, const char* Bs, f32x4 (&acc)[8][8], int lane,
-                                             int wm, int wn) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int ch = ks * 4 + (lane >> 4);
-      bf16x8 af[8], bfr[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int ra = wm * 128 + t * 16 + (lane & 15);
-        const int rbn = wn * 128 + t * 16 + (lane & 15);
-        af[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(As + lds_offset(ra, ch)));
-        bfr[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Bs + lds_offset(rbn, ch)));
-      }
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
-    }
+  __device__ __forceinline__ static void mac(f32x4& acc, const u32x4& a, const u32x4& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc,
+                                                  0, 0, 0);
   }
 };
 
 template <>
 struct Mma<float> {
-  __device__ __forceinline__ static void run(const char* As, const char* Bs, f32x4 (&acc)[8][8], int lane,
-                                             int wm, int wn) {
+  __device__ __forceinline__ static void mac(f32x4& acc, const u32x4& a, const u32x4& b) {
+    // the four floats of each fragment feed four K=4 products
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int ch = ks * 4 + (lane >> 4);
-      f32x4 af[8], bfr[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int ra = wm * 128 + t * 16 + (lane & 15);
-        const int rbn = wn * 128 + t * 16 + (lane & 15);
-        af[t] = *(const f32x4*)(As + lds_offset(ra, ch));
-        bfr[t] = *(const f32x4*)(Bs + lds_offset(rbn, ch));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < 8; ++nt)
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[mt][j], bfr[nt][j], acc[mt][nt], 0, 0, 0);
-    }
+    for (int j = 0; j < 4; ++j)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j]), __uint_as_float(b[j]), acc, 0, 0, 0);
   }
 };
+
+template <typename T>
+__device__ __forceinline__ void mma_tile(f32x4 (&acc)[kFragM][kFragN], const u32x4 (&fa)[kFragM],
+                                         const u32x4 (&fb)[kFragN]) {
+#pragma unroll
+  for (int mt = 0; mt < kFragM; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < kFragN; ++nt) Mma<T>::mac(acc[mt][nt], fa[mt], fb[nt]);
+}
+
+// Workgroup barriers of the pipeline.  stage_barrier waits until at most two
+// k-tiles of this wavefront's direct loads (kDmaSlots per operand each) are
+// still in flight and its LDS reads are done, then meets the other
+// wavefronts: after it, every wavefront's loads of all older k-tiles have
+// landed.
+// drain_barrier waits for everything.  The memory clobber keeps the compiler
+// from moving LDS accesses across either.
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(2 * (2 * kDmaSlots) == 8, "the vmcnt literal assumes two k-tiles of 2 x kDmaSlots loads");
+  asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ void drain_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 struct GemmArgs {
   int M, N, K;
@@ -263,77 +271,96 @@ struct GemmArgs {
   uint32_t b_span;
 };
 
-constexpr int kLdsBytes = 4 * kStageBytes;  // two stages x (A tile + B tile) = 128 KiB
+// One step of the k-pipeline for k-tile kt held in stage S:
+//   issue the direct loads of tile kt+3 into stage (S+3) % 4,
+//   read the fragments of tile kt from stage S and run its 64 products,
+//   stage_barrier: this wavefront's loads of tile kt+1 have landed (only
+//   tiles kt+2 and kt+3 may still be in flight) and its reads of stage S
+//   are done; after the barrier that holds for every wavefront.
+// Stage (S+3) % 4 held tile kt-1, read in step kt-1 before its barrier, so
+// it is free.  Tiles past the end of K load as zeros, so steps need no guards.
+template <typename T, bool A_KC, bool B_KC, int S>
+__device__ __forceinline__ void kstep(char* const (&st)[kStages], const Dma<T, A_KC>& da, const Dma<T, B_KC>& db,
+                                      FragReader<T, A_KC, kFragM>& ra, FragReader<T, B_KC, kFragN>& rb,
+                                      f32x4 (&acc)[kFragM][kFragN], int kt, int K, int wave) {
+  constexpr int SL = (S + 3) % kStages;
+  da.issue(st[SL], kt + 3, K, wave);
+  db.issue(st[SL] + kOperandBytes, kt + 3, K, wave);
+  u32x4 fa[kFragM], fb[kFragN];
+  ra.read(st[S], fa);
+  rb.read(st[S] + kOperandBytes, fb);
+  mma_tile<T>(acc, fa, fb);
+  stage_barrier();
+}
 
 // The epilogue sees the wavefront's accumulators 16 rows at a time, staged
 // through LDS so that each lane holds 8 consecutive columns of one row:
-// lane l, slot q (0..3) gets row (l/16 + 4q) of the 16-row slab and columns
-// [8*(l%16), 8*(l%16)+8) of the wavefront's 128.  Epi provides
+// lane l, slot q (0..1) gets row (l/8 + 8q) of the 16-row slab and columns
+// [8*(l%8), 8*(l%8)+8) of the wavefront's 64.  Epi provides
 //   apply(q, row, col, v[8])   for rows < M and columns < N (col % 8 == 0)
-//   end_slab(mt, slab_row0)    after all lanes applied one 16-row slab
+//   end_slab(slab_row0)        after all lanes applied one 16-row slab
 template <typename T, bool A_KC, bool B_KC, class Epi>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(
     GemmArgs g, typename Epi::Params ep) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  constexpr int KT = kRowBytes / sizeof(T);  // contraction elements per k-tile
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  __shared__ __attribute__((aligned(1024))) char st0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char st1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char st2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char st3[kStageBytes];
+  char* const st[kStages] = {st0, st1, st2, st3};
+  constexpr int KTE = kKTBytes / (int)sizeof(T);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
   int tm, tn;
   map_tile(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, &tm, &tn);
   const int m0 = tm * kTileM, n0 = tn * kTileN;
 
-  Stager<T, A_KC> sa;
-  Stager<T, B_KC> sb;
-  sa.init((const T*)g.a, g.a_span, g.lda, m0, g.M, tid);
-  sb.init((const T*)g.b, g.b_span, g.ldb, n0, g.N, tid);
-  // byte step per k-tile: along a row (contraction contiguous) or down rows
-  const uint32_t a_step = A_KC ? (uint32_t)kRowBytes : (uint32_t)(KT * g.lda * (int64_t)sizeof(T));
-  const uint32_t b_step = B_KC ? (uint32_t)kRowBytes : (uint32_t)(KT * g.ldb * (int64_t)sizeof(T));
-  f32x4 acc[8][8];
+  Dma<T, A_KC> da;
+  Dma<T, B_KC> db;
+  da.init(g.a, g.a_span, g.lda, m0, g.M, wave, lane);
+  db.init(g.b, g.b_span, g.ldb, n0, g.N, wave, lane);
+  FragReader<T, A_KC, kFragM> ra(wm * kWaveM, lane);
+  FragReader<T, B_KC, kFragN> rb(wn * kWaveN, lane);
+  f32x4 acc[kFragM][kFragN];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < kFragM; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kFragN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = (g.K + KT - 1) / KT;
-  sa.load(0, 0, g.K);
-  sb.load(0, 0, g.K);
-  sa.store(lds, tid);
-  sb.store(lds + kStageBytes, tid);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const char* As = lds + (kt & 1) * 2 * kStageBytes;
-    const char* Bs = As + kStageBytes;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      sa.load((kt + 1) * KT, (uint32_t)(kt + 1) * a_step, g.K);
-      sb.load((kt + 1) * KT, (uint32_t)(kt + 1) * b_step, g.K);
-    }
-    Mma<T>::run(As, Bs, acc, lane, wm, wn);
-    if (more) {
-      char* nxt = lds + ((kt + 1) & 1) * 2 * kStageBytes;
-      sa.store(nxt, tid);
-      sb.store(nxt + kStageBytes, tid);
-    }
-    __syncthreads();
+  const int nk = (g.K + KTE - 1) / KTE;
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    da.issue(st[t], t, g.K, wave);
+    db.issue(st[t] + kOperandBytes, t, g.K, wave);
   }
+  asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");  // tile 0 landed everywhere
+  // whole groups of four k-steps: a ragged end runs up to three all-zero
+  // tiles (harmless products of zeros) and keeps the loop body uniform
+  for (int kt = 0; kt < nk; kt += kStages) {
+    kstep<T, A_KC, B_KC, 0>(st, da, db, ra, rb, acc, kt, g.K, wave);
+    kstep<T, A_KC, B_KC, 1>(st, da, db, ra, rb, acc, kt + 1, g.K, wave);
+    kstep<T, A_KC, B_KC, 2>(st, da, db, ra, rb, acc, kt + 2, g.K, wave);
+    kstep<T, A_KC, B_KC, 3>(st, da, db, ra, rb, acc, kt + 3, g.K, wave);
+  }
+  drain_barrier();  // no direct load may land in the LDS the epilogue reuses
 
   // ---- epilogue ----
   Epi epi(ep, lane, wm, wn, m0, n0, tn, g.M, g.N);
-  float* slab = (float*)(lds + wave * 16 * kEpiPitch * 4);
-  const int row_base = m0 + wm * 128;
-  const int col = n0 + wn * 128 + (lane & 15) * 8;
+  float* slab = (float*)(((wave & 3) == 0 ? st0 : (wave & 3) == 1 ? st1 : (wave & 3) == 2 ? st2 : st3) +
+                         (wave >> 2) * kEpiSlabBytes);
+  const int row_base = m0 + wm * kWaveM;
+  const int col = n0 + wn * kWaveN + (lane & 7) * 8;
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
+  for (int mt = 0; mt < kFragM; ++mt) {
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
+    for (int nt = 0; nt < kFragN; ++nt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) slab[(4 * (lane >> 4) + e) * kEpiPitch + nt * 16 + (lane & 15)] = acc[mt][nt][e];
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int rl = (lane >> 4) + 4 * q;
-      const float* src = slab + rl * kEpiPitch + (lane & 15) * 8;
+    for (int q = 0; q < 2; ++q) {
+      const int rl = (lane >> 3) + 8 * q;
+      const float* src = slab + rl * kEpiPitch + (lane & 7) * 8;
       const f32x4 lo = *(const f32x4*)src, hi = *(const f32x4*)(src + 4);
       float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       const int row = row_base + mt * 16 + rl;

@@ -2,7 +2,8 @@
 //
 // Everything here is pure integer math, usable from device code and from a
 // plain C++ host compiler (the unit test builds it with g++ and checks that
-// every map is a bijection that stays inside its buffer).
+// every map is a bijection that stays inside its buffer and that fragment
+// reads spread over distinct LDS banks).
 #pragma once
 
 #include <stdint.h>
@@ -15,24 +16,100 @@
 
 namespace coda {
 
-// Macro tile: 256 x 256 outputs per workgroup of 4 wavefronts (2 x 2), each
-// wavefront owning a 128 x 128 sub-tile.  One k-tile is 128 bytes of the
-// contraction per operand row (64 bf16 or 32 fp32), i.e. eight 16-byte chunks.
+// Macro tile: 256 x 256 outputs per workgroup of 8 wavefronts (2 x 4, two per
+// SIMD), each wavefront owning a 128 x 64 sub-tile.  One k-tile is 64 bytes of
+// the contraction per operand row (32 bf16 or 16 fp32).  Four LDS stages.
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;
-constexpr int kThreads = 256;
-constexpr int kRowBytes = 128;
-constexpr int kChunks = 8;
-constexpr int kStageBytes = kTileM * kRowBytes;  // one operand, one k-tile: 32 KiB
-constexpr int kEpiPitch = 132;                   // floats per row of the epilogue slab
-constexpr int kPartialCols = 128;                // columns per partial-RMS tile
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWaveM = 128;                         // rows of a wavefront's sub-tile
+constexpr int kWaveN = 64;                          // columns of a wavefront's sub-tile
+constexpr int kFragM = kWaveM / 16;                 // 16-row A fragments per wavefront: 8
+constexpr int kFragN = kWaveN / 16;                 // 16-column B fragments per wavefront: 4
+constexpr int kKTBytes = 64;                        // contraction bytes per row per k-tile
+constexpr int kOperandBytes = kTileM * kKTBytes;    // one operand, one k-tile: 16 KiB
+constexpr int kStageBytes = 2 * kOperandBytes;      // A + B: 32 KiB
+constexpr int kStages = 4;
+constexpr int kDmaSlots = kOperandBytes / (kWaves * 1024);  // 1 KiB DMA blocks per wave per operand: 2
+constexpr int kEpiPitch = kWaveN + 4;               // floats per row of the epilogue slab
+constexpr int kEpiSlabBytes = 16 * kEpiPitch * 4;   // one wavefront's 16-row slab
+constexpr int kPartialCols = kWaveN;                // columns per partial-RMS tile
 
-// LDS placement of chunk `c` (0..7) of tile row `row`.  The chunk index is
-// XOR-swizzled with a function of the row so that the 16 rows one MFMA
-// fragment read touches land on distinct banks for both 32- and 64-bank
-// views of the LDS (rows r and r+8 get different swizzles).
-CODA_HD int lds_swizzle(int row) { return (row ^ (row >> 3)) & 7; }
-CODA_HD int lds_offset(int row, int c) { return row * kRowBytes + ((c ^ lds_swizzle(row)) << 4); }
+// ---- contraction-contiguous ("KC") operand tile ---------------------------
+// 256 operand rows x 64 bytes (four 16-byte chunks).  Chunk c of row r is
+// stored at chunk position c ^ ((r >> 2) & 3): the 16 rows one MFMA fragment
+// read touches (r0..r0+15 at one chunk) then cover all 64 banks once.
+CODA_HD int kc_swizzle(int r) { return (r >> 2) & 3; }
+CODA_HD int kc_offset(int r, int c) { return r * kKTBytes + ((c ^ kc_swizzle(r)) << 4); }
+
+// ---- row-contiguous ("RC") operand tile --------------------------------
+// The contraction runs across memory rows: KTE contraction rows (32 bf16 /
+// 16 fp32) of 256 operand elements (512 / 1024 bytes).  16-byte chunk c of
+// contraction row k is stored at chunk position c ^ rc_swizzle(k), an even
+// XOR (whole 32-byte segments move) that spreads the 16 rows one transposing
+// fragment read touches over all banks, each bank exactly twice.
+CODA_HD int rc_swizzle(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
+CODA_HD int rc_row_bytes(int E) { return kTileM * (16 / E); }  // E elements per chunk
+CODA_HD int rc_offset(int k, int c, int E) { return k * rc_row_bytes(E) + ((c ^ rc_swizzle(k)) << 4); }
+
+// ---- HBM -> LDS direct loads ---------------------------------------------
+// Each load instruction of a wavefront writes one contiguous 1 KiB LDS block,
+// lane L's 16 bytes at block + 16 L.  Slot s of wavefront w fills block
+// b = kWaves s + w of the operand tile; the maps below give the logical
+// element each lane must fetch so that the block holds the swizzled layout.
+//
+// KC: block b holds rows 16 b .. 16 b + 15; lane L -> row 16 b + L/4,
+//     logical chunk (L % 4) ^ kc_swizzle(row).
+CODA_HD void dma_kc(int s, int w, int L, int* row, int* chunk) {
+  const int b = s * kWaves + w;
+  *row = 16 * b + (L >> 2);
+  *chunk = (L & 3) ^ kc_swizzle(*row);
+}
+// RC: block b holds 1024 / row_bytes contraction rows; lane L -> contraction
+//     row k and logical chunk c (operand elements c*E .. c*E + E - 1).
+CODA_HD void dma_rc(int s, int w, int L, int E, int* k, int* chunk) {
+  const int b = s * kWaves + w;
+  const int chunks_per_row = rc_row_bytes(E) / 16;  // 32 (bf16) or 64 (fp32)
+  const int pos = b * 64 + L;                        // 16-byte position within the tile
+  *k = pos / chunks_per_row;
+  *chunk = (pos % chunks_per_row) ^ rc_swizzle(*k);
+}
+
+// ---- MFMA fragment reads (16 x 16 x 32 bf16 / 16 x 16 x 4 fp32) -----------
+// Lane l = 16 g + i.  Fragment t of a wavefront covers operand rows
+// base + 16 t .. + 15; lane l supplies operand row base + 16 t + i and
+// contraction elements [g*E, g*E + E) of the k-tile (E = 8 bf16, 4 fp32).
+//
+// KC: one 16-byte read at kc_offset(base + 16 t + i, g).
+//
+// RC bf16: two 8-byte transposing reads (ds_read_b64_tr_b16), h = 0, 1.
+// Within each 16-lane group the hardware hands lane i the i-th 16-bit value
+// of every 16-lane stripe of the group's concatenated reads.  Lane j of the
+// group reads 4 consecutive operand elements at contraction row
+// 8 g + 4 h + j / 4, operand columns base + 16 t + 4 (j % 4) .. + 3; lane i
+// then receives operand column base + 16 t + i at contraction rows
+// 8 g + 4 h .. + 3, exactly the MFMA operand layout.
+CODA_HD int rc_tr_offset(int base, int t, int h, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int k = 8 * g + 4 * h + (j >> 2);
+  const int col = base + 16 * t + 4 * (j & 3);  // first of 4 bf16 elements
+  const int c = col >> 3, within = (col & 7) * 2;
+  return rc_offset(k, c, 8) + within;
+}
+// For bf16 the t dependence is a single XOR: the swizzle and t both act on
+// address bits 5..7 only and every other term leaves those bits clear, so
+// rc_tr_offset(base, t, h, lane) == rc_tr_offset(base, 0, h, lane) ^ (32 t)
+// for base a multiple of 128 (checked on the host).
+CODA_HD int rc_tr_lane_base(int base, int h, int lane) { return rc_tr_offset(base, 0, h, lane); }
+// RC fp32: four 4-byte reads, u = 0..3: contraction row 4 g + u, operand
+// column base + 16 t + i (feeding the u-th K=4 product).
+CODA_HD int rc_f32_offset(int base, int t, int u, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int k = 4 * g + u;
+  const int col = base + 16 * t + i;
+  return rc_offset(k, col >> 2, 4) + (col & 3) * 4;
+}
 
 // Workgroup -> output tile.  The dispatcher places workgroup b on XCD b % 8;
 // each XCD is given a contiguous range of logical tile ids so that tiles
@@ -49,52 +126,6 @@ CODA_HD void map_tile(int b, int tiles_m, int tiles_n, int group_m, int* tm, int
   const int within = logical - gidx * per_group;
   *tm = first_m + within % gsize;
   *tn = within / gsize;
-}
-
-// Staging of one k-tile of one operand (kTileM rows x kRowBytes) by the
-// workgroup's 256 threads, eight 16-byte registers per thread.
-//
-// Contraction-contiguous operand: thread t, slot i handles chunk id = i*256+t,
-// row id/8, chunk id%8 (one global 16-byte load, one LDS 16-byte store).
-CODA_HD void kc_slot(int tid, int i, int* row, int* chunk) {
-  const int id = i * kThreads + tid;
-  *row = id >> 3;
-  *chunk = id & 7;
-}
-
-// Row-contiguous operand (the contraction runs across rows of memory): the
-// tile is cut into E x E element blocks (E elements per chunk); block id
-// = i*256 + t covers tile rows [rb*E, rb*E+E) and contraction chunk kb.  The
-// thread loads E global chunks (one per contraction index), transposes the
-// E x E block in registers and stores E LDS chunks (one per tile row).
-CODA_HD void rc_block(int tid, int i, int E, int* rb, int* kb) {
-  const int id = i * kThreads + tid;
-  const int per_k = kTileM / E;
-  *rb = id % per_k;
-  *kb = id / per_k;
-}
-
-// Byte permute of two dwords (the semantics of v_perm_b32 for selector bytes
-// 0..7): byte b of the result is byte sel.b of the 8-byte value {hi, lo}, lo
-// supplying bytes 0..3.
-CODA_HD uint32_t perm_bytes(uint32_t hi, uint32_t lo, uint32_t sel) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  return __builtin_amdgcn_perm(hi, lo, sel);
-#else
-  const uint64_t v = ((uint64_t)hi << 32) | lo;
-  uint32_t r = 0;
-  for (int b = 0; b < 4; ++b) r |= (uint32_t)((v >> (8 * ((sel >> (8 * b)) & 7))) & 0xff) << (8 * b);
-  return r;
-#endif
-}
-
-// Transpose of an 8 x 8 block of 16-bit values held as 8 rows of 4 dwords
-// (two values per dword, the lower column in the low half): out[c] is column
-// c of `in`, packed the same way.
-CODA_HD void transpose8x8_b16(const uint32_t (&in)[8][4], uint32_t (&out)[8][4]) {
-  for (int c = 0; c < 8; ++c)
-    for (int p = 0; p < 4; ++p)
-      out[c][p] = perm_bytes(in[2 * p + 1][c >> 1], in[2 * p][c >> 1], (c & 1) ? 0x07060302u : 0x05040100u);
 }
 
 }  // namespace coda
