@@ -47,6 +47,23 @@ def parse():
     return ap.parse_args()
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the second GEMM from the committed counter
+    profile, or None when the kernel sources changed since it was taken."""
+    import glob
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"traffic_gemm_rowscale_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    csrc = os.path.join(ROOT, "transformer_gemm_epilogue_gemm1_amd", "csrc")
+    files = sorted(glob.glob(os.path.join(csrc, "*.hpp")) + glob.glob(os.path.join(csrc, "*.hip")))
+    h = hashlib.sha256(b"".join(open(p, "rb").read() for p in files)).hexdigest()
+    return rec["bytes_per_launch"] if h == rec.get("csrc_sha256") else None
+
+
 def cpu_baseline(wl, x, budget_s: float):
     """The fp64 oracle, as it stands, on a bounded sample of rows of the same workload."""
     import threadpoolctl
@@ -167,7 +184,8 @@ def main():
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "roofline": {"bound": "mfma", "kernel": "coda_gemm_rowscale (second GEMM, row-scale epilogue)",
                      "achieved": round(g2_tflops, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
-                     "frac": round(g2_tflops / peak, 4), "traffic": None,
+                     "frac": round(g2_tflops / peak, 4), "traffic": measured_traffic(wl.name),
+                     "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "algorithmic_flops_per_launch": g2_flops},
         "kernels_ms": {"coda_gemm_res_prms": round(g1_avg, 4), "coda_rms_combine": round(comb_avg, 4),
                        "coda_gemm_rowscale": round(g2_avg, 4)},
