@@ -194,16 +194,16 @@ struct FragReader {
 #pragma unroll
       for (int t = 0; t < NF; ++t) f[t] = *(const u32x4*)(p + t * 1024);
     } else if constexpr (sizeof(T) == 2) {
-      // fragment t at (tile + lane base) ^ 32 t, computed on the 32-bit LDS
-      // address (stage bases are 1 KiB aligned, so the XOR stays inside the
-      // tile); h = 1 is 4 contraction rows (2 KiB) further
-      const uint32_t p = (uint32_t)(uintptr_t)((const lds_char*)tile + off0);
+      // fragment t at lane base ^ 32 t; h = 1 is 4 contraction rows (2 KiB)
+      // further.  The address stays a pointer into the stage array: with an
+      // integer-made address the compiler cannot tell which direct loads the
+      // read depends on and waits for all of them.
+      const lds_char* p = (const lds_char*)tile;
 #pragma unroll
       for (int t = 0; t < NF; ++t) {
-        const uint32_t q = p ^ (uint32_t)(32 * t);
-        const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)q));
-        const u32x2 hi =
-            __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(q + 2048)));
+        const lds_char* q = p + (off0 ^ (32 * t));
+        const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)q));
+        const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(q + 2048)));
         f[t] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
     } else {
@@ -254,7 +254,7 @@ __device__ __forceinline__ void mma_tile(f32x4 (&acc)[kFragM][kFragN], const u32
 // from moving LDS accesses across either.
 __device__ __forceinline__ void stage_barrier() {
   static_assert(2 * (2 * kDmaSlots) == 8, "the vmcnt literal assumes two k-tiles of 2 x kDmaSlots loads");
-  asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 __device__ __forceinline__ void drain_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
