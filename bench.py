@@ -12,7 +12,9 @@ N2 = 28672 (gate||up of F = 14336), bf16 storage, fp32 accumulation.
 Prints ONE JSON line: whole-job TFLOP/s (algorithmic GEMM flops
 2MKD + 2MDN2 per step), the roofline of the dominant kernel (the second GEMM)
 timed with HIP events on the launch stream, the unfused reference chain for
-A/B comparison, and the fp64 CPU oracle timed on a bounded row sample.
+A/B comparison, the same chain in plain PyTorch (torch.matmul, i.e. the
+vendor GEMM library, plus torch elementwise and reduction ops) for context,
+and the fp64 CPU oracle timed on a bounded row sample.
 """
 from __future__ import annotations
 
@@ -44,6 +46,8 @@ def parse():
                     help="approximate CPU work budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ref-chain", action="store_true")
+    ap.add_argument("--no-torch-chain", action="store_true",
+                    help="skip timing the same chain in plain PyTorch (vendor GEMMs + torch elementwise ops)")
     return ap.parse_args()
 
 
@@ -215,6 +219,32 @@ def main():
                                                                else Hr, H.view(torch.int16)
                                                                if tdt == torch.bfloat16 else H))
         del ws, Hr, rr, Yr
+
+    if not args.no_torch_chain:
+        # the unfused library path: vendor GEMMs with torch's RMSNorm in between
+        # (context only; nothing in the fused path calls torch compute)
+        gf = d["g"].float()
+
+        def torch_chain():
+            Ht = torch.addmm(d["R"], d["A"], d["W1"])
+            hf = Ht.float()
+            rt = torch.rsqrt(hf.square().mean(dim=1, keepdim=True) + wl.eps)
+            return torch.matmul((hf * rt * gf).to(tdt), d["W2"])
+
+        for _ in range(max(2, args.warmup // 2)):
+            torch_chain()
+        nt = max(5, args.steps // 2)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(nt):
+            torch_chain()
+        b.record(stream)
+        torch.cuda.synchronize()
+        t_ms = a.elapsed_time(b) / nt
+        out["torch_chain_ms"] = round(t_ms, 4)
+        out["speedup_vs_torch_chain"] = round(t_ms / ms_step, 4)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)

@@ -178,7 +178,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // registers (four stages x eight fragments would not fit).
 __device__ __forceinline__ void opaque(int& v) { asm volatile("" : "+v"(v)); }
 
-template <typename T, bool KC, int NF>
+template <typename T, bool KC>
 struct FragReader {
   int off0;  // lane's byte offset of fragment 0 in the operand tile (RC bf16: h = 0 base)
   int base, lane;
@@ -186,31 +186,26 @@ struct FragReader {
     off0 = KC ? kc_offset(base_ + (lane_ & 15), lane_ >> 4)
               : (sizeof(T) == 2 ? rc_tr_lane_base(base_, 0, lane_) : 0);
   }
-  __device__ __forceinline__ void read(const char* tile, u32x4 (&f)[NF]) {
-    opaque(off0);
+  __device__ __forceinline__ void refresh() { opaque(off0); }
+  // fragment t (compile-time after unrolling) of the operand tile at `tile`
+  __device__ __forceinline__ u32x4 read(const char* tile, int t) const {
     if constexpr (KC) {
       // the swizzle depends on row % 16 only: fragment t lies 16 rows (1 KiB) further
-      const char* p = tile + off0;
-#pragma unroll
-      for (int t = 0; t < NF; ++t) f[t] = *(const u32x4*)(p + t * 1024);
+      return *(const u32x4*)(tile + off0 + t * 1024);
     } else if constexpr (sizeof(T) == 2) {
       // fragment t at lane base ^ 32 t; h = 1 is 4 contraction rows (2 KiB)
       // further.  The address stays a pointer into the stage array: with an
       // integer-made address the compiler cannot tell which direct loads the
       // read depends on and waits for all of them.
-      const lds_char* p = (const lds_char*)tile;
-#pragma unroll
-      for (int t = 0; t < NF; ++t) {
-        const lds_char* q = p + (off0 ^ (32 * t));
-        const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)q));
-        const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(q + 2048)));
-        f[t] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-      }
+      const lds_char* q = (const lds_char*)tile + (off0 ^ (32 * t));
+      const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)q));
+      const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(q + 2048)));
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
     } else {
+      u32x4 f;
 #pragma unroll
-      for (int t = 0; t < NF; ++t)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) f[t][u] = *(const uint32_t*)(tile + rc_f32_offset(base, t, u, lane));
+      for (int u = 0; u < 4; ++u) f[u] = *(const uint32_t*)(tile + rc_f32_offset(base, t, u, lane));
+      return f;
     }
   }
 };
@@ -236,28 +231,26 @@ struct Mma<float> {
   }
 };
 
-template <typename T>
-__device__ __forceinline__ void mma_tile(f32x4 (&acc)[kFragM][kFragN], const u32x4 (&fa)[kFragM],
-                                         const u32x4 (&fb)[kFragN]) {
-#pragma unroll
-  for (int mt = 0; mt < kFragM; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < kFragN; ++nt) Mma<T>::mac(acc[mt][nt], fa[mt], fb[nt]);
-}
-
 // Workgroup barriers of the pipeline.  stage_barrier waits until at most two
 // k-tiles of this wavefront's direct loads (kDmaSlots per operand each) are
-// still in flight and its LDS reads are done, then meets the other
-// wavefronts: after it, every wavefront's loads of all older k-tiles have
-// landed.
-// drain_barrier waits for everything.  The memory clobber keeps the compiler
-// from moving LDS accesses across either.
+// still in flight, then meets the other wavefronts: after it, every
+// wavefront's loads of all older k-tiles have landed.  LDS reads may stay in
+// flight across it (their stage is not overwritten before the step that
+// uses them).  The scheduling fence keeps the compiler from moving any
+// instruction across, so every product of a step, and the wait for the
+// fragment reads it uses, comes before that step's barrier.
+// drain_barrier waits for everything.
+constexpr int kLoadsPerTile = 2 * kDmaSlots;  // direct loads per wavefront per k-tile
 __device__ __forceinline__ void stage_barrier() {
-  static_assert(2 * (2 * kDmaSlots) == 8, "the vmcnt literal assumes two k-tiles of 2 x kDmaSlots loads");
-  asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  static_assert(2 * kLoadsPerTile == 8, "the vmcnt literal assumes two k-tiles of 2 x kDmaSlots loads");
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 __device__ __forceinline__ void drain_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 struct GemmArgs {
@@ -271,25 +264,48 @@ struct GemmArgs {
   uint32_t b_span;
 };
 
-// One step of the k-pipeline for k-tile kt held in stage S:
-//   issue the direct loads of tile kt+3 into stage (S+3) % 4,
-//   read the fragments of tile kt from stage S and run its 64 products,
-//   stage_barrier: this wavefront's loads of tile kt+1 have landed (only
-//   tiles kt+2 and kt+3 may still be in flight) and its reads of stage S
-//   are done; after the barrier that holds for every wavefront.
-// Stage (S+3) % 4 held tile kt-1, read in step kt-1 before its barrier, so
-// it is free.  Tiles past the end of K load as zeros, so steps need no guards.
+// Fragments of one k-tile held in registers.
+struct Frags {
+  u32x4 a[kFragM], b[kFragN];
+};
+
+// One step of the k-pipeline, k-tile kt held in stage S = kt % kStages, its
+// fragments already in `cur`:
+//   issue the direct loads of tile kt + kStages - 1 into stage (S - 1) mod
+//   kStages, which held tile kt - 1 (read in step kt - 2, used before the
+//   barrier of step kt - 1);
+//   read tile kt + 1's B fragments from stage S + 1 into a second set;
+//   for each A fragment mt: run its 4 products of tile kt, then read tile
+//   kt + 1's fragment mt into the same registers, so each read has about a
+//   whole step to land before its products in the next step;
+//   stage_barrier: at most tiles kt + 3 and kt + 4 are still in flight, so
+//   tile kt + 2, which the next step reads, has landed everywhere.
+// The scheduling fences pin this order (left alone, the scheduler sinks the
+// reads behind the products).  Tiles past the end of K load as zeros; their
+// fragments are read but never multiplied.
 template <typename T, bool A_KC, bool B_KC, int S>
 __device__ __forceinline__ void kstep(char* const (&st)[kStages], const Dma<T, A_KC>& da, const Dma<T, B_KC>& db,
-                                      FragReader<T, A_KC, kFragM>& ra, FragReader<T, B_KC, kFragN>& rb,
-                                      f32x4 (&acc)[kFragM][kFragN], int kt, int K, int wave) {
-  constexpr int SL = (S + 3) % kStages;
-  da.issue(st[SL], kt + 3, K, wave);
-  db.issue(st[SL] + kOperandBytes, kt + 3, K, wave);
-  u32x4 fa[kFragM], fb[kFragN];
-  ra.read(st[S], fa);
-  rb.read(st[S] + kOperandBytes, fb);
-  mma_tile<T>(acc, fa, fb);
+                                      FragReader<T, A_KC>& ra, FragReader<T, B_KC>& rb,
+                                      f32x4 (&acc)[kFragM][kFragN], Frags& cur, int kt, int K, int wave) {
+  constexpr int SL = (S + kStages - 1) % kStages;
+  constexpr int SN = (S + 1) % kStages;
+  da.issue(st[SL], kt + kStages - 1, K, wave);
+  db.issue(st[SL] + kOperandBytes, kt + kStages - 1, K, wave);
+  ra.refresh();
+  rb.refresh();
+  u32x4 nb[kFragN];
+#pragma unroll
+  for (int nt = 0; nt < kFragN; ++nt) nb[nt] = rb.read(st[SN] + kOperandBytes, nt);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int mt = 0; mt < kFragM; ++mt) {
+#pragma unroll
+    for (int nt = 0; nt < kFragN; ++nt) Mma<T>::mac(acc[mt][nt], cur.a[mt], cur.b[nt]);
+    cur.a[mt] = ra.read(st[SN], mt);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int nt = 0; nt < kFragN; ++nt) cur.b[nt] = nb[nt];
   stage_barrier();
 }
 
@@ -302,11 +318,13 @@ __device__ __forceinline__ void kstep(char* const (&st)[kStages], const Dma<T, A
 template <typename T, bool A_KC, bool B_KC, class Epi>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(
     GemmArgs g, typename Epi::Params ep) {
+  static_assert(kStages == 5, "the stage arrays and the unrolled steps below assume five stages");
   __shared__ __attribute__((aligned(1024))) char st0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char st1[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char st2[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char st3[kStageBytes];
-  char* const st[kStages] = {st0, st1, st2, st3};
+  __shared__ __attribute__((aligned(1024))) char st4[kStageBytes];
+  char* const st[kStages] = {st0, st1, st2, st3, st4};
   constexpr int KTE = kKTBytes / (int)sizeof(T);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -319,8 +337,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   Dma<T, B_KC> db;
   da.init(g.a, g.a_span, g.lda, m0, g.M, wave, lane);
   db.init(g.b, g.b_span, g.ldb, n0, g.N, wave, lane);
-  FragReader<T, A_KC, kFragM> ra(wm * kWaveM, lane);
-  FragReader<T, B_KC, kFragN> rb(wn * kWaveN, lane);
+  FragReader<T, A_KC> ra(wm * kWaveM, lane);
+  FragReader<T, B_KC> rb(wn * kWaveN, lane);
   f32x4 acc[kFragM][kFragN];
 #pragma unroll
   for (int i = 0; i < kFragM; ++i)
@@ -328,20 +346,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int j = 0; j < kFragN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = (g.K + KTE - 1) / KTE;
+  // prologue: tiles 0 .. kStages - 2 in flight, wait for tiles 0 and 1
 #pragma unroll
-  for (int t = 0; t < 3; ++t) {
+  for (int t = 0; t < kStages - 1; ++t) {
     da.issue(st[t], t, g.K, wave);
     db.issue(st[t] + kOperandBytes, t, g.K, wave);
   }
-  asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");  // tile 0 landed everywhere
-  // whole groups of four k-steps: a ragged end runs up to three all-zero
-  // tiles (harmless products of zeros) and keeps the loop body uniform
-  for (int kt = 0; kt < nk; kt += kStages) {
-    kstep<T, A_KC, B_KC, 0>(st, da, db, ra, rb, acc, kt, g.K, wave);
-    kstep<T, A_KC, B_KC, 1>(st, da, db, ra, rb, acc, kt + 1, g.K, wave);
-    kstep<T, A_KC, B_KC, 2>(st, da, db, ra, rb, acc, kt + 2, g.K, wave);
-    kstep<T, A_KC, B_KC, 3>(st, da, db, ra, rb, acc, kt + 3, g.K, wave);
+  static_assert((kStages - 3) * kLoadsPerTile == 8, "the prologue vmcnt literal assumes kStages - 3 tiles in flight");
+  asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  Frags cur;
+#pragma unroll
+  for (int mt = 0; mt < kFragM; ++mt) cur.a[mt] = ra.read(st[0], mt);
+#pragma unroll
+  for (int nt = 0; nt < kFragN; ++nt) cur.b[nt] = rb.read(st[0] + kOperandBytes, nt);
+  int kt = 0;
+  for (; kt + kStages <= nk; kt += kStages) {
+    kstep<T, A_KC, B_KC, 0>(st, da, db, ra, rb, acc, cur, kt, g.K, wave);
+    kstep<T, A_KC, B_KC, 1>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave);
+    kstep<T, A_KC, B_KC, 2>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave);
+    kstep<T, A_KC, B_KC, 3>(st, da, db, ra, rb, acc, cur, kt + 3, g.K, wave);
+    kstep<T, A_KC, B_KC, 4>(st, da, db, ra, rb, acc, cur, kt + 4, g.K, wave);
   }
+  // ragged end: the remaining nk - kt < kStages tiles start again at stage 0
+  const int rem = nk - kt;
+  if (rem > 0) kstep<T, A_KC, B_KC, 0>(st, da, db, ra, rb, acc, cur, kt, g.K, wave);
+  if (rem > 1) kstep<T, A_KC, B_KC, 1>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave);
+  if (rem > 2) kstep<T, A_KC, B_KC, 2>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave);
+  if (rem > 3) kstep<T, A_KC, B_KC, 3>(st, da, db, ra, rb, acc, cur, kt + 3, g.K, wave);
   drain_barrier();  // no direct load may land in the LDS the epilogue reuses
 
   // ---- epilogue ----
