@@ -46,6 +46,9 @@ def parse():
                     help="approximate CPU work budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ref-chain", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before the warm-up, copy this many MiB device to device twice (a transfer of known "
+                         "size that calibrates HBM byte counters in a profiler run)")
     ap.add_argument("--no-torch-chain", action="store_true",
                     help="skip timing the same chain in plain PyTorch (vendor GEMMs + torch elementwise ops)")
     return ap.parse_args()
@@ -137,6 +140,14 @@ def main():
         coda.coda_gemm_rowscale(Hg, d["W2"], r, Y, stream)
         if ev is not None:
             ev[2].record(stream)
+
+    if args.copy_probe_mib > 0:
+        src = torch.ones((args.copy_probe_mib << 20,), device=dev, dtype=torch.uint8)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()
