@@ -29,7 +29,7 @@
  *     returned, nothing is enqueued, and coda_last_error() describes it.
  *     CODA_ERR_HIP means a launch failed (hipGetLastError reported it).
  *   - Requirements (CODA_ERR_SHAPE / CODA_ERR_ALIGN otherwise): M >= 0 (M = 0
- *     is a no-op); K, D, N2 >= 1 and multiples of 8 (bf16) or 4 (f32);
+ *     is a no-op, except where stated); K, D, N2 >= 1 and multiples of 8;
  *     ld >= row width and a multiple of 8 (bf16) or 4 (f32) elements; base
  *     pointers 16-byte aligned; each matrix spans less than 2 GiB.
  *   - Outputs must not overlap inputs (CODA_ERR_ALIAS), except where stated.
@@ -116,6 +116,49 @@ coda_status coda_ref_chain(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64
                            const void* A, const void* W1, const void* R,
                            const void* g, const void* W2,
                            void* H, float* r, void* Y,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* ---- backward ------------------------------------------------------------
+ * Gradients of a scalar loss L through the chain, given dY = dL/dY.  The
+ * article (section "CODA：「尾声」里藏着宝藏") notes that the backward pass
+ * keeps the tile-local structure of the forward; written out with
+ * G = dY W2^T, P = G diag(g) and s_i = <P_i, H_i>:
+ *
+ *     dW2 = X_n^T dY,        X_n = diag(r) H diag(g)
+ *     dg_j = sum_i r_i H_ij G_ij
+ *     dH_i = r_i P_i - (r_i^3 s_i / D) H_i        (through X_n and through r)
+ *     dR = dH,   dA = dH W1^T,   dW1 = A^T dH
+ *
+ * Only s and dg need reductions across tiles.  Six kernels, in stream order:
+ *   1. GEMM G = dY W2^T; epilogue: P = round(g_j G_ij) into dR, X_n =
+ *      round((float(H_ij) r_i) g_j) into the workspace, per-row partial sums
+ *      of P_ij H_ij per 64 columns (unrounded P), per-column partial sums of
+ *      r_i H_ij G_ij per 128 rows;
+ *   2. combine: c_i = r_i^3 (sum of the row partials) / D, dg_j = sum of the
+ *      column partials (both in fixed order);
+ *   3. dH = round(r_i float(P_ij) - c_i float(H_ij)), in place in dR;
+ *   4. dA = round(dH W1^T);  5. dW1 = round(A^T dH);  6. dW2 = round(X_n^T dY).
+ * H and r are the forward's stored values (coda_gemm_res_prms, coda_rms_combine).
+ * All float32 accumulation.  With M = 0, dW1, dW2 and dg are written as zeros
+ * and the M-row arguments (dY, A, H, r, dA, dR) may be NULL. */
+
+/* Bytes of workspace coda_chain_bwd needs: X_n[M,D] (dtype), row partials
+ * float[T*M] (T = coda_prms_num_partials(dt, D)), column partials
+ * float[ceil(M/128)*D] and c float[M], each part 256-byte aligned; at least
+ * 256 bytes.  0 for invalid arguments. */
+size_t coda_chain_bwd_workspace_bytes(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64_t N2);
+
+/* Backward of the chain.  All matrices dense (ld = width).
+ *   dY[M,N2], A[M,K], W1[K,D], g[D], W2[D,N2], H[M,D] (dtype); r[M] float
+ *   dA[M,K], dR[M,D] (= dH; also the operand of dA and dW1), dW1[K,D],
+ *   dW2[D,N2] (dtype); dg[D] float
+ * ws: device memory of coda_chain_bwd_workspace_bytes(), 256-byte aligned,
+ * overwritten.  Outputs and workspace must not overlap any input or each
+ * other.  Errors as in the forward calls. */
+coda_status coda_chain_bwd(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64_t N2,
+                           const void* dY, const void* A, const void* W1, const void* g,
+                           const void* W2, const void* H, const float* r,
+                           void* dA, void* dR, void* dW1, void* dW2, float* dg,
                            void* ws, size_t ws_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */

@@ -19,7 +19,8 @@ from transformer_gemm_epilogue_gemm1_amd import _lib  # noqa: E402
 OK, NULL, SHAPE, ALIGN, DTYPE, ALIAS, WS, HIP = range(8)
 BF16, F32 = 0, 1
 P = 0x7F0000000000  # fake device addresses, far apart
-A_, W1_, R_, G_, H_, HG_, PART_, W2_, Y_, R2_, WS_ = (P + i * (1 << 36) for i in range(11))
+A_, W1_, R_, G_, H_, HG_, PART_, W2_, Y_, R2_, WS_, DY_, DA_, DR_, DW1_, DW2_, DG_ = (
+    P + i * (1 << 36) for i in range(17))
 
 
 def declared_functions():
@@ -157,6 +158,83 @@ def test_ref_chain_validation(lib):
     assert call(Y=A_) == ALIAS
     assert call(ws=H_ - 1024 * 256) == ALIAS  # workspace overlapping H
     assert call(M=0, A=None) == OK
+
+
+def test_chain_bwd_workspace_bytes(lib):
+    def al(x):
+        return (x + 255) // 256 * 256
+    # X_n [M, D] (dtype), row partials [T, M], column partials [ceil(M/128), D], c [M]
+    M, D = 16384, 4096
+    xn = al(M * D * 2)
+    srow = al(xn + 64 * M * 4)
+    dgcol = al(srow + (M // 128) * D * 4)
+    assert lib.coda_chain_bwd_workspace_bytes(BF16, M, 4096, D, 28672) == al(dgcol + M * 4)
+    M, D = 300, 264   # ragged: T = 8, U = 3
+    xn = al(M * D * 4)
+    srow = al(xn + 8 * M * 4)
+    dgcol = al(srow + 3 * D * 4)
+    assert lib.coda_chain_bwd_workspace_bytes(F32, M, 8, D, 16) == al(dgcol + M * 4)
+    assert lib.coda_chain_bwd_workspace_bytes(7, 16, 8, 8, 8) == 0
+    assert lib.coda_chain_bwd_workspace_bytes(BF16, -1, 8, 8, 8) == 0
+    assert lib.coda_chain_bwd_workspace_bytes(BF16, 16, 0, 8, 8) == 0
+
+
+def chain_bwd(lib, ws=WS_, ws_bytes=None, **kw):
+    a = dict(dt=BF16, M=512, K=256, D=256, N2=512, dY=DY_, A=A_, W1=W1_, g=G_, W2=W2_, H=H_, r=R2_, dA=DA_,
+             dR=DR_, dW1=DW1_, dW2=DW2_, dg=DG_)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = lib.coda_chain_bwd_workspace_bytes(a["dt"] if a["dt"] in (0, 1) else 0, max(a["M"], 0),
+                                                      max(a["K"], 1), max(a["D"], 1), max(a["N2"], 1))
+    return lib.coda_chain_bwd(a["dt"], a["M"], a["K"], a["D"], a["N2"], a["dY"], a["A"], a["W1"], a["g"],
+                              a["W2"], a["H"], a["r"], a["dA"], a["dR"], a["dW1"], a["dW2"], a["dg"], ws,
+                              ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=2), DTYPE),
+    (dict(M=-3), SHAPE),
+    (dict(K=12), SHAPE),
+    (dict(D=0), SHAPE),
+    (dict(N2=100), SHAPE),
+    (dict(dY=None), NULL),
+    (dict(A=None), NULL),
+    (dict(W1=None), NULL),
+    (dict(g=None), NULL),
+    (dict(W2=None), NULL),
+    (dict(H=None), NULL),
+    (dict(r=None), NULL),
+    (dict(dA=None), NULL),
+    (dict(dR=None), NULL),
+    (dict(dW1=None), NULL),
+    (dict(dW2=None), NULL),
+    (dict(dg=None), NULL),
+    (dict(ws=None), WS),
+    (dict(ws_bytes=1024), WS),
+    (dict(ws=WS_ + 128), ALIGN),
+    (dict(dY=DY_ + 8), ALIGN),
+    (dict(r=R2_ + 1), ALIGN),
+    (dict(dg=DG_ + 2), ALIGN),
+    (dict(dR=H_), ALIAS),            # dH may not overwrite the stored H
+    (dict(dA=A_ + 512), ALIAS),
+    (dict(dW2=W2_), ALIAS),
+    (dict(dg=R2_), ALIAS),
+    (dict(dW1=DR_ + 4096), ALIAS),   # two outputs overlapping
+    (dict(ws=DY_), ALIAS),           # workspace overlapping an input
+    (dict(ws=DW2_ - 256), ALIAS),    # workspace overlapping an output
+    (dict(M=16384, N2=65536), SHAPE),  # dY spans more than 2 GiB
+])
+def test_chain_bwd_rejects(lib, kw, status):
+    assert chain_bwd(lib, **kw) == status
+    assert lib.coda_last_error().decode() != ""
+
+
+def test_chain_bwd_empty_still_checks_weights(lib):
+    # with M = 0 the M-row arguments may be NULL, the weight gradients may not
+    none = dict(dY=None, A=None, H=None, r=None, dA=None, dR=None)
+    assert chain_bwd(lib, M=0, dW1=None, **none) == NULL
+    assert chain_bwd(lib, M=0, dg=None, **none) == NULL
+    assert chain_bwd(lib, M=0, dW2=W2_, **none) == ALIAS
 
 
 def test_index_maps_host_check(tmp_path):

@@ -1,4 +1,4 @@
-"""libcoda: the fused GEMM-Residual-PartialRMS-GEMM chain on AMD MI355X (gfx950).
+"""libcoda: the fused GEMM-Residual-PartialRMS-GEMM chain and its backward on AMD MI355X (gfx950).
 
 The HIP kernels and the C ABI live in csrc/ and include/coda.h; this package
 is a thin binding over libcoda.so.  Importing it loads the library and fails
@@ -6,8 +6,9 @@ if it has not been built.
 """
 from . import _lib
 from ._lib import CodaError
-from .binding import (coda_gemm_res_prms, coda_gemm_rowscale, coda_prms_num_partials,  # noqa: F401
-                      coda_ref_chain, coda_ref_chain_workspace_bytes, coda_rms_combine, fused_forward,
+from .binding import (coda_chain_bwd, coda_chain_bwd_workspace_bytes, coda_gemm_res_prms,  # noqa: F401
+                      coda_gemm_rowscale, coda_prms_num_partials, coda_ref_chain,
+                      coda_ref_chain_workspace_bytes, coda_rms_combine, fused_backward, fused_forward,
                       ref_chain)
 
 _lib.load()

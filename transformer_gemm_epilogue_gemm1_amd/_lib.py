@@ -34,7 +34,7 @@ SIGNATURES = {
     "coda_ref_chain": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64, c_float, c_vp, c_vp, c_vp, c_vp,
                                c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "coda_chain_bwd_workspace_bytes": (c_size, [c_int, c_i64, c_i64, c_i64, c_i64]),
-    "coda_chain_bwd": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64, c_float,
+    "coda_chain_bwd": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64,
                                c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "coda_status_string": (ctypes.c_char_p, [c_int]),

@@ -133,6 +133,34 @@ def coda_ref_chain(A, W1, R, g, W2, H, r, Y, ws, eps: float, stream=None) -> Non
     _lib.check("coda_ref_chain", st)
 
 
+def coda_chain_bwd_workspace_bytes(dtype: torch.dtype, M: int, K: int, D: int, N2: int) -> int:
+    return int(_lib.load().coda_chain_bwd_workspace_bytes(_DT[dtype], M, K, D, N2))
+
+
+def coda_chain_bwd(dY, A, W1, g, W2, H, r, dA, dR, dW1, dW2, dg, ws, stream=None) -> None:
+    """Backward of the chain: dA, dR (= dH), dW1, dW2, dg from dY and the
+    forward's stored H and r (all dense tensors; see coda.h)."""
+    lib = _lib.load()
+    dt = A.dtype
+    M, K = A.shape
+    D = W1.shape[1]
+    N2 = W2.shape[1]
+    for t, n, dtp, shp in ((dY, "dY", dt, (M, N2)), (A, "A", dt, (M, K)), (W1, "W1", dt, (K, D)),
+                           (g, "g", dt, (D,)), (W2, "W2", dt, (D, N2)), (H, "H", dt, (M, D)),
+                           (r, "r", torch.float32, (M,)), (dA, "dA", dt, (M, K)), (dR, "dR", dt, (M, D)),
+                           (dW1, "dW1", dt, (K, D)), (dW2, "dW2", dt, (D, N2)),
+                           (dg, "dg", torch.float32, (D,))):
+        _mat(t, n, dtp, shp)
+        _dense(t, n)
+    if ws.device.type != "cuda":
+        raise ValueError("workspace must be on a HIP device")
+    st = lib.coda_chain_bwd(_dtype_code(A), M, K, D, N2, dY.data_ptr(), A.data_ptr(), W1.data_ptr(),
+                            g.data_ptr(), W2.data_ptr(), H.data_ptr(), r.data_ptr(), dA.data_ptr(),
+                            dR.data_ptr(), dW1.data_ptr(), dW2.data_ptr(), dg.data_ptr(), ws.data_ptr(),
+                            ws.numel() * ws.element_size(), _stream(stream))
+    _lib.check("coda_chain_bwd", st)
+
+
 # ---- conveniences that allocate outputs with torch, then call the above ----
 
 def fused_forward(A, W1, R, g, W2, eps: float, stream=None):
@@ -160,3 +188,18 @@ def ref_chain(A, W1, R, g, W2, eps: float, stream=None):
     ws = torch.empty((coda_ref_chain_workspace_bytes(dt, M, D),), device=dev, dtype=torch.uint8)
     coda_ref_chain(A, W1, R, g, W2, H, r, Y, ws, eps, stream)
     return H, r, Y
+
+
+def fused_backward(dY, A, W1, g, W2, H, r, stream=None):
+    """Backward of the chain, returns (dA, dR, dW1, dW2, dg); dR = dH."""
+    M, K = A.shape
+    D, N2 = W1.shape[1], W2.shape[1]
+    dev, dt = A.device, A.dtype
+    dA = torch.empty((M, K), device=dev, dtype=dt)
+    dR = torch.empty((M, D), device=dev, dtype=dt)
+    dW1 = torch.empty((K, D), device=dev, dtype=dt)
+    dW2 = torch.empty((D, N2), device=dev, dtype=dt)
+    dg = torch.empty((D,), device=dev, dtype=torch.float32)
+    ws = torch.empty((coda_chain_bwd_workspace_bytes(dt, M, K, D, N2),), device=dev, dtype=torch.uint8)
+    coda_chain_bwd(dY, A, W1, g, W2, H, r, dA, dR, dW1, dW2, dg, ws, stream)
+    return dA, dR, dW1, dW2, dg

@@ -143,6 +143,73 @@ coda_status combine_impl(int M, int D, int T, float eps, const float* partials, 
   return launch_status("coda_rms_combine");
 }
 
+// ---- backward ------------------------------------------------------------
+constexpr size_t kWsAlign = 256;
+size_t align_up(size_t x) { return (x + kWsAlign - 1) & ~(kWsAlign - 1); }
+
+// Workspace parts of the backward, in this order, each 256-byte aligned.
+struct BwdWs {
+  size_t xn, srow, dgcol, c, total;
+  BwdWs(int64_t M, int64_t D, int es) {
+    const int64_t T = num_partials(D), U = (M + kWaveM - 1) / kWaveM;
+    xn = 0;
+    srow = align_up(xn + (size_t)M * D * es);
+    dgcol = align_up(srow + (size_t)T * M * 4);
+    c = align_up(dgcol + (size_t)U * D * 4);
+    total = align_up(c + (size_t)M * 4);
+    if (total < kWsAlign) total = kWsAlign;  // never empty: a zero-byte workspace would come as NULL
+  }
+};
+
+template <typename T>
+coda_status chain_bwd_impl(int M, int K, int D, int N2, const void* dY, const void* A, const void* W1,
+                           const void* g, const void* W2, const void* H, const float* r, void* dA, void* dR,
+                           void* dW1, void* dW2, float* dg, char* ws, hipStream_t s) {
+  const BwdWs L(M, D, sizeof(T));
+  T* Xn = (T*)(ws + L.xn);
+  float* srow = (float*)(ws + L.srow);
+  float* dgcol = (float*)(ws + L.dgcol);
+  float* c = (float*)(ws + L.c);
+  const int Tn = (int)num_partials(D), U = (M + kWaveM - 1) / kWaveM;
+  coda_status st;
+  if (M > 0) {
+    // 1. G = dY W2^T with the P / X_n / partial-sum epilogue
+    typename EpiBwdG<T>::Params ep{(const T*)H, (const T*)g, r, (T*)dR, Xn, D, srow, dgcol};
+    if ((st = launch_gemm<T, true, true, EpiBwdG<T>>("coda_chain_bwd G", M, D, N2, dY, N2, W2, N2, ep, s)) !=
+        CODA_OK)
+      return st;
+  }
+  // 2. c and dg (with M = 0 only the columns: dg = 0)
+  hipLaunchKernelGGL(bwd_combine_kernel, dim3((unsigned)((M + (int64_t)D + 255) / 256)), dim3(256), 0, s, srow,
+                     dgcol, r, c, dg, M, Tn, D, U);
+  if ((st = launch_status("coda_chain_bwd combine")) != CODA_OK) return st;
+  if (M > 0) {
+    // 3. dH in place in dR
+    const int64_t nchunks = (int64_t)M * D / 8;
+    const int blocks = (int)((nchunks + 255) / 256 < 16384 ? (nchunks + 255) / 256 : 16384);
+    hipLaunchKernelGGL(dh_finalize_kernel<T>, dim3(blocks), dim3(256), 0, s, (T*)dR, (const T*)H, r, c, D, nchunks);
+    if ((st = launch_status("coda_chain_bwd dH")) != CODA_OK) return st;
+    // 4. dA = dH W1^T  (W1[K, D] read as the contraction-contiguous operand)
+    if ((st = launch_gemm<T, true, true, EpiRowScale<T>>("coda_chain_bwd dA", M, K, D, dR, D, W1, D,
+                                                         typename EpiRowScale<T>::Params{nullptr, (T*)dA, K}, s)) !=
+        CODA_OK)
+      return st;
+  }
+  // 5. dW1 = A^T dH  and  6. dW2 = X_n^T dY: contraction over the M rows.
+  // With M = 0 the main loop runs no k-tile and writes zeros; the M-row
+  // operands (possibly NULL then) are replaced by W1 with an empty span, so
+  // no load is ever made from them.
+  const void* a5 = M > 0 ? A : W1;
+  const void* b5 = M > 0 ? (const void*)dR : W1;
+  const void* b6 = M > 0 ? dY : W1;
+  if ((st = launch_gemm<T, false, false, EpiRowScale<T>>("coda_chain_bwd dW1", K, D, M, a5, K, b5, D,
+                                                         typename EpiRowScale<T>::Params{nullptr, (T*)dW1, D}, s)) !=
+      CODA_OK)
+    return st;
+  return launch_gemm<T, false, false, EpiRowScale<T>>("coda_chain_bwd dW2", D, N2, M, Xn, D, b6, N2,
+                                                      typename EpiRowScale<T>::Params{nullptr, (T*)dW2, N2}, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -279,6 +346,54 @@ coda_status coda_ref_chain(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64
     if ((st = launch_status("coda_ref_chain rmsnorm")) != CODA_OK) return st;
     return gemm_rowscale_impl<T>((int)M, (int)D, (int)N2, Xn, D, W2, N2, nullptr, Y, N2, s);
   }
+}
+
+size_t coda_chain_bwd_workspace_bytes(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64_t N2) {
+  if (dt != CODA_BF16 && dt != CODA_F32) return 0;
+  if (M < 0 || M > kMaxDim || K < 1 || K > kMaxDim || D < 1 || D > kMaxDim || N2 < 1 || N2 > kMaxDim) return 0;
+  return BwdWs(M, D, elem_size(dt)).total;
+}
+
+coda_status coda_chain_bwd(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64_t N2, const void* dY,
+                           const void* A, const void* W1, const void* g, const void* W2, const void* H,
+                           const float* r, void* dA, void* dR, void* dW1, void* dW2, float* dg, void* ws,
+                           size_t ws_bytes, void* stream) {
+  coda_status st = check_dims(dt, M, {{"K", K}, {"D", D}, {"N2", N2}});
+  if (st != CODA_OK) return st;
+  const int es = elem_size(dt), E = elems_per_chunk(dt);
+  // matrices with M rows are checked only when M > 0 (they may be NULL then)
+  const Mat mdY{dY, M, N2, N2, es, "dY"}, mA{A, M, K, K, es, "A"}, mH{H, M, D, D, es, "H"};
+  const Mat mdA{dA, M, K, K, es, "dA"}, mdR{dR, M, D, D, es, "dR"};
+  const Mat mW1{W1, K, D, D, es, "W1"}, mg{g, 1, D, D, es, "g"}, mW2{W2, D, N2, N2, es, "W2"};
+  const Mat mdW1{dW1, K, D, D, es, "dW1"}, mdW2{dW2, D, N2, N2, es, "dW2"};
+  const Mat mr{r, 1, M, M, 4, "r"}, mdg{dg, 1, D, D, 4, "dg"};
+  for (const Mat* m : {&mW1, &mg, &mW2, &mdW1, &mdW2})
+    if ((st = check_mat(*m, E)) != CODA_OK) return st;
+  if (M > 0) {
+    for (const Mat* m : {&mdY, &mA, &mH, &mdA, &mdR})
+      if ((st = check_mat(*m, E)) != CODA_OK) return st;
+    if (r == nullptr) return fail(CODA_ERR_NULL, "r is NULL");
+    if (((uintptr_t)r & 3) != 0) return fail(CODA_ERR_ALIGN, "r is not 4-byte aligned");
+  }
+  if (dg == nullptr) return fail(CODA_ERR_NULL, "dg is NULL");
+  if (((uintptr_t)dg & 3) != 0) return fail(CODA_ERR_ALIGN, "dg is not 4-byte aligned");
+  const BwdWs L(M, D, es);
+  if (ws == nullptr || ws_bytes < L.total)
+    return fail(CODA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, ws ? ws_bytes : (size_t)0);
+  if (((uintptr_t)ws & (kWsAlign - 1)) != 0) return fail(CODA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const Mat mws{ws, 1, (int64_t)L.total, (int64_t)L.total, 1, "workspace"};
+  const Mat mXn{(char*)ws + L.xn, M, D, D, es, "workspace X_n"};
+  if (mXn.span() > kMaxSpan) return fail(CODA_ERR_SHAPE, "workspace X_n spans more than 2 GiB");
+  const Mat none{nullptr, 0, 0, 0, es, ""};
+  const Mat outs[6] = {M > 0 ? mdA : none, M > 0 ? mdR : none, mdW1, mdW2, mdg, mws};
+  const Mat ins[7] = {M > 0 ? mdY : none, M > 0 ? mA : none, mW1, mg, mW2, M > 0 ? mH : none, M > 0 ? mr : none};
+  if ((st = check_alias(outs, 6, ins, 7)) != CODA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == CODA_BF16)
+    return chain_bwd_impl<uint16_t>((int)M, (int)K, (int)D, (int)N2, dY, A, W1, g, W2, H, r, dA, dR, dW1, dW2, dg,
+                                    (char*)ws, s);
+  return chain_bwd_impl<float>((int)M, (int)K, (int)D, (int)N2, dY, A, W1, g, W2, H, r, dA, dR, dW1, dW2, dg,
+                               (char*)ws, s);
 }
 
 const char* coda_status_string(coda_status s) {

@@ -315,6 +315,7 @@ __device__ __forceinline__ void kstep(char* const (&st)[kStages], const Dma<T, A
 // [8*(l%8), 8*(l%8)+8) of the wavefront's 64.  Epi provides
 //   apply(q, row, col, v[8])   for rows < M and columns < N (col % 8 == 0)
 //   end_slab(slab_row0)        after all lanes applied one 16-row slab
+//   finish()                   on every lane after the last slab
 template <typename T, bool A_KC, bool B_KC, class Epi>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(
     GemmArgs g, typename Epi::Params ep) {
@@ -400,6 +401,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     epi.end_slab(row_base + mt * 16);
     __syncthreads();
   }
+  epi.finish();
 }
 
 }  // namespace coda

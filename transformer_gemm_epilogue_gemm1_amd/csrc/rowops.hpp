@@ -1,5 +1,6 @@
-// Small row-wise kernels: the combine of the partial sums of squares, and the
-// unfused chain's residual-add and RMSNorm passes.
+// Small row-wise kernels: the combine of the partial sums of squares, the
+// unfused chain's residual-add and RMSNorm passes, and the backward's combine
+// and dH passes.
 #pragma once
 
 #include "gemm.hpp"
@@ -66,6 +67,48 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const T* __restrict__
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = (v[i] * rr) * gv[i];
     Chunk8<T>::store(Xn + row * D + c * 8, v);
+  }
+}
+
+// Backward combine.  Threads 0 .. M-1 take one row each:
+//   c_i = r_i^3 * (sum_t srow[t][i]) / D
+// (the coefficient of H_i in dH_i; the sum in increasing t, the product in
+// double, rounded once).  Threads M .. M+D-1 take one column each:
+//   dg_j = sum_u dgcol[u][j], u = 0 .. U-1 in increasing order.
+__global__ __launch_bounds__(256) void bwd_combine_kernel(const float* __restrict__ srow,
+                                                          const float* __restrict__ dgcol,
+                                                          const float* __restrict__ r, float* __restrict__ c,
+                                                          float* __restrict__ dg, int M, int T, int D, int U) {
+  const int64_t i = blockIdx.x * 256ll + threadIdx.x;
+  if (i < M) {
+    float s = 0.f;
+    for (int t = 0; t < T; ++t) s += srow[(int64_t)t * M + i];
+    const double rr = (double)r[i];
+    c[i] = (float)(rr * rr * rr * (double)s / (double)D);
+  } else if (i < (int64_t)M + D) {
+    const int j = (int)(i - M);
+    float s = 0.f;
+    for (int u = 0; u < U; ++u) s += dgcol[(int64_t)u * D + j];
+    dg[j] = s;
+  }
+}
+
+// Backward dH, in place over dense [M, D]: the buffer holds P = round(g G) on
+// entry and dH = round(r_i float(P_ij) - c_i float(H_ij)) on exit.
+template <typename T>
+__global__ __launch_bounds__(256) void dh_finalize_kernel(T* __restrict__ PdH, const T* __restrict__ H,
+                                                          const float* __restrict__ r,
+                                                          const float* __restrict__ c, int D, int64_t nchunks) {
+  const int cpr = D / 8;  // chunks per row
+  for (int64_t k = blockIdx.x * 256ll + threadIdx.x; k < nchunks; k += (int64_t)gridDim.x * 256) {
+    const int64_t row = k / cpr;
+    float pv[8], hv[8];
+    Chunk8<T>::load(PdH + k * 8, pv);
+    Chunk8<T>::load(H + k * 8, hv);
+    const float rr = r[row], cc = c[row];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pv[i] = rr * pv[i] - cc * hv[i];
+    Chunk8<T>::store(PdH + k * 8, pv);
   }
 }
 
