@@ -14,7 +14,9 @@ Prints ONE JSON line: whole-job TFLOP/s (algorithmic GEMM flops
 timed with HIP events on the launch stream, the unfused reference chain for
 A/B comparison, the same chain in plain PyTorch (torch.matmul, i.e. the
 vendor GEMM library, plus torch elementwise and reduction ops) for context,
-and the fp64 CPU oracle timed on a bounded row sample.
+the backward chain (coda_chain_bwd) on the 7B backward workload with a
+training step (fused forward + backward) beside PyTorch autograd on the same
+chain, and the fp64 CPU oracle timed on a bounded row sample.
 """
 from __future__ import annotations
 
@@ -46,6 +48,8 @@ def parse():
                     help="approximate CPU work budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ref-chain", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward chain (7b-bwd-bf16) and the training-step comparison")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the warm-up, copy this many MiB device to device twice (a transfer of known "
                          "size that calibrates HBM byte counters in a profiler run)")
@@ -92,6 +96,91 @@ def cpu_baseline(wl, x, budget_s: float):
             "kind": "oracle",
             "sample": f"rows 0..{n - 1} of the {wl.M}-row {wl.name} forward chain (rows are independent), "
                       f"fp64 numpy, {dt:.2f} s, including the oracle's own fp64 weight conversion"}
+
+
+def time_ms(fn, stream, n, warmup):
+    """Average milliseconds of fn() over n calls, HIP events on `stream`."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(n):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def bench_backward(args, up, stream):
+    """The backward chain on the 7B backward workload (dY of 16384 x 28672 and
+    the forward's saved H, r), and a training step of the chain (fused forward
+    + backward) beside PyTorch autograd of the same chain."""
+    import torch
+
+    import coda_inputs as ci
+    import transformer_gemm_epilogue_gemm1_amd as coda
+
+    wl = ci.WORKLOADS["7b-bwd-bf16"]
+    x = ci.make_inputs(wl, seed=args.seed)
+    d = {k: up(v) for k, v in x.items()}
+    M, K, D, N2 = wl.M, wl.K, wl.D, wl.N2
+    dev, tdt = d["A"].device, d["A"].dtype
+    H = torch.empty((M, D), device=dev, dtype=tdt)
+    Hg = torch.empty((M, D), device=dev, dtype=tdt)
+    P = torch.empty((coda.coda_prms_num_partials(tdt, D), M), device=dev, dtype=torch.float32)
+    r = torch.empty((M,), device=dev, dtype=torch.float32)
+    Y = torch.empty((M, N2), device=dev, dtype=tdt)
+    dA = torch.empty((M, K), device=dev, dtype=tdt)
+    dR = torch.empty((M, D), device=dev, dtype=tdt)
+    dW1 = torch.empty((K, D), device=dev, dtype=tdt)
+    dW2 = torch.empty((D, N2), device=dev, dtype=tdt)
+    dg = torch.empty((D,), device=dev, dtype=torch.float32)
+    ws = torch.empty((coda.coda_chain_bwd_workspace_bytes(tdt, M, K, D, N2),), device=dev, dtype=torch.uint8)
+
+    def fwd():
+        coda.coda_gemm_res_prms(d["A"], d["W1"], d["R"], d["g"], H, Hg, P, stream)
+        coda.coda_rms_combine(P, r, D, wl.eps, stream)
+        coda.coda_gemm_rowscale(Hg, d["W2"], r, Y, stream)
+
+    def bwd():
+        coda.coda_chain_bwd(d["dY"], d["A"], d["W1"], d["g"], d["W2"], H, r, dA, dR, dW1, dW2, dg, ws, stream)
+
+    def train():
+        fwd()
+        bwd()
+
+    n = max(5, args.steps // 2)
+    w = max(2, args.warmup // 2)
+    fwd()
+    bwd_ms = time_ms(bwd, stream, n, w)
+    train_ms = time_ms(train, stream, n, w)
+    bwd_flops = 4.0 * M * D * N2 + 4.0 * M * K * D
+    out = {"workload": f"{wl.name}: dY {M}x{N2}, saved H and r; M={M} K={K} D={D} N2={N2}",
+           "ms": round(bwd_ms, 4),
+           "tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
+           "pct_of_peak": round(100.0 * bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+           "algorithmic_flops": bwd_flops,
+           "train_step_ms": round(train_ms, 4)}
+    if not args.no_torch_chain:
+        leaves = {k: d[k].clone().requires_grad_(True) for k in ("A", "W1", "R", "g", "W2")}
+
+        def torch_train():
+            for t in leaves.values():
+                t.grad = None
+            Ht = torch.addmm(leaves["R"], leaves["A"], leaves["W1"])
+            Xn = torch.nn.functional.rms_norm(Ht.float(), (D,), leaves["g"].float(), wl.eps).to(tdt)
+            Yt = torch.matmul(Xn, leaves["W2"])
+            Yt.backward(d["dY"])
+
+        t_ms = time_ms(torch_train, stream, n, w)
+        out["torch_autograd_train_step_ms"] = round(t_ms, 4)
+        out["train_step_speedup_vs_torch_autograd"] = round(t_ms / train_ms, 4)
+        del leaves
+    return out
 
 
 def main():
@@ -256,6 +345,9 @@ def main():
         t_ms = a.elapsed_time(b) / nt
         out["torch_chain_ms"] = round(t_ms, 4)
         out["speedup_vs_torch_chain"] = round(t_ms / ms_step, 4)
+
+    if not args.no_backward:
+        out["backward"] = bench_backward(args, up, stream)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)

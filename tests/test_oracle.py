@@ -103,6 +103,44 @@ def test_r_times_rms():
             np.testing.assert_allclose(out["r"] * rms, 1.0, rtol=1e-14)
 
 
+def test_deferred_row_scale_equals_normalise_then_multiply():
+    # the re-association the fused path relies on (epilogue section of the
+    # article): scaling the rows of (H diag(g)) W2 by r afterwards gives the
+    # normalise-then-multiply result; brute-force sums in exact rationals on
+    # a tiny case, so neither side shares the oracle's matmul
+    rng = np.random.default_rng(21)
+    A, W1, R, g, W2 = _case(rng, 3, 4, 5, 2)
+    eps = 0.25
+    out = oracle.forward(A, W1, R, g, W2, eps)
+    H = [[Fraction(v) for v in row] for row in out["H"]]
+    r = [Fraction(v) for v in out["r"]]
+    gq = [Fraction(v) for v in g]
+    W2q = [[Fraction(v) for v in row] for row in W2]
+    for i in range(3):
+        for k in range(2):
+            deferred = r[i] * sum(H[i][j] * gq[j] * W2q[j][k] for j in range(5))
+            normalised = sum((r[i] * H[i][j] * gq[j]) * W2q[j][k] for j in range(5))
+            assert deferred == normalised
+            assert float(deferred) == pytest.approx(out["Y"][i, k], rel=1e-13, abs=1e-15)
+
+
+def test_constant_rows_with_unit_weight():
+    # g = 1 and a row of H constant c: r = 1/sqrt(c^2 + eps) and the
+    # normalised row is c r (1, ..., 1), so Y_i = c r (column sums of W2)
+    rng = np.random.default_rng(22)
+    M, K, D, N2 = 4, 8, 16, 6
+    A = np.zeros((M, K))
+    W1 = rng.standard_normal((K, D))
+    R = np.repeat(np.array([[2.0], [-0.5], [0.0], [7.0]]), D, axis=1)
+    W2 = rng.standard_normal((D, N2))
+    eps = 1e-3
+    out = oracle.forward(A, W1, R, np.ones(D), W2, eps)
+    c = R[:, 0]
+    r = 1.0 / np.sqrt(c * c + eps)
+    np.testing.assert_allclose(out["r"], r, rtol=1e-15)
+    np.testing.assert_allclose(out["Y"], (c * r)[:, None] * W2.sum(axis=0)[None, :], rtol=1e-13, atol=1e-15)
+
+
 def test_scale_invariance_and_row_permutation():
     rng = np.random.default_rng(5)
     A, W1, R, g, W2 = _case(rng, 7, 8, 16, 9)
