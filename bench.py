@@ -48,6 +48,9 @@ def parse():
                     help="approximate CPU work budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ref-chain", action="store_true")
+    ap.add_argument("--power-probe-s", type=float, default=2.0,
+                    help="seconds of back-to-back forward chains while amd-smi samples socket power and "
+                         "gfx clocks (0 disables; skipped when amd-smi is absent)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward chain (7b-bwd-bf16) and the training-step comparison")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -113,6 +116,69 @@ def time_ms(fn, stream, n, warmup):
     b.record(stream)
     torch.cuda.synchronize()
     return a.elapsed_time(b) / n
+
+
+def _smi_sample():
+    """(socket power W, mean gfx clock MHz) from one amd-smi reading, or None."""
+    import shutil
+    import subprocess
+
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    try:
+        res = subprocess.run([exe, "metric", "-p", "-c", "--json"], capture_output=True, text=True, timeout=10)
+        d = json.loads(res.stdout)
+    except Exception:
+        return None
+    if isinstance(d, dict) and "gpu_data" in d:
+        d = d["gpu_data"]
+    d = d[0] if isinstance(d, list) and d else d
+    try:
+        pw = d["power"]["socket_power"]
+        pw = float(pw["value"] if isinstance(pw, dict) else pw)
+        clks = [float(v["clk"]["value"]) for k, v in d["clock"].items()
+                if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+    except (KeyError, TypeError, ValueError):
+        return None
+    return (pw, sum(clks) / len(clks)) if clks else None
+
+
+def power_probe(fn, seconds):
+    """Runs fn() back to back for `seconds` while a thread samples amd-smi;
+    returns median socket power and gfx clock over the samples taken after
+    the first half second (the ramp), or None."""
+    import threading
+
+    import torch
+
+    if seconds <= 0 or _smi_sample() is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        t0 = time.time()
+        while not stop.is_set():
+            s = _smi_sample()
+            if s is not None and time.time() - t0 > 0.5:
+                samples.append(s)
+            time.sleep(0.2)
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    t0 = time.time()
+    while time.time() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    pw = sorted(x[0] for x in samples)
+    ck = sorted(x[1] for x in samples)
+    return {"socket_power_w": pw[len(pw) // 2], "gfx_clock_mhz": round(ck[len(ck) // 2], 1),
+            "samples": len(samples), "seconds": seconds}
 
 
 def bench_backward(args, up, stream):
@@ -295,6 +361,14 @@ def main():
                        "coda_gemm_rowscale": round(g2_avg, 4)},
         "wall_s_timed_region": round(wall_s, 3),
     }
+
+    pp = power_probe(step, args.power_probe_s)
+    if pp is not None:
+        # the dense peak at the clock the chip holds under this load
+        peak_clk = 256 * 4096 * pp["gfx_clock_mhz"] * 1e6 / 1e12
+        pp["peak_at_clock_tflops"] = round(peak_clk, 1)
+        pp["dominant_kernel_frac_at_clock"] = round(g2_tflops / peak_clk, 4)
+        out["power"] = pp
 
     if not args.no_ref_chain:
         ws = torch.empty((coda.coda_ref_chain_workspace_bytes(tdt, M, D),), device=dev, dtype=torch.uint8)

@@ -6,17 +6,67 @@
 // H out), tile reduction (partial sums of squares per row).
 //
 // The GEMM kernel hands each lane 8 consecutive columns `col .. col+7` of one
-// row through apply(q, row, col, v) (q = which of the lane's 2 rows of the
-// current 16-row slab), calls end_slab(slab_row0) on every lane once the
-// slab is done, and finish() on every lane after the last slab.  Lanes l and
-// l' with l/8 == l'/8 hold the same rows; the 8 lanes of such a group
-// together cover the wavefront's 64 columns, and lanes with equal l % 8 hold
-// the same 8 columns in every slab.
+// row through apply(mt, q, row, col, v) (mt = which of the wavefront's eight
+// 16-row slabs, q = which of the lane's 2 rows in it), calls
+// end_slab(slab_row0) on every lane once the slab is done, and finish() on
+// every lane after the last slab.  Lanes l and l' with l/8 == l'/8 hold the
+// same rows; the 8 lanes of such a group together cover the wavefront's 64
+// columns, and lanes with equal l % 8 hold the same 8 columns in every slab.
+//
+// Epilogues that read global memory (R, H, r) issue all of a lane's loads in
+// their constructor, before the first slab, so the wavefront waits for one
+// memory round trip rather than one per slab (the stores of a slab could
+// otherwise alias the next slab's loads, so the compiler keeps them in order).
 #pragma once
 
 #include "gemm.hpp"
 
 namespace coda {
+
+// Row of slot (mt, q) of `lane` in the wavefront's epilogue.
+__device__ __forceinline__ int epi_row(int row_base, int mt, int q, int lane) {
+  return row_base + mt * 16 + (lane >> 3) + 8 * q;
+}
+
+// Prefetched 8-column chunks of one operand for a lane's 16 epilogue rows:
+// bf16 only (64 registers as stored); for fp32 (128 registers) the loads
+// stay in apply().
+template <typename T>
+struct RowChunks {
+  static constexpr bool kPrefetch = sizeof(T) == 2;
+  u32x4 raw[kPrefetch ? kFragM : 1][2];
+  __device__ __forceinline__ void prefetch(const T* base, int64_t ld, int row_base, int col, int lane, int M, int N) {
+    if constexpr (kPrefetch) {
+#pragma unroll
+      for (int mt = 0; mt < kFragM; ++mt)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int row = epi_row(row_base, mt, q, lane);
+          raw[mt][q] = (row < M && col < N) ? Chunk8<T>::load_raw(base + (int64_t)row * ld + col) : u32x4{0, 0, 0, 0};
+        }
+    }
+  }
+  __device__ __forceinline__ void get(const T* base, int64_t ld, int mt, int q, int row, int col, float v[8]) const {
+    if constexpr (kPrefetch)
+      Chunk8<T>::unpack(raw[mt][q], v);
+    else
+      Chunk8<T>::load(base + (int64_t)row * ld + col, v);
+  }
+};
+
+// Per-row float values (r) for a lane's 16 epilogue rows.
+struct RowScalars {
+  float v[kFragM][2];
+  __device__ __forceinline__ void prefetch(const float* p, int row_base, int lane, int M) {
+#pragma unroll
+    for (int mt = 0; mt < kFragM; ++mt)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int row = epi_row(row_base, mt, q, lane);
+        v[mt][q] = row < M ? p[row] : 0.f;
+      }
+  }
+};
 
 // First GEMM of the chain: H = round(acc + R), Hg = round(float(H) * g),
 // partials[t][row] = sum over the 64 columns of partial tile t of float(H)^2
@@ -36,6 +86,7 @@ struct EpiResPrms {
     float* partials;  // [T][M]
   };
   Params p;
+  RowChunks<T> rc;
   float gv[8];
   float ss[2];
   int lane, t, M;
@@ -43,18 +94,17 @@ struct EpiResPrms {
   __device__ __forceinline__ EpiResPrms(const Params& p_, int lane_, int wm, int wn, int m0, int n0, int tn,
                                         int M_, int N)
       : p(p_), lane(lane_), t(4 * tn + wn), M(M_) {
-    (void)wm;
-    (void)m0;
     const int col = n0 + wn * kWaveN + (lane & 7) * 8;
+    rc.prefetch(p.R, p.ldr, m0 + wm * kWaveM, col, lane, M_, N);
 #pragma unroll
     for (int i = 0; i < 8; ++i) gv[i] = 1.f;
     if (p.g != nullptr && col < N) Chunk8<T>::load(p.g + col, gv);
     ss[0] = ss[1] = 0.f;
   }
 
-  __device__ __forceinline__ void apply(int q, int row, int col, float v[8]) {
+  __device__ __forceinline__ void apply(int mt, int q, int row, int col, float v[8]) {
     float rv[8], h[8];
-    Chunk8<T>::load(p.R + (int64_t)row * p.ldr + col, rv);
+    rc.get(p.R, p.ldr, mt, q, row, col, rv);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       h[i] = Chunk8<T>::round(v[i] + rv[i]);
@@ -94,9 +144,13 @@ struct EpiRowScale {
     int64_t ldy;
   };
   Params p;
-  __device__ __forceinline__ EpiRowScale(const Params& p_, int, int, int, int, int, int, int, int) : p(p_) {}
-  __device__ __forceinline__ void apply(int, int row, int col, float v[8]) {
-    const float s = p.r != nullptr ? p.r[row] : 1.f;
+  RowScalars rs;
+  __device__ __forceinline__ EpiRowScale(const Params& p_, int lane, int wm, int, int m0, int, int, int M, int)
+      : p(p_) {
+    if (p.r != nullptr) rs.prefetch(p.r, m0 + wm * kWaveM, lane, M);
+  }
+  __device__ __forceinline__ void apply(int mt, int q, int row, int col, float v[8]) {
+    const float s = p.r != nullptr ? rs.v[mt][q] : 1.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] *= s;
     Chunk8<T>::store(p.Y + (int64_t)row * p.ldy + col, v);
@@ -113,7 +167,7 @@ struct EpiStoreF32 {
   };
   Params p;
   __device__ __forceinline__ EpiStoreF32(const Params& p_, int, int, int, int, int, int, int, int) : p(p_) {}
-  __device__ __forceinline__ void apply(int, int row, int col, float v[8]) {
+  __device__ __forceinline__ void apply(int, int, int row, int col, float v[8]) {
     Chunk8<float>::store(p.C + (int64_t)row * p.ldc + col, v);
   }
   __device__ __forceinline__ void end_slab(int) {}
@@ -143,6 +197,8 @@ struct EpiBwdG {
     float* dgcol;      // [ceil(M / 128)][D]
   };
   Params p;
+  RowChunks<T> hc;
+  RowScalars rs;
   float gv[8];
   float colsum[8];
   float ss[2];
@@ -155,6 +211,8 @@ struct EpiBwdG {
     col = n0 + wn * kWaveN + (lane & 7) * 8;
     u = m0 / kWaveM + wm;
     rows_in = m0 + wm * kWaveM < M_;
+    hc.prefetch(p.H, p.ld, m0 + wm * kWaveM, col, lane, M_, N_);
+    rs.prefetch(p.r, m0 + wm * kWaveM, lane, M_);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       gv[i] = 0.f;
@@ -164,11 +222,11 @@ struct EpiBwdG {
     ss[0] = ss[1] = 0.f;
   }
 
-  __device__ __forceinline__ void apply(int q, int row, int col_, float v[8]) {
+  __device__ __forceinline__ void apply(int mt, int q, int row, int col_, float v[8]) {
     float hv[8], pv[8], xv[8];
     const int64_t o = (int64_t)row * p.ld + col_;
-    Chunk8<T>::load(p.H + o, hv);
-    const float rr = p.r[row];
+    hc.get(p.H, p.ld, mt, q, row, col_, hv);
+    const float rr = rs.v[mt][q];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       pv[i] = gv[i] * v[i];

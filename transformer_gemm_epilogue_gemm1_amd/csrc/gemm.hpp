@@ -85,6 +85,15 @@ struct Chunk8<uint16_t> {
   }
   // value after a round trip through storage (rounding to the stored dtype)
   __device__ static float round(float x) { return bf16_to_f32(f32_to_bf16(x)); }
+  // the 8 values as stored (16 bytes), and their expansion
+  __device__ static u32x4 load_raw(const uint16_t* p) { return *(const u32x4*)p; }
+  __device__ static void unpack(const u32x4& u, float v[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(u[i] << 16);
+      v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  }
 };
 template <>
 struct Chunk8<float> {
@@ -313,7 +322,9 @@ __device__ __forceinline__ void kstep(char* const (&st)[kStages], const Dma<T, A
 // through LDS so that each lane holds 8 consecutive columns of one row:
 // lane l, slot q (0..1) gets row (l/8 + 8q) of the 16-row slab and columns
 // [8*(l%8), 8*(l%8)+8) of the wavefront's 64.  Epi provides
-//   apply(q, row, col, v[8])   for rows < M and columns < N (col % 8 == 0)
+//   apply(mt, q, row, col, v)  for rows < M and columns < N (col % 8 == 0);
+//                              row = row_base + 16 mt + l/8 + 8 q
+//                              (epi_row), v[8] the accumulators
 //   end_slab(slab_row0)        after all lanes applied one 16-row slab
 //   finish()                   on every lane after the last slab
 template <typename T, bool A_KC, bool B_KC, class Epi>
@@ -396,7 +407,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const f32x4 lo = *(const f32x4*)src, hi = *(const f32x4*)(src + 4);
       float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       const int row = row_base + mt * 16 + rl;
-      if (row < g.M && col < g.N) epi.apply(q, row, col, v);
+      if (row < g.M && col < g.N) epi.apply(mt, q, row, col, v);
     }
     epi.end_slab(row_base + mt * 16);
     __syncthreads();
