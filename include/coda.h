@@ -85,9 +85,12 @@ coda_status coda_gemm_res_prms(coda_dtype dt, int64_t M, int64_t K, int64_t D,
                                void* Hg, int64_t ldhg,
                                float* partials, void* stream);
 
-/* Combine: r_i = 1 / sqrt((sum_{t<T} partials[t*M + i]) / D + eps), summed in
- * increasing t.  partials: float[T*M] as written above; r: float[M].
- * T >= 1, D >= 1, eps >= 0. */
+/* Combine: r_i = 1 / sqrt((sum_{t<T} partials[t*M + i]) / D + eps).  The sum
+ * runs in a fixed order (four consecutive quarters of t, each in increasing
+ * t, then added first to last), so the result is deterministic; the mean and
+ * square root are taken in double and rounded once to float.
+ * partials: float[T*M] as written above; r: float[M]. T >= 1, D >= 1,
+ * eps >= 0. */
 coda_status coda_rms_combine(int64_t M, int64_t D, int64_t T, float eps,
                              const float* partials, float* r, void* stream);
 

@@ -139,7 +139,7 @@ coda_status gemm_rowscale_impl(int M, int D, int N2, const void* X, int64_t ldx,
 }
 
 coda_status combine_impl(int M, int D, int T, float eps, const float* partials, float* r, hipStream_t s) {
-  hipLaunchKernelGGL(rms_combine_kernel, dim3((M + 255) / 256), dim3(256), 0, s, partials, r, M, T, D, eps);
+  hipLaunchKernelGGL(rms_combine_kernel, dim3((M + 63) / 64), dim3(256), 0, s, partials, r, M, T, D, eps);
   return launch_status("coda_rms_combine");
 }
 
@@ -180,7 +180,7 @@ coda_status chain_bwd_impl(int M, int K, int D, int N2, const void* dY, const vo
       return st;
   }
   // 2. c and dg (with M = 0 only the columns: dg = 0)
-  hipLaunchKernelGGL(bwd_combine_kernel, dim3((unsigned)((M + (int64_t)D + 255) / 256)), dim3(256), 0, s, srow,
+  hipLaunchKernelGGL(bwd_combine_kernel, dim3((unsigned)((M + 63) / 64 + (D + 63) / 64)), dim3(256), 0, s, srow,
                      dgcol, r, c, dg, M, Tn, D, U);
   if ((st = launch_status("coda_chain_bwd combine")) != CODA_OK) return st;
   if (M > 0) {

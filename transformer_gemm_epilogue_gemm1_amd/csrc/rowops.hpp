@@ -7,19 +7,38 @@
 
 namespace coda {
 
+// Fixed-order sum of parts[t * stride + i], t = 0 .. T-1, for the 64
+// indices i = i0 .. i0+63 of a 256-thread workgroup: wavefront q sums its
+// quarter of t in increasing order, then the quarters are added as
+// ((q0 + q1) + q2) + q3.  Lane l of every wavefront gets the sum for i0 + l.
+// Each load of a wavefront reads 64 consecutive floats.
+__device__ __forceinline__ float quarter_sum(const float* __restrict__ parts, int64_t stride, int T, int i, bool in,
+                                             float (*red)[64]) {
+  const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tq = (T + 3) / 4;
+  const int t0 = q * tq, t1 = t0 + tq < T ? t0 + tq : T;
+  float s = 0.f;
+  if (in) {
+#pragma unroll 8
+    for (int t = t0; t < t1; ++t) s += parts[(int64_t)t * stride + i];
+  }
+  red[q][lane] = s;
+  __syncthreads();
+  return ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+}
+
 // r_i = 1/sqrt(mean_j H_ij^2 + eps) from the per-tile partial sums of squares
 // (the light auxiliary reduction of the CODA news article by Synced, section
-// "CODA：「尾声」里藏着宝藏").  One thread per row; partials[t*M + i] are summed
-// in increasing t (fixed order: deterministic), the mean and reciprocal
-// square root are taken in double precision and rounded once to float.
+// "CODA：「尾声」里藏着宝藏").  64 rows per 256-thread workgroup, partials
+// [T][M] summed in the fixed order of quarter_sum (deterministic); the mean
+// and reciprocal square root are taken in double precision and rounded once.
 __global__ __launch_bounds__(256) void rms_combine_kernel(const float* __restrict__ partials,
                                                           float* __restrict__ r, int M, int T, int D,
                                                           float eps) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= M) return;
-  float s = 0.f;
-  for (int t = 0; t < T; ++t) s += partials[(int64_t)t * M + i];
-  r[i] = (float)(1.0 / sqrt((double)s / (double)D + (double)eps));
+  __shared__ float red[4][64];
+  const int i = blockIdx.x * 64 + (threadIdx.x & 63);
+  const float s = quarter_sum(partials, M, T, i, i < M, red);
+  if (threadIdx.x < 64 && i < M) r[i] = (float)(1.0 / sqrt((double)s / (double)D + (double)eps));
 }
 
 // Unfused chain, step 2: H = round(C + R), elementwise over dense [M, D].
@@ -70,26 +89,30 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const T* __restrict__
   }
 }
 
-// Backward combine.  Threads 0 .. M-1 take one row each:
+// Backward combine.  Workgroups 0 .. ceil(M/64)-1 take 64 rows each:
 //   c_i = r_i^3 * (sum_t srow[t][i]) / D
-// (the coefficient of H_i in dH_i; the sum in increasing t, the product in
-// double, rounded once).  Threads M .. M+D-1 take one column each:
-//   dg_j = sum_u dgcol[u][j], u = 0 .. U-1 in increasing order.
+// (the coefficient of H_i in dH_i; the product in double, rounded once);
+// the following ceil(D/64) workgroups take 64 columns each:
+//   dg_j = sum_u dgcol[u][j], u = 0 .. U-1.
+// Both sums in the fixed order of quarter_sum.
 __global__ __launch_bounds__(256) void bwd_combine_kernel(const float* __restrict__ srow,
                                                           const float* __restrict__ dgcol,
                                                           const float* __restrict__ r, float* __restrict__ c,
                                                           float* __restrict__ dg, int M, int T, int D, int U) {
-  const int64_t i = blockIdx.x * 256ll + threadIdx.x;
-  if (i < M) {
-    float s = 0.f;
-    for (int t = 0; t < T; ++t) s += srow[(int64_t)t * M + i];
-    const double rr = (double)r[i];
-    c[i] = (float)(rr * rr * rr * (double)s / (double)D);
-  } else if (i < (int64_t)M + D) {
-    const int j = (int)(i - M);
-    float s = 0.f;
-    for (int u = 0; u < U; ++u) s += dgcol[(int64_t)u * D + j];
-    dg[j] = s;
+  __shared__ float red[4][64];
+  const int row_blocks = (M + 63) / 64;
+  const int lane = threadIdx.x & 63;
+  if ((int)blockIdx.x < row_blocks) {
+    const int i = blockIdx.x * 64 + lane;
+    const float s = quarter_sum(srow, M, T, i, i < M, red);
+    if (threadIdx.x < 64 && i < M) {
+      const double rr = (double)r[i];
+      c[i] = (float)(rr * rr * rr * (double)s / (double)D);
+    }
+  } else {
+    const int j = (blockIdx.x - row_blocks) * 64 + lane;
+    const float s = quarter_sum(dgcol, D, U, j, j < D, red);
+    if (threadIdx.x < 64 && j < D) dg[j] = s;
   }
 }
 
