@@ -48,6 +48,8 @@ def parse():
                     help="approximate CPU work budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ref-chain", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip timing the fused forward at the 1B and 70B shapes")
     ap.add_argument("--power-probe-s", type=float, default=2.0,
                     help="seconds of back-to-back forward chains while amd-smi samples socket power and "
                          "gfx clocks (0 disables; skipped when amd-smi is absent)")
@@ -179,6 +181,46 @@ def power_probe(fn, seconds):
     ck = sorted(x[1] for x in samples)
     return {"socket_power_w": pw[len(pw) // 2], "gfx_clock_mhz": round(ck[len(ck) // 2], 1),
             "samples": len(samples), "seconds": seconds}
+
+
+def bench_forward_shape(wl, stream, steps, warmup, seed):
+    """Fused forward chain at another workload's shape, for the metric at
+    that size: inputs drawn on the device with a seeded generator (same
+    distributions as the host generators; timing only, parity is tested
+    elsewhere)."""
+    import torch
+
+    import transformer_gemm_epilogue_gemm1_amd as coda
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    M, K, D, N2 = wl.M, wl.K, wl.D, wl.N2
+
+    def randn(*shape, scale=1.0, shift=0.0):
+        return (torch.randn(shape, device=dev, generator=gen) * scale + shift).to(torch.bfloat16)
+
+    A, R = randn(M, K), randn(M, D)
+    W1, W2 = randn(K, D, scale=K ** -0.5), randn(D, N2, scale=D ** -0.5)
+    g = randn(D, scale=0.1, shift=1.0)
+    H = torch.empty((M, D), device=dev, dtype=torch.bfloat16)
+    Hg = torch.empty_like(H)
+    P = torch.empty((coda.coda_prms_num_partials(torch.bfloat16, D), M), device=dev, dtype=torch.float32)
+    r = torch.empty((M,), device=dev, dtype=torch.float32)
+    Y = torch.empty((M, N2), device=dev, dtype=torch.bfloat16)
+
+    def step():
+        coda.coda_gemm_res_prms(A, W1, R, g, H, Hg, P, stream)
+        coda.coda_rms_combine(P, r, D, wl.eps, stream)
+        coda.coda_gemm_rowscale(Hg, W2, r, Y, stream)
+
+    ms = time_ms(step, stream, steps, warmup)
+    g2_ms = time_ms(lambda: coda.coda_gemm_rowscale(Hg, W2, r, Y, stream), stream, steps, warmup)
+    tf = wl.fwd_flops / (ms * 1e-3) / 1e12
+    g2_tf = 2.0 * M * D * N2 / (g2_ms * 1e-3) / 1e12
+    return {"shape": {"M": M, "K": K, "D": D, "N2": N2}, "ms_per_step": round(ms, 4), "value": round(tf, 2),
+            "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
+            "coda_gemm_rowscale_frac": round(g2_tf / PEAK_BF16_TFLOPS, 4)}
 
 
 def bench_backward(args, up, stream):
@@ -329,6 +371,8 @@ def main():
         comb_ms.append(evs[i][0].elapsed_time(evs[i][1]))
         g2_ms.append(evs[i][1].elapsed_time(evs[i][2]))
     g1_avg, comb_avg, g2_avg = (float(np.mean(v)) for v in (g1_ms, comb_ms, g2_ms))
+    step_ms = [a + b + c for a, b, c in zip(g1_ms, comb_ms, g2_ms)]
+    pct = {f"p{q}": round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)}
 
     flops = wl.fwd_flops
     tflops = flops / (ms_step * 1e-3) / 1e12
@@ -359,7 +403,10 @@ def main():
                      "algorithmic_flops_per_launch": g2_flops},
         "kernels_ms": {"coda_gemm_res_prms": round(g1_avg, 4), "coda_rms_combine": round(comb_avg, 4),
                        "coda_gemm_rowscale": round(g2_avg, 4)},
+        "step_ms_percentiles": pct,
         "wall_s_timed_region": round(wall_s, 3),
+        "device": {"name": torch.cuda.get_device_name(dev),
+                   "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count},
     }
 
     pp = power_probe(step, args.power_probe_s)
@@ -419,6 +466,12 @@ def main():
         t_ms = a.elapsed_time(b) / nt
         out["torch_chain_ms"] = round(t_ms, 4)
         out["speedup_vs_torch_chain"] = round(t_ms / ms_step, 4)
+
+    if not args.no_other_workloads and wl.name == "7b-bf16":
+        out["other_workloads"] = {
+            name: bench_forward_shape(ci.WORKLOADS[name], stream, max(5, args.steps // 2),
+                                      max(2, args.warmup // 2), args.seed)
+            for name in ("1b-bf16", "70b-bf16")}
 
     if not args.no_backward:
         out["backward"] = bench_backward(args, up, stream)
