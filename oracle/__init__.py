@@ -1,6 +1,7 @@
-"""CPU fp64 oracle for the GEMM-Residual-RMSNorm-GEMM chain.
+"""CPU fp64 oracle for the GEMM-Residual-RMSNorm-GEMM chain (and its SwiGLU epilogue).
 
 TEST INFRASTRUCTURE ONLY: imported by the test-suite, the smoke check and the
 benchmark's CPU-baseline leg, never by the library or its Python binding.
 """
 from .chain import backward, forward  # noqa: F401
+from .swiglu import backward_swiglu, forward_swiglu, silu, swiglu_dy  # noqa: F401
