@@ -104,6 +104,27 @@ coda_status coda_gemm_rowscale(coda_dtype dt, int64_t M, int64_t D, int64_t N2,
                                const float* r,
                                void* Y, int64_t ldy, void* stream);
 
+/* Second GEMM with the deferred row scale and a SwiGLU gate in the epilogue.
+ * The article (section "CODA：「尾声」里藏着宝藏") says the re-parameterisation
+ * applies to SwiGLU as well, and its results section measures SwiGLU epilogue
+ * compositions; it does not write SwiGLU out.  Reading taken (the LLaMA gate):
+ * W2 = [W_gate | W_up], columns [0, F) and [F, 2F), and with
+ * y = r_i * (X W2)_ik (fp32 accumulation):
+ *   Z_ij = round(silu(y_ij) * y_i,F+j)    [M,F],  silu(x) = x / (1 + e^-x)
+ *   Y_ik = round(y_ik)                    [M,2F], only if Y != NULL (the
+ *                                          pre-activation kept for a backward)
+ * Z (and Y) are written straight from the accumulators: the [M,2F]
+ * pre-activation never goes through HBM unless asked for.
+ *   X: [M,D] (ldx); W2: [D,2F] (ldw2 >= 2F); r: float[M] or NULL (no row
+ *   scale); Z: [M,F] (ldz); Y: [M,2F] (ldy) or NULL.
+ * F >= 1, a multiple of 8.  Z and Y must not overlap X, W2, r or each other. */
+coda_status coda_gemm_rowscale_swiglu(coda_dtype dt, int64_t M, int64_t D, int64_t F,
+                                      const void* X, int64_t ldx,
+                                      const void* W2, int64_t ldw2,
+                                      const float* r,
+                                      void* Z, int64_t ldz,
+                                      void* Y, int64_t ldy, void* stream);
+
 /* Bytes of workspace coda_ref_chain needs: float C[M,D] + X_n[M,D]. */
 size_t coda_ref_chain_workspace_bytes(coda_dtype dt, int64_t M, int64_t D);
 

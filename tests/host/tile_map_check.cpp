@@ -163,6 +163,33 @@ static void check_rc(int E) {
       }
 }
 
+// SwiGLU column order: a bijection of [0, 2F) onto itself whose chunk pair
+// (2m, 2m+1) holds gate columns 8m.. and up columns F + 8m.., with every DMA
+// chunk (8 bf16 or 4 fp32 elements) contiguous in memory.
+static void check_swiglu_col() {
+  const int Fs[] = {8, 16, 24, 256, 264, 1000, 14336};
+  for (int F : Fs) {
+    std::vector<int> seen(2 * F, 0);
+    for (int n = 0; n < 2 * F; ++n) {
+      const int p = swiglu_col(n, F);
+      CHECK(p >= 0 && p < 2 * F, "swiglu_col(%d, %d) = %d out of range", n, F, p);
+      if (p >= 0 && p < 2 * F) seen[p]++;
+      const int c = n / 8, m = c / 2, i = n % 8;
+      CHECK(p == (c % 2 ? F : 0) + 8 * m + i, "swiglu_col(%d, %d) = %d", n, F, p);
+      if (n % 4 != 0) CHECK(p == swiglu_col(n - 1, F) + 1, "SwiGLU chunk not contiguous at %d", n);
+    }
+    for (int p = 0; p < 2 * F; ++p) CHECK(seen[p] == 1, "SwiGLU column %d of F=%d hit %d times", p, F, seen[p]);
+  }
+  // the epilogue pairs lane l (gate) with lane l ^ 1 (up): same output columns
+  for (int n0 = 0; n0 < 1024; n0 += kTileN)
+    for (int wn = 0; wn < 4; ++wn)
+      for (int lane = 0; lane < 64; lane += 2) {
+        const int col = n0 + wn * kWaveN + (lane & 7) * 8, col_up = n0 + wn * kWaveN + ((lane ^ 1) & 7) * 8;
+        CHECK(((col >> 3) & 1) == 0 && ((col_up >> 3) & 1) == 1, "SwiGLU lane parity");
+        CHECK((col >> 4) == (col_up >> 4), "SwiGLU lane pair covers different output columns");
+      }
+}
+
 static void check_epilogue_slab() {
   const int slab_floats = 16 * kEpiPitch;
   CHECK((kWaves / 4) * kEpiSlabBytes <= kStageBytes, "slabs exceed their stage");
@@ -185,6 +212,7 @@ int main() {
   check_rc(8);
   check_rc(4);
   check_epilogue_slab();
+  check_swiglu_col();
   if (failures) {
     fprintf(stderr, "%d failures\n", failures);
     return 1;

@@ -160,6 +160,39 @@ def test_ref_chain_validation(lib):
     assert call(M=0, A=None) == OK
 
 
+def swiglu(lib, dt=BF16, M=512, D=256, F=256, X=H_, ldx=None, W2=W2_, ldw2=None, r=R2_, Z=Y_, ldz=None,
+           Y=DY_, ldy=None):
+    return lib.coda_gemm_rowscale_swiglu(dt, M, D, F, X, ldx or D, W2, ldw2 or 2 * F, r, Z, ldz or F, Y,
+                                         ldy or 2 * F, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=4), DTYPE),
+    (dict(F=0), SHAPE),
+    (dict(F=12), SHAPE),
+    (dict(D=20), SHAPE),
+    (dict(X=None), NULL),
+    (dict(W2=None), NULL),
+    (dict(Z=None), NULL),
+    (dict(ldw2=256), SHAPE),      # ld < 2F
+    (dict(ldz=100), SHAPE),       # ld < F
+    (dict(ldy=516), ALIGN),       # not a multiple of 8 elements
+    (dict(Z=Y_ + 8), ALIGN),
+    (dict(r=R2_ + 1), ALIGN),
+    (dict(Z=H_), ALIAS),
+    (dict(Y=W2_ + 1024), ALIAS),
+    (dict(Y=Y_ + 512), ALIAS),    # Z and Y overlapping
+    (dict(Z=R2_), ALIAS),
+])
+def test_gemm_rowscale_swiglu_rejects(lib, kw, status):
+    assert swiglu(lib, **kw) == status
+    assert lib.coda_last_error().decode() != ""
+
+
+def test_gemm_rowscale_swiglu_empty_is_noop(lib):
+    assert swiglu(lib, M=0, X=None, Z=None, Y=None, r=None) == OK
+
+
 def test_chain_bwd_workspace_bytes(lib):
     def al(x):
         return (x + 255) // 256 * 256

@@ -109,6 +109,29 @@ def coda_gemm_rowscale(X, W2, r: Optional[torch.Tensor], Y, stream=None) -> None
     _lib.check("coda_gemm_rowscale", st)
 
 
+def coda_gemm_rowscale_swiglu(X, W2, r: Optional[torch.Tensor], Z, Y: Optional[torch.Tensor] = None,
+                              stream=None) -> None:
+    """Z = silu(Y_gate) * Y_up with Y = diag(r) (X W2), W2 = [W_gate | W_up];
+    Y (the pre-activation) is also written when given."""
+    lib = _lib.load()
+    dt = X.dtype
+    M, D = X.shape
+    F2 = W2.shape[1]
+    if F2 % 2:
+        raise ValueError("W2 must have an even number of columns (gate | up)")
+    F = F2 // 2
+    ldx = _mat(X, "X", dt, (M, D))
+    ldw2 = _mat(W2, "W2", dt, (D, F2))
+    ldz = _mat(Z, "Z", dt, (M, F))
+    ldy = _mat(Y, "Y", dt, (M, F2)) if Y is not None else 0
+    if r is not None:
+        _mat(r, "r", torch.float32, (M,))
+    st = lib.coda_gemm_rowscale_swiglu(_dtype_code(X), M, D, F, X.data_ptr(), ldx, W2.data_ptr(), ldw2,
+                                       r.data_ptr() if r is not None else None, Z.data_ptr(), ldz,
+                                       Y.data_ptr() if Y is not None else None, ldy, _stream(stream))
+    _lib.check("coda_gemm_rowscale_swiglu", st)
+
+
 def coda_ref_chain_workspace_bytes(dtype: torch.dtype, M: int, D: int) -> int:
     return int(_lib.load().coda_ref_chain_workspace_bytes(_DT[dtype], M, D))
 
@@ -203,3 +226,20 @@ def fused_backward(dY, A, W1, g, W2, H, r, stream=None):
     ws = torch.empty((coda_chain_bwd_workspace_bytes(dt, M, K, D, N2),), device=dev, dtype=torch.uint8)
     coda_chain_bwd(dY, A, W1, g, W2, H, r, dA, dR, dW1, dW2, dg, ws, stream)
     return dA, dR, dW1, dW2, dg
+
+
+def fused_forward_swiglu(A, W1, R, g, W2, eps: float, keep_y: bool = False, stream=None):
+    """The fused chain with the SwiGLU gate in the second GEMM's epilogue:
+    returns (H, Hg, r, Z, Y) with Y None unless keep_y."""
+    M, D, F2 = A.shape[0], W1.shape[1], W2.shape[1]
+    dev, dt = A.device, A.dtype
+    H = torch.empty((M, D), device=dev, dtype=dt)
+    Hg = torch.empty((M, D), device=dev, dtype=dt)
+    P = torch.empty((coda_prms_num_partials(dt, D), M), device=dev, dtype=torch.float32)
+    r = torch.empty((M,), device=dev, dtype=torch.float32)
+    Z = torch.empty((M, F2 // 2), device=dev, dtype=dt)
+    Y = torch.empty((M, F2), device=dev, dtype=dt) if keep_y else None
+    coda_gemm_res_prms(A, W1, R, g, H, Hg, P, stream)
+    coda_rms_combine(P, r, D, eps, stream)
+    coda_gemm_rowscale_swiglu(Hg, W2, r, Z, Y, stream)
+    return H, Hg, r, Z, Y

@@ -102,7 +102,7 @@ uint32_t span_bytes(int64_t rows, int64_t cols, int64_t ld, int es) {
 
 template <typename T, bool AKC, bool BKC, class Epi>
 coda_status launch_gemm(const char* what, int M, int N, int K, const void* a, int64_t lda, const void* b,
-                        int64_t ldb, const typename Epi::Params& ep, hipStream_t s) {
+                        int64_t ldb, const typename Epi::Params& ep, hipStream_t s, int b_split = 0) {
   GemmArgs g;
   g.M = M;
   g.N = N;
@@ -116,6 +116,7 @@ coda_status launch_gemm(const char* what, int M, int N, int K, const void* a, in
   g.b = b;
   g.ldb = ldb;
   g.b_span = BKC ? span_bytes(N, K, ldb, sizeof(T)) : span_bytes(K, N, ldb, sizeof(T));
+  g.b_split = b_split;
   const int nblocks = g.tiles_m * g.tiles_n;
   hipLaunchKernelGGL((gemm_kernel<T, AKC, BKC, Epi>), dim3(nblocks), dim3(kThreads), 0, s, g, ep);
   return launch_status(what);
@@ -136,6 +137,15 @@ coda_status gemm_rowscale_impl(int M, int D, int N2, const void* X, int64_t ldx,
                                const float* r, void* Y, int64_t ldy, hipStream_t s) {
   typename EpiRowScale<T>::Params ep{r, (T*)Y, ldy};
   return launch_gemm<T, true, false, EpiRowScale<T>>("coda_gemm_rowscale", M, N2, D, X, ldx, W2, ldw2, ep, s);
+}
+
+template <typename T>
+coda_status gemm_rowscale_swiglu_impl(int M, int D, int F, const void* X, int64_t ldx, const void* W2,
+                                      int64_t ldw2, const float* r, void* Z, int64_t ldz, void* Y, int64_t ldy,
+                                      hipStream_t s) {
+  typename EpiSwiGLU<T>::Params ep{r, (T*)Z, ldz, (T*)Y, ldy, F};
+  return launch_gemm<T, true, false, EpiSwiGLU<T>>("coda_gemm_rowscale_swiglu", M, 2 * F, D, X, ldx, W2, ldw2, ep,
+                                                   s, F);
 }
 
 coda_status combine_impl(int M, int D, int T, float eps, const float* partials, float* r, hipStream_t s) {
@@ -283,6 +293,30 @@ coda_status coda_gemm_rowscale(coda_dtype dt, int64_t M, int64_t D, int64_t N2, 
   hipStream_t s = (hipStream_t)stream;
   if (dt == CODA_BF16) return gemm_rowscale_impl<uint16_t>((int)M, (int)D, (int)N2, X, ldx, W2, ldw2, r, Y, ldy, s);
   return gemm_rowscale_impl<float>((int)M, (int)D, (int)N2, X, ldx, W2, ldw2, r, Y, ldy, s);
+}
+
+coda_status coda_gemm_rowscale_swiglu(coda_dtype dt, int64_t M, int64_t D, int64_t F, const void* X, int64_t ldx,
+                                      const void* W2, int64_t ldw2, const float* r, void* Z, int64_t ldz, void* Y,
+                                      int64_t ldy, void* stream) {
+  coda_status st = check_dims(dt, M, {{"D", D}, {"F", F}});
+  if (st != CODA_OK) return st;
+  if (2 * F > kMaxDim) return fail(CODA_ERR_SHAPE, "2F = %lld out of range", (long long)(2 * F));
+  if (M == 0) return ok();
+  const int es = elem_size(dt), E = elems_per_chunk(dt);
+  const Mat mX{X, M, D, ldx, es, "X"}, mW2{W2, D, 2 * F, ldw2, es, "W2"}, mZ{Z, M, F, ldz, es, "Z"};
+  const Mat mY{Y, M, 2 * F, ldy, es, "Y"}, mr{r, 1, M, M, 4, "r"};
+  for (const Mat* m : {&mX, &mW2, &mZ})
+    if ((st = check_mat(*m, E)) != CODA_OK) return st;
+  if (Y != nullptr && (st = check_mat(mY, E)) != CODA_OK) return st;
+  if (r != nullptr && ((uintptr_t)r & 3) != 0) return fail(CODA_ERR_ALIGN, "r is not 4-byte aligned");
+  const Mat none{nullptr, 0, 0, 0, es, ""};
+  const Mat outs[2] = {mZ, Y ? mY : none};
+  const Mat ins[3] = {mX, mW2, r ? mr : none};
+  if ((st = check_alias(outs, 2, ins, 3)) != CODA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == CODA_BF16)
+    return gemm_rowscale_swiglu_impl<uint16_t>((int)M, (int)D, (int)F, X, ldx, W2, ldw2, r, Z, ldz, Y, ldy, s);
+  return gemm_rowscale_swiglu_impl<float>((int)M, (int)D, (int)F, X, ldx, W2, ldw2, r, Z, ldz, Y, ldy, s);
 }
 
 size_t coda_ref_chain_workspace_bytes(coda_dtype dt, int64_t M, int64_t D) {

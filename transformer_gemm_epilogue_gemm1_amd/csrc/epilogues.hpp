@@ -159,6 +159,52 @@ struct EpiRowScale {
   __device__ __forceinline__ void finish() {}
 };
 
+// Second GEMM with the SwiGLU gate (CODA news article by Synced, epilogue
+// section: the re-parameterisation carries over to SwiGLU).  The B operand is
+// read in the SwiGLU order (swiglu_col in tile_map.hpp): logical column col
+// is a gate column when (col / 8) is even and the matching up column when it
+// is odd, both for output column (col / 16) * 8 + i.  With y = r[row] * acc:
+//   Y_row, gate or up column = round(y)           (only when Y is set)
+//   Z_row, out = round(silu(y_gate) * y_up),  silu(x) = x / (1 + e^-x)
+// Lanes l (gate) and l ^ 1 (up) hold the same row and output columns; the up
+// values cross over with one lane shuffle and the gate lane writes Z.
+template <typename T>
+struct EpiSwiGLU {
+  struct Params {
+    const float* r;  // may be null (no row scale)
+    T* Z;
+    int64_t ldz;
+    T* Y;            // may be null (pre-activation not kept)
+    int64_t ldy;
+    int F;
+  };
+  Params p;
+  RowScalars rs;
+  __device__ __forceinline__ EpiSwiGLU(const Params& p_, int lane, int wm, int, int m0, int, int, int M, int)
+      : p(p_) {
+    if (p.r != nullptr) rs.prefetch(p.r, m0 + wm * kWaveM, lane, M);
+  }
+  __device__ __forceinline__ void apply(int mt, int q, int row, int col, float v[8]) {
+    const float s = p.r != nullptr ? rs.v[mt][q] : 1.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] *= s;
+    const bool up = ((col >> 3) & 1) != 0;
+    const int oc = (col >> 4) << 3;
+    if (p.Y != nullptr) Chunk8<T>::store(p.Y + (int64_t)row * p.ldy + (up ? p.F : 0) + oc, v);
+    float o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = __shfl_xor(v[i], 1);
+    if (!up) {
+      float z[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) z[i] = v[i] / (1.f + expf(-v[i])) * o[i];
+      Chunk8<T>::store(p.Z + (int64_t)row * p.ldz + oc, z);
+    }
+  }
+  __device__ __forceinline__ void end_slab(int) {}
+  __device__ __forceinline__ void finish() {}
+};
+
 // Plain float32 output of the accumulators (the unfused chain's first GEMM).
 struct EpiStoreF32 {
   struct Params {

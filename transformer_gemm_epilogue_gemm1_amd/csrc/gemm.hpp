@@ -136,8 +136,10 @@ struct Dma {
   int kslot;                 // contraction index step between slots (KC: 0, RC: rows per slot)
   uint32_t kstep;            // bytes between consecutive k-tiles
 
+  // split > 0 (row-contiguous operands only): operand rows are read in the
+  // SwiGLU order of swiglu_col(row, split) (nrows counts logical rows).
   __device__ __forceinline__ void init(const void* p, uint32_t span_bytes, int64_t ld, int row0, int nrows,
-                                       int wave, int lane) {
+                                       int wave, int lane, int split = 0) {
     rsrc = make_rsrc(p, span_bytes);
 #pragma unroll
     for (int s = 0; s < kDmaSlots; ++s) {
@@ -151,8 +153,9 @@ struct Dma {
         int k, c;
         dma_rc(s, wave, lane, E, &k, &c);
         const int gr = row0 + c * E;
+        const int pr = split > 0 ? swiglu_col(gr, split) : gr;  // E elements stay contiguous
         if (s == 0) kidx0 = k;  // slot s: contraction row k + s * kslot
-        voff[s] = gr < nrows ? (uint32_t)(((int64_t)k * ld + gr) * (int64_t)sizeof(T)) : kOutOfRange;
+        voff[s] = gr < nrows ? (uint32_t)(((int64_t)k * ld + pr) * (int64_t)sizeof(T)) : kOutOfRange;
       }
     }
     kslot = KC ? 0 : (kWaves * 1024) / rc_row_bytes(E);
@@ -271,6 +274,7 @@ struct GemmArgs {
   const void* b;
   int64_t ldb;
   uint32_t b_span;
+  int b_split;  // > 0: B (row-contiguous) read in the SwiGLU column order, gate/up halves at b_split
 };
 
 // Fragments of one k-tile held in registers.
@@ -348,7 +352,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   Dma<T, A_KC> da;
   Dma<T, B_KC> db;
   da.init(g.a, g.a_span, g.lda, m0, g.M, wave, lane);
-  db.init(g.b, g.b_span, g.ldb, n0, g.N, wave, lane);
+  db.init(g.b, g.b_span, g.ldb, n0, g.N, wave, lane, B_KC ? 0 : g.b_split);
   FragReader<T, A_KC> ra(wm * kWaveM, lane);
   FragReader<T, B_KC> rb(wn * kWaveN, lane);
   f32x4 acc[kFragM][kFragN];

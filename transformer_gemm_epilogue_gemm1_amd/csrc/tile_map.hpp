@@ -112,6 +112,18 @@ CODA_HD int rc_f32_offset(int base, int t, int u, int lane) {
   return rc_offset(k, col >> 2, 4) + (col & 3) * 4;
 }
 
+// SwiGLU operand order.  For the gated second GEMM the B operand is
+// W2 = [W_gate | W_up] (columns [0, F) and [F, 2F)); the kernel reads it in
+// a logical column order that alternates 8-column chunks of the two halves:
+// logical chunk 2m holds gate columns 8m .. 8m+7 and chunk 2m+1 the matching
+// up columns F + 8m .. F + 8m + 7.  An epilogue lane holding logical chunk
+// 2m and its neighbour lane holding 2m+1 then have the gate and up values of
+// the same 8 output columns.  F must be a multiple of 8.
+CODA_HD int swiglu_col(int n, int F) {
+  const int c = n >> 3;
+  return ((c & 1) ? F : 0) + ((c >> 1) << 3) + (n & 7);
+}
+
 // Workgroup -> output tile.  The dispatcher places workgroup b on XCD b % 8;
 // each XCD is given a contiguous range of logical tile ids so that tiles
 // sharing A rows / B columns share that XCD's L2.  Logical ids are then laid
