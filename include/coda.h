@@ -125,6 +125,18 @@ coda_status coda_gemm_rowscale_swiglu(coda_dtype dt, int64_t M, int64_t D, int64
                                       void* Z, int64_t ldz,
                                       void* Y, int64_t ldy, void* stream);
 
+/* Backward through the SwiGLU gate (the article's results section measures
+ * the SwiGLU backward; the formula is the derivative of the reading above):
+ * with s = sigmoid(Y_gate),
+ *   dY_ij     = round(dZ_ij * Y_i,F+j * s (1 + Y_ij (1 - s)))   j < F (gate)
+ *   dY_i,F+j  = round(dZ_ij * Y_ij * s)                          (up)
+ * elementwise, fp32 arithmetic.  dZ: [M,F] (ldz); Y: the kept pre-activation
+ * [M,2F] (ldy); dY: [M,2F] (lddy), the dY that coda_chain_bwd takes.
+ * F >= 1, a multiple of 8.  dY must not overlap dZ or Y. */
+coda_status coda_swiglu_bwd(coda_dtype dt, int64_t M, int64_t F,
+                            const void* dZ, int64_t ldz, const void* Y, int64_t ldy,
+                            void* dY, int64_t lddy, void* stream);
+
 /* Bytes of workspace coda_ref_chain needs: float C[M,D] + X_n[M,D]. */
 size_t coda_ref_chain_workspace_bytes(coda_dtype dt, int64_t M, int64_t D);
 

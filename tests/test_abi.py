@@ -193,6 +193,23 @@ def test_gemm_rowscale_swiglu_empty_is_noop(lib):
     assert swiglu(lib, M=0, X=None, Z=None, Y=None, r=None) == OK
 
 
+@pytest.mark.parametrize("args,status", [
+    ((BF16, 512, 0, DY_, 0, Y_, 0, DA_, 0), SHAPE),
+    ((BF16, 512, 100, DY_, 100, Y_, 200, DA_, 200), SHAPE),
+    ((7, 512, 256, DY_, 256, Y_, 512, DA_, 512), DTYPE),
+    ((BF16, 512, 256, None, 256, Y_, 512, DA_, 512), NULL),
+    ((BF16, 512, 256, DY_, 256, None, 512, DA_, 512), NULL),
+    ((BF16, 512, 256, DY_, 256, Y_, 512, None, 512), NULL),
+    ((BF16, 512, 256, DY_, 256, Y_, 256, DA_, 512), SHAPE),     # ldy < 2F
+    ((BF16, 512, 256, DY_, 260, Y_, 512, DA_, 512), ALIGN),
+    ((BF16, 512, 256, DY_, 256, Y_, 512, Y_ + 1024, 512), ALIAS),
+    ((BF16, 512, 256, DY_, 256, Y_, 512, DY_, 512), ALIAS),
+    ((BF16, 0, 256, None, 256, None, 512, None, 512), OK),
+])
+def test_swiglu_bwd_validation(lib, args, status):
+    assert lib.coda_swiglu_bwd(*args, None) == status
+
+
 def test_chain_bwd_workspace_bytes(lib):
     def al(x):
         return (x + 255) // 256 * 256

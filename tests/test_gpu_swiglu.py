@@ -1,4 +1,5 @@
-"""GPU parity of the SwiGLU epilogue (coda_gemm_rowscale_swiglu) through the C ABI.
+"""GPU parity of the SwiGLU epilogue (coda_gemm_rowscale_swiglu) and of the
+backward through the gate (coda_swiglu_bwd + coda_chain_bwd), through the C ABI.
 
 The chain runs on the GPU up to r and Hg (coda_gemm_res_prms +
 coda_rms_combine), then the gated second GEMM writes Z = silu(Y_gate) * Y_up
@@ -128,3 +129,53 @@ def test_full_size_7b_sampled_rows():
     err = _check(wl, x, o, rows=rows)
     print(f"7b-bf16 SwiGLU sampled-row error {err:.3e}")
     assert torch.isfinite(o["Z"].float()).all().item()
+
+
+# ---- backward through the gate (coda_swiglu_bwd), then the chain's backward ----
+# dZ is the first F columns of the seeded upstream-gradient draw (N(0, 1)).
+
+def _swiglu_train(wl, seed):
+    x = ci.make_inputs(wl, seed=seed, with_dy=True)
+    F = wl.N2 // 2
+    d = {k: dev(v) for k, v in x.items()}
+    dZ = d["dY"][:, :F].contiguous()
+    H, Hg, r, Z, Y = coda.fused_forward_swiglu(d["A"], d["W1"], d["R"], d["g"], d["W2"], wl.eps, keep_y=True)
+    grads = coda.fused_backward_swiglu(dZ, Y, d["A"], d["W1"], d["g"], d["W2"], H, r)
+    torch.cuda.synchronize()
+    return x, dZ, Y, dict(zip(("dA", "dR", "dW1", "dW2", "dg", "dY"), grads))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(3, 136, 264, 264), (257, 256, 512, 384), (513, 512, 1024, 1024)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_swiglu_backward_matches_oracle(shape, dtype):
+    M, K, D, F = shape
+    wl = ci.custom_workload(M, K, D, 2 * F, eps=1e-5 if dtype == "bf16" else 1e-6, dtype=dtype, wl_id=410)
+    x, dZ, Y, out = _swiglu_train(wl, seed=5)
+    dz = host_f32(dZ).astype(np.float64)
+    # stage: dY against host fp64 on the GPU's own dZ and Y (one rounding)
+    dy_host = oracle.swiglu_dy(dz, host_f32(Y).astype(np.float64))
+    assert max_rel(host_f32(out["dY"]), dy_host) <= (2.0 ** -8 if dtype == "bf16" else 2e-6)
+    # end to end: every gradient against the oracle's backward of <dZ, Z>
+    orc = oracle.backward_swiglu(dz, x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps)
+    for k in ("dY", "dA", "dR", "dW1", "dW2", "dg"):
+        err = max_rel(host_f32(out[k]), orc[k])
+        assert err <= tolerance(dtype), f"{k}: error {err:.3e}"
+
+
+@pytest.mark.slow
+def test_swiglu_bwd_full_size_sampled_rows():
+    # the gate's backward at the 7B shape (M = 16384, F = 14336) on sampled rows
+    wl = ci.WORKLOADS["7b-bf16"]
+    F = wl.N2 // 2
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    Y = (torch.randn((wl.M, 2 * F), device="cuda", generator=gen) * 2.0).bfloat16()
+    dZ = torch.randn((wl.M, F), device="cuda", generator=gen).bfloat16()
+    dY = torch.full_like(Y, float("nan"))
+    coda.coda_swiglu_bwd(dZ, Y, dY)
+    torch.cuda.synchronize()
+    rows = torch.tensor([0, 1, 4097, 9000, wl.M - 1], device="cuda")
+    ref = oracle.swiglu_dy(host_f32(dZ[rows]).astype(np.float64), host_f32(Y[rows]).astype(np.float64))
+    assert max_rel(host_f32(dY[rows]), ref) <= 2.0 ** -8
+    assert torch.isfinite(dY.float()).all().item()

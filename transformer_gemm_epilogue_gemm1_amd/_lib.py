@@ -32,6 +32,7 @@ SIGNATURES = {
                                    c_vp, c_i64, c_vp]),
     "coda_gemm_rowscale_swiglu": (c_int, [c_int, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp,
                                           c_vp, c_i64, c_vp, c_i64, c_vp]),
+    "coda_swiglu_bwd": (c_int, [c_int, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
     "coda_ref_chain_workspace_bytes": (c_size, [c_int, c_i64, c_i64]),
     "coda_ref_chain": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64, c_float, c_vp, c_vp, c_vp, c_vp,
                                c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),

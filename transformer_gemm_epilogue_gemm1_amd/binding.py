@@ -132,6 +132,19 @@ def coda_gemm_rowscale_swiglu(X, W2, r: Optional[torch.Tensor], Z, Y: Optional[t
     _lib.check("coda_gemm_rowscale_swiglu", st)
 
 
+def coda_swiglu_bwd(dZ, Y, dY, stream=None) -> None:
+    """dY [M, 2F] from dZ [M, F] through Z = silu(Y_gate) * Y_up."""
+    lib = _lib.load()
+    dt = dZ.dtype
+    M, F = dZ.shape
+    ldz = _mat(dZ, "dZ", dt, (M, F))
+    ldy = _mat(Y, "Y", dt, (M, 2 * F))
+    lddy = _mat(dY, "dY", dt, (M, 2 * F))
+    st = lib.coda_swiglu_bwd(_dtype_code(dZ), M, F, dZ.data_ptr(), ldz, Y.data_ptr(), ldy, dY.data_ptr(), lddy,
+                             _stream(stream))
+    _lib.check("coda_swiglu_bwd", st)
+
+
 def coda_ref_chain_workspace_bytes(dtype: torch.dtype, M: int, D: int) -> int:
     return int(_lib.load().coda_ref_chain_workspace_bytes(_DT[dtype], M, D))
 
@@ -243,3 +256,11 @@ def fused_forward_swiglu(A, W1, R, g, W2, eps: float, keep_y: bool = False, stre
     coda_rms_combine(P, r, D, eps, stream)
     coda_gemm_rowscale_swiglu(Hg, W2, r, Z, Y, stream)
     return H, Hg, r, Z, Y
+
+
+def fused_backward_swiglu(dZ, Y, A, W1, g, W2, H, r, stream=None):
+    """Backward of the chain with the SwiGLU gate: dY through the gate, then
+    the chain's backward; returns (dA, dR, dW1, dW2, dg, dY)."""
+    dY = torch.empty_like(Y)
+    coda_swiglu_bwd(dZ, Y, dY, stream)
+    return fused_backward(dY, A, W1, g, W2, H, r, stream) + (dY,)

@@ -319,6 +319,30 @@ coda_status coda_gemm_rowscale_swiglu(coda_dtype dt, int64_t M, int64_t D, int64
   return gemm_rowscale_swiglu_impl<float>((int)M, (int)D, (int)F, X, ldx, W2, ldw2, r, Z, ldz, Y, ldy, s);
 }
 
+coda_status coda_swiglu_bwd(coda_dtype dt, int64_t M, int64_t F, const void* dZ, int64_t ldz, const void* Y,
+                            int64_t ldy, void* dY, int64_t lddy, void* stream) {
+  coda_status st = check_dims(dt, M, {{"F", F}});
+  if (st != CODA_OK) return st;
+  if (2 * F > kMaxDim) return fail(CODA_ERR_SHAPE, "2F = %lld out of range", (long long)(2 * F));
+  if (M == 0) return ok();
+  const int es = elem_size(dt), E = elems_per_chunk(dt);
+  const Mat mdZ{dZ, M, F, ldz, es, "dZ"}, mY{Y, M, 2 * F, ldy, es, "Y"}, mdY{dY, M, 2 * F, lddy, es, "dY"};
+  for (const Mat* m : {&mdZ, &mY, &mdY})
+    if ((st = check_mat(*m, E)) != CODA_OK) return st;
+  const Mat ins[2] = {mdZ, mY};
+  if ((st = check_alias(&mdY, 1, ins, 2)) != CODA_OK) return st;
+  const int64_t nchunks = M * F / 8;
+  const int blocks = (int)((nchunks + 255) / 256 < 16384 ? (nchunks + 255) / 256 : 16384);
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == CODA_BF16)
+    hipLaunchKernelGGL(swiglu_bwd_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, (const uint16_t*)dZ, ldz,
+                       (const uint16_t*)Y, ldy, (uint16_t*)dY, lddy, (int)F, nchunks);
+  else
+    hipLaunchKernelGGL(swiglu_bwd_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)dZ, ldz,
+                       (const float*)Y, ldy, (float*)dY, lddy, (int)F, nchunks);
+  return launch_status("coda_swiglu_bwd");
+}
+
 size_t coda_ref_chain_workspace_bytes(coda_dtype dt, int64_t M, int64_t D) {
   if ((dt != CODA_BF16 && dt != CODA_F32) || M < 0 || D < 1) return 0;
   const size_t c = (size_t)M * D * 4;

@@ -135,4 +135,33 @@ __global__ __launch_bounds__(256) void dh_finalize_kernel(T* __restrict__ PdH, c
   }
 }
 
+// SwiGLU backward through the gate, elementwise over [M, F]: with
+// Z = silu(Y_gate) * Y_up, s = sigmoid(Y_gate),
+//   dY_gate = dZ * Y_up * s (1 + Y_gate (1 - s))
+//   dY_up   = dZ * Y_gate * s
+// One thread per 8-column chunk; dY[:, :F] and dY[:, F:] written side by side
+// as the [M, 2F] gradient of the second GEMM's output.
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const T* __restrict__ dZ, int64_t ldz,
+                                                         const T* __restrict__ Y, int64_t ldy, T* __restrict__ dY,
+                                                         int64_t lddy, int F, int64_t nchunks) {
+  const int cpr = F / 8;
+  for (int64_t k = blockIdx.x * 256ll + threadIdx.x; k < nchunks; k += (int64_t)gridDim.x * 256) {
+    const int64_t row = k / cpr;
+    const int col = (int)(k - row * cpr) * 8;
+    float dz[8], yg[8], yu[8], dg[8], du[8];
+    Chunk8<T>::load(dZ + row * ldz + col, dz);
+    Chunk8<T>::load(Y + row * ldy + col, yg);
+    Chunk8<T>::load(Y + row * ldy + F + col, yu);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float sg = 1.f / (1.f + expf(-yg[i]));
+      dg[i] = dz[i] * yu[i] * (sg * (1.f + yg[i] * (1.f - sg)));
+      du[i] = dz[i] * (yg[i] * sg);
+    }
+    Chunk8<T>::store(dY + row * lddy + col, dg);
+    Chunk8<T>::store(dY + row * lddy + F + col, du);
+  }
+}
+
 }  // namespace coda
