@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--power-probe-s", type=float, default=2.0,
                     help="seconds of back-to-back forward chains while amd-smi samples socket power and "
                          "gfx clocks (0 disables; skipped when amd-smi is absent)")
+    ap.add_argument("--no-swiglu", action="store_true",
+                    help="skip the SwiGLU-gated chain (forward, and the training step when timing the backward)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward chain (7b-bwd-bf16) and the training-step comparison")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -221,6 +223,93 @@ def bench_forward_shape(wl, stream, steps, warmup, seed):
     return {"shape": {"M": M, "K": K, "D": D, "N2": N2}, "ms_per_step": round(ms, 4), "value": round(tf, 2),
             "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
             "coda_gemm_rowscale_frac": round(g2_tf / PEAK_BF16_TFLOPS, 4)}
+
+
+def bench_swiglu(args, up, stream, with_backward):
+    """The chain with the SwiGLU gate in the second GEMM's epilogue (7B shape,
+    W2 = [W_gate | W_up], F = N2 / 2): the fused forward writing Z only, the
+    PyTorch forward (vendor GEMMs, torch RMSNorm, torch silu), and, when the
+    backward is timed, a training step (forward keeping Y, gate backward,
+    chain backward) beside PyTorch autograd of the same chain."""
+    import torch
+
+    import coda_inputs as ci
+    import transformer_gemm_epilogue_gemm1_amd as coda
+
+    wl = ci.WORKLOADS["7b-bwd-bf16"]
+    x = ci.make_inputs(wl, seed=args.seed)
+    d = {k: up(v) for k, v in x.items()}
+    M, K, D, N2 = wl.M, wl.K, wl.D, wl.N2
+    F = N2 // 2
+    dev, tdt = d["A"].device, d["A"].dtype
+    dZ = d["dY"][:, :F].contiguous()
+    H = torch.empty((M, D), device=dev, dtype=tdt)
+    Hg = torch.empty_like(H)
+    P = torch.empty((coda.coda_prms_num_partials(tdt, D), M), device=dev, dtype=torch.float32)
+    r = torch.empty((M,), device=dev, dtype=torch.float32)
+    Z = torch.empty((M, F), device=dev, dtype=tdt)
+    Y = torch.empty((M, N2), device=dev, dtype=tdt)
+
+    def fwd(keep_y):
+        coda.coda_gemm_res_prms(d["A"], d["W1"], d["R"], d["g"], H, Hg, P, stream)
+        coda.coda_rms_combine(P, r, D, wl.eps, stream)
+        coda.coda_gemm_rowscale_swiglu(Hg, d["W2"], r, Z, Y if keep_y else None, stream)
+
+    n = max(5, args.steps // 2)
+    w = max(2, args.warmup // 2)
+    fwd_ms = time_ms(lambda: fwd(False), stream, n, w)
+    gated_ms = time_ms(lambda: coda.coda_gemm_rowscale_swiglu(Hg, d["W2"], r, Z, None, stream), stream, n, w)
+    plain_ms = time_ms(lambda: coda.coda_gemm_rowscale(Hg, d["W2"], r, Y, stream), stream, n, w)
+    out = {"workload": f"7b-bf16 with the gate: M={M} K={K} D={D} F={F} (W2 {D}x{N2} = gate|up)",
+           "forward_ms": round(fwd_ms, 4),
+           "forward_tflops": round(wl.fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
+           "coda_gemm_rowscale_swiglu_ms": round(gated_ms, 4),
+           "coda_gemm_rowscale_same_inputs_ms": round(plain_ms, 4)}
+    gf = d["g"].float()
+    if not args.no_torch_chain:
+        def torch_fwd():
+            Ht = torch.addmm(d["R"], d["A"], d["W1"])
+            hf = Ht.float()
+            rt = torch.rsqrt(hf.square().mean(dim=1, keepdim=True) + wl.eps)
+            Yt = torch.matmul((hf * rt * gf).to(tdt), d["W2"])
+            return torch.nn.functional.silu(Yt[:, :F]) * Yt[:, F:]
+
+        t_ms = time_ms(torch_fwd, stream, n, w)
+        out["torch_forward_ms"] = round(t_ms, 4)
+        out["forward_speedup_vs_torch"] = round(t_ms / fwd_ms, 4)
+    if with_backward:
+        dA = torch.empty((M, K), device=dev, dtype=tdt)
+        dR = torch.empty((M, D), device=dev, dtype=tdt)
+        dW1 = torch.empty((K, D), device=dev, dtype=tdt)
+        dW2 = torch.empty((D, N2), device=dev, dtype=tdt)
+        dg = torch.empty((D,), device=dev, dtype=torch.float32)
+        dY = torch.empty((M, N2), device=dev, dtype=tdt)
+        ws = torch.empty((coda.coda_chain_bwd_workspace_bytes(tdt, M, K, D, N2),), device=dev, dtype=torch.uint8)
+
+        def train():
+            fwd(True)
+            coda.coda_swiglu_bwd(dZ, Y, dY, stream)
+            coda.coda_chain_bwd(dY, d["A"], d["W1"], d["g"], d["W2"], H, r, dA, dR, dW1, dW2, dg, ws, stream)
+
+        tr_ms = time_ms(train, stream, n, w)
+        out["train_step_ms"] = round(tr_ms, 4)
+        if not args.no_torch_chain:
+            leaves = {k: d[k].clone().requires_grad_(True) for k in ("A", "W1", "R", "g", "W2")}
+
+            def torch_train():
+                for t in leaves.values():
+                    t.grad = None
+                Ht = torch.addmm(leaves["R"], leaves["A"], leaves["W1"])
+                Xn = torch.nn.functional.rms_norm(Ht.float(), (D,), leaves["g"].float(), wl.eps).to(tdt)
+                Yt = torch.matmul(Xn, leaves["W2"])
+                Zt = torch.nn.functional.silu(Yt[:, :F]) * Yt[:, F:]
+                Zt.backward(dZ)
+
+            t_ms = time_ms(torch_train, stream, n, w)
+            out["torch_autograd_train_step_ms"] = round(t_ms, 4)
+            out["train_step_speedup_vs_torch_autograd"] = round(t_ms / tr_ms, 4)
+            del leaves
+    return out
 
 
 def bench_backward(args, up, stream):
@@ -475,6 +564,9 @@ def main():
 
     if not args.no_backward:
         out["backward"] = bench_backward(args, up, stream)
+
+    if not args.no_swiglu:
+        out["swiglu"] = bench_swiglu(args, up, stream, with_backward=not args.no_backward)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)

@@ -117,7 +117,8 @@ coda_status coda_gemm_rowscale(coda_dtype dt, int64_t M, int64_t D, int64_t N2,
  * pre-activation never goes through HBM unless asked for.
  *   X: [M,D] (ldx); W2: [D,2F] (ldw2 >= 2F); r: float[M] or NULL (no row
  *   scale); Z: [M,F] (ldz); Y: [M,2F] (ldy) or NULL.
- * F >= 1, a multiple of 8.  Z and Y must not overlap X, W2, r or each other. */
+ * F >= 1, a multiple of 32 (the gate and up halves are read in interleaved
+ * 32-column runs).  Z and Y must not overlap X, W2, r or each other. */
 coda_status coda_gemm_rowscale_swiglu(coda_dtype dt, int64_t M, int64_t D, int64_t F,
                                       const void* X, int64_t ldx,
                                       const void* W2, int64_t ldw2,

@@ -163,30 +163,37 @@ static void check_rc(int E) {
       }
 }
 
-// SwiGLU column order: a bijection of [0, 2F) onto itself whose chunk pair
-// (2m, 2m+1) holds gate columns 8m.. and up columns F + 8m.., with every DMA
-// chunk (8 bf16 or 4 fp32 elements) contiguous in memory.
+// SwiGLU column order: a bijection of [0, 2F) onto itself whose run pair
+// (2m, 2m+1) holds gate columns R m.. and up columns F + R m.. (R =
+// kSwiGLURun), with every DMA chunk (8 bf16 or 4 fp32 elements) contiguous in
+// memory, and output columns / up flags consistent with it.
 static void check_swiglu_col() {
-  const int Fs[] = {8, 16, 24, 256, 264, 1000, 14336};
+  const int R = kSwiGLURun;
+  const int Fs[] = {32, 64, 96, 256, 288, 1024, 14336};
   for (int F : Fs) {
     std::vector<int> seen(2 * F, 0);
     for (int n = 0; n < 2 * F; ++n) {
       const int p = swiglu_col(n, F);
       CHECK(p >= 0 && p < 2 * F, "swiglu_col(%d, %d) = %d out of range", n, F, p);
       if (p >= 0 && p < 2 * F) seen[p]++;
-      const int c = n / 8, m = c / 2, i = n % 8;
-      CHECK(p == (c % 2 ? F : 0) + 8 * m + i, "swiglu_col(%d, %d) = %d", n, F, p);
+      const int c = n / R, m = c / 2, i = n % R;
+      CHECK(p == (c % 2 ? F : 0) + R * m + i, "swiglu_col(%d, %d) = %d", n, F, p);
+      CHECK(swiglu_is_up(n) == (c % 2 == 1), "swiglu_is_up(%d)", n);
+      CHECK(swiglu_out_col(n) == R * m + i && p == (swiglu_is_up(n) ? F : 0) + swiglu_out_col(n), "swiglu_out_col(%d)", n);
       if (n % 4 != 0) CHECK(p == swiglu_col(n - 1, F) + 1, "SwiGLU chunk not contiguous at %d", n);
     }
     for (int p = 0; p < 2 * F; ++p) CHECK(seen[p] == 1, "SwiGLU column %d of F=%d hit %d times", p, F, seen[p]);
   }
-  // the epilogue pairs lane l (gate) with lane l ^ 1 (up): same output columns
+  // the epilogue pairs lane l (gate) with lane l ^ kSwiGLUPartner (up): same
+  // row group (l / 8) and the same output columns
   for (int n0 = 0; n0 < 1024; n0 += kTileN)
     for (int wn = 0; wn < 4; ++wn)
-      for (int lane = 0; lane < 64; lane += 2) {
-        const int col = n0 + wn * kWaveN + (lane & 7) * 8, col_up = n0 + wn * kWaveN + ((lane ^ 1) & 7) * 8;
-        CHECK(((col >> 3) & 1) == 0 && ((col_up >> 3) & 1) == 1, "SwiGLU lane parity");
-        CHECK((col >> 4) == (col_up >> 4), "SwiGLU lane pair covers different output columns");
+      for (int lane = 0; lane < 64; ++lane) {
+        const int pl = lane ^ kSwiGLUPartner;
+        const int col = n0 + wn * kWaveN + (lane & 7) * 8, col_p = n0 + wn * kWaveN + (pl & 7) * 8;
+        CHECK((pl >> 3) == (lane >> 3), "SwiGLU partner in another row group");
+        CHECK(swiglu_is_up(col) != swiglu_is_up(col_p), "SwiGLU partner of the same kind");
+        CHECK(swiglu_out_col(col) == swiglu_out_col(col_p), "SwiGLU partner covers different output columns");
       }
 }
 

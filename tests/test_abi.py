@@ -170,6 +170,7 @@ def swiglu(lib, dt=BF16, M=512, D=256, F=256, X=H_, ldx=None, W2=W2_, ldw2=None,
     (dict(dt=4), DTYPE),
     (dict(F=0), SHAPE),
     (dict(F=12), SHAPE),
+    (dict(F=264), SHAPE),         # not a multiple of 32
     (dict(D=20), SHAPE),
     (dict(X=None), NULL),
     (dict(W2=None), NULL),

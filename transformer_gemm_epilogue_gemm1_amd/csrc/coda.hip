@@ -301,6 +301,7 @@ coda_status coda_gemm_rowscale_swiglu(coda_dtype dt, int64_t M, int64_t D, int64
   coda_status st = check_dims(dt, M, {{"D", D}, {"F", F}});
   if (st != CODA_OK) return st;
   if (2 * F > kMaxDim) return fail(CODA_ERR_SHAPE, "2F = %lld out of range", (long long)(2 * F));
+  if (F % kSwiGLURun != 0) return fail(CODA_ERR_SHAPE, "F = %lld is not a multiple of %d", (long long)F, kSwiGLURun);
   if (M == 0) return ok();
   const int es = elem_size(dt), E = elems_per_chunk(dt);
   const Mat mX{X, M, D, ldx, es, "X"}, mW2{W2, D, 2 * F, ldw2, es, "W2"}, mZ{Z, M, F, ldz, es, "Z"};

@@ -162,12 +162,17 @@ struct EpiRowScale {
 // Second GEMM with the SwiGLU gate (CODA news article by Synced, epilogue
 // section: the re-parameterisation carries over to SwiGLU).  The B operand is
 // read in the SwiGLU order (swiglu_col in tile_map.hpp): logical column col
-// is a gate column when (col / 8) is even and the matching up column when it
-// is odd, both for output column (col / 16) * 8 + i.  With y = r[row] * acc:
+// is a gate or an up column (swiglu_is_up) of output column
+// swiglu_out_col(col) + i.  With y = r[row] * acc:
 //   Y_row, gate or up column = round(y)           (only when Y is set)
 //   Z_row, out = round(silu(y_gate) * y_up),  silu(x) = x / (1 + e^-x)
-// Lanes l (gate) and l ^ 1 (up) hold the same row and output columns; the up
-// values cross over with one lane shuffle and the gate lane writes Z.
+// Lanes l (gate) and l ^ kSwiGLUPartner (up) hold the same row and output
+// columns; the up values cross over with one lane shuffle and the gate lane
+// writes Z.  silu uses the hardware exp2 and reciprocal (v_exp_f32,
+// v_rcp_f32, about 1 ulp each): the library expf and IEEE division would
+// inline tens of instructions per value into an epilogue that runs once per
+// tile and is fetched cold.  Large |x| behave: e^-x -> inf gives 0, -> 0
+// gives x.
 template <typename T>
 struct EpiSwiGLU {
   struct Params {
@@ -188,16 +193,19 @@ struct EpiSwiGLU {
     const float s = p.r != nullptr ? rs.v[mt][q] : 1.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] *= s;
-    const bool up = ((col >> 3) & 1) != 0;
-    const int oc = (col >> 4) << 3;
+    const bool up = swiglu_is_up(col);
+    const int oc = swiglu_out_col(col);
     if (p.Y != nullptr) Chunk8<T>::store(p.Y + (int64_t)row * p.ldy + (up ? p.F : 0) + oc, v);
     float o[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = __shfl_xor(v[i], 1);
+    for (int i = 0; i < 8; ++i) o[i] = __shfl_xor(v[i], kSwiGLUPartner);
     if (!up) {
       float z[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) z[i] = v[i] / (1.f + expf(-v[i])) * o[i];
+      for (int i = 0; i < 8; ++i) {
+        const float e = __builtin_amdgcn_exp2f(v[i] * -1.4426950408889634f);  // e^-x
+        z[i] = v[i] * __builtin_amdgcn_rcpf(1.f + e) * o[i];
+      }
       Chunk8<T>::store(p.Z + (int64_t)row * p.ldz + oc, z);
     }
   }

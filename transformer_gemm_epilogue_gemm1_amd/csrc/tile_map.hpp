@@ -114,15 +114,23 @@ CODA_HD int rc_f32_offset(int base, int t, int u, int lane) {
 
 // SwiGLU operand order.  For the gated second GEMM the B operand is
 // W2 = [W_gate | W_up] (columns [0, F) and [F, 2F)); the kernel reads it in
-// a logical column order that alternates 8-column chunks of the two halves:
-// logical chunk 2m holds gate columns 8m .. 8m+7 and chunk 2m+1 the matching
-// up columns F + 8m .. F + 8m + 7.  An epilogue lane holding logical chunk
-// 2m and its neighbour lane holding 2m+1 then have the gate and up values of
-// the same 8 output columns.  F must be a multiple of 8.
+// a logical column order that alternates kSwiGLURun-column runs of the two
+// halves: logical run 2m holds gate columns kSwiGLURun m .. + kSwiGLURun - 1
+// and run 2m+1 the matching up columns F + kSwiGLURun m ...  Runs of 32
+// columns keep 4 consecutive lanes of a direct load on one contiguous 64-byte
+// segment.  An epilogue lane holding 8 columns of run 2m and lane l ^ 4
+// (8 columns further in run 2m+1) then have the gate and up values of the
+// same 8 output columns.  F must be a multiple of kSwiGLURun.
+constexpr int kSwiGLURun = 32;
 CODA_HD int swiglu_col(int n, int F) {
-  const int c = n >> 3;
-  return ((c & 1) ? F : 0) + ((c >> 1) << 3) + (n & 7);
+  const int c = n / kSwiGLURun;
+  return ((c & 1) ? F : 0) + (c >> 1) * kSwiGLURun + n % kSwiGLURun;
 }
+// Output column of logical column n (gate or up), and whether n is an up column.
+CODA_HD int swiglu_out_col(int n) { return (n / (2 * kSwiGLURun)) * kSwiGLURun + n % kSwiGLURun; }
+CODA_HD bool swiglu_is_up(int n) { return ((n / kSwiGLURun) & 1) != 0; }
+// The epilogue lane holding the up values for a gate lane (and vice versa).
+constexpr int kSwiGLUPartner = kSwiGLURun / 8;
 
 // Workgroup -> output tile.  The dispatcher places workgroup b on XCD b % 8;
 // each XCD is given a contiguous range of logical tile ids so that tiles
