@@ -265,6 +265,11 @@ __device__ __forceinline__ void drain_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Orders a wavefront's own LDS accesses for the compiler.  The hardware
+// performs one wavefront's LDS instructions in order, so a slab that only its
+// own wavefront touches needs no barrier between writing and reading it.
+__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
 struct GemmArgs {
   int M, N, K;
   int tiles_m, tiles_n, group_m;
@@ -323,7 +328,8 @@ __device__ __forceinline__ void kstep(char* const (&st)[kStages], const Dma<T, A
 }
 
 // The epilogue sees the wavefront's accumulators 16 rows at a time, staged
-// through LDS so that each lane holds 8 consecutive columns of one row:
+// through a slab of LDS private to the wavefront (after drain_barrier the
+// stages are free), so that each lane holds 8 consecutive columns of one row:
 // lane l, slot q (0..1) gets row (l/8 + 8q) of the 16-row slab and columns
 // [8*(l%8), 8*(l%8)+8) of the wavefront's 64.  Epi provides
 //   apply(mt, q, row, col, v)  for rows < M and columns < N (col % 8 == 0);
@@ -403,7 +409,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int nt = 0; nt < kFragN; ++nt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) slab[(4 * (lane >> 4) + e) * kEpiPitch + nt * 16 + (lane & 15)] = acc[mt][nt][e];
-    __syncthreads();
+    wave_lds_fence();
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int rl = (lane >> 3) + 8 * q;
@@ -414,7 +420,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       if (row < g.M && col < g.N) epi.apply(mt, q, row, col, v);
     }
     epi.end_slab(row_base + mt * 16);
-    __syncthreads();
+    wave_lds_fence();  // the slab's reads are done before the next slab overwrites it
   }
   epi.finish();
 }
