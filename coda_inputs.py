@@ -15,6 +15,11 @@ Value recipe (every workload):
     dY ~ N(0, 1)                       upstream gradient (backward only)
 drawn in float32 from numpy's PCG64 seeded by SeedSequence([seed, wl_id,
 tensor_id]), then rounded to nearest-even bfloat16 for the bf16 workloads.
+
+fp8 workloads (make_inputs_fp8) draw the same values and store A, W1 and W2
+as OCP e4m3 codes with float32 scales: A per row, W1 and W2 per output
+channel, each scale = (max |value| over the scaled vector) / 448, the
+weights transposed to [N, K] (contraction contiguous).  R and g stay bf16.
 """
 from __future__ import annotations
 
@@ -61,6 +66,8 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("70b-bf16", 3, 8192, 8192, 8192, 57344, 1e-5, "bf16"),
         # backward of the 7B-style chain
         Workload("7b-bwd-bf16", 4, 16384, 4096, 4096, 28672, 1e-5, "bf16", True),
+        # 7B-style chain with fp8 (e4m3) GEMM operands
+        Workload("7b-fp8", 5, 16384, 4096, 4096, 28672, 1e-5, "fp8"),
     ]
 }
 
@@ -139,3 +146,56 @@ def make_inputs(wl: Workload, seed: int = 0, with_dy: Optional[bool] = None) -> 
     if with_dy if with_dy is not None else wl.backward:
         out["dY"] = HostTensor(_draw(seed, wl, "dY", (M, N2), 1.0), wl.dtype)
     return out
+
+
+# ---- fp8 (OCP e4m3: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+# largest finite 448, no infinities, S.1111.111 is NaN) ----
+
+E4M3_MAX = 448.0
+
+
+def e4m3_values(codes: np.ndarray) -> np.ndarray:
+    """Exact float32 values of e4m3 codes (NaN for the two NaN codes)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int32)
+    e = (c >> 3) & 0xF
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.exp2(e - 10.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(c & 0x80, -mag, mag).astype(np.float32)
+
+
+def e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to nearest-even e4m3 codes, saturating at +-448."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    # spacing of the representable values around a: 2^(e - 3), subnormals 2^-9
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    step = np.exp2(e - 3.0)
+    q = np.round(a / step) * step            # numpy rounds halves to even
+    q = np.minimum(q, E4M3_MAX)
+    eq = np.floor(np.log2(np.maximum(q, 2.0 ** -6)))
+    norm = q >= 2.0 ** -6
+    code = np.where(norm, ((eq + 7).astype(np.int64) << 3) + (q / np.exp2(eq - 3.0) - 8).astype(np.int64),
+                    (q / 2.0 ** -9).astype(np.int64))
+    sign = np.signbit(x).astype(np.int64) << 7
+    return (code | sign).astype(np.uint8)
+
+
+def _quantize_rows(x: np.ndarray):
+    """Per-row e4m3 codes and float32 scales: scale = max|row| / 448."""
+    amax = np.max(np.abs(x), axis=1).astype(np.float32)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    return e4m3_codes(x / scale[:, None]), scale
+
+
+def make_inputs_fp8(wl: Workload, seed: int = 0) -> Dict[str, object]:
+    """fp8 inputs of one workload (same draws as make_inputs):
+    A8[M,K] codes + sa[M]; W1t8[D,K] codes (W1 transposed) + sw1[D];
+    W2t8[N2,D] codes (W2 transposed) + sw2[N2]; R[M,D], g[D] bf16."""
+    M, K, D, N2 = wl.M, wl.K, wl.D, wl.N2
+    A8, sa = _quantize_rows(_draw(seed, wl, "A", (M, K), 1.0))
+    W1t8, sw1 = _quantize_rows(np.ascontiguousarray(_draw(seed, wl, "W1", (K, D), 1.0 / np.sqrt(K)).T))
+    W2t8, sw2 = _quantize_rows(np.ascontiguousarray(_draw(seed, wl, "W2", (D, N2), 1.0 / np.sqrt(D)).T))
+    return {"A8": A8, "sa": sa, "W1t8": W1t8, "sw1": sw1, "W2t8": W2t8, "sw2": sw2,
+            "R": HostTensor(_draw(seed, wl, "R", (M, D), 1.0), "bf16"),
+            "g": HostTensor(_draw(seed, wl, "g", (D,), 0.1, 1.0), "bf16")}

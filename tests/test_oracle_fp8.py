@@ -1,0 +1,181 @@
+"""Pins for the fp64 CPU oracle of the fp8 chain (CPU only).
+
+The pages give no fp8 recipe (the CODA news article by Synced names FP8 only
+as making matrix products faster); the readings are in oracle/fp8.py.  Pins:
+the e4m3 code table against values the OCP format definition fixes, the
+encoder's round trip, ties and saturation, two independent encoders agreeing,
+bf16 rounding against torch's cast, a pure-Python brute force of the whole
+fp8 chain, a lossless special case that reduces to the plain chain's oracle,
+a hand-worked case for the quantisation of the stored bf16 H, and planted
+mistakes that the brute force or the hand-worked case rejects.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import coda_inputs as ci
+import oracle
+
+
+def test_code_table_fixed_values():
+    dec = oracle.e4m3_decode
+    assert dec(0x38) == 1.0 and dec(0xB8) == -1.0
+    assert dec(0x7E) == 448.0 and dec(0xFE) == -448.0          # largest finite
+    assert dec(0x08) == 2.0 ** -6 and dec(0x01) == 2.0 ** -9      # smallest normal / subnormal
+    assert dec(0x07) == 7 * 2.0 ** -9
+    assert dec(0x40) == 2.0 and dec(0x3C) == 1.5 and dec(0x39) == 1.125
+    assert dec(0x00) == 0.0 and np.signbit(dec(0x80))
+    assert np.isnan(dec(0x7F)) and np.isnan(dec(0xFF))
+    pos = dec(np.arange(0x7F))
+    assert np.all(np.diff(pos) > 0)                               # increasing, 127 distinct
+
+
+def test_encoder_round_trip_ties_and_saturation():
+    codes = np.arange(0x7F)
+    vals = oracle.e4m3_decode(codes)
+    np.testing.assert_array_equal(oracle.e4m3_encode(vals), codes)
+    np.testing.assert_array_equal(oracle.e4m3_encode(-vals[1:]), codes[1:] | 0x80)
+    mids = (vals[:-1] + vals[1:]) / 2
+    got = oracle.e4m3_encode(mids)
+    want = np.where(codes[:-1] % 2 == 0, codes[:-1], codes[1:])   # halfway: the even code
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(oracle.e4m3_encode(np.nextafter(mids, 0)), codes[:-1])
+    np.testing.assert_array_equal(oracle.e4m3_encode(np.nextafter(mids, 1e9)), codes[1:])
+    np.testing.assert_array_equal(oracle.e4m3_encode([448.0, 464.0, 1e6, -1e30]), [0x7E, 0x7E, 0x7E, 0xFE])
+    assert oracle.e4m3_encode([np.nan])[0] == 0x7F
+
+
+def test_two_independent_encoders_agree():
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(200000) * 40, rng.standard_normal(20000) * 1e-3,
+                        oracle.e4m3_decode(np.arange(0x7F))]).astype(np.float32)
+    np.testing.assert_array_equal(oracle.e4m3_encode(x), ci.e4m3_codes(x))
+
+
+def test_bf16_round_is_torch_cast():
+    rng = np.random.default_rng(2)
+    x = np.concatenate([rng.standard_normal(100000) * 10, [1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8)]])
+    x = x.astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.bf16_round(x), ref)
+
+
+def _case(seed, M, K, D, N2):
+    wl = ci.custom_workload(M, K, D, N2, dtype="fp8", wl_id=seed)
+    x = ci.make_inputs_fp8(wl, seed=seed)
+    return wl, x
+
+
+def _args(x):
+    return (x["A8"], x["sa"], x["W1t8"], x["sw1"], x["R"].f32, x["g"].f32, x["W2t8"], x["sw2"])
+
+
+def _brute(A8, sa, W1t8, sw1, R, g, W2t8, sw2, eps):
+    """Pure-Python fp8 chain: the code table from the format definition,
+    math.fsum sums, float32 product and nearest-even e4m3 by direct search."""
+    def val(c):
+        s = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 15, c & 7
+        return s * (m / 8 * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+    pos = [val(c) for c in range(0x7F)]
+
+    def enc(x):
+        a = min(abs(x), 448.0)
+        best = min(range(0x7F), key=lambda c: (abs(pos[c] - a), c % 2))
+        return best | (0x80 if math.copysign(1.0, x) < 0 else 0)
+
+    M, K = len(A8), len(A8[0])
+    D, N2 = len(W1t8), len(W2t8)
+    H = [[math.fsum([val(A8[i][k]) * float(sa[i]) * val(W1t8[j][k]) * float(sw1[j]) for k in range(K)]
+                    + [float(R[i][j])]) for j in range(D)] for i in range(M)]
+    Hb = [[float(torch.tensor(h, dtype=torch.float64).to(torch.bfloat16)) for h in row] for row in H]
+    Hg8 = [[enc(float(np.float32(np.float32(Hb[i][j]) * np.float32(g[j])))) for j in range(D)] for i in range(M)]
+    r = [1.0 / math.sqrt(math.fsum(h * h for h in H[i]) / D + eps) for i in range(M)]
+    Y = [[r[i] * math.fsum(val(Hg8[i][j]) * val(W2t8[n][j]) * float(sw2[n]) for j in range(D))
+          for n in range(N2)] for i in range(M)]
+    return np.array(H), np.array(Hg8, dtype=np.uint8), np.array(r), np.array(Y)
+
+
+@pytest.mark.parametrize("shape", [(1, 16, 8, 8), (3, 32, 16, 8), (5, 16, 24, 16)])
+def test_brute_force(shape):
+    wl, x = _case(40 + sum(shape), *shape)
+    out = oracle.forward_fp8(*_args(x), wl.eps)
+    H, Hg8, r, Y = _brute(*(np.asarray(a).tolist() if np.asarray(a).ndim == 2 else np.asarray(a) for a in _args(x)),
+                          wl.eps)
+    np.testing.assert_allclose(out["H"], H, rtol=1e-13, atol=1e-14)
+    np.testing.assert_array_equal(out["Hg8"], Hg8)
+    np.testing.assert_allclose(out["r"], r, rtol=1e-13)
+    np.testing.assert_allclose(out["Y"], Y, rtol=1e-12, atol=1e-13)
+
+
+def test_lossless_case_reduces_to_the_plain_chain():
+    # small-integer codes, unit scales, g = 1 and integer R: every H g is an
+    # integer of magnitude < 16, exactly representable in e4m3, so the fp8
+    # chain equals the plain oracle on the dequantised operands
+    rng = np.random.default_rng(5)
+    M, K, D, N2 = 4, 8, 16, 12
+    enc = {v: int(oracle.e4m3_encode([float(v)])[0]) for v in range(-2, 3)}
+    A = rng.integers(-1, 2, size=(M, K))
+    W1t = rng.integers(-1, 2, size=(D, K))
+    W2t = rng.integers(-2, 3, size=(N2, D))
+    R = rng.integers(-3, 4, size=(M, D)).astype(np.float64)
+    to8 = np.vectorize(lambda v: enc[int(v)])
+    out = oracle.forward_fp8(to8(A).astype(np.uint8), np.ones(M), to8(W1t).astype(np.uint8), np.ones(D), R,
+                             np.ones(D), to8(W2t).astype(np.uint8), np.ones(N2), 1e-5)
+    ref = oracle.forward(A.astype(float), W1t.T.astype(float), R, np.ones(D), W2t.T.astype(float), 1e-5)
+    assert np.all(np.abs(out["H"]) < 16)
+    np.testing.assert_array_equal(out["Hb"], ref["H"])
+    np.testing.assert_allclose(out["Y"], ref["Y"], rtol=1e-13, atol=1e-13)
+
+
+def _hand_case():
+    # K = 1: A = 1.0 (code 0x38, sa 1), W1 = 2^-9 (code 0x01) with sw1 0.5,
+    # R = 1.0625, g = 1: H = 1.0625 + 2^-10.  The stored bf16 H is 1.0625
+    # (spacing 2^-7 near 1), halfway between e4m3 1.0 and 1.125, so the
+    # even code 0x38 (1.0); the unrounded H would give 0x39 (1.125).
+    return (np.array([[0x38]], np.uint8), np.array([1.0], np.float32), np.array([[0x01]], np.uint8),
+            np.array([0.5], np.float32), np.array([[1.0625]]), np.array([1.0]),
+            np.array([[0x38]], np.uint8), np.array([1.0], np.float32))
+
+
+def test_quantises_the_stored_bf16_h():
+    out = oracle.forward_fp8(*_hand_case(), 0.0)
+    assert out["H"][0, 0] == 1.0625 + 2.0 ** -10
+    assert out["Hb"][0, 0] == 1.0625
+    assert out["Hg8"][0, 0] == 0x38
+    assert out["Y"][0, 0] == pytest.approx(1.0 / (1.0625 + 2.0 ** -10), rel=1e-15)   # r * 1.0 * 1.0
+
+
+def _mutant_codes(kind, a, eps):
+    A8, sa, W1t8, sw1, R, g, W2t8, sw2 = a
+    W1 = (oracle.e4m3_decode(W1t8) * sw1[:, None]).T
+    A = oracle.e4m3_decode(A8) * sa[:, None]
+    if kind == "scale_columns_of_A":
+        A = oracle.e4m3_decode(A8) * np.resize(sa, A8.shape[1])[None, :]
+    if kind == "weights_not_transposed":
+        W1 = (oracle.e4m3_decode(W1t8) * sw1[:, None]).reshape(W1.shape)
+    H = A @ W1 + R
+    prod = H if kind == "no_bf16_before_quantising" else oracle.bf16_round(H)
+    prod = (np.asarray(prod, dtype=np.float32) * np.asarray(g, np.float32)).astype(np.float32)
+    codes = oracle.e4m3_encode(prod)
+    if kind == "round_down":
+        v = oracle.e4m3_decode(codes)
+        codes = np.where(np.abs(v) > np.abs(prod), np.where(codes & 0x7F, codes - 1, codes), codes).astype(np.uint8)
+    r = 1.0 / np.sqrt(np.mean(H * H, axis=1) + eps)
+    return codes, r[:, None] * (oracle.e4m3_decode(codes) @ (oracle.e4m3_decode(W2t8) * sw2[:, None]).T)
+
+
+@pytest.mark.parametrize("kind", ["no_bf16_before_quantising", "scale_columns_of_A", "weights_not_transposed",
+                                  "round_down"])
+def test_pins_reject_planted_mistakes(kind):
+    if kind == "no_bf16_before_quantising":
+        codes, _ = _mutant_codes(kind, _hand_case(), 0.0)
+        assert codes[0, 0] != oracle.forward_fp8(*_hand_case(), 0.0)["Hg8"][0, 0] == 0x38
+        return
+    wl, x = _case(77, 3, 16, 16, 8)
+    a = _args(x)
+    _, Hg8, _, Y = _brute(*(np.asarray(v).tolist() if np.asarray(v).ndim == 2 else np.asarray(v) for v in a), wl.eps)
+    codes, Ym = _mutant_codes(kind, a, wl.eps)
+    assert (not np.array_equal(codes, Hg8)) or np.max(np.abs(Ym - Y)) > 1e-9
