@@ -138,6 +138,41 @@ coda_status coda_swiglu_bwd(coda_dtype dt, int64_t M, int64_t F,
                             const void* dZ, int64_t ldz, const void* Y, int64_t ldy,
                             void* dY, int64_t lddy, void* stream);
 
+/* ---- fp8 operands -------------------------------------------------------
+ * The article's opening section notes that FP8 makes the matrix products
+ * faster while the memory-bound operations around them do not shrink, so
+ * fusing them matters more at low precision; it gives no fp8 recipe.  The
+ * one taken here: GEMM operands are OCP e4m3 codes (1 sign, 4 exponent bits,
+ * bias 7, 3 mantissa bits; largest finite 448; no infinities) with float32
+ * dequantisation scales, A per row and the weights per output channel, the
+ * weights stored transposed ([N, K], contraction contiguous).  H stays bf16;
+ * the second GEMM's operand is H g quantised without a scale.  Products run
+ * on v_mfma_f32_32x32x64_f8f6f4 with fp32 accumulation.  Sizes: K, D, N2
+ * multiples of 16; e4m3 leading dimensions multiples of 16 elements, bf16
+ * ones multiples of 8. */
+
+/* First GEMM, fp8 operands:
+ *   H_ij   = round_bf16((acc_ij * sa_i) * sw1_j + R_ij)     acc = sum_k A8_ik W1t8_jk
+ *   Hg8_ij = e4m3_rne(clamp(float(H_ij) * g_j, -448, 448))  (float32 product)
+ *   partials as coda_gemm_res_prms (coda_prms_num_partials(CODA_BF16, D) rows)
+ *   A8: e4m3 [M,K] (lda); sa: float[M]; W1t8: e4m3 [D,K] (ldw1t); sw1: float[D],
+ *   16-byte aligned; R, g, H: bf16; Hg8: e4m3 [M,D] (ldhg). */
+coda_status coda_gemm_res_prms_fp8(int64_t M, int64_t K, int64_t D,
+                                   const void* A8, int64_t lda, const float* sa,
+                                   const void* W1t8, int64_t ldw1t, const float* sw1,
+                                   const void* R, int64_t ldr, const void* g,
+                                   void* H, int64_t ldh, void* Hg8, int64_t ldhg,
+                                   float* partials, void* stream);
+
+/* Second GEMM, fp8 operands, deferred row scale:
+ *   Y_ik = round_bf16((acc_ik * r_i) * sw2_k)    acc = sum_j X8_ij W2t8_kj
+ *   X8: e4m3 [M,D] (ldx), e.g. Hg8; W2t8: e4m3 [N2,D] (ldw2t); sw2: float[N2],
+ *   16-byte aligned; r: float[M] or NULL; Y: bf16 [M,N2] (ldy). */
+coda_status coda_gemm_rowscale_fp8(int64_t M, int64_t D, int64_t N2,
+                                   const void* X8, int64_t ldx,
+                                   const void* W2t8, int64_t ldw2t, const float* sw2,
+                                   const float* r, void* Y, int64_t ldy, void* stream);
+
 /* Bytes of workspace coda_ref_chain needs: float C[M,D] + X_n[M,D]. */
 size_t coda_ref_chain_workspace_bytes(coda_dtype dt, int64_t M, int64_t D);
 

@@ -197,6 +197,44 @@ static void check_swiglu_col() {
       }
 }
 
+// fp8 fragments: 32-row fragments read as two 16-byte chunks per lane; the
+// lane gets operand row base + 32 t + l % 32 and k-bytes [32 (l/32), +32);
+// every 16-lane pass of a read hits each bank once; reads stay in the tile;
+// the second chunk is the first XOR 16 bytes, fragment t is 2 KiB further.
+static void check_kc8() {
+  for (int base = 0; base < kTileM; base += kWaveM)
+    for (int t = 0; t < kFrag8M && base + 32 * t < kTileM; ++t)
+      for (int half = 0; half < 2; ++half) {
+        for (int lane = 0; lane < 64; ++lane) {
+          const int off = kc8_offset(base, t, half, lane);
+          CHECK(off >= 0 && off + 16 <= kOperandBytes, "kc8 read out of tile");
+          CHECK(off == (kc8_offset(base, 0, 0, lane) ^ (16 * half)) + 2048 * t, "kc8 address shortcut");
+          const int row = base + 32 * t + (lane & 31), chunk = 2 * (lane >> 5) + half;
+          CHECK(off == kc_offset(row, chunk), "kc8 element");
+        }
+        for (int g = 0; g < 4; ++g) {
+          int used[64] = {0};
+          for (int i = 0; i < 16; ++i) {
+            const int bank = (kc8_offset(base, t, half, 16 * g + i) / 4) % 64;
+            for (int q = 0; q < 4; ++q) used[(bank + q) % 64]++;
+          }
+          for (int b = 0; b < 64; ++b) CHECK(used[b] == 1, "kc8 bank conflict");
+        }
+      }
+  // 32 x 32 accumulators into 16-row slabs: every slab cell written once
+  for (int s = 0; s < 8; ++s) {
+    std::vector<int> cell(16 * 64, 0);
+    for (int lane = 0; lane < 64; ++lane)
+      for (int nt = 0; nt < kFrag8N; ++nt)
+        for (int e = 8 * (s & 1); e < 8 * (s & 1) + 8; ++e) {
+          const int r = acc32_row(e, lane) - 16 * (s & 1), c = 32 * nt + (lane & 31);
+          CHECK(r >= 0 && r < 16 && c >= 0 && c < 64, "acc32 slab cell out of range");
+          if (r >= 0 && r < 16) cell[r * 64 + c]++;
+        }
+    for (int i = 0; i < 16 * 64; ++i) CHECK(cell[i] == 1, "acc32 slab cell %d of slab %d written %d times", i, s, cell[i]);
+  }
+}
+
 static void check_epilogue_slab() {
   const int slab_floats = 16 * kEpiPitch;
   CHECK((kWaves / 4) * kEpiSlabBytes <= kStageBytes, "slabs exceed their stage");
@@ -220,6 +258,7 @@ int main() {
   check_rc(4);
   check_epilogue_slab();
   check_swiglu_col();
+  check_kc8();
   if (failures) {
     fprintf(stderr, "%d failures\n", failures);
     return 1;

@@ -211,6 +211,64 @@ def test_swiglu_bwd_validation(lib, args, status):
     assert lib.coda_swiglu_bwd(*args, None) == status
 
 
+def prms8(lib, M=512, K=256, D=512, A=A_, lda=None, sa=R2_, W=W1_, ldw=None, sw=G_ + 4096, R=R_, ldr=None, g=G_,
+           H=H_, ldh=None, Hg=HG_, ldhg=None, part=PART_):
+    return lib.coda_gemm_res_prms_fp8(M, K, D, A, lda or K, sa, W, ldw or K, sw, R, ldr or D, g, H, ldh or D, Hg,
+                                      ldhg or D, part, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=8), SHAPE),            # fp8 sizes are multiples of 16
+    (dict(D=520), SHAPE),
+    (dict(M=-1), SHAPE),
+    (dict(A=None), NULL),
+    (dict(sa=None), NULL),
+    (dict(W=None), NULL),
+    (dict(sw=None), NULL),
+    (dict(R=None), NULL),
+    (dict(g=None), NULL),
+    (dict(H=None), NULL),
+    (dict(Hg=None), NULL),
+    (dict(part=None), NULL),
+    (dict(lda=264), ALIGN),        # e4m3 ld must be a multiple of 16 elements
+    (dict(ldhg=520), ALIGN),
+    (dict(ldr=516), ALIGN),        # bf16 ld a multiple of 8
+    (dict(sw=G_ + 4), ALIGN),      # column scales read 16 bytes at a time
+    (dict(sa=R2_ + 2), ALIGN),
+    (dict(ldw=128), SHAPE),
+    (dict(Hg=A_ + 64), ALIAS),
+    (dict(H=R_), ALIAS),
+    (dict(part=HG_ + 256), ALIAS),
+])
+def test_gemm_res_prms_fp8_rejects(lib, kw, status):
+    assert prms8(lib, **kw) == status
+    assert lib.coda_last_error().decode() != ""
+
+
+def rowscale8(lib, M=512, D=256, N2=512, X=HG_, ldx=None, W=W2_, ldw=None, sw=G_, r=R2_, Y=Y_, ldy=None):
+    return lib.coda_gemm_rowscale_fp8(M, D, N2, X, ldx or D, W, ldw or D, sw, r, Y, ldy or N2, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N2=24), SHAPE),
+    (dict(X=None), NULL),
+    (dict(W=None), NULL),
+    (dict(sw=None), NULL),
+    (dict(Y=None), NULL),
+    (dict(ldx=264), ALIGN),
+    (dict(sw=G_ + 8), ALIGN),
+    (dict(Y=HG_), ALIAS),
+    (dict(Y=G_ - 64), ALIAS),
+])
+def test_gemm_rowscale_fp8_rejects(lib, kw, status):
+    assert rowscale8(lib, **kw) == status
+
+
+def test_fp8_empty_is_noop(lib):
+    assert prms8(lib, M=0, A=None, sa=None, R=None, H=None, Hg=None, part=None) == OK
+    assert rowscale8(lib, M=0, X=None, Y=None, r=None) == OK
+
+
 def test_chain_bwd_workspace_bytes(lib):
     def al(x):
         return (x + 255) // 256 * 256

@@ -33,6 +33,10 @@ SIGNATURES = {
     "coda_gemm_rowscale_swiglu": (c_int, [c_int, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp,
                                           c_vp, c_i64, c_vp, c_i64, c_vp]),
     "coda_swiglu_bwd": (c_int, [c_int, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
+    "coda_gemm_res_prms_fp8": (c_int, [c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_i64,
+                                       c_vp, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp]),
+    "coda_gemm_rowscale_fp8": (c_int, [c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_i64,
+                                       c_vp]),
     "coda_ref_chain_workspace_bytes": (c_size, [c_int, c_i64, c_i64]),
     "coda_ref_chain": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64, c_float, c_vp, c_vp, c_vp, c_vp,
                                c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),

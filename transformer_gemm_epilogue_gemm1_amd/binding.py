@@ -145,6 +145,54 @@ def coda_swiglu_bwd(dZ, Y, dY, stream=None) -> None:
     _lib.check("coda_swiglu_bwd", st)
 
 
+_FP8 = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
+
+
+def _mat8(t: torch.Tensor, name: str, shape) -> int:
+    """e4m3 operand: torch.float8_e4m3fn (OCP e4m3) or raw uint8 codes."""
+    if t.dtype not in _FP8:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected float8_e4m3fn or uint8 e4m3 codes")
+    return _mat(t, name, t.dtype, shape)
+
+
+def coda_gemm_res_prms_fp8(A8, sa, W1t8, sw1, R, g, H, Hg8, partials, stream=None) -> None:
+    """fp8 first GEMM: H = bf16(acc sa sw1 + R), Hg8 = e4m3(H g), partial sums of squares."""
+    lib = _lib.load()
+    M, K = A8.shape
+    D = W1t8.shape[0]
+    T = coda_prms_num_partials(torch.bfloat16, D)
+    lda = _mat8(A8, "A8", (M, K))
+    ldw = _mat8(W1t8, "W1t8", (D, K))
+    ldhg = _mat8(Hg8, "Hg8", (M, D))
+    _mat(sa, "sa", torch.float32, (M,))
+    _mat(sw1, "sw1", torch.float32, (D,))
+    ldr = _mat(R, "R", torch.bfloat16, (M, D))
+    _mat(g, "g", torch.bfloat16, (D,))
+    ldh = _mat(H, "H", torch.bfloat16, (M, D))
+    _mat(partials, "partials", torch.float32, (T, M))
+    _dense(partials, "partials")
+    st = lib.coda_gemm_res_prms_fp8(M, K, D, A8.data_ptr(), lda, sa.data_ptr(), W1t8.data_ptr(), ldw,
+                                    sw1.data_ptr(), R.data_ptr(), ldr, g.data_ptr(), H.data_ptr(), ldh,
+                                    Hg8.data_ptr(), ldhg, partials.data_ptr(), _stream(stream))
+    _lib.check("coda_gemm_res_prms_fp8", st)
+
+
+def coda_gemm_rowscale_fp8(X8, W2t8, sw2, r: Optional[torch.Tensor], Y, stream=None) -> None:
+    """fp8 second GEMM: Y = bf16(acc r sw2), W2 given transposed ([N2, D])."""
+    lib = _lib.load()
+    M, D = X8.shape
+    N2 = W2t8.shape[0]
+    ldx = _mat8(X8, "X8", (M, D))
+    ldw = _mat8(W2t8, "W2t8", (N2, D))
+    _mat(sw2, "sw2", torch.float32, (N2,))
+    ldy = _mat(Y, "Y", torch.bfloat16, (M, N2))
+    if r is not None:
+        _mat(r, "r", torch.float32, (M,))
+    st = lib.coda_gemm_rowscale_fp8(M, D, N2, X8.data_ptr(), ldx, W2t8.data_ptr(), ldw, sw2.data_ptr(),
+                                    r.data_ptr() if r is not None else None, Y.data_ptr(), ldy, _stream(stream))
+    _lib.check("coda_gemm_rowscale_fp8", st)
+
+
 def coda_ref_chain_workspace_bytes(dtype: torch.dtype, M: int, D: int) -> int:
     return int(_lib.load().coda_ref_chain_workspace_bytes(_DT[dtype], M, D))
 
@@ -264,3 +312,18 @@ def fused_backward_swiglu(dZ, Y, A, W1, g, W2, H, r, stream=None):
     dY = torch.empty_like(Y)
     coda_swiglu_bwd(dZ, Y, dY, stream)
     return fused_backward(dY, A, W1, g, W2, H, r, stream) + (dY,)
+
+
+def fused_forward_fp8(A8, sa, W1t8, sw1, R, g, W2t8, sw2, eps: float, stream=None):
+    """The fused chain with fp8 GEMM operands: returns (H, Hg8, r, Y, partials)."""
+    M, D, N2 = A8.shape[0], W1t8.shape[0], W2t8.shape[0]
+    dev = A8.device
+    H = torch.empty((M, D), device=dev, dtype=torch.bfloat16)
+    Hg8 = torch.empty((M, D), device=dev, dtype=A8.dtype)
+    P = torch.empty((coda_prms_num_partials(torch.bfloat16, D), M), device=dev, dtype=torch.float32)
+    r = torch.empty((M,), device=dev, dtype=torch.float32)
+    Y = torch.empty((M, N2), device=dev, dtype=torch.bfloat16)
+    coda_gemm_res_prms_fp8(A8, sa, W1t8, sw1, R, g, H, Hg8, P, stream)
+    coda_rms_combine(P, r, D, eps, stream)
+    coda_gemm_rowscale_fp8(Hg8, W2t8, sw2, r, Y, stream)
+    return H, Hg8, r, Y, P

@@ -13,6 +13,8 @@
 
 #include "../../include/coda.h"
 #include "epilogues.hpp"
+#include "epilogues_fp8.hpp"
+#include "gemm_fp8.hpp"
 #include "rowops.hpp"
 
 using namespace coda;
@@ -120,6 +122,45 @@ coda_status launch_gemm(const char* what, int M, int N, int K, const void* a, in
   const int nblocks = g.tiles_m * g.tiles_n;
   hipLaunchKernelGGL((gemm_kernel<T, AKC, BKC, Epi>), dim3(nblocks), dim3(kThreads), 0, s, g, ep);
   return launch_status(what);
+}
+
+template <class Epi>
+coda_status launch_gemm_fp8(const char* what, int M, int N, int K, const void* a, int64_t lda, const void* b,
+                            int64_t ldb, const typename Epi::Params& ep, hipStream_t s) {
+  GemmArgs g;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.tiles_m = (M + kTileM - 1) / kTileM;
+  g.tiles_n = (N + kTileN - 1) / kTileN;
+  g.group_m = kGroupM;
+  g.a = a;
+  g.lda = lda;
+  g.a_span = span_bytes(M, K, lda, 1);
+  g.b = b;
+  g.ldb = ldb;
+  g.b_span = span_bytes(N, K, ldb, 1);
+  g.b_split = 0;
+  hipLaunchKernelGGL((gemm_fp8_kernel<Epi>), dim3(g.tiles_m * g.tiles_n), dim3(kThreads), 0, s, g, ep);
+  return launch_status(what);
+}
+
+// fp8 operands come in 16-element (16-byte) chunks: contraction lengths and
+// widths are multiples of 16.
+coda_status check_dims_fp8(int64_t M, std::initializer_list<std::pair<const char*, int64_t>> dims) {
+  if (M < 0 || M > kMaxDim) return fail(CODA_ERR_SHAPE, "M = %lld out of range", (long long)M);
+  for (auto& d : dims) {
+    if (d.second < 1 || d.second > kMaxDim) return fail(CODA_ERR_SHAPE, "%s = %lld out of range", d.first, (long long)d.second);
+    if (d.second % 16 != 0) return fail(CODA_ERR_SHAPE, "%s = %lld is not a multiple of 16", d.first, (long long)d.second);
+  }
+  return CODA_OK;
+}
+
+coda_status check_vec(const float* p, int64_t n, int align, const char* name) {
+  if (p == nullptr) return fail(CODA_ERR_NULL, "%s is NULL", name);
+  if (((uintptr_t)p & (align - 1)) != 0) return fail(CODA_ERR_ALIGN, "%s is not %d-byte aligned", name, align);
+  if (n * 4 > kMaxSpan) return fail(CODA_ERR_SHAPE, "%s too long", name);
+  return CODA_OK;
 }
 
 int64_t num_partials(int64_t D) { return (kTileN / kPartialCols) * ((D + kTileN - 1) / kTileN); }
@@ -342,6 +383,55 @@ coda_status coda_swiglu_bwd(coda_dtype dt, int64_t M, int64_t F, const void* dZ,
     hipLaunchKernelGGL(swiglu_bwd_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)dZ, ldz,
                        (const float*)Y, ldy, (float*)dY, lddy, (int)F, nchunks);
   return launch_status("coda_swiglu_bwd");
+}
+
+coda_status coda_gemm_res_prms_fp8(int64_t M, int64_t K, int64_t D, const void* A8, int64_t lda, const float* sa,
+                                   const void* W1t8, int64_t ldw1t, const float* sw1, const void* R, int64_t ldr,
+                                   const void* g, void* H, int64_t ldh, void* Hg8, int64_t ldhg, float* partials,
+                                   void* stream) {
+  coda_status st = check_dims_fp8(M, {{"K", K}, {"D", D}});
+  if (st != CODA_OK) return st;
+  if (M == 0) return ok();
+  const int64_t T = num_partials(D);
+  const Mat mA{A8, M, K, lda, 1, "A8"}, mW{W1t8, D, K, ldw1t, 1, "W1t8"}, mR{R, M, D, ldr, 2, "R"};
+  const Mat mg{g, 1, D, D, 2, "g"}, mH{H, M, D, ldh, 2, "H"}, mHg{Hg8, M, D, ldhg, 1, "Hg8"};
+  const Mat mP{partials, T, M, M, 4, "partials"}, msa{sa, 1, M, M, 4, "sa"}, msw{sw1, 1, D, D, 4, "sw1"};
+  for (const Mat* m : {&mA, &mW, &mHg})
+    if ((st = check_mat(*m, 16)) != CODA_OK) return st;
+  for (const Mat* m : {&mR, &mg, &mH})
+    if ((st = check_mat(*m, 8)) != CODA_OK) return st;
+  if ((st = check_vec(sa, M, 4, "sa")) != CODA_OK || (st = check_vec(sw1, D, 16, "sw1")) != CODA_OK) return st;
+  if (partials == nullptr) return fail(CODA_ERR_NULL, "partials is NULL");
+  if (((uintptr_t)partials & 3) != 0) return fail(CODA_ERR_ALIGN, "partials is not 4-byte aligned");
+  if (mP.span() > kMaxSpan) return fail(CODA_ERR_SHAPE, "partials span too large");
+  const Mat outs[3] = {mH, mHg, mP};
+  const Mat ins[6] = {mA, mW, mR, mg, msa, msw};
+  if ((st = check_alias(outs, 3, ins, 6)) != CODA_OK) return st;
+  EpiResPrmsFp8::Params ep{sa, sw1, (const uint16_t*)R, ldr, (const uint16_t*)g, (uint16_t*)H, ldh,
+                           (uint8_t*)Hg8, ldhg, partials};
+  return launch_gemm_fp8<EpiResPrmsFp8>("coda_gemm_res_prms_fp8", (int)M, (int)D, (int)K, A8, lda, W1t8, ldw1t,
+                                        ep, (hipStream_t)stream);
+}
+
+coda_status coda_gemm_rowscale_fp8(int64_t M, int64_t D, int64_t N2, const void* X8, int64_t ldx, const void* W2t8,
+                                   int64_t ldw2t, const float* sw2, const float* r, void* Y, int64_t ldy,
+                                   void* stream) {
+  coda_status st = check_dims_fp8(M, {{"D", D}, {"N2", N2}});
+  if (st != CODA_OK) return st;
+  if (M == 0) return ok();
+  const Mat mX{X8, M, D, ldx, 1, "X8"}, mW{W2t8, N2, D, ldw2t, 1, "W2t8"}, mY{Y, M, N2, ldy, 2, "Y"};
+  const Mat mr{r, 1, M, M, 4, "r"}, msw{sw2, 1, N2, N2, 4, "sw2"};
+  for (const Mat* m : {&mX, &mW})
+    if ((st = check_mat(*m, 16)) != CODA_OK) return st;
+  if ((st = check_mat(mY, 8)) != CODA_OK) return st;
+  if ((st = check_vec(sw2, N2, 16, "sw2")) != CODA_OK) return st;
+  if (r != nullptr && ((uintptr_t)r & 3) != 0) return fail(CODA_ERR_ALIGN, "r is not 4-byte aligned");
+  const Mat none{nullptr, 0, 0, 0, 4, ""};
+  const Mat ins[4] = {mX, mW, msw, r ? mr : none};
+  if ((st = check_alias(&mY, 1, ins, 4)) != CODA_OK) return st;
+  EpiRowScaleFp8::Params ep{r, sw2, (uint16_t*)Y, ldy};
+  return launch_gemm_fp8<EpiRowScaleFp8>("coda_gemm_rowscale_fp8", (int)M, (int)N2, (int)D, X8, ldx, W2t8, ldw2t,
+                                         ep, (hipStream_t)stream);
 }
 
 size_t coda_ref_chain_workspace_bytes(coda_dtype dt, int64_t M, int64_t D) {

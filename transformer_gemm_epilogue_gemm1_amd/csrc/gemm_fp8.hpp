@@ -1,0 +1,171 @@
+// MFMA GEMM main loop for fp8 (OCP e4m3) operands on gfx950.
+//
+//   C[m, n] = sum_k A[m, k] B[n, k],  both operands contraction-contiguous
+//   (A[M, K] row-major, B stored [N, K]), fp32 accumulation.
+//
+// The loop is the bf16 one (gemm.hpp) with fp8 fragments: the same 64-byte
+// k-tiles (64 elements), direct HBM->LDS loads into the same five stages, the
+// same barrier, tile order and epilogue interface.  What differs: a
+// wavefront's 128 x 64 sub-tile is 4 x 2 products v_mfma_f32_32x32x64_f8f6f4
+// (16 accumulators per lane each, 128 in all), each k-tile is one product per
+// fragment pair, and fragments are 32 rows (two 16-byte reads per lane,
+// kc8_offset).  Per k-tile a wavefront moves the same bytes as in bf16 for
+// twice the flops.
+#pragma once
+
+#include "gemm.hpp"
+
+namespace coda {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <>
+struct Elem<uint8_t> {  // OCP e4m3, stored as its 8-bit code
+  static constexpr int E = 16;
+};
+
+// 32-row fragment t of a contraction-contiguous operand tile.
+struct FragReader8 {
+  int off0;  // lane's byte offset of fragment 0, first chunk
+  __device__ __forceinline__ FragReader8(int base, int lane) : off0(kc8_offset(base, 0, 0, lane)) {}
+  __device__ __forceinline__ void refresh() { opaque(off0); }
+  __device__ __forceinline__ i32x8 read(const char* tile, int t) const {
+    // second chunk: the first XOR 16 bytes (the swizzle only moves whole
+    // chunk pairs); fragment t lies 32 rows (2 KiB) further
+    const u32x4 lo = *(const u32x4*)(tile + off0 + 2048 * t);
+    const u32x4 hi = *(const u32x4*)(tile + (off0 ^ 16) + 2048 * t);
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+};
+
+__device__ __forceinline__ void mac8(f32x16& acc, const i32x8& a, const i32x8& b) {
+  // formats 0, 0: both operands e4m3; zero scale selectors: unscaled
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
+}
+
+struct Frags8 {
+  i32x8 a[kFrag8M], b[kFrag8N];
+};
+
+// One k-step, k-tile kt in stage S (the schedule of kstep in gemm.hpp):
+// loads of tile kt + kStages - 1, B fragments of tile kt + 1, then per A
+// fragment its 2 products of tile kt and its reload for tile kt + 1.
+template <int S>
+__device__ __forceinline__ void kstep8(char* const (&st)[kStages], const Dma<uint8_t, true>& da,
+                                       const Dma<uint8_t, true>& db, FragReader8& ra, FragReader8& rb,
+                                       f32x16 (&acc)[kFrag8M][kFrag8N], Frags8& cur, int kt, int K, int wave) {
+  constexpr int SL = (S + kStages - 1) % kStages;
+  constexpr int SN = (S + 1) % kStages;
+  da.issue(st[SL], kt + kStages - 1, K, wave);
+  db.issue(st[SL] + kOperandBytes, kt + kStages - 1, K, wave);
+  ra.refresh();
+  rb.refresh();
+  i32x8 nb[kFrag8N];
+#pragma unroll
+  for (int nt = 0; nt < kFrag8N; ++nt) nb[nt] = rb.read(st[SN] + kOperandBytes, nt);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int mt = 0; mt < kFrag8M; ++mt) {
+#pragma unroll
+    for (int nt = 0; nt < kFrag8N; ++nt) mac8(acc[mt][nt], cur.a[mt], cur.b[nt]);
+    cur.a[mt] = ra.read(st[SN], mt);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int nt = 0; nt < kFrag8N; ++nt) cur.b[nt] = nb[nt];
+  stage_barrier();
+}
+
+// C = A B^T for fp8 A[M, K] (g.a, g.lda) and B[N, K] (g.b, g.ldb); the
+// epilogue interface is the bf16 kernel's (16-row slabs, apply / end_slab /
+// finish).
+template <class Epi>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_fp8_kernel(
+    GemmArgs g, typename Epi::Params ep) {
+  static_assert(kStages == 5, "the stage arrays and the unrolled steps below assume five stages");
+  __shared__ __attribute__((aligned(1024))) char st0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char st1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char st2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char st3[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char st4[kStageBytes];
+  char* const st[kStages] = {st0, st1, st2, st3, st4};
+  constexpr int KTE = kKTBytes;  // fp8 elements per k-tile
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  int tm, tn;
+  map_tile(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, &tm, &tn);
+  const int m0 = tm * kTileM, n0 = tn * kTileN;
+
+  Dma<uint8_t, true> da, db;
+  da.init(g.a, g.a_span, g.lda, m0, g.M, wave, lane);
+  db.init(g.b, g.b_span, g.ldb, n0, g.N, wave, lane);
+  FragReader8 ra(wm * kWaveM, lane), rb(wn * kWaveN, lane);
+  f32x16 acc[kFrag8M][kFrag8N];
+#pragma unroll
+  for (int i = 0; i < kFrag8M; ++i)
+#pragma unroll
+    for (int j = 0; j < kFrag8N; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int nk = (g.K + KTE - 1) / KTE;
+#pragma unroll
+  for (int t = 0; t < kStages - 1; ++t) {
+    da.issue(st[t], t, g.K, wave);
+    db.issue(st[t] + kOperandBytes, t, g.K, wave);
+  }
+  static_assert((kStages - 3) * kLoadsPerTile == 8, "the prologue vmcnt literal assumes kStages - 3 tiles in flight");
+  asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  Frags8 cur;
+#pragma unroll
+  for (int mt = 0; mt < kFrag8M; ++mt) cur.a[mt] = ra.read(st[0], mt);
+#pragma unroll
+  for (int nt = 0; nt < kFrag8N; ++nt) cur.b[nt] = rb.read(st[0] + kOperandBytes, nt);
+  int kt = 0;
+  for (; kt + kStages <= nk; kt += kStages) {
+    kstep8<0>(st, da, db, ra, rb, acc, cur, kt, g.K, wave);
+    kstep8<1>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave);
+    kstep8<2>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave);
+    kstep8<3>(st, da, db, ra, rb, acc, cur, kt + 3, g.K, wave);
+    kstep8<4>(st, da, db, ra, rb, acc, cur, kt + 4, g.K, wave);
+  }
+  const int rem = nk - kt;
+  if (rem > 0) kstep8<0>(st, da, db, ra, rb, acc, cur, kt, g.K, wave);
+  if (rem > 1) kstep8<1>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave);
+  if (rem > 2) kstep8<2>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave);
+  if (rem > 3) kstep8<3>(st, da, db, ra, rb, acc, cur, kt + 3, g.K, wave);
+  drain_barrier();  // no direct load may land in the LDS the epilogue reuses
+
+  // ---- epilogue: slab s = rows 16 s .. 16 s + 15 of the wavefront's 128 =
+  // half s % 2 of row fragment s / 2 (acc32_row) ----
+  Epi epi(ep, lane, wm, wn, m0, n0, tn, g.M, g.N);
+  float* slab = (float*)(((wave & 3) == 0 ? st0 : (wave & 3) == 1 ? st1 : (wave & 3) == 2 ? st2 : st3) +
+                         (wave >> 2) * kEpiSlabBytes);
+  const int row_base = m0 + wm * kWaveM;
+  const int col = n0 + wn * kWaveN + (lane & 7) * 8;
+#pragma unroll
+  for (int s = 0; s < 2 * kFrag8M; ++s) {
+#pragma unroll
+    for (int nt = 0; nt < kFrag8N; ++nt)
+#pragma unroll
+      for (int e = 8 * (s & 1); e < 8 * (s & 1) + 8; ++e)
+        slab[(acc32_row(e, lane) - 16 * (s & 1)) * kEpiPitch + 32 * nt + (lane & 31)] = acc[s >> 1][nt][e];
+    wave_lds_fence();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int rl = (lane >> 3) + 8 * q;
+      const float* src = slab + rl * kEpiPitch + (lane & 7) * 8;
+      const f32x4 lo = *(const f32x4*)src, hi = *(const f32x4*)(src + 4);
+      float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const int row = row_base + s * 16 + rl;
+      if (row < g.M && col < g.N) epi.apply(s, q, row, col, v);
+    }
+    epi.end_slab(row_base + s * 16);
+    wave_lds_fence();
+  }
+  epi.finish();
+}
+
+}  // namespace coda

@@ -132,6 +132,25 @@ CODA_HD bool swiglu_is_up(int n) { return ((n / kSwiGLURun) & 1) != 0; }
 // The epilogue lane holding the up values for a gate lane (and vice versa).
 constexpr int kSwiGLUPartner = kSwiGLURun / 8;
 
+// ---- fp8 (e4m3) operands: v_mfma_f32_32x32x64_f8f6f4 ---------------------
+// One k-tile is 64 bytes = 64 fp8 elements per operand row, so both operands
+// use the contraction-contiguous layout above unchanged.  A wavefront's
+// 128 x 64 sub-tile is 4 x 2 products of 32 x 32.  Lane l = 32 g + i of a
+// 32-row fragment t supplies operand row base + 32 t + i and contraction
+// bytes [32 g, 32 g + 32) of the k-tile: chunks 2 g and 2 g + 1, read with
+// two 16-byte reads.  The same (lane, byte) -> k assignment on both operands
+// makes the product independent of how the hardware orders k.
+constexpr int kFrag8M = kWaveM / 32;  // 4 fragments of 32 A rows
+constexpr int kFrag8N = kWaveN / 32;  // 2 fragments of 32 B rows
+CODA_HD int kc8_offset(int base, int t, int half, int lane) {
+  return kc_offset(base + 32 * t + (lane & 31), 2 * (lane >> 5) + half);
+}
+// Accumulator element e (0..15) of lane l in a 32 x 32 product is output
+// row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32 (established by a GPU
+// probe against a host product).  Epilogue slab s (16 rows) is half s % 2 of
+// row fragment s / 2 and holds elements e = 8 (s % 2) .. 8 (s % 2) + 7.
+CODA_HD int acc32_row(int e, int lane) { return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
+
 // Workgroup -> output tile.  The dispatcher places workgroup b on XCD b % 8;
 // each XCD is given a contiguous range of logical tile ids so that tiles
 // sharing A rows / B columns share that XCD's L2.  Logical ids are then laid
