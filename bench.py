@@ -35,6 +35,8 @@ METRIC = "fused GEMM-Res-PartialRMS-GEMM TFLOP/s at 7B hidden; % of bf16 MFMA pe
 # MI355X dense bf16 MFMA peak: 256 CUs x 4096 flop/CU/clk x 2.4 GHz
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 PEAK_F32_TFLOPS = 157.3
+# dense fp8 (e4m3) MFMA peak: twice the bf16 rate
+PEAK_FP8_TFLOPS = 256 * 8192 * 2.4e9 / 1e12
 
 
 def parse():
@@ -53,6 +55,7 @@ def parse():
     ap.add_argument("--power-probe-s", type=float, default=2.0,
                     help="seconds of back-to-back forward chains while amd-smi samples socket power and "
                          "gfx clocks (0 disables; skipped when amd-smi is absent)")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 (e4m3) chain at the 7B shape")
     ap.add_argument("--no-swiglu", action="store_true",
                     help="skip the SwiGLU-gated chain (forward, and the training step when timing the backward)")
     ap.add_argument("--no-backward", action="store_true",
@@ -223,6 +226,60 @@ def bench_forward_shape(wl, stream, steps, warmup, seed):
     return {"shape": {"M": M, "K": K, "D": D, "N2": N2}, "ms_per_step": round(ms, 4), "value": round(tf, 2),
             "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
             "coda_gemm_rowscale_frac": round(g2_tf / PEAK_BF16_TFLOPS, 4)}
+
+
+def bench_fp8(args, stream):
+    """The fused chain with fp8 (OCP e4m3) GEMM operands at the 7B shape:
+    A per-row and weights per-channel quantised on the device from the same
+    distributions (timing only; parity is tested against the oracle
+    elsewhere), H and Y bf16."""
+    import torch
+
+    import coda_inputs as ci
+    import transformer_gemm_epilogue_gemm1_amd as coda
+
+    wl = ci.WORKLOADS["7b-fp8"]
+    M, K, D, N2 = wl.M, wl.K, wl.D, wl.N2
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+
+    def quant_rows(x):
+        s = (x.abs().amax(dim=1) / 448.0).clamp_min(1e-30)
+        return (x / s[:, None]).to(torch.float8_e4m3fn).view(torch.uint8), s.float().contiguous()
+
+    A8, sa = quant_rows(torch.randn((M, K), device=dev, generator=gen))
+    W1t8, sw1 = quant_rows(torch.randn((D, K), device=dev, generator=gen) * K ** -0.5)
+    W2t8, sw2 = quant_rows(torch.randn((N2, D), device=dev, generator=gen) * D ** -0.5)
+    R = torch.randn((M, D), device=dev, generator=gen).to(torch.bfloat16)
+    g = (1.0 + 0.1 * torch.randn((D,), device=dev, generator=gen)).to(torch.bfloat16)
+    H = torch.empty((M, D), device=dev, dtype=torch.bfloat16)
+    Hg8 = torch.empty((M, D), device=dev, dtype=torch.uint8)
+    P = torch.empty((coda.coda_prms_num_partials(torch.bfloat16, D), M), device=dev, dtype=torch.float32)
+    r = torch.empty((M,), device=dev, dtype=torch.float32)
+    Y = torch.empty((M, N2), device=dev, dtype=torch.bfloat16)
+
+    def step():
+        coda.coda_gemm_res_prms_fp8(A8, sa, W1t8, sw1, R, g, H, Hg8, P, stream)
+        coda.coda_rms_combine(P, r, D, wl.eps, stream)
+        coda.coda_gemm_rowscale_fp8(Hg8, W2t8, sw2, r, Y, stream)
+
+    n = max(5, args.steps // 2)
+    w = max(2, args.warmup // 2)
+    ms = time_ms(step, stream, n, w)
+    g2_ms = time_ms(lambda: coda.coda_gemm_rowscale_fp8(Hg8, W2t8, sw2, r, Y, stream), stream, n, w)
+    tf = wl.fwd_flops / (ms * 1e-3) / 1e12
+    g2_tf = 2.0 * M * D * N2 / (g2_ms * 1e-3) / 1e12
+    out = {"workload": f"7b-fp8: M={M} K={K} D={D} N2={N2}, e4m3 operands with per-row / per-channel scales",
+           "ms_per_step": round(ms, 4), "tflops": round(tf, 2),
+           "pct_of_fp8_peak": round(100.0 * tf / PEAK_FP8_TFLOPS, 2), "fp8_peak_tflops": round(PEAK_FP8_TFLOPS, 1),
+           "coda_gemm_rowscale_fp8_ms": round(g2_ms, 4), "coda_gemm_rowscale_fp8_tflops": round(g2_tf, 2),
+           "coda_gemm_rowscale_fp8_frac": round(g2_tf / PEAK_FP8_TFLOPS, 4)}
+    pp = power_probe(step, min(args.power_probe_s, 2.0))
+    if pp is not None:
+        pp["fp8_peak_at_clock_tflops"] = round(256 * 8192 * pp["gfx_clock_mhz"] * 1e6 / 1e12, 1)
+        out["power"] = pp
+    return out
 
 
 def bench_swiglu(args, up, stream, with_backward):
@@ -567,6 +624,9 @@ def main():
 
     if not args.no_swiglu:
         out["swiglu"] = bench_swiglu(args, up, stream, with_backward=not args.no_backward)
+
+    if not args.no_fp8:
+        out["fp8"] = bench_fp8(args, stream)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
