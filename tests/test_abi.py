@@ -352,3 +352,20 @@ def test_index_maps_host_check(tmp_path):
     subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-o", str(exe), src], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     assert out.returncode == 0, out.stderr
+
+
+def test_package_without_library_fails_loudly(tmp_path):
+    # the binding has no fallback: a copy of the package without libcoda.so
+    # must refuse to import
+    import shutil
+    import sys as _sys
+    src = os.path.join(ROOT, "transformer_gemm_epilogue_gemm1_amd")
+    dst = tmp_path / "transformer_gemm_epilogue_gemm1_amd"
+    shutil.copytree(src, dst, ignore=shutil.ignore_patterns("*.so", "*.so.tmp", "__pycache__", "csrc"))
+    assert not any(p.suffix == ".so" for p in dst.iterdir())
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "try:\n    import transformer_gemm_epilogue_gemm1_amd\nexcept ImportError as e:\n"
+            "    print('ImportError:', e); sys.exit(3)\nsys.exit(0)\n") % str(tmp_path)
+    out = subprocess.run([_sys.executable, "-c", code], capture_output=True, text=True, cwd=str(tmp_path))
+    assert out.returncode == 3, out.stdout + out.stderr
+    assert "libcoda.so not built" in out.stdout
