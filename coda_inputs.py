@@ -29,7 +29,7 @@ from typing import Dict, Optional
 import numpy as np
 
 # tensor ids inside one workload's seed sequence
-TENSOR_IDS = {"A": 0, "R": 1, "W1": 2, "W2": 3, "g": 4, "dY": 5}
+TENSOR_IDS = {"A": 0, "R": 1, "W1": 2, "W2": 3, "g": 4, "dY": 5, "targets": 6}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -68,6 +68,9 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("7b-bwd-bf16", 4, 16384, 4096, 4096, 28672, 1e-5, "bf16", True),
         # 7B-style chain with fp8 (e4m3) GEMM operands
         Workload("7b-fp8", 5, 16384, 4096, 4096, 28672, 1e-5, "fp8"),
+        # 7B-style chain ending in the LM head (vocabulary 32000) and the
+        # per-token cross-entropy
+        Workload("7b-ce-bf16", 6, 16384, 4096, 4096, 32000, 1e-5, "bf16"),
     ]
 }
 
@@ -199,3 +202,8 @@ def make_inputs_fp8(wl: Workload, seed: int = 0) -> Dict[str, object]:
     return {"A8": A8, "sa": sa, "W1t8": W1t8, "sw1": sw1, "W2t8": W2t8, "sw2": sw2,
             "R": HostTensor(_draw(seed, wl, "R", (M, D), 1.0), "bf16"),
             "g": HostTensor(_draw(seed, wl, "g", (D,), 0.1, 1.0), "bf16")}
+
+
+def make_targets(wl: Workload, seed: int = 0) -> np.ndarray:
+    """One target class per row, uniform over the N2 (vocabulary) columns, int32."""
+    return generator(seed, wl.wl_id, "targets").integers(0, wl.N2, size=wl.M).astype(np.int32)
