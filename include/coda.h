@@ -138,6 +138,37 @@ coda_status coda_swiglu_bwd(coda_dtype dt, int64_t M, int64_t F,
                             const void* dZ, int64_t ldz, const void* Y, int64_t ldy,
                             void* dY, int64_t lddy, void* stream);
 
+/* ---- cross-entropy head --------------------------------------------------
+ * The article says the re-parameterisation covers the cross-entropy loss
+ * (section "CODA：「尾声」里藏着宝藏") and lists the tile log-sum-exp and the
+ * max / sum-exp state of online normalisation among the epilogue building
+ * blocks (section "五种「积木」和一套「乐高语言」").  Reading taken: the chain's
+ * second GEMM is the LM head (W2 = W_vocab [D,V]) and the loss is the
+ * per-token cross-entropy loss_i = lse_i - Y_i,t_i, lse_i = log sum_j e^Y_ij.
+ * The [M,V] logits are never written. */
+
+/* LM-head GEMM with the cross-entropy statistics in the epilogue.  With
+ * y = r_i * (X W_v)_ij in fp32 (never stored) and T = coda_prms_num_partials(dt, V)
+ * partial tiles of 64 columns:
+ *   pmax[t*M + i] = max of y over partial tile t;  psum[t*M + i] = sum of
+ *   e^(y - pmax) over it ((-inf, 0) for a tile past the last column);
+ *   tgt[i] = y at column targets[i] (not written if the target is outside
+ *   [0, V)).
+ * X: [M,D] (ldx, e.g. Hg); Wv: [D,V] (ldw); r: float[M] or NULL; targets:
+ * int32[M]; pmax, psum: float[T*M]; tgt: float[M].  V a multiple of 8. */
+coda_status coda_gemm_rowscale_lse(coda_dtype dt, int64_t M, int64_t D, int64_t V,
+                                   const void* X, int64_t ldx, const void* Wv, int64_t ldw,
+                                   const float* r, const int32_t* targets,
+                                   float* pmax, float* psum, float* tgt, void* stream);
+
+/* Cross-entropy combine: lse_i = M_i + log(sum_t psum[t*M+i] e^(pmax[t*M+i] - M_i))
+ * with M_i = max_t pmax, merged in a fixed order (four quarters of t, each in
+ * increasing t, then first to last); loss_i = lse_i - tgt[i], or NaN when
+ * targets[i] is outside [0, V).  All arrays float[M] / float[T*M] / int32[M]. */
+coda_status coda_ce_combine(int64_t M, int64_t V, int64_t T, const float* pmax, const float* psum,
+                            const float* tgt, const int32_t* targets, float* lse, float* loss,
+                            void* stream);
+
 /* ---- fp8 operands -------------------------------------------------------
  * The article's opening section notes that FP8 makes the matrix products
  * faster while the memory-bound operations around them do not shrink, so

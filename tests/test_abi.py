@@ -211,6 +211,46 @@ def test_swiglu_bwd_validation(lib, args, status):
     assert lib.coda_swiglu_bwd(*args, None) == status
 
 
+def lse_call(lib, dt=BF16, M=512, D=256, V=1000, X=H_, ldx=None, W=W2_, ldw=None, r=R2_, t=DY_, pm=PART_,
+             ps=PART_ + (1 << 24), tg=DG_):
+    return lib.coda_gemm_rowscale_lse(dt, M, D, V, X, ldx or D, W, ldw or V, r, t, pm, ps, tg, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=5), DTYPE),
+    (dict(V=1001), SHAPE),
+    (dict(X=None), NULL),
+    (dict(W=None), NULL),
+    (dict(t=None), NULL),
+    (dict(pm=None), NULL),
+    (dict(ps=None), NULL),
+    (dict(tg=None), NULL),
+    (dict(pm=PART_ + 2), ALIGN),
+    (dict(t=DY_ + 1), ALIGN),
+    (dict(ldw=996), SHAPE),
+    (dict(ps=PART_ + 4096), ALIAS),    # the two statistics arrays overlapping
+    (dict(tg=H_), ALIAS),
+    (dict(pm=DY_), ALIAS),
+])
+def test_gemm_rowscale_lse_rejects(lib, kw, status):
+    assert lse_call(lib, **kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 1000, 16, PART_, R_, DG_, DY_, DA_, DR_), SHAPE),
+    ((512, 0, 16, PART_, R_, DG_, DY_, DA_, DR_), SHAPE),
+    ((512, 1000, 0, PART_, R_, DG_, DY_, DA_, DR_), SHAPE),
+    ((512, 1000, 16, None, R_, DG_, DY_, DA_, DR_), NULL),
+    ((512, 1000, 16, PART_, R_, DG_, DY_, None, DR_), NULL),
+    ((512, 1000, 16, PART_ + 1, R_, DG_, DY_, DA_, DR_), ALIGN),
+    ((512, 1000, 16, PART_, R_, DG_, DY_, PART_ + 64, DR_), ALIAS),
+    ((512, 1000, 16, PART_, R_, DG_, DY_, DA_, DA_ + 8), ALIAS),
+    ((0, 1000, 16, None, None, None, None, None, None), OK),
+])
+def test_ce_combine_validation(lib, args, status):
+    assert lib.coda_ce_combine(*args, None) == status
+
+
 def prms8(lib, M=512, K=256, D=512, A=A_, lda=None, sa=R2_, W=W1_, ldw=None, sw=G_ + 4096, R=R_, ldr=None, g=G_,
            H=H_, ldh=None, Hg=HG_, ldhg=None, part=PART_):
     return lib.coda_gemm_res_prms_fp8(M, K, D, A, lda or K, sa, W, ldw or K, sw, R, ldr or D, g, H, ldh or D, Hg,

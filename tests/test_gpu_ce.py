@@ -1,0 +1,128 @@
+"""GPU parity of the chain ending in the LM head and the per-token
+cross-entropy (coda_gemm_rowscale_lse + coda_ce_combine) through the C ABI.
+
+The logits are never written: the second GEMM's epilogue keeps per-tile
+max / sum-exp statistics and the target logit, a combine turns them into
+lse and loss.  Compared with the fp64 oracle (oracle/ce.py) on the same
+seeded inputs and targets: max|x - x_ref| / max|x_ref| <= 1e-2 (bf16) or
+1e-5 (fp32) for lse and loss.  Stage-wise (fp32, where the LM-head GEMM with
+a row scale stores exactly the y the statistics see): pmax and the target
+logit bit-exact against the host on coda_gemm_rowscale's output, psum to
+fp32 rounding.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import coda_inputs as ci
+import oracle
+import transformer_gemm_epilogue_gemm1_amd as coda
+from tests.gpu_util import dev, host_f32, max_rel, tolerance
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu-test] {request.node.nodeid}", file=sys.__stderr__, flush=True)
+    yield
+    torch.cuda.synchronize()
+
+
+def _run(wl, seed, targets=None):
+    x = ci.make_inputs(wl, seed=seed)
+    t = ci.make_targets(wl, seed=seed) if targets is None else np.asarray(targets, dtype=np.int32)
+    d = {k: dev(v) for k, v in x.items()}
+    tt = torch.from_numpy(t).cuda()
+    H, r, lse, loss = coda.fused_forward_ce(d["A"], d["W1"], d["R"], d["g"], d["W2"], wl.eps, tt)
+    torch.cuda.synchronize()
+    return x, d, t, tt, {"H": H, "r": r, "lse": lse, "loss": loss}
+
+
+def _check(wl, x, t, o, rows=None):
+    orc = oracle.forward_ce(x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps, t, rows=rows)
+    sel = slice(None) if rows is None else np.asarray(rows)
+    for k in ("lse", "loss"):
+        err = max_rel(o[k].cpu().numpy()[sel], orc[k])
+        assert err <= tolerance(wl.dtype), f"{k} error {err:.3e}"
+    return max_rel(o["loss"].cpu().numpy()[sel], orc["loss"])
+
+
+SHAPES = [  # M, K, D, V (V ragged against the 256-column tiles)
+    (1, 64, 256, 256),
+    (3, 136, 264, 520),
+    (257, 256, 512, 1000),
+    (300, 512, 384, 2056),
+    (513, 1024, 1024, 4096),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_ce_chain_matches_oracle(shape, dtype):
+    wl = ci.custom_workload(*shape, eps=1e-5 if dtype == "bf16" else 1e-6, dtype=dtype, wl_id=600)
+    x, d, t, tt, o = _run(wl, seed=1)
+    _check(wl, x, t, o)
+
+
+def test_statistics_against_the_logits_fp32():
+    M, K, D, V = 300, 256, 384, 1000
+    wl = ci.custom_workload(M, K, D, V, eps=1e-6, dtype="f32", wl_id=601)
+    # targets on tile and chunk edges
+    t = (np.arange(M) * 37) % V
+    t[:6] = [0, 7, 8, 63, 64, V - 1]
+    x, d, t, tt, o = _run(wl, seed=2, targets=t)
+    Hg = torch.empty((M, D), device="cuda")
+    P = torch.empty((coda.coda_prms_num_partials(torch.float32, D), M), device="cuda")
+    H = torch.empty_like(Hg)
+    r = torch.empty((M,), device="cuda")
+    coda.coda_gemm_res_prms(d["A"], d["W1"], d["R"], d["g"], H, Hg, P)
+    coda.coda_rms_combine(P, r, D, wl.eps)
+    Y = torch.empty((M, V), device="cuda")
+    coda.coda_gemm_rowscale(Hg, d["W2"], r, Y)
+    T = coda.coda_prms_num_partials(torch.float32, V)
+    pmax = torch.full((T, M), float("nan"), device="cuda")
+    psum = torch.full_like(pmax, float("nan"))
+    tgt = torch.full((M,), float("nan"), device="cuda")
+    coda.coda_gemm_rowscale_lse(Hg, d["W2"], r, tt, pmax, psum, tgt)
+    torch.cuda.synchronize()
+    y = Y.cpu().numpy()
+    pm, ps = pmax.cpu().numpy(), psum.cpu().numpy()
+    for ti in range(T):
+        cols = slice(64 * ti, min(64 * ti + 64, V))
+        if 64 * ti >= V:
+            assert np.all(pm[ti] == -np.inf) and np.all(ps[ti] == 0.0)
+            continue
+        np.testing.assert_array_equal(pm[ti], y[:, cols].max(axis=1))
+        ref = np.sum(np.exp(y[:, cols].astype(np.float64) - pm[ti][:, None]), axis=1)
+        np.testing.assert_allclose(ps[ti], ref, rtol=2e-6)
+    np.testing.assert_array_equal(tgt.cpu().numpy(), y[np.arange(M), t])
+
+
+def test_invalid_target_gives_nan_only_there():
+    wl = ci.custom_workload(64, 128, 256, 512, wl_id=602)
+    t = ci.make_targets(wl, seed=3)
+    t[5] = -1
+    t[9] = 512
+    x, d, t, tt, o = _run(wl, seed=3, targets=t)
+    loss = o["loss"].cpu().numpy()
+    assert np.isnan(loss[5]) and np.isnan(loss[9])
+    ok = np.ones(64, bool)
+    ok[[5, 9]] = False
+    assert np.isfinite(loss[ok]).all()
+    orc = oracle.forward_ce(x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps,
+                            np.where(ok, t, 0))
+    assert max_rel(loss[ok], orc["loss"][ok]) <= 1e-2
+
+
+@pytest.mark.slow
+def test_full_size_7b_lm_head_sampled_rows():
+    wl = ci.WORKLOADS["7b-ce-bf16"]
+    x, d, t, tt, o = _run(wl, seed=0)
+    rng = np.random.default_rng(21)
+    rows = np.unique(np.concatenate([[0, 255, 256, wl.M - 1], rng.integers(0, wl.M, 20)]))
+    err = _check(wl, x, t, o, rows=rows)
+    print(f"7b-ce sampled-row loss error {err:.3e}")
+    assert torch.isfinite(o["loss"]).all().item()

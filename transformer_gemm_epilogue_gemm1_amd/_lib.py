@@ -33,6 +33,9 @@ SIGNATURES = {
     "coda_gemm_rowscale_swiglu": (c_int, [c_int, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp,
                                           c_vp, c_i64, c_vp, c_i64, c_vp]),
     "coda_swiglu_bwd": (c_int, [c_int, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
+    "coda_gemm_rowscale_lse": (c_int, [c_int, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp,
+                                       c_vp, c_vp, c_vp]),
+    "coda_ce_combine": (c_int, [c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "coda_gemm_res_prms_fp8": (c_int, [c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_i64,
                                        c_vp, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp]),
     "coda_gemm_rowscale_fp8": (c_int, [c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_i64,

@@ -145,6 +145,44 @@ def coda_swiglu_bwd(dZ, Y, dY, stream=None) -> None:
     _lib.check("coda_swiglu_bwd", st)
 
 
+def coda_gemm_rowscale_lse(X, Wv, r: Optional[torch.Tensor], targets, pmax, psum, tgt, stream=None) -> None:
+    """LM-head GEMM writing the cross-entropy statistics (per-tile max and
+    sum-exp of y = diag(r) X Wv, and the target logit) instead of the logits."""
+    lib = _lib.load()
+    dt = X.dtype
+    M, D = X.shape
+    V = Wv.shape[1]
+    T = coda_prms_num_partials(dt, V)
+    ldx = _mat(X, "X", dt, (M, D))
+    ldw = _mat(Wv, "Wv", dt, (D, V))
+    _mat(targets, "targets", torch.int32, (M,))
+    for t, n in ((pmax, "pmax"), (psum, "psum")):
+        _mat(t, n, torch.float32, (T, M))
+        _dense(t, n)
+    _mat(tgt, "tgt", torch.float32, (M,))
+    if r is not None:
+        _mat(r, "r", torch.float32, (M,))
+    st = lib.coda_gemm_rowscale_lse(_dtype_code(X), M, D, V, X.data_ptr(), ldx, Wv.data_ptr(), ldw,
+                                    r.data_ptr() if r is not None else None, targets.data_ptr(), pmax.data_ptr(),
+                                    psum.data_ptr(), tgt.data_ptr(), _stream(stream))
+    _lib.check("coda_gemm_rowscale_lse", st)
+
+
+def coda_ce_combine(pmax, psum, tgt, targets, lse, loss, V: int, stream=None) -> None:
+    """lse and per-token loss from the LM-head statistics."""
+    lib = _lib.load()
+    T, M = pmax.shape
+    for t, n in ((pmax, "pmax"), (psum, "psum")):
+        _mat(t, n, torch.float32, (T, M))
+        _dense(t, n)
+    for t, n in ((tgt, "tgt"), (lse, "lse"), (loss, "loss")):
+        _mat(t, n, torch.float32, (M,))
+    _mat(targets, "targets", torch.int32, (M,))
+    st = lib.coda_ce_combine(M, V, T, pmax.data_ptr(), psum.data_ptr(), tgt.data_ptr(), targets.data_ptr(),
+                             lse.data_ptr(), loss.data_ptr(), _stream(stream))
+    _lib.check("coda_ce_combine", st)
+
+
 _FP8 = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
 
 
@@ -327,3 +365,25 @@ def fused_forward_fp8(A8, sa, W1t8, sw1, R, g, W2t8, sw2, eps: float, stream=Non
     coda_rms_combine(P, r, D, eps, stream)
     coda_gemm_rowscale_fp8(Hg8, W2t8, sw2, r, Y, stream)
     return H, Hg8, r, Y, P
+
+
+def fused_forward_ce(A, W1, R, g, Wv, eps: float, targets, stream=None):
+    """The chain ending in the LM head and the per-token cross-entropy:
+    returns (H, r, lse, loss); the logits are never materialised."""
+    M, D, V = A.shape[0], W1.shape[1], Wv.shape[1]
+    dev, dt = A.device, A.dtype
+    H = torch.empty((M, D), device=dev, dtype=dt)
+    Hg = torch.empty((M, D), device=dev, dtype=dt)
+    P = torch.empty((coda_prms_num_partials(dt, D), M), device=dev, dtype=torch.float32)
+    r = torch.empty((M,), device=dev, dtype=torch.float32)
+    T = coda_prms_num_partials(dt, V)
+    pmax = torch.empty((T, M), device=dev, dtype=torch.float32)
+    psum = torch.empty((T, M), device=dev, dtype=torch.float32)
+    tgt = torch.empty((M,), device=dev, dtype=torch.float32)
+    lse = torch.empty((M,), device=dev, dtype=torch.float32)
+    loss = torch.empty((M,), device=dev, dtype=torch.float32)
+    coda_gemm_res_prms(A, W1, R, g, H, Hg, P, stream)
+    coda_rms_combine(P, r, D, eps, stream)
+    coda_gemm_rowscale_lse(Hg, Wv, r, targets, pmax, psum, tgt, stream)
+    coda_ce_combine(pmax, psum, tgt, targets, lse, loss, V, stream)
+    return H, r, lse, loss

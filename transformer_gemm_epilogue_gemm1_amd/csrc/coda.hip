@@ -434,6 +434,62 @@ coda_status coda_gemm_rowscale_fp8(int64_t M, int64_t D, int64_t N2, const void*
                                          ep, (hipStream_t)stream);
 }
 
+coda_status coda_gemm_rowscale_lse(coda_dtype dt, int64_t M, int64_t D, int64_t V, const void* X, int64_t ldx,
+                                   const void* Wv, int64_t ldw, const float* r, const int32_t* targets, float* pmax,
+                                   float* psum, float* tgt, void* stream) {
+  coda_status st = check_dims(dt, M, {{"D", D}, {"V", V}});
+  if (st != CODA_OK) return st;
+  if (M == 0) return ok();
+  const int es = elem_size(dt), E = elems_per_chunk(dt);
+  const int64_t T = num_partials(V);
+  const Mat mX{X, M, D, ldx, es, "X"}, mW{Wv, D, V, ldw, es, "Wv"};
+  for (const Mat* m : {&mX, &mW})
+    if ((st = check_mat(*m, E)) != CODA_OK) return st;
+  if (targets == nullptr || pmax == nullptr || psum == nullptr || tgt == nullptr)
+    return fail(CODA_ERR_NULL, "targets, pmax, psum and tgt must be set");
+  if ((((uintptr_t)targets | (uintptr_t)pmax | (uintptr_t)psum | (uintptr_t)tgt) & 3) != 0 ||
+      (r != nullptr && ((uintptr_t)r & 3) != 0))
+    return fail(CODA_ERR_ALIGN, "r, targets, pmax, psum and tgt must be 4-byte aligned");
+  const Mat mpm{pmax, T, M, M, 4, "pmax"}, mps{psum, T, M, M, 4, "psum"}, mtg{tgt, 1, M, M, 4, "tgt"};
+  const Mat mt{targets, 1, M, M, 4, "targets"}, mr{r, 1, M, M, 4, "r"};
+  if (mpm.span() > kMaxSpan) return fail(CODA_ERR_SHAPE, "pmax span too large");
+  const Mat none{nullptr, 0, 0, 0, 4, ""};
+  const Mat outs[3] = {mpm, mps, mtg};
+  const Mat ins[4] = {mX, mW, mt, r ? mr : none};
+  if ((st = check_alias(outs, 3, ins, 4)) != CODA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == CODA_BF16) {
+    typename EpiLSE<uint16_t>::Params ep{r, targets, pmax, psum, tgt};
+    return launch_gemm<uint16_t, true, false, EpiLSE<uint16_t>>("coda_gemm_rowscale_lse", (int)M, (int)V, (int)D,
+                                                                X, ldx, Wv, ldw, ep, s);
+  }
+  typename EpiLSE<float>::Params ep{r, targets, pmax, psum, tgt};
+  return launch_gemm<float, true, false, EpiLSE<float>>("coda_gemm_rowscale_lse", (int)M, (int)V, (int)D, X, ldx,
+                                                        Wv, ldw, ep, s);
+}
+
+coda_status coda_ce_combine(int64_t M, int64_t V, int64_t T, const float* pmax, const float* psum, const float* tgt,
+                            const int32_t* targets, float* lse, float* loss, void* stream) {
+  if (M < 0 || M > kMaxDim) return fail(CODA_ERR_SHAPE, "M = %lld out of range", (long long)M);
+  if (V < 1 || V > kMaxDim) return fail(CODA_ERR_SHAPE, "V = %lld out of range", (long long)V);
+  if (T < 1 || T > 65536) return fail(CODA_ERR_SHAPE, "T = %lld out of range", (long long)T);
+  if (M == 0) return ok();
+  if (!pmax || !psum || !tgt || !targets || !lse || !loss) return fail(CODA_ERR_NULL, "a pointer is NULL");
+  if ((((uintptr_t)pmax | (uintptr_t)psum | (uintptr_t)tgt | (uintptr_t)targets | (uintptr_t)lse |
+        (uintptr_t)loss) & 3) != 0)
+    return fail(CODA_ERR_ALIGN, "arrays must be 4-byte aligned");
+  const Mat mpm{pmax, T, M, M, 4, "pmax"}, mps{psum, T, M, M, 4, "psum"}, mtg{tgt, 1, M, M, 4, "tgt"};
+  const Mat mt{targets, 1, M, M, 4, "targets"}, ml{lse, 1, M, M, 4, "lse"}, mlo{loss, 1, M, M, 4, "loss"};
+  if (mpm.span() > kMaxSpan) return fail(CODA_ERR_SHAPE, "pmax span too large");
+  const Mat outs[2] = {ml, mlo};
+  const Mat ins[4] = {mpm, mps, mtg, mt};
+  coda_status st;
+  if ((st = check_alias(outs, 2, ins, 4)) != CODA_OK) return st;
+  hipLaunchKernelGGL(ce_combine_kernel, dim3((unsigned)((M + 63) / 64)), dim3(256), 0, (hipStream_t)stream, pmax, psum,
+                     tgt, targets, lse, loss, (int)M, (int)T, (int)V);
+  return launch_status("coda_ce_combine");
+}
+
 size_t coda_ref_chain_workspace_bytes(coda_dtype dt, int64_t M, int64_t D) {
   if ((dt != CODA_BF16 && dt != CODA_F32) || M < 0 || D < 1) return 0;
   const size_t c = (size_t)M * D * 4;

@@ -213,6 +213,94 @@ struct EpiSwiGLU {
   __device__ __forceinline__ void finish() {}
 };
 
+// (max, sum e^(y - max)) statistics merged: the online-normalisation state.
+// An empty side is (-inf, 0); two empty sides stay empty.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float mm = fmaxf(m, m2);
+  if (mm == -INFINITY) return;
+  s = s * __builtin_amdgcn_exp2f((m - mm) * 1.4426950408889634f) +
+      s2 * __builtin_amdgcn_exp2f((m2 - mm) * 1.4426950408889634f);
+  m = mm;
+}
+
+// The chain's second GEMM as the LM head, ending in the cross-entropy
+// statistics instead of the logits (CODA news article by Synced, sections
+// "CODA：「尾声」里藏着宝藏" and "五种「积木」和一套「乐高语言」": the tile
+// log-sum-exp reduction and the max / sum-exp state of online
+// normalisation).  With y = r[row] * acc, never written to memory:
+//   pmax[t][row] = max of y over the 64 columns of partial tile t
+//   psum[t][row] = sum of e^(y - pmax) over those columns
+//   tgt[row]     = y at column targets[row] (by the lane holding it)
+// t = 4 * (column tile) + (column quarter), as for the partial RMS; a
+// partial tile past the last column gets (-inf, 0).  Lanes reduce their 8
+// columns, then the 8 lanes of a row group merge in fixed order.
+template <typename T>
+struct EpiLSE {
+  struct Params {
+    const float* r;        // [M] or null
+    const int* targets;    // [M]
+    float* pmax;           // [T][M]
+    float* psum;           // [T][M]
+    float* tgt;            // [M]
+  };
+  Params p;
+  RowScalars rs;
+  int tg[kFragM][2];
+  float mx[2], sm[2];
+  int lane, t, M;
+  __device__ __forceinline__ EpiLSE(const Params& p_, int lane_, int wm, int wn, int m0, int, int tn, int M_, int)
+      : p(p_), lane(lane_), t(4 * tn + wn), M(M_) {
+    const int row_base = m0 + wm * kWaveM;
+    if (p.r != nullptr) rs.prefetch(p.r, row_base, lane, M_);
+#pragma unroll
+    for (int mt = 0; mt < kFragM; ++mt)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int row = epi_row(row_base, mt, q, lane);
+        tg[mt][q] = row < M_ ? p.targets[row] : -1;
+      }
+    mx[0] = mx[1] = -INFINITY;
+    sm[0] = sm[1] = 0.f;
+  }
+  __device__ __forceinline__ void apply(int mt, int q, int row, int col, float v[8]) {
+    const float s = p.r != nullptr ? rs.v[mt][q] : 1.f;
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] *= s;
+      m = fmaxf(m, v[i]);
+    }
+    float e = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e += __builtin_amdgcn_exp2f((v[i] - m) * 1.4426950408889634f);
+    mx[q] = m;
+    sm[q] = e;
+    const int k = tg[mt][q] - col;
+    if (k >= 0 && k < 8) {
+      float y = v[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) y = k == i ? v[i] : y;
+      p.tgt[row] = y;
+    }
+  }
+  __device__ __forceinline__ void end_slab(int slab_row0) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      float m = mx[q], s = sm[q];
+#pragma unroll
+      for (int x = 1; x < 8; x <<= 1) lse_merge(m, s, __shfl_xor(m, x), __shfl_xor(s, x));
+      const int row = slab_row0 + (lane >> 3) + 8 * q;
+      if ((lane & 7) == 0 && row < M) {
+        p.pmax[(int64_t)t * M + row] = m;
+        p.psum[(int64_t)t * M + row] = s;
+      }
+      mx[q] = -INFINITY;
+      sm[q] = 0.f;
+    }
+  }
+  __device__ __forceinline__ void finish() {}
+};
+
 // Plain float32 output of the accumulators (the unfused chain's first GEMM).
 struct EpiStoreF32 {
   struct Params {

@@ -164,4 +164,49 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const T* __restrict__ d
   }
 }
 
+// Cross-entropy combine, 64 rows per 256-thread workgroup: wavefront q
+// merges the (max, sum-exp) statistics of its quarter of the T partial tiles
+// in increasing t, then the quarters are merged first to last (fixed order):
+//   lse_i  = M_i + log(sum_t psum[t][i] e^(pmax[t][i] - M_i)),  M_i = max_t pmax
+//   loss_i = lse_i - tgt[i], or NaN when targets[i] is outside [0, V).
+__global__ __launch_bounds__(256) void ce_combine_kernel(const float* __restrict__ pmax,
+                                                         const float* __restrict__ psum,
+                                                         const float* __restrict__ tgt,
+                                                         const int* __restrict__ targets, float* __restrict__ lse,
+                                                         float* __restrict__ loss, int M, int T, int V) {
+  __shared__ float red_m[4][64], red_s[4][64];
+  const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 64 + lane;
+  const int tq = (T + 3) / 4;
+  const int t0 = q * tq, t1 = t0 + tq < T ? t0 + tq : T;
+  float m = -INFINITY, s = 0.f;
+  if (i < M) {
+    for (int t = t0; t < t1; ++t) {
+      const float pm = pmax[(int64_t)t * M + i], ps = psum[(int64_t)t * M + i];
+      const float mm = fmaxf(m, pm);
+      if (mm != -INFINITY) {
+        s = s * expf(m - mm) + ps * expf(pm - mm);
+        m = mm;
+      }
+    }
+  }
+  red_m[q][lane] = m;
+  red_s[q][lane] = s;
+  __syncthreads();
+  if (q == 0 && i < M) {
+    for (int k = 1; k < 4; ++k) {
+      const float pm = red_m[k][lane], ps = red_s[k][lane];
+      const float mm = fmaxf(m, pm);
+      if (mm != -INFINITY) {
+        s = s * expf(m - mm) + ps * expf(pm - mm);
+        m = mm;
+      }
+    }
+    const float l = m + logf(s);
+    lse[i] = l;
+    const int ti = targets[i];
+    loss[i] = (ti >= 0 && ti < V) ? l - tgt[i] : __builtin_nanf("");
+  }
+}
+
 }  // namespace coda
