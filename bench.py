@@ -56,6 +56,8 @@ def parse():
                     help="seconds of back-to-back forward chains while amd-smi samples socket power and "
                          "gfx clocks (0 disables; skipped when amd-smi is absent)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 (e4m3) chain at the 7B shape")
+    ap.add_argument("--no-ce", action="store_true",
+                    help="skip the chain ending in the LM head and the per-token cross-entropy")
     ap.add_argument("--no-swiglu", action="store_true",
                     help="skip the SwiGLU-gated chain (forward, and the training step when timing the backward)")
     ap.add_argument("--no-backward", action="store_true",
@@ -226,6 +228,71 @@ def bench_forward_shape(wl, stream, steps, warmup, seed):
     return {"shape": {"M": M, "K": K, "D": D, "N2": N2}, "ms_per_step": round(ms, 4), "value": round(tf, 2),
             "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
             "coda_gemm_rowscale_frac": round(g2_tf / PEAK_BF16_TFLOPS, 4)}
+
+
+def bench_ce(args, up, stream):
+    """The chain ending in the LM head (7B hidden size, vocabulary 32000) and
+    the per-token cross-entropy, fused (the logits never leave the
+    registers), beside the same chain writing the bf16 logits followed by
+    torch's cross_entropy, and the whole chain in plain PyTorch."""
+    import torch
+
+    import coda_inputs as ci
+    import transformer_gemm_epilogue_gemm1_amd as coda
+
+    wl = ci.WORKLOADS["7b-ce-bf16"]
+    x = ci.make_inputs(wl, seed=args.seed)
+    d = {k: up(v) for k, v in x.items()}
+    M, K, D, V = wl.M, wl.K, wl.D, wl.N2
+    dev, tdt = d["A"].device, d["A"].dtype
+    targets = torch.from_numpy(ci.make_targets(wl, seed=args.seed)).to(dev)
+    H = torch.empty((M, D), device=dev, dtype=tdt)
+    Hg = torch.empty_like(H)
+    P = torch.empty((coda.coda_prms_num_partials(tdt, D), M), device=dev, dtype=torch.float32)
+    r = torch.empty((M,), device=dev, dtype=torch.float32)
+    T = coda.coda_prms_num_partials(tdt, V)
+    pmax = torch.empty((T, M), device=dev, dtype=torch.float32)
+    psum = torch.empty_like(pmax)
+    tgt = torch.empty((M,), device=dev, dtype=torch.float32)
+    lse = torch.empty_like(tgt)
+    loss = torch.empty_like(tgt)
+    Y = torch.empty((M, V), device=dev, dtype=tdt)
+
+    def head():
+        coda.coda_gemm_res_prms(d["A"], d["W1"], d["R"], d["g"], H, Hg, P, stream)
+        coda.coda_rms_combine(P, r, D, wl.eps, stream)
+
+    def fused():
+        head()
+        coda.coda_gemm_rowscale_lse(Hg, d["W2"], r, targets, pmax, psum, tgt, stream)
+        coda.coda_ce_combine(pmax, psum, tgt, targets, lse, loss, V, stream)
+
+    def logits_then_torch():
+        head()
+        coda.coda_gemm_rowscale(Hg, d["W2"], r, Y, stream)
+        return torch.nn.functional.cross_entropy(Y.float(), targets.long(), reduction="none")
+
+    n = max(5, args.steps // 2)
+    w = max(2, args.warmup // 2)
+    f_ms = time_ms(fused, stream, n, w)
+    l_ms = time_ms(logits_then_torch, stream, n, w)
+    out = {"workload": f"7b-ce-bf16: M={M} K={K} D={D} vocabulary V={V}, per-token loss",
+           "fused_ms": round(f_ms, 4), "fused_tflops": round(wl.fwd_flops / (f_ms * 1e-3) / 1e12, 2),
+           "logits_then_torch_ce_ms": round(l_ms, 4), "speedup_vs_logits_then_torch_ce": round(l_ms / f_ms, 4)}
+    if not args.no_torch_chain:
+        gf = d["g"].float()
+
+        def torch_chain():
+            Ht = torch.addmm(d["R"], d["A"], d["W1"])
+            hf = Ht.float()
+            rt = torch.rsqrt(hf.square().mean(dim=1, keepdim=True) + wl.eps)
+            logits = torch.matmul((hf * rt * gf).to(tdt), d["W2"])
+            return torch.nn.functional.cross_entropy(logits.float(), targets.long(), reduction="none")
+
+        t_ms = time_ms(torch_chain, stream, n, w)
+        out["torch_chain_ms"] = round(t_ms, 4)
+        out["speedup_vs_torch_chain"] = round(t_ms / f_ms, 4)
+    return out
 
 
 def bench_fp8(args, stream):
@@ -627,6 +694,9 @@ def main():
 
     if not args.no_fp8:
         out["fp8"] = bench_fp8(args, stream)
+
+    if not args.no_ce:
+        out["ce"] = bench_ce(args, up, stream)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
