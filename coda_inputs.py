@@ -71,6 +71,9 @@ WORKLOADS: Dict[str, Workload] = {
         # 7B-style chain ending in the LM head (vocabulary 32000) and the
         # per-token cross-entropy
         Workload("7b-ce-bf16", 6, 16384, 4096, 4096, 32000, 1e-5, "bf16"),
+        # 7B-style chain whose second GEMM is the attention QKV projection
+        # (32 query, 32 key and 32 value heads of 128) with RoPE
+        Workload("7b-rope-bf16", 7, 16384, 4096, 4096, 12288, 1e-5, "bf16"),
     ]
 }
 
@@ -207,3 +210,9 @@ def make_inputs_fp8(wl: Workload, seed: int = 0) -> Dict[str, object]:
 def make_targets(wl: Workload, seed: int = 0) -> np.ndarray:
     """One target class per row, uniform over the N2 (vocabulary) columns, int32."""
     return generator(seed, wl.wl_id, "targets").integers(0, wl.N2, size=wl.M).astype(np.int32)
+
+
+def make_positions(wl: Workload, seq_len: int = 2048) -> np.ndarray:
+    """Token positions of the rows: M / seq_len sequences of seq_len tokens
+    (position = row mod seq_len), int32."""
+    return (np.arange(wl.M) % seq_len).astype(np.int32)

@@ -1,4 +1,4 @@
-"""CPU fp64 oracle for the GEMM-Residual-RMSNorm-GEMM chain (its SwiGLU epilogue, its fp8 variant and its cross-entropy head).
+"""CPU fp64 oracle for the GEMM-Residual-RMSNorm-GEMM chain (its SwiGLU epilogue, fp8 variant, cross-entropy head and RoPE projection).
 
 TEST INFRASTRUCTURE ONLY: imported by the test-suite, the smoke check and the
 benchmark's CPU-baseline leg, never by the library or its Python binding.
@@ -7,3 +7,4 @@ from .chain import backward, forward  # noqa: F401
 from .swiglu import backward_swiglu, forward_swiglu, silu, swiglu_dy  # noqa: F401
 from .fp8 import bf16_round, e4m3_decode, e4m3_encode, forward_fp8  # noqa: F401
 from .ce import cross_entropy_rows, forward_ce, logsumexp_rows  # noqa: F401
+from .rope import forward_rope, rope_angles, rope_rotate  # noqa: F401
