@@ -169,6 +169,56 @@ coda_status coda_ce_combine(int64_t M, int64_t V, int64_t T, const float* pmax, 
                             const float* tgt, const int32_t* targets, float* lse, float* loss,
                             void* stream);
 
+/* ---- QKV projection with RoPE -------------------------------------------
+ * The article says the re-parameterisation covers RoPE (section
+ * "CODA：「尾声」里藏着宝藏") and counts RoPE among the element-wise epilogue
+ * transforms (section "五种「积木」和一套「乐高语言」"); it does not write RoPE
+ * out.  Reading taken (the rotary embedding in its interleaved form): the
+ * chain's second GEMM is the attention QKV projection, its output columns
+ * [Q | K | V] with n_q and n_k columns of heads of d_head columns; inside a
+ * Q or K head the pair (2i, 2i+1), i < d_head/2, of row m turns by the angle
+ * p_m theta_i, theta_i = base^(-2i/d_head), p_m the row's position:
+ *   Y_m,2i = y_2i cos - y_2i+1 sin,   Y_m,2i+1 = y_2i sin + y_2i+1 cos.
+ * V columns are not rotated.  The unrotated [M,N2] projection is never
+ * written. */
+
+/* Rotary table: cos_sin[(p * d_head/2 + i) * 2 + {0, 1}] = cos, sin of
+ * p theta_i for p < max_pos, i < d_head/2, evaluated in double precision and
+ * rounded to float.  cos_sin: float[max_pos * d_head], 8-byte aligned,
+ * written on `stream`.  d_head even; base finite and > 0 (10000 in the
+ * original RoPE, 500000 in LLaMA 3). */
+coda_status coda_rope_cache(float* cos_sin, int64_t max_pos, int64_t d_head, double base,
+                            void* stream);
+
+/* Second GEMM with the deferred row scale and RoPE in the epilogue: with
+ * y = r_i * (X W2)_ik (fp32), Y = round(rotate(y)) as above, using the
+ * table entries cos_sin[positions[i]] (so theta and base are the table's).
+ *   X: [M,D] (ldx, e.g. Hg); W2: [D,N2] (ldw2, W_qkv); r: float[M] or NULL;
+ *   positions: int32[M]; cos_sin: the table of coda_rope_cache, float
+ *   [max_pos * d_head], 16-byte aligned; Y: [M,N2] (ldy).
+ * d_head a multiple of 8 in [8, 4096]; n_q, n_k whole heads (>= 0) with
+ * n_q + n_k <= N2.  A position outside [0, max_pos) is not read: the row's
+ * rotated columns become NaN (its V columns stay valid).  Y must not overlap
+ * any input. */
+coda_status coda_gemm_rowscale_rope(coda_dtype dt, int64_t M, int64_t D, int64_t N2,
+                                    const void* X, int64_t ldx, const void* W2, int64_t ldw2,
+                                    const float* r, const int32_t* positions,
+                                    const float* cos_sin, int64_t max_pos,
+                                    int64_t n_q, int64_t n_k, int64_t d_head,
+                                    void* Y, int64_t ldy, void* stream);
+
+/* Backward through RoPE (the derivative of the reading above; the rotation
+ * is orthogonal, so the gradient turns back by the same angle):
+ *   dY_m,2i = g_2i cos + g_2i+1 sin,   dY_m,2i+1 = g_2i+1 cos - g_2i sin
+ * in the rotated columns (NaN for a position outside [0, max_pos)), dY = g in
+ * the V columns.  dYr: the gradient of the rotated output [M,N2] (ldg); dY:
+ * [M,N2] (lddy), the dY that coda_chain_bwd takes.  Arguments and limits as
+ * coda_gemm_rowscale_rope; dY must not overlap dYr, positions or cos_sin. */
+coda_status coda_rope_bwd(coda_dtype dt, int64_t M, int64_t N2, const void* dYr, int64_t ldg,
+                          const int32_t* positions, const float* cos_sin, int64_t max_pos,
+                          int64_t n_q, int64_t n_k, int64_t d_head,
+                          void* dY, int64_t lddy, void* stream);
+
 /* ---- fp8 operands -------------------------------------------------------
  * The article's opening section notes that FP8 makes the matrix products
  * faster while the memory-bound operations around them do not shrink, so

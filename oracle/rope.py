@@ -19,6 +19,8 @@ theta_i = base^(-2i / d):
 
     y'_2i   = y_2i cos(p theta_i) - y_2i+1 sin(p theta_i)
     y'_2i+1 = y_2i sin(p theta_i) + y_2i+1 cos(p theta_i)
+
+The backward of this linear map is its transpose, the rotation by -p theta_i.
 """
 from __future__ import annotations
 
@@ -47,6 +49,12 @@ def rope_rotate(Y, positions, n_q: int, n_k: int, d_head: int, base: float) -> n
         head[:, 0::2] = even * c - odd * s
         head[:, 1::2] = even * s + odd * c
     return Y
+
+
+def rope_backward(G, positions, n_q: int, n_k: int, d_head: int, base: float) -> np.ndarray:
+    """Gradient of the unrotated values from the gradient G of the rotated
+    ones: each pair turned back by its angle (the rotation's transpose)."""
+    return rope_rotate(G, -np.asarray(positions, dtype=np.float64), n_q, n_k, d_head, base)
 
 
 def forward_rope(A, W1, R, g, Wqkv, eps: float, positions, n_q: int, n_k: int, d_head: int, base: float,

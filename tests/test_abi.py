@@ -251,6 +251,59 @@ def test_ce_combine_validation(lib, args, status):
     assert lib.coda_ce_combine(*args, None) == status
 
 
+def rope_call(lib, dt=BF16, M=512, D=256, N2=1536, X=H_, ldx=None, W=W2_, ldw=None, r=R2_, pos=DY_, cs=DG_,
+              max_pos=2048, nq=512, nk=512, dh=128, Y=Y_, ldy=None):
+    return lib.coda_gemm_rowscale_rope(dt, M, D, N2, X, ldx or D, W, ldw or N2, r, pos, cs, max_pos, nq, nk, dh, Y,
+                                       ldy or N2, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=5), DTYPE),
+    (dict(dh=100), SHAPE),            # not a multiple of 8
+    (dict(dh=0), SHAPE),
+    (dict(nq=500), SHAPE),            # not whole heads
+    (dict(nk=-128), SHAPE),
+    (dict(nq=1024, nk=640), SHAPE),   # more rotated columns than the width
+    (dict(max_pos=0), SHAPE),
+    (dict(pos=None), NULL),
+    (dict(cs=None), NULL),
+    (dict(Y=None), NULL),
+    (dict(pos=DY_ + 2), ALIGN),
+    (dict(cs=DG_ + 8), ALIGN),
+    (dict(ldy=1540), ALIGN),
+    (dict(Y=DG_ + 4096), ALIAS),      # Y over the table
+    (dict(Y=DY_), ALIAS),             # Y over the positions
+    (dict(Y=H_ + 64), ALIAS),
+])
+def test_gemm_rowscale_rope_rejects(lib, kw, status):
+    assert rope_call(lib, **kw) == status
+
+
+def test_rope_empty_and_cache_validation(lib):
+    assert rope_call(lib, M=0, pos=None, cs=None) == OK
+    assert rope_call(lib, M=0, dh=12) == SHAPE
+    assert lib.coda_rope_cache(DG_, 2048, 127, 10000.0, None) == SHAPE
+    assert lib.coda_rope_cache(DG_, 0, 128, 10000.0, None) == SHAPE
+    assert lib.coda_rope_cache(DG_, 2048, 128, 0.0, None) == SHAPE
+    assert lib.coda_rope_cache(DG_, 2048, 128, float("inf"), None) == SHAPE
+    assert lib.coda_rope_cache(None, 2048, 128, 10000.0, None) == NULL
+    assert lib.coda_rope_cache(DG_ + 4, 2048, 128, 10000.0, None) == ALIGN
+    assert lib.coda_rope_cache(DG_, 1 << 22, 256, 10000.0, None) == SHAPE   # 4 GiB table
+
+
+@pytest.mark.parametrize("args,status", [
+    ((5, 512, 1536, Y_, 1536, DY_, DG_, 2048, 512, 512, 128, DA_, 1536), DTYPE),
+    ((BF16, 512, 1536, Y_, 1536, DY_, DG_, 2048, 512, 512, 96 + 4, DA_, 1536), SHAPE),
+    ((BF16, 512, 1536, None, 1536, DY_, DG_, 2048, 512, 512, 128, DA_, 1536), NULL),
+    ((BF16, 512, 1536, Y_, 1536, None, DG_, 2048, 512, 512, 128, DA_, 1536), NULL),
+    ((BF16, 512, 1536, Y_, 1536, DY_, DG_, 2048, 512, 512, 128, Y_ + 64, 1536), ALIAS),
+    ((BF16, 512, 1536, Y_, 1536, DY_, DG_, 2048, 512, 512, 128, DG_, 1536), ALIAS),
+    ((BF16, 0, 1536, None, 1536, None, None, 2048, 512, 512, 128, None, 1536), OK),
+])
+def test_rope_bwd_validation(lib, args, status):
+    assert lib.coda_rope_bwd(*args, None) == status
+
+
 def prms8(lib, M=512, K=256, D=512, A=A_, lda=None, sa=R2_, W=W1_, ldw=None, sw=G_ + 4096, R=R_, ldr=None, g=G_,
            H=H_, ldh=None, Hg=HG_, ldhg=None, part=PART_):
     return lib.coda_gemm_res_prms_fp8(M, K, D, A, lda or K, sa, W, ldw or K, sw, R, ldr or D, g, H, ldh or D, Hg,

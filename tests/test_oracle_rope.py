@@ -81,6 +81,27 @@ def test_inputs_and_shapes():
         oracle.forward_rope(*([np.zeros((1, 8))] * 3), np.ones(8), np.zeros((8, 24)), 1e-5, [0], 12, 8, 8, 1e4)
 
 
+def test_backward_is_the_adjoint():
+    # <rotate(y), G> = <y, rope_backward(G)> for all y, G (the gradient of a
+    # linear map), checked on the unit basis of a small case; and the backward
+    # inverts the rotation
+    d, nq, nk, nv = 8, 8, 8, 8
+    N = nq + nk + nv
+    pos = np.array([0, 3, 700])
+    G = _y(6, 3, N)
+    back = oracle.rope_backward(G, pos, nq, nk, d, 10000.0)
+    for i in range(3):
+        for j in range(N):
+            e = np.zeros((3, N))
+            e[i, j] = 1.0
+            fwd = oracle.rope_rotate(e, pos, nq, nk, d, 10000.0)
+            assert np.sum(fwd * G) == pytest.approx(back[i, j], abs=1e-13)
+    Y = _y(7, 3, N)
+    np.testing.assert_allclose(oracle.rope_backward(oracle.rope_rotate(Y, pos, nq, nk, d, 10000.0), pos, nq, nk, d,
+                                                    10000.0), Y, atol=1e-13)
+    np.testing.assert_array_equal(back[:, nq + nk:], G[:, nq + nk:])
+
+
 @pytest.mark.parametrize("kind", ["rotate_half_pairs", "theta_without_2", "sin_sign", "rotate_v"])
 def test_pins_reject_planted_mistakes(kind):
     d, nq, nk = 8, 16, 8

@@ -15,6 +15,7 @@ c_vp = ctypes.c_void_p
 c_int = ctypes.c_int
 c_float = ctypes.c_float
 c_size = ctypes.c_size_t
+c_double = ctypes.c_double
 
 CODA_BF16 = 0
 CODA_F32 = 1
@@ -36,6 +37,11 @@ SIGNATURES = {
     "coda_gemm_rowscale_lse": (c_int, [c_int, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp,
                                        c_vp, c_vp, c_vp]),
     "coda_ce_combine": (c_int, [c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "coda_rope_cache": (c_int, [c_vp, c_i64, c_i64, c_double, c_vp]),
+    "coda_gemm_rowscale_rope": (c_int, [c_int, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp,
+                                        c_i64, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp]),
+    "coda_rope_bwd": (c_int, [c_int, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp,
+                              c_i64, c_vp]),
     "coda_gemm_res_prms_fp8": (c_int, [c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_i64,
                                        c_vp, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp]),
     "coda_gemm_rowscale_fp8": (c_int, [c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_i64,

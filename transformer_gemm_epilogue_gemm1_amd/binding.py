@@ -168,6 +168,58 @@ def coda_gemm_rowscale_lse(X, Wv, r: Optional[torch.Tensor], targets, pmax, psum
     _lib.check("coda_gemm_rowscale_lse", st)
 
 
+def rope_cache(max_pos: int, d_head: int, base: float = 10000.0, device="cuda", stream=None) -> torch.Tensor:
+    """The rotary table [max_pos, d_head // 2, 2] (cos, sin) of coda_rope_cache."""
+    cs = torch.empty((max_pos, d_head // 2, 2), device=device, dtype=torch.float32)
+    st = _lib.load().coda_rope_cache(cs.data_ptr(), max_pos, d_head, float(base), _stream(stream))
+    _lib.check("coda_rope_cache", st)
+    return cs
+
+
+def _rope_args(positions, cos_sin, M: int, d_head: int):
+    _mat(positions, "positions", torch.int32, (M,))
+    if not isinstance(cos_sin, torch.Tensor) or cos_sin.dim() != 3 or tuple(cos_sin.shape[1:]) != (d_head // 2, 2):
+        raise ValueError(f"cos_sin must be the [max_pos, {d_head // 2}, 2] table of rope_cache")
+    if cos_sin.dtype != torch.float32 or cos_sin.device.type != "cuda":
+        raise TypeError("cos_sin must be a float32 device tensor")
+    _dense(cos_sin, "cos_sin")
+    return cos_sin.shape[0]
+
+
+def coda_gemm_rowscale_rope(X, Wqkv, r: Optional[torch.Tensor], positions, cos_sin, n_q: int, n_k: int,
+                            d_head: int, Y, stream=None) -> None:
+    """Y = rope(diag(r) X Wqkv): the QKV projection with the rotary embedding
+    applied to its first n_q + n_k columns (heads of d_head)."""
+    lib = _lib.load()
+    dt = X.dtype
+    M, D = X.shape
+    N2 = Wqkv.shape[1]
+    ldx = _mat(X, "X", dt, (M, D))
+    ldw = _mat(Wqkv, "Wqkv", dt, (D, N2))
+    ldy = _mat(Y, "Y", dt, (M, N2))
+    if r is not None:
+        _mat(r, "r", torch.float32, (M,))
+    max_pos = _rope_args(positions, cos_sin, M, d_head)
+    st = lib.coda_gemm_rowscale_rope(_dtype_code(X), M, D, N2, X.data_ptr(), ldx, Wqkv.data_ptr(), ldw,
+                                     r.data_ptr() if r is not None else None, positions.data_ptr(),
+                                     cos_sin.data_ptr(), max_pos, n_q, n_k, d_head, Y.data_ptr(), ldy,
+                                     _stream(stream))
+    _lib.check("coda_gemm_rowscale_rope", st)
+
+
+def coda_rope_bwd(dYr, positions, cos_sin, n_q: int, n_k: int, d_head: int, dY, stream=None) -> None:
+    """dY = the gradient dYr of the rotated projection turned back by RoPE."""
+    lib = _lib.load()
+    dt = dYr.dtype
+    M, N2 = dYr.shape
+    ldg = _mat(dYr, "dYr", dt, (M, N2))
+    lddy = _mat(dY, "dY", dt, (M, N2))
+    max_pos = _rope_args(positions, cos_sin, M, d_head)
+    st = lib.coda_rope_bwd(_dtype_code(dYr), M, N2, dYr.data_ptr(), ldg, positions.data_ptr(), cos_sin.data_ptr(),
+                           max_pos, n_q, n_k, d_head, dY.data_ptr(), lddy, _stream(stream))
+    _lib.check("coda_rope_bwd", st)
+
+
 def coda_ce_combine(pmax, psum, tgt, targets, lse, loss, V: int, stream=None) -> None:
     """lse and per-token loss from the LM-head statistics."""
     lib = _lib.load()
@@ -387,3 +439,20 @@ def fused_forward_ce(A, W1, R, g, Wv, eps: float, targets, stream=None):
     coda_gemm_rowscale_lse(Hg, Wv, r, targets, pmax, psum, tgt, stream)
     coda_ce_combine(pmax, psum, tgt, targets, lse, loss, V, stream)
     return H, r, lse, loss
+
+
+def fused_forward_rope(A, W1, R, g, Wqkv, eps: float, positions, cos_sin, n_q: int, n_k: int, d_head: int,
+                       stream=None):
+    """The chain whose second GEMM is the QKV projection with RoPE: returns
+    (H, Hg, r, Y) with Y the rotated [Q | K | V]."""
+    M, D, N2 = A.shape[0], W1.shape[1], Wqkv.shape[1]
+    dev, dt = A.device, A.dtype
+    H = torch.empty((M, D), device=dev, dtype=dt)
+    Hg = torch.empty((M, D), device=dev, dtype=dt)
+    P = torch.empty((coda_prms_num_partials(dt, D), M), device=dev, dtype=torch.float32)
+    r = torch.empty((M,), device=dev, dtype=torch.float32)
+    Y = torch.empty((M, N2), device=dev, dtype=dt)
+    coda_gemm_res_prms(A, W1, R, g, H, Hg, P, stream)
+    coda_rms_combine(P, r, D, eps, stream)
+    coda_gemm_rowscale_rope(Hg, Wqkv, r, positions, cos_sin, n_q, n_k, d_head, Y, stream)
+    return H, Hg, r, Y

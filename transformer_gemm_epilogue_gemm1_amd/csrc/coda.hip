@@ -14,6 +14,7 @@
 #include "../../include/coda.h"
 #include "epilogues.hpp"
 #include "epilogues_fp8.hpp"
+#include "epilogues_rope.hpp"
 #include "gemm_fp8.hpp"
 #include "rowops.hpp"
 
@@ -261,6 +262,27 @@ coda_status chain_bwd_impl(int M, int K, int D, int N2, const void* dY, const vo
                                                       typename EpiRowScale<T>::Params{nullptr, (T*)dW2, N2}, s);
 }
 
+// Shared checks of the RoPE entry points: head layout, positions, table.
+coda_status check_rope(int64_t M, int64_t N, const int32_t* positions, const float* cos_sin, int64_t max_pos,
+                       int64_t n_q, int64_t n_k, int64_t d_head, Mat* mpos, Mat* mcs) {
+  if (d_head < 8 || d_head > 4096 || d_head % 8 != 0)
+    return fail(CODA_ERR_SHAPE, "d_head = %lld is not a multiple of 8 in [8, 4096]", (long long)d_head);
+  if (n_q < 0 || n_k < 0 || n_q % d_head != 0 || n_k % d_head != 0)
+    return fail(CODA_ERR_SHAPE, "n_q = %lld and n_k = %lld must be whole heads of %lld", (long long)n_q,
+                (long long)n_k, (long long)d_head);
+  if (n_q + n_k > N) return fail(CODA_ERR_SHAPE, "n_q + n_k = %lld exceeds the width %lld", (long long)(n_q + n_k),
+                                 (long long)N);
+  if (max_pos < 1 || max_pos > kMaxDim) return fail(CODA_ERR_SHAPE, "max_pos = %lld out of range", (long long)max_pos);
+  if (M == 0) return CODA_OK;  // nothing is read
+  if (positions == nullptr || cos_sin == nullptr) return fail(CODA_ERR_NULL, "positions and cos_sin must be set");
+  if (((uintptr_t)positions & 3) != 0) return fail(CODA_ERR_ALIGN, "positions is not 4-byte aligned");
+  if (((uintptr_t)cos_sin & 15) != 0) return fail(CODA_ERR_ALIGN, "cos_sin is not 16-byte aligned");
+  *mpos = Mat{positions, 1, M, M, 4, "positions"};
+  *mcs = Mat{cos_sin, max_pos, d_head, d_head, 4, "cos_sin"};
+  if (mcs->span() > kMaxSpan) return fail(CODA_ERR_SHAPE, "cos_sin spans more than 2 GiB");
+  return CODA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -383,6 +405,76 @@ coda_status coda_swiglu_bwd(coda_dtype dt, int64_t M, int64_t F, const void* dZ,
     hipLaunchKernelGGL(swiglu_bwd_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)dZ, ldz,
                        (const float*)Y, ldy, (float*)dY, lddy, (int)F, nchunks);
   return launch_status("coda_swiglu_bwd");
+}
+
+coda_status coda_rope_cache(float* cos_sin, int64_t max_pos, int64_t d_head, double base, void* stream) {
+  if (d_head < 2 || d_head > 4096 || d_head % 2 != 0)
+    return fail(CODA_ERR_SHAPE, "d_head = %lld is not even in [2, 4096]", (long long)d_head);
+  if (max_pos < 1 || max_pos > kMaxDim) return fail(CODA_ERR_SHAPE, "max_pos = %lld out of range", (long long)max_pos);
+  if (!(base > 0.0) || isinf(base)) return fail(CODA_ERR_SHAPE, "base must be finite and > 0");
+  if (cos_sin == nullptr) return fail(CODA_ERR_NULL, "cos_sin is NULL");
+  if (((uintptr_t)cos_sin & 7) != 0) return fail(CODA_ERR_ALIGN, "cos_sin is not 8-byte aligned");
+  if (max_pos * d_head * 4 > kMaxSpan) return fail(CODA_ERR_SHAPE, "cos_sin spans more than 2 GiB");
+  const int64_t n = max_pos * (d_head / 2);
+  hipLaunchKernelGGL(rope_cache_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, cos_sin,
+                     n, (int)(d_head / 2), base);
+  return launch_status("coda_rope_cache");
+}
+
+coda_status coda_gemm_rowscale_rope(coda_dtype dt, int64_t M, int64_t D, int64_t N2, const void* X, int64_t ldx,
+                                    const void* W2, int64_t ldw2, const float* r, const int32_t* positions,
+                                    const float* cos_sin, int64_t max_pos, int64_t n_q, int64_t n_k, int64_t d_head,
+                                    void* Y, int64_t ldy, void* stream) {
+  coda_status st = check_dims(dt, M, {{"D", D}, {"N2", N2}});
+  if (st != CODA_OK) return st;
+  Mat mpos, mcs;
+  if ((st = check_rope(M, N2, positions, cos_sin, max_pos, n_q, n_k, d_head, &mpos, &mcs)) != CODA_OK) return st;
+  if (M == 0) return ok();
+  const int es = elem_size(dt), E = elems_per_chunk(dt);
+  const Mat mX{X, M, D, ldx, es, "X"}, mW2{W2, D, N2, ldw2, es, "W2"}, mY{Y, M, N2, ldy, es, "Y"};
+  const Mat mr{r, 1, M, M, 4, "r"};
+  for (const Mat* m : {&mX, &mW2, &mY})
+    if ((st = check_mat(*m, E)) != CODA_OK) return st;
+  if (r != nullptr && ((uintptr_t)r & 3) != 0) return fail(CODA_ERR_ALIGN, "r is not 4-byte aligned");
+  const Mat ins[5] = {mX, mW2, r ? mr : Mat{nullptr, 0, 0, 0, 4, "r"}, mpos, mcs};
+  if ((st = check_alias(&mY, 1, ins, 5)) != CODA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const int nrot = (int)(n_q + n_k), mp = (int)max_pos, dh = (int)d_head;
+  if (dt == CODA_BF16) {
+    typename EpiRowScaleRope<uint16_t>::Params ep{r, positions, cos_sin, mp, nrot, dh, (uint16_t*)Y, ldy};
+    return launch_gemm<uint16_t, true, false, EpiRowScaleRope<uint16_t>>("coda_gemm_rowscale_rope", (int)M, (int)N2,
+                                                                         (int)D, X, ldx, W2, ldw2, ep, s);
+  }
+  typename EpiRowScaleRope<float>::Params ep{r, positions, cos_sin, mp, nrot, dh, (float*)Y, ldy};
+  return launch_gemm<float, true, false, EpiRowScaleRope<float>>("coda_gemm_rowscale_rope", (int)M, (int)N2, (int)D,
+                                                                 X, ldx, W2, ldw2, ep, s);
+}
+
+coda_status coda_rope_bwd(coda_dtype dt, int64_t M, int64_t N2, const void* dYr, int64_t ldg,
+                          const int32_t* positions, const float* cos_sin, int64_t max_pos, int64_t n_q, int64_t n_k,
+                          int64_t d_head, void* dY, int64_t lddy, void* stream) {
+  coda_status st = check_dims(dt, M, {{"N2", N2}});
+  if (st != CODA_OK) return st;
+  Mat mpos, mcs;
+  if ((st = check_rope(M, N2, positions, cos_sin, max_pos, n_q, n_k, d_head, &mpos, &mcs)) != CODA_OK) return st;
+  if (M == 0) return ok();
+  const int es = elem_size(dt), E = elems_per_chunk(dt);
+  const Mat mG{dYr, M, N2, ldg, es, "dYr"}, mdY{dY, M, N2, lddy, es, "dY"};
+  for (const Mat* m : {&mG, &mdY})
+    if ((st = check_mat(*m, E)) != CODA_OK) return st;
+  const Mat ins[3] = {mG, mpos, mcs};
+  if ((st = check_alias(&mdY, 1, ins, 3)) != CODA_OK) return st;
+  const int64_t nchunks = M * N2 / 8;
+  const int blocks = (int)((nchunks + 255) / 256 < 16384 ? (nchunks + 255) / 256 : 16384);
+  hipStream_t s = (hipStream_t)stream;
+  const int nrot = (int)(n_q + n_k), mp = (int)max_pos, dh = (int)d_head;
+  if (dt == CODA_BF16)
+    hipLaunchKernelGGL(rope_bwd_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, (const uint16_t*)dYr, ldg, positions,
+                       cos_sin, mp, nrot, dh, (uint16_t*)dY, lddy, (int)N2, nchunks);
+  else
+    hipLaunchKernelGGL(rope_bwd_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)dYr, ldg, positions,
+                       cos_sin, mp, nrot, dh, (float*)dY, lddy, (int)N2, nchunks);
+  return launch_status("coda_rope_bwd");
 }
 
 coda_status coda_gemm_res_prms_fp8(int64_t M, int64_t K, int64_t D, const void* A8, int64_t lda, const float* sa,

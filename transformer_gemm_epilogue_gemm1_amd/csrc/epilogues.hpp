@@ -8,7 +8,7 @@
 // The GEMM kernel hands each lane 8 consecutive columns `col .. col+7` of one
 // row through apply(mt, q, row, col, v) (mt = which of the wavefront's eight
 // 16-row slabs, q = which of the lane's 2 rows in it), calls
-// end_slab(slab_row0) on every lane once the slab is done, and finish() on
+// end_slab(mt, slab_row0) on every lane once slab mt is done, and finish() on
 // every lane after the last slab.  Lanes l and l' with l/8 == l'/8 hold the
 // same rows; the 8 lanes of such a group together cover the wavefront's 64
 // columns, and lanes with equal l % 8 hold the same 8 columns in every slab.
@@ -119,7 +119,7 @@ struct EpiResPrms {
     }
   }
 
-  __device__ __forceinline__ void end_slab(int slab_row0) {
+  __device__ __forceinline__ void end_slab(int, int slab_row0) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       float s = ss[q];
@@ -155,7 +155,7 @@ struct EpiRowScale {
     for (int i = 0; i < 8; ++i) v[i] *= s;
     Chunk8<T>::store(p.Y + (int64_t)row * p.ldy + col, v);
   }
-  __device__ __forceinline__ void end_slab(int) {}
+  __device__ __forceinline__ void end_slab(int, int) {}
   __device__ __forceinline__ void finish() {}
 };
 
@@ -209,7 +209,7 @@ struct EpiSwiGLU {
       Chunk8<T>::store(p.Z + (int64_t)row * p.ldz + oc, z);
     }
   }
-  __device__ __forceinline__ void end_slab(int) {}
+  __device__ __forceinline__ void end_slab(int, int) {}
   __device__ __forceinline__ void finish() {}
 };
 
@@ -283,7 +283,7 @@ struct EpiLSE {
       p.tgt[row] = y;
     }
   }
-  __device__ __forceinline__ void end_slab(int slab_row0) {
+  __device__ __forceinline__ void end_slab(int, int slab_row0) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       float m = mx[q], s = sm[q];
@@ -312,7 +312,7 @@ struct EpiStoreF32 {
   __device__ __forceinline__ void apply(int, int, int row, int col, float v[8]) {
     Chunk8<float>::store(p.C + (int64_t)row * p.ldc + col, v);
   }
-  __device__ __forceinline__ void end_slab(int) {}
+  __device__ __forceinline__ void end_slab(int, int) {}
   __device__ __forceinline__ void finish() {}
 };
 
@@ -380,7 +380,7 @@ struct EpiBwdG {
     Chunk8<T>::store(p.Xn + o, xv);
   }
 
-  __device__ __forceinline__ void end_slab(int slab_row0) {
+  __device__ __forceinline__ void end_slab(int, int slab_row0) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       float s = ss[q];

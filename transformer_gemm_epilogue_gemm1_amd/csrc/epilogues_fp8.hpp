@@ -92,7 +92,7 @@ struct EpiResPrmsFp8 {
     *(u32x2*)(p.Hg8 + (int64_t)row * p.ldhg + col) = u32x2{lo, hi};
   }
 
-  __device__ __forceinline__ void end_slab(int slab_row0) {
+  __device__ __forceinline__ void end_slab(int, int slab_row0) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       float s = ss[q];
@@ -131,7 +131,7 @@ struct EpiRowScaleFp8 {
     for (int i = 0; i < 8; ++i) v[i] = (v[i] * s) * sw[i];
     Chunk8<uint16_t>::store(p.Y + (int64_t)row * p.ldy + col, v);
   }
-  __device__ __forceinline__ void end_slab(int) {}
+  __device__ __forceinline__ void end_slab(int, int) {}
   __device__ __forceinline__ void finish() {}
 };
 

@@ -335,7 +335,7 @@ __device__ __forceinline__ void kstep(char* const (&st)[kStages], const Dma<T, A
 //   apply(mt, q, row, col, v)  for rows < M and columns < N (col % 8 == 0);
 //                              row = row_base + 16 mt + l/8 + 8 q
 //                              (epi_row), v[8] the accumulators
-//   end_slab(slab_row0)        after all lanes applied one 16-row slab
+//   end_slab(mt, slab_row0)    after all lanes applied 16-row slab mt
 //   finish()                   on every lane after the last slab
 template <typename T, bool A_KC, bool B_KC, class Epi>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int row = row_base + mt * 16 + rl;
       if (row < g.M && col < g.N) epi.apply(mt, q, row, col, v);
     }
-    epi.end_slab(row_base + mt * 16);
+    epi.end_slab(mt, row_base + mt * 16);
     wave_lds_fence();  // the slab's reads are done before the next slab overwrites it
   }
   epi.finish();

@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int row = row_base + s * 16 + rl;
       if (row < g.M && col < g.N) epi.apply(s, q, row, col, v);
     }
-    epi.end_slab(row_base + s * 16);
+    epi.end_slab(s, row_base + s * 16);
     wave_lds_fence();
   }
   epi.finish();

@@ -209,4 +209,56 @@ __global__ __launch_bounds__(256) void ce_combine_kernel(const float* __restrict
   }
 }
 
+// Table of the rotary embedding: cos_sin[p][i] = (cos(p theta_i), sin(p theta_i))
+// with theta_i = base^(-2i / d_head), i < half = d_head / 2, evaluated in
+// double precision and stored as float.  One thread per entry.
+__global__ __launch_bounds__(256) void rope_cache_kernel(float* __restrict__ cs, int64_t n, int half, double base) {
+  const int64_t k = blockIdx.x * 256ll + threadIdx.x;
+  if (k >= n) return;
+  const int64_t p = k / half;
+  const int i = (int)(k - p * half);
+  const double theta = pow(base, -(double)i / (double)half);
+  double sn, cn;
+  sincos((double)p * theta, &sn, &cn);
+  *(float2*)(cs + 2 * k) = float2{(float)cn, (float)sn};
+}
+
+// Gradient through the rotary embedding: the rotation is orthogonal, so the
+// gradient of the unrotated values is the incoming gradient turned back,
+//   dY_2i = g_2i c_i + g_2i+1 s_i,  dY_2i+1 = -g_2i s_i + g_2i+1 c_i,
+// in the rotated columns [0, n_rot) (NaN for a position outside
+// [0, max_pos)), copied in the others.  One thread per 8-column chunk.
+template <typename T>
+__global__ __launch_bounds__(256) void rope_bwd_kernel(const T* __restrict__ dYr, int64_t ldg,
+                                                       const int* __restrict__ positions,
+                                                       const float* __restrict__ cos_sin, int max_pos, int n_rot,
+                                                       int d_head, T* __restrict__ dY, int64_t lddy, int N,
+                                                       int64_t nchunks) {
+  const int cpr = N / 8;
+  for (int64_t k = blockIdx.x * 256ll + threadIdx.x; k < nchunks; k += (int64_t)gridDim.x * 256) {
+    const int64_t row = k / cpr;
+    const int col = (int)(k - row * cpr) * 8;
+    float gv[8];
+    Chunk8<T>::load(dYr + row * ldg + col, gv);
+    if (col < n_rot) {
+      const int pp = positions[row];
+      if ((unsigned)pp < (unsigned)max_pos) {
+        const float* t = cos_sin + (int64_t)pp * d_head + col % d_head;
+        const f32x4 a = *(const f32x4*)t, b = *(const f32x4*)(t + 4);
+        const float c[4] = {a[0], a[2], b[0], b[2]}, s[4] = {a[1], a[3], b[1], b[3]};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = gv[2 * i], o = gv[2 * i + 1];
+          gv[2 * i] = e * c[i] + o * s[i];
+          gv[2 * i + 1] = o * c[i] - e * s[i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gv[i] = __builtin_nanf("");
+      }
+    }
+    Chunk8<T>::store(dY + row * lddy + col, gv);
+  }
+}
+
 }  // namespace coda
