@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 (e4m3) chain at the 7B shape")
     ap.add_argument("--no-ce", action="store_true",
                     help="skip the chain ending in the LM head and the per-token cross-entropy")
+    ap.add_argument("--no-rope", action="store_true",
+                    help="skip the QKV projection with RoPE (7B attention shape)")
     ap.add_argument("--no-swiglu", action="store_true",
                     help="skip the SwiGLU-gated chain (forward, and the training step when timing the backward)")
     ap.add_argument("--no-backward", action="store_true",
@@ -70,21 +72,28 @@ def parse():
     return ap.parse_args()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the second GEMM from the committed counter
-    profile, or None when the kernel sources changed since it was taken."""
-    import glob
+# The second GEMM (gemm_kernel with the EpiRowScale epilogue) is compiled from
+# these files alone (the build script carries the compiler flags).
+SECOND_GEMM_SOURCES = ("csrc/gemm.hpp", "csrc/tile_map.hpp", "csrc/epilogues.hpp", "build.py")
+
+
+def second_gemm_sources_sha256() -> str:
     import hashlib
 
+    pkg = os.path.join(ROOT, "transformer_gemm_epilogue_gemm1_amd")
+    return hashlib.sha256(b"".join(open(os.path.join(pkg, p), "rb").read() for p in SECOND_GEMM_SOURCES)).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the second GEMM from the committed counter
+    profile, or None when that kernel's sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_gemm_rowscale_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    csrc = os.path.join(ROOT, "transformer_gemm_epilogue_gemm1_amd", "csrc")
-    files = sorted(glob.glob(os.path.join(csrc, "*.hpp")) + glob.glob(os.path.join(csrc, "*.hip")))
-    h = hashlib.sha256(b"".join(open(p, "rb").read() for p in files)).hexdigest()
-    return rec["bytes_per_launch"] if h == rec.get("csrc_sha256") else None
+    ok = rec.get("sources_sha256") == second_gemm_sources_sha256()
+    return rec["bytes_per_launch"] if ok else None
 
 
 def cpu_baseline(wl, x, budget_s: float):
@@ -125,6 +134,16 @@ def time_ms(fn, stream, n, warmup):
     b.record(stream)
     torch.cuda.synchronize()
     return a.elapsed_time(b) / n
+
+
+def time_ms_alternating(fns, stream, n, warmup, reps=3):
+    """Best-of-`reps` average milliseconds of each fn() over n calls, the
+    variants timed in turn so that clock and power drift hit them alike."""
+    best = [float("inf")] * len(fns)
+    for _ in range(reps):
+        for i, fn in enumerate(fns):
+            best[i] = min(best[i], time_ms(fn, stream, n, warmup))
+    return best
 
 
 def _smi_sample():
@@ -288,6 +307,79 @@ def bench_ce(args, up, stream):
             rt = torch.rsqrt(hf.square().mean(dim=1, keepdim=True) + wl.eps)
             logits = torch.matmul((hf * rt * gf).to(tdt), d["W2"])
             return torch.nn.functional.cross_entropy(logits.float(), targets.long(), reduction="none")
+
+        t_ms = time_ms(torch_chain, stream, n, w)
+        out["torch_chain_ms"] = round(t_ms, 4)
+        out["speedup_vs_torch_chain"] = round(t_ms / f_ms, 4)
+    return out
+
+
+def bench_rope(args, up, stream):
+    """The chain whose second GEMM is the attention QKV projection (7B: 32
+    query, 32 key and 32 value heads of 128) with RoPE on Q and K, fused,
+    beside the same chain writing the unrotated projection followed by the
+    rotation in torch, the plain projection without RoPE (the epilogue's
+    cost), and the whole chain in plain PyTorch."""
+    import torch
+
+    import coda_inputs as ci
+    import transformer_gemm_epilogue_gemm1_amd as coda
+
+    wl = ci.WORKLOADS["7b-rope-bf16"]
+    x = ci.make_inputs(wl, seed=args.seed)
+    d = {k: up(v) for k, v in x.items()}
+    M, K, D, N2 = wl.M, wl.K, wl.D, wl.N2
+    dh, nq, nk, max_pos = 128, 4096, 4096, 2048
+    nrot = nq + nk
+    dev, tdt = d["A"].device, d["A"].dtype
+    pos = torch.from_numpy(ci.make_positions(wl, max_pos)).to(dev)
+    cs = coda.rope_cache(max_pos, dh, 10000.0, device=dev, stream=stream)
+    H = torch.empty((M, D), device=dev, dtype=tdt)
+    Hg = torch.empty_like(H)
+    P = torch.empty((coda.coda_prms_num_partials(tdt, D), M), device=dev, dtype=torch.float32)
+    r = torch.empty((M,), device=dev, dtype=torch.float32)
+    Y = torch.empty((M, N2), device=dev, dtype=tdt)
+    csp = cs[pos.long()]  # [M, dh/2, 2], gathered once outside the timed region
+    c, s = csp[:, None, :, 0], csp[:, None, :, 1]
+
+    def head():
+        coda.coda_gemm_res_prms(d["A"], d["W1"], d["R"], d["g"], H, Hg, P, stream)
+        coda.coda_rms_combine(P, r, D, wl.eps, stream)
+
+    def fused():
+        head()
+        coda.coda_gemm_rowscale_rope(Hg, d["W2"], r, pos, cs, nq, nk, dh, Y, stream)
+
+    def plain():
+        head()
+        coda.coda_gemm_rowscale(Hg, d["W2"], r, Y, stream)
+
+    def torch_rope(y):
+        q = y[:, :nrot].view(M, nrot // dh, dh // 2, 2).float()
+        e, o = q[..., 0], q[..., 1]
+        y[:, :nrot] = torch.stack((e * c - o * s, e * s + o * c), dim=-1).view(M, nrot).to(y.dtype)
+        return y
+
+    def proj_then_torch():
+        plain()
+        torch_rope(Y)
+
+    n = max(5, args.steps // 2)
+    w = max(2, args.warmup // 2)
+    f_ms, p_ms, u_ms = time_ms_alternating([fused, plain, proj_then_torch], stream, n, w)
+    out = {"workload": f"7b-rope-bf16: M={M} K={K} D={D} QKV N2={N2} (32+32+32 heads of 128), positions row mod 2048",
+           "fused_ms": round(f_ms, 4), "fused_tflops": round(wl.fwd_flops / (f_ms * 1e-3) / 1e12, 2),
+           "no_rope_ms": round(p_ms, 4), "rope_epilogue_overhead": round(f_ms / p_ms - 1.0, 4),
+           "projection_then_torch_rope_ms": round(u_ms, 4),
+           "speedup_vs_projection_then_torch_rope": round(u_ms / f_ms, 4)}
+    if not args.no_torch_chain:
+        gf = d["g"].float()
+
+        def torch_chain():
+            Ht = torch.addmm(d["R"], d["A"], d["W1"])
+            hf = Ht.float()
+            rt = torch.rsqrt(hf.square().mean(dim=1, keepdim=True) + wl.eps)
+            return torch_rope(torch.matmul((hf * rt * gf).to(tdt), d["W2"]))
 
         t_ms = time_ms(torch_chain, stream, n, w)
         out["torch_chain_ms"] = round(t_ms, 4)
@@ -697,6 +789,8 @@ def main():
 
     if not args.no_ce:
         out["ce"] = bench_ce(args, up, stream)
+    if not args.no_rope:
+        out["rope"] = bench_rope(args, up, stream)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
