@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 (e4m3) chain at the 7B shape")
     ap.add_argument("--no-ce", action="store_true",
                     help="skip the chain ending in the LM head and the per-token cross-entropy")
+    ap.add_argument("--no-g-placement", action="store_true",
+                    help="skip timing the chain with g folded into W2 against g in the first GEMM's epilogue")
     ap.add_argument("--no-rope", action="store_true",
                     help="skip the QKV projection with RoPE (7B attention shape)")
     ap.add_argument("--no-swiglu", action="store_true",
@@ -312,6 +314,36 @@ def bench_ce(args, up, stream):
         out["torch_chain_ms"] = round(t_ms, 4)
         out["speedup_vs_torch_chain"] = round(t_ms / f_ms, 4)
     return out
+
+
+def bench_g_placement(wl, d, H, Hg, P, r, Y, step, stream, args):
+    """Where the RMSNorm weight g is applied: in the first GEMM's epilogue
+    (Hg = H g stored beside H, the default) against g folded into the
+    second GEMM's weight, diag(g) W2, so the first GEMM stores H only.  The
+    fold is free for inference; in training it has to be redone each step
+    (timed separately as one elementwise pass over W2)."""
+    import torch
+
+    import transformer_gemm_epilogue_gemm1_amd as coda
+
+    D = wl.D
+    W2g = (d["W2"].float() * d["g"].float()[:, None]).to(d["W2"].dtype)
+
+    def folded():
+        coda.coda_gemm_res_prms(d["A"], d["W1"], d["R"], None, H, None, P, stream)
+        coda.coda_rms_combine(P, r, D, wl.eps, stream)
+        coda.coda_gemm_rowscale(H, W2g, r, Y, stream)
+
+    def refold():
+        torch.mul(d["W2"], d["g"][:, None], out=W2g)
+
+    n = max(5, args.steps // 2)
+    w = max(2, args.warmup // 2)
+    g_epi_ms, folded_ms, refold_ms = time_ms_alternating([step, folded, refold], stream, n, w)
+    return {"g_in_first_epilogue_ms": round(g_epi_ms, 4), "g_folded_into_w2_ms": round(folded_ms, 4),
+            "refold_w2_per_step_ms": round(refold_ms, 4),
+            "folded_speedup_inference": round(g_epi_ms / folded_ms, 4),
+            "folded_speedup_training_with_refold": round(g_epi_ms / (folded_ms + refold_ms), 4)}
 
 
 def bench_rope(args, up, stream):
@@ -745,6 +777,9 @@ def main():
                                                                else Hr, H.view(torch.int16)
                                                                if tdt == torch.bfloat16 else H))
         del ws, Hr, rr, Yr
+
+    if not args.no_g_placement:
+        out["g_placement"] = bench_g_placement(wl, d, H, Hg, P, r, Y, step, stream, args)
 
     if not args.no_torch_chain:
         # the unfused library path: vendor GEMMs with torch's RMSNorm in between

@@ -17,6 +17,11 @@ its output the logits Y; per row i with target class t_i
     loss_i = lse_i - Y_i,t_i
 
 the per-token cross-entropy (no reduction over tokens, no label smoothing).
+
+Backward: for an upstream gradient dloss_i per token (1/M for a mean over
+tokens), the gradient of sum_i dloss_i loss_i with respect to the logits is
+dloss_i (softmax(Y_i) - onehot(t_i)); the chain's own backward takes it from
+there as its dY.
 """
 from __future__ import annotations
 
@@ -24,7 +29,7 @@ from typing import Dict, Optional, Sequence
 
 import numpy as np
 
-from .chain import forward
+from .chain import backward, forward
 
 
 def logsumexp_rows(Y) -> np.ndarray:
@@ -53,4 +58,26 @@ def forward_ce(A, W1, R, g, Wv, eps: float, targets, rows: Optional[Sequence[int
     if rows is not None:
         t = t[np.asarray(rows, dtype=np.int64)]
     out.update(cross_entropy_rows(out["Y"], t))
+    return out
+
+
+def cross_entropy_grad(Y, targets, dloss) -> np.ndarray:
+    """d(sum_i dloss_i loss_i)/dY = dloss_i (e^(Y_ij - lse_i) - [j == t_i])."""
+    Y = np.asarray(Y, dtype=np.float64)
+    t = np.asarray(targets, dtype=np.int64)
+    if t.shape != (Y.shape[0],) or np.any(t < 0) or np.any(t >= Y.shape[1]):
+        raise ValueError("one target class in [0, V) per row")
+    p = np.exp(Y - logsumexp_rows(Y)[:, None])
+    p[np.arange(Y.shape[0]), t] -= 1.0
+    return p * np.asarray(dloss, dtype=np.float64)[:, None]
+
+
+def backward_ce(A, W1, R, g, Wv, eps: float, targets, dloss) -> Dict[str, np.ndarray]:
+    """Gradients of sum_i dloss_i loss_i through the chain: dY from the loss,
+    then the chain's backward (dA, dR, dW1, dW2 = dWv, dg)."""
+    Y = forward(A, W1, R, g, Wv, eps)["Y"]
+    dY = cross_entropy_grad(Y, targets, dloss)
+    out = backward(dY, A, W1, R, g, Wv, eps)
+    out["dY"] = dY
+    out["Y"] = Y
     return out

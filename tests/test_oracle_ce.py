@@ -90,3 +90,64 @@ def test_pins_reject_planted_mistakes(kind):
     else:
         bad = Y[np.arange(4), t] - oracle.logsumexp_rows(Y)
     assert np.max(np.abs(bad - ref)) > 1e-3
+
+
+def test_grad_matches_torch_autograd_and_sums_to_zero():
+    rng = np.random.default_rng(7)
+    Y = rng.standard_normal((6, 40)) * 3
+    t = rng.integers(0, 40, size=6)
+    dl = rng.standard_normal(6)
+    got = oracle.cross_entropy_grad(Y, t, dl)
+    y = torch.from_numpy(Y).requires_grad_(True)
+    loss = torch.nn.functional.cross_entropy(y, torch.from_numpy(t), reduction="none")
+    (loss * torch.from_numpy(dl)).sum().backward()
+    np.testing.assert_allclose(got, y.grad.numpy(), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(got.sum(axis=1), 0.0, atol=1e-14)          # softmax and one-hot both sum to 1
+    big = np.array([[1000.0, 0.0, -1000.0]])                              # no overflow
+    np.testing.assert_allclose(oracle.cross_entropy_grad(big, [0], [1.0]), [[0.0, 0.0, 0.0]], atol=1e-300)
+
+
+def test_chain_backward_against_finite_differences():
+    # d(sum_i dloss_i loss_i) / dW, through the whole chain, by central
+    # differences of the forward oracle on a tiny case
+    A, W1, R, g, Wv, t = _case(8, 3, 4, 8, 7)
+    dl = np.array([0.5, -1.0, 2.0])
+    out = oracle.backward_ce(A, W1, R, g, Wv, 1e-5, t, dl)
+
+    def f(**kw):
+        args = dict(A=A, W1=W1, R=R, g=g, Wv=Wv)
+        args.update(kw)
+        o = oracle.forward_ce(args["A"], args["W1"], args["R"], args["g"], args["Wv"], 1e-5, t)
+        return float(np.sum(dl * o["loss"]))
+
+    h = 1e-6
+    for name, arr, grad in (("Wv", Wv, out["dW2"]), ("W1", W1, out["dW1"]), ("A", A, out["dA"]),
+                            ("R", R, out["dR"]), ("g", g, out["dg"])):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            up, dn = arr.copy(), arr.copy()
+            up[idx] += h
+            dn[idx] -= h
+            num[idx] = (f(**{name: up}) - f(**{name: dn})) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+@pytest.mark.parametrize("kind", ["no_onehot", "sign", "unscaled", "softmax_over_rows"])
+def test_grad_pins_reject_planted_mistakes(kind):
+    rng = np.random.default_rng(9)
+    Y = rng.standard_normal((5, 8)) * 2
+    t = rng.integers(0, 8, size=5)
+    dl = rng.standard_normal(5) + 2.0
+    y = torch.from_numpy(Y).requires_grad_(True)
+    (torch.nn.functional.cross_entropy(y, torch.from_numpy(t), reduction="none") * torch.from_numpy(dl)).sum().backward()
+    ref = y.grad.numpy()
+    p = np.exp(Y - oracle.logsumexp_rows(Y)[:, None])
+    if kind == "softmax_over_rows":
+        p = np.exp(Y) / np.exp(Y).sum(axis=0, keepdims=True)
+    bad = p.copy()
+    if kind != "no_onehot":
+        bad[np.arange(5), t] -= 1.0
+    bad = -bad if kind == "sign" else bad
+    if kind != "unscaled":
+        bad = bad * dl[:, None]
+    assert np.max(np.abs(bad - ref)) > 1e-3
