@@ -75,15 +75,19 @@ def parse():
 
 
 # The second GEMM (gemm_kernel with the EpiRowScale epilogue) is compiled from
-# these files alone (the build script carries the compiler flags).
-SECOND_GEMM_SOURCES = ("csrc/gemm.hpp", "csrc/tile_map.hpp", "csrc/epilogues.hpp", "build.py")
+# these files alone, with the build's compiler flags.
+SECOND_GEMM_SOURCES = ("csrc/gemm.hpp", "csrc/tile_map.hpp", "csrc/epilogues.hpp")
 
 
 def second_gemm_sources_sha256() -> str:
+    """sha256 of those sources followed by the compiler flags."""
     import hashlib
 
+    from transformer_gemm_epilogue_gemm1_amd.build import HIP_FLAGS
+
     pkg = os.path.join(ROOT, "transformer_gemm_epilogue_gemm1_amd")
-    return hashlib.sha256(b"".join(open(os.path.join(pkg, p), "rb").read() for p in SECOND_GEMM_SOURCES)).hexdigest()
+    blob = b"".join(open(os.path.join(pkg, p), "rb").read() for p in SECOND_GEMM_SOURCES)
+    return hashlib.sha256(blob + " ".join(HIP_FLAGS).encode()).hexdigest()
 
 
 def measured_traffic(workload: str):
@@ -255,7 +259,10 @@ def bench_ce(args, up, stream):
     """The chain ending in the LM head (7B hidden size, vocabulary 32000) and
     the per-token cross-entropy, fused (the logits never leave the
     registers), beside the same chain writing the bf16 logits followed by
-    torch's cross_entropy, and the whole chain in plain PyTorch."""
+    torch's cross_entropy, and the whole chain in plain PyTorch; and a
+    training step for the mean loss (fused forward, the logits' gradient from
+    the recomputing LM-head GEMM, the chain's backward) beside PyTorch
+    autograd of the same chain and loss."""
     import torch
 
     import coda_inputs as ci
@@ -313,6 +320,45 @@ def bench_ce(args, up, stream):
         t_ms = time_ms(torch_chain, stream, n, w)
         out["torch_chain_ms"] = round(t_ms, 4)
         out["speedup_vs_torch_chain"] = round(t_ms / f_ms, 4)
+    if not args.no_backward:
+        # training step for the mean loss over tokens: fused forward, the
+        # gradient of the logits recomputed in the LM-head GEMM's epilogue,
+        # then the chain's backward (the [M, V] logits are never stored)
+        dloss = torch.full((M,), 1.0 / M, device=dev, dtype=torch.float32)
+        dY = torch.empty((M, V), device=dev, dtype=tdt)
+        dA = torch.empty((M, K), device=dev, dtype=tdt)
+        dR = torch.empty((M, D), device=dev, dtype=tdt)
+        dW1 = torch.empty((K, D), device=dev, dtype=tdt)
+        dWv = torch.empty((D, V), device=dev, dtype=tdt)
+        dg = torch.empty((D,), device=dev, dtype=torch.float32)
+        ws = torch.empty((coda.coda_chain_bwd_workspace_bytes(tdt, M, K, D, V),), device=dev, dtype=torch.uint8)
+
+        def train():
+            fused()
+            coda.coda_gemm_rowscale_ce_bwd(Hg, d["W2"], r, targets, lse, dloss, dY, stream)
+            coda.coda_chain_bwd(dY, d["A"], d["W1"], d["g"], d["W2"], H, r, dA, dR, dW1, dWv, dg, ws, stream)
+
+        tr_ms = time_ms(train, stream, n, w)
+        bwd_flops = 2.0 * M * D * V + 4.0 * M * D * V + 4.0 * M * K * D
+        out["train_step_ms"] = round(tr_ms, 4)
+        out["train_step_tflops"] = round((wl.fwd_flops + bwd_flops) / (tr_ms * 1e-3) / 1e12, 2)
+        if not args.no_torch_chain:
+            leaves = {k: d[k].clone().requires_grad_(True) for k in ("A", "W1", "R", "g", "W2")}
+            tl = targets.long()
+
+            def torch_train():
+                for t in leaves.values():
+                    t.grad = None
+                Ht = torch.addmm(leaves["R"], leaves["A"], leaves["W1"])
+                Xn = torch.nn.functional.rms_norm(Ht.float(), (D,), leaves["g"].float(), wl.eps).to(tdt)
+                logits = torch.matmul(Xn, leaves["W2"])
+                torch.nn.functional.cross_entropy(logits.float(), tl).backward()
+
+            t_ms = time_ms(torch_train, stream, n, w)
+            out["torch_autograd_train_step_ms"] = round(t_ms, 4)
+            out["train_step_speedup_vs_torch_autograd"] = round(t_ms / tr_ms, 4)
+            del leaves
+        del dY, dA, dR, dW1, dWv, ws
     return out
 
 
@@ -340,8 +386,8 @@ def bench_g_placement(wl, d, H, Hg, P, r, Y, step, stream, args):
     n = max(5, args.steps // 2)
     w = max(2, args.warmup // 2)
     g_epi_ms, folded_ms, refold_ms = time_ms_alternating([step, folded, refold], stream, n, w)
-    return {"g_in_first_epilogue_ms": round(g_epi_ms, 4), "g_folded_into_w2_ms": round(folded_ms, 4),
-            "refold_w2_per_step_ms": round(refold_ms, 4),
+    return {"g_in_first_epilogue_ms": round(g_epi_ms, 5), "g_folded_into_w2_ms": round(folded_ms, 5),
+            "refold_w2_per_step_ms": round(refold_ms, 5),
             "folded_speedup_inference": round(g_epi_ms / folded_ms, 4),
             "folded_speedup_training_with_refold": round(g_epi_ms / (folded_ms + refold_ms), 4)}
 

@@ -219,6 +219,20 @@ coda_status coda_rope_bwd(coda_dtype dt, int64_t M, int64_t N2, const void* dYr,
                           int64_t n_q, int64_t n_k, int64_t d_head,
                           void* dY, int64_t lddy, void* stream);
 
+/* Backward of the cross-entropy head (the derivative of the reading above):
+ * recomputes y = r_i * (X W_v)_ij in fp32 and writes the gradient of
+ * sum_i dloss_i loss_i with respect to the logits,
+ *   dY_ij = round(dloss_i * (e^(y_ij - lse_i) - [j == targets[i]])),
+ * the dY that coda_chain_bwd takes (with W2 = W_v).  lse: the forward's
+ * (coda_ce_combine); dloss: float[M] upstream gradient per token (1/M for a
+ * mean over tokens).  A target outside [0, V) makes the row NaN.  X, Wv, r,
+ * targets as coda_gemm_rowscale_lse; dY: [M,V] (lddy), not overlapping any
+ * input.  The [M,V] logits are recomputed, never read. */
+coda_status coda_gemm_rowscale_ce_bwd(coda_dtype dt, int64_t M, int64_t D, int64_t V,
+                                      const void* X, int64_t ldx, const void* Wv, int64_t ldw,
+                                      const float* r, const int32_t* targets, const float* lse,
+                                      const float* dloss, void* dY, int64_t lddy, void* stream);
+
 /* ---- fp8 operands -------------------------------------------------------
  * The article's opening section notes that FP8 makes the matrix products
  * faster while the memory-bound operations around them do not shrink, so

@@ -251,6 +251,29 @@ def test_ce_combine_validation(lib, args, status):
     assert lib.coda_ce_combine(*args, None) == status
 
 
+def ce_bwd_call(lib, dt=BF16, M=512, D=256, V=1000, X=H_, ldx=None, W=W2_, ldw=None, r=R2_, t=DY_, lse=DG_,
+                dl=DG_ + 4096, dY=Y_, lddy=None):
+    return lib.coda_gemm_rowscale_ce_bwd(dt, M, D, V, X, ldx or D, W, ldw or V, r, t, lse, dl, dY, lddy or V, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=5), DTYPE),
+    (dict(V=1001), SHAPE),
+    (dict(X=None), NULL),
+    (dict(t=None), NULL),
+    (dict(lse=None), NULL),
+    (dict(dl=None), NULL),
+    (dict(dY=None), NULL),
+    (dict(lse=DG_ + 2), ALIGN),
+    (dict(lddy=1004), ALIGN),
+    (dict(dY=DG_ - 64), ALIAS),       # dY over lse
+    (dict(dY=W2_ + 512), ALIAS),
+    (dict(M=0, X=None, t=None), OK),
+])
+def test_gemm_rowscale_ce_bwd_rejects(lib, kw, status):
+    assert ce_bwd_call(lib, **kw) == status
+
+
 def rope_call(lib, dt=BF16, M=512, D=256, N2=1536, X=H_, ldx=None, W=W2_, ldw=None, r=R2_, pos=DY_, cs=DG_,
               max_pos=2048, nq=512, nk=512, dh=128, Y=Y_, ldy=None):
     return lib.coda_gemm_rowscale_rope(dt, M, D, N2, X, ldx or D, W, ldw or N2, r, pos, cs, max_pos, nq, nk, dh, Y,

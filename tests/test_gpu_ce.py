@@ -1,5 +1,6 @@
 """GPU parity of the chain ending in the LM head and the per-token
-cross-entropy (coda_gemm_rowscale_lse + coda_ce_combine) through the C ABI.
+cross-entropy (coda_gemm_rowscale_lse + coda_ce_combine) and of its backward
+(coda_gemm_rowscale_ce_bwd, then coda_chain_bwd) through the C ABI.
 
 The logits are never written: the second GEMM's epilogue keeps per-tile
 max / sum-exp statistics and the target logit, a combine turns them into
@@ -8,7 +9,8 @@ seeded inputs and targets: max|x - x_ref| / max|x_ref| <= 1e-2 (bf16) or
 1e-5 (fp32) for lse and loss.  Stage-wise (fp32, where the LM-head GEMM with
 a row scale stores exactly the y the statistics see): pmax and the target
 logit bit-exact against the host on coda_gemm_rowscale's output, psum to
-fp32 rounding.
+fp32 rounding.  Backward: dY and every chain gradient against the oracle
+(same bars); in fp32 dY against the host formula on the same logits and lse.
 """
 import sys
 
@@ -36,9 +38,9 @@ def _run(wl, seed, targets=None):
     t = ci.make_targets(wl, seed=seed) if targets is None else np.asarray(targets, dtype=np.int32)
     d = {k: dev(v) for k, v in x.items()}
     tt = torch.from_numpy(t).cuda()
-    H, r, lse, loss = coda.fused_forward_ce(d["A"], d["W1"], d["R"], d["g"], d["W2"], wl.eps, tt)
+    H, Hg, r, lse, loss = coda.fused_forward_ce(d["A"], d["W1"], d["R"], d["g"], d["W2"], wl.eps, tt)
     torch.cuda.synchronize()
-    return x, d, t, tt, {"H": H, "r": r, "lse": lse, "loss": loss}
+    return x, d, t, tt, {"H": H, "Hg": Hg, "r": r, "lse": lse, "loss": loss}
 
 
 def _check(wl, x, t, o, rows=None):
@@ -126,3 +128,84 @@ def test_full_size_7b_lm_head_sampled_rows():
     err = _check(wl, x, t, o, rows=rows)
     print(f"7b-ce sampled-row loss error {err:.3e}")
     assert torch.isfinite(o["loss"]).all().item()
+
+
+GRADS = ("dA", "dR", "dW1", "dW2", "dg")
+
+
+def _dloss(M, seed):
+    return np.random.default_rng(seed + 1000).standard_normal(M).astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", SHAPES[1:], ids=lambda s: "x".join(map(str, s)))
+def test_ce_backward_matches_oracle(shape, dtype):
+    wl = ci.custom_workload(*shape, eps=1e-5 if dtype == "bf16" else 1e-6, dtype=dtype, wl_id=610)
+    x, d, t, tt, o = _run(wl, seed=4)
+    dl = _dloss(wl.M, 4)
+    tdl = torch.from_numpy(dl).cuda()
+    grads = coda.fused_backward_ce(d["A"], d["W1"], d["g"], d["W2"], o["H"], o["Hg"], o["r"], tt, o["lse"], tdl)
+    torch.cuda.synchronize()
+    out = dict(zip(GRADS + ("dY",), grads))
+    orc = oracle.backward_ce(x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps, t, dl)
+    for k in GRADS + ("dY",):
+        err = max_rel(host_f32(out[k]), orc[k])
+        assert err <= tolerance(dtype), f"{k}: error {err:.3e}"
+
+
+def test_ce_grad_against_the_logits_fp32():
+    M, K, D, V = 300, 256, 384, 1000
+    wl = ci.custom_workload(M, K, D, V, eps=1e-6, dtype="f32", wl_id=611)
+    t = (np.arange(M) * 37) % V
+    t[:6] = [0, 7, 8, 63, 64, V - 1]
+    x, d, t, tt, o = _run(wl, seed=5, targets=t)
+    dl = _dloss(M, 5)
+    dY = torch.full((M, V), float("nan"), device="cuda")
+    coda.coda_gemm_rowscale_ce_bwd(o["Hg"], d["W2"], o["r"], tt, o["lse"], torch.from_numpy(dl).cuda(), dY)
+    Y = torch.empty((M, V), device="cuda")
+    coda.coda_gemm_rowscale(o["Hg"], d["W2"], o["r"], Y)
+    torch.cuda.synchronize()
+    y = host_f32(Y).astype(np.float64)
+    lse = o["lse"].cpu().numpy().astype(np.float64)
+    ref = np.exp(y - lse[:, None])
+    ref[np.arange(M), t] -= 1.0
+    ref *= dl[:, None]
+    got = host_f32(dY)
+    # the exponential of the same y, in fp32 with the hardware exp2: a few
+    # float32 roundings of |dloss| (e^(y - lse) + 1)
+    bound = 4e-6 * np.abs(dl)[:, None] * (np.exp(y - lse[:, None]) + 1.0)
+    assert np.all(np.abs(got - ref) <= bound)
+    np.testing.assert_allclose(got.sum(axis=1), 0.0, atol=1e-5 * np.abs(dl).max())
+
+
+def test_ce_grad_invalid_target_gives_nan_row():
+    wl = ci.custom_workload(64, 128, 256, 512, wl_id=612)
+    t = ci.make_targets(wl, seed=6)
+    t[3], t[40] = -5, 512
+    x, d, t, tt, o = _run(wl, seed=6, targets=t)
+    dY = torch.empty((64, 512), device="cuda", dtype=torch.bfloat16)
+    coda.coda_gemm_rowscale_ce_bwd(o["Hg"], d["W2"], o["r"], tt, o["lse"], torch.ones(64, device="cuda"), dY)
+    torch.cuda.synchronize()
+    g = host_f32(dY)
+    assert np.isnan(g[[3, 40]]).all()
+    ok = np.ones(64, bool)
+    ok[[3, 40]] = False
+    assert np.isfinite(g[ok]).all()
+
+
+@pytest.mark.slow
+def test_full_size_7b_lm_head_grad_sampled_rows():
+    wl = ci.WORKLOADS["7b-ce-bf16"]
+    x, d, t, tt, o = _run(wl, seed=0)
+    dl = np.full(wl.M, 1.0 / wl.M, dtype=np.float32)
+    dY = torch.empty((wl.M, wl.N2), device="cuda", dtype=torch.bfloat16)
+    coda.coda_gemm_rowscale_ce_bwd(o["Hg"], d["W2"], o["r"], tt, o["lse"], torch.from_numpy(dl).cuda(), dY)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(22)
+    rows = np.unique(np.concatenate([[0, 255, 256, wl.M - 1], rng.integers(0, wl.M, 12)]))
+    Yo = oracle.forward(x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps, rows=rows)["Y"]
+    ref = oracle.cross_entropy_grad(Yo, t[rows], dl[rows])
+    err = max_rel(host_f32(dY)[rows], ref)
+    print(f"7b-ce sampled-row dY error {err:.3e}")
+    assert err <= 1e-2
+    assert np.all(np.abs(host_f32(dY)[rows].astype(np.float64).sum(axis=1)) <= 1e-2 / wl.M)

@@ -220,6 +220,27 @@ def coda_rope_bwd(dYr, positions, cos_sin, n_q: int, n_k: int, d_head: int, dY, 
     _lib.check("coda_rope_bwd", st)
 
 
+def coda_gemm_rowscale_ce_bwd(X, Wv, r: Optional[torch.Tensor], targets, lse, dloss, dY, stream=None) -> None:
+    """dY = dloss * (softmax(diag(r) X Wv) - onehot(targets)): the gradient of
+    the per-token losses with respect to the logits, recomputed from X."""
+    lib = _lib.load()
+    dt = X.dtype
+    M, D = X.shape
+    V = Wv.shape[1]
+    ldx = _mat(X, "X", dt, (M, D))
+    ldw = _mat(Wv, "Wv", dt, (D, V))
+    lddy = _mat(dY, "dY", dt, (M, V))
+    _mat(targets, "targets", torch.int32, (M,))
+    _mat(lse, "lse", torch.float32, (M,))
+    _mat(dloss, "dloss", torch.float32, (M,))
+    if r is not None:
+        _mat(r, "r", torch.float32, (M,))
+    st = lib.coda_gemm_rowscale_ce_bwd(_dtype_code(X), M, D, V, X.data_ptr(), ldx, Wv.data_ptr(), ldw,
+                                       r.data_ptr() if r is not None else None, targets.data_ptr(), lse.data_ptr(),
+                                       dloss.data_ptr(), dY.data_ptr(), lddy, _stream(stream))
+    _lib.check("coda_gemm_rowscale_ce_bwd", st)
+
+
 def coda_ce_combine(pmax, psum, tgt, targets, lse, loss, V: int, stream=None) -> None:
     """lse and per-token loss from the LM-head statistics."""
     lib = _lib.load()
@@ -421,7 +442,7 @@ def fused_forward_fp8(A8, sa, W1t8, sw1, R, g, W2t8, sw2, eps: float, stream=Non
 
 def fused_forward_ce(A, W1, R, g, Wv, eps: float, targets, stream=None):
     """The chain ending in the LM head and the per-token cross-entropy:
-    returns (H, r, lse, loss); the logits are never materialised."""
+    returns (H, Hg, r, lse, loss); the logits are never materialised."""
     M, D, V = A.shape[0], W1.shape[1], Wv.shape[1]
     dev, dt = A.device, A.dtype
     H = torch.empty((M, D), device=dev, dtype=dt)
@@ -438,7 +459,16 @@ def fused_forward_ce(A, W1, R, g, Wv, eps: float, targets, stream=None):
     coda_rms_combine(P, r, D, eps, stream)
     coda_gemm_rowscale_lse(Hg, Wv, r, targets, pmax, psum, tgt, stream)
     coda_ce_combine(pmax, psum, tgt, targets, lse, loss, V, stream)
-    return H, r, lse, loss
+    return H, Hg, r, lse, loss
+
+
+def fused_backward_ce(A, W1, g, Wv, H, Hg, r, targets, lse, dloss, stream=None):
+    """Backward of the chain ending in the cross-entropy head: dY from the
+    recomputed logits, then the chain's backward; returns
+    (dA, dR, dW1, dWv, dg, dY)."""
+    dY = torch.empty((A.shape[0], Wv.shape[1]), device=A.device, dtype=A.dtype)
+    coda_gemm_rowscale_ce_bwd(Hg, Wv, r, targets, lse, dloss, dY, stream)
+    return fused_backward(dY, A, W1, g, Wv, H, r, stream) + (dY,)
 
 
 def fused_forward_rope(A, W1, R, g, Wqkv, eps: float, positions, cos_sin, n_q: int, n_k: int, d_head: int,

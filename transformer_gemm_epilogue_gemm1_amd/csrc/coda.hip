@@ -14,6 +14,7 @@
 #include "../../include/coda.h"
 #include "epilogues.hpp"
 #include "epilogues_fp8.hpp"
+#include "epilogues_ce.hpp"
 #include "epilogues_rope.hpp"
 #include "gemm_fp8.hpp"
 #include "rowops.hpp"
@@ -558,6 +559,35 @@ coda_status coda_gemm_rowscale_lse(coda_dtype dt, int64_t M, int64_t D, int64_t 
   typename EpiLSE<float>::Params ep{r, targets, pmax, psum, tgt};
   return launch_gemm<float, true, false, EpiLSE<float>>("coda_gemm_rowscale_lse", (int)M, (int)V, (int)D, X, ldx,
                                                         Wv, ldw, ep, s);
+}
+
+coda_status coda_gemm_rowscale_ce_bwd(coda_dtype dt, int64_t M, int64_t D, int64_t V, const void* X, int64_t ldx,
+                                      const void* Wv, int64_t ldw, const float* r, const int32_t* targets,
+                                      const float* lse, const float* dloss, void* dY, int64_t lddy, void* stream) {
+  coda_status st = check_dims(dt, M, {{"D", D}, {"V", V}});
+  if (st != CODA_OK) return st;
+  if (M == 0) return ok();
+  const int es = elem_size(dt), E = elems_per_chunk(dt);
+  const Mat mX{X, M, D, ldx, es, "X"}, mW{Wv, D, V, ldw, es, "Wv"}, mdY{dY, M, V, lddy, es, "dY"};
+  for (const Mat* m : {&mX, &mW, &mdY})
+    if ((st = check_mat(*m, E)) != CODA_OK) return st;
+  if (targets == nullptr || lse == nullptr || dloss == nullptr)
+    return fail(CODA_ERR_NULL, "targets, lse and dloss must be set");
+  if ((((uintptr_t)targets | (uintptr_t)lse | (uintptr_t)dloss) & 3) != 0 || (r != nullptr && ((uintptr_t)r & 3) != 0))
+    return fail(CODA_ERR_ALIGN, "r, targets, lse and dloss must be 4-byte aligned");
+  const Mat mt{targets, 1, M, M, 4, "targets"}, ml{lse, 1, M, M, 4, "lse"}, md{dloss, 1, M, M, 4, "dloss"};
+  const Mat mr{r, 1, M, M, 4, "r"};
+  const Mat ins[6] = {mX, mW, mt, ml, md, r ? mr : Mat{nullptr, 0, 0, 0, 4, "r"}};
+  if ((st = check_alias(&mdY, 1, ins, 6)) != CODA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == CODA_BF16) {
+    typename EpiCEGrad<uint16_t>::Params ep{r, targets, lse, dloss, (uint16_t*)dY, lddy, (int)V};
+    return launch_gemm<uint16_t, true, false, EpiCEGrad<uint16_t>>("coda_gemm_rowscale_ce_bwd", (int)M, (int)V,
+                                                                   (int)D, X, ldx, Wv, ldw, ep, s);
+  }
+  typename EpiCEGrad<float>::Params ep{r, targets, lse, dloss, (float*)dY, lddy, (int)V};
+  return launch_gemm<float, true, false, EpiCEGrad<float>>("coda_gemm_rowscale_ce_bwd", (int)M, (int)V, (int)D, X,
+                                                           ldx, Wv, ldw, ep, s);
 }
 
 coda_status coda_ce_combine(int64_t M, int64_t V, int64_t T, const float* pmax, const float* psum, const float* tgt,
