@@ -282,6 +282,12 @@ struct GemmArgs {
   int b_split;  // > 0: B (row-contiguous) read in the SwiGLU column order, gate/up halves at b_split
 };
 
+// A fragment index after whose products a k-step issues its direct loads
+// (see kstep).  With both operands row-contiguous (the weight-gradient
+// products) the loads go out first (-1): any later point spills registers.
+constexpr int kDmaIssueAfter = 3;
+constexpr int kDmaIssueAfterRR = -1;
+
 // Fragments of one k-tile held in registers.
 struct Frags {
   u32x4 a[kFragM], b[kFragN];
@@ -289,26 +295,38 @@ struct Frags {
 
 // One step of the k-pipeline, k-tile kt held in stage S = kt % kStages, its
 // fragments already in `cur`:
-//   issue the direct loads of tile kt + kStages - 1 into stage (S - 1) mod
-//   kStages, which held tile kt - 1 (read in step kt - 2, used before the
-//   barrier of step kt - 1);
 //   read tile kt + 1's B fragments from stage S + 1 into a second set;
 //   for each A fragment mt: run its 4 products of tile kt, then read tile
 //   kt + 1's fragment mt into the same registers, so each read has about a
 //   whole step to land before its products in the next step;
+//   after the products of A fragment kDmaIssueAfter (at the start of the
+//   step for the weight-gradient products), issue the direct loads of tile
+//   kt + kStages - 1 into stage (S - 1) mod kStages, which held tile kt - 1
+//   (read in step kt - 2, used before the barrier of step kt - 1);
 //   stage_barrier: at most tiles kt + 3 and kt + 4 are still in flight, so
 //   tile kt + 2, which the next step reads, has landed everywhere.
 // The scheduling fences pin this order (left alone, the scheduler sinks the
 // reads behind the products).  Tiles past the end of K load as zeros; their
 // fragments are read but never multiplied.
+//
+// Why the loads are issued mid-step: every wavefront of the workgroup leaves
+// the barrier together, and the two wavefronts of a SIMD would otherwise
+// both spend their first ~40 instructions on load addressing while the
+// matrix unit idles.  Issued behind 16 products (256 matrix-core cycles),
+// the addressing overlaps them; measured at the 7B second-GEMM shape under
+// the power cap, 1.7-2.4% faster than issuing first (after 1 fragment: 1.2%,
+// after 4-7: 0.3-0.8%; the A and B loads split over two points: 0.6-1.7%).
 template <typename T, bool A_KC, bool B_KC, int S>
 __device__ __forceinline__ void kstep(char* const (&st)[kStages], const Dma<T, A_KC>& da, const Dma<T, B_KC>& db,
                                       FragReader<T, A_KC>& ra, FragReader<T, B_KC>& rb,
                                       f32x4 (&acc)[kFragM][kFragN], Frags& cur, int kt, int K, int wave) {
   constexpr int SL = (S + kStages - 1) % kStages;
   constexpr int SN = (S + 1) % kStages;
-  da.issue(st[SL], kt + kStages - 1, K, wave);
-  db.issue(st[SL] + kOperandBytes, kt + kStages - 1, K, wave);
+  constexpr int issue_at = A_KC || B_KC ? kDmaIssueAfter : kDmaIssueAfterRR;
+  if constexpr (issue_at < 0) {
+    da.issue(st[SL], kt + kStages - 1, K, wave);
+    db.issue(st[SL] + kOperandBytes, kt + kStages - 1, K, wave);
+  }
   ra.refresh();
   rb.refresh();
   u32x4 nb[kFragN];
@@ -320,6 +338,10 @@ __device__ __forceinline__ void kstep(char* const (&st)[kStages], const Dma<T, A
 #pragma unroll
     for (int nt = 0; nt < kFragN; ++nt) Mma<T>::mac(acc[mt][nt], cur.a[mt], cur.b[nt]);
     cur.a[mt] = ra.read(st[SN], mt);
+    if (mt == issue_at) {
+      da.issue(st[SL], kt + kStages - 1, K, wave);
+      db.issue(st[SL] + kOperandBytes, kt + kStages - 1, K, wave);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll

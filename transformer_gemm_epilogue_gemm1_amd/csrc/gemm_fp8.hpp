@@ -44,21 +44,23 @@ __device__ __forceinline__ void mac8(f32x16& acc, const i32x8& a, const i32x8& b
   acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
 }
 
+constexpr int kDmaIssueAfter8 = 1;
+
 struct Frags8 {
   i32x8 a[kFrag8M], b[kFrag8N];
 };
 
-// One k-step, k-tile kt in stage S (the schedule of kstep in gemm.hpp):
-// loads of tile kt + kStages - 1, B fragments of tile kt + 1, then per A
-// fragment its 2 products of tile kt and its reload for tile kt + 1.
+// One k-step, k-tile kt in stage S (the schedule of kstep in gemm.hpp): B
+// fragments of tile kt + 1, then per A fragment its 2 products of tile kt and
+// its reload for tile kt + 1; the loads of tile kt + kStages - 1 go out
+// after the products of A fragment kDmaIssueAfter8 (4 products, 256
+// matrix-core cycles, as in the bf16 step).
 template <int S>
 __device__ __forceinline__ void kstep8(char* const (&st)[kStages], const Dma<uint8_t, true>& da,
                                        const Dma<uint8_t, true>& db, FragReader8& ra, FragReader8& rb,
                                        f32x16 (&acc)[kFrag8M][kFrag8N], Frags8& cur, int kt, int K, int wave) {
   constexpr int SL = (S + kStages - 1) % kStages;
   constexpr int SN = (S + 1) % kStages;
-  da.issue(st[SL], kt + kStages - 1, K, wave);
-  db.issue(st[SL] + kOperandBytes, kt + kStages - 1, K, wave);
   ra.refresh();
   rb.refresh();
   i32x8 nb[kFrag8N];
@@ -70,6 +72,10 @@ __device__ __forceinline__ void kstep8(char* const (&st)[kStages], const Dma<uin
 #pragma unroll
     for (int nt = 0; nt < kFrag8N; ++nt) mac8(acc[mt][nt], cur.a[mt], cur.b[nt]);
     cur.a[mt] = ra.read(st[SN], mt);
+    if (mt == kDmaIssueAfter8) {
+      da.issue(st[SL], kt + kStages - 1, K, wave);
+      db.issue(st[SL] + kOperandBytes, kt + kStages - 1, K, wave);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
