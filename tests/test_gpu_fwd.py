@@ -216,3 +216,28 @@ def test_full_size_sampled_rows(name):
     expect = torch.sqrt(ms / (ms + wl.eps))
     assert torch.max(torch.abs(rr - expect)).item() < 1e-5
     assert torch.isfinite(o["Y"].float()).all().item()
+
+
+@pytest.mark.slow
+def test_largest_matrix_spans():
+    # A [32768, 32760] and Y [32768, 32760] each span 2,146,959,360 bytes, just
+    # under the 2 GiB - 256 limit of one matrix: the direct loads address A
+    # with 32-bit offsets up to the top of that range, and the contraction
+    # (32760 = 1023 k-tiles + 24) and Y's columns (127 tiles + 248) both end
+    # ragged.  Sampled rows against the oracle.
+    M, K, D, N2 = 32768, 32760, 256, 32760
+    wl = ci.custom_workload(M, K, D, N2, wl_id=130)
+    assert M * K * 2 <= 2 ** 31 - 256 and M * N2 * 2 <= 2 ** 31 - 256
+    o = _run(wl, seed=3, ref=False)
+    rng = np.random.default_rng(13)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, M - 256, M - 1], rng.integers(0, M, 10)]))
+    x = o["x"]
+    orc = oracle.forward(x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps, rows=rows)
+    tr = torch.from_numpy(rows).cuda()
+    Y = o["Y"].index_select(0, tr).float().cpu().numpy()
+    H = o["H"].index_select(0, tr).float().cpu().numpy()
+    np.testing.assert_allclose(H, orc["H"], rtol=2.0 ** -8 * 1.01, atol=1e-5)
+    err = max_rel(Y, orc["Y"])
+    print(f"largest spans: sampled-row Y error {err:.3e}")
+    assert err <= 1e-2
+    assert torch.isfinite(o["Y"][-1].float()).all().item()
