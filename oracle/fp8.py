@@ -16,7 +16,11 @@ Sources (the CODA news article by Synced / 机器之心, mirrored by KuCoin News
     second GEMM without a scale: Hg8 = e4m3(clamp(float(H_bf16) * g, +-448)),
     the product taken in float32 and rounded to nearest-even, which is the
     precision the kernel takes that decision in;
-  * r comes from the exact H, as in the bf16 chain.
+  * r comes from the exact H, as in the bf16 chain;
+  * quantising a bf16 operand (quantize_rows): per row, scale = amax / 448
+    in float32 (1 for an all-zero row), codes = e4m3(float32(x) / scale),
+    the division correctly rounded in float32; a column-wise variant gives
+    the transposed weight codes with per-output-channel scales.
 
     A   = e4m3(A8) * sa[:, None]            W1 = (e4m3(W1t8) * sw1[:, None])^T
     H   = A W1 + R                          Hb = bf16(H)
@@ -69,6 +73,22 @@ def e4m3_encode(x) -> np.ndarray:
     code = np.where(a == _POS[hi], hi, code)
     code = np.where(np.isnan(x), 0x7F, code | (np.signbit(x).astype(np.int64) << 7))
     return code.astype(np.uint8)
+
+
+def quantize_rows(x):
+    """Per-row e4m3 codes and float32 scales of a float32 matrix: the row's
+    largest magnitude maps to 448 (scale = amax / 448, taken in float32; an
+    all-zero row gets scale 1)."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    return e4m3_encode(x / scale[:, None]), scale
+
+
+def quantize_cols_transposed(w):
+    """Codes of w^T [N, K] with one scale per column of w [K, N] (the weight
+    stored transposed with per-output-channel scales)."""
+    return quantize_rows(np.ascontiguousarray(np.asarray(w, dtype=np.float32).T))
 
 
 def bf16_round(x) -> np.ndarray:

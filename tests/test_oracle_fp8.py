@@ -179,3 +179,43 @@ def test_pins_reject_planted_mistakes(kind):
     _, Hg8, _, Y = _brute(*(np.asarray(v).tolist() if np.asarray(v).ndim == 2 else np.asarray(v) for v in a), wl.eps)
     codes, Ym = _mutant_codes(kind, a, wl.eps)
     assert (not np.array_equal(codes, Hg8)) or np.max(np.abs(Ym - Y)) > 1e-9
+
+
+def test_quantize_rows_pins():
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((6, 200)) * np.array([[1e-3], [1.0], [30.0], [1e4], [0.0], [2.0]])).astype(np.float32)
+    x[5, 17] = -9.0                                  # a row whose largest magnitude is negative
+    codes, scale = oracle.quantize_rows(x)
+    assert codes.dtype == np.uint8 and scale.dtype == np.float32
+    assert scale[4] == 1.0 and np.all(codes[4] & 0x7F == 0)          # zero row (signed zeros kept)
+    # the largest magnitude of each row maps to the largest code, 448
+    for i in (0, 1, 2, 3, 5):
+        j = np.argmax(np.abs(x[i]))
+        assert oracle.e4m3_decode(codes[i, j]) == np.sign(x[i, j]) * 448.0
+    assert codes[5, 17] == 0xFE                                       # -448
+    # round trip within half an e4m3 step (3 mantissa bits: relative 2^-4
+    # for normals; absolute 2^-10 scale for subnormals)
+    back = oracle.e4m3_decode(codes) * scale[:, None].astype(np.float64)
+    err = np.abs(back - x)
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * scale[:, None])
+    assert np.all(err <= bound * 1.0000001)
+    # brute force: each code is the nearest representable value of x / scale
+    vals = oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    for i in (1, 2):
+        for j in range(0, 200, 13):
+            q = np.float32(x[i, j]) / scale[i]
+            d = np.abs(np.abs(np.float64(q)) - vals)
+            assert abs(oracle.e4m3_decode(codes[i, j])) in vals[d == d.min()]
+
+
+def test_quantize_matches_the_input_generators_recipe():
+    # two independent implementations of the same recipe agree bit for bit
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((64, 96)).astype(np.float32) * 3
+    c1, s1 = oracle.quantize_rows(x)
+    c2, s2 = ci._quantize_rows(x)
+    np.testing.assert_array_equal(s1, s2)
+    np.testing.assert_array_equal(c1, c2)
+    ct, st = oracle.quantize_cols_transposed(x)
+    np.testing.assert_array_equal(ct, oracle.quantize_rows(x.T)[0])
+    assert ct.shape == (96, 64) and st.shape == (96,)
