@@ -259,6 +259,21 @@ coda_status coda_gemm_res_prms_fp8(int64_t M, int64_t K, int64_t D,
                                    void* H, int64_t ldh, void* Hg8, int64_t ldhg,
                                    float* partials, void* stream);
 
+/* Quantisation of a bf16 operand for the fp8 GEMMs (the recipe above): per
+ * row of X [M,K], scale = amax / 448 (1 for an all-zero row) and
+ * X8 = e4m3_rne(clamp(x / scale, +-448)), the division correctly rounded in
+ * float32.  X: bf16 [M,K] (ldx); X8: e4m3 [M,K] (ldx8); scales: float[M].
+ * K a multiple of 16; inputs finite.  X8 and scales must not overlap X. */
+coda_status coda_quantize_rows_e4m3(int64_t M, int64_t K, const void* X, int64_t ldx,
+                                    void* X8, int64_t ldx8, float* scales, void* stream);
+
+/* The weight variant: W bf16 [K,N] (ldw, N contiguous) gives the transposed
+ * codes Wt8 [N,K] (ldwt, K contiguous) with one scale per output channel n,
+ * the layout coda_gemm_res_prms_fp8 and coda_gemm_rowscale_fp8 take.  K and
+ * N multiples of 16.  Run once per weight update. */
+coda_status coda_quantize_cols_e4m3(int64_t K, int64_t N, const void* W, int64_t ldw,
+                                    void* Wt8, int64_t ldwt, float* scales, void* stream);
+
 /* Second GEMM, fp8 operands, deferred row scale:
  *   Y_ik = round_bf16((acc_ik * r_i) * sw2_k)    acc = sum_j X8_ij W2t8_kj
  *   X8: e4m3 [M,D] (ldx), e.g. Hg8; W2t8: e4m3 [N2,D] (ldw2t); sw2: float[N2],

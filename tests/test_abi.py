@@ -274,6 +274,25 @@ def test_gemm_rowscale_ce_bwd_rejects(lib, kw, status):
     assert ce_bwd_call(lib, **kw) == status
 
 
+def test_quantize_validation(lib):
+    q = lib.coda_quantize_rows_e4m3
+    assert q(512, 264, H_, 264, HG_, 264, PART_, None) == SHAPE            # K not a multiple of 16
+    assert q(512, 256, None, 256, HG_, 256, PART_, None) == NULL
+    assert q(512, 256, H_, 256, HG_, 256, None, None) == NULL
+    assert q(512, 256, H_, 260, HG_, 256, PART_, None) == ALIGN            # ldx not a multiple of 8
+    assert q(512, 256, H_, 256, HG_, 264, PART_, None) == ALIGN            # ldx8 not a multiple of 16
+    assert q(512, 256, H_, 256, PART_ + 2, 256, PART_, None) == ALIGN
+    assert q(512, 256, H_, 256, H_ + 4096, 256, PART_, None) == ALIAS      # codes over X
+    assert q(512, 256, H_, 256, HG_, 256, H_ + 64, None) == ALIAS          # scales over X
+    assert q(0, 256, None, 256, None, 256, None, None) == OK
+    c = lib.coda_quantize_cols_e4m3
+    assert c(256, 264, W1_, 264, HG_, 256, PART_, None) == SHAPE            # N not a multiple of 16
+    assert c(264, 256, W1_, 256, HG_, 264, PART_, None) == SHAPE            # K not a multiple of 16
+    assert c(256, 512, None, 512, HG_, 256, PART_, None) == NULL
+    assert c(256, 512, W1_, 512, W1_ + 1024, 256, PART_, None) == ALIAS
+    assert c(256, 512, W1_, 512, HG_, 256, PART_ + 1, None) == ALIGN
+
+
 def rope_call(lib, dt=BF16, M=512, D=256, N2=1536, X=H_, ldx=None, W=W2_, ldw=None, r=R2_, pos=DY_, cs=DG_,
               max_pos=2048, nq=512, nk=512, dh=128, Y=Y_, ldy=None):
     return lib.coda_gemm_rowscale_rope(dt, M, D, N2, X, ldx or D, W, ldw or N2, r, pos, cs, max_pos, nq, nk, dh, Y,

@@ -142,3 +142,57 @@ def test_full_size_7b_fp8_sampled_rows():
     err, frac = _check(wl, x, o, rows=rows)
     print(f"7b-fp8 sampled-row Y error {err:.3e}, differing codes {frac:.2e}")
     assert torch.isfinite(o["Y"].float()).all().item()
+
+
+def _bf16_dev(x32):
+    bits = ci.bf16_bits(np.asarray(x32, dtype=np.float32))
+    return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16), ci.bf16_bits_to_f32(bits)
+
+
+@pytest.mark.parametrize("shape", [(1, 16), (3, 48), (257, 272), (300, 4096), (64, 8208)], ids=str)
+def test_quantize_rows_bit_exact(shape):
+    M, K = shape
+    rng = np.random.default_rng(M + K)
+    x = rng.standard_normal((M, K)).astype(np.float32) * np.exp(rng.uniform(-8, 8, size=(M, 1))).astype(np.float32)
+    x[0, :] = 0.0                                   # an all-zero row: scale 1, zero codes
+    if M > 2:
+        x[2, K // 2] = -1e4                         # a negative largest magnitude
+    dx, xf = _bf16_dev(x)
+    X8, sc = coda.quantize_rows_e4m3(dx)
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.quantize_rows(xf)
+    np.testing.assert_array_equal(sc.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(X8.cpu().numpy(), c_ref)
+
+
+@pytest.mark.parametrize("shape", [(16, 16), (48, 80), (272, 144), (4096, 1040)], ids=str)
+def test_quantize_weight_bit_exact(shape):
+    K, N = shape
+    rng = np.random.default_rng(K * 7 + N)
+    w = (rng.standard_normal((K, N)) / np.sqrt(K)).astype(np.float32) * np.exp(rng.uniform(-4, 4, size=(1, N))).astype(np.float32)
+    w[:, 3] = 0.0                                   # an all-zero output channel
+    dw, wf = _bf16_dev(w)
+    Wt8, sc = coda.quantize_weight_e4m3(dw)
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.quantize_cols_transposed(wf)
+    np.testing.assert_array_equal(sc.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(Wt8.cpu().numpy(), c_ref)
+
+
+def test_chain_from_bf16_activation():
+    # A quantised on the device gives the same codes as the oracle's recipe,
+    # and the chain on them meets the fp8 bars
+    wl = ci.custom_workload(300, 512, 384, 1040, dtype="fp8", wl_id=503)
+    x = ci.make_inputs_fp8(wl, seed=4)
+    A32 = np.random.default_rng(5).standard_normal((wl.M, wl.K)).astype(np.float32)
+    dA, Af = _bf16_dev(A32)
+    A8_ref, sa_ref = oracle.quantize_rows(Af)
+    d = {"W1t8": _u8(x["W1t8"]), "sw1": _f32(x["sw1"]), "W2t8": _u8(x["W2t8"]), "sw2": _f32(x["sw2"]),
+         "R": dev(x["R"]), "g": dev(x["g"])}
+    H, Hg8, r, Y, P, A8, sa = coda.fused_forward_fp8_from_bf16(dA, d["W1t8"], d["sw1"], d["R"], d["g"], d["W2t8"],
+                                                               d["sw2"], wl.eps)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(A8.cpu().numpy(), A8_ref)
+    np.testing.assert_array_equal(sa.cpu().numpy(), sa_ref)
+    x2 = dict(x, A8=A8_ref, sa=sa_ref)
+    _check(wl, x2, {"H": H, "Hg8": Hg8, "r": r, "Y": Y})

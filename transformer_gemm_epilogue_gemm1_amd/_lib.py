@@ -39,6 +39,8 @@ SIGNATURES = {
     "coda_ce_combine": (c_int, [c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "coda_gemm_rowscale_ce_bwd": (c_int, [c_int, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp,
                                           c_vp, c_vp, c_i64, c_vp]),
+    "coda_quantize_rows_e4m3": (c_int, [c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp]),
+    "coda_quantize_cols_e4m3": (c_int, [c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp]),
     "coda_rope_cache": (c_int, [c_vp, c_i64, c_i64, c_double, c_vp]),
     "coda_gemm_rowscale_rope": (c_int, [c_int, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp,
                                         c_i64, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp]),

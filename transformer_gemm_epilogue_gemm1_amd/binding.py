@@ -425,6 +425,37 @@ def fused_backward_swiglu(dZ, Y, A, W1, g, W2, H, r, stream=None):
     return fused_backward(dY, A, W1, g, W2, H, r, stream) + (dY,)
 
 
+def quantize_rows_e4m3(X, stream=None, X8=None, scales=None):
+    """Per-row e4m3 codes (uint8 [M, K]) and float32 scales of a bf16 X,
+    into X8 / scales when given."""
+    M, K = X.shape
+    ldx = _mat(X, "X", torch.bfloat16, (M, K))
+    if X8 is None:
+        X8 = torch.empty((M, K), device=X.device, dtype=torch.uint8)
+    if scales is None:
+        scales = torch.empty((M,), device=X.device, dtype=torch.float32)
+    ldx8 = _mat(X8, "X8", torch.uint8, (M, K))
+    _mat(scales, "scales", torch.float32, (M,))
+    sc = scales
+    st = _lib.load().coda_quantize_rows_e4m3(M, K, X.data_ptr(), ldx, X8.data_ptr(), ldx8, sc.data_ptr(),
+                                             _stream(stream))
+    _lib.check("coda_quantize_rows_e4m3", st)
+    return X8, sc
+
+
+def quantize_weight_e4m3(W, stream=None):
+    """Transposed e4m3 codes (uint8 [N, K]) and per-output-channel float32
+    scales of a bf16 weight W [K, N]."""
+    K, N = W.shape
+    ldw = _mat(W, "W", torch.bfloat16, (K, N))
+    Wt8 = torch.empty((N, K), device=W.device, dtype=torch.uint8)
+    sc = torch.empty((N,), device=W.device, dtype=torch.float32)
+    st = _lib.load().coda_quantize_cols_e4m3(K, N, W.data_ptr(), ldw, Wt8.data_ptr(), K, sc.data_ptr(),
+                                             _stream(stream))
+    _lib.check("coda_quantize_cols_e4m3", st)
+    return Wt8, sc
+
+
 def fused_forward_fp8(A8, sa, W1t8, sw1, R, g, W2t8, sw2, eps: float, stream=None):
     """The fused chain with fp8 GEMM operands: returns (H, Hg8, r, Y, partials)."""
     M, D, N2 = A8.shape[0], W1t8.shape[0], W2t8.shape[0]
@@ -486,3 +517,10 @@ def fused_forward_rope(A, W1, R, g, Wqkv, eps: float, positions, cos_sin, n_q: i
     coda_rms_combine(P, r, D, eps, stream)
     coda_gemm_rowscale_rope(Hg, Wqkv, r, positions, cos_sin, n_q, n_k, d_head, Y, stream)
     return H, Hg, r, Y
+
+
+def fused_forward_fp8_from_bf16(A, W1t8, sw1, R, g, W2t8, sw2, eps: float, stream=None):
+    """The fp8 chain fed with a bf16 activation A: A quantised per row on the
+    device, then the fp8 chain; returns (H, Hg8, r, Y, partials, A8, sa)."""
+    A8, sa = quantize_rows_e4m3(A, stream)
+    return fused_forward_fp8(A8, sa, W1t8, sw1, R, g, W2t8, sw2, eps, stream) + (A8, sa)

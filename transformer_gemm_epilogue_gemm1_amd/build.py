@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libcoda.so")
 SOURCES = ["coda.hip"]
 HEADERS = ["gemm.hpp", "gemm_fp8.hpp", "epilogues.hpp", "epilogues_fp8.hpp", "epilogues_rope.hpp",
-           "epilogues_ce.hpp", "rowops.hpp", "tile_map.hpp"]
+           "epilogues_ce.hpp", "quantize_fp8.hpp", "rowops.hpp", "tile_map.hpp"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",

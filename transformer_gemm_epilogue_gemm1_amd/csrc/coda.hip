@@ -16,6 +16,7 @@
 #include "epilogues_fp8.hpp"
 #include "epilogues_ce.hpp"
 #include "epilogues_rope.hpp"
+#include "quantize_fp8.hpp"
 #include "gemm_fp8.hpp"
 #include "rowops.hpp"
 
@@ -504,6 +505,39 @@ coda_status coda_gemm_res_prms_fp8(int64_t M, int64_t K, int64_t D, const void* 
                            (uint8_t*)Hg8, ldhg, partials};
   return launch_gemm_fp8<EpiResPrmsFp8>("coda_gemm_res_prms_fp8", (int)M, (int)D, (int)K, A8, lda, W1t8, ldw1t,
                                         ep, (hipStream_t)stream);
+}
+
+coda_status coda_quantize_rows_e4m3(int64_t M, int64_t K, const void* X, int64_t ldx, void* X8, int64_t ldx8,
+                                    float* scales, void* stream) {
+  coda_status st = check_dims_fp8(M, {{"K", K}});
+  if (st != CODA_OK) return st;
+  if (M == 0) return ok();
+  const Mat mX{X, M, K, ldx, 2, "X"}, mX8{X8, M, K, ldx8, 1, "X8"}, ms{scales, 1, M, M, 4, "scales"};
+  if ((st = check_mat(mX, 8)) != CODA_OK || (st = check_mat(mX8, 16)) != CODA_OK) return st;
+  if (scales == nullptr) return fail(CODA_ERR_NULL, "scales is NULL");
+  if (((uintptr_t)scales & 3) != 0) return fail(CODA_ERR_ALIGN, "scales is not 4-byte aligned");
+  const Mat outs[2] = {mX8, ms};
+  if ((st = check_alias(outs, 2, &mX, 1)) != CODA_OK) return st;
+  hipLaunchKernelGGL(quantize_rows_e4m3_kernel, dim3((unsigned)M), dim3(256), 0, (hipStream_t)stream,
+                     (const uint16_t*)X, ldx, (int)K, (uint8_t*)X8, ldx8, scales);
+  return launch_status("coda_quantize_rows_e4m3");
+}
+
+coda_status coda_quantize_cols_e4m3(int64_t K, int64_t N, const void* W, int64_t ldw, void* Wt8, int64_t ldwt,
+                                    float* scales, void* stream) {
+  coda_status st = check_dims_fp8(N, {{"K", K}});
+  if (st != CODA_OK) return st;
+  if (N == 0) return ok();
+  if (N % 16 != 0) return fail(CODA_ERR_SHAPE, "N = %lld is not a multiple of 16", (long long)N);
+  const Mat mW{W, K, N, ldw, 2, "W"}, mWt{Wt8, N, K, ldwt, 1, "Wt8"}, ms{scales, 1, N, N, 4, "scales"};
+  if ((st = check_mat(mW, 8)) != CODA_OK || (st = check_mat(mWt, 16)) != CODA_OK) return st;
+  if (scales == nullptr) return fail(CODA_ERR_NULL, "scales is NULL");
+  if (((uintptr_t)scales & 3) != 0) return fail(CODA_ERR_ALIGN, "scales is not 4-byte aligned");
+  const Mat outs[2] = {mWt, ms};
+  if ((st = check_alias(outs, 2, &mW, 1)) != CODA_OK) return st;
+  hipLaunchKernelGGL(quantize_cols_e4m3_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, (hipStream_t)stream,
+                     (const uint16_t*)W, ldw, (int)K, (int)N, (uint8_t*)Wt8, ldwt, scales);
+  return launch_status("coda_quantize_cols_e4m3");
 }
 
 coda_status coda_gemm_rowscale_fp8(int64_t M, int64_t D, int64_t N2, const void* X8, int64_t ldx, const void* W2t8,

@@ -1,0 +1,118 @@
+// Quantisation of bf16 operands to e4m3 codes with float32 scales, the
+// recipe of the fp8 chain: the largest magnitude of a row (activations) or of
+// an output channel (weights, stored transposed) maps to 448,
+//   scale = amax / 448 (1 for an all-zero vector),
+//   code  = e4m3_rne(clamp(x / scale, +-448)),
+// the division correctly rounded in float32.  Inputs are finite.
+#pragma once
+
+#include "epilogues_fp8.hpp"
+
+namespace coda {
+
+__device__ __forceinline__ float e4m3_scale(float amax) { return amax > 0.f ? amax / 448.f : 1.f; }
+
+// Largest magnitude over a 256-thread workgroup (wavefront shuffles, then
+// the four wavefronts through LDS); every thread gets the result.
+__device__ __forceinline__ float block_amax(float v, float* red) {
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) v = fmaxf(v, __shfl_xor(v, x));
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return m;
+}
+
+// One workgroup per row of X [M, K] (bf16): scales[row] and the row's codes.
+// K % 8 == 0; each thread takes 8-element chunks, the second pass reads the
+// row again (from cache).
+__global__ __launch_bounds__(256) void quantize_rows_e4m3_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+                                                                 int K, uint8_t* __restrict__ X8, int64_t ldx8,
+                                                                 float* __restrict__ scales) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const uint16_t* x = X + row * ldx;
+  const int nc = K / 8;
+  float m = 0.f;
+  for (int c = threadIdx.x; c < nc; c += 256) {
+    float v[8];
+    Chunk8<uint16_t>::load(x + 8 * c, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  }
+  const float s = e4m3_scale(block_amax(m, red));
+  if (threadIdx.x == 0) scales[row] = s;
+  uint8_t* y = X8 + row * ldx8;
+  for (int c = threadIdx.x; c < nc; c += 256) {
+    float v[8];
+    Chunk8<uint16_t>::load(x + 8 * c, v);
+    const uint32_t lo = pack_e4m3x4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
+    const uint32_t hi = pack_e4m3x4(v[4] / s, v[5] / s, v[6] / s, v[7] / s);
+    *(u32x2*)(y + 8 * c) = u32x2{lo, hi};
+  }
+}
+
+// One workgroup per 64-column strip of W [K, N] (bf16, N contiguous):
+// scales[n] over the strip's columns, then the codes of W^T, Wt8 [N, K]
+// (K contiguous), through 64 x 64 tiles transposed in LDS.  Thread t reads
+// column 8 * (t % 8) .. +7 of k-row t / 8 (+32), and writes 16 codes of
+// output row t / 4 at k offset 16 * (t % 4).  K % 16 == 0, N % 16 == 0;
+// columns past N and k past K are neither read nor written.
+__global__ __launch_bounds__(256) void quantize_cols_e4m3_kernel(const uint16_t* __restrict__ W, int64_t ldw, int K,
+                                                                 int N, uint8_t* __restrict__ Wt8, int64_t ldwt,
+                                                                 float* __restrict__ scales) {
+  __shared__ float tile[64][65];
+  __shared__ float colmax[4][64];
+  __shared__ float colscale[64];
+  const int t = threadIdx.x;
+  const int n0 = blockIdx.x * 64;
+  // pass 1: column maxima; thread t takes column n0 + t % 64, k = t / 64 + 4 j
+  {
+    const int c = t & 63, n = n0 + c;
+    float m = 0.f;
+    if (n < N)
+      for (int k = t >> 6; k < K; k += 4) m = fmaxf(m, fabsf(__uint_as_float((uint32_t)W[(int64_t)k * ldw + n] << 16)));
+    colmax[t >> 6][c] = m;
+    __syncthreads();
+    if (t < 64) {
+      const float s = e4m3_scale(fmaxf(fmaxf(colmax[0][t], colmax[1][t]), fmaxf(colmax[2][t], colmax[3][t])));
+      colscale[t] = s;
+      if (n0 + t < N) scales[n0 + t] = s;
+    }
+    __syncthreads();
+  }
+  // pass 2: 64-row k-blocks, scaled into LDS, written out transposed
+  const int rc = (t & 7) * 8;  // read: column offset in the strip
+  const int wr = t >> 2;       // write: output row (column of W) in the strip
+  const int wk = (t & 3) * 16; // write: k offset in the block
+  for (int k0 = 0; k0 < K; k0 += 64) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kr = (t >> 3) + 32 * h, k = k0 + kr;
+      float v[8];
+      if (k < K && n0 + rc < N) {
+        Chunk8<uint16_t>::load(W + (int64_t)k * ldw + n0 + rc, v);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) tile[kr][rc + i] = v[i] / colscale[rc + i];
+    }
+    __syncthreads();
+    if (n0 + wr < N && k0 + wk < K) {
+      float q[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) q[i] = tile[wk + i][wr];
+      u32x4 out;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[j] = pack_e4m3x4(q[4 * j], q[4 * j + 1], q[4 * j + 2], q[4 * j + 3]);
+      *(u32x4*)(Wt8 + (int64_t)(n0 + wr) * ldwt + k0 + wk) = out;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace coda
