@@ -20,7 +20,15 @@ Sources (the CODA news article by Synced / 机器之心, mirrored by KuCoin News
   * quantising a bf16 operand (quantize_rows): per row, scale = amax / 448
     in float32 (1 for an all-zero row), codes = e4m3(float32(x) / scale),
     the division correctly rounded in float32; a column-wise variant gives
-    the transposed weight codes with per-output-channel scales.
+    the transposed weight codes with per-output-channel scales;
+  * backward (backward_fp8): every product of the chain's backward takes
+    e4m3 operands quantised along its contraction: G = dY W2^T with dY and
+    W2 [D, N2] per row; dW2 = Xn^T dY with Xn and dY per column (their
+    contraction runs over the M rows); dA = dH W1^T with dH and W1 [K, D]
+    per row; dW1 = A^T dH with A and dH per column.  The quantisers are
+    treated as the identity when differentiating (straight-through); the
+    rest is the bf16 chain's backward: P = g G, s = sum_j P H,
+    dg = sum_i r H G, Xn = (H r) g, dH = r P - (r^3 s / D) H, dR = dH.
 
     A   = e4m3(A8) * sa[:, None]            W1 = (e4m3(W1t8) * sw1[:, None])^T
     H   = A W1 + R                          Hb = bf16(H)
@@ -115,3 +123,50 @@ def forward_fp8(A8, sa, W1t8, sw1, R, g, W2t8, sw2, eps: float,
     r = 1.0 / np.sqrt(ms + eps)
     Y = r[:, None] * (e4m3_decode(Hg8) @ W2)
     return {"H": H, "Hb": Hb, "Hg8": Hg8, "r": r, "Y": Y}
+
+
+def _deq_rows(x, on: bool) -> np.ndarray:
+    """x after per-row quantisation and dequantisation (x itself when off)."""
+    if not on:
+        return np.asarray(x, dtype=np.float64)
+    codes, scale = quantize_rows(x)
+    return e4m3_decode(codes) * scale[:, None].astype(np.float64)
+
+
+def _deq_cols(x, on: bool) -> np.ndarray:
+    """x after per-column quantisation and dequantisation."""
+    if not on:
+        return np.asarray(x, dtype=np.float64)
+    return _deq_rows(np.ascontiguousarray(np.asarray(x, dtype=np.float32).T), True).T
+
+
+def backward_fp8(dY, A, W1, R, g, W2, eps: float, H=None, r=None, quantise: bool = True) -> Dict[str, np.ndarray]:
+    """Gradients of <dY, Y> with e4m3 operands in every backward product.
+
+    dY[M,N2], A[M,K], W1[K,D], R[M,D], g[D], W2[D,N2] as float32 values;
+    H[M,D] and r[M] are the forward's (recomputed exactly from A, W1, R when
+    not given).  With quantise=False this is the plain chain's backward.
+    Returns float64 dA, dR, dW1, dW2, dg and the intermediates G, dH, Xn.
+    """
+    A = np.asarray(A, dtype=np.float32)
+    W1 = np.asarray(W1, dtype=np.float32)
+    W2 = np.asarray(W2, dtype=np.float32)
+    dY = np.asarray(dY, dtype=np.float32)
+    g = np.asarray(g, dtype=np.float64)
+    D = W1.shape[1]
+    if H is None:
+        H = A.astype(np.float64) @ W1.astype(np.float64) + np.asarray(R, dtype=np.float64)
+        r = 1.0 / np.sqrt(np.mean(H * H, axis=1) + eps)
+    H = np.asarray(H, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    q = quantise
+    G = _deq_rows(dY, q) @ _deq_rows(W2, q).T          # contraction over N2
+    P = G * g[None, :]
+    s = np.sum(P * H, axis=1)
+    dg = np.sum(r[:, None] * H * G, axis=0)
+    Xn = (H * r[:, None]) * g[None, :]
+    dH = r[:, None] * P - (r ** 3 * s / D)[:, None] * H
+    dW2 = _deq_cols(Xn, q).T @ _deq_cols(dY, q)        # contraction over M
+    dA = _deq_rows(dH, q) @ _deq_rows(W1, q).T          # contraction over D
+    dW1 = _deq_cols(A, q).T @ _deq_cols(dH, q)          # contraction over M
+    return {"dA": dA, "dR": dH.copy(), "dW1": dW1, "dW2": dW2, "dg": dg, "G": G, "dH": dH, "Xn": Xn}

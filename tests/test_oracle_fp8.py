@@ -219,3 +219,69 @@ def test_quantize_matches_the_input_generators_recipe():
     ct, st = oracle.quantize_cols_transposed(x)
     np.testing.assert_array_equal(ct, oracle.quantize_rows(x.T)[0])
     assert ct.shape == (96, 64) and st.shape == (96,)
+
+
+def _bwd_case(seed, M=24, K=32, D=48, N2=64):
+    rng = np.random.default_rng(seed)
+    return dict(dY=rng.standard_normal((M, N2)).astype(np.float32),
+                A=rng.standard_normal((M, K)).astype(np.float32),
+                W1=(rng.standard_normal((K, D)) / np.sqrt(K)).astype(np.float32),
+                R=rng.standard_normal((M, D)).astype(np.float32),
+                g=(1 + 0.1 * rng.standard_normal(D)).astype(np.float32),
+                W2=(rng.standard_normal((D, N2)) / np.sqrt(D)).astype(np.float32))
+
+
+def test_fp8_backward_without_quantisation_is_the_chain_backward():
+    c = _bwd_case(31)
+    got = oracle.backward_fp8(c["dY"], c["A"], c["W1"], c["R"], c["g"], c["W2"], 1e-5, quantise=False)
+    ref = oracle.backward(c["dY"], c["A"], c["W1"], c["R"], c["g"], c["W2"], 1e-5)
+    for k in ("dA", "dR", "dW1", "dW2", "dg"):
+        np.testing.assert_allclose(got[k], ref[k], rtol=1e-10, atol=1e-12, err_msg=k)
+
+
+def test_fp8_backward_close_to_exact():
+    c = _bwd_case(32, M=256, K=128, D=128, N2=256)
+    got = oracle.backward_fp8(c["dY"], c["A"], c["W1"], c["R"], c["g"], c["W2"], 1e-5)
+    ref = oracle.backward(c["dY"], c["A"], c["W1"], c["R"], c["g"], c["W2"], 1e-5)
+    for k in ("dA", "dW1", "dW2", "dg"):
+        rel = np.max(np.abs(got[k] - ref[k])) / np.max(np.abs(ref[k]))
+        assert 1e-4 < rel < 0.08, (k, rel)     # quantised, but within a few e4m3 steps
+
+
+@pytest.mark.parametrize("which", ["dY_row", "W2_row", "dY_col", "W1_row", "A_col"])
+def test_fp8_backward_quantisation_axes(which):
+    # quantisation commutes with a power-of-two scaling of the vector its
+    # scale covers: scaling row i of dY by 8 scales row i of G exactly and
+    # leaves the other rows alone (per-row quantisation of dY); likewise for
+    # W2's rows (G's columns), dY's columns (dW2's columns), W1's rows (dA's
+    # columns) and A's columns (dW1's rows).  A quantiser on the wrong axis
+    # would change the other rows or columns too.
+    c = _bwd_case(33)
+    # fix H and r so that only the backward products see the change
+    H = c["A"].astype(np.float64) @ c["W1"].astype(np.float64) + c["R"]
+    r = 1.0 / np.sqrt(np.mean(H * H, axis=1) + 1e-5)
+    base = oracle.backward_fp8(c["dY"], c["A"], c["W1"], c["R"], c["g"], c["W2"], 1e-5, H=H, r=r)
+    c2 = {k: v.copy() for k, v in c.items()}
+    if which == "dY_row":
+        c2["dY"][5] *= 8
+        out, key, sel, axis = "G", "G", 5, 0
+    elif which == "W2_row":
+        c2["W2"][7] *= 8
+        out, key, sel, axis = "G", "G", 7, 1
+    elif which == "dY_col":
+        c2["dY"][:, 9] *= 8
+        out, key, sel, axis = "dW2", "dW2", 9, 1
+    elif which == "W1_row":
+        c2["W1"][3] *= 8
+        out, key, sel, axis = "dA", "dA", 3, 1
+    else:
+        c2["A"][:, 4] *= 8
+        out, key, sel, axis = "dW1", "dW1", 4, 0
+    new = oracle.backward_fp8(c2["dY"], c2["A"], c2["W1"], c2["R"], c2["g"], c2["W2"], 1e-5, H=H, r=r)
+    a, b = base[key], new[key]
+    if axis == 0:
+        np.testing.assert_array_equal(b[sel], 8 * a[sel])
+        np.testing.assert_array_equal(np.delete(b, sel, axis=0), np.delete(a, sel, axis=0))
+    else:
+        np.testing.assert_array_equal(b[:, sel], 8 * a[:, sel])
+        np.testing.assert_array_equal(np.delete(b, sel, axis=1), np.delete(a, sel, axis=1))

@@ -56,28 +56,39 @@ __global__ __launch_bounds__(256) void quantize_rows_e4m3_kernel(const uint16_t*
 
 // One workgroup per 64-column strip of W [K, N] (bf16, N contiguous):
 // scales[n] over the strip's columns, then the codes of W^T, Wt8 [N, K]
-// (K contiguous), through 64 x 64 tiles transposed in LDS.  Thread t reads
-// column 8 * (t % 8) .. +7 of k-row t / 8 (+32), and writes 16 codes of
-// output row t / 4 at k offset 16 * (t % 4).  K % 16 == 0, N % 16 == 0;
-// columns past N and k past K are neither read nor written.
+// (K contiguous), through 64 x 64 tiles transposed in LDS.  Pass 1: thread t
+// takes the 8 columns 8 * (t % 8) .. +7 of rows t / 8 + 32 j (16-byte
+// loads), the 32 row phases meet in LDS.  Pass 2: thread t reads columns
+// 8 * (t % 8) .. +7 of k-rows t / 8 and t / 8 + 32 of a block, and writes 16
+// codes of output row t / 4 at k offset 16 * (t % 4).  K % 16 == 0,
+// N % 16 == 0; columns past N and k past K are neither read nor written.
 __global__ __launch_bounds__(256) void quantize_cols_e4m3_kernel(const uint16_t* __restrict__ W, int64_t ldw, int K,
                                                                  int N, uint8_t* __restrict__ Wt8, int64_t ldwt,
                                                                  float* __restrict__ scales) {
   __shared__ float tile[64][65];
-  __shared__ float colmax[4][64];
+  __shared__ float colmax[32][65];
   __shared__ float colscale[64];
   const int t = threadIdx.x;
   const int n0 = blockIdx.x * 64;
-  // pass 1: column maxima; thread t takes column n0 + t % 64, k = t / 64 + 4 j
   {
-    const int c = t & 63, n = n0 + c;
-    float m = 0.f;
-    if (n < N)
-      for (int k = t >> 6; k < K; k += 4) m = fmaxf(m, fabsf(__uint_as_float((uint32_t)W[(int64_t)k * ldw + n] << 16)));
-    colmax[t >> 6][c] = m;
+    const int c8 = (t & 7) * 8;
+    float m[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m[i] = 0.f;
+    if (n0 + c8 < N)
+      for (int k = t >> 3; k < K; k += 32) {
+        float v[8];
+        Chunk8<uint16_t>::load(W + (int64_t)k * ldw + n0 + c8, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(v[i]));
+      }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) colmax[t >> 3][c8 + i] = m[i];
     __syncthreads();
     if (t < 64) {
-      const float s = e4m3_scale(fmaxf(fmaxf(colmax[0][t], colmax[1][t]), fmaxf(colmax[2][t], colmax[3][t])));
+      float mx = 0.f;
+      for (int j = 0; j < 32; ++j) mx = fmaxf(mx, colmax[j][t]);
+      const float s = e4m3_scale(mx);
       colscale[t] = s;
       if (n0 + t < N) scales[n0 + t] = s;
     }
