@@ -140,12 +140,17 @@ def _deq_cols(x, on: bool) -> np.ndarray:
     return _deq_rows(np.ascontiguousarray(np.asarray(x, dtype=np.float32).T), True).T
 
 
-def backward_fp8(dY, A, W1, R, g, W2, eps: float, H=None, r=None, quantise: bool = True) -> Dict[str, np.ndarray]:
+def backward_fp8(dY, A, W1, R, g, W2, eps: float, H=None, r=None, quantise: bool = True,
+                 store_bf16: bool = True) -> Dict[str, np.ndarray]:
     """Gradients of <dY, Y> with e4m3 operands in every backward product.
 
     dY[M,N2], A[M,K], W1[K,D], R[M,D], g[D], W2[D,N2] as float32 values;
     H[M,D] and r[M] are the forward's (recomputed exactly from A, W1, R when
-    not given).  With quantise=False this is the plain chain's backward.
+    not given).  store_bf16: the intermediates the recipe keeps in bf16
+    (P, X_n and dH, whose stored values the quantisers see) are rounded to
+    bf16, so that the quantisation decisions are taken on the values the
+    kernels store; s and dg use the unrounded products.  With
+    quantise=False and store_bf16=False this is the plain chain's backward.
     Returns float64 dA, dR, dW1, dW2, dg and the intermediates G, dH, Xn.
     """
     A = np.asarray(A, dtype=np.float32)
@@ -160,12 +165,13 @@ def backward_fp8(dY, A, W1, R, g, W2, eps: float, H=None, r=None, quantise: bool
     H = np.asarray(H, dtype=np.float64)
     r = np.asarray(r, dtype=np.float64)
     q = quantise
+    rnd = bf16_round if store_bf16 else (lambda v: v)
     G = _deq_rows(dY, q) @ _deq_rows(W2, q).T          # contraction over N2
     P = G * g[None, :]
     s = np.sum(P * H, axis=1)
     dg = np.sum(r[:, None] * H * G, axis=0)
-    Xn = (H * r[:, None]) * g[None, :]
-    dH = r[:, None] * P - (r ** 3 * s / D)[:, None] * H
+    Xn = rnd((H * r[:, None]) * g[None, :])
+    dH = rnd(r[:, None] * rnd(P) - (r ** 3 * s / D)[:, None] * H)
     dW2 = _deq_cols(Xn, q).T @ _deq_cols(dY, q)        # contraction over M
     dA = _deq_rows(dH, q) @ _deq_rows(W1, q).T          # contraction over D
     dW1 = _deq_cols(A, q).T @ _deq_cols(dH, q)          # contraction over M
