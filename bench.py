@@ -529,6 +529,50 @@ def bench_fp8(args, stream):
     if pp is not None:
         pp["fp8_peak_at_clock_tflops"] = round(256 * 8192 * pp["gfx_clock_mhz"] * 1e6 / 1e12, 1)
         out["power"] = pp
+    if not args.no_backward:
+        # training step with e4m3 products throughout: the weights re-quantised
+        # (they change every step), A quantised, the fp8 chain, then the fp8
+        # backward (coda_chain_bwd_fp8), beside the bf16 training step
+        dY = torch.randn((M, N2), device=dev, generator=gen).to(torch.bfloat16)
+        dA = torch.empty((M, K), device=dev, dtype=torch.bfloat16)
+        dR = torch.empty((M, D), device=dev, dtype=torch.bfloat16)
+        dW1 = torch.empty((K, D), device=dev, dtype=torch.bfloat16)
+        dW2 = torch.empty((D, N2), device=dev, dtype=torch.bfloat16)
+        dg = torch.empty((D,), device=dev, dtype=torch.float32)
+        lib = coda._lib.load()
+        ws8 = torch.empty((int(lib.coda_chain_bwd_fp8_workspace_bytes(M, K, D, N2)),), device=dev, dtype=torch.uint8)
+        ws16 = torch.empty((int(coda.coda_chain_bwd_workspace_bytes(torch.bfloat16, M, K, D, N2)),), device=dev,
+                           dtype=torch.uint8)
+        Hg = torch.empty((M, D), device=dev, dtype=torch.bfloat16)
+        Y16 = torch.empty((M, N2), device=dev, dtype=torch.bfloat16)
+
+        def bwd8():
+            st = lib.coda_chain_bwd_fp8(M, K, D, N2, dY.data_ptr(), A.data_ptr(), W1.data_ptr(), g.data_ptr(),
+                                        W2.data_ptr(), H.data_ptr(), r.data_ptr(), dA.data_ptr(), dR.data_ptr(),
+                                        dW1.data_ptr(), dW2.data_ptr(), dg.data_ptr(), ws8.data_ptr(), ws8.numel(),
+                                        stream.cuda_stream)
+            coda._lib.check("coda_chain_bwd_fp8", st)
+
+        def train8():
+            coda.quantize_weight_e4m3(W1, stream, W1t8, sw1)
+            coda.quantize_weight_e4m3(W2, stream, W2t8, sw2)
+            step()
+            bwd8()
+
+        def train16():
+            coda.coda_gemm_res_prms(A, W1, R, g, H, Hg, P, stream)
+            coda.coda_rms_combine(P, r, D, wl.eps, stream)
+            coda.coda_gemm_rowscale(Hg, W2, r, Y16, stream)
+            coda.coda_chain_bwd(dY, A, W1, g, W2, H, r, dA, dR, dW1, dW2, dg, ws16, stream)
+
+        b8_ms, t8_ms, t16_ms = time_ms_alternating([bwd8, train8, train16], stream, n, w)
+        bwd_flops = 4.0 * M * D * N2 + 4.0 * M * K * D
+        out["backward_fp8_ms"] = round(b8_ms, 4)
+        out["backward_fp8_tflops"] = round(bwd_flops / (b8_ms * 1e-3) / 1e12, 2)
+        out["train_step_fp8_ms"] = round(t8_ms, 4)
+        out["train_step_bf16_ms"] = round(t16_ms, 4)
+        out["train_step_fp8_speedup_vs_bf16"] = round(t16_ms / t8_ms, 4)
+        del ws8, ws16
     return out
 
 

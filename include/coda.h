@@ -270,7 +270,8 @@ coda_status coda_quantize_rows_e4m3(int64_t M, int64_t K, const void* X, int64_t
 /* The weight variant: W bf16 [K,N] (ldw, N contiguous) gives the transposed
  * codes Wt8 [N,K] (ldwt, K contiguous) with one scale per output channel n,
  * the layout coda_gemm_res_prms_fp8 and coda_gemm_rowscale_fp8 take.  K and
- * N multiples of 16.  Run once per weight update. */
+ * N multiples of 16, K <= 4194240.  scales also serves as the column maxima
+ * while the call runs. */
 coda_status coda_quantize_cols_e4m3(int64_t K, int64_t N, const void* W, int64_t ldw,
                                     void* Wt8, int64_t ldwt, float* scales, void* stream);
 
@@ -342,6 +343,27 @@ coda_status coda_chain_bwd(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64
                            const void* W2, const void* H, const float* r,
                            void* dA, void* dR, void* dW1, void* dW2, float* dg,
                            void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the chain with e4m3 products (the fp8 recipe above, carried to
+ * the backward; the pages give none).  Every product takes e4m3 operands
+ * quantised along its contraction, as coda_quantize_rows_e4m3 does:
+ *   G = dY W2^T       dY per row, W2 [D,N2] per row
+ *   dW2 = X_n^T dY    X_n and dY per column (contraction over the M rows)
+ *   dA = dH W1^T      dH per row, W1 [K,D] per row
+ *   dW1 = A^T dH      A and dH per column
+ * with fp32 accumulation and dequantisation in the epilogues; everything
+ * else (P, X_n, the partial sums, c, dg, dH = r P - c H, dR = dH) is the
+ * bf16 backward's.  The quantisers count as the identity when
+ * differentiating (straight-through).  Arguments as coda_chain_bwd, all
+ * bf16 (r, dg float); M, K, D, N2 multiples of 16, M <= 4194240; ws of
+ * coda_chain_bwd_fp8_workspace_bytes() (the bf16 backward's workspace plus
+ * the e4m3 operands and their scales). */
+size_t coda_chain_bwd_fp8_workspace_bytes(int64_t M, int64_t K, int64_t D, int64_t N2);
+coda_status coda_chain_bwd_fp8(int64_t M, int64_t K, int64_t D, int64_t N2,
+                               const void* dY, const void* A, const void* W1, const void* g,
+                               const void* W2, const void* H, const float* r,
+                               void* dA, void* dR, void* dW1, void* dW2, float* dg,
+                               void* ws, size_t ws_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* coda_status_string(coda_status s);

@@ -504,3 +504,21 @@ def test_package_without_library_fails_loudly(tmp_path):
     out = subprocess.run([_sys.executable, "-c", code], capture_output=True, text=True, cwd=str(tmp_path))
     assert out.returncode == 3, out.stdout + out.stderr
     assert "libcoda.so not built" in out.stdout
+
+
+def test_chain_bwd_fp8_validation(lib):
+    M, K, D, N2 = 512, 256, 512, 768
+    need = lib.coda_chain_bwd_fp8_workspace_bytes(M, K, D, N2)
+    assert need > lib.coda_chain_bwd_workspace_bytes(BF16, M, K, D, N2)   # plus the e4m3 operands
+    assert lib.coda_chain_bwd_fp8_workspace_bytes(-1, K, D, N2) == 0
+
+    def call(M=M, K=K, D=D, N2=N2, dY=DY_, ws=WS_, ws_bytes=None, r=R2_, dW2=DW2_):
+        return lib.coda_chain_bwd_fp8(M, K, D, N2, dY, A_, W1_, G_, W2_, H_, r, DA_, DR_, DW1_, dW2, DG_, ws,
+                                      need if ws_bytes is None else ws_bytes, None)
+    assert call(M=520) == SHAPE            # M not a multiple of 16
+    assert call(D=520) == SHAPE
+    assert call(dY=None) == NULL
+    assert call(r=None) == NULL
+    assert call(ws_bytes=need - 1) == WS
+    assert call(ws=WS_ + 8) == ALIGN
+    assert call(dW2=W2_ + 64) == ALIAS

@@ -20,7 +20,7 @@ import torch
 import coda_inputs as ci
 import oracle
 import transformer_gemm_epilogue_gemm1_amd as coda
-from tests.gpu_util import dev, host_f32, max_rel
+from tests.gpu_util import dev, host_f32, max_rel, round_to
 
 pytestmark = pytest.mark.gpu
 
@@ -196,3 +196,71 @@ def test_chain_from_bf16_activation():
     np.testing.assert_array_equal(sa.cpu().numpy(), sa_ref)
     x2 = dict(x, A8=A8_ref, sa=sa_ref)
     _check(wl, x2, {"H": H, "Hg8": Hg8, "r": r, "Y": Y})
+
+
+GRADS8 = ("dA", "dR", "dW1", "dW2", "dg")
+BWD_SHAPES = [  # M, K, D, N2: multiples of 16, ragged against the 256 tiles
+    (16, 64, 256, 256),
+    (272, 144, 272, 528),
+    (528, 512, 384, 1040),
+    (1024, 1024, 1024, 2048),
+]
+
+
+@pytest.mark.parametrize("shape", BWD_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fp8_backward_matches_oracle(shape):
+    wl = ci.custom_workload(*shape, wl_id=510)
+    x = ci.make_inputs(wl, seed=6, with_dy=True)
+    d = {k: dev(v) for k, v in x.items()}
+    H, Hg, r, Y, P = coda.fused_forward(d["A"], d["W1"], d["R"], d["g"], d["W2"], wl.eps)
+    grads = coda.fused_backward_fp8(d["dY"], d["A"], d["W1"], d["g"], d["W2"], H, r)
+    torch.cuda.synchronize()
+    out = dict(zip(GRADS8, grads))
+    orc = oracle.backward_fp8(x["dY"].f32, x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps,
+                              H=host_f32(H).astype(np.float64), r=r.cpu().numpy().astype(np.float64))
+    # the oracle quantises its own (fp64-computed, bf16-stored) dH and X_n;
+    # where their last bit differs from the GPU's, a code moves one e4m3 step
+    # (up to 2^-3 of that element).  Contractions over many rows average
+    # that out below 1e-2; over the 16 rows of the smallest case it can
+    # reach 2^-3 / sqrt(16) of a term, hence the wider bar there.  The
+    # stage-wise checks below take the GPU's own stored operands.
+    bar = 1e-2 if wl.M >= 256 else 3e-2
+    errs = {}
+    for k in GRADS8:
+        errs[k] = max_rel(host_f32(out[k]), orc[k])
+        assert errs[k] <= bar, f"{k}: error {errs[k]:.3e}"
+    print("fp8 backward errors", {k: f"{v:.2e}" for k, v in errs.items()}, file=sys.__stderr__, flush=True)
+    # stage-wise: dA and dW1 on the GPU's own stored dH, quantised on the host
+    # (one bf16 rounding of an fp32 accumulation)
+    dH = host_f32(out["dR"])
+    deq = lambda c_s: oracle.e4m3_decode(c_s[0]) * c_s[1][:, None].astype(np.float64)
+    dA_host = deq(oracle.quantize_rows(dH)) @ deq(oracle.quantize_rows(x["W1"].f32)).T
+    assert max_rel(host_f32(out["dA"]), dA_host) <= 2.0 ** -8
+    dW1_host = deq(oracle.quantize_cols_transposed(x["A"].f32)) @ deq(oracle.quantize_cols_transposed(dH)).T
+    assert max_rel(host_f32(out["dW1"]), dW1_host) <= 2.0 ** -8
+    Hf, rf = host_f32(H), r.cpu().numpy().astype(np.float32)
+    xn = round_to("bf16", (Hf * rf[:, None]).astype(np.float32) * x["g"].f32[None, :])
+    dW2_host = deq(oracle.quantize_cols_transposed(xn)) @ deq(oracle.quantize_cols_transposed(x["dY"].f32)).T
+    assert max_rel(host_f32(out["dW2"]), dW2_host) <= 2.0 ** -8
+    # repeat calls are bit-identical
+    again = coda.fused_backward_fp8(d["dY"], d["A"], d["W1"], d["g"], d["W2"], H, r)
+    torch.cuda.synchronize()
+    for a, b in zip(grads, again):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
+
+def test_fp8_backward_empty_batch():
+    K, D, N2 = 64, 256, 256
+    dev_ = "cuda"
+    W1 = torch.randn(K, D, device=dev_).to(torch.bfloat16)
+    W2 = torch.randn(D, N2, device=dev_).to(torch.bfloat16)
+    g = torch.ones(D, device=dev_).to(torch.bfloat16)
+    e = torch.empty((0, N2), device=dev_, dtype=torch.bfloat16)
+    a = torch.empty((0, K), device=dev_, dtype=torch.bfloat16)
+    h = torch.empty((0, D), device=dev_, dtype=torch.bfloat16)
+    r = torch.empty((0,), device=dev_, dtype=torch.float32)
+    dA, dR, dW1, dW2, dg = coda.fused_backward_fp8(e, a, W1, g, W2, h, r)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dW1).item() == 0 and torch.count_nonzero(dW2).item() == 0
+    assert torch.count_nonzero(dg).item() == 0

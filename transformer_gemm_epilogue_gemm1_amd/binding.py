@@ -443,14 +443,19 @@ def quantize_rows_e4m3(X, stream=None, X8=None, scales=None):
     return X8, sc
 
 
-def quantize_weight_e4m3(W, stream=None):
+def quantize_weight_e4m3(W, stream=None, Wt8=None, scales=None):
     """Transposed e4m3 codes (uint8 [N, K]) and per-output-channel float32
-    scales of a bf16 weight W [K, N]."""
+    scales of a bf16 weight W [K, N], into Wt8 / scales when given."""
     K, N = W.shape
     ldw = _mat(W, "W", torch.bfloat16, (K, N))
-    Wt8 = torch.empty((N, K), device=W.device, dtype=torch.uint8)
-    sc = torch.empty((N,), device=W.device, dtype=torch.float32)
-    st = _lib.load().coda_quantize_cols_e4m3(K, N, W.data_ptr(), ldw, Wt8.data_ptr(), K, sc.data_ptr(),
+    if Wt8 is None:
+        Wt8 = torch.empty((N, K), device=W.device, dtype=torch.uint8)
+    if scales is None:
+        scales = torch.empty((N,), device=W.device, dtype=torch.float32)
+    ldwt = _mat(Wt8, "Wt8", torch.uint8, (N, K))
+    _mat(scales, "scales", torch.float32, (N,))
+    sc = scales
+    st = _lib.load().coda_quantize_cols_e4m3(K, N, W.data_ptr(), ldw, Wt8.data_ptr(), ldwt, sc.data_ptr(),
                                              _stream(stream))
     _lib.check("coda_quantize_cols_e4m3", st)
     return Wt8, sc
@@ -524,3 +529,30 @@ def fused_forward_fp8_from_bf16(A, W1t8, sw1, R, g, W2t8, sw2, eps: float, strea
     device, then the fp8 chain; returns (H, Hg8, r, Y, partials, A8, sa)."""
     A8, sa = quantize_rows_e4m3(A, stream)
     return fused_forward_fp8(A8, sa, W1t8, sw1, R, g, W2t8, sw2, eps, stream) + (A8, sa)
+
+
+def fused_backward_fp8(dY, A, W1, g, W2, H, r, stream=None):
+    """Backward of the chain with e4m3 products (coda_chain_bwd_fp8), bf16
+    tensors in and out; returns (dA, dR, dW1, dW2, dg)."""
+    lib = _lib.load()
+    M, K = A.shape
+    D, N2 = W1.shape[1], W2.shape[1]
+    bf = torch.bfloat16
+    for t, n, shp in ((dY, "dY", (M, N2)), (A, "A", (M, K)), (W1, "W1", (K, D)), (g, "g", (D,)), (W2, "W2", (D, N2)),
+                      (H, "H", (M, D))):
+        _mat(t, n, bf, shp)
+        _dense(t, n)
+    _mat(r, "r", torch.float32, (M,))
+    dev = A.device
+    dA = torch.empty((M, K), device=dev, dtype=bf)
+    dR = torch.empty((M, D), device=dev, dtype=bf)
+    dW1 = torch.empty((K, D), device=dev, dtype=bf)
+    dW2 = torch.empty((D, N2), device=dev, dtype=bf)
+    dg = torch.empty((D,), device=dev, dtype=torch.float32)
+    nbytes = int(lib.coda_chain_bwd_fp8_workspace_bytes(M, K, D, N2))
+    ws = torch.empty((max(nbytes, 256),), device=dev, dtype=torch.uint8)
+    st = lib.coda_chain_bwd_fp8(M, K, D, N2, dY.data_ptr(), A.data_ptr(), W1.data_ptr(), g.data_ptr(), W2.data_ptr(),
+                                H.data_ptr(), r.data_ptr(), dA.data_ptr(), dR.data_ptr(), dW1.data_ptr(),
+                                dW2.data_ptr(), dg.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
+    _lib.check("coda_chain_bwd_fp8", st)
+    return dA, dR, dW1, dW2, dg

@@ -43,6 +43,7 @@ coda_status ok() {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 constexpr int64_t kMaxSpan = ((int64_t)1 << 31) - 256;  // 32-bit buffer offsets inside one matrix
+constexpr int64_t kMaxColRows = 65535 * 64;  // rows of a column-wise quantisation (grid y of its 64-row blocks)
 
 int elem_size(coda_dtype dt) { return dt == CODA_BF16 ? 2 : 4; }
 int elems_per_chunk(coda_dtype dt) { return dt == CODA_BF16 ? 8 : 4; }
@@ -262,6 +263,108 @@ coda_status chain_bwd_impl(int M, int K, int D, int N2, const void* dY, const vo
     return st;
   return launch_gemm<T, false, false, EpiRowScale<T>>("coda_chain_bwd dW2", D, N2, M, Xn, D, b6, N2,
                                                       typename EpiRowScale<T>::Params{nullptr, (T*)dW2, N2}, s);
+}
+
+// Workspace of the fp8 backward: the bf16 backward's (X_n, partial sums, c)
+// followed by the e4m3 operands of the four products and their scales.
+struct Bwd8Ws {
+  BwdWs b;
+  size_t dy8, sdy, dyt8, sdyt, w2q, sw2, w1q, sw1, dh8, sdh, dht8, sdht, xnt8, sxn, at8, sat, total;
+  Bwd8Ws(int64_t M, int64_t K, int64_t D, int64_t N2) : b(M, D, 2) {
+    size_t o = b.total;
+    auto take = [&o](int64_t bytes) {
+      const size_t at = o;
+      o = align_up(o + (size_t)bytes);
+      return at;
+    };
+    dy8 = take(M * N2);
+    sdy = take(M * 4);
+    dyt8 = take(N2 * M);
+    sdyt = take(N2 * 4);
+    w2q = take(D * N2);
+    sw2 = take(D * 4);
+    w1q = take(K * D);
+    sw1 = take(K * 4);
+    dh8 = take(M * D);
+    sdh = take(M * 4);
+    dht8 = take(D * M);
+    sdht = take(D * 4);
+    xnt8 = take(D * M);
+    sxn = take(D * 4);
+    at8 = take(K * M);
+    sat = take(K * 4);
+    total = o;
+  }
+};
+
+// Unchecked launches of the quantisers (shapes validated by the caller).
+void q_rows(const void* X, int64_t ldx, int M, int K, void* X8, int64_t ldx8, float* sc, hipStream_t s) {
+  hipLaunchKernelGGL(quantize_rows_e4m3_kernel, dim3((unsigned)M), dim3(256), 0, s, (const uint16_t*)X, ldx, K,
+                     (uint8_t*)X8, ldx8, sc);
+}
+void q_cols(const void* W, int64_t ldw, int K, int N, void* Wt8, int64_t ldwt, float* sc, hipStream_t s) {
+  const unsigned strips = (unsigned)((N + 63) / 64);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, (uint32_t*)sc, N, 0u);
+  hipLaunchKernelGGL(colmax_kernel, dim3(strips, (unsigned)((K + 255) / 256)), dim3(256), 0, s, (const uint16_t*)W,
+                     ldw, K, N, (uint32_t*)sc);
+  hipLaunchKernelGGL(quantize_cols_kernel, dim3(strips, (unsigned)((K + 63) / 64)), dim3(256), 0, s,
+                     (const uint16_t*)W, ldw, K, N, (const uint32_t*)sc, (uint8_t*)Wt8, ldwt);
+  hipLaunchKernelGGL(amax_to_scale_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, sc, N);
+}
+
+// The chain's backward with every product on e4m3 operands quantised along
+// its contraction (bf16 tensors in and out); the per-element steps are the
+// bf16 backward's.  M > 0, all sizes multiples of 16.
+coda_status chain_bwd_fp8_impl(int M, int K, int D, int N2, const void* dY, const void* A, const void* W1,
+                               const void* g, const void* W2, const void* H, const float* r, void* dA, void* dR,
+                               void* dW1, void* dW2, float* dg, char* ws, hipStream_t s) {
+  const Bwd8Ws L(M, K, D, N2);
+  uint16_t* Xn = (uint16_t*)(ws + L.b.xn);
+  float* srow = (float*)(ws + L.b.srow);
+  float* dgcol = (float*)(ws + L.b.dgcol);
+  float* c = (float*)(ws + L.b.c);
+  auto f = [ws](size_t o) { return (float*)(ws + o); };
+  const int Tn = (int)num_partials(D), U = (M + kWaveM - 1) / kWaveM;
+  coda_status st;
+  // operands of G = dY W2^T (rows) and dW2 = X_n^T dY (dY's columns)
+  q_rows(dY, N2, M, N2, ws + L.dy8, N2, f(L.sdy), s);
+  q_cols(dY, N2, M, N2, ws + L.dyt8, M, f(L.sdyt), s);
+  q_rows(W2, N2, D, N2, ws + L.w2q, N2, f(L.sw2), s);
+  q_rows(W1, D, K, D, ws + L.w1q, D, f(L.sw1), s);
+  if ((st = launch_status("coda_chain_bwd_fp8 quantise dY, W1, W2")) != CODA_OK) return st;
+  // 1. G with the P / X_n / partial-sum epilogue, after dequantisation
+  using EpiG = EpiDequant<EpiBwdG<uint16_t>>;
+  typename EpiG::Params eg{f(L.sdy), f(L.sw2), {(const uint16_t*)H, (const uint16_t*)g, r, (uint16_t*)dR, Xn, D,
+                                                srow, dgcol}};
+  if ((st = launch_gemm_fp8<EpiG>("coda_chain_bwd_fp8 G", M, D, N2, ws + L.dy8, N2, ws + L.w2q, N2, eg, s)) !=
+      CODA_OK)
+    return st;
+  // 2. c and dg;  3. dH in place in dR
+  hipLaunchKernelGGL(bwd_combine_kernel, dim3((unsigned)((M + 63) / 64 + (D + 63) / 64)), dim3(256), 0, s, srow,
+                     dgcol, r, c, dg, M, Tn, D, U);
+  const int64_t nchunks = (int64_t)M * D / 8;
+  const int blocks = (int)((nchunks + 255) / 256 < 16384 ? (nchunks + 255) / 256 : 16384);
+  hipLaunchKernelGGL(dh_finalize_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, (uint16_t*)dR, (const uint16_t*)H,
+                     r, c, D, nchunks);
+  // operands of dA = dH W1^T (dH rows), dW1 = A^T dH and dW2 = X_n^T dY (columns)
+  q_rows(dR, D, M, D, ws + L.dh8, D, f(L.sdh), s);
+  q_cols(dR, D, M, D, ws + L.dht8, M, f(L.sdht), s);
+  q_cols(Xn, D, M, D, ws + L.xnt8, M, f(L.sxn), s);
+  q_cols(A, K, M, K, ws + L.at8, M, f(L.sat), s);
+  if ((st = launch_status("coda_chain_bwd_fp8 combine, dH, quantise")) != CODA_OK) return st;
+  using EpiO = EpiDequant<EpiRowScale<uint16_t>>;
+  // 4. dA = dH W1^T
+  if ((st = launch_gemm_fp8<EpiO>("coda_chain_bwd_fp8 dA", M, K, D, ws + L.dh8, D, ws + L.w1q, D,
+                                  typename EpiO::Params{f(L.sdh), f(L.sw1), {nullptr, (uint16_t*)dA, K}}, s)) !=
+      CODA_OK)
+    return st;
+  // 5. dW1 = A^T dH;  6. dW2 = X_n^T dY  (contraction over the M rows)
+  if ((st = launch_gemm_fp8<EpiO>("coda_chain_bwd_fp8 dW1", K, D, M, ws + L.at8, M, ws + L.dht8, M,
+                                  typename EpiO::Params{f(L.sat), f(L.sdht), {nullptr, (uint16_t*)dW1, D}}, s)) !=
+      CODA_OK)
+    return st;
+  return launch_gemm_fp8<EpiO>("coda_chain_bwd_fp8 dW2", D, N2, M, ws + L.xnt8, M, ws + L.dyt8, M,
+                               typename EpiO::Params{f(L.sxn), f(L.sdyt), {nullptr, (uint16_t*)dW2, N2}}, s);
 }
 
 // Shared checks of the RoPE entry points: head layout, positions, table.
@@ -529,14 +632,14 @@ coda_status coda_quantize_cols_e4m3(int64_t K, int64_t N, const void* W, int64_t
   if (st != CODA_OK) return st;
   if (N == 0) return ok();
   if (N % 16 != 0) return fail(CODA_ERR_SHAPE, "N = %lld is not a multiple of 16", (long long)N);
+  if (K > kMaxColRows) return fail(CODA_ERR_SHAPE, "K = %lld exceeds %lld rows", (long long)K, (long long)kMaxColRows);
   const Mat mW{W, K, N, ldw, 2, "W"}, mWt{Wt8, N, K, ldwt, 1, "Wt8"}, ms{scales, 1, N, N, 4, "scales"};
   if ((st = check_mat(mW, 8)) != CODA_OK || (st = check_mat(mWt, 16)) != CODA_OK) return st;
   if (scales == nullptr) return fail(CODA_ERR_NULL, "scales is NULL");
   if (((uintptr_t)scales & 3) != 0) return fail(CODA_ERR_ALIGN, "scales is not 4-byte aligned");
   const Mat outs[2] = {mWt, ms};
   if ((st = check_alias(outs, 2, &mW, 1)) != CODA_OK) return st;
-  hipLaunchKernelGGL(quantize_cols_e4m3_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, (hipStream_t)stream,
-                     (const uint16_t*)W, ldw, (int)K, (int)N, (uint8_t*)Wt8, ldwt, scales);
+  q_cols(W, ldw, (int)K, (int)N, Wt8, ldwt, scales, (hipStream_t)stream);
   return launch_status("coda_quantize_cols_e4m3");
 }
 
@@ -755,6 +858,53 @@ coda_status coda_chain_bwd(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64
                                     (char*)ws, s);
   return chain_bwd_impl<float>((int)M, (int)K, (int)D, (int)N2, dY, A, W1, g, W2, H, r, dA, dR, dW1, dW2, dg,
                                (char*)ws, s);
+}
+
+size_t coda_chain_bwd_fp8_workspace_bytes(int64_t M, int64_t K, int64_t D, int64_t N2) {
+  if (M < 0 || K < 1 || D < 1 || N2 < 1) return 0;
+  return Bwd8Ws(M, K, D, N2).total;
+}
+
+coda_status coda_chain_bwd_fp8(int64_t M, int64_t K, int64_t D, int64_t N2, const void* dY, const void* A,
+                               const void* W1, const void* g, const void* W2, const void* H, const float* r,
+                               void* dA, void* dR, void* dW1, void* dW2, float* dg, void* ws, size_t ws_bytes,
+                               void* stream) {
+  coda_status st = check_dims_fp8(M, {{"K", K}, {"D", D}, {"N2", N2}});
+  if (st != CODA_OK) return st;
+  if (M % 16 != 0) return fail(CODA_ERR_SHAPE, "M = %lld is not a multiple of 16", (long long)M);
+  if (M > kMaxColRows) return fail(CODA_ERR_SHAPE, "M = %lld exceeds %lld rows", (long long)M, (long long)kMaxColRows);
+  const Mat mdY{dY, M, N2, N2, 2, "dY"}, mA{A, M, K, K, 2, "A"}, mH{H, M, D, D, 2, "H"};
+  const Mat mdA{dA, M, K, K, 2, "dA"}, mdR{dR, M, D, D, 2, "dR"};
+  const Mat mW1{W1, K, D, D, 2, "W1"}, mg{g, 1, D, D, 2, "g"}, mW2{W2, D, N2, N2, 2, "W2"};
+  const Mat mdW1{dW1, K, D, D, 2, "dW1"}, mdW2{dW2, D, N2, N2, 2, "dW2"};
+  const Mat mr{r, 1, M, M, 4, "r"}, mdg{dg, 1, D, D, 4, "dg"};
+  for (const Mat* m : {&mW1, &mg, &mW2, &mdW1, &mdW2})
+    if ((st = check_mat(*m, 8)) != CODA_OK) return st;
+  if (M > 0) {
+    for (const Mat* m : {&mdY, &mA, &mH, &mdA, &mdR})
+      if ((st = check_mat(*m, 8)) != CODA_OK) return st;
+    if (r == nullptr) return fail(CODA_ERR_NULL, "r is NULL");
+    if (((uintptr_t)r & 3) != 0) return fail(CODA_ERR_ALIGN, "r is not 4-byte aligned");
+  }
+  if (dg == nullptr) return fail(CODA_ERR_NULL, "dg is NULL");
+  if (((uintptr_t)dg & 3) != 0) return fail(CODA_ERR_ALIGN, "dg is not 4-byte aligned");
+  const Bwd8Ws L(M, K, D, N2);
+  if (ws == nullptr || ws_bytes < L.total)
+    return fail(CODA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, ws ? ws_bytes : (size_t)0);
+  if (((uintptr_t)ws & (kWsAlign - 1)) != 0) return fail(CODA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  for (int64_t bytes : {M * N2, N2 * M, D * N2, K * D, M * D, K * M})
+    if (bytes > kMaxSpan) return fail(CODA_ERR_SHAPE, "an e4m3 workspace operand spans more than 2 GiB");
+  const Mat mws{ws, 1, (int64_t)L.total, (int64_t)L.total, 1, "workspace"};
+  const Mat none{nullptr, 0, 0, 0, 2, ""};
+  const Mat outs[6] = {M > 0 ? mdA : none, M > 0 ? mdR : none, mdW1, mdW2, mdg, mws};
+  const Mat ins[7] = {M > 0 ? mdY : none, M > 0 ? mA : none, mW1, mg, mW2, M > 0 ? mH : none, M > 0 ? mr : none};
+  if ((st = check_alias(outs, 6, ins, 7)) != CODA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (M == 0)  // no rows: zero weight gradients and dg, as the bf16 backward writes them
+    return chain_bwd_impl<uint16_t>(0, (int)K, (int)D, (int)N2, dY, A, W1, g, W2, H, r, dA, dR, dW1, dW2, dg,
+                                    (char*)ws, s);
+  return chain_bwd_fp8_impl((int)M, (int)K, (int)D, (int)N2, dY, A, W1, g, W2, H, r, dA, dR, dW1, dW2, dg,
+                            (char*)ws, s);
 }
 
 const char* coda_status_string(coda_status s) {

@@ -54,76 +54,94 @@ __global__ __launch_bounds__(256) void quantize_rows_e4m3_kernel(const uint16_t*
   }
 }
 
-// One workgroup per 64-column strip of W [K, N] (bf16, N contiguous):
-// scales[n] over the strip's columns, then the codes of W^T, Wt8 [N, K]
-// (K contiguous), through 64 x 64 tiles transposed in LDS.  Pass 1: thread t
-// takes the 8 columns 8 * (t % 8) .. +7 of rows t / 8 + 32 j (16-byte
-// loads), the 32 row phases meet in LDS.  Pass 2: thread t reads columns
-// 8 * (t % 8) .. +7 of k-rows t / 8 and t / 8 + 32 of a block, and writes 16
-// codes of output row t / 4 at k offset 16 * (t % 4).  K % 16 == 0,
-// N % 16 == 0; columns past N and k past K are neither read nor written.
-__global__ __launch_bounds__(256) void quantize_cols_e4m3_kernel(const uint16_t* __restrict__ W, int64_t ldw, int K,
-                                                                 int N, uint8_t* __restrict__ Wt8, int64_t ldwt,
-                                                                 float* __restrict__ scales) {
+// Column-wise quantisation of W [K, N] (bf16, N contiguous) into the codes
+// of W^T, Wt8 [N, K] (K contiguous), one scale per column, in three steps
+// that keep every CU busy for tall matrices (activations of 16k rows as
+// well as weights):
+//   1. colmax_kernel: each workgroup takes a 64-column x 256-row block and
+//      folds its column maxima into amax (the scales array, zeroed first) with
+//      atomic max on the float bits (non-negative floats order like their
+//      bits; the result does not depend on the order);
+//   2. quantize_cols_kernel: each workgroup encodes a 64 x 64 block through
+//      LDS, transposed, with the scales of its columns;
+//   3. amax_to_scale_kernel turns the maxima into the scales in place.
+// K % 16 == 0, N % 16 == 0; columns past N and rows past K are neither read
+// nor written.
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p, int n, uint32_t v) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// Thread t: the 8 columns 8 * (t % 8) .. +7 of the block's rows t / 8 + 32 j.
+__global__ __launch_bounds__(256) void colmax_kernel(const uint16_t* __restrict__ W, int64_t ldw, int K, int N,
+                                                     uint32_t* __restrict__ amax) {
+  __shared__ float part[32][65];
+  const int t = threadIdx.x;
+  const int n0 = blockIdx.x * 64, k0 = blockIdx.y * 256;
+  const int c8 = (t & 7) * 8;
+  float m[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m[i] = 0.f;
+  if (n0 + c8 < N) {
+    const int k1 = k0 + 256 < K ? k0 + 256 : K;
+    for (int k = k0 + (t >> 3); k < k1; k += 32) {
+      float v[8];
+      Chunk8<uint16_t>::load(W + (int64_t)k * ldw + n0 + c8, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(v[i]));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) part[t >> 3][c8 + i] = m[i];
+  __syncthreads();
+  if (t < 64 && n0 + t < N) {
+    float mx = 0.f;
+    for (int j = 0; j < 32; ++j) mx = fmaxf(mx, part[j][t]);
+    atomicMax(amax + n0 + t, __float_as_uint(mx));
+  }
+}
+
+// Thread t reads columns 8 * (t % 8) .. +7 of block rows t / 8 and t / 8 + 32,
+// and writes 16 codes of output row t / 4 at k offset 16 * (t % 4).
+__global__ __launch_bounds__(256) void quantize_cols_kernel(const uint16_t* __restrict__ W, int64_t ldw, int K,
+                                                            int N, const uint32_t* __restrict__ amax,
+                                                            uint8_t* __restrict__ Wt8, int64_t ldwt) {
   __shared__ float tile[64][65];
-  __shared__ float colmax[32][65];
   __shared__ float colscale[64];
   const int t = threadIdx.x;
-  const int n0 = blockIdx.x * 64;
-  {
-    const int c8 = (t & 7) * 8;
-    float m[8];
+  const int n0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
+  if (t < 64) colscale[t] = e4m3_scale(n0 + t < N ? __uint_as_float(amax[n0 + t]) : 0.f);
+  __syncthreads();
+  const int rc = (t & 7) * 8;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m[i] = 0.f;
-    if (n0 + c8 < N)
-      for (int k = t >> 3; k < K; k += 32) {
-        float v[8];
-        Chunk8<uint16_t>::load(W + (int64_t)k * ldw + n0 + c8, v);
+  for (int h = 0; h < 2; ++h) {
+    const int kr = (t >> 3) + 32 * h, k = k0 + kr;
+    float v[8];
+    if (k < K && n0 + rc < N) {
+      Chunk8<uint16_t>::load(W + (int64_t)k * ldw + n0 + rc, v);
+    } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(v[i]));
-      }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) colmax[t >> 3][c8 + i] = m[i];
-    __syncthreads();
-    if (t < 64) {
-      float mx = 0.f;
-      for (int j = 0; j < 32; ++j) mx = fmaxf(mx, colmax[j][t]);
-      const float s = e4m3_scale(mx);
-      colscale[t] = s;
-      if (n0 + t < N) scales[n0 + t] = s;
+      for (int i = 0; i < 8; ++i) v[i] = 0.f;
     }
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tile[kr][rc + i] = v[i] / colscale[rc + i];
   }
-  // pass 2: 64-row k-blocks, scaled into LDS, written out transposed
-  const int rc = (t & 7) * 8;  // read: column offset in the strip
-  const int wr = t >> 2;       // write: output row (column of W) in the strip
-  const int wk = (t & 3) * 16; // write: k offset in the block
-  for (int k0 = 0; k0 < K; k0 += 64) {
+  __syncthreads();
+  const int wr = t >> 2, wk = (t & 3) * 16;
+  if (n0 + wr < N && k0 + wk < K) {
+    float q[16];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int kr = (t >> 3) + 32 * h, k = k0 + kr;
-      float v[8];
-      if (k < K && n0 + rc < N) {
-        Chunk8<uint16_t>::load(W + (int64_t)k * ldw + n0 + rc, v);
-      } else {
+    for (int i = 0; i < 16; ++i) q[i] = tile[wk + i][wr];
+    u32x4 out;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.f;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) tile[kr][rc + i] = v[i] / colscale[rc + i];
-    }
-    __syncthreads();
-    if (n0 + wr < N && k0 + wk < K) {
-      float q[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) q[i] = tile[wk + i][wr];
-      u32x4 out;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) out[j] = pack_e4m3x4(q[4 * j], q[4 * j + 1], q[4 * j + 2], q[4 * j + 3]);
-      *(u32x4*)(Wt8 + (int64_t)(n0 + wr) * ldwt + k0 + wk) = out;
-    }
-    __syncthreads();
+    for (int j = 0; j < 4; ++j) out[j] = pack_e4m3x4(q[4 * j], q[4 * j + 1], q[4 * j + 2], q[4 * j + 3]);
+    *(u32x4*)(Wt8 + (int64_t)(n0 + wr) * ldwt + k0 + wk) = out;
   }
+}
+
+__global__ __launch_bounds__(256) void amax_to_scale_kernel(float* __restrict__ scales, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) scales[i] = e4m3_scale(scales[i]);
 }
 
 }  // namespace coda
