@@ -60,6 +60,9 @@ def parse():
                     help="skip the chain ending in the LM head and the per-token cross-entropy")
     ap.add_argument("--no-g-placement", action="store_true",
                     help="skip timing the chain with g folded into W2 against g in the first GEMM's epilogue")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="cold-cache sensitivity check: write this many MiB of scratch before each of a few extra "
+                         "steps timed on their own (0 disables)")
     ap.add_argument("--no-rope", action="store_true",
                     help="skip the QKV projection with RoPE (7B attention shape)")
     ap.add_argument("--no-swiglu", action="store_true",
@@ -119,10 +122,23 @@ def cpu_baseline(wl, x, budget_s: float):
     t0 = time.perf_counter()
     oracle.forward(x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps, rows=rows)
     dt = time.perf_counter() - t0
-    return {"value": round(n * row_flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"rows 0..{n - 1} of the {wl.M}-row {wl.name} forward chain (rows are independent), "
-                      f"fp64 numpy, {dt:.2f} s, including the oracle's own fp64 weight conversion"}
+    out = {"value": round(n * row_flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores),
+           "kind": "oracle", "seconds": round(dt, 3),
+           "sample": f"rows 0..{n - 1} of the {wl.M}-row {wl.name} forward chain (rows are independent), "
+                     f"fp64 numpy, {dt:.2f} s, including the oracle's own fp64 weight conversion"}
+    # the backward on a row sample (the weight gradients are sums over rows,
+    # so a row sample is a proportional share of the work): same dY recipe
+    nb = int(min(wl.M, 2048))
+    rng = np.random.default_rng(0)
+    dY = rng.standard_normal((nb, wl.N2)).astype(np.float32)
+    t0 = time.perf_counter()
+    oracle.backward(dY, x["A"].f32[:nb], x["W1"].f32, x["R"].f32[:nb], x["g"].f32, x["W2"].f32, wl.eps)
+    db = time.perf_counter() - t0
+    bwd_row_flops = 2.0 * (2.0 * wl.D * wl.N2 + 2.0 * wl.K * wl.D)
+    out["backward"] = {"value": round(nb * bwd_row_flops / db / 1e12, 5), "unit": "TFLOP/s", "seconds": round(db, 3),
+                       "sample": f"rows 0..{nb - 1}: the fp64 backward of the chain on them (with its forward "
+                                 "recomputation, not counted)"}
+    return out
 
 
 def time_ms(fn, stream, n, warmup):
@@ -880,6 +896,24 @@ def main():
                                                                else Hr, H.view(torch.int16)
                                                                if tdt == torch.bfloat16 else H))
         del ws, Hr, rr, Yr
+
+    if args.flush_mib > 0:
+        # sensitivity check: every step starts with cold caches (a write of
+        # flush_mib of scratch before it, outside the step's events)
+        scratch = torch.empty((args.flush_mib << 20,), device=dev, dtype=torch.uint8)
+        nf = max(5, args.steps // 2)
+        fe = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nf)]
+        for i in range(nf):
+            scratch.fill_(i & 0xFF)
+            fe[i][0].record(stream)
+            step()
+            fe[i][1].record(stream)
+        torch.cuda.synchronize()
+        cold = [a.elapsed_time(b) for a, b in fe]
+        out["cold_cache"] = {"flush_mib": args.flush_mib, "steps": nf,
+                             "ms_per_step_median": round(float(np.median(cold)), 4),
+                             "slowdown_vs_warm": round(float(np.median(cold)) / ms_step, 4)}
+        del scratch
 
     if not args.no_g_placement:
         out["g_placement"] = bench_g_placement(wl, d, H, Hg, P, r, Y, step, stream, args)
