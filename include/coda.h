@@ -327,8 +327,9 @@ coda_status coda_ref_chain(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64
 
 /* Bytes of workspace coda_chain_bwd needs: X_n[M,D] (dtype), row partials
  * float[T*M] (T = coda_prms_num_partials(dt, D)), column partials
- * float[ceil(M/128)*D] and c float[M], each part 256-byte aligned; at least
- * 256 bytes.  0 for invalid arguments. */
+ * float[ceil(M/128)*D], c float[M], and the transposed weights W2^T [N2,D]
+ * and W1^T [D,K] (dtype; G and dA read them row-contiguously), each part
+ * 256-byte aligned; at least 256 bytes.  0 for invalid arguments. */
 size_t coda_chain_bwd_workspace_bytes(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64_t N2);
 
 /* Backward of the chain.  All matrices dense (ld = width).

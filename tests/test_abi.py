@@ -407,17 +407,22 @@ def test_fp8_empty_is_noop(lib):
 def test_chain_bwd_workspace_bytes(lib):
     def al(x):
         return (x + 255) // 256 * 256
-    # X_n [M, D] (dtype), row partials [T, M], column partials [ceil(M/128), D], c [M]
-    M, D = 16384, 4096
+    # X_n [M, D] (dtype), row partials [T, M], column partials [ceil(M/128), D],
+    # c [M], W2^T [N2, D] and W1^T [D, K] (dtype)
+    M, K, D, N2 = 16384, 4096, 4096, 28672
     xn = al(M * D * 2)
     srow = al(xn + 64 * M * 4)
     dgcol = al(srow + (M // 128) * D * 4)
-    assert lib.coda_chain_bwd_workspace_bytes(BF16, M, 4096, D, 28672) == al(dgcol + M * 4)
-    M, D = 300, 264   # ragged: T = 8, U = 3
+    w2t = al(dgcol + M * 4)
+    w1t = al(w2t + N2 * D * 2)
+    assert lib.coda_chain_bwd_workspace_bytes(BF16, M, K, D, N2) == al(w1t + D * K * 2)
+    M, K, D, N2 = 300, 8, 264, 16   # ragged: T = 8, U = 3
     xn = al(M * D * 4)
     srow = al(xn + 8 * M * 4)
     dgcol = al(srow + 3 * D * 4)
-    assert lib.coda_chain_bwd_workspace_bytes(F32, M, 8, D, 16) == al(dgcol + M * 4)
+    w2t = al(dgcol + M * 4)
+    w1t = al(w2t + N2 * D * 4)
+    assert lib.coda_chain_bwd_workspace_bytes(F32, M, K, D, N2) == al(w1t + D * K * 4)
     assert lib.coda_chain_bwd_workspace_bytes(7, 16, 8, 8, 8) == 0
     assert lib.coda_chain_bwd_workspace_bytes(BF16, -1, 8, 8, 8) == 0
     assert lib.coda_chain_bwd_workspace_bytes(BF16, 16, 0, 8, 8) == 0

@@ -203,15 +203,20 @@ constexpr size_t kWsAlign = 256;
 size_t align_up(size_t x) { return (x + kWsAlign - 1) & ~(kWsAlign - 1); }
 
 // Workspace parts of the backward, in this order, each 256-byte aligned.
+// Workspace of the backward: X_n, the row and column partial sums, c, and
+// the transposed weights W2^T [N2, D] and W1^T [D, K] (K = N2 = 0: none), so
+// that G = dY W2^T and dA = dH W1^T read their weight row-contiguously.
 struct BwdWs {
-  size_t xn, srow, dgcol, c, total;
-  BwdWs(int64_t M, int64_t D, int es) {
+  size_t xn, srow, dgcol, c, w2t, w1t, total;
+  BwdWs(int64_t M, int64_t K, int64_t D, int64_t N2, int es) {
     const int64_t T = num_partials(D), U = (M + kWaveM - 1) / kWaveM;
     xn = 0;
     srow = align_up(xn + (size_t)M * D * es);
     dgcol = align_up(srow + (size_t)T * M * 4);
     c = align_up(dgcol + (size_t)U * D * 4);
-    total = align_up(c + (size_t)M * 4);
+    w2t = align_up(c + (size_t)M * 4);
+    w1t = align_up(w2t + (size_t)N2 * D * es);
+    total = align_up(w1t + (size_t)D * K * es);
     if (total < kWsAlign) total = kWsAlign;  // never empty: a zero-byte workspace would come as NULL
   }
 };
@@ -220,17 +225,26 @@ template <typename T>
 coda_status chain_bwd_impl(int M, int K, int D, int N2, const void* dY, const void* A, const void* W1,
                            const void* g, const void* W2, const void* H, const float* r, void* dA, void* dR,
                            void* dW1, void* dW2, float* dg, char* ws, hipStream_t s) {
-  const BwdWs L(M, D, sizeof(T));
+  const BwdWs L(M, K, D, N2, sizeof(T));
   T* Xn = (T*)(ws + L.xn);
   float* srow = (float*)(ws + L.srow);
   float* dgcol = (float*)(ws + L.dgcol);
   float* c = (float*)(ws + L.c);
+  T* W2t = (T*)(ws + L.w2t);
+  T* W1t = (T*)(ws + L.w1t);
   const int Tn = (int)num_partials(D), U = (M + kWaveM - 1) / kWaveM;
   coda_status st;
   if (M > 0) {
+    // 0. W2^T and W1^T: the contraction of G and dA then runs across their
+    // rows (transposing LDS reads, no bank conflicts) instead of along them
+    hipLaunchKernelGGL(transpose_kernel<T>, dim3((unsigned)((N2 + 63) / 64), (unsigned)((D + 63) / 64)), dim3(256), 0,
+                       s, (const T*)W2, N2, D, N2, W2t, D);
+    hipLaunchKernelGGL(transpose_kernel<T>, dim3((unsigned)((D + 63) / 64), (unsigned)((K + 63) / 64)), dim3(256), 0,
+                       s, (const T*)W1, D, K, D, W1t, K);
+    if ((st = launch_status("coda_chain_bwd transpose")) != CODA_OK) return st;
     // 1. G = dY W2^T with the P / X_n / partial-sum epilogue
     typename EpiBwdG<T>::Params ep{(const T*)H, (const T*)g, r, (T*)dR, Xn, D, srow, dgcol};
-    if ((st = launch_gemm<T, true, true, EpiBwdG<T>>("coda_chain_bwd G", M, D, N2, dY, N2, W2, N2, ep, s)) !=
+    if ((st = launch_gemm<T, true, false, EpiBwdG<T>>("coda_chain_bwd G", M, D, N2, dY, N2, W2t, D, ep, s)) !=
         CODA_OK)
       return st;
   }
@@ -244,9 +258,9 @@ coda_status chain_bwd_impl(int M, int K, int D, int N2, const void* dY, const vo
     const int blocks = (int)((nchunks + 255) / 256 < 16384 ? (nchunks + 255) / 256 : 16384);
     hipLaunchKernelGGL(dh_finalize_kernel<T>, dim3(blocks), dim3(256), 0, s, (T*)dR, (const T*)H, r, c, D, nchunks);
     if ((st = launch_status("coda_chain_bwd dH")) != CODA_OK) return st;
-    // 4. dA = dH W1^T  (W1[K, D] read as the contraction-contiguous operand)
-    if ((st = launch_gemm<T, true, true, EpiRowScale<T>>("coda_chain_bwd dA", M, K, D, dR, D, W1, D,
-                                                         typename EpiRowScale<T>::Params{nullptr, (T*)dA, K}, s)) !=
+    // 4. dA = dH W1^T  (W1^T [D, K] read row-contiguously)
+    if ((st = launch_gemm<T, true, false, EpiRowScale<T>>("coda_chain_bwd dA", M, K, D, dR, D, W1t, K,
+                                                          typename EpiRowScale<T>::Params{nullptr, (T*)dA, K}, s)) !=
         CODA_OK)
       return st;
   }
@@ -270,7 +284,7 @@ coda_status chain_bwd_impl(int M, int K, int D, int N2, const void* dY, const vo
 struct Bwd8Ws {
   BwdWs b;
   size_t dy8, sdy, dyt8, sdyt, w2q, sw2, w1q, sw1, dh8, sdh, dht8, sdht, xnt8, sxn, at8, sat, total;
-  Bwd8Ws(int64_t M, int64_t K, int64_t D, int64_t N2) : b(M, D, 2) {
+  Bwd8Ws(int64_t M, int64_t K, int64_t D, int64_t N2) : b(M, 0, D, 0, 2) {
     size_t o = b.total;
     auto take = [&o](int64_t bytes) {
       const size_t at = o;
@@ -815,7 +829,7 @@ coda_status coda_ref_chain(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64
 size_t coda_chain_bwd_workspace_bytes(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64_t N2) {
   if (dt != CODA_BF16 && dt != CODA_F32) return 0;
   if (M < 0 || M > kMaxDim || K < 1 || K > kMaxDim || D < 1 || D > kMaxDim || N2 < 1 || N2 > kMaxDim) return 0;
-  return BwdWs(M, D, elem_size(dt)).total;
+  return BwdWs(M, K, D, N2, elem_size(dt)).total;
 }
 
 coda_status coda_chain_bwd(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64_t N2, const void* dY,
@@ -841,7 +855,7 @@ coda_status coda_chain_bwd(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64
   }
   if (dg == nullptr) return fail(CODA_ERR_NULL, "dg is NULL");
   if (((uintptr_t)dg & 3) != 0) return fail(CODA_ERR_ALIGN, "dg is not 4-byte aligned");
-  const BwdWs L(M, D, es);
+  const BwdWs L(M, K, D, N2, es);
   if (ws == nullptr || ws_bytes < L.total)
     return fail(CODA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, ws ? ws_bytes : (size_t)0);
   if (((uintptr_t)ws & (kWsAlign - 1)) != 0) return fail(CODA_ERR_ALIGN, "workspace must be 256-byte aligned");

@@ -261,4 +261,39 @@ __global__ __launch_bounds__(256) void rope_bwd_kernel(const T* __restrict__ dYr
   }
 }
 
+// Y = X^T for X [R, C] (row-major, ldx) into Y [C, R] (ldy), bit-exact,
+// through 64 x 64 tiles in LDS.  Thread t loads 8-element chunk t % 8 of tile
+// rows t / 8 and t / 8 + 32, and stores the two 8-element chunks of output
+// row t / 4 at offsets 16 (t % 4) and 16 (t % 4) + 8.  R % 8 == 0, C % 8 == 0.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ X, int64_t ldx, int R, int C,
+                                                        T* __restrict__ Y, int64_t ldy) {
+  __shared__ float tile[64][65];
+  const int t = threadIdx.x;
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const int cc = (t & 7) * 8;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int rr = (t >> 3) + 32 * h;
+    if (r0 + rr < R && c0 + cc < C) {
+      float v[8];
+      Chunk8<T>::load(X + (int64_t)(r0 + rr) * ldx + c0 + cc, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) tile[rr][cc + i] = v[i];
+    }
+  }
+  __syncthreads();
+  const int j = t >> 2;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i0 = (t & 3) * 16 + 8 * h;
+    if (c0 + j < C && r0 + i0 < R) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = tile[i0 + i][j];
+      Chunk8<T>::store(Y + (int64_t)(c0 + j) * ldy + r0 + i0, v);
+    }
+  }
+}
+
 }  // namespace coda
