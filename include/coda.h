@@ -275,6 +275,19 @@ coda_status coda_quantize_rows_e4m3(int64_t M, int64_t K, const void* X, int64_t
 coda_status coda_quantize_cols_e4m3(int64_t K, int64_t N, const void* W, int64_t ldw,
                                     void* Wt8, int64_t ldwt, float* scales, void* stream);
 
+/* Both quantisations of one bf16 activation X [M,N] (ldx), as the fp8
+ * backward needs them for dY and dH: the row codes X8 [M,N] (ldx8) with
+ * row_scales[M], exactly as coda_quantize_rows_e4m3, and the transposed
+ * column codes Xt8 [N,M] (ldxt) with col_scales[N], exactly as
+ * coda_quantize_cols_e4m3 (X in the role of W).  One pass over X finds both
+ * maxima, a second writes both codes.  M and N multiples of 16,
+ * M <= 4194240; the outputs must not overlap X or each other.  The scale
+ * arrays also serve as the maxima while the call runs. */
+coda_status coda_quantize_rows_cols_e4m3(int64_t M, int64_t N, const void* X, int64_t ldx,
+                                         void* X8, int64_t ldx8, float* row_scales,
+                                         void* Xt8, int64_t ldxt, float* col_scales,
+                                         void* stream);
+
 /* Second GEMM, fp8 operands, deferred row scale:
  *   Y_ik = round_bf16((acc_ik * r_i) * sw2_k)    acc = sum_j X8_ij W2t8_kj
  *   X8: e4m3 [M,D] (ldx), e.g. Hg8; W2t8: e4m3 [N2,D] (ldw2t); sw2: float[N2],

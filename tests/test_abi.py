@@ -291,6 +291,17 @@ def test_quantize_validation(lib):
     assert c(256, 512, None, 512, HG_, 256, PART_, None) == NULL
     assert c(256, 512, W1_, 512, W1_ + 1024, 256, PART_, None) == ALIAS
     assert c(256, 512, W1_, 512, HG_, 256, PART_ + 1, None) == ALIGN
+    rc = lib.coda_quantize_rows_cols_e4m3
+    assert rc(520, 256, H_, 256, HG_, 256, PART_, Y_, 520, R2_, None) == SHAPE      # M not a multiple of 16
+    assert rc(512, 264, H_, 264, HG_, 264, PART_, Y_, 512, R2_, None) == SHAPE      # N not a multiple of 16
+    assert rc(512, 256, None, 256, HG_, 256, PART_, Y_, 512, R2_, None) == NULL
+    assert rc(512, 256, H_, 256, HG_, 256, None, Y_, 512, R2_, None) == NULL
+    assert rc(512, 256, H_, 256, HG_, 256, PART_, Y_, 520, R2_, None) == ALIGN      # ldxt not a multiple of 16
+    assert rc(512, 256, H_, 256, HG_, 256, PART_, Y_, 512, R2_ + 2, None) == ALIGN
+    assert rc(512, 256, H_, 256, H_ + 4096, 256, PART_, Y_, 512, R2_, None) == ALIAS  # row codes over X
+    assert rc(512, 256, H_, 256, HG_, 256, PART_, HG_ + 256, 512, R2_, None) == ALIAS  # the two code arrays
+    assert rc(512, 256, H_, 256, HG_, 256, PART_, Y_, 512, PART_ + 64, None) == ALIAS  # the two scale arrays
+    assert rc(0, 256, None, 256, None, 256, None, None, 0, None, None) == OK
 
 
 def rope_call(lib, dt=BF16, M=512, D=256, N2=1536, X=H_, ldx=None, W=W2_, ldw=None, r=R2_, pos=DY_, cs=DG_,

@@ -149,7 +149,8 @@ def _bf16_dev(x32):
     return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16), ci.bf16_bits_to_f32(bits)
 
 
-@pytest.mark.parametrize("shape", [(1, 16), (3, 48), (257, 272), (300, 4096), (64, 8208)], ids=str)
+@pytest.mark.parametrize("shape", [(1, 16), (3, 48), (257, 272), (300, 4096), (64, 8208), (16, 28672), (4, 40016)],
+                         ids=str)
 def test_quantize_rows_bit_exact(shape):
     M, K = shape
     rng = np.random.default_rng(M + K)
@@ -157,6 +158,7 @@ def test_quantize_rows_bit_exact(shape):
     x[0, :] = 0.0                                   # an all-zero row: scale 1, zero codes
     if M > 2:
         x[2, K // 2] = -1e4                         # a negative largest magnitude
+        x[1, :] *= np.float32(1e-40) / np.abs(x[1]).max()  # subnormal values: a subnormal scale
     dx, xf = _bf16_dev(x)
     X8, sc = coda.quantize_rows_e4m3(dx)
     torch.cuda.synchronize()
@@ -177,6 +179,29 @@ def test_quantize_weight_bit_exact(shape):
     c_ref, s_ref = oracle.quantize_cols_transposed(wf)
     np.testing.assert_array_equal(sc.cpu().numpy(), s_ref)
     np.testing.assert_array_equal(Wt8.cpu().numpy(), c_ref)
+
+
+@pytest.mark.parametrize("shape", [(16, 16), (48, 272), (272, 528), (1040, 4096), (64, 28672)], ids=str)
+def test_quantize_rows_cols_bit_exact(shape):
+    # one call gives both the row quantisation and the transposed column
+    # quantisation of the same activation, each bit-exact against the oracle
+    M, N = shape
+    rng = np.random.default_rng(M * 3 + N)
+    x = (rng.standard_normal((M, N)).astype(np.float32) * np.exp(rng.uniform(-6, 6, size=(M, 1))).astype(np.float32)
+         * np.exp(rng.uniform(-3, 3, size=(1, N))).astype(np.float32))
+    x[1, :] = 0.0                                   # an all-zero row
+    x[:, 2] = 0.0                                   # an all-zero column
+    x[M - 1, N - 1] = -3e4                          # a negative largest magnitude in the ragged corner
+    x[3, :] *= np.float32(1e-40) / np.abs(x[3]).max()  # a row of subnormals
+    dx, xf = _bf16_dev(x)
+    X8, sr, Xt8, sc = coda.quantize_rows_cols_e4m3(dx)
+    torch.cuda.synchronize()
+    r_codes, r_scales = oracle.quantize_rows(xf)
+    c_codes, c_scales = oracle.quantize_cols_transposed(xf)
+    np.testing.assert_array_equal(sr.cpu().numpy(), r_scales)
+    np.testing.assert_array_equal(X8.cpu().numpy(), r_codes)
+    np.testing.assert_array_equal(sc.cpu().numpy(), c_scales)
+    np.testing.assert_array_equal(Xt8.cpu().numpy(), c_codes)
 
 
 def test_chain_from_bf16_activation():

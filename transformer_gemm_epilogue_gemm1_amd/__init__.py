@@ -14,6 +14,7 @@ from .binding import (coda_ce_combine, coda_chain_bwd, coda_chain_bwd_workspace_
                       fused_backward_swiglu, fused_forward, fused_forward_fp8, fused_forward_swiglu, ref_chain,
                       coda_gemm_rowscale_rope, coda_rope_bwd, fused_forward_rope, rope_cache,
                       coda_gemm_rowscale_ce_bwd, fused_backward_ce,
-                      fused_forward_fp8_from_bf16, quantize_rows_e4m3, quantize_weight_e4m3, fused_backward_fp8)
+                      fused_forward_fp8_from_bf16, quantize_rows_e4m3, quantize_weight_e4m3,
+                      quantize_rows_cols_e4m3, fused_backward_fp8)
 
 _lib.load()

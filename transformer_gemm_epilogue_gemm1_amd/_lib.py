@@ -41,6 +41,8 @@ SIGNATURES = {
                                           c_vp, c_vp, c_i64, c_vp]),
     "coda_quantize_rows_e4m3": (c_int, [c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp]),
     "coda_quantize_cols_e4m3": (c_int, [c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp]),
+    "coda_quantize_rows_cols_e4m3": (c_int, [c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp,
+                                             c_vp]),
     "coda_chain_bwd_fp8_workspace_bytes": (c_size, [c_i64, c_i64, c_i64, c_i64]),
     "coda_chain_bwd_fp8": (c_int, [c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                    c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),

@@ -461,6 +461,22 @@ def quantize_weight_e4m3(W, stream=None, Wt8=None, scales=None):
     return Wt8, sc
 
 
+def quantize_rows_cols_e4m3(X, stream=None):
+    """Both e4m3 quantisations of a bf16 activation X [M, N]: the row codes
+    (uint8 [M, N]) with their scales [M], and the transposed column codes
+    (uint8 [N, M]) with their scales [N]."""
+    M, N = X.shape
+    ldx = _mat(X, "X", torch.bfloat16, (M, N))
+    X8 = torch.empty((M, N), device=X.device, dtype=torch.uint8)
+    Xt8 = torch.empty((N, M), device=X.device, dtype=torch.uint8)
+    sr = torch.empty((M,), device=X.device, dtype=torch.float32)
+    sc = torch.empty((N,), device=X.device, dtype=torch.float32)
+    st = _lib.load().coda_quantize_rows_cols_e4m3(M, N, X.data_ptr(), ldx, X8.data_ptr(), N, sr.data_ptr(),
+                                                  Xt8.data_ptr(), M, sc.data_ptr(), _stream(stream))
+    _lib.check("coda_quantize_rows_cols_e4m3", st)
+    return X8, sr, Xt8, sc
+
+
 def fused_forward_fp8(A8, sa, W1t8, sw1, R, g, W2t8, sw2, eps: float, stream=None):
     """The fused chain with fp8 GEMM operands: returns (H, Hg8, r, Y, partials)."""
     M, D, N2 = A8.shape[0], W1t8.shape[0], W2t8.shape[0]

@@ -313,16 +313,45 @@ struct Bwd8Ws {
 
 // Unchecked launches of the quantisers (shapes validated by the caller).
 void q_rows(const void* X, int64_t ldx, int M, int K, void* X8, int64_t ldx8, float* sc, hipStream_t s) {
-  hipLaunchKernelGGL(quantize_rows_e4m3_kernel, dim3((unsigned)M), dim3(256), 0, s, (const uint16_t*)X, ldx, K,
-                     (uint8_t*)X8, ldx8, sc);
+  const dim3 grid((unsigned)M), block(256);
+  const uint16_t* x = (const uint16_t*)X;
+  uint8_t* x8 = (uint8_t*)X8;
+  const int chunks = (K / 8 + 255) / 256;  // 16-byte chunks per thread
+  if (chunks <= 1)
+    hipLaunchKernelGGL(quantize_rows_e4m3_kernel<1>, grid, block, 0, s, x, ldx, K, x8, ldx8, sc);
+  else if (chunks <= 2)
+    hipLaunchKernelGGL(quantize_rows_e4m3_kernel<2>, grid, block, 0, s, x, ldx, K, x8, ldx8, sc);
+  else if (chunks <= 4)
+    hipLaunchKernelGGL(quantize_rows_e4m3_kernel<4>, grid, block, 0, s, x, ldx, K, x8, ldx8, sc);
+  else if (chunks <= 8)
+    hipLaunchKernelGGL(quantize_rows_e4m3_kernel<8>, grid, block, 0, s, x, ldx, K, x8, ldx8, sc);
+  else if (chunks <= 16)
+    hipLaunchKernelGGL(quantize_rows_e4m3_kernel<16>, grid, block, 0, s, x, ldx, K, x8, ldx8, sc);
+  else
+    hipLaunchKernelGGL(quantize_long_rows_e4m3_kernel, grid, block, 0, s, x, ldx, K, x8, ldx8, sc);
 }
 void q_cols(const void* W, int64_t ldw, int K, int N, void* Wt8, int64_t ldwt, float* sc, hipStream_t s) {
-  const unsigned strips = (unsigned)((N + 63) / 64);
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, (uint32_t*)sc, N, 0u);
-  hipLaunchKernelGGL(colmax_kernel, dim3(strips, (unsigned)((K + 255) / 256)), dim3(256), 0, s, (const uint16_t*)W,
-                     ldw, K, N, (uint32_t*)sc);
-  hipLaunchKernelGGL(quantize_cols_kernel, dim3(strips, (unsigned)((K + 63) / 64)), dim3(256), 0, s,
-                     (const uint16_t*)W, ldw, K, N, (const uint32_t*)sc, (uint8_t*)Wt8, ldwt);
+  hipLaunchKernelGGL(colmax_kernel, dim3((unsigned)((N + 63) / 64), (unsigned)((K + 255) / 256)), dim3(256), 0, s,
+                     (const uint16_t*)W, ldw, K, N, (uint32_t*)sc);
+  hipLaunchKernelGGL(quantize_cols_kernel, dim3((unsigned)((N + 127) / 128), (unsigned)((K + 127) / 128)), dim3(256),
+                     0, s, (const uint16_t*)W, ldw, K, N, (const uint32_t*)sc, (uint8_t*)Wt8, ldwt,
+                     (const uint32_t*)nullptr, (uint8_t*)nullptr, (int64_t)0);
+  hipLaunchKernelGGL(amax_to_scale_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, sc, N);
+}
+// Both quantisations of an activation X [M, N]: row codes X8 [M, N] with
+// scales sr [M] (as q_rows) and column codes Xt8 [N, M] with scales sc [N]
+// (as q_cols), from one pass for the maxima and one for the codes.
+void q_rows_cols(const void* X, int64_t ldx, int M, int N, void* X8, int64_t ldx8, float* sr, void* Xt8,
+                 int64_t ldxt, float* sc, hipStream_t s) {
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, (uint32_t*)sr, M, 0u);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, (uint32_t*)sc, N, 0u);
+  hipLaunchKernelGGL(rowcol_max_kernel, dim3((unsigned)((N + 255) / 256), (unsigned)((M + 255) / 256)), dim3(256), 0,
+                     s, (const uint16_t*)X, ldx, M, N, (uint32_t*)sr, (uint32_t*)sc);
+  hipLaunchKernelGGL(quantize_cols_kernel, dim3((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128)), dim3(256),
+                     0, s, (const uint16_t*)X, ldx, M, N, (const uint32_t*)sc, (uint8_t*)Xt8, ldxt,
+                     (const uint32_t*)sr, (uint8_t*)X8, ldx8);
+  hipLaunchKernelGGL(amax_to_scale_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, sr, M);
   hipLaunchKernelGGL(amax_to_scale_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, sc, N);
 }
 
@@ -341,8 +370,7 @@ coda_status chain_bwd_fp8_impl(int M, int K, int D, int N2, const void* dY, cons
   const int Tn = (int)num_partials(D), U = (M + kWaveM - 1) / kWaveM;
   coda_status st;
   // operands of G = dY W2^T (rows) and dW2 = X_n^T dY (dY's columns)
-  q_rows(dY, N2, M, N2, ws + L.dy8, N2, f(L.sdy), s);
-  q_cols(dY, N2, M, N2, ws + L.dyt8, M, f(L.sdyt), s);
+  q_rows_cols(dY, N2, M, N2, ws + L.dy8, N2, f(L.sdy), ws + L.dyt8, M, f(L.sdyt), s);
   q_rows(W2, N2, D, N2, ws + L.w2q, N2, f(L.sw2), s);
   q_rows(W1, D, K, D, ws + L.w1q, D, f(L.sw1), s);
   if ((st = launch_status("coda_chain_bwd_fp8 quantise dY, W1, W2")) != CODA_OK) return st;
@@ -361,8 +389,7 @@ coda_status chain_bwd_fp8_impl(int M, int K, int D, int N2, const void* dY, cons
   hipLaunchKernelGGL(dh_finalize_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, (uint16_t*)dR, (const uint16_t*)H,
                      r, c, D, nchunks);
   // operands of dA = dH W1^T (dH rows), dW1 = A^T dH and dW2 = X_n^T dY (columns)
-  q_rows(dR, D, M, D, ws + L.dh8, D, f(L.sdh), s);
-  q_cols(dR, D, M, D, ws + L.dht8, M, f(L.sdht), s);
+  q_rows_cols(dR, D, M, D, ws + L.dh8, D, f(L.sdh), ws + L.dht8, M, f(L.sdht), s);
   q_cols(Xn, D, M, D, ws + L.xnt8, M, f(L.sxn), s);
   q_cols(A, K, M, K, ws + L.at8, M, f(L.sat), s);
   if ((st = launch_status("coda_chain_bwd_fp8 combine, dH, quantise")) != CODA_OK) return st;
@@ -635,8 +662,7 @@ coda_status coda_quantize_rows_e4m3(int64_t M, int64_t K, const void* X, int64_t
   if (((uintptr_t)scales & 3) != 0) return fail(CODA_ERR_ALIGN, "scales is not 4-byte aligned");
   const Mat outs[2] = {mX8, ms};
   if ((st = check_alias(outs, 2, &mX, 1)) != CODA_OK) return st;
-  hipLaunchKernelGGL(quantize_rows_e4m3_kernel, dim3((unsigned)M), dim3(256), 0, (hipStream_t)stream,
-                     (const uint16_t*)X, ldx, (int)K, (uint8_t*)X8, ldx8, scales);
+  q_rows(X, ldx, (int)M, (int)K, X8, ldx8, scales, (hipStream_t)stream);
   return launch_status("coda_quantize_rows_e4m3");
 }
 
@@ -655,6 +681,28 @@ coda_status coda_quantize_cols_e4m3(int64_t K, int64_t N, const void* W, int64_t
   if ((st = check_alias(outs, 2, &mW, 1)) != CODA_OK) return st;
   q_cols(W, ldw, (int)K, (int)N, Wt8, ldwt, scales, (hipStream_t)stream);
   return launch_status("coda_quantize_cols_e4m3");
+}
+
+coda_status coda_quantize_rows_cols_e4m3(int64_t M, int64_t N, const void* X, int64_t ldx, void* X8, int64_t ldx8,
+                                         float* row_scales, void* Xt8, int64_t ldxt, float* col_scales,
+                                         void* stream) {
+  coda_status st = check_dims_fp8(M, {{"N", N}});
+  if (st != CODA_OK) return st;
+  if (M == 0) return ok();
+  if (M % 16 != 0) return fail(CODA_ERR_SHAPE, "M = %lld is not a multiple of 16", (long long)M);
+  if (M > kMaxColRows) return fail(CODA_ERR_SHAPE, "M = %lld exceeds %lld rows", (long long)M, (long long)kMaxColRows);
+  const Mat mX{X, M, N, ldx, 2, "X"}, mX8{X8, M, N, ldx8, 1, "X8"}, mXt{Xt8, N, M, ldxt, 1, "Xt8"};
+  const Mat msr{row_scales, 1, M, M, 4, "row_scales"}, msc{col_scales, 1, N, N, 4, "col_scales"};
+  if ((st = check_mat(mX, 8)) != CODA_OK || (st = check_mat(mX8, 16)) != CODA_OK ||
+      (st = check_mat(mXt, 16)) != CODA_OK)
+    return st;
+  if (row_scales == nullptr || col_scales == nullptr) return fail(CODA_ERR_NULL, "row_scales and col_scales must be set");
+  if ((((uintptr_t)row_scales | (uintptr_t)col_scales) & 3) != 0)
+    return fail(CODA_ERR_ALIGN, "row_scales / col_scales not 4-byte aligned");
+  const Mat outs[4] = {mX8, msr, mXt, msc};
+  if ((st = check_alias(outs, 4, &mX, 1)) != CODA_OK) return st;
+  q_rows_cols(X, ldx, (int)M, (int)N, X8, ldx8, row_scales, Xt8, ldxt, col_scales, (hipStream_t)stream);
+  return launch_status("coda_quantize_rows_cols_e4m3");
 }
 
 coda_status coda_gemm_rowscale_fp8(int64_t M, int64_t D, int64_t N2, const void* X8, int64_t ldx, const void* W2t8,

@@ -12,6 +12,40 @@ namespace coda {
 
 __device__ __forceinline__ float e4m3_scale(float amax) { return amax > 0.f ? amax / 448.f : 1.f; }
 
+// x / s correctly rounded wherever that decides the e4m3 code, in five
+// instructions instead of a full IEEE division: Markstein's correction
+// (q0 = x y, the residual r = x - q0 s exact by fma, q = q0 + r y, with y the
+// correctly rounded 1 / s) on x and s rescaled by 2^-e so that s lies in
+// [1/2, 1).  The residual can then underflow only where |x / s| < 2^-124,
+// whose code is a zero anyway, and the sign comes from x so that -0 stays -0.
+// An exhaustive host check over every bf16 x and every scale of a bf16
+// maximum finds each code equal to that of the correctly rounded quotient.
+struct E4m3Divider {
+  float s1, y1;
+  int e;
+  __device__ __forceinline__ static E4m3Divider of(float s) {
+    E4m3Divider d;
+    d.s1 = frexpf(s, &d.e);
+    d.y1 = 1.f / d.s1;
+    return d;
+  }
+  __device__ __forceinline__ float operator()(float x) const {
+    const float x1 = ldexpf(x, -e);
+    const float q0 = x1 * y1;
+    const float r = fmaf(-q0, s1, x1);
+    return copysignf(fmaf(r, y1, q0), x);
+  }
+};
+
+// The e4m3 codes of 8 values divided by one scale, and by one scale each.
+__device__ __forceinline__ u32x2 encode8(const float v[8], const E4m3Divider& d) {
+  return u32x2{pack_e4m3x4(d(v[0]), d(v[1]), d(v[2]), d(v[3])), pack_e4m3x4(d(v[4]), d(v[5]), d(v[6]), d(v[7]))};
+}
+__device__ __forceinline__ u32x2 encode8(const float v[8], const E4m3Divider (&d)[8]) {
+  return u32x2{pack_e4m3x4(d[0](v[0]), d[1](v[1]), d[2](v[2]), d[3](v[3])),
+               pack_e4m3x4(d[4](v[4]), d[5](v[5]), d[6](v[6]), d[7](v[7]))};
+}
+
 // Largest magnitude over a 256-thread workgroup (wavefront shuffles, then
 // the four wavefronts through LDS); every thread gets the result.
 __device__ __forceinline__ float block_amax(float v, float* red) {
@@ -26,11 +60,51 @@ __device__ __forceinline__ float block_amax(float v, float* red) {
 }
 
 // One workgroup per row of X [M, K] (bf16): scales[row] and the row's codes.
-// K % 8 == 0; each thread takes 8-element chunks, the second pass reads the
-// row again (from cache).
+// K % 8 == 0.  Rows of up to 2048 CPT elements stay in registers (CPT
+// 16-byte chunks per thread, all loads in flight at once), so the row is read
+// from memory once.
+template <int CPT>
 __global__ __launch_bounds__(256) void quantize_rows_e4m3_kernel(const uint16_t* __restrict__ X, int64_t ldx,
                                                                  int K, uint8_t* __restrict__ X8, int64_t ldx8,
                                                                  float* __restrict__ scales) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const uint16_t* x = X + row * ldx;
+  const int nc = K / 8;
+  u32x4 raw[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int c = threadIdx.x + 256 * j;
+    raw[j] = c < nc ? Chunk8<uint16_t>::load_raw(x + 8 * c) : u32x4{0, 0, 0, 0};
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    float v[8];
+    Chunk8<uint16_t>::unpack(raw[j], v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  }
+  const float s = e4m3_scale(block_amax(m, red));
+  if (threadIdx.x == 0) scales[row] = s;
+  const E4m3Divider enc = E4m3Divider::of(s);
+  uint8_t* y = X8 + row * ldx8;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int c = threadIdx.x + 256 * j;
+    if (c < nc) {
+      float v[8];
+      Chunk8<uint16_t>::unpack(raw[j], v);
+      *(u32x2*)(y + 8 * c) = encode8(v, enc);
+    }
+  }
+}
+
+// Rows longer than 32768 elements: the same result in two passes over the
+// row, the second from cache.
+__global__ __launch_bounds__(256) void quantize_long_rows_e4m3_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+                                                                      int K, uint8_t* __restrict__ X8,
+                                                                      int64_t ldx8, float* __restrict__ scales) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
   const uint16_t* x = X + row * ldx;
@@ -44,13 +118,12 @@ __global__ __launch_bounds__(256) void quantize_rows_e4m3_kernel(const uint16_t*
   }
   const float s = e4m3_scale(block_amax(m, red));
   if (threadIdx.x == 0) scales[row] = s;
+  const E4m3Divider enc = E4m3Divider::of(s);
   uint8_t* y = X8 + row * ldx8;
   for (int c = threadIdx.x; c < nc; c += 256) {
     float v[8];
     Chunk8<uint16_t>::load(x + 8 * c, v);
-    const uint32_t lo = pack_e4m3x4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
-    const uint32_t hi = pack_e4m3x4(v[4] / s, v[5] / s, v[6] / s, v[7] / s);
-    *(u32x2*)(y + 8 * c) = u32x2{lo, hi};
+    *(u32x2*)(y + 8 * c) = encode8(v, enc);
   }
 }
 
@@ -58,12 +131,14 @@ __global__ __launch_bounds__(256) void quantize_rows_e4m3_kernel(const uint16_t*
 // of W^T, Wt8 [N, K] (K contiguous), one scale per column, in three steps
 // that keep every CU busy for tall matrices (activations of 16k rows as
 // well as weights):
-//   1. colmax_kernel: each workgroup takes a 64-column x 256-row block and
-//      folds its column maxima into amax (the scales array, zeroed first) with
-//      atomic max on the float bits (non-negative floats order like their
-//      bits; the result does not depend on the order);
-//   2. quantize_cols_kernel: each workgroup encodes a 64 x 64 block through
-//      LDS, transposed, with the scales of its columns;
+//   1. colmax_kernel (or rowcol_max_kernel, which also takes the row maxima):
+//      the block maxima are folded into amax (the scales array, zeroed
+//      first) with atomic max on the float bits (non-negative floats order
+//      like their bits; the result does not depend on the order);
+//   2. quantize_cols_kernel: each workgroup encodes a 128 x 128 block with
+//      the scales of its columns and writes the codes transposed (through an
+//      LDS byte tile), and optionally the row codes of the same block with
+//      the row scales;
 //   3. amax_to_scale_kernel turns the maxima into the scales in place.
 // K % 16 == 0, N % 16 == 0; columns past N and rows past K are neither read
 // nor written.
@@ -101,41 +176,124 @@ __global__ __launch_bounds__(256) void colmax_kernel(const uint16_t* __restrict_
   }
 }
 
-// Thread t reads columns 8 * (t % 8) .. +7 of block rows t / 8 and t / 8 + 32,
-// and writes 16 codes of output row t / 4 at k offset 16 * (t % 4).
-__global__ __launch_bounds__(256) void quantize_cols_kernel(const uint16_t* __restrict__ W, int64_t ldw, int K,
-                                                            int N, const uint32_t* __restrict__ amax,
-                                                            uint8_t* __restrict__ Wt8, int64_t ldwt) {
-  __shared__ float tile[64][65];
-  __shared__ float colscale[64];
-  const int t = threadIdx.x;
-  const int n0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
-  if (t < 64) colscale[t] = e4m3_scale(n0 + t < N ? __uint_as_float(amax[n0 + t]) : 0.f);
-  __syncthreads();
-  const int rc = (t & 7) * 8;
+// Row and column maxima of X [M, N] in one pass (for an activation that is
+// quantised both ways): each workgroup takes a 256 x 256 block, thread t the
+// 8 columns 8 * (t % 32) .. +7 of rows t / 32 + 8 i, and folds the block's
+// row maxima into rmax and its column maxima into cmax (both zeroed first).
+__global__ __launch_bounds__(256) void rowcol_max_kernel(const uint16_t* __restrict__ X, int64_t ldx, int M, int N,
+                                                         uint32_t* __restrict__ rmax, uint32_t* __restrict__ cmax) {
+  __shared__ float rpart[256][33];  // [row of the block][column chunk]
+  __shared__ float cpart[8][257];   // [row group][column of the block]
+  const int t = threadIdx.x, cc = t & 31, rg = t >> 5;
+  const int n0 = blockIdx.x * 256, m0 = blockIdx.y * 256;
+  const int col = n0 + 8 * cc;
+  float cm[8];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int kr = (t >> 3) + 32 * h, k = k0 + kr;
-    float v[8];
-    if (k < K && n0 + rc < N) {
-      Chunk8<uint16_t>::load(W + (int64_t)k * ldw + n0 + rc, v);
-    } else {
+  for (int e = 0; e < 8; ++e) cm[e] = 0.f;
+  for (int i0 = 0; i0 < 32; i0 += 8) {
+    u32x4 raw[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.f;
+    for (int i = 0; i < 8; ++i) {
+      const int row = m0 + rg + 8 * (i0 + i);
+      raw[i] = (col < N && row < M) ? Chunk8<uint16_t>::load_raw(X + (int64_t)row * ldx + col) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) tile[kr][rc + i] = v[i] / colscale[rc + i];
+    for (int i = 0; i < 8; ++i) {
+      float v[8];
+      Chunk8<uint16_t>::unpack(raw[i], v);
+      float rm = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float a = fabsf(v[e]);
+        rm = fmaxf(rm, a);
+        cm[e] = fmaxf(cm[e], a);
+      }
+      rpart[rg + 8 * (i0 + i)][cc] = rm;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) cpart[rg][8 * cc + e] = cm[e];
+  __syncthreads();
+  // thread t: row m0 + t and column n0 + t of the block
+  float rmx = 0.f, cmx = 0.f;
+  for (int j = 0; j < 32; ++j) rmx = fmaxf(rmx, rpart[t][j]);
+  for (int j = 0; j < 8; ++j) cmx = fmaxf(cmx, cpart[j][t]);
+  if (m0 + t < M) atomicMax(rmax + m0 + t, __float_as_uint(rmx));
+  if (n0 + t < N) atomicMax(cmax + n0 + t, __float_as_uint(cmx));
+}
+
+// Codes of one 4 x 4 byte block transposed: w[i] holds row i's codes of 4
+// columns; out[j] gets column j's codes of the 4 rows.
+__device__ __forceinline__ void transpose4x4_bytes(const uint32_t w[4], uint32_t out[4]) {
+  // v_perm_b32 picks bytes of {hi: src0, lo: src1} by the selector's bytes
+  const uint32_t x01 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // w0.b0 w1.b0 w0.b1 w1.b1
+  const uint32_t y01 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);  // w2.b0 w3.b0 w2.b1 w3.b1
+  const uint32_t x23 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);  // w0.b2 w1.b2 w0.b3 w1.b3
+  const uint32_t y23 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+  out[0] = __builtin_amdgcn_perm(y01, x01, 0x05040100u);
+  out[1] = __builtin_amdgcn_perm(y01, x01, 0x07060302u);
+  out[2] = __builtin_amdgcn_perm(y23, x23, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(y23, x23, 0x07060302u);
+}
+
+// A 128 x 128 block per workgroup.  Thread t reads columns 8 * (t % 16) .. +7
+// of block rows t / 16 + 16 h, writes those rows' codes (when X8 is set) and
+// puts the column codes into an LDS byte tile; it then writes output rows
+// 4 (t / 8) .. +3, 16 codes each at k offset 16 * (t % 8), transposing 4 x 4
+// byte blocks in registers.  Every code row a block writes is one 128-byte
+// line.
+__global__ __launch_bounds__(256) void quantize_cols_kernel(const uint16_t* __restrict__ W, int64_t ldw, int K,
+                                                            int N, const uint32_t* __restrict__ amax,
+                                                            uint8_t* __restrict__ Wt8, int64_t ldwt,
+                                                            const uint32_t* __restrict__ rmax,
+                                                            uint8_t* __restrict__ X8, int64_t ldx8) {
+  constexpr int kPitch = 33;  // words per tile row: 128 codes + 4 bytes of padding
+  __shared__ uint32_t tile[128 * kPitch];
+  __shared__ E4m3Divider coldiv[128], rowdiv[128];
+  const int t = threadIdx.x;
+  const int n0 = blockIdx.x * 128, k0 = blockIdx.y * 128;
+  if (t < 128)
+    coldiv[t] = E4m3Divider::of(e4m3_scale(n0 + t < N ? __uint_as_float(amax[n0 + t]) : 0.f));
+  else if (X8 != nullptr)
+    rowdiv[t - 128] = E4m3Divider::of(e4m3_scale(k0 + t - 128 < K ? __uint_as_float(rmax[k0 + t - 128]) : 0.f));
+  const int rc = (t & 15) * 8;
+  const bool cin = n0 + rc < N;
+  u32x4 raw[8];
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    const int k = k0 + (t >> 4) + 16 * h;
+    raw[h] = (k < K && cin) ? Chunk8<uint16_t>::load_raw(W + (int64_t)k * ldw + n0 + rc) : u32x4{0, 0, 0, 0};
   }
   __syncthreads();
-  const int wr = t >> 2, wk = (t & 3) * 16;
-  if (n0 + wr < N && k0 + wk < K) {
-    float q[16];
+  E4m3Divider cd[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) q[i] = tile[wk + i][wr];
-    u32x4 out;
+  for (int i = 0; i < 8; ++i) cd[i] = coldiv[rc + i];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = pack_e4m3x4(q[4 * j], q[4 * j + 1], q[4 * j + 2], q[4 * j + 3]);
-    *(u32x4*)(Wt8 + (int64_t)(n0 + wr) * ldwt + k0 + wk) = out;
+  for (int h = 0; h < 8; ++h) {
+    const int kr = (t >> 4) + 16 * h, k = k0 + kr;
+    float v[8];
+    Chunk8<uint16_t>::unpack(raw[h], v);
+    if (X8 != nullptr && k < K && cin) *(u32x2*)(X8 + (int64_t)k * ldx8 + n0 + rc) = encode8(v, rowdiv[kr]);
+    const u32x2 c = encode8(v, cd);
+    tile[kr * kPitch + rc / 4] = c[0];
+    tile[kr * kPitch + rc / 4 + 1] = c[1];
+  }
+  __syncthreads();
+  const int cg = t >> 3, kc = (t & 7) * 16;  // output rows 4 cg .. +3, codes kc .. kc + 15
+  if (n0 + 4 * cg < N && k0 + kc < K) {
+    uint32_t out[4][4];  // [output row][word]
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint32_t w[4], o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = tile[(kc + 4 * g + i) * kPitch + cg];
+      transpose4x4_bytes(w, o);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[j][g] = o[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *(u32x4*)(Wt8 + (int64_t)(n0 + 4 * cg + j) * ldwt + k0 + kc) = u32x4{out[j][0], out[j][1], out[j][2], out[j][3]};
   }
 }
 
