@@ -4,11 +4,13 @@
  * the e4m3 code of
  *     x1 = x 2^-e, s1 = s 2^-e in [1/2, 1), y1 = RN(1 / s1),
  *     q0 = RN(x1 y1), r = fma(-q0, s1, x1), q = copysign(fma(r, y1, q0), x)
- * equals the e4m3 code of the correctly rounded quotient RN(x / s).  Codes
- * are round-to-nearest-even after clamping to +-448, the sign bit kept for
+ * equals the e4m3 code of the correctly rounded quotient RN(x / s), and q
+ * itself equals RN(x / s) wherever |x / s| >= 2^-100 (below, the residual may
+ * underflow; such quotients have a zero code).  Codes are
+ * round-to-nearest-even after clamping to +-448, the sign bit kept for
  * zeros.  Usage: e4m3_division_check PART NPARTS (maxima a with
  * (bits(a) - 1) % NPARTS == PART).  Prints the counts; exit status 1 on any
- * differing code. */
+ * difference. */
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -57,8 +59,9 @@ int main(int argc, char** argv) {
       if (!(fabsf(x) <= a)) continue;
       const float x1 = ldexpf(x, -e), q0 = x1 * y1, r = fmaf(-q0, s1, x1);
       const float q = copysignf(fmaf(r, y1, q0), x);
+      const float ref = x / s;
       ++pairs;
-      if (e4m3_code(q) != e4m3_code(x / s)) {
+      if (e4m3_code(q) != e4m3_code(ref) || (fabsf(ref) >= 0x1p-100f && memcmp(&q, &ref, 4) != 0)) {
         if (bad < 5) printf("differs: a=%a x=%a\n", a, x);
         ++bad;
       }

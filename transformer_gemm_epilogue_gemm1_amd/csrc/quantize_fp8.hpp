@@ -16,10 +16,11 @@ __device__ __forceinline__ float e4m3_scale(float amax) { return amax > 0.f ? am
 // instructions instead of a full IEEE division: Markstein's correction
 // (q0 = x y, the residual r = x - q0 s exact by fma, q = q0 + r y, with y the
 // correctly rounded 1 / s) on x and s rescaled by 2^-e so that s lies in
-// [1/2, 1).  The residual can then underflow only where |x / s| < 2^-124,
+// [1/2, 1).  The residual can then underflow only where |x / s| < 2^-100,
 // whose code is a zero anyway, and the sign comes from x so that -0 stays -0.
 // An exhaustive host check over every bf16 x and every scale of a bf16
-// maximum finds each code equal to that of the correctly rounded quotient.
+// maximum finds the quotient correctly rounded wherever |x / s| >= 2^-100
+// and each code equal to that of the correctly rounded quotient.
 struct E4m3Divider {
   float s1, y1;
   int e;
