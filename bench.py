@@ -111,7 +111,10 @@ def cpu_baseline(wl, x, budget_s: float):
 
     import oracle
 
-    cores = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+    pools = threadpoolctl.threadpool_info()
+    cores = max((i.get("num_threads", 1) for i in pools), default=1)
+    blas = ", ".join(sorted({f"{i.get('internal_api', '?')} ({i.get('num_threads', '?')} threads)" for i in pools
+                             if i.get("user_api") == "blas"})) or "unknown"
     row_flops = 2.0 * wl.K * wl.D + 2.0 * wl.D * wl.N2
     probe = min(wl.M, 256)
     t0 = time.perf_counter()
@@ -123,7 +126,8 @@ def cpu_baseline(wl, x, budget_s: float):
     oracle.forward(x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps, rows=rows)
     dt = time.perf_counter() - t0
     out = {"value": round(n * row_flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores),
-           "kind": "oracle", "seconds": round(dt, 3),
+           "kind": "oracle", "seconds": round(dt, 3), "blas": blas,
+           "affinity_cores": len(os.sched_getaffinity(0)),
            "sample": f"rows 0..{n - 1} of the {wl.M}-row {wl.name} forward chain (rows are independent), "
                      f"fp64 numpy, {dt:.2f} s, including the oracle's own fp64 weight conversion"}
     # the backward on a row sample (the weight gradients are sums over rows,
@@ -862,6 +866,7 @@ def main():
         "step_ms_percentiles": pct,
         "wall_s_timed_region": round(wall_s, 3),
         "device": {"name": torch.cuda.get_device_name(dev),
+                   "arch": getattr(torch.cuda.get_device_properties(dev), "gcnArchName", "unknown"),
                    "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count},
     }
 
