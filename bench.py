@@ -754,7 +754,7 @@ def bench_backward(args, up, stream):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: libcoda runs on one GPU; --gpus {args.gpus} is not supported "
               "(the chain is row-independent and would shard over M with no exchange in the forward)",
               file=sys.stderr)
         sys.exit(2)
