@@ -74,6 +74,8 @@ def parse():
                          "size that calibrates HBM byte counters in a profiler run)")
     ap.add_argument("--no-torch-chain", action="store_true",
                     help="skip timing the same chain in plain PyTorch (vendor GEMMs + torch elementwise ops)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip measuring the sustained matrix-core throughput (products only, no memory)")
     return ap.parse_args()
 
 
@@ -485,6 +487,51 @@ def bench_rope(args, up, stream):
     return out
 
 
+def mfma_ceiling(kind: str, stream, reps: int = 3):
+    """Sustained matrix-core throughput (TFLOP/s) of a kernel that does
+    nothing but the GEMM main loop's products on register operands that
+    change between bursts (libcoda_ceiling.so, csrc/mfma_ceiling.hip),
+    launched like the GEMMs: 2048 workgroups of 512 threads.  Median of
+    `reps` launches of about 0.25 s each after one warm-up launch.  This is
+    what the chip sustains with its clock management under a full matrix
+    load; the nominal peak assumes the top clock throughout."""
+    import ctypes
+
+    import torch
+
+    from transformer_gemm_epilogue_gemm1_amd.build import CEILING_LIB_PATH
+
+    if not os.path.exists(CEILING_LIB_PATH):
+        raise RuntimeError(f"{CEILING_LIB_PATH} is not built: run __graft_entry__.build()")
+    lib = ctypes.CDLL(CEILING_LIB_PATH)
+    fn = getattr(lib, f"coda_ceiling_{kind}")
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_void_p]
+    grid = 2048
+    iters, flops_per_wave_iter = (40000, 524288.0) if kind == "bf16" else (25000, 2097152.0)
+    out = torch.empty((grid * 512,), device="cuda", dtype=torch.float32)
+    flops = grid * 8 * iters * flops_per_wave_iter
+
+    def launch(seed):
+        rc = fn(out.data_ptr(), out.numel(), grid, iters, seed, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"coda_ceiling_{kind} failed: {rc}")
+
+    launch(1)
+    ms = []
+    for i in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        launch(2 + i)
+        b.record(stream)
+        b.synchronize()
+        ms.append(a.elapsed_time(b))
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError(f"coda_ceiling_{kind}: non-finite sums")
+    return round(flops / (float(np.median(ms)) * 1e-3) / 1e12, 1)
+
+
 def bench_fp8(args, stream):
     """The fused chain with fp8 (OCP e4m3) GEMM operands at the 7B shape:
     the weights quantised once per output channel (coda_quantize_cols_e4m3),
@@ -545,6 +592,10 @@ def bench_fp8(args, stream):
            "chain_on_quantised_a_tflops": round(wl.fwd_flops / (chain_ms * 1e-3) / 1e12, 2),
            "coda_gemm_rowscale_fp8_ms": round(g2_ms, 4), "coda_gemm_rowscale_fp8_tflops": round(g2_tf, 2),
            "coda_gemm_rowscale_fp8_frac": round(g2_tf / PEAK_FP8_TFLOPS, 4)}
+    if not args.no_ceiling:
+        ceil8 = mfma_ceiling("fp8", stream)
+        out["sustained_mfma_tflops"] = ceil8
+        out["coda_gemm_rowscale_fp8_frac_of_sustained"] = round(g2_tf / ceil8, 4)
     pp = power_probe(step, min(args.power_probe_s, 2.0))
     if pp is not None:
         pp["fp8_peak_at_clock_tflops"] = round(256 * 8192 * pp["gfx_clock_mhz"] * 1e6 / 1e12, 1)
@@ -869,6 +920,11 @@ def main():
                    "arch": getattr(torch.cuda.get_device_properties(dev), "gcnArchName", "unknown"),
                    "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count},
     }
+
+    if not args.no_ceiling and wl.dtype == "bf16":
+        ceil = mfma_ceiling("bf16", stream)
+        out["roofline"]["sustained_mfma_tflops"] = ceil
+        out["roofline"]["frac_of_sustained"] = round(g2_tflops / ceil, 4)
 
     pp = power_probe(step, args.power_probe_s)
     if pp is not None:

@@ -538,3 +538,23 @@ def test_chain_bwd_fp8_validation(lib):
     assert call(ws_bytes=need - 1) == WS
     assert call(ws=WS_ + 8) == ALIGN
     assert call(dW2=W2_ + 64) == ALIAS
+
+
+def test_ceiling_library_exports_and_rejects():
+    """The benchmark's matrix-core throughput library exports its two calls
+    and turns bad arguments into -1 before any launch."""
+    import ctypes
+
+    from transformer_gemm_epilogue_gemm1_amd.build import CEILING_LIB_PATH
+
+    lib = ctypes.CDLL(CEILING_LIB_PATH)
+    for kind in ("bf16", "fp8"):
+        fn = getattr(lib, f"coda_ceiling_{kind}")
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
+                       ctypes.c_void_p]
+        fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call below is rejected first
+        assert fn(None, 1 << 20, 2048, 1, 0, None) == -1
+        assert fn(fake, 2048 * 512 - 1, 2048, 1, 0, None) == -1
+        assert fn(fake, 2048 * 512, 0, 1, 0, None) == -1
+        assert fn(fake, 2048 * 512, 2048, 0, 0, None) == -1

@@ -1,4 +1,5 @@
-"""Builds libcoda.so (HIP, gfx950 only) next to this file with hipcc."""
+"""Builds libcoda.so (HIP, gfx950 only) next to this file with hipcc, and
+libcoda_ceiling.so, the benchmark's matrix-core throughput kernel."""
 from __future__ import annotations
 
 import os
@@ -9,6 +10,8 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libcoda.so")
 SOURCES = ["coda.hip"]
+CEILING_LIB_PATH = os.path.join(PKG_DIR, "libcoda_ceiling.so")
+CEILING_SOURCES = ["mfma_ceiling.hip"]
 HEADERS = ["gemm.hpp", "gemm_fp8.hpp", "epilogues.hpp", "epilogues_fp8.hpp", "epilogues_rope.hpp",
            "epilogues_ce.hpp", "quantize_fp8.hpp", "rowops.hpp", "tile_map.hpp"]
 
@@ -21,21 +24,26 @@ def hipcc() -> str:
     return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libcoda.so (always recompiles)."""
-    fd, tmp = tempfile.mkstemp(prefix="libcoda.", suffix=".so.tmp", dir=PKG_DIR)
+def _compile(sources, out_path, verbose):
+    fd, tmp = tempfile.mkstemp(prefix=os.path.basename(out_path)[:-len(".so")] + ".", suffix=".so.tmp", dir=PKG_DIR)
     os.close(fd)
-    cmd = [hipcc()] + HIP_FLAGS + ["-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+    cmd = [hipcc()] + HIP_FLAGS + ["-o", tmp] + [os.path.join(CSRC, s) for s in sources]
     try:
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{res.stderr}")
         if verbose:
             print(" ".join(cmd))
-        os.replace(tmp, LIB_PATH)
+        os.replace(tmp, out_path)
     finally:
         if os.path.exists(tmp):
             os.unlink(tmp)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source: libcoda.so and libcoda_ceiling.so (always recompiles)."""
+    _compile(SOURCES, LIB_PATH, verbose)
+    _compile(CEILING_SOURCES, CEILING_LIB_PATH, verbose)
     return LIB_PATH
 
 
