@@ -200,6 +200,38 @@ def _smi_sample():
     return (pw, sum(clks) / len(clks)) if clks else None
 
 
+def _smi_market_name():
+    """The device's marketing name from amd-smi's static ASIC data, or None."""
+    import shutil
+    import subprocess
+
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    try:
+        res = subprocess.run([exe, "static", "--asic", "--json"], capture_output=True, text=True, timeout=10)
+        d = json.loads(res.stdout)
+    except Exception:
+        return None
+
+    def find(o):
+        if isinstance(o, dict):
+            for k, v in o.items():
+                if k == "market_name" and isinstance(v, str):
+                    return v
+                r = find(v)
+                if r is not None:
+                    return r
+        elif isinstance(o, list):
+            for v in o:
+                r = find(v)
+                if r is not None:
+                    return r
+        return None
+
+    return find(d)
+
+
 def power_probe(fn, seconds):
     """Runs fn() back to back for `seconds` while a thread samples amd-smi;
     returns median socket power and gfx clock over the samples taken after
@@ -918,7 +950,8 @@ def main():
         "wall_s_timed_region": round(wall_s, 3),
         "device": {"name": torch.cuda.get_device_name(dev),
                    "arch": getattr(torch.cuda.get_device_properties(dev), "gcnArchName", "unknown"),
-                   "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count},
+                   "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count,
+                   "market_name": _smi_market_name()},
     }
 
     if not args.no_ceiling and wl.dtype == "bf16":
