@@ -243,8 +243,8 @@ struct Mma<float> {
   }
 };
 
-// Workgroup barriers of the pipeline.  stage_barrier waits until at most two
-// k-tiles of this wavefront's direct loads (kDmaSlots per operand each) are
+// Workgroup barriers of the pipeline.  stage_barrier waits until at most one
+// k-tile of this wavefront's direct loads (kDmaSlots per operand each) is
 // still in flight, then meets the other wavefronts: after it, every
 // wavefront's loads of all older k-tiles have landed.  LDS reads may stay in
 // flight across it (their stage is not overwritten before the step that
@@ -254,9 +254,9 @@ struct Mma<float> {
 // drain_barrier waits for everything.
 constexpr int kLoadsPerTile = 2 * kDmaSlots;  // direct loads per wavefront per k-tile
 __device__ __forceinline__ void stage_barrier() {
-  static_assert(2 * kLoadsPerTile == 8, "the vmcnt literal assumes two k-tiles of 2 x kDmaSlots loads");
+  static_assert(kLoadsPerTile == 4, "the vmcnt literal assumes one k-tile of 2 x kDmaSlots loads");
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 __device__ __forceinline__ void drain_barrier() {
@@ -303,8 +303,8 @@ struct Frags {
 //   step for the weight-gradient products), issue the direct loads of tile
 //   kt + kStages - 1 into stage (S - 1) mod kStages, which held tile kt - 1
 //   (read in step kt - 2, used before the barrier of step kt - 1);
-//   stage_barrier: at most tiles kt + 3 and kt + 4 are still in flight, so
-//   tile kt + 2, which the next step reads, has landed everywhere.
+//   stage_barrier: at most tile kt + 3 is still in flight, so tile kt + 2,
+//   which the next step reads, has landed everywhere.
 // The scheduling fences pin this order (left alone, the scheduler sinks the
 // reads behind the products).  Tiles past the end of K load as zeros; their
 // fragments are read but never multiplied.
@@ -362,13 +362,12 @@ __device__ __forceinline__ void kstep(char* const (&st)[kStages], const Dma<T, A
 template <typename T, bool A_KC, bool B_KC, class Epi>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(
     GemmArgs g, typename Epi::Params ep) {
-  static_assert(kStages == 5, "the stage arrays and the unrolled steps below assume five stages");
+  static_assert(kStages == 4, "the stage arrays and the unrolled steps below assume four stages");
   __shared__ __attribute__((aligned(1024))) char st0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char st1[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char st2[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char st3[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char st4[kStageBytes];
-  char* const st[kStages] = {st0, st1, st2, st3, st4};
+  char* const st[kStages] = {st0, st1, st2, st3};
   constexpr int KTE = kKTBytes / (int)sizeof(T);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -396,8 +395,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     da.issue(st[t], t, g.K, wave);
     db.issue(st[t] + kOperandBytes, t, g.K, wave);
   }
-  static_assert((kStages - 3) * kLoadsPerTile == 8, "the prologue vmcnt literal assumes kStages - 3 tiles in flight");
-  asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  static_assert((kStages - 3) * kLoadsPerTile == 4, "the prologue vmcnt literal assumes kStages - 3 tiles in flight");
+  asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
   Frags cur;
 #pragma unroll
   for (int mt = 0; mt < kFragM; ++mt) cur.a[mt] = ra.read(st[0], mt);
@@ -409,14 +408,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     kstep<T, A_KC, B_KC, 1>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave);
     kstep<T, A_KC, B_KC, 2>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave);
     kstep<T, A_KC, B_KC, 3>(st, da, db, ra, rb, acc, cur, kt + 3, g.K, wave);
-    kstep<T, A_KC, B_KC, 4>(st, da, db, ra, rb, acc, cur, kt + 4, g.K, wave);
   }
   // ragged end: the remaining nk - kt < kStages tiles start again at stage 0
   const int rem = nk - kt;
   if (rem > 0) kstep<T, A_KC, B_KC, 0>(st, da, db, ra, rb, acc, cur, kt, g.K, wave);
   if (rem > 1) kstep<T, A_KC, B_KC, 1>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave);
   if (rem > 2) kstep<T, A_KC, B_KC, 2>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave);
-  if (rem > 3) kstep<T, A_KC, B_KC, 3>(st, da, db, ra, rb, acc, cur, kt + 3, g.K, wave);
   drain_barrier();  // no direct load may land in the LDS the epilogue reuses
 
   // ---- epilogue ----

@@ -4,7 +4,7 @@
 //   (A[M, K] row-major, B stored [N, K]), fp32 accumulation.
 //
 // The loop is the bf16 one (gemm.hpp) with fp8 fragments: the same 64-byte
-// k-tiles (64 elements), direct HBM->LDS loads into the same five stages, the
+// k-tiles (64 elements), direct HBM->LDS loads into the same four stages, the
 // same barrier, tile order and epilogue interface.  What differs: a
 // wavefront's 128 x 64 sub-tile is 4 x 2 products v_mfma_f32_32x32x64_f8f6f4
 // (16 accumulators per lane each, 128 in all), each k-tile is one product per
@@ -89,13 +89,12 @@ __device__ __forceinline__ void kstep8(char* const (&st)[kStages], const Dma<uin
 template <class Epi>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_fp8_kernel(
     GemmArgs g, typename Epi::Params ep) {
-  static_assert(kStages == 5, "the stage arrays and the unrolled steps below assume five stages");
+  static_assert(kStages == 4, "the stage arrays and the unrolled steps below assume four stages");
   __shared__ __attribute__((aligned(1024))) char st0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char st1[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char st2[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char st3[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char st4[kStageBytes];
-  char* const st[kStages] = {st0, st1, st2, st3, st4};
+  char* const st[kStages] = {st0, st1, st2, st3};
   constexpr int KTE = kKTBytes;  // fp8 elements per k-tile
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -122,8 +121,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     da.issue(st[t], t, g.K, wave);
     db.issue(st[t] + kOperandBytes, t, g.K, wave);
   }
-  static_assert((kStages - 3) * kLoadsPerTile == 8, "the prologue vmcnt literal assumes kStages - 3 tiles in flight");
-  asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  static_assert((kStages - 3) * kLoadsPerTile == 4, "the prologue vmcnt literal assumes kStages - 3 tiles in flight");
+  asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
   Frags8 cur;
 #pragma unroll
   for (int mt = 0; mt < kFrag8M; ++mt) cur.a[mt] = ra.read(st[0], mt);
@@ -135,13 +134,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     kstep8<1>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave);
     kstep8<2>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave);
     kstep8<3>(st, da, db, ra, rb, acc, cur, kt + 3, g.K, wave);
-    kstep8<4>(st, da, db, ra, rb, acc, cur, kt + 4, g.K, wave);
   }
   const int rem = nk - kt;
   if (rem > 0) kstep8<0>(st, da, db, ra, rb, acc, cur, kt, g.K, wave);
   if (rem > 1) kstep8<1>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave);
   if (rem > 2) kstep8<2>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave);
-  if (rem > 3) kstep8<3>(st, da, db, ra, rb, acc, cur, kt + 3, g.K, wave);
   drain_barrier();  // no direct load may land in the LDS the epilogue reuses
 
   // ---- epilogue: slab s = rows 16 s .. 16 s + 15 of the wavefront's 128 =
