@@ -3,9 +3,12 @@
 
 One step = one pass of the fused forward chain over one batch of synthetic
 LLaMA-shaped input already resident in HBM:
-    coda_gemm_res_prms  (H = A W1 + R, Hg = H g, partial sums of squares)
-    coda_rms_combine    (r = 1/sqrt(mean(H^2) + eps))
-    coda_gemm_rowscale  (Y = diag(r) Hg W2)
+    coda_gemm_res_prms_packed  (H = A W1 + R, Hg = H g stored tile-packed,
+                                partial sums of squares)
+    coda_rms_combine           (r = 1/sqrt(mean(H^2) + eps))
+    coda_gemm_rowscale_packed  (Y = diag(r) Hg W2)
+(the same chain with Hg row-major, coda_gemm_res_prms + coda_gemm_rowscale,
+is timed beside it).
 Default workload: 7B-style hidden size, M = 16384 tokens, K = D = 4096,
 N2 = 28672 (gate||up of F = 14336), bf16 storage, fp32 accumulation.
 
@@ -290,23 +293,23 @@ def bench_forward_shape(wl, stream, steps, warmup, seed):
     W1, W2 = randn(K, D, scale=K ** -0.5), randn(D, N2, scale=D ** -0.5)
     g = randn(D, scale=0.1, shift=1.0)
     H = torch.empty((M, D), device=dev, dtype=torch.bfloat16)
-    Hg = torch.empty_like(H)
+    Hgp = coda.packed_empty(M, D, dev)
     P = torch.empty((coda.coda_prms_num_partials(torch.bfloat16, D), M), device=dev, dtype=torch.float32)
     r = torch.empty((M,), device=dev, dtype=torch.float32)
     Y = torch.empty((M, N2), device=dev, dtype=torch.bfloat16)
 
-    def step():
-        coda.coda_gemm_res_prms(A, W1, R, g, H, Hg, P, stream)
+    def step():  # the headline's chain: Hg tile-packed between the GEMMs
+        coda.coda_gemm_res_prms_packed(A, W1, R, g, H, Hgp, P, stream)
         coda.coda_rms_combine(P, r, D, wl.eps, stream)
-        coda.coda_gemm_rowscale(Hg, W2, r, Y, stream)
+        coda.coda_gemm_rowscale_packed(Hgp, W2, r, Y, stream)
 
     ms = time_ms(step, stream, steps, warmup)
-    g2_ms = time_ms(lambda: coda.coda_gemm_rowscale(Hg, W2, r, Y, stream), stream, steps, warmup)
+    g2_ms = time_ms(lambda: coda.coda_gemm_rowscale_packed(Hgp, W2, r, Y, stream), stream, steps, warmup)
     tf = wl.fwd_flops / (ms * 1e-3) / 1e12
     g2_tf = 2.0 * M * D * N2 / (g2_ms * 1e-3) / 1e12
     return {"shape": {"M": M, "K": K, "D": D, "N2": N2}, "ms_per_step": round(ms, 4), "value": round(tf, 2),
             "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
-            "coda_gemm_rowscale_frac": round(g2_tf / PEAK_BF16_TFLOPS, 4)}
+            "coda_gemm_rowscale_packed_frac": round(g2_tf / PEAK_BF16_TFLOPS, 4)}
 
 
 def bench_ce(args, up, stream):
@@ -869,17 +872,32 @@ def main():
     r = torch.empty((M,), device=dev, dtype=torch.float32)
     Y = torch.empty((M, N2), device=dev, dtype=tdt)
     stream = torch.cuda.current_stream()
+    # bf16: Hg goes between the GEMMs tile-packed (coda_gemm_res_prms_packed /
+    # coda_gemm_rowscale_packed); fp32 has only the row-major pair
+    packed = tdt == torch.bfloat16
+    Hgp = coda.packed_empty(M, D, dev) if packed else None
 
     def step(ev=None):
-        coda.coda_gemm_res_prms(d["A"], d["W1"], d["R"], d["g"], H, Hg, P, stream)
+        if packed:
+            coda.coda_gemm_res_prms_packed(d["A"], d["W1"], d["R"], d["g"], H, Hgp, P, stream)
+        else:
+            coda.coda_gemm_res_prms(d["A"], d["W1"], d["R"], d["g"], H, Hg, P, stream)
         if ev is not None:
             ev[0].record(stream)
         coda.coda_rms_combine(P, r, D, wl.eps, stream)
         if ev is not None:
             ev[1].record(stream)
-        coda.coda_gemm_rowscale(Hg, d["W2"], r, Y, stream)
+        if packed:
+            coda.coda_gemm_rowscale_packed(Hgp, d["W2"], r, Y, stream)
+        else:
+            coda.coda_gemm_rowscale(Hg, d["W2"], r, Y, stream)
         if ev is not None:
             ev[2].record(stream)
+
+    def step_row_major():
+        coda.coda_gemm_res_prms(d["A"], d["W1"], d["R"], d["g"], H, Hg, P, stream)
+        coda.coda_rms_combine(P, r, D, wl.eps, stream)
+        coda.coda_gemm_rowscale(Hg, d["W2"], r, Y, stream)
 
     if args.copy_probe_mib > 0:
         src = torch.ones((args.copy_probe_mib << 20,), device=dev, dtype=torch.uint8)
@@ -936,16 +954,21 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{wl.name} fused forward chain", "M": M, "K": K, "D": D, "N2": N2,
+        "config": {"workload": f"{wl.name} fused forward chain" + (", Hg tile-packed between the GEMMs"
+                                                                  if packed else ""),
+                   "M": M, "K": K, "D": D, "N2": N2,
                    "eps": wl.eps, "seed": args.seed},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
-        "roofline": {"bound": "mfma", "kernel": "coda_gemm_rowscale (second GEMM, row-scale epilogue)",
+        "roofline": {"bound": "mfma",
+                     "kernel": ("coda_gemm_rowscale_packed (second GEMM, row-scale epilogue, Hg tile-packed)"
+                                if packed else "coda_gemm_rowscale (second GEMM, row-scale epilogue)"),
                      "achieved": round(g2_tflops, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
                      "frac": round(g2_tflops / peak, 4), "traffic": measured_traffic(wl.name),
                      "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "algorithmic_flops_per_launch": g2_flops},
-        "kernels_ms": {"coda_gemm_res_prms": round(g1_avg, 4), "coda_rms_combine": round(comb_avg, 4),
-                       "coda_gemm_rowscale": round(g2_avg, 4)},
+        "kernels_ms": {("coda_gemm_res_prms_packed" if packed else "coda_gemm_res_prms"): round(g1_avg, 4),
+                       "coda_rms_combine": round(comb_avg, 4),
+                       ("coda_gemm_rowscale_packed" if packed else "coda_gemm_rowscale"): round(g2_avg, 4)},
         "step_ms_percentiles": pct,
         "wall_s_timed_region": round(wall_s, 3),
         "device": {"name": torch.cuda.get_device_name(dev),
@@ -966,6 +989,15 @@ def main():
         pp["peak_at_clock_tflops"] = round(peak_clk, 1)
         pp["dominant_kernel_frac_at_clock"] = round(g2_tflops / peak_clk, 4)
         out["power"] = pp
+
+    if packed:
+        # the same chain with Hg row-major between the GEMMs (coda_gemm_res_prms
+        # + coda_gemm_rowscale): same arithmetic and outputs, the A operand of
+        # the second GEMM read with 16-row gathers instead of contiguous runs
+        pk_ms, rm_ms = time_ms_alternating([step, step_row_major], stream, max(5, args.steps // 2),
+                                           max(2, args.warmup // 2))
+        out["hg_layout"] = {"tile_packed_ms": round(pk_ms, 4), "row_major_ms": round(rm_ms, 4),
+                            "packed_speedup": round(rm_ms / pk_ms, 4)}
 
     if not args.no_ref_chain:
         ws = torch.empty((coda.coda_ref_chain_workspace_bytes(tdt, M, D),), device=dev, dtype=torch.uint8)
@@ -1010,7 +1042,7 @@ def main():
         del scratch
 
     if not args.no_g_placement:
-        out["g_placement"] = bench_g_placement(wl, d, H, Hg, P, r, Y, step, stream, args)
+        out["g_placement"] = bench_g_placement(wl, d, H, Hg, P, r, Y, step_row_major, stream, args)
 
     if not args.no_torch_chain:
         # the unfused library path: vendor GEMMs with torch's RMSNorm in between

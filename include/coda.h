@@ -104,6 +104,43 @@ coda_status coda_gemm_rowscale(coda_dtype dt, int64_t M, int64_t D, int64_t N2,
                                const float* r,
                                void* Y, int64_t ldy, void* stream);
 
+/* The forward pair with the Hg intermediate tile-packed (bfloat16 only).
+ * The article's epilogue section has the first GEMM's epilogue write what the
+ * second GEMM consumes; here it also writes it in the order the second GEMM's
+ * MFMA fragment reads take it.  Tile-packed layout of an [M,D] matrix (D a
+ * multiple of 8, rows padded to a multiple of 16): element (i, 8c + e) lies
+ * at bfloat16 index ((i/16 * D/8 + c) * 16 + i%16) * 8 + e, i.e. for each
+ * 16-row block and each run of 8 columns, the 16 rows' 16-byte pieces are
+ * contiguous.  Padding rows are never written nor read.  Values, H,
+ * partials, r and Y are bit-identical to coda_gemm_res_prms +
+ * coda_gemm_rowscale; only where Hg lives differs. */
+
+/* Bytes of a tile-packed bfloat16 matrix of `rows` rows and `cols` columns
+ * (cols a multiple of 8): 2 * cols * (rows rounded up to 16).  -1 for bad
+ * arguments. */
+int64_t coda_packed_bytes(int64_t rows, int64_t cols);
+
+/* coda_gemm_res_prms (bfloat16) with Hg tile-packed: Hgp holds
+ * coda_packed_bytes(M, D) bytes, 16-byte aligned; g and Hgp must be set.
+ * The other arguments and outputs are those of coda_gemm_res_prms. */
+coda_status coda_gemm_res_prms_packed(int64_t M, int64_t K, int64_t D,
+                                      const void* A, int64_t lda,
+                                      const void* W1, int64_t ldw1,
+                                      const void* R, int64_t ldr,
+                                      const void* g,
+                                      void* H, int64_t ldh,
+                                      void* Hgp, float* partials, void* stream);
+
+/* coda_gemm_rowscale (bfloat16) reading X = Hg tile-packed (Xp, as written
+ * by coda_gemm_res_prms_packed for the same M and D):
+ *   Y_ik = round(r_i * sum_j X_ij W2_jk)          [M,N2]
+ * r may be NULL (plain GEMM).  W2: ldw2 >= N2; Y: ldy >= N2. */
+coda_status coda_gemm_rowscale_packed(int64_t M, int64_t D, int64_t N2,
+                                      const void* Xp,
+                                      const void* W2, int64_t ldw2,
+                                      const float* r,
+                                      void* Y, int64_t ldy, void* stream);
+
 /* Second GEMM with the deferred row scale and a SwiGLU gate in the epilogue.
  * The article (section "CODA：「尾声」里藏着宝藏") says the re-parameterisation
  * applies to SwiGLU as well, and its results section measures SwiGLU epilogue

@@ -94,6 +94,70 @@ static void check_kc() {
     }
 }
 
+// ---- tile-packed contraction-contiguous layout --------------------------
+// The DMA of a k-tile fills the same LDS positions kp_offset reads back; a
+// lane's 16 bytes come from consecutive global units (each 1 KiB block is
+// one contiguous 1 KiB of the packed matrix); fragment reads are 256
+// contiguous bytes per 16 lanes (every bank once); kp_unit is a bijection
+// from (row, chunk) onto the packed units.
+static void check_kp() {
+  std::vector<int> hits(kOperandBytes / 16, 0), pos_of(kTileM * 4, -1);
+  const int nck = 40;  // chunks per row of a packed matrix (D = 320)
+  for (int s = 0; s < kDmaSlots; ++s)
+    for (int w = 0; w < kWaves; ++w) {
+      int64_t unit0[3] = {-1, -1, -1};
+      for (int L = 0; L < 64; ++L) {
+        int r, c;
+        dma_kp(s, w, L, &r, &c);
+        CHECK(r >= 0 && r < kTileM && c >= 0 && c < 4, "dma_kp(%d,%d,%d) -> (%d,%d)", s, w, L, r, c);
+        const int pos = (s * kWaves + w) * 1024 + 16 * L;
+        CHECK(kp_offset(r, c) == pos, "KP: DMA writes (%d,%d) at %d, reads expect %d", r, c, pos, kp_offset(r, c));
+        hits[pos / 16]++;
+        pos_of[r * 4 + c] = pos;
+        int r0, c0;
+        dma_kp(0, w, L, &r0, &c0);
+        CHECK(c0 == c, "KP chunk differs between slots");
+        // k-tile kt of tile row m0 = 256: chunk 4 kt + c; consecutive lanes read consecutive units
+        for (int kt = 0; kt < 3; ++kt) {
+          const int64_t u = kp_unit(256 + r, 4 * kt + c, nck);
+          if (L == 0) unit0[kt] = u;
+          CHECK(u == unit0[kt] + L, "KP DMA block not contiguous (s %d w %d L %d kt %d)", s, w, L, kt);
+          // the kernel adds 1 KiB per k-tile to the k-tile-0 offset
+          CHECK(u * 16 == kp_unit(256 + r, c, nck) * 16 + 1024 * kt, "KP k-tile stride");
+        }
+      }
+    }
+  for (size_t i = 0; i < hits.size(); ++i) CHECK(hits[i] == 1, "KP LDS slot %zu written %d times", i, hits[i]);
+  for (size_t i = 0; i < pos_of.size(); ++i) CHECK(pos_of[i] >= 0, "KP element chunk %zu never loaded", i);
+  for (int base = 0; base < kTileM; base += 128)
+    for (int t = 0; t < kFragM; ++t)
+      for (int g = 0; g < 4; ++g) {
+        int used[64] = {0};
+        for (int i = 0; i < 16; ++i) {
+          const int off = kp_offset(base + 16 * t + i, g);
+          CHECK(off == kp_offset(base + i, g) + 1024 * t, "KP fragment stride");
+          CHECK(off == kp_offset(base + 16 * t, g) + 16 * i, "KP fragment not contiguous");
+          const int bank = (off / 4) % 64;
+          for (int q = 0; q < 4; ++q) used[(bank + q) % 64]++;
+        }
+        for (int b = 0; b < 64; ++b) CHECK(used[b] == 1, "KP fragment bank conflict base %d t %d g %d", base, t, g);
+      }
+  // kp_unit: a bijection from 37 rows x nck chunks onto 48 x nck units (rows padded to 16)
+  std::vector<int> seen(48 * nck, 0);
+  for (int r = 0; r < 37; ++r)
+    for (int c = 0; c < nck; ++c) {
+      const int64_t u = kp_unit(r, c, nck);
+      CHECK(u >= 0 && u < 48 * nck, "kp_unit out of range");
+      seen[u]++;
+    }
+  int total = 0;
+  for (int v : seen) {
+    CHECK(v <= 1, "kp_unit not injective");
+    total += v;
+  }
+  CHECK(total == 37 * nck, "kp_unit count");
+}
+
 // ---- row-contiguous layout ----------------------------------------------
 static void check_rc(int E) {
   const int KTE = kKTBytes / (16 / E);  // contraction rows per k-tile (32 bf16, 16 fp32)
@@ -254,6 +318,7 @@ static void check_epilogue_slab() {
 int main() {
   check_map_tile();
   check_kc();
+  check_kp();
   check_rc(8);
   check_rc(4);
   check_epilogue_slab();

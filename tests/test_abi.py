@@ -558,3 +558,54 @@ def test_ceiling_library_exports_and_rejects():
         assert fn(fake, 2048 * 512 - 1, 2048, 1, 0, None) == -1
         assert fn(fake, 2048 * 512, 0, 1, 0, None) == -1
         assert fn(fake, 2048 * 512, 2048, 0, 0, None) == -1
+
+
+# ---- the forward pair with Hg tile-packed ----
+def test_packed_bytes(lib):
+    assert lib.coda_packed_bytes(300, 512) == 304 * 512 * 2
+    assert lib.coda_packed_bytes(16, 8) == 16 * 8 * 2
+    assert lib.coda_packed_bytes(0, 8) == 0
+    assert lib.coda_packed_bytes(1, 12) == -1
+    assert lib.coda_packed_bytes(-1, 8) == -1
+    assert lib.coda_packed_bytes(1, 0) == -1
+
+
+def prms_packed(lib, M=300, K=256, D=512, A=A_, lda=256, W1=W1_, ldw1=512, R=R_, ldr=512, g=G_, H=H_, ldh=512,
+                Hgp=HG_, part=PART_):
+    return lib.coda_gemm_res_prms_packed(M, K, D, A, lda, W1, ldw1, R, ldr, g, H, ldh, Hgp, part, None)
+
+
+def rowscale_packed(lib, M=300, D=512, N2=768, Xp=HG_, W2=W2_, ldw2=768, r=R2_, Y=Y_, ldy=768):
+    return lib.coda_gemm_rowscale_packed(M, D, N2, Xp, W2, ldw2, r, Y, ldy, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=500), SHAPE),
+    (dict(g=None), NULL),
+    (dict(Hgp=None), NULL),
+    (dict(Hgp=HG_ + 8), ALIGN),
+    (dict(part=PART_ + 2), ALIGN),
+    (dict(ldh=256), SHAPE),
+    (dict(Hgp=H_ + 64), ALIAS),   # overlaps H
+    (dict(Hgp=R_), ALIAS),
+])
+def test_gemm_res_prms_packed_rejects(lib, kw, status):
+    assert prms_packed(lib, **kw) == status
+    assert lib.coda_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N2=12), SHAPE),
+    (dict(Xp=None), NULL),
+    (dict(Xp=HG_ + 4), ALIGN),
+    (dict(ldy=256), SHAPE),
+    (dict(Y=HG_ + 1024), ALIAS),
+    (dict(r=R2_ + 2), ALIGN),
+])
+def test_gemm_rowscale_packed_rejects(lib, kw, status):
+    assert rowscale_packed(lib, **kw) == status
+
+
+def test_packed_pair_empty_is_noop(lib):
+    assert prms_packed(lib, M=0, A=None, R=None, H=None, Hgp=None, part=None) == OK
+    assert rowscale_packed(lib, M=0, Xp=None, Y=None) == OK

@@ -1,0 +1,138 @@
+"""GPU parity of the forward pair with the Hg intermediate tile-packed
+(coda_gemm_res_prms_packed + coda_rms_combine + coda_gemm_rowscale_packed).
+
+The packed pair computes exactly what the row-major pair computes: H,
+partials, r and Y must be bit-identical to coda_gemm_res_prms +
+coda_gemm_rowscale on the same inputs, and the packed Hg must hold exactly
+the row-major Hg, permuted (element (i, 8c + e) at bfloat16 index
+((i/16 * D/8 + c) * 16 + i%16) * 8 + e).  Y is also checked against the fp64
+oracle (the plain chain of the CODA news article by Synced, epilogue
+section) with the bf16 bar of 1e-2.  Shapes include ragged M (padding rows
+in the last block), D not a multiple of the 32-column k-tile, and the full
+7B workload in the benchmark's launch configuration (sampled rows against
+the oracle).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import coda_inputs as ci
+import oracle
+import transformer_gemm_epilogue_gemm1_amd as coda
+from tests.gpu_util import dev, host_bits, host_f32, max_rel
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu-test] {request.node.nodeid}", file=sys.__stderr__, flush=True)
+    yield
+    torch.cuda.synchronize()
+
+
+def _both(wl, seed):
+    x = ci.make_inputs(wl, seed=seed)
+    d = {k: dev(v) for k, v in x.items()}
+    row = coda.fused_forward(d["A"], d["W1"], d["R"], d["g"], d["W2"], wl.eps)
+    pk = coda.fused_forward_packed(d["A"], d["W1"], d["R"], d["g"], d["W2"], wl.eps)
+    torch.cuda.synchronize()
+    return x, row, pk
+
+
+def _same(a, b, what):
+    assert np.array_equal(host_bits(a) if a.dtype == torch.bfloat16 else a.cpu().numpy().view(np.uint32),
+                          host_bits(b) if b.dtype == torch.bfloat16 else b.cpu().numpy().view(np.uint32)), \
+        f"{what} differs between the packed and the row-major pair"
+
+
+def _index_check(Hgp, Hg, M, D):
+    # the documented index formula, element by element on the host
+    flat = host_bits(Hgp).reshape(-1)
+    ref = host_bits(Hg)
+    i = np.arange(M)[:, None]
+    col = np.arange(D)[None, :]
+    idx = ((i // 16 * (D // 8) + col // 8) * 16 + i % 16) * 8 + col % 8
+    np.testing.assert_array_equal(flat[idx], ref)
+
+
+SHAPES = [(256, 256, 256, 512), (300, 256, 512, 768), (1, 64, 72, 40), (33, 96, 40, 264), (513, 320, 328, 600)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_packed_pair_matches_row_major_and_oracle(shape):
+    M, K, D, N2 = shape
+    wl = ci.custom_workload(M, K, D, N2, eps=1e-5, dtype="bf16", wl_id=700 + M % 97)
+    x, (H, Hg, r, Y, P), (Hp, Hgp, rp, Yp, Pp) = _both(wl, seed=5)
+    _same(H, Hp, "H")
+    _same(P, Pp, "partials")
+    _same(r, rp, "r")
+    _same(Y, Yp, "Y")
+    assert tuple(Hgp.shape) == ((M + 15) // 16, D // 8, 16, 8)
+    _index_check(Hgp, Hg, M, D)
+    assert torch.equal(coda.unpack(Hgp, M).view(torch.int16), Hg.view(torch.int16))
+    orc = oracle.forward(x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps)
+    err = max_rel(host_f32(Yp), orc["Y"])
+    print(f"{shape}: packed Y error {err:.3e}")
+    assert err <= 1e-2
+
+
+def test_packed_rowscale_without_r_and_strided_y():
+    # r = NULL (plain GEMM) and a Y with ldy > N2, against the row-major kernel
+    M, D, N2 = 200, 256, 304
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    X = torch.randn((M, D), device="cuda", generator=g).to(torch.bfloat16)
+    W2 = (torch.randn((D, N2), device="cuda", generator=g) * D ** -0.5).to(torch.bfloat16)
+    Xp = coda.packed_empty(M, D, "cuda")
+    Xp.copy_(torch.nn.functional.pad(X, (0, 0, 0, (-M) % 16)).reshape(-1, 16, D // 8, 8).permute(0, 2, 1, 3))
+    assert torch.equal(coda.unpack(Xp, M), X)
+    Yb = torch.full((M, N2 + 40), float("nan"), device="cuda", dtype=torch.bfloat16)
+    Yp = Yb[:, :N2]
+    Yr = torch.empty((M, N2), device="cuda", dtype=torch.bfloat16)
+    coda.coda_gemm_rowscale(X, W2, None, Yr)
+    lib = coda._lib.load()
+    st = lib.coda_gemm_rowscale_packed(M, D, N2, Xp.data_ptr(), W2.data_ptr(), N2, None, Yp.data_ptr(), N2 + 40,
+                                       torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert torch.equal(Yp.view(torch.int16), Yr.view(torch.int16))
+    assert torch.isnan(Yb[:, N2:].float()).all()  # the padding columns are not written
+
+
+def test_packed_repeatable():
+    wl = ci.custom_workload(300, 256, 512, 768, eps=1e-5, dtype="bf16", wl_id=790)
+    x = ci.make_inputs(wl, seed=2)
+    d = {k: dev(v) for k, v in x.items()}
+    a = coda.fused_forward_packed(d["A"], d["W1"], d["R"], d["g"], d["W2"], wl.eps)
+    b = coda.fused_forward_packed(d["A"], d["W1"], d["R"], d["g"], d["W2"], wl.eps)
+    torch.cuda.synchronize()
+    # the packed Hg is compared on its M rows: the last block's padding rows
+    # are never written
+    a = list(a)
+    b = list(b)
+    a[1], b[1] = coda.unpack(a[1], wl.M), coda.unpack(b[1], wl.M)
+    for t, u in zip(a, b):
+        assert torch.equal(t.view(torch.int16) if t.dtype == torch.bfloat16 else t,
+                           u.view(torch.int16) if u.dtype == torch.bfloat16 else u)
+
+
+@pytest.mark.slow
+def test_full_size_7b_packed_sampled_rows():
+    # the benchmark's workload and launch configuration; Y bit-identical to
+    # the row-major pair, sampled rows against the oracle
+    wl = ci.WORKLOADS["7b-bf16"]
+    x, (H, Hg, r, Y, P), (Hp, Hgp, rp, Yp, Pp) = _both(wl, seed=0)
+    _same(H, Hp, "H")
+    _same(r, rp, "r")
+    _same(Y, Yp, "Y")
+    assert torch.equal(coda.unpack(Hgp, wl.M).view(torch.int16), Hg.view(torch.int16))
+    rng = np.random.default_rng(17)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, wl.M - 1], rng.integers(0, wl.M, 11)]))
+    orc = oracle.forward(x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps, rows=rows)
+    tr = torch.from_numpy(rows).cuda()
+    err = max_rel(Yp.index_select(0, tr).float().cpu().numpy(), orc["Y"])
+    print(f"7b packed sampled-row Y error {err:.3e}")
+    assert err <= 1e-2

@@ -31,6 +31,10 @@ SIGNATURES = {
     "coda_rms_combine": (c_int, [c_i64, c_i64, c_i64, c_float, c_vp, c_vp, c_vp]),
     "coda_gemm_rowscale": (c_int, [c_int, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp,
                                    c_vp, c_i64, c_vp]),
+    "coda_packed_bytes": (c_i64, [c_i64, c_i64]),
+    "coda_gemm_res_prms_packed": (c_int, [c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp,
+                                          c_vp, c_i64, c_vp, c_vp, c_vp]),
+    "coda_gemm_rowscale_packed": (c_int, [c_i64, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp]),
     "coda_gemm_rowscale_swiglu": (c_int, [c_int, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp,
                                           c_vp, c_i64, c_vp, c_i64, c_vp]),
     "coda_swiglu_bwd": (c_int, [c_int, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),

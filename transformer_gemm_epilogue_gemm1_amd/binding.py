@@ -109,6 +109,69 @@ def coda_gemm_rowscale(X, W2, r: Optional[torch.Tensor], Y, stream=None) -> None
     _lib.check("coda_gemm_rowscale", st)
 
 
+def coda_packed_bytes(rows: int, cols: int) -> int:
+    return int(_lib.load().coda_packed_bytes(rows, cols))
+
+
+def packed_empty(M: int, D: int, device) -> torch.Tensor:
+    """A bfloat16 buffer for a tile-packed [M, D] matrix, shaped
+    [ceil(M/16), D/8, 16, 8] (row block, column run, row in block, column)."""
+    if D % 8 != 0:
+        raise ValueError(f"D = {D} must be a multiple of 8")
+    return torch.empty(((M + 15) // 16, D // 8, 16, 8), device=device, dtype=torch.bfloat16)
+
+
+def _packed(Xp: torch.Tensor, name: str, M: int, D: int) -> None:
+    if Xp.dtype != torch.bfloat16 or not Xp.is_cuda:
+        raise TypeError(f"{name}: expected a bfloat16 CUDA tensor")
+    if tuple(Xp.shape) != ((M + 15) // 16, D // 8, 16, 8) or not Xp.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tile-packed buffer of shape "
+                         f"{((M + 15) // 16, D // 8, 16, 8)}, got {tuple(Xp.shape)}")
+
+
+def coda_gemm_res_prms_packed(A, W1, R, g, H, Hgp, partials, stream=None) -> None:
+    """coda_gemm_res_prms with Hg written tile-packed into Hgp (packed_empty)."""
+    lib = _lib.load()
+    dt = A.dtype
+    M, K = A.shape
+    D = W1.shape[1]
+    T = coda_prms_num_partials(dt, D)
+    lda = _mat(A, "A", dt, (M, K))
+    ldw1 = _mat(W1, "W1", dt, (K, D))
+    ldr = _mat(R, "R", dt, (M, D))
+    ldh = _mat(H, "H", dt, (M, D))
+    _mat(g, "g", dt, (D,))
+    _packed(Hgp, "Hg", M, D)
+    _mat(partials, "partials", torch.float32, (T, M))
+    _dense(partials, "partials")
+    st = lib.coda_gemm_res_prms_packed(M, K, D, A.data_ptr(), lda, W1.data_ptr(), ldw1, R.data_ptr(), ldr,
+                                       g.data_ptr(), H.data_ptr(), ldh, Hgp.data_ptr(), partials.data_ptr(),
+                                       _stream(stream))
+    _lib.check("coda_gemm_res_prms_packed", st)
+
+
+def coda_gemm_rowscale_packed(Xp, W2, r: Optional[torch.Tensor], Y, stream=None) -> None:
+    """Y = diag(r) (X W2) with X tile-packed in Xp (as coda_gemm_res_prms_packed writes it)."""
+    lib = _lib.load()
+    M, N2 = Y.shape
+    D = W2.shape[0]
+    _packed(Xp, "X", M, D)
+    ldw2 = _mat(W2, "W2", torch.bfloat16, (D, N2))
+    ldy = _mat(Y, "Y", torch.bfloat16, (M, N2))
+    if r is not None:
+        _mat(r, "r", torch.float32, (M,))
+    st = lib.coda_gemm_rowscale_packed(M, D, N2, Xp.data_ptr(), W2.data_ptr(), ldw2,
+                                       r.data_ptr() if r is not None else None, Y.data_ptr(), ldy,
+                                       _stream(stream))
+    _lib.check("coda_gemm_rowscale_packed", st)
+
+
+def unpack(Xp: torch.Tensor, M: int) -> torch.Tensor:
+    """The [M, D] row-major matrix held by a tile-packed buffer (a copy)."""
+    nb, nck, _, _ = Xp.shape
+    return Xp.permute(0, 2, 1, 3).reshape(nb * 16, nck * 8)[:M]
+
+
 def coda_gemm_rowscale_swiglu(X, W2, r: Optional[torch.Tensor], Z, Y: Optional[torch.Tensor] = None,
                               stream=None) -> None:
     """Z = silu(Y_gate) * Y_up with Y = diag(r) (X W2), W2 = [W_gate | W_up];
@@ -371,6 +434,22 @@ def fused_forward(A, W1, R, g, W2, eps: float, stream=None):
     coda_rms_combine(P, r, D, eps, stream)
     coda_gemm_rowscale(Hg, W2, r, Y, stream)
     return H, Hg, r, Y, P
+
+
+def fused_forward_packed(A, W1, R, g, W2, eps: float, stream=None):
+    """The fused chain with Hg tile-packed between the two GEMMs: returns
+    (H, Hgp, r, Y, partials); Hgp as packed_empty (unpack gives Hg)."""
+    M, D, N2 = A.shape[0], W1.shape[1], W2.shape[1]
+    dev, dt = A.device, A.dtype
+    H = torch.empty((M, D), device=dev, dtype=dt)
+    Hgp = packed_empty(M, D, dev)
+    P = torch.empty((coda_prms_num_partials(dt, D), M), device=dev, dtype=torch.float32)
+    r = torch.empty((M,), device=dev, dtype=torch.float32)
+    Y = torch.empty((M, N2), device=dev, dtype=dt)
+    coda_gemm_res_prms_packed(A, W1, R, g, H, Hgp, P, stream)
+    coda_rms_combine(P, r, D, eps, stream)
+    coda_gemm_rowscale_packed(Hgp, W2, r, Y, stream)
+    return H, Hgp, r, Y, P
 
 
 def ref_chain(A, W1, R, g, W2, eps: float, stream=None):

@@ -106,7 +106,11 @@ uint32_t span_bytes(int64_t rows, int64_t cols, int64_t ld, int es) {
   return (uint32_t)(rows <= 0 ? 0 : ((rows - 1) * ld + cols) * es);
 }
 
-template <typename T, bool AKC, bool BKC, class Epi>
+// Bytes of a tile-packed bf16 matrix (kp_unit): rows padded to 16, cols / 8 chunks.
+int64_t packed_bytes(int64_t rows, int64_t cols) { return (rows + 15) / 16 * 16 * cols * 2; }
+
+// APK: A is tile-packed and lda counts its 16-byte chunks per row.
+template <typename T, bool AKC, bool BKC, class Epi, bool APK = false>
 coda_status launch_gemm(const char* what, int M, int N, int K, const void* a, int64_t lda, const void* b,
                         int64_t ldb, const typename Epi::Params& ep, hipStream_t s, int b_split = 0) {
   GemmArgs g;
@@ -118,13 +122,14 @@ coda_status launch_gemm(const char* what, int M, int N, int K, const void* a, in
   g.group_m = kGroupM;
   g.a = a;
   g.lda = lda;
-  g.a_span = AKC ? span_bytes(M, K, lda, sizeof(T)) : span_bytes(K, M, lda, sizeof(T));
+  g.a_span = APK ? (uint32_t)packed_bytes(M, 8 * lda)
+                 : AKC ? span_bytes(M, K, lda, sizeof(T)) : span_bytes(K, M, lda, sizeof(T));
   g.b = b;
   g.ldb = ldb;
   g.b_span = BKC ? span_bytes(N, K, ldb, sizeof(T)) : span_bytes(K, N, ldb, sizeof(T));
   g.b_split = b_split;
   const int nblocks = g.tiles_m * g.tiles_n;
-  hipLaunchKernelGGL((gemm_kernel<T, AKC, BKC, Epi>), dim3(nblocks), dim3(kThreads), 0, s, g, ep);
+  hipLaunchKernelGGL((gemm_kernel<T, AKC, BKC, Epi, APK>), dim3(nblocks), dim3(kThreads), 0, s, g, ep);
   return launch_status(what);
 }
 
@@ -182,6 +187,24 @@ coda_status gemm_rowscale_impl(int M, int D, int N2, const void* X, int64_t ldx,
                                const float* r, void* Y, int64_t ldy, hipStream_t s) {
   typename EpiRowScale<T>::Params ep{r, (T*)Y, ldy};
   return launch_gemm<T, true, false, EpiRowScale<T>>("coda_gemm_rowscale", M, N2, D, X, ldx, W2, ldw2, ep, s);
+}
+
+// The forward pair with the Hg intermediate tile-packed (bf16): the first
+// GEMM's epilogue stores Hg in the order the second GEMM's fragment reads use.
+coda_status gemm_res_prms_packed_impl(int M, int K, int D, const void* A, int64_t lda, const void* W1, int64_t ldw1,
+                                      const void* R, int64_t ldr, const void* g, void* H, int64_t ldh, void* Hgp,
+                                      float* partials, hipStream_t s) {
+  typename EpiResPrms<uint16_t>::Params ep{(const uint16_t*)R, ldr, (const uint16_t*)g, (uint16_t*)H, ldh,
+                                           (uint16_t*)Hgp, 0, partials, D / 8};
+  return launch_gemm<uint16_t, true, false, EpiResPrms<uint16_t>>("coda_gemm_res_prms_packed", M, D, K, A, lda, W1,
+                                                                  ldw1, ep, s);
+}
+
+coda_status gemm_rowscale_packed_impl(int M, int D, int N2, const void* Xp, const void* W2, int64_t ldw2,
+                                      const float* r, void* Y, int64_t ldy, hipStream_t s) {
+  typename EpiRowScale<uint16_t>::Params ep{r, (uint16_t*)Y, ldy};
+  return launch_gemm<uint16_t, true, false, EpiRowScale<uint16_t>, true>("coda_gemm_rowscale_packed", M, N2, D, Xp,
+                                                                         D / 8, W2, ldw2, ep, s);
 }
 
 template <typename T>
@@ -502,6 +525,54 @@ coda_status coda_gemm_rowscale(coda_dtype dt, int64_t M, int64_t D, int64_t N2, 
   hipStream_t s = (hipStream_t)stream;
   if (dt == CODA_BF16) return gemm_rowscale_impl<uint16_t>((int)M, (int)D, (int)N2, X, ldx, W2, ldw2, r, Y, ldy, s);
   return gemm_rowscale_impl<float>((int)M, (int)D, (int)N2, X, ldx, W2, ldw2, r, Y, ldy, s);
+}
+
+int64_t coda_packed_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || rows > kMaxDim || cols < 1 || cols > kMaxDim || cols % 8 != 0) return -1;
+  return packed_bytes(rows, cols);
+}
+
+coda_status coda_gemm_res_prms_packed(int64_t M, int64_t K, int64_t D, const void* A, int64_t lda, const void* W1,
+                                      int64_t ldw1, const void* R, int64_t ldr, const void* g, void* H, int64_t ldh,
+                                      void* Hgp, float* partials, void* stream) {
+  coda_status st = check_dims(CODA_BF16, M, {{"K", K}, {"D", D}});
+  if (st != CODA_OK) return st;
+  if (M == 0) return ok();
+  const int es = 2, E = 8;
+  const int64_t T = num_partials(D);
+  if (g == nullptr || Hgp == nullptr) return fail(CODA_ERR_NULL, "g and Hg must be set");
+  const Mat mA{A, M, K, lda, es, "A"}, mW1{W1, K, D, ldw1, es, "W1"}, mR{R, M, D, ldr, es, "R"};
+  const Mat mg{g, 1, D, D, es, "g"}, mH{H, M, D, ldh, es, "H"};
+  const int64_t hg_elems = packed_bytes(M, D) / 2;
+  const Mat mHg{Hgp, 1, hg_elems, hg_elems, es, "Hg"};  // the packed matrix as one flat row
+  const Mat mP{partials, T, M, M, 4, "partials"};
+  for (const Mat* m : {&mA, &mW1, &mR, &mH, &mg, &mHg})
+    if ((st = check_mat(*m, E)) != CODA_OK) return st;
+  if (partials == nullptr) return fail(CODA_ERR_NULL, "partials is NULL");
+  if (((uintptr_t)partials & 3) != 0) return fail(CODA_ERR_ALIGN, "partials is not 4-byte aligned");
+  if (mP.span() > kMaxSpan) return fail(CODA_ERR_SHAPE, "partials span too large");
+  const Mat outs[3] = {mH, mHg, mP};
+  const Mat ins[4] = {mA, mW1, mR, mg};
+  if ((st = check_alias(outs, 3, ins, 4)) != CODA_OK) return st;
+  return gemm_res_prms_packed_impl((int)M, (int)K, (int)D, A, lda, W1, ldw1, R, ldr, g, H, ldh, Hgp, partials,
+                                   (hipStream_t)stream);
+}
+
+coda_status coda_gemm_rowscale_packed(int64_t M, int64_t D, int64_t N2, const void* Xp, const void* W2, int64_t ldw2,
+                                      const float* r, void* Y, int64_t ldy, void* stream) {
+  coda_status st = check_dims(CODA_BF16, M, {{"D", D}, {"N2", N2}});
+  if (st != CODA_OK) return st;
+  if (M == 0) return ok();
+  const int es = 2, E = 8;
+  const int64_t x_elems = packed_bytes(M, D) / 2;
+  const Mat mX{Xp, 1, x_elems, x_elems, es, "X"}, mW2{W2, D, N2, ldw2, es, "W2"}, mY{Y, M, N2, ldy, es, "Y"};
+  const Mat mr{r, 1, M, M, 4, "r"};
+  for (const Mat* m : {&mX, &mW2, &mY})
+    if ((st = check_mat(*m, E)) != CODA_OK) return st;
+  if (r != nullptr && ((uintptr_t)r & 3) != 0) return fail(CODA_ERR_ALIGN, "r is not 4-byte aligned");
+  const Mat ins[3] = {mX, mW2, r ? mr : Mat{nullptr, 0, 0, 0, 4, "r"}};
+  if ((st = check_alias(&mY, 1, ins, 3)) != CODA_OK) return st;
+  return gemm_rowscale_packed_impl((int)M, (int)D, (int)N2, Xp, W2, ldw2, r, Y, ldy, (hipStream_t)stream);
 }
 
 coda_status coda_gemm_rowscale_swiglu(coda_dtype dt, int64_t M, int64_t D, int64_t F, const void* X, int64_t ldx,

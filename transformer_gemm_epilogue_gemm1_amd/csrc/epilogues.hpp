@@ -84,6 +84,7 @@ struct EpiResPrms {
     T* Hg;
     int64_t ldhg;
     float* partials;  // [T][M]
+    int64_t hg_nck;   // > 0: Hg is tile-packed (kp_unit) with hg_nck chunks per row, bf16 only
   };
   Params p;
   RowChunks<T> rc;
@@ -115,7 +116,10 @@ struct EpiResPrms {
       float hg[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) hg[i] = h[i] * gv[i];
-      Chunk8<T>::store(p.Hg + (int64_t)row * p.ldhg + col, hg);
+      T* dst = p.Hg + (int64_t)row * p.ldhg + col;
+      if constexpr (sizeof(T) == 2)
+        if (p.hg_nck > 0) dst = p.Hg + kp_unit(row, col >> 3, p.hg_nck) * 8;
+      Chunk8<T>::store(dst, hg);
     }
   }
 

@@ -46,6 +46,29 @@ constexpr int kPartialCols = kWaveN;                // columns per partial-RMS t
 CODA_HD int kc_swizzle(int r) { return (r >> 2) & 3; }
 CODA_HD int kc_offset(int r, int c) { return r * kKTBytes + ((c ^ kc_swizzle(r)) << 4); }
 
+// ---- tile-packed contraction-contiguous ("KP") operand -----------------
+// A contraction-contiguous bf16 matrix may also be stored tile-packed, in the
+// order the fragment reads want: for row block R = row / 16 and 16-byte chunk
+// c of the contraction (8 bf16), the chunks of the block's 16 rows lie
+// together,
+//   element (row, 8 c + e) at 16-byte unit (R nck + c) 16 + row % 16, byte 2 e,
+// with nck chunks per row and the rows padded to a multiple of 16.  One
+// k-tile of 16 rows is then 1 KiB contiguous in memory, and the LDS tile
+// keeps that order: [row block][chunk 0..3][row % 16][16 B].  The 16 lanes
+// of a fragment read take 256 contiguous bytes, which the LDS serves at full
+// rate (the KC layout's 16-byte reads gather 16 rows 64 bytes apart and run
+// at half rate), and every direct load reads 1 KiB of consecutive memory.
+CODA_HD int kp_offset(int r, int c) { return ((r >> 4) * 4 + c) * 256 + (r & 15) * 16; }
+// KP direct loads: block b of the tile is row block b; lane L -> row
+// 16 b + L % 16, chunk L / 16 (position 16 L of the block, as kp_offset).
+CODA_HD void dma_kp(int s, int w, int L, int* row, int* chunk) {
+  const int b = s * kWaves + w;
+  *row = 16 * b + (L & 15);
+  *chunk = L >> 4;
+}
+// 16-byte unit holding chunk c of row r in a packed matrix of nck chunks per row.
+CODA_HD int64_t kp_unit(int64_t r, int64_t c, int64_t nck) { return ((r >> 4) * nck + c) * 16 + (r & 15); }
+
 // ---- row-contiguous ("RC") operand tile --------------------------------
 // The contraction runs across memory rows: KTE contraction rows (32 bf16 /
 // 16 fp32) of 256 operand elements (512 / 1024 bytes).  16-byte chunk c of
