@@ -334,6 +334,41 @@ coda_status coda_gemm_rowscale_fp8(int64_t M, int64_t D, int64_t N2,
                                    const void* W2t8, int64_t ldw2t, const float* sw2,
                                    const float* r, void* Y, int64_t ldy, void* stream);
 
+/* The fp8 forward with tile-packed operands (the layout of
+ * coda_gemm_res_prms_packed, with 16 codes per 16-byte piece): element
+ * (i, 16c + e) of an e4m3 [rows, cols] matrix at byte
+ * ((i/16 * cols/16 + c) * 16 + i%16) * 16 + e, rows padded to a multiple of
+ * 16 (never written nor read).  The second GEMM then reads both operands
+ * with contiguous 1 KiB direct loads and full-rate fragment reads.  Codes,
+ * scales, H, partials and Y are bit-identical to the row-major calls. */
+
+/* Bytes of a tile-packed e4m3 matrix: cols * (rows rounded up to 16); cols a
+ * multiple of 16.  -1 for bad arguments. */
+int64_t coda_packed_bytes_e4m3(int64_t rows, int64_t cols);
+
+/* coda_quantize_cols_e4m3 with the transposed codes Wt8 [N,K] written
+ * tile-packed into Wt8p (coda_packed_bytes_e4m3(N, K) bytes, 16-byte aligned). */
+coda_status coda_quantize_cols_e4m3_packed(int64_t K, int64_t N, const void* W, int64_t ldw,
+                                           void* Wt8p, float* scales, void* stream);
+
+/* coda_gemm_res_prms_fp8 with Hg8 written tile-packed into Hg8p
+ * (coda_packed_bytes_e4m3(M, D) bytes, 16-byte aligned); A8 and W1t8 as in
+ * coda_gemm_res_prms_fp8. */
+coda_status coda_gemm_res_prms_fp8_packed(int64_t M, int64_t K, int64_t D,
+                                          const void* A8, int64_t lda, const float* sa,
+                                          const void* W1t8, int64_t ldw1t, const float* sw1,
+                                          const void* R, int64_t ldr, const void* g,
+                                          void* H, int64_t ldh, void* Hg8p,
+                                          float* partials, void* stream);
+
+/* coda_gemm_rowscale_fp8 with both operands tile-packed: X8p [M,D] (as
+ * coda_gemm_res_prms_fp8_packed writes Hg8) and W2t8p [N2,D] (as
+ * coda_quantize_cols_e4m3_packed writes it).  sw2, r, Y as in
+ * coda_gemm_rowscale_fp8. */
+coda_status coda_gemm_rowscale_fp8_packed(int64_t M, int64_t D, int64_t N2,
+                                          const void* X8p, const void* W2t8p, const float* sw2,
+                                          const float* r, void* Y, int64_t ldy, void* stream);
+
 /* Bytes of workspace coda_ref_chain needs: float C[M,D] + X_n[M,D]. */
 size_t coda_ref_chain_workspace_bytes(coda_dtype dt, int64_t M, int64_t D);
 

@@ -609,3 +609,21 @@ def test_gemm_rowscale_packed_rejects(lib, kw, status):
 def test_packed_pair_empty_is_noop(lib):
     assert prms_packed(lib, M=0, A=None, R=None, H=None, Hgp=None, part=None) == OK
     assert rowscale_packed(lib, M=0, Xp=None, Y=None) == OK
+
+
+def test_fp8_packed_validation(lib):
+    assert lib.coda_packed_bytes_e4m3(300, 512) == 304 * 512
+    assert lib.coda_packed_bytes_e4m3(1, 8) == -1
+    # quantiser: N not a multiple of 16, NULL output, misaligned output, output overlapping W
+    assert lib.coda_quantize_cols_e4m3_packed(256, 24, W2_, 24, WS_, R2_, None) == SHAPE
+    assert lib.coda_quantize_cols_e4m3_packed(256, 512, W2_, 512, None, R2_, None) == NULL
+    assert lib.coda_quantize_cols_e4m3_packed(256, 512, W2_, 512, WS_ + 8, R2_, None) == ALIGN
+    assert lib.coda_quantize_cols_e4m3_packed(256, 512, W2_, 512, W2_ + 64, R2_, None) == ALIAS
+    # first GEMM: Hg8 overlapping H
+    assert lib.coda_gemm_res_prms_fp8_packed(300, 256, 512, A_, 256, R2_, W1_, 256, DG_, R_, 512, G_, H_, 512,
+                                             H_ + 64, PART_, None) == ALIAS
+    # second GEMM: D not a multiple of 16, NULL operand, Y overlapping X
+    assert lib.coda_gemm_rowscale_fp8_packed(300, 264, 512, HG_, W2_, DG_, R2_, Y_, 512, None) == SHAPE
+    assert lib.coda_gemm_rowscale_fp8_packed(300, 256, 512, None, W2_, DG_, R2_, Y_, 512, None) == NULL
+    assert lib.coda_gemm_rowscale_fp8_packed(300, 256, 512, HG_, W2_, DG_, R2_, HG_ + 16, 512, None) == ALIAS
+    assert lib.coda_gemm_rowscale_fp8_packed(0, 256, 512, None, None, None, None, None, 512, None) == OK

@@ -136,3 +136,80 @@ def test_full_size_7b_packed_sampled_rows():
     err = max_rel(Yp.index_select(0, tr).float().cpu().numpy(), orc["Y"])
     print(f"7b packed sampled-row Y error {err:.3e}")
     assert err <= 1e-2
+
+
+# ---- fp8: Hg8 and W2t8 tile-packed ----
+def _u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def _f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+FP8_SHAPES = [(1, 64, 256, 256), (3, 144, 272, 528), (300, 512, 384, 1040), (513, 1024, 1024, 2048)]
+
+
+@pytest.mark.parametrize("shape", FP8_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fp8_packed_chain_matches_row_major_and_oracle(shape):
+    M, K, D, N2 = shape
+    wl = ci.custom_workload(M, K, D, N2, dtype="fp8", wl_id=520)
+    x = ci.make_inputs_fp8(wl, seed=3)
+    d = {"A8": _u8(x["A8"]), "sa": _f32(x["sa"]), "W1t8": _u8(x["W1t8"]), "sw1": _f32(x["sw1"]),
+         "W2t8": _u8(x["W2t8"]), "sw2": _f32(x["sw2"]), "R": dev(x["R"]), "g": dev(x["g"])}
+    H, Hg8, r, Y, P = coda.fused_forward_fp8(d["A8"], d["sa"], d["W1t8"], d["sw1"], d["R"], d["g"], d["W2t8"],
+                                             d["sw2"], wl.eps)
+    # the packed weight codes: the row-major codes permuted
+    W2p = coda.packed_empty_e4m3(N2, D, "cuda")
+    W2p.copy_(torch.nn.functional.pad(d["W2t8"], (0, 0, 0, (-N2) % 16)).reshape(-1, 16, D // 16, 16)
+              .permute(0, 2, 1, 3))
+    Hp, Hg8p, rp, Yp, Pp = coda.fused_forward_fp8_packed(d["A8"], d["sa"], d["W1t8"], d["sw1"], d["R"], d["g"], W2p,
+                                                         d["sw2"], wl.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(coda.unpack_e4m3(Hg8p, M), Hg8)
+    _same(H, Hp, "H")
+    _same(P, Pp, "partials")
+    _same(r, rp, "r")
+    _same(Y, Yp, "Y")
+    orc = oracle.forward_fp8(x["A8"], x["sa"], x["W1t8"], x["sw1"], x["R"].f32, x["g"].f32, x["W2t8"], x["sw2"],
+                             wl.eps)
+    err = max_rel(host_f32(Yp), orc["Y"])
+    print(f"{shape}: fp8 packed Y error {err:.3e}")
+    assert err <= 1e-2
+
+
+@pytest.mark.parametrize("KN", [(256, 512), (4096, 272), (64, 16)], ids=lambda s: "x".join(map(str, s)))
+def test_quantize_weight_packed_is_the_row_major_codes_permuted(KN):
+    K, N = KN
+    g = torch.Generator(device="cuda")
+    g.manual_seed(K + N)
+    W = (torch.randn((K, N), device="cuda", generator=g) * K ** -0.5).to(torch.bfloat16)
+    Wt8, s = coda.quantize_weight_e4m3(W)
+    Wt8p, sp = coda.quantize_weight_e4m3_packed(W)
+    torch.cuda.synchronize()
+    assert torch.equal(s, sp)
+    assert torch.equal(coda.unpack_e4m3(Wt8p, N), Wt8)
+
+
+@pytest.mark.slow
+def test_full_size_7b_fp8_packed():
+    # the 7B fp8 workload in the benchmark's configuration: quantised on the
+    # device, packed and row-major chains bit-identical
+    M, K, D, N2 = 16384, 4096, 4096, 28672
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    A = torch.randn((M, K), device="cuda", generator=g).to(torch.bfloat16)
+    W1 = (torch.randn((K, D), device="cuda", generator=g) * K ** -0.5).to(torch.bfloat16)
+    W2 = (torch.randn((D, N2), device="cuda", generator=g) * D ** -0.5).to(torch.bfloat16)
+    R = torch.randn((M, D), device="cuda", generator=g).to(torch.bfloat16)
+    gg = (1.0 + 0.1 * torch.randn((D,), device="cuda", generator=g)).to(torch.bfloat16)
+    A8, sa = coda.quantize_rows_e4m3(A)
+    W1t8, sw1 = coda.quantize_weight_e4m3(W1)
+    W2t8, sw2 = coda.quantize_weight_e4m3(W2)
+    W2t8p, sw2p = coda.quantize_weight_e4m3_packed(W2)
+    H, Hg8, r, Y, P = coda.fused_forward_fp8(A8, sa, W1t8, sw1, R, gg, W2t8, sw2, 1e-5)
+    Hp, Hg8p, rp, Yp, Pp = coda.fused_forward_fp8_packed(A8, sa, W1t8, sw1, R, gg, W2t8p, sw2p, 1e-5)
+    torch.cuda.synchronize()
+    assert torch.equal(coda.unpack_e4m3(W2t8p, N2), W2t8)
+    assert torch.equal(coda.unpack_e4m3(Hg8p, M), Hg8)
+    _same(Y, Yp, "Y")

@@ -540,6 +540,99 @@ def quantize_weight_e4m3(W, stream=None, Wt8=None, scales=None):
     return Wt8, sc
 
 
+def packed_empty_e4m3(rows: int, cols: int, device) -> torch.Tensor:
+    """A uint8 buffer for a tile-packed e4m3 [rows, cols] matrix, shaped
+    [ceil(rows/16), cols/16, 16, 16] (row block, 16-code run, row in block, code)."""
+    if cols % 16 != 0:
+        raise ValueError(f"cols = {cols} must be a multiple of 16")
+    return torch.empty(((rows + 15) // 16, cols // 16, 16, 16), device=device, dtype=torch.uint8)
+
+
+def _packed8(Xp: torch.Tensor, name: str, rows: int, cols: int) -> None:
+    if Xp.dtype not in _FP8 or not Xp.is_cuda:
+        raise TypeError(f"{name}: expected a uint8 / float8_e4m3fn CUDA tensor")
+    if tuple(Xp.shape) != ((rows + 15) // 16, cols // 16, 16, 16) or not Xp.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tile-packed buffer of shape "
+                         f"{((rows + 15) // 16, cols // 16, 16, 16)}, got {tuple(Xp.shape)}")
+
+
+def quantize_weight_e4m3_packed(W, stream=None, Wt8p=None, scales=None):
+    """quantize_weight_e4m3 with the transposed codes [N, K] written
+    tile-packed (packed_empty_e4m3(N, K)); returns (Wt8p, scales)."""
+    K, N = W.shape
+    ldw = _mat(W, "W", torch.bfloat16, (K, N))
+    if Wt8p is None:
+        Wt8p = packed_empty_e4m3(N, K, W.device)
+    if scales is None:
+        scales = torch.empty((N,), device=W.device, dtype=torch.float32)
+    _packed8(Wt8p, "Wt8", N, K)
+    _mat(scales, "scales", torch.float32, (N,))
+    st = _lib.load().coda_quantize_cols_e4m3_packed(K, N, W.data_ptr(), ldw, Wt8p.data_ptr(), scales.data_ptr(),
+                                                    _stream(stream))
+    _lib.check("coda_quantize_cols_e4m3_packed", st)
+    return Wt8p, scales
+
+
+def coda_gemm_res_prms_fp8_packed(A8, sa, W1t8, sw1, R, g, H, Hg8p, partials, stream=None) -> None:
+    """coda_gemm_res_prms_fp8 with Hg8 written tile-packed into Hg8p."""
+    lib = _lib.load()
+    M, K = A8.shape
+    D = W1t8.shape[0]
+    T = coda_prms_num_partials(torch.bfloat16, D)
+    lda = _mat8(A8, "A8", (M, K))
+    ldw = _mat8(W1t8, "W1t8", (D, K))
+    _packed8(Hg8p, "Hg8", M, D)
+    _mat(sa, "sa", torch.float32, (M,))
+    _mat(sw1, "sw1", torch.float32, (D,))
+    ldr = _mat(R, "R", torch.bfloat16, (M, D))
+    _mat(g, "g", torch.bfloat16, (D,))
+    ldh = _mat(H, "H", torch.bfloat16, (M, D))
+    _mat(partials, "partials", torch.float32, (T, M))
+    _dense(partials, "partials")
+    st = lib.coda_gemm_res_prms_fp8_packed(M, K, D, A8.data_ptr(), lda, sa.data_ptr(), W1t8.data_ptr(), ldw,
+                                           sw1.data_ptr(), R.data_ptr(), ldr, g.data_ptr(), H.data_ptr(), ldh,
+                                           Hg8p.data_ptr(), partials.data_ptr(), _stream(stream))
+    _lib.check("coda_gemm_res_prms_fp8_packed", st)
+
+
+def coda_gemm_rowscale_fp8_packed(X8p, W2t8p, sw2, r: Optional[torch.Tensor], Y, stream=None) -> None:
+    """coda_gemm_rowscale_fp8 with both operands tile-packed."""
+    lib = _lib.load()
+    M, N2 = Y.shape
+    D = X8p.shape[1] * 16
+    _packed8(X8p, "X8", M, D)
+    _packed8(W2t8p, "W2t8", N2, D)
+    _mat(sw2, "sw2", torch.float32, (N2,))
+    ldy = _mat(Y, "Y", torch.bfloat16, (M, N2))
+    if r is not None:
+        _mat(r, "r", torch.float32, (M,))
+    st = lib.coda_gemm_rowscale_fp8_packed(M, D, N2, X8p.data_ptr(), W2t8p.data_ptr(), sw2.data_ptr(),
+                                           r.data_ptr() if r is not None else None, Y.data_ptr(), ldy,
+                                           _stream(stream))
+    _lib.check("coda_gemm_rowscale_fp8_packed", st)
+
+
+def unpack_e4m3(Xp: torch.Tensor, rows: int) -> torch.Tensor:
+    """The [rows, cols] row-major codes held by a tile-packed e4m3 buffer (a copy)."""
+    nb, nck, _, _ = Xp.shape
+    return Xp.permute(0, 2, 1, 3).reshape(nb * 16, nck * 16)[:rows]
+
+
+def fused_forward_fp8_packed(A8, sa, W1t8, sw1, R, g, W2t8p, sw2, eps: float, stream=None):
+    """The fp8 chain with Hg8 and W2t8 tile-packed: returns (H, Hg8p, r, Y, partials)."""
+    M, D, N2 = A8.shape[0], W1t8.shape[0], sw2.shape[0]
+    dev = A8.device
+    H = torch.empty((M, D), device=dev, dtype=torch.bfloat16)
+    Hg8p = packed_empty_e4m3(M, D, dev)
+    P = torch.empty((coda_prms_num_partials(torch.bfloat16, D), M), device=dev, dtype=torch.float32)
+    r = torch.empty((M,), device=dev, dtype=torch.float32)
+    Y = torch.empty((M, N2), device=dev, dtype=torch.bfloat16)
+    coda_gemm_res_prms_fp8_packed(A8, sa, W1t8, sw1, R, g, H, Hg8p, P, stream)
+    coda_rms_combine(P, r, D, eps, stream)
+    coda_gemm_rowscale_fp8_packed(Hg8p, W2t8p, sw2, r, Y, stream)
+    return H, Hg8p, r, Y, P
+
+
 def quantize_rows_cols_e4m3(X, stream=None):
     """Both e4m3 quantisations of a bf16 activation X [M, N]: the row codes
     (uint8 [M, N]) with their scales [M], and the transposed column codes

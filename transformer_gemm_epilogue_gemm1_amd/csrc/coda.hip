@@ -133,7 +133,11 @@ coda_status launch_gemm(const char* what, int M, int N, int K, const void* a, in
   return launch_status(what);
 }
 
-template <class Epi>
+// Bytes of a tile-packed e4m3 matrix (kp_unit): rows padded to 16, cols / 16 chunks.
+int64_t packed_bytes_e4m3(int64_t rows, int64_t cols) { return (rows + 15) / 16 * 16 * cols; }
+
+// PK: both operands tile-packed, lda / ldb counting 16-byte chunks per row.
+template <class Epi, bool PK = false>
 coda_status launch_gemm_fp8(const char* what, int M, int N, int K, const void* a, int64_t lda, const void* b,
                             int64_t ldb, const typename Epi::Params& ep, hipStream_t s) {
   GemmArgs g;
@@ -145,12 +149,12 @@ coda_status launch_gemm_fp8(const char* what, int M, int N, int K, const void* a
   g.group_m = kGroupM;
   g.a = a;
   g.lda = lda;
-  g.a_span = span_bytes(M, K, lda, 1);
+  g.a_span = PK ? (uint32_t)packed_bytes_e4m3(M, 16 * lda) : span_bytes(M, K, lda, 1);
   g.b = b;
   g.ldb = ldb;
-  g.b_span = span_bytes(N, K, ldb, 1);
+  g.b_span = PK ? (uint32_t)packed_bytes_e4m3(N, 16 * ldb) : span_bytes(N, K, ldb, 1);
   g.b_split = 0;
-  hipLaunchKernelGGL((gemm_fp8_kernel<Epi>), dim3(g.tiles_m * g.tiles_n), dim3(kThreads), 0, s, g, ep);
+  hipLaunchKernelGGL((gemm_fp8_kernel<Epi, PK>), dim3(g.tiles_m * g.tiles_n), dim3(kThreads), 0, s, g, ep);
   return launch_status(what);
 }
 
@@ -353,13 +357,15 @@ void q_rows(const void* X, int64_t ldx, int M, int K, void* X8, int64_t ldx8, fl
   else
     hipLaunchKernelGGL(quantize_long_rows_e4m3_kernel, grid, block, 0, s, x, ldx, K, x8, ldx8, sc);
 }
-void q_cols(const void* W, int64_t ldw, int K, int N, void* Wt8, int64_t ldwt, float* sc, hipStream_t s) {
+// wt_nck > 0: Wt8 written tile-packed with wt_nck chunks per row (K / 16).
+void q_cols(const void* W, int64_t ldw, int K, int N, void* Wt8, int64_t ldwt, float* sc, hipStream_t s,
+            int64_t wt_nck = 0) {
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, (uint32_t*)sc, N, 0u);
   hipLaunchKernelGGL(colmax_kernel, dim3((unsigned)((N + 63) / 64), (unsigned)((K + 255) / 256)), dim3(256), 0, s,
                      (const uint16_t*)W, ldw, K, N, (uint32_t*)sc);
   hipLaunchKernelGGL(quantize_cols_kernel, dim3((unsigned)((N + 127) / 128), (unsigned)((K + 127) / 128)), dim3(256),
                      0, s, (const uint16_t*)W, ldw, K, N, (const uint32_t*)sc, (uint8_t*)Wt8, ldwt,
-                     (const uint32_t*)nullptr, (uint8_t*)nullptr, (int64_t)0);
+                     (const uint32_t*)nullptr, (uint8_t*)nullptr, (int64_t)0, wt_nck);
   hipLaunchKernelGGL(amax_to_scale_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, sc, N);
 }
 // Both quantisations of an activation X [M, N]: row codes X8 [M, N] with
@@ -373,7 +379,7 @@ void q_rows_cols(const void* X, int64_t ldx, int M, int N, void* X8, int64_t ldx
                      s, (const uint16_t*)X, ldx, M, N, (uint32_t*)sr, (uint32_t*)sc);
   hipLaunchKernelGGL(quantize_cols_kernel, dim3((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128)), dim3(256),
                      0, s, (const uint16_t*)X, ldx, M, N, (const uint32_t*)sc, (uint8_t*)Xt8, ldxt,
-                     (const uint32_t*)sr, (uint8_t*)X8, ldx8);
+                     (const uint32_t*)sr, (uint8_t*)X8, ldx8, (int64_t)0);
   hipLaunchKernelGGL(amax_to_scale_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, sr, M);
   hipLaunchKernelGGL(amax_to_scale_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, sc, N);
 }
@@ -795,6 +801,79 @@ coda_status coda_gemm_rowscale_fp8(int64_t M, int64_t D, int64_t N2, const void*
   EpiRowScaleFp8::Params ep{r, sw2, (uint16_t*)Y, ldy};
   return launch_gemm_fp8<EpiRowScaleFp8>("coda_gemm_rowscale_fp8", (int)M, (int)N2, (int)D, X8, ldx, W2t8, ldw2t,
                                          ep, (hipStream_t)stream);
+}
+
+int64_t coda_packed_bytes_e4m3(int64_t rows, int64_t cols) {
+  if (rows < 0 || rows > kMaxDim || cols < 1 || cols > kMaxDim || cols % 16 != 0) return -1;
+  return packed_bytes_e4m3(rows, cols);
+}
+
+coda_status coda_quantize_cols_e4m3_packed(int64_t K, int64_t N, const void* W, int64_t ldw, void* Wt8p,
+                                           float* scales, void* stream) {
+  coda_status st = check_dims_fp8(N, {{"K", K}});
+  if (st != CODA_OK) return st;
+  if (N == 0) return ok();
+  if (N % 16 != 0) return fail(CODA_ERR_SHAPE, "N = %lld is not a multiple of 16", (long long)N);
+  if (K > kMaxColRows) return fail(CODA_ERR_SHAPE, "K = %lld exceeds %lld rows", (long long)K, (long long)kMaxColRows);
+  const int64_t wt_bytes = packed_bytes_e4m3(N, K);
+  const Mat mW{W, K, N, ldw, 2, "W"}, mWt{Wt8p, 1, wt_bytes, wt_bytes, 1, "Wt8"}, ms{scales, 1, N, N, 4, "scales"};
+  if ((st = check_mat(mW, 8)) != CODA_OK || (st = check_mat(mWt, 16)) != CODA_OK) return st;
+  if (scales == nullptr) return fail(CODA_ERR_NULL, "scales is NULL");
+  if (((uintptr_t)scales & 3) != 0) return fail(CODA_ERR_ALIGN, "scales is not 4-byte aligned");
+  const Mat outs[2] = {mWt, ms};
+  if ((st = check_alias(outs, 2, &mW, 1)) != CODA_OK) return st;
+  q_cols(W, ldw, (int)K, (int)N, Wt8p, K, scales, (hipStream_t)stream, K / 16);
+  return launch_status("coda_quantize_cols_e4m3_packed");
+}
+
+coda_status coda_gemm_res_prms_fp8_packed(int64_t M, int64_t K, int64_t D, const void* A8, int64_t lda,
+                                          const float* sa, const void* W1t8, int64_t ldw1t, const float* sw1,
+                                          const void* R, int64_t ldr, const void* g, void* H, int64_t ldh,
+                                          void* Hg8p, float* partials, void* stream) {
+  coda_status st = check_dims_fp8(M, {{"K", K}, {"D", D}});
+  if (st != CODA_OK) return st;
+  if (M == 0) return ok();
+  const int64_t T = num_partials(D);
+  const int64_t hg_bytes = packed_bytes_e4m3(M, D);
+  const Mat mA{A8, M, K, lda, 1, "A8"}, mW{W1t8, D, K, ldw1t, 1, "W1t8"}, mR{R, M, D, ldr, 2, "R"};
+  const Mat mg{g, 1, D, D, 2, "g"}, mH{H, M, D, ldh, 2, "H"}, mHg{Hg8p, 1, hg_bytes, hg_bytes, 1, "Hg8"};
+  const Mat mP{partials, T, M, M, 4, "partials"}, msa{sa, 1, M, M, 4, "sa"}, msw{sw1, 1, D, D, 4, "sw1"};
+  for (const Mat* m : {&mA, &mW, &mHg})
+    if ((st = check_mat(*m, 16)) != CODA_OK) return st;
+  for (const Mat* m : {&mR, &mg, &mH})
+    if ((st = check_mat(*m, 8)) != CODA_OK) return st;
+  if ((st = check_vec(sa, M, 4, "sa")) != CODA_OK || (st = check_vec(sw1, D, 16, "sw1")) != CODA_OK) return st;
+  if (partials == nullptr) return fail(CODA_ERR_NULL, "partials is NULL");
+  if (((uintptr_t)partials & 3) != 0) return fail(CODA_ERR_ALIGN, "partials is not 4-byte aligned");
+  if (mP.span() > kMaxSpan) return fail(CODA_ERR_SHAPE, "partials span too large");
+  const Mat outs[3] = {mH, mHg, mP};
+  const Mat ins[6] = {mA, mW, mR, mg, msa, msw};
+  if ((st = check_alias(outs, 3, ins, 6)) != CODA_OK) return st;
+  EpiResPrmsFp8::Params ep{sa, sw1, (const uint16_t*)R, ldr, (const uint16_t*)g, (uint16_t*)H, ldh,
+                           (uint8_t*)Hg8p, 0, partials, D / 16};
+  return launch_gemm_fp8<EpiResPrmsFp8>("coda_gemm_res_prms_fp8_packed", (int)M, (int)D, (int)K, A8, lda, W1t8,
+                                        ldw1t, ep, (hipStream_t)stream);
+}
+
+coda_status coda_gemm_rowscale_fp8_packed(int64_t M, int64_t D, int64_t N2, const void* X8p, const void* W2t8p,
+                                          const float* sw2, const float* r, void* Y, int64_t ldy, void* stream) {
+  coda_status st = check_dims_fp8(M, {{"D", D}, {"N2", N2}});
+  if (st != CODA_OK) return st;
+  if (M == 0) return ok();
+  const int64_t x_bytes = packed_bytes_e4m3(M, D), w_bytes = packed_bytes_e4m3(N2, D);
+  const Mat mX{X8p, 1, x_bytes, x_bytes, 1, "X8"}, mW{W2t8p, 1, w_bytes, w_bytes, 1, "W2t8"};
+  const Mat mY{Y, M, N2, ldy, 2, "Y"}, mr{r, 1, M, M, 4, "r"}, msw{sw2, 1, N2, N2, 4, "sw2"};
+  for (const Mat* m : {&mX, &mW})
+    if ((st = check_mat(*m, 16)) != CODA_OK) return st;
+  if ((st = check_mat(mY, 8)) != CODA_OK) return st;
+  if ((st = check_vec(sw2, N2, 16, "sw2")) != CODA_OK) return st;
+  if (r != nullptr && ((uintptr_t)r & 3) != 0) return fail(CODA_ERR_ALIGN, "r is not 4-byte aligned");
+  const Mat none{nullptr, 0, 0, 0, 4, ""};
+  const Mat ins[4] = {mX, mW, msw, r ? mr : none};
+  if ((st = check_alias(&mY, 1, ins, 4)) != CODA_OK) return st;
+  EpiRowScaleFp8::Params ep{r, sw2, (uint16_t*)Y, ldy};
+  return launch_gemm_fp8<EpiRowScaleFp8, true>("coda_gemm_rowscale_fp8_packed", (int)M, (int)N2, (int)D, X8p,
+                                               D / 16, W2t8p, D / 16, ep, (hipStream_t)stream);
 }
 
 coda_status coda_gemm_rowscale_lse(coda_dtype dt, int64_t M, int64_t D, int64_t V, const void* X, int64_t ldx,

@@ -56,6 +56,7 @@ struct EpiResPrmsFp8 {
     uint8_t* Hg8;       // e4m3
     int64_t ldhg;
     float* partials;    // [T][M]
+    int64_t hg_nck;     // > 0: Hg8 is tile-packed (kp_unit) with hg_nck 16-byte chunks per row
   };
   Params p;
   RowChunks<uint16_t> rc;
@@ -89,7 +90,9 @@ struct EpiResPrmsFp8 {
     Chunk8<uint16_t>::store(p.H + (int64_t)row * p.ldh + col, h);
     const uint32_t lo = pack_e4m3x4(h[0] * gv[0], h[1] * gv[1], h[2] * gv[2], h[3] * gv[3]);
     const uint32_t hi = pack_e4m3x4(h[4] * gv[4], h[5] * gv[5], h[6] * gv[6], h[7] * gv[7]);
-    *(u32x2*)(p.Hg8 + (int64_t)row * p.ldhg + col) = u32x2{lo, hi};
+    uint8_t* dst = p.hg_nck > 0 ? p.Hg8 + kp_unit(row, col >> 4, p.hg_nck) * 16 + (col & 15)
+                                : p.Hg8 + (int64_t)row * p.ldhg + col;
+    *(u32x2*)dst = u32x2{lo, hi};
   }
 
   __device__ __forceinline__ void end_slab(int, int slab_row0) {

@@ -247,7 +247,8 @@ __global__ __launch_bounds__(256) void quantize_cols_kernel(const uint16_t* __re
                                                             int N, const uint32_t* __restrict__ amax,
                                                             uint8_t* __restrict__ Wt8, int64_t ldwt,
                                                             const uint32_t* __restrict__ rmax,
-                                                            uint8_t* __restrict__ X8, int64_t ldx8) {
+                                                            uint8_t* __restrict__ X8, int64_t ldx8,
+                                                            int64_t wt_nck) {
   constexpr int kPitch = 33;  // words per tile row: 128 codes + 4 bytes of padding
   __shared__ uint32_t tile[128 * kPitch];
   __shared__ E4m3Divider coldiv[128], rowdiv[128];
@@ -293,8 +294,12 @@ __global__ __launch_bounds__(256) void quantize_cols_kernel(const uint16_t* __re
       for (int j = 0; j < 4; ++j) out[j][g] = o[j];
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *(u32x4*)(Wt8 + (int64_t)(n0 + 4 * cg + j) * ldwt + k0 + kc) = u32x4{out[j][0], out[j][1], out[j][2], out[j][3]};
+    for (int j = 0; j < 4; ++j) {
+      // wt_nck > 0: Wt8 tile-packed (kp_unit), 16 codes = one 16-byte unit
+      uint8_t* dst = wt_nck > 0 ? Wt8 + kp_unit(n0 + 4 * cg + j, (k0 + kc) >> 4, wt_nck) * 16
+                                : Wt8 + (int64_t)(n0 + 4 * cg + j) * ldwt + k0 + kc;
+      *(u32x4*)dst = u32x4{out[j][0], out[j][1], out[j][2], out[j][3]};
+    }
   }
 }
 
