@@ -719,22 +719,27 @@ def bench_swiglu(args, up, stream, with_backward):
     r = torch.empty((M,), device=dev, dtype=torch.float32)
     Z = torch.empty((M, F), device=dev, dtype=tdt)
     Y = torch.empty((M, N2), device=dev, dtype=tdt)
+    Hgp = coda.packed_empty(M, D, dev)
 
-    def fwd(keep_y):
-        coda.coda_gemm_res_prms(d["A"], d["W1"], d["R"], d["g"], H, Hg, P, stream)
+    def fwd(keep_y):  # Hg tile-packed between the GEMMs, as the headline chain
+        coda.coda_gemm_res_prms_packed(d["A"], d["W1"], d["R"], d["g"], H, Hgp, P, stream)
         coda.coda_rms_combine(P, r, D, wl.eps, stream)
-        coda.coda_gemm_rowscale_swiglu(Hg, d["W2"], r, Z, Y if keep_y else None, stream)
+        coda.coda_gemm_rowscale_swiglu_packed(Hgp, d["W2"], r, Z, Y if keep_y else None, stream)
 
     n = max(5, args.steps // 2)
     w = max(2, args.warmup // 2)
-    fwd_ms = time_ms(lambda: fwd(False), stream, n, w)
-    gated_ms = time_ms(lambda: coda.coda_gemm_rowscale_swiglu(Hg, d["W2"], r, Z, None, stream), stream, n, w)
-    plain_ms = time_ms(lambda: coda.coda_gemm_rowscale(Hg, d["W2"], r, Y, stream), stream, n, w)
-    out = {"workload": f"7b-bf16 with the gate: M={M} K={K} D={D} F={F} (W2 {D}x{N2} = gate|up)",
+    fwd(False)
+    coda.coda_gemm_res_prms(d["A"], d["W1"], d["R"], d["g"], H, Hg, P, stream)  # row-major Hg for the comparisons
+    fwd_ms, gated_ms, gated_rm_ms, plain_ms = time_ms_alternating(
+        [lambda: fwd(False), lambda: coda.coda_gemm_rowscale_swiglu_packed(Hgp, d["W2"], r, Z, None, stream),
+         lambda: coda.coda_gemm_rowscale_swiglu(Hg, d["W2"], r, Z, None, stream),
+         lambda: coda.coda_gemm_rowscale_packed(Hgp, d["W2"], r, Y, stream)], stream, n, w)
+    out = {"workload": f"7b-bf16 with the gate: M={M} K={K} D={D} F={F} (W2 {D}x{N2} = gate|up), Hg tile-packed",
            "forward_ms": round(fwd_ms, 4),
            "forward_tflops": round(wl.fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
-           "coda_gemm_rowscale_swiglu_ms": round(gated_ms, 4),
-           "coda_gemm_rowscale_same_inputs_ms": round(plain_ms, 4)}
+           "coda_gemm_rowscale_swiglu_packed_ms": round(gated_ms, 4),
+           "coda_gemm_rowscale_swiglu_row_major_hg_ms": round(gated_rm_ms, 4),
+           "coda_gemm_rowscale_packed_same_inputs_ms": round(plain_ms, 4)}
     gf = d["g"].float()
     if not args.no_torch_chain:
         def torch_fwd():
@@ -807,11 +812,17 @@ def bench_backward(args, up, stream):
     dW2 = torch.empty((D, N2), device=dev, dtype=tdt)
     dg = torch.empty((D,), device=dev, dtype=torch.float32)
     ws = torch.empty((coda.coda_chain_bwd_workspace_bytes(tdt, M, K, D, N2),), device=dev, dtype=torch.uint8)
+    Hgp = coda.packed_empty(M, D, dev) if tdt == torch.bfloat16 else None
 
-    def fwd():
-        coda.coda_gemm_res_prms(d["A"], d["W1"], d["R"], d["g"], H, Hg, P, stream)
-        coda.coda_rms_combine(P, r, D, wl.eps, stream)
-        coda.coda_gemm_rowscale(Hg, d["W2"], r, Y, stream)
+    def fwd():  # the headline's forward (Hg tile-packed for bf16)
+        if Hgp is not None:
+            coda.coda_gemm_res_prms_packed(d["A"], d["W1"], d["R"], d["g"], H, Hgp, P, stream)
+            coda.coda_rms_combine(P, r, D, wl.eps, stream)
+            coda.coda_gemm_rowscale_packed(Hgp, d["W2"], r, Y, stream)
+        else:
+            coda.coda_gemm_res_prms(d["A"], d["W1"], d["R"], d["g"], H, Hg, P, stream)
+            coda.coda_rms_combine(P, r, D, wl.eps, stream)
+            coda.coda_gemm_rowscale(Hg, d["W2"], r, Y, stream)
 
     def bwd():
         coda.coda_chain_bwd(d["dY"], d["A"], d["W1"], d["g"], d["W2"], H, r, dA, dR, dW1, dW2, dg, ws, stream)

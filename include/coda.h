@@ -163,6 +163,16 @@ coda_status coda_gemm_rowscale_swiglu(coda_dtype dt, int64_t M, int64_t D, int64
                                       void* Z, int64_t ldz,
                                       void* Y, int64_t ldy, void* stream);
 
+/* coda_gemm_rowscale_swiglu (bfloat16) reading X = Hg tile-packed (Xp, as
+ * written by coda_gemm_res_prms_packed for the same M and D).  Z and Y are
+ * bit-identical to coda_gemm_rowscale_swiglu's. */
+coda_status coda_gemm_rowscale_swiglu_packed(int64_t M, int64_t D, int64_t F,
+                                             const void* Xp,
+                                             const void* W2, int64_t ldw2,
+                                             const float* r,
+                                             void* Z, int64_t ldz,
+                                             void* Y, int64_t ldy, void* stream);
+
 /* Backward through the SwiGLU gate (the article's results section measures
  * the SwiGLU backward; the formula is the derivative of the reading above):
  * with s = sigmoid(Y_gate),

@@ -496,6 +496,43 @@ def fused_forward_swiglu(A, W1, R, g, W2, eps: float, keep_y: bool = False, stre
     return H, Hg, r, Z, Y
 
 
+def coda_gemm_rowscale_swiglu_packed(Xp, W2, r: Optional[torch.Tensor], Z, Y: Optional[torch.Tensor] = None,
+                                     stream=None) -> None:
+    """coda_gemm_rowscale_swiglu with X tile-packed in Xp (as coda_gemm_res_prms_packed writes it)."""
+    lib = _lib.load()
+    M, F = Z.shape
+    D, F2 = W2.shape
+    if F2 != 2 * F:
+        raise ValueError("W2 must have 2F columns (gate | up)")
+    _packed(Xp, "X", M, D)
+    ldw2 = _mat(W2, "W2", torch.bfloat16, (D, F2))
+    ldz = _mat(Z, "Z", torch.bfloat16, (M, F))
+    ldy = _mat(Y, "Y", torch.bfloat16, (M, F2)) if Y is not None else 0
+    if r is not None:
+        _mat(r, "r", torch.float32, (M,))
+    st = lib.coda_gemm_rowscale_swiglu_packed(M, D, F, Xp.data_ptr(), W2.data_ptr(), ldw2,
+                                              r.data_ptr() if r is not None else None, Z.data_ptr(), ldz,
+                                              Y.data_ptr() if Y is not None else None, ldy, _stream(stream))
+    _lib.check("coda_gemm_rowscale_swiglu_packed", st)
+
+
+def fused_forward_swiglu_packed(A, W1, R, g, W2, eps: float, keep_y: bool = False, stream=None):
+    """fused_forward_swiglu with Hg tile-packed between the GEMMs: returns
+    (H, Hgp, r, Z, Y) with Y None unless keep_y."""
+    M, D, F2 = A.shape[0], W1.shape[1], W2.shape[1]
+    dev, dt = A.device, A.dtype
+    H = torch.empty((M, D), device=dev, dtype=dt)
+    Hgp = packed_empty(M, D, dev)
+    P = torch.empty((coda_prms_num_partials(dt, D), M), device=dev, dtype=torch.float32)
+    r = torch.empty((M,), device=dev, dtype=torch.float32)
+    Z = torch.empty((M, F2 // 2), device=dev, dtype=dt)
+    Y = torch.empty((M, F2), device=dev, dtype=dt) if keep_y else None
+    coda_gemm_res_prms_packed(A, W1, R, g, H, Hgp, P, stream)
+    coda_rms_combine(P, r, D, eps, stream)
+    coda_gemm_rowscale_swiglu_packed(Hgp, W2, r, Z, Y, stream)
+    return H, Hgp, r, Z, Y
+
+
 def fused_backward_swiglu(dZ, Y, A, W1, g, W2, H, r, stream=None):
     """Backward of the chain with the SwiGLU gate: dY through the gate, then
     the chain's backward; returns (dA, dR, dW1, dW2, dg, dY)."""

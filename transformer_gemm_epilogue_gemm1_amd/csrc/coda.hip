@@ -220,6 +220,14 @@ coda_status gemm_rowscale_swiglu_impl(int M, int D, int F, const void* X, int64_
                                                    s, F);
 }
 
+coda_status gemm_rowscale_swiglu_packed_impl(int M, int D, int F, const void* Xp, const void* W2, int64_t ldw2,
+                                             const float* r, void* Z, int64_t ldz, void* Y, int64_t ldy,
+                                             hipStream_t s) {
+  typename EpiSwiGLU<uint16_t>::Params ep{r, (uint16_t*)Z, ldz, (uint16_t*)Y, ldy, F};
+  return launch_gemm<uint16_t, true, false, EpiSwiGLU<uint16_t>, true>("coda_gemm_rowscale_swiglu_packed", M, 2 * F,
+                                                                       D, Xp, D / 8, W2, ldw2, ep, s, F);
+}
+
 coda_status combine_impl(int M, int D, int T, float eps, const float* partials, float* r, hipStream_t s) {
   hipLaunchKernelGGL(rms_combine_kernel, dim3((M + 63) / 64), dim3(256), 0, s, partials, r, M, T, D, eps);
   return launch_status("coda_rms_combine");
@@ -604,6 +612,30 @@ coda_status coda_gemm_rowscale_swiglu(coda_dtype dt, int64_t M, int64_t D, int64
   if (dt == CODA_BF16)
     return gemm_rowscale_swiglu_impl<uint16_t>((int)M, (int)D, (int)F, X, ldx, W2, ldw2, r, Z, ldz, Y, ldy, s);
   return gemm_rowscale_swiglu_impl<float>((int)M, (int)D, (int)F, X, ldx, W2, ldw2, r, Z, ldz, Y, ldy, s);
+}
+
+coda_status coda_gemm_rowscale_swiglu_packed(int64_t M, int64_t D, int64_t F, const void* Xp, const void* W2,
+                                             int64_t ldw2, const float* r, void* Z, int64_t ldz, void* Y,
+                                             int64_t ldy, void* stream) {
+  coda_status st = check_dims(CODA_BF16, M, {{"D", D}, {"F", F}});
+  if (st != CODA_OK) return st;
+  if (2 * F > kMaxDim) return fail(CODA_ERR_SHAPE, "2F = %lld out of range", (long long)(2 * F));
+  if (F % kSwiGLURun != 0) return fail(CODA_ERR_SHAPE, "F = %lld is not a multiple of %d", (long long)F, kSwiGLURun);
+  if (M == 0) return ok();
+  const int es = 2, E = 8;
+  const int64_t x_elems = packed_bytes(M, D) / 2;
+  const Mat mX{Xp, 1, x_elems, x_elems, es, "X"}, mW2{W2, D, 2 * F, ldw2, es, "W2"}, mZ{Z, M, F, ldz, es, "Z"};
+  const Mat mY{Y, M, 2 * F, ldy, es, "Y"}, mr{r, 1, M, M, 4, "r"};
+  for (const Mat* m : {&mX, &mW2, &mZ})
+    if ((st = check_mat(*m, E)) != CODA_OK) return st;
+  if (Y != nullptr && (st = check_mat(mY, E)) != CODA_OK) return st;
+  if (r != nullptr && ((uintptr_t)r & 3) != 0) return fail(CODA_ERR_ALIGN, "r is not 4-byte aligned");
+  const Mat none{nullptr, 0, 0, 0, es, ""};
+  const Mat outs[2] = {mZ, Y ? mY : none};
+  const Mat ins[3] = {mX, mW2, r ? mr : none};
+  if ((st = check_alias(outs, 2, ins, 3)) != CODA_OK) return st;
+  return gemm_rowscale_swiglu_packed_impl((int)M, (int)D, (int)F, Xp, W2, ldw2, r, Z, ldz, Y, ldy,
+                                          (hipStream_t)stream);
 }
 
 coda_status coda_swiglu_bwd(coda_dtype dt, int64_t M, int64_t F, const void* dZ, int64_t ldz, const void* Y,
