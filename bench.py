@@ -177,16 +177,36 @@ def time_ms_alternating(fns, stream, n, warmup, reps=3):
     return best
 
 
-def _smi_sample():
-    """(socket power W, mean gfx clock MHz) from one amd-smi reading, or None."""
+def _amd_smi_cmd():
+    """The command that runs amd-smi, or None.  amd-smi is a Python script
+    started through `/usr/bin/env python3`; it is run with this interpreter
+    directly so that no process replaces itself with another (under a
+    profiler's preloaded library that hop would come after GPU init)."""
     import shutil
-    import subprocess
 
     exe = shutil.which("amd-smi")
     if exe is None:
         return None
     try:
-        res = subprocess.run([exe, "metric", "-p", "-c", "--json"], capture_output=True, text=True, timeout=10)
+        with open(exe, "rb") as f:
+            first = f.readline()
+    except OSError:
+        return None
+    if b"python" not in first:
+        return [exe]
+    py = shutil.which("python3") or sys.executable  # the interpreter `env python3` would pick
+    return [py, os.path.realpath(exe)]
+
+
+def _smi_sample():
+    """(socket power W, mean gfx clock MHz) from one amd-smi reading, or None."""
+    import subprocess
+
+    cmd = _amd_smi_cmd()
+    if cmd is None:
+        return None
+    try:
+        res = subprocess.run(cmd + ["metric", "-p", "-c", "--json"], capture_output=True, text=True, timeout=10)
         d = json.loads(res.stdout)
     except Exception:
         return None
@@ -205,14 +225,13 @@ def _smi_sample():
 
 def _smi_market_name():
     """The device's marketing name from amd-smi's static ASIC data, or None."""
-    import shutil
     import subprocess
 
-    exe = shutil.which("amd-smi")
-    if exe is None:
+    cmd = _amd_smi_cmd()
+    if cmd is None:
         return None
     try:
-        res = subprocess.run([exe, "static", "--asic", "--json"], capture_output=True, text=True, timeout=10)
+        res = subprocess.run(cmd + ["static", "--asic", "--json"], capture_output=True, text=True, timeout=10)
         d = json.loads(res.stdout)
     except Exception:
         return None
