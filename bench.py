@@ -361,27 +361,35 @@ def bench_ce(args, up, stream):
     lse = torch.empty_like(tgt)
     loss = torch.empty_like(tgt)
     Y = torch.empty((M, V), device=dev, dtype=tdt)
+    Hgp = coda.packed_empty(M, D, dev)
 
     def head():
-        coda.coda_gemm_res_prms(d["A"], d["W1"], d["R"], d["g"], H, Hg, P, stream)
+        coda.coda_gemm_res_prms_packed(d["A"], d["W1"], d["R"], d["g"], H, Hgp, P, stream)
         coda.coda_rms_combine(P, r, D, wl.eps, stream)
 
     def fused():
         head()
+        coda.coda_gemm_rowscale_lse_packed(Hgp, d["W2"], r, targets, pmax, psum, tgt, stream)
+        coda.coda_ce_combine(pmax, psum, tgt, targets, lse, loss, V, stream)
+
+    def fused_row_major():
+        coda.coda_gemm_res_prms(d["A"], d["W1"], d["R"], d["g"], H, Hg, P, stream)
+        coda.coda_rms_combine(P, r, D, wl.eps, stream)
         coda.coda_gemm_rowscale_lse(Hg, d["W2"], r, targets, pmax, psum, tgt, stream)
         coda.coda_ce_combine(pmax, psum, tgt, targets, lse, loss, V, stream)
 
     def logits_then_torch():
         head()
-        coda.coda_gemm_rowscale(Hg, d["W2"], r, Y, stream)
+        coda.coda_gemm_rowscale_packed(Hgp, d["W2"], r, Y, stream)
         return torch.nn.functional.cross_entropy(Y.float(), targets.long(), reduction="none")
 
     n = max(5, args.steps // 2)
     w = max(2, args.warmup // 2)
-    f_ms = time_ms(fused, stream, n, w)
+    f_ms, fr_ms = time_ms_alternating([fused, fused_row_major], stream, n, w)
     l_ms = time_ms(logits_then_torch, stream, n, w)
-    out = {"workload": f"7b-ce-bf16: M={M} K={K} D={D} vocabulary V={V}, per-token loss",
+    out = {"workload": f"7b-ce-bf16: M={M} K={K} D={D} vocabulary V={V}, per-token loss, Hg tile-packed",
            "fused_ms": round(f_ms, 4), "fused_tflops": round(wl.fwd_flops / (f_ms * 1e-3) / 1e12, 2),
+           "fused_hg_row_major_ms": round(fr_ms, 4),
            "logits_then_torch_ce_ms": round(l_ms, 4), "speedup_vs_logits_then_torch_ce": round(l_ms / f_ms, 4)}
     if not args.no_torch_chain:
         gf = d["g"].float()
@@ -411,7 +419,7 @@ def bench_ce(args, up, stream):
 
         def train():
             fused()
-            coda.coda_gemm_rowscale_ce_bwd(Hg, d["W2"], r, targets, lse, dloss, dY, stream)
+            coda.coda_gemm_rowscale_ce_bwd_packed(Hgp, d["W2"], r, targets, lse, dloss, dY, stream)
             coda.coda_chain_bwd(dY, d["A"], d["W1"], d["g"], d["W2"], H, r, dA, dR, dW1, dWv, dg, ws, stream)
 
         tr_ms = time_ms(train, stream, n, w)
@@ -493,20 +501,26 @@ def bench_rope(args, up, stream):
     P = torch.empty((coda.coda_prms_num_partials(tdt, D), M), device=dev, dtype=torch.float32)
     r = torch.empty((M,), device=dev, dtype=torch.float32)
     Y = torch.empty((M, N2), device=dev, dtype=tdt)
+    Hgp = coda.packed_empty(M, D, dev)
     csp = cs[pos.long()]  # [M, dh/2, 2], gathered once outside the timed region
     c, s = csp[:, None, :, 0], csp[:, None, :, 1]
 
     def head():
-        coda.coda_gemm_res_prms(d["A"], d["W1"], d["R"], d["g"], H, Hg, P, stream)
+        coda.coda_gemm_res_prms_packed(d["A"], d["W1"], d["R"], d["g"], H, Hgp, P, stream)
         coda.coda_rms_combine(P, r, D, wl.eps, stream)
 
     def fused():
         head()
+        coda.coda_gemm_rowscale_rope_packed(Hgp, d["W2"], r, pos, cs, nq, nk, dh, Y, stream)
+
+    def fused_row_major():
+        coda.coda_gemm_res_prms(d["A"], d["W1"], d["R"], d["g"], H, Hg, P, stream)
+        coda.coda_rms_combine(P, r, D, wl.eps, stream)
         coda.coda_gemm_rowscale_rope(Hg, d["W2"], r, pos, cs, nq, nk, dh, Y, stream)
 
     def plain():
         head()
-        coda.coda_gemm_rowscale(Hg, d["W2"], r, Y, stream)
+        coda.coda_gemm_rowscale_packed(Hgp, d["W2"], r, Y, stream)
 
     def torch_rope(y):
         q = y[:, :nrot].view(M, nrot // dh, dh // 2, 2).float()
@@ -520,9 +534,11 @@ def bench_rope(args, up, stream):
 
     n = max(5, args.steps // 2)
     w = max(2, args.warmup // 2)
-    f_ms, p_ms, u_ms = time_ms_alternating([fused, plain, proj_then_torch], stream, n, w)
-    out = {"workload": f"7b-rope-bf16: M={M} K={K} D={D} QKV N2={N2} (32+32+32 heads of 128), positions row mod 2048",
+    f_ms, fr_ms, p_ms, u_ms = time_ms_alternating([fused, fused_row_major, plain, proj_then_torch], stream, n, w)
+    out = {"workload": f"7b-rope-bf16: M={M} K={K} D={D} QKV N2={N2} (32+32+32 heads of 128), positions row mod 2048,"
+                       " Hg tile-packed",
            "fused_ms": round(f_ms, 4), "fused_tflops": round(wl.fwd_flops / (f_ms * 1e-3) / 1e12, 2),
+           "fused_hg_row_major_ms": round(fr_ms, 4),
            "no_rope_ms": round(p_ms, 4), "rope_epilogue_overhead": round(f_ms / p_ms - 1.0, 4),
            "projection_then_torch_rope_ms": round(u_ms, 4),
            "speedup_vs_projection_then_torch_rope": round(u_ms / f_ms, 4)}

@@ -208,6 +208,14 @@ coda_status coda_gemm_rowscale_lse(coda_dtype dt, int64_t M, int64_t D, int64_t 
                                    const float* r, const int32_t* targets,
                                    float* pmax, float* psum, float* tgt, void* stream);
 
+/* coda_gemm_rowscale_lse (bfloat16) reading X = Hg tile-packed (Xp, as
+ * written by coda_gemm_res_prms_packed for the same M and D).  pmax, psum and
+ * tgt are bit-identical to coda_gemm_rowscale_lse's. */
+coda_status coda_gemm_rowscale_lse_packed(int64_t M, int64_t D, int64_t V,
+                                          const void* Xp, const void* Wv, int64_t ldw,
+                                          const float* r, const int32_t* targets,
+                                          float* pmax, float* psum, float* tgt, void* stream);
+
 /* Cross-entropy combine: lse_i = M_i + log(sum_t psum[t*M+i] e^(pmax[t*M+i] - M_i))
  * with M_i = max_t pmax, merged in a fixed order (four quarters of t, each in
  * increasing t, then first to last); loss_i = lse_i - tgt[i], or NaN when
@@ -254,6 +262,16 @@ coda_status coda_gemm_rowscale_rope(coda_dtype dt, int64_t M, int64_t D, int64_t
                                     int64_t n_q, int64_t n_k, int64_t d_head,
                                     void* Y, int64_t ldy, void* stream);
 
+/* coda_gemm_rowscale_rope (bfloat16) reading X = Hg tile-packed (Xp, as
+ * written by coda_gemm_res_prms_packed for the same M and D).  Y is
+ * bit-identical to coda_gemm_rowscale_rope's. */
+coda_status coda_gemm_rowscale_rope_packed(int64_t M, int64_t D, int64_t N2,
+                                           const void* Xp, const void* W2, int64_t ldw2,
+                                           const float* r, const int32_t* positions,
+                                           const float* cos_sin, int64_t max_pos,
+                                           int64_t n_q, int64_t n_k, int64_t d_head,
+                                           void* Y, int64_t ldy, void* stream);
+
 /* Backward through RoPE (the derivative of the reading above; the rotation
  * is orthogonal, so the gradient turns back by the same angle):
  *   dY_m,2i = g_2i cos + g_2i+1 sin,   dY_m,2i+1 = g_2i+1 cos - g_2i sin
@@ -279,6 +297,15 @@ coda_status coda_gemm_rowscale_ce_bwd(coda_dtype dt, int64_t M, int64_t D, int64
                                       const void* X, int64_t ldx, const void* Wv, int64_t ldw,
                                       const float* r, const int32_t* targets, const float* lse,
                                       const float* dloss, void* dY, int64_t lddy, void* stream);
+
+/* coda_gemm_rowscale_ce_bwd (bfloat16) reading X = Hg tile-packed (Xp, as
+ * written by coda_gemm_res_prms_packed for the same M and D).  dY is
+ * bit-identical to coda_gemm_rowscale_ce_bwd's. */
+coda_status coda_gemm_rowscale_ce_bwd_packed(int64_t M, int64_t D, int64_t V,
+                                             const void* Xp, const void* Wv, int64_t ldw,
+                                             const float* r, const int32_t* targets,
+                                             const float* lse, const float* dloss,
+                                             void* dY, int64_t lddy, void* stream);
 
 /* ---- fp8 operands -------------------------------------------------------
  * The article's opening section notes that FP8 makes the matrix products

@@ -627,3 +627,33 @@ def test_fp8_packed_validation(lib):
     assert lib.coda_gemm_rowscale_fp8_packed(300, 256, 512, None, W2_, DG_, R2_, Y_, 512, None) == NULL
     assert lib.coda_gemm_rowscale_fp8_packed(300, 256, 512, HG_, W2_, DG_, R2_, HG_ + 16, 512, None) == ALIAS
     assert lib.coda_gemm_rowscale_fp8_packed(0, 256, 512, None, None, None, None, None, 512, None) == OK
+
+
+def test_lse_ce_rope_packed_validation(lib):
+    # LM head with the cross-entropy statistics: M=300, D=512, V=1000
+    lse = lambda **k: lib.coda_gemm_rowscale_lse_packed(
+        k.get("M", 300), k.get("D", 512), k.get("V", 1000), k.get("Xp", HG_), W2_, 1000, R2_,
+        k.get("t", DY_), k.get("pmax", DA_), DR_, DW1_, None)
+    assert lse(V=1001) == SHAPE
+    assert lse(Xp=None) == NULL
+    assert lse(t=None) == NULL
+    assert lse(Xp=HG_ + 4) == ALIGN
+    assert lse(pmax=HG_ + 256) == ALIAS          # statistics written over the packed Hg
+    assert lse(M=0, Xp=None, t=None, pmax=None) == OK
+    # its backward
+    ce = lambda **k: lib.coda_gemm_rowscale_ce_bwd_packed(
+        300, k.get("D", 512), 1000, k.get("Xp", HG_), W2_, 1000, R2_, DY_, DA_, DR_, k.get("dY", Y_),
+        k.get("lddy", 1000), None)
+    assert ce(D=12) == SHAPE
+    assert ce(Xp=None) == NULL
+    assert ce(lddy=999) == SHAPE
+    assert ce(dY=HG_ + 1024) == ALIAS
+    # QKV projection with RoPE: N2=1040, n_q=512, n_k=256, d_head=64, max_pos=4096
+    rope = lambda **k: lib.coda_gemm_rowscale_rope_packed(
+        300, 384, 1040, k.get("Xp", HG_), W2_, 1040, R2_, DY_, k.get("cs", DA_), 4096, k.get("nq", 512), 256, 64,
+        k.get("Y", Y_), 1040, None)
+    assert rope(nq=500) == SHAPE
+    assert rope(Xp=None) == NULL
+    assert rope(cs=None) == NULL
+    assert rope(Xp=HG_ + 8) == ALIGN
+    assert rope(Y=HG_ + 512) == ALIAS

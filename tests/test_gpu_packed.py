@@ -10,7 +10,10 @@ oracle (the plain chain of the CODA news article by Synced, epilogue
 section) with the bf16 bar of 1e-2.  Shapes include ragged M (padding rows
 in the last block), D not a multiple of the 32-column k-tile, and the full
 7B workload in the benchmark's launch configuration (sampled rows against
-the oracle).
+the oracle).  The same bit-identity holds for the other second GEMMs on the
+packed Hg (SwiGLU, the LM head with the cross-entropy statistics and its
+backward, the QKV projection with RoPE) and for the fp8 chain with both
+second-GEMM operands packed; each is also checked against the oracle.
 """
 import sys
 
@@ -237,3 +240,105 @@ def test_swiglu_packed_matches_row_major(shape):
     err = max_rel(host_f32(Zp), orc["Z"])
     print(f"{shape}: packed SwiGLU Z error {err:.3e}")
     assert err <= 1e-2
+
+
+# ---- the LM-head (cross-entropy) and QKV (RoPE) second GEMMs on the packed Hg ----
+CE_SHAPES = [(3, 136, 264, 520), (257, 256, 512, 1000), (300, 512, 384, 2056)]  # M, K, D, V
+
+
+def _ce_pair(wl, seed):
+    x = ci.make_inputs(wl, seed=seed)
+    t = ci.make_targets(wl, seed=seed)
+    d = {k: dev(v) for k, v in x.items()}
+    tt = torch.from_numpy(t).cuda()
+    row = coda.fused_forward_ce(d["A"], d["W1"], d["R"], d["g"], d["W2"], wl.eps, tt)
+    pk = coda.fused_forward_ce_packed(d["A"], d["W1"], d["R"], d["g"], d["W2"], wl.eps, tt)
+    torch.cuda.synchronize()
+    return x, d, t, tt, row, pk
+
+
+@pytest.mark.parametrize("shape", CE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_ce_packed_matches_row_major_and_oracle(shape):
+    wl = ci.custom_workload(*shape, eps=1e-5, dtype="bf16", wl_id=750)
+    x, d, t, tt, (H, Hg, r, lse, loss), (Hp, Hgp, rp, lsep, lossp) = _ce_pair(wl, seed=3)
+    _same(lse, lsep, "lse")
+    _same(loss, lossp, "loss")
+    orc = oracle.forward_ce(x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps, t)
+    err = max_rel(lossp.cpu().numpy(), orc["loss"])
+    print(f"{shape}: packed CE loss error {err:.3e}")
+    assert err <= 1e-2
+    # backward: dY from the packed Hg equals the row-major one bit for bit,
+    # and every gradient meets the oracle's bar
+    dl = np.random.default_rng(5).standard_normal(wl.M).astype(np.float32)
+    tdl = torch.from_numpy(dl).cuda()
+    g_row = coda.fused_backward_ce(d["A"], d["W1"], d["g"], d["W2"], H, Hg, r, tt, lse, tdl)
+    g_pk = coda.fused_backward_ce_packed(d["A"], d["W1"], d["g"], d["W2"], Hp, Hgp, rp, tt, lsep, tdl)
+    torch.cuda.synchronize()
+    _same(g_row[-1], g_pk[-1], "dY")
+    orc_b = oracle.backward_ce(x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps, t, dl)
+    for k, v in zip(("dA", "dR", "dW1", "dW2", "dg", "dY"), g_pk):
+        err = max_rel(host_f32(v), orc_b[k])
+        assert err <= 1e-2, f"{k}: error {err:.3e}"
+
+
+ROPE_SHAPES = [  # M, K, D, N2, n_q, n_k, d_head
+    (3, 136, 264, 520, 256, 128, 64),
+    (300, 512, 384, 1040, 512, 256, 64),
+    (130, 128, 256, 264, 128, 64, 8),
+]
+
+
+def _positions(M, max_pos, seed):
+    p = np.random.default_rng(seed).integers(0, max_pos, size=M).astype(np.int32)
+    p[: min(M, 3)] = [0, max_pos - 1, max_pos // 2][: min(M, 3)]
+    return p
+
+
+@pytest.mark.parametrize("shape", ROPE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_rope_packed_matches_row_major_and_oracle(shape):
+    M, K, D, N2, nq, nk, dh = shape
+    wl = ci.custom_workload(M, K, D, N2, eps=1e-5, dtype="bf16", wl_id=760)
+    x = ci.make_inputs(wl, seed=6)
+    d = {k: dev(v) for k, v in x.items()}
+    pos = _positions(M, 4096, 6)
+    tp = torch.from_numpy(pos).cuda()
+    cs = coda.rope_cache(4096, dh, 10000.0)
+    _, _, r, Y = coda.fused_forward_rope(d["A"], d["W1"], d["R"], d["g"], d["W2"], wl.eps, tp, cs, nq, nk, dh)
+    _, _, rp, Yp = coda.fused_forward_rope_packed(d["A"], d["W1"], d["R"], d["g"], d["W2"], wl.eps, tp, cs, nq, nk,
+                                                  dh)
+    torch.cuda.synchronize()
+    _same(Y, Yp, "Y")
+    orc = oracle.forward_rope(x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps, pos, nq, nk, dh,
+                              10000.0)
+    err = max_rel(host_f32(Yp), orc["Yr"])
+    print(f"{shape}: packed RoPE Y error {err:.3e}")
+    assert err <= 1e-2
+
+
+@pytest.mark.slow
+def test_full_size_7b_ce_and_qkv_packed():
+    # the LM-head and QKV workloads at full size: the packed calls equal the
+    # row-major ones bit for bit (loss, lse, dY; rotated Y)
+    wl = ci.WORKLOADS["7b-ce-bf16"]
+    x, d, t, tt, (H, Hg, r, lse, loss), (Hp, Hgp, rp, lsep, lossp) = _ce_pair(wl, seed=0)
+    _same(lse, lsep, "lse")
+    _same(loss, lossp, "loss")
+    assert torch.isfinite(lossp).all().item()
+    tdl = torch.full((wl.M,), 1.0 / wl.M, device="cuda", dtype=torch.float32)
+    dY = torch.empty((wl.M, wl.N2), device="cuda", dtype=torch.bfloat16)
+    dYp = torch.empty_like(dY)
+    coda.coda_gemm_rowscale_ce_bwd(Hg, d["W2"], r, tt, lse, tdl, dY)
+    coda.coda_gemm_rowscale_ce_bwd_packed(Hgp, d["W2"], rp, tt, lsep, tdl, dYp)
+    torch.cuda.synchronize()
+    _same(dY, dYp, "dY")
+    del dY, dYp, d, x
+    wl = ci.WORKLOADS["7b-rope-bf16"]
+    x = ci.make_inputs(wl, seed=0)
+    d = {k: dev(v) for k, v in x.items()}
+    tp = torch.from_numpy(ci.make_positions(wl)).cuda()
+    cs = coda.rope_cache(2048, 128, 10000.0)
+    _, _, _, Y = coda.fused_forward_rope(d["A"], d["W1"], d["R"], d["g"], d["W2"], wl.eps, tp, cs, 4096, 4096, 128)
+    _, _, _, Yp = coda.fused_forward_rope_packed(d["A"], d["W1"], d["R"], d["g"], d["W2"], wl.eps, tp, cs, 4096,
+                                                 4096, 128)
+    torch.cuda.synchronize()
+    _same(Y, Yp, "Y")

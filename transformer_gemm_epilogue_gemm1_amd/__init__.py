@@ -20,6 +20,8 @@ from .binding import (coda_ce_combine, coda_chain_bwd, coda_chain_bwd_workspace_
                       coda_gemm_rowscale_packed, fused_forward_packed,
                       packed_empty_e4m3, unpack_e4m3, quantize_weight_e4m3_packed,
                       coda_gemm_res_prms_fp8_packed, coda_gemm_rowscale_fp8_packed, fused_forward_fp8_packed,
-                      coda_gemm_rowscale_swiglu_packed, fused_forward_swiglu_packed)
+                      coda_gemm_rowscale_swiglu_packed, fused_forward_swiglu_packed,
+                      coda_gemm_rowscale_lse_packed, coda_gemm_rowscale_ce_bwd_packed, coda_gemm_rowscale_rope_packed,
+                      fused_forward_ce_packed, fused_backward_ce_packed, fused_forward_rope_packed)
 
 _lib.load()

@@ -42,6 +42,12 @@ SIGNATURES = {
     "coda_gemm_rowscale_fp8_packed": (c_int, [c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp]),
     "coda_gemm_rowscale_swiglu_packed": (c_int, [c_i64, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp,
                                                  c_i64, c_vp]),
+    "coda_gemm_rowscale_lse_packed": (c_int, [c_i64, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp,
+                                              c_vp, c_vp]),
+    "coda_gemm_rowscale_ce_bwd_packed": (c_int, [c_i64, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp,
+                                                 c_vp, c_i64, c_vp]),
+    "coda_gemm_rowscale_rope_packed": (c_int, [c_i64, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_i64,
+                                               c_i64, c_i64, c_i64, c_vp, c_i64, c_vp]),
     "coda_gemm_rowscale_swiglu": (c_int, [c_int, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp,
                                           c_vp, c_i64, c_vp, c_i64, c_vp]),
     "coda_swiglu_bwd": (c_int, [c_int, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),

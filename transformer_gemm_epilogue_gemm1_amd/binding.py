@@ -749,6 +749,114 @@ def fused_forward_rope(A, W1, R, g, Wqkv, eps: float, positions, cos_sin, n_q: i
     return H, Hg, r, Y
 
 
+def coda_gemm_rowscale_lse_packed(Xp, Wv, r: Optional[torch.Tensor], targets, pmax, psum, tgt,
+                                  stream=None) -> None:
+    """coda_gemm_rowscale_lse with X tile-packed in Xp (as coda_gemm_res_prms_packed writes it)."""
+    lib = _lib.load()
+    M = targets.shape[0]
+    D, V = Wv.shape
+    T = coda_prms_num_partials(torch.bfloat16, V)
+    _packed(Xp, "X", M, D)
+    ldw = _mat(Wv, "Wv", torch.bfloat16, (D, V))
+    _mat(targets, "targets", torch.int32, (M,))
+    for t, n in ((pmax, "pmax"), (psum, "psum")):
+        _mat(t, n, torch.float32, (T, M))
+        _dense(t, n)
+    _mat(tgt, "tgt", torch.float32, (M,))
+    if r is not None:
+        _mat(r, "r", torch.float32, (M,))
+    st = lib.coda_gemm_rowscale_lse_packed(M, D, V, Xp.data_ptr(), Wv.data_ptr(), ldw,
+                                           r.data_ptr() if r is not None else None, targets.data_ptr(),
+                                           pmax.data_ptr(), psum.data_ptr(), tgt.data_ptr(), _stream(stream))
+    _lib.check("coda_gemm_rowscale_lse_packed", st)
+
+
+def coda_gemm_rowscale_ce_bwd_packed(Xp, Wv, r: Optional[torch.Tensor], targets, lse, dloss, dY,
+                                     stream=None) -> None:
+    """coda_gemm_rowscale_ce_bwd with X tile-packed in Xp (as coda_gemm_res_prms_packed writes it)."""
+    lib = _lib.load()
+    M = dY.shape[0]
+    D, V = Wv.shape
+    _packed(Xp, "X", M, D)
+    ldw = _mat(Wv, "Wv", torch.bfloat16, (D, V))
+    lddy = _mat(dY, "dY", torch.bfloat16, (M, V))
+    _mat(targets, "targets", torch.int32, (M,))
+    _mat(lse, "lse", torch.float32, (M,))
+    _mat(dloss, "dloss", torch.float32, (M,))
+    if r is not None:
+        _mat(r, "r", torch.float32, (M,))
+    st = lib.coda_gemm_rowscale_ce_bwd_packed(M, D, V, Xp.data_ptr(), Wv.data_ptr(), ldw,
+                                              r.data_ptr() if r is not None else None, targets.data_ptr(),
+                                              lse.data_ptr(), dloss.data_ptr(), dY.data_ptr(), lddy,
+                                              _stream(stream))
+    _lib.check("coda_gemm_rowscale_ce_bwd_packed", st)
+
+
+def coda_gemm_rowscale_rope_packed(Xp, Wqkv, r: Optional[torch.Tensor], positions, cos_sin, n_q: int, n_k: int,
+                                   d_head: int, Y, stream=None) -> None:
+    """coda_gemm_rowscale_rope with X tile-packed in Xp (as coda_gemm_res_prms_packed writes it)."""
+    lib = _lib.load()
+    M, N2 = Y.shape
+    D = Wqkv.shape[0]
+    _packed(Xp, "X", M, D)
+    ldw = _mat(Wqkv, "Wqkv", torch.bfloat16, (D, N2))
+    ldy = _mat(Y, "Y", torch.bfloat16, (M, N2))
+    if r is not None:
+        _mat(r, "r", torch.float32, (M,))
+    max_pos = _rope_args(positions, cos_sin, M, d_head)
+    st = lib.coda_gemm_rowscale_rope_packed(M, D, N2, Xp.data_ptr(), Wqkv.data_ptr(), ldw,
+                                            r.data_ptr() if r is not None else None, positions.data_ptr(),
+                                            cos_sin.data_ptr(), max_pos, n_q, n_k, d_head, Y.data_ptr(), ldy,
+                                            _stream(stream))
+    _lib.check("coda_gemm_rowscale_rope_packed", st)
+
+
+def fused_forward_ce_packed(A, W1, R, g, Wv, eps: float, targets, stream=None):
+    """fused_forward_ce with Hg tile-packed between the GEMMs: returns
+    (H, Hgp, r, lse, loss)."""
+    M, D, V = A.shape[0], W1.shape[1], Wv.shape[1]
+    dev, dt = A.device, A.dtype
+    H = torch.empty((M, D), device=dev, dtype=dt)
+    Hgp = packed_empty(M, D, dev)
+    P = torch.empty((coda_prms_num_partials(dt, D), M), device=dev, dtype=torch.float32)
+    r = torch.empty((M,), device=dev, dtype=torch.float32)
+    T = coda_prms_num_partials(dt, V)
+    pmax = torch.empty((T, M), device=dev, dtype=torch.float32)
+    psum = torch.empty((T, M), device=dev, dtype=torch.float32)
+    tgt = torch.empty((M,), device=dev, dtype=torch.float32)
+    lse = torch.empty((M,), device=dev, dtype=torch.float32)
+    loss = torch.empty((M,), device=dev, dtype=torch.float32)
+    coda_gemm_res_prms_packed(A, W1, R, g, H, Hgp, P, stream)
+    coda_rms_combine(P, r, D, eps, stream)
+    coda_gemm_rowscale_lse_packed(Hgp, Wv, r, targets, pmax, psum, tgt, stream)
+    coda_ce_combine(pmax, psum, tgt, targets, lse, loss, V, stream)
+    return H, Hgp, r, lse, loss
+
+
+def fused_backward_ce_packed(A, W1, g, Wv, H, Hgp, r, targets, lse, dloss, stream=None):
+    """fused_backward_ce reading the tile-packed Hgp of fused_forward_ce_packed."""
+    dY = torch.empty((A.shape[0], Wv.shape[1]), device=A.device, dtype=A.dtype)
+    coda_gemm_rowscale_ce_bwd_packed(Hgp, Wv, r, targets, lse, dloss, dY, stream)
+    return fused_backward(dY, A, W1, g, Wv, H, r, stream) + (dY,)
+
+
+def fused_forward_rope_packed(A, W1, R, g, Wqkv, eps: float, positions, cos_sin, n_q: int, n_k: int, d_head: int,
+                              stream=None):
+    """fused_forward_rope with Hg tile-packed between the GEMMs: returns
+    (H, Hgp, r, Y)."""
+    M, D, N2 = A.shape[0], W1.shape[1], Wqkv.shape[1]
+    dev, dt = A.device, A.dtype
+    H = torch.empty((M, D), device=dev, dtype=dt)
+    Hgp = packed_empty(M, D, dev)
+    P = torch.empty((coda_prms_num_partials(dt, D), M), device=dev, dtype=torch.float32)
+    r = torch.empty((M,), device=dev, dtype=torch.float32)
+    Y = torch.empty((M, N2), device=dev, dtype=dt)
+    coda_gemm_res_prms_packed(A, W1, R, g, H, Hgp, P, stream)
+    coda_rms_combine(P, r, D, eps, stream)
+    coda_gemm_rowscale_rope_packed(Hgp, Wqkv, r, positions, cos_sin, n_q, n_k, d_head, Y, stream)
+    return H, Hgp, r, Y
+
+
 def fused_forward_fp8_from_bf16(A, W1t8, sw1, R, g, W2t8, sw2, eps: float, stream=None):
     """The fp8 chain fed with a bf16 activation A: A quantised per row on the
     device, then the fp8 chain; returns (H, Hg8, r, Y, partials, A8, sa)."""

@@ -971,6 +971,84 @@ coda_status coda_gemm_rowscale_ce_bwd(coda_dtype dt, int64_t M, int64_t D, int64
                                                            ldx, Wv, ldw, ep, s);
 }
 
+coda_status coda_gemm_rowscale_rope_packed(int64_t M, int64_t D, int64_t N2, const void* Xp, const void* W2,
+                                           int64_t ldw2, const float* r, const int32_t* positions,
+                                           const float* cos_sin, int64_t max_pos, int64_t n_q, int64_t n_k,
+                                           int64_t d_head, void* Y, int64_t ldy, void* stream) {
+  coda_status st = check_dims(CODA_BF16, M, {{"D", D}, {"N2", N2}});
+  if (st != CODA_OK) return st;
+  Mat mpos, mcs;
+  if ((st = check_rope(M, N2, positions, cos_sin, max_pos, n_q, n_k, d_head, &mpos, &mcs)) != CODA_OK) return st;
+  if (M == 0) return ok();
+  const int es = 2, E = 8;
+  const int64_t x_elems = packed_bytes(M, D) / 2;
+  const Mat mX{Xp, 1, x_elems, x_elems, es, "X"}, mW2{W2, D, N2, ldw2, es, "W2"}, mY{Y, M, N2, ldy, es, "Y"};
+  const Mat mr{r, 1, M, M, 4, "r"};
+  for (const Mat* m : {&mX, &mW2, &mY})
+    if ((st = check_mat(*m, E)) != CODA_OK) return st;
+  if (r != nullptr && ((uintptr_t)r & 3) != 0) return fail(CODA_ERR_ALIGN, "r is not 4-byte aligned");
+  const Mat ins[5] = {mX, mW2, r ? mr : Mat{nullptr, 0, 0, 0, 4, "r"}, mpos, mcs};
+  if ((st = check_alias(&mY, 1, ins, 5)) != CODA_OK) return st;
+  typename EpiRowScaleRope<uint16_t>::Params ep{r, positions, cos_sin, (int)max_pos, (int)(n_q + n_k), (int)d_head,
+                                                (uint16_t*)Y, ldy};
+  return launch_gemm<uint16_t, true, false, EpiRowScaleRope<uint16_t>, true>(
+      "coda_gemm_rowscale_rope_packed", (int)M, (int)N2, (int)D, Xp, D / 8, W2, ldw2, ep, (hipStream_t)stream);
+}
+
+coda_status coda_gemm_rowscale_lse_packed(int64_t M, int64_t D, int64_t V, const void* Xp, const void* Wv,
+                                          int64_t ldw, const float* r, const int32_t* targets, float* pmax,
+                                          float* psum, float* tgt, void* stream) {
+  coda_status st = check_dims(CODA_BF16, M, {{"D", D}, {"V", V}});
+  if (st != CODA_OK) return st;
+  if (M == 0) return ok();
+  const int es = 2, E = 8;
+  const int64_t T = num_partials(V), x_elems = packed_bytes(M, D) / 2;
+  const Mat mX{Xp, 1, x_elems, x_elems, es, "X"}, mW{Wv, D, V, ldw, es, "Wv"};
+  for (const Mat* m : {&mX, &mW})
+    if ((st = check_mat(*m, E)) != CODA_OK) return st;
+  if (targets == nullptr || pmax == nullptr || psum == nullptr || tgt == nullptr)
+    return fail(CODA_ERR_NULL, "targets, pmax, psum and tgt must be set");
+  if ((((uintptr_t)targets | (uintptr_t)pmax | (uintptr_t)psum | (uintptr_t)tgt) & 3) != 0 ||
+      (r != nullptr && ((uintptr_t)r & 3) != 0))
+    return fail(CODA_ERR_ALIGN, "r, targets, pmax, psum and tgt must be 4-byte aligned");
+  const Mat mpm{pmax, T, M, M, 4, "pmax"}, mps{psum, T, M, M, 4, "psum"}, mtg{tgt, 1, M, M, 4, "tgt"};
+  const Mat mt{targets, 1, M, M, 4, "targets"}, mr{r, 1, M, M, 4, "r"};
+  if (mpm.span() > kMaxSpan) return fail(CODA_ERR_SHAPE, "pmax span too large");
+  const Mat none{nullptr, 0, 0, 0, 4, ""};
+  const Mat outs[3] = {mpm, mps, mtg};
+  const Mat ins[4] = {mX, mW, mt, r ? mr : none};
+  if ((st = check_alias(outs, 3, ins, 4)) != CODA_OK) return st;
+  typename EpiLSE<uint16_t>::Params ep{r, targets, pmax, psum, tgt};
+  return launch_gemm<uint16_t, true, false, EpiLSE<uint16_t>, true>("coda_gemm_rowscale_lse_packed", (int)M, (int)V,
+                                                                    (int)D, Xp, D / 8, Wv, ldw, ep,
+                                                                    (hipStream_t)stream);
+}
+
+coda_status coda_gemm_rowscale_ce_bwd_packed(int64_t M, int64_t D, int64_t V, const void* Xp, const void* Wv,
+                                             int64_t ldw, const float* r, const int32_t* targets, const float* lse,
+                                             const float* dloss, void* dY, int64_t lddy, void* stream) {
+  coda_status st = check_dims(CODA_BF16, M, {{"D", D}, {"V", V}});
+  if (st != CODA_OK) return st;
+  if (M == 0) return ok();
+  const int es = 2, E = 8;
+  const int64_t x_elems = packed_bytes(M, D) / 2;
+  const Mat mX{Xp, 1, x_elems, x_elems, es, "X"}, mW{Wv, D, V, ldw, es, "Wv"}, mdY{dY, M, V, lddy, es, "dY"};
+  for (const Mat* m : {&mX, &mW, &mdY})
+    if ((st = check_mat(*m, E)) != CODA_OK) return st;
+  if (targets == nullptr || lse == nullptr || dloss == nullptr)
+    return fail(CODA_ERR_NULL, "targets, lse and dloss must be set");
+  if ((((uintptr_t)targets | (uintptr_t)lse | (uintptr_t)dloss) & 3) != 0 || (r != nullptr && ((uintptr_t)r & 3) != 0))
+    return fail(CODA_ERR_ALIGN, "r, targets, lse and dloss must be 4-byte aligned");
+  const Mat mt{targets, 1, M, M, 4, "targets"}, ml{lse, 1, M, M, 4, "lse"}, md{dloss, 1, M, M, 4, "dloss"};
+  const Mat mr{r, 1, M, M, 4, "r"};
+  const Mat ins[6] = {mX, mW, mt, ml, md, r ? mr : Mat{nullptr, 0, 0, 0, 4, "r"}};
+  if ((st = check_alias(&mdY, 1, ins, 6)) != CODA_OK) return st;
+  typename EpiCEGrad<uint16_t>::Params ep{r, targets, lse, dloss, (uint16_t*)dY, lddy, (int)V};
+  return launch_gemm<uint16_t, true, false, EpiCEGrad<uint16_t>, true>("coda_gemm_rowscale_ce_bwd_packed", (int)M,
+                                                                       (int)V, (int)D, Xp, D / 8, Wv, ldw, ep,
+                                                                       (hipStream_t)stream);
+}
+
 coda_status coda_ce_combine(int64_t M, int64_t V, int64_t T, const float* pmax, const float* psum, const float* tgt,
                             const int32_t* targets, float* lse, float* loss, void* stream) {
   if (M < 0 || M > kMaxDim) return fail(CODA_ERR_SHAPE, "M = %lld out of range", (long long)M);
