@@ -347,23 +347,26 @@ struct Bwd8Ws {
 };
 
 // Unchecked launches of the quantisers (shapes validated by the caller).
-void q_rows(const void* X, int64_t ldx, int M, int K, void* X8, int64_t ldx8, float* sc, hipStream_t s) {
+// A nonzero *_nck writes that code array tile-packed (kp_unit) with that many
+// 16-code units per row instead of row-major.
+void q_rows(const void* X, int64_t ldx, int M, int K, void* X8, int64_t ldx8, float* sc, hipStream_t s,
+            int64_t x8_nck = 0) {
   const dim3 grid((unsigned)M), block(256);
   const uint16_t* x = (const uint16_t*)X;
   uint8_t* x8 = (uint8_t*)X8;
   const int chunks = (K / 8 + 255) / 256;  // 16-byte chunks per thread
   if (chunks <= 1)
-    hipLaunchKernelGGL(quantize_rows_e4m3_kernel<1>, grid, block, 0, s, x, ldx, K, x8, ldx8, sc);
+    hipLaunchKernelGGL(quantize_rows_e4m3_kernel<1>, grid, block, 0, s, x, ldx, K, x8, ldx8, sc, x8_nck);
   else if (chunks <= 2)
-    hipLaunchKernelGGL(quantize_rows_e4m3_kernel<2>, grid, block, 0, s, x, ldx, K, x8, ldx8, sc);
+    hipLaunchKernelGGL(quantize_rows_e4m3_kernel<2>, grid, block, 0, s, x, ldx, K, x8, ldx8, sc, x8_nck);
   else if (chunks <= 4)
-    hipLaunchKernelGGL(quantize_rows_e4m3_kernel<4>, grid, block, 0, s, x, ldx, K, x8, ldx8, sc);
+    hipLaunchKernelGGL(quantize_rows_e4m3_kernel<4>, grid, block, 0, s, x, ldx, K, x8, ldx8, sc, x8_nck);
   else if (chunks <= 8)
-    hipLaunchKernelGGL(quantize_rows_e4m3_kernel<8>, grid, block, 0, s, x, ldx, K, x8, ldx8, sc);
+    hipLaunchKernelGGL(quantize_rows_e4m3_kernel<8>, grid, block, 0, s, x, ldx, K, x8, ldx8, sc, x8_nck);
   else if (chunks <= 16)
-    hipLaunchKernelGGL(quantize_rows_e4m3_kernel<16>, grid, block, 0, s, x, ldx, K, x8, ldx8, sc);
+    hipLaunchKernelGGL(quantize_rows_e4m3_kernel<16>, grid, block, 0, s, x, ldx, K, x8, ldx8, sc, x8_nck);
   else
-    hipLaunchKernelGGL(quantize_long_rows_e4m3_kernel, grid, block, 0, s, x, ldx, K, x8, ldx8, sc);
+    hipLaunchKernelGGL(quantize_long_rows_e4m3_kernel, grid, block, 0, s, x, ldx, K, x8, ldx8, sc, x8_nck);
 }
 // wt_nck > 0: Wt8 written tile-packed with wt_nck chunks per row (K / 16).
 void q_cols(const void* W, int64_t ldw, int K, int N, void* Wt8, int64_t ldwt, float* sc, hipStream_t s,
@@ -373,28 +376,30 @@ void q_cols(const void* W, int64_t ldw, int K, int N, void* Wt8, int64_t ldwt, f
                      (const uint16_t*)W, ldw, K, N, (uint32_t*)sc);
   hipLaunchKernelGGL(quantize_cols_kernel, dim3((unsigned)((N + 127) / 128), (unsigned)((K + 127) / 128)), dim3(256),
                      0, s, (const uint16_t*)W, ldw, K, N, (const uint32_t*)sc, (uint8_t*)Wt8, ldwt,
-                     (const uint32_t*)nullptr, (uint8_t*)nullptr, (int64_t)0, wt_nck);
+                     (const uint32_t*)nullptr, (uint8_t*)nullptr, (int64_t)0, wt_nck, (int64_t)0);
   hipLaunchKernelGGL(amax_to_scale_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, sc, N);
 }
 // Both quantisations of an activation X [M, N]: row codes X8 [M, N] with
 // scales sr [M] (as q_rows) and column codes Xt8 [N, M] with scales sc [N]
 // (as q_cols), from one pass for the maxima and one for the codes.
 void q_rows_cols(const void* X, int64_t ldx, int M, int N, void* X8, int64_t ldx8, float* sr, void* Xt8,
-                 int64_t ldxt, float* sc, hipStream_t s) {
+                 int64_t ldxt, float* sc, hipStream_t s, int64_t x8_nck = 0, int64_t xt_nck = 0) {
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, (uint32_t*)sr, M, 0u);
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, (uint32_t*)sc, N, 0u);
   hipLaunchKernelGGL(rowcol_max_kernel, dim3((unsigned)((N + 255) / 256), (unsigned)((M + 255) / 256)), dim3(256), 0,
                      s, (const uint16_t*)X, ldx, M, N, (uint32_t*)sr, (uint32_t*)sc);
   hipLaunchKernelGGL(quantize_cols_kernel, dim3((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128)), dim3(256),
                      0, s, (const uint16_t*)X, ldx, M, N, (const uint32_t*)sc, (uint8_t*)Xt8, ldxt,
-                     (const uint32_t*)sr, (uint8_t*)X8, ldx8, (int64_t)0);
+                     (const uint32_t*)sr, (uint8_t*)X8, ldx8, xt_nck, x8_nck);
   hipLaunchKernelGGL(amax_to_scale_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, sr, M);
   hipLaunchKernelGGL(amax_to_scale_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, sc, N);
 }
 
 // The chain's backward with every product on e4m3 operands quantised along
 // its contraction (bf16 tensors in and out); the per-element steps are the
-// bf16 backward's.  M > 0, all sizes multiples of 16.
+// bf16 backward's.  M > 0, all sizes multiples of 16.  Every code array is
+// written tile-packed (no padding rows, since all row counts are multiples of
+// 16), so all four products read both operands in the packed layout.
 coda_status chain_bwd_fp8_impl(int M, int K, int D, int N2, const void* dY, const void* A, const void* W1,
                                const void* g, const void* W2, const void* H, const float* r, void* dA, void* dR,
                                void* dW1, void* dW2, float* dg, char* ws, hipStream_t s) {
@@ -407,15 +412,16 @@ coda_status chain_bwd_fp8_impl(int M, int K, int D, int N2, const void* dY, cons
   const int Tn = (int)num_partials(D), U = (M + kWaveM - 1) / kWaveM;
   coda_status st;
   // operands of G = dY W2^T (rows) and dW2 = X_n^T dY (dY's columns)
-  q_rows_cols(dY, N2, M, N2, ws + L.dy8, N2, f(L.sdy), ws + L.dyt8, M, f(L.sdyt), s);
-  q_rows(W2, N2, D, N2, ws + L.w2q, N2, f(L.sw2), s);
-  q_rows(W1, D, K, D, ws + L.w1q, D, f(L.sw1), s);
+  q_rows_cols(dY, N2, M, N2, ws + L.dy8, N2, f(L.sdy), ws + L.dyt8, M, f(L.sdyt), s, N2 / 16, M / 16);
+  q_rows(W2, N2, D, N2, ws + L.w2q, N2, f(L.sw2), s, N2 / 16);
+  q_rows(W1, D, K, D, ws + L.w1q, D, f(L.sw1), s, D / 16);
   if ((st = launch_status("coda_chain_bwd_fp8 quantise dY, W1, W2")) != CODA_OK) return st;
   // 1. G with the P / X_n / partial-sum epilogue, after dequantisation
   using EpiG = EpiDequant<EpiBwdG<uint16_t>>;
   typename EpiG::Params eg{f(L.sdy), f(L.sw2), {(const uint16_t*)H, (const uint16_t*)g, r, (uint16_t*)dR, Xn, D,
                                                 srow, dgcol}};
-  if ((st = launch_gemm_fp8<EpiG>("coda_chain_bwd_fp8 G", M, D, N2, ws + L.dy8, N2, ws + L.w2q, N2, eg, s)) !=
+  if ((st = launch_gemm_fp8<EpiG, true>("coda_chain_bwd_fp8 G", M, D, N2, ws + L.dy8, N2 / 16, ws + L.w2q, N2 / 16,
+                                        eg, s)) !=
       CODA_OK)
     return st;
   // 2. c and dg;  3. dH in place in dR
@@ -426,22 +432,22 @@ coda_status chain_bwd_fp8_impl(int M, int K, int D, int N2, const void* dY, cons
   hipLaunchKernelGGL(dh_finalize_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, (uint16_t*)dR, (const uint16_t*)H,
                      r, c, D, nchunks);
   // operands of dA = dH W1^T (dH rows), dW1 = A^T dH and dW2 = X_n^T dY (columns)
-  q_rows_cols(dR, D, M, D, ws + L.dh8, D, f(L.sdh), ws + L.dht8, M, f(L.sdht), s);
-  q_cols(Xn, D, M, D, ws + L.xnt8, M, f(L.sxn), s);
-  q_cols(A, K, M, K, ws + L.at8, M, f(L.sat), s);
+  q_rows_cols(dR, D, M, D, ws + L.dh8, D, f(L.sdh), ws + L.dht8, M, f(L.sdht), s, D / 16, M / 16);
+  q_cols(Xn, D, M, D, ws + L.xnt8, M, f(L.sxn), s, M / 16);
+  q_cols(A, K, M, K, ws + L.at8, M, f(L.sat), s, M / 16);
   if ((st = launch_status("coda_chain_bwd_fp8 combine, dH, quantise")) != CODA_OK) return st;
   using EpiO = EpiDequant<EpiRowScale<uint16_t>>;
   // 4. dA = dH W1^T
-  if ((st = launch_gemm_fp8<EpiO>("coda_chain_bwd_fp8 dA", M, K, D, ws + L.dh8, D, ws + L.w1q, D,
+  if ((st = launch_gemm_fp8<EpiO, true>("coda_chain_bwd_fp8 dA", M, K, D, ws + L.dh8, D / 16, ws + L.w1q, D / 16,
                                   typename EpiO::Params{f(L.sdh), f(L.sw1), {nullptr, (uint16_t*)dA, K}}, s)) !=
       CODA_OK)
     return st;
   // 5. dW1 = A^T dH;  6. dW2 = X_n^T dY  (contraction over the M rows)
-  if ((st = launch_gemm_fp8<EpiO>("coda_chain_bwd_fp8 dW1", K, D, M, ws + L.at8, M, ws + L.dht8, M,
+  if ((st = launch_gemm_fp8<EpiO, true>("coda_chain_bwd_fp8 dW1", K, D, M, ws + L.at8, M / 16, ws + L.dht8, M / 16,
                                   typename EpiO::Params{f(L.sat), f(L.sdht), {nullptr, (uint16_t*)dW1, D}}, s)) !=
       CODA_OK)
     return st;
-  return launch_gemm_fp8<EpiO>("coda_chain_bwd_fp8 dW2", D, N2, M, ws + L.xnt8, M, ws + L.dyt8, M,
+  return launch_gemm_fp8<EpiO, true>("coda_chain_bwd_fp8 dW2", D, N2, M, ws + L.xnt8, M / 16, ws + L.dyt8, M / 16,
                                typename EpiO::Params{f(L.sxn), f(L.sdyt), {nullptr, (uint16_t*)dW2, N2}}, s);
 }
 

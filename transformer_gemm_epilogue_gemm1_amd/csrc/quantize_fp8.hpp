@@ -64,10 +64,17 @@ __device__ __forceinline__ float block_amax(float v, float* red) {
 // K % 8 == 0.  Rows of up to 2048 CPT elements stay in registers (CPT
 // 16-byte chunks per thread, all loads in flight at once), so the row is read
 // from memory once.
+// Where the 8 row codes of columns col .. col + 7 (col a multiple of 8) of
+// row `row` go: row-major with leading dimension ldx8, or, for x8_nck > 0,
+// tile-packed with x8_nck 16-code units per row (kp_unit).
+__device__ __forceinline__ uint8_t* row_codes(uint8_t* X8, int64_t ldx8, int64_t x8_nck, int64_t row, int col) {
+  return x8_nck > 0 ? X8 + kp_unit(row, col >> 4, x8_nck) * 16 + (col & 15) : X8 + row * ldx8 + col;
+}
+
 template <int CPT>
 __global__ __launch_bounds__(256) void quantize_rows_e4m3_kernel(const uint16_t* __restrict__ X, int64_t ldx,
                                                                  int K, uint8_t* __restrict__ X8, int64_t ldx8,
-                                                                 float* __restrict__ scales) {
+                                                                 float* __restrict__ scales, int64_t x8_nck) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
   const uint16_t* x = X + row * ldx;
@@ -89,14 +96,13 @@ __global__ __launch_bounds__(256) void quantize_rows_e4m3_kernel(const uint16_t*
   const float s = e4m3_scale(block_amax(m, red));
   if (threadIdx.x == 0) scales[row] = s;
   const E4m3Divider enc = E4m3Divider::of(s);
-  uint8_t* y = X8 + row * ldx8;
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
     const int c = threadIdx.x + 256 * j;
     if (c < nc) {
       float v[8];
       Chunk8<uint16_t>::unpack(raw[j], v);
-      *(u32x2*)(y + 8 * c) = encode8(v, enc);
+      *(u32x2*)row_codes(X8, ldx8, x8_nck, row, 8 * c) = encode8(v, enc);
     }
   }
 }
@@ -105,7 +111,8 @@ __global__ __launch_bounds__(256) void quantize_rows_e4m3_kernel(const uint16_t*
 // row, the second from cache.
 __global__ __launch_bounds__(256) void quantize_long_rows_e4m3_kernel(const uint16_t* __restrict__ X, int64_t ldx,
                                                                       int K, uint8_t* __restrict__ X8,
-                                                                      int64_t ldx8, float* __restrict__ scales) {
+                                                                      int64_t ldx8, float* __restrict__ scales,
+                                                                      int64_t x8_nck) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
   const uint16_t* x = X + row * ldx;
@@ -120,11 +127,10 @@ __global__ __launch_bounds__(256) void quantize_long_rows_e4m3_kernel(const uint
   const float s = e4m3_scale(block_amax(m, red));
   if (threadIdx.x == 0) scales[row] = s;
   const E4m3Divider enc = E4m3Divider::of(s);
-  uint8_t* y = X8 + row * ldx8;
   for (int c = threadIdx.x; c < nc; c += 256) {
     float v[8];
     Chunk8<uint16_t>::load(x + 8 * c, v);
-    *(u32x2*)(y + 8 * c) = encode8(v, enc);
+    *(u32x2*)row_codes(X8, ldx8, x8_nck, row, 8 * c) = encode8(v, enc);
   }
 }
 
@@ -248,7 +254,7 @@ __global__ __launch_bounds__(256) void quantize_cols_kernel(const uint16_t* __re
                                                             uint8_t* __restrict__ Wt8, int64_t ldwt,
                                                             const uint32_t* __restrict__ rmax,
                                                             uint8_t* __restrict__ X8, int64_t ldx8,
-                                                            int64_t wt_nck) {
+                                                            int64_t wt_nck, int64_t x8_nck) {
   constexpr int kPitch = 33;  // words per tile row: 128 codes + 4 bytes of padding
   __shared__ uint32_t tile[128 * kPitch];
   __shared__ E4m3Divider coldiv[128], rowdiv[128];
@@ -275,7 +281,7 @@ __global__ __launch_bounds__(256) void quantize_cols_kernel(const uint16_t* __re
     const int kr = (t >> 4) + 16 * h, k = k0 + kr;
     float v[8];
     Chunk8<uint16_t>::unpack(raw[h], v);
-    if (X8 != nullptr && k < K && cin) *(u32x2*)(X8 + (int64_t)k * ldx8 + n0 + rc) = encode8(v, rowdiv[kr]);
+    if (X8 != nullptr && k < K && cin) *(u32x2*)row_codes(X8, ldx8, x8_nck, k, n0 + rc) = encode8(v, rowdiv[kr]);
     const u32x2 c = encode8(v, cd);
     tile[kr * kPitch + rc / 4] = c[0];
     tile[kr * kPitch + rc / 4 + 1] = c[1];
