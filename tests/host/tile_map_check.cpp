@@ -90,6 +90,13 @@ static void check_kc() {
           for (int q = 0; q < 4; ++q) used[(bank + q) % 64]++;
         }
         for (int b = 0; b < 64; ++b) CHECK(used[b] == 1, "KC fragment bank conflict base %d t %d g %d", base, t, g);
+        // also conflict-free when the LDS serves 8 or 4 lanes (128 or 64 bytes) at a time
+        for (int w : {4, 8})
+          for (int i0 = 0; i0 < 16; i0 += w) {
+            std::vector<int> slot(w, 0);
+            for (int i = i0; i < i0 + w; ++i) slot[(kc_offset(base + 16 * t + i, g) % (16 * w)) / 16]++;
+            for (int q = 0; q < w; ++q) CHECK(slot[q] == 1, "KC fragment: %d-lane window conflict at base %d t %d g %d", w, base, t, g);
+          }
       }
     }
 }
@@ -283,6 +290,12 @@ static void check_kc8() {
             for (int q = 0; q < 4; ++q) used[(bank + q) % 64]++;
           }
           for (int b = 0; b < 64; ++b) CHECK(used[b] == 1, "kc8 bank conflict");
+          for (int w : {4, 8})
+            for (int i0 = 0; i0 < 16; i0 += w) {
+              std::vector<int> slot(w, 0);
+              for (int i = i0; i < i0 + w; ++i) slot[(kc8_offset(base, t, half, 16 * g + i) % (16 * w)) / 16]++;
+              for (int q = 0; q < w; ++q) CHECK(slot[q] == 1, "kc8: %d-lane window conflict", w);
+            }
         }
       }
   // 32 x 32 accumulators into 16-row slabs: every slab cell written once

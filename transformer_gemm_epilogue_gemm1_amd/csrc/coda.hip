@@ -109,8 +109,9 @@ uint32_t span_bytes(int64_t rows, int64_t cols, int64_t ld, int es) {
 // Bytes of a tile-packed bf16 matrix (kp_unit): rows padded to 16, cols / 8 chunks.
 int64_t packed_bytes(int64_t rows, int64_t cols) { return (rows + 15) / 16 * 16 * cols * 2; }
 
-// APK: A is tile-packed and lda counts its 16-byte chunks per row.
-template <typename T, bool AKC, bool BKC, class Epi, bool APK = false>
+// AL, BL: OpLayout of a contraction-contiguous A or B (kLayPacked: lda / ldb
+// count 16-byte chunks per row).
+template <typename T, bool AKC, bool BKC, class Epi, int AL = kLayKC, int BL = kLayKC>
 coda_status launch_gemm(const char* what, int M, int N, int K, const void* a, int64_t lda, const void* b,
                         int64_t ldb, const typename Epi::Params& ep, hipStream_t s, int b_split = 0) {
   GemmArgs g;
@@ -122,22 +123,25 @@ coda_status launch_gemm(const char* what, int M, int N, int K, const void* a, in
   g.group_m = kGroupM;
   g.a = a;
   g.lda = lda;
-  g.a_span = APK ? (uint32_t)packed_bytes(M, 8 * lda)
-                 : AKC ? span_bytes(M, K, lda, sizeof(T)) : span_bytes(K, M, lda, sizeof(T));
+  constexpr int al = AKC ? AL : kLayKC, bl = BKC ? BL : kLayKC;
+  g.a_span = al == kLayPacked ? (uint32_t)packed_bytes(M, 8 * lda)
+                              : AKC ? span_bytes(M, K, lda, sizeof(T)) : span_bytes(K, M, lda, sizeof(T));
   g.b = b;
   g.ldb = ldb;
-  g.b_span = BKC ? span_bytes(N, K, ldb, sizeof(T)) : span_bytes(K, N, ldb, sizeof(T));
+  g.b_span = bl == kLayPacked ? (uint32_t)packed_bytes(N, 8 * ldb)
+                              : BKC ? span_bytes(N, K, ldb, sizeof(T)) : span_bytes(K, N, ldb, sizeof(T));
   g.b_split = b_split;
   const int nblocks = g.tiles_m * g.tiles_n;
-  hipLaunchKernelGGL((gemm_kernel<T, AKC, BKC, Epi, APK>), dim3(nblocks), dim3(kThreads), 0, s, g, ep);
+  hipLaunchKernelGGL((gemm_kernel<T, AKC, BKC, Epi, al, bl>), dim3(nblocks), dim3(kThreads), 0, s, g, ep);
   return launch_status(what);
 }
 
 // Bytes of a tile-packed e4m3 matrix (kp_unit): rows padded to 16, cols / 16 chunks.
 int64_t packed_bytes_e4m3(int64_t rows, int64_t cols) { return (rows + 15) / 16 * 16 * cols; }
 
-// PK: both operands tile-packed, lda / ldb counting 16-byte chunks per row.
-template <class Epi, bool PK = false>
+// L: OpLayout of both operands (kLayPacked: lda / ldb counting 16-byte chunks
+// per row).
+template <class Epi, int L = kLayKC>
 coda_status launch_gemm_fp8(const char* what, int M, int N, int K, const void* a, int64_t lda, const void* b,
                             int64_t ldb, const typename Epi::Params& ep, hipStream_t s) {
   GemmArgs g;
@@ -149,12 +153,12 @@ coda_status launch_gemm_fp8(const char* what, int M, int N, int K, const void* a
   g.group_m = kGroupM;
   g.a = a;
   g.lda = lda;
-  g.a_span = PK ? (uint32_t)packed_bytes_e4m3(M, 16 * lda) : span_bytes(M, K, lda, 1);
+  g.a_span = L == kLayPacked ? (uint32_t)packed_bytes_e4m3(M, 16 * lda) : span_bytes(M, K, lda, 1);
   g.b = b;
   g.ldb = ldb;
-  g.b_span = PK ? (uint32_t)packed_bytes_e4m3(N, 16 * ldb) : span_bytes(N, K, ldb, 1);
+  g.b_span = L == kLayPacked ? (uint32_t)packed_bytes_e4m3(N, 16 * ldb) : span_bytes(N, K, ldb, 1);
   g.b_split = 0;
-  hipLaunchKernelGGL((gemm_fp8_kernel<Epi, PK>), dim3(g.tiles_m * g.tiles_n), dim3(kThreads), 0, s, g, ep);
+  hipLaunchKernelGGL((gemm_fp8_kernel<Epi, L>), dim3(g.tiles_m * g.tiles_n), dim3(kThreads), 0, s, g, ep);
   return launch_status(what);
 }
 
@@ -207,7 +211,7 @@ coda_status gemm_res_prms_packed_impl(int M, int K, int D, const void* A, int64_
 coda_status gemm_rowscale_packed_impl(int M, int D, int N2, const void* Xp, const void* W2, int64_t ldw2,
                                       const float* r, void* Y, int64_t ldy, hipStream_t s) {
   typename EpiRowScale<uint16_t>::Params ep{r, (uint16_t*)Y, ldy};
-  return launch_gemm<uint16_t, true, false, EpiRowScale<uint16_t>, true>("coda_gemm_rowscale_packed", M, N2, D, Xp,
+  return launch_gemm<uint16_t, true, false, EpiRowScale<uint16_t>, kLayPacked>("coda_gemm_rowscale_packed", M, N2, D, Xp,
                                                                          D / 8, W2, ldw2, ep, s);
 }
 
@@ -224,7 +228,7 @@ coda_status gemm_rowscale_swiglu_packed_impl(int M, int D, int F, const void* Xp
                                              const float* r, void* Z, int64_t ldz, void* Y, int64_t ldy,
                                              hipStream_t s) {
   typename EpiSwiGLU<uint16_t>::Params ep{r, (uint16_t*)Z, ldz, (uint16_t*)Y, ldy, F};
-  return launch_gemm<uint16_t, true, false, EpiSwiGLU<uint16_t>, true>("coda_gemm_rowscale_swiglu_packed", M, 2 * F,
+  return launch_gemm<uint16_t, true, false, EpiSwiGLU<uint16_t>, kLayPacked>("coda_gemm_rowscale_swiglu_packed", M, 2 * F,
                                                                        D, Xp, D / 8, W2, ldw2, ep, s, F);
 }
 
@@ -237,10 +241,12 @@ coda_status combine_impl(int M, int D, int T, float eps, const float* partials, 
 constexpr size_t kWsAlign = 256;
 size_t align_up(size_t x) { return (x + kWsAlign - 1) & ~(kWsAlign - 1); }
 
-// Workspace parts of the backward, in this order, each 256-byte aligned.
-// Workspace of the backward: X_n, the row and column partial sums, c, and
-// the transposed weights W2^T [N2, D] and W1^T [D, K] (K = N2 = 0: none), so
-// that G = dY W2^T and dA = dH W1^T read their weight row-contiguously.
+// Workspace of the backward, in this order, each part 256-byte aligned: X_n,
+// the row and column partial sums, c, and the transposed weights W2^T [N2, D]
+// and W1^T [D, K] (K = N2 = 0: none), so that G = dY W2^T and dA = dH W1^T
+// read their weight row-contiguously.  (Read in place, both operands of those
+// products are contraction-contiguous; measured 1% slower for the whole
+// backward at 7B than transposing first.)
 struct BwdWs {
   size_t xn, srow, dgcol, c, w2t, w1t, total;
   BwdWs(int64_t M, int64_t K, int64_t D, int64_t N2, int es) {
@@ -420,7 +426,7 @@ coda_status chain_bwd_fp8_impl(int M, int K, int D, int N2, const void* dY, cons
   using EpiG = EpiDequant<EpiBwdG<uint16_t>>;
   typename EpiG::Params eg{f(L.sdy), f(L.sw2), {(const uint16_t*)H, (const uint16_t*)g, r, (uint16_t*)dR, Xn, D,
                                                 srow, dgcol}};
-  if ((st = launch_gemm_fp8<EpiG, true>("coda_chain_bwd_fp8 G", M, D, N2, ws + L.dy8, N2 / 16, ws + L.w2q, N2 / 16,
+  if ((st = launch_gemm_fp8<EpiG, kLayPacked>("coda_chain_bwd_fp8 G", M, D, N2, ws + L.dy8, N2 / 16, ws + L.w2q, N2 / 16,
                                         eg, s)) !=
       CODA_OK)
     return st;
@@ -438,16 +444,16 @@ coda_status chain_bwd_fp8_impl(int M, int K, int D, int N2, const void* dY, cons
   if ((st = launch_status("coda_chain_bwd_fp8 combine, dH, quantise")) != CODA_OK) return st;
   using EpiO = EpiDequant<EpiRowScale<uint16_t>>;
   // 4. dA = dH W1^T
-  if ((st = launch_gemm_fp8<EpiO, true>("coda_chain_bwd_fp8 dA", M, K, D, ws + L.dh8, D / 16, ws + L.w1q, D / 16,
+  if ((st = launch_gemm_fp8<EpiO, kLayPacked>("coda_chain_bwd_fp8 dA", M, K, D, ws + L.dh8, D / 16, ws + L.w1q, D / 16,
                                   typename EpiO::Params{f(L.sdh), f(L.sw1), {nullptr, (uint16_t*)dA, K}}, s)) !=
       CODA_OK)
     return st;
   // 5. dW1 = A^T dH;  6. dW2 = X_n^T dY  (contraction over the M rows)
-  if ((st = launch_gemm_fp8<EpiO, true>("coda_chain_bwd_fp8 dW1", K, D, M, ws + L.at8, M / 16, ws + L.dht8, M / 16,
+  if ((st = launch_gemm_fp8<EpiO, kLayPacked>("coda_chain_bwd_fp8 dW1", K, D, M, ws + L.at8, M / 16, ws + L.dht8, M / 16,
                                   typename EpiO::Params{f(L.sat), f(L.sdht), {nullptr, (uint16_t*)dW1, D}}, s)) !=
       CODA_OK)
     return st;
-  return launch_gemm_fp8<EpiO, true>("coda_chain_bwd_fp8 dW2", D, N2, M, ws + L.xnt8, M / 16, ws + L.dyt8, M / 16,
+  return launch_gemm_fp8<EpiO, kLayPacked>("coda_chain_bwd_fp8 dW2", D, N2, M, ws + L.xnt8, M / 16, ws + L.dyt8, M / 16,
                                typename EpiO::Params{f(L.sxn), f(L.sdyt), {nullptr, (uint16_t*)dW2, N2}}, s);
 }
 
@@ -910,7 +916,7 @@ coda_status coda_gemm_rowscale_fp8_packed(int64_t M, int64_t D, int64_t N2, cons
   const Mat ins[4] = {mX, mW, msw, r ? mr : none};
   if ((st = check_alias(&mY, 1, ins, 4)) != CODA_OK) return st;
   EpiRowScaleFp8::Params ep{r, sw2, (uint16_t*)Y, ldy};
-  return launch_gemm_fp8<EpiRowScaleFp8, true>("coda_gemm_rowscale_fp8_packed", (int)M, (int)N2, (int)D, X8p,
+  return launch_gemm_fp8<EpiRowScaleFp8, kLayPacked>("coda_gemm_rowscale_fp8_packed", (int)M, (int)N2, (int)D, X8p,
                                                D / 16, W2t8p, D / 16, ep, (hipStream_t)stream);
 }
 
@@ -997,7 +1003,7 @@ coda_status coda_gemm_rowscale_rope_packed(int64_t M, int64_t D, int64_t N2, con
   if ((st = check_alias(&mY, 1, ins, 5)) != CODA_OK) return st;
   typename EpiRowScaleRope<uint16_t>::Params ep{r, positions, cos_sin, (int)max_pos, (int)(n_q + n_k), (int)d_head,
                                                 (uint16_t*)Y, ldy};
-  return launch_gemm<uint16_t, true, false, EpiRowScaleRope<uint16_t>, true>(
+  return launch_gemm<uint16_t, true, false, EpiRowScaleRope<uint16_t>, kLayPacked>(
       "coda_gemm_rowscale_rope_packed", (int)M, (int)N2, (int)D, Xp, D / 8, W2, ldw2, ep, (hipStream_t)stream);
 }
 
@@ -1025,7 +1031,7 @@ coda_status coda_gemm_rowscale_lse_packed(int64_t M, int64_t D, int64_t V, const
   const Mat ins[4] = {mX, mW, mt, r ? mr : none};
   if ((st = check_alias(outs, 3, ins, 4)) != CODA_OK) return st;
   typename EpiLSE<uint16_t>::Params ep{r, targets, pmax, psum, tgt};
-  return launch_gemm<uint16_t, true, false, EpiLSE<uint16_t>, true>("coda_gemm_rowscale_lse_packed", (int)M, (int)V,
+  return launch_gemm<uint16_t, true, false, EpiLSE<uint16_t>, kLayPacked>("coda_gemm_rowscale_lse_packed", (int)M, (int)V,
                                                                     (int)D, Xp, D / 8, Wv, ldw, ep,
                                                                     (hipStream_t)stream);
 }
@@ -1050,7 +1056,7 @@ coda_status coda_gemm_rowscale_ce_bwd_packed(int64_t M, int64_t D, int64_t V, co
   const Mat ins[6] = {mX, mW, mt, ml, md, r ? mr : Mat{nullptr, 0, 0, 0, 4, "r"}};
   if ((st = check_alias(&mdY, 1, ins, 6)) != CODA_OK) return st;
   typename EpiCEGrad<uint16_t>::Params ep{r, targets, lse, dloss, (uint16_t*)dY, lddy, (int)V};
-  return launch_gemm<uint16_t, true, false, EpiCEGrad<uint16_t>, true>("coda_gemm_rowscale_ce_bwd_packed", (int)M,
+  return launch_gemm<uint16_t, true, false, EpiCEGrad<uint16_t>, kLayPacked>("coda_gemm_rowscale_ce_bwd_packed", (int)M,
                                                                        (int)V, (int)D, Xp, D / 8, Wv, ldw, ep,
                                                                        (hipStream_t)stream);
 }

@@ -126,9 +126,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) char lds_char;
 
-// PK (contraction-contiguous operands only): the operand is tile-packed
-// (kp_unit in tile_map.hpp) and ld counts its 16-byte chunks per row.
-template <typename T, bool KC, bool PK = false>
+// How a contraction-contiguous operand lies in memory and in the LDS stages.
+//   kLayKC:     row-major in memory; LDS [row][k], XOR swizzled (kc_offset).
+//               A direct load covers 16 rows x 64 bytes.
+//   kLayPacked: tile-packed in memory (kp_unit, ld = 16-byte chunks per
+//               row); LDS in the packed order (kp_offset).  Every direct load
+//               copies 1 KiB of consecutive memory.
+// (Loading a row-major operand into the packed LDS order, each lane fetching
+// its own row's 16-byte chunk, made the second GEMM 7% and the backward 13%
+// slower at 7B: the memory side wants 4 consecutive lanes on one row.)
+enum OpLayout : int { kLayKC = 0, kLayPacked = 1 };
+__host__ __device__ constexpr bool lds_packed(int layout) { return layout != kLayKC; }
+
+// L (contraction-contiguous operands only): one of OpLayout.
+template <typename T, bool KC, int L = kLayKC>
 struct Dma {
   static constexpr int E = Elem<T>::E;
   static constexpr int KTE = kKTBytes / (int)sizeof(T);  // contraction elements per k-tile
@@ -145,7 +156,7 @@ struct Dma {
     rsrc = make_rsrc(p, span_bytes);
 #pragma unroll
     for (int s = 0; s < kDmaSlots; ++s) {
-      if constexpr (KC && PK) {
+      if constexpr (KC && lds_packed(L)) {
         int r, c;
         dma_kp(s, wave, lane, &r, &c);
         const int gr = row0 + r;
@@ -167,8 +178,8 @@ struct Dma {
       }
     }
     kslot = KC ? 0 : (kWaves * 1024) / rc_row_bytes(E);
-    // packed: a k-tile is 4 chunks of 16 rows further
-    kstep = KC ? (uint32_t)(PK ? 4 * 256 : kKTBytes) : (uint32_t)(KTE * ld * (int64_t)sizeof(T));
+    // tile-packed: a k-tile is 4 chunks of 16 rows further
+    kstep = KC ? (uint32_t)(L == kLayPacked ? 4 * 256 : kKTBytes) : (uint32_t)(KTE * ld * (int64_t)sizeof(T));
   }
 
   // Loads k-tile kt into the operand tile at `dst`.  `wave` is wave-uniform;
@@ -199,6 +210,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // registers (four stages x eight fragments would not fit).
 __device__ __forceinline__ void opaque(int& v) { asm volatile("" : "+v"(v)); }
 
+// PK: the tile is in the packed LDS order (lds_packed of its layout).
 template <typename T, bool KC, bool PK = false>
 struct FragReader {
   int off0;  // lane's byte offset of fragment 0 in the operand tile (RC bf16: h = 0 base)
@@ -325,9 +337,10 @@ struct Frags {
 // the addressing overlaps them; measured at the 7B second-GEMM shape under
 // the power cap, 1.7-2.4% faster than issuing first (after 1 fragment: 1.2%,
 // after 4-7: 0.3-0.8%; the A and B loads split over two points: 0.6-1.7%).
-template <typename T, bool A_KC, bool B_KC, int S, bool A_PK = false>
-__device__ __forceinline__ void kstep(char* const (&st)[kStages], const Dma<T, A_KC, A_PK>& da,
-                                      const Dma<T, B_KC>& db, FragReader<T, A_KC, A_PK>& ra, FragReader<T, B_KC>& rb,
+template <typename T, bool A_KC, bool B_KC, int S, int A_L = kLayKC, int B_L = kLayKC>
+__device__ __forceinline__ void kstep(char* const (&st)[kStages], const Dma<T, A_KC, A_L>& da,
+                                      const Dma<T, B_KC, B_L>& db, FragReader<T, A_KC, lds_packed(A_L)>& ra,
+                                      FragReader<T, B_KC, lds_packed(B_L)>& rb,
                                       f32x4 (&acc)[kFragM][kFragN], Frags& cur, int kt, int K, int wave) {
   constexpr int SL = (S + kStages - 1) % kStages;
   constexpr int SN = (S + 1) % kStages;
@@ -368,11 +381,13 @@ __device__ __forceinline__ void kstep(char* const (&st)[kStages], const Dma<T, A
 //                              (epi_row), v[8] the accumulators
 //   end_slab(mt, slab_row0)    after all lanes applied 16-row slab mt
 //   finish()                   on every lane after the last slab
-template <typename T, bool A_KC, bool B_KC, class Epi, bool A_PK = false>
+// A_L, B_L: OpLayout of a contraction-contiguous operand.
+template <typename T, bool A_KC, bool B_KC, class Epi, int A_L = kLayKC, int B_L = kLayKC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(
     GemmArgs g, typename Epi::Params ep) {
   static_assert(kStages == 4, "the stage arrays and the unrolled steps below assume four stages");
-  static_assert(!A_PK || (A_KC && sizeof(T) == 2), "only a contraction-contiguous bf16 A operand is tile-packed");
+  static_assert((A_L == kLayKC || A_KC) && (B_L == kLayKC || B_KC), "only contraction-contiguous operands are packed");
+  static_assert((A_L != kLayPacked && B_L != kLayPacked) || sizeof(T) == 2, "tile-packed operands are bf16");
   __shared__ __attribute__((aligned(1024))) char st0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char st1[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char st2[kStageBytes];
@@ -386,12 +401,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   map_tile(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, &tm, &tn);
   const int m0 = tm * kTileM, n0 = tn * kTileN;
 
-  Dma<T, A_KC, A_PK> da;
-  Dma<T, B_KC> db;
+  Dma<T, A_KC, A_L> da;
+  Dma<T, B_KC, B_L> db;
   da.init(g.a, g.a_span, g.lda, m0, g.M, wave, lane);
   db.init(g.b, g.b_span, g.ldb, n0, g.N, wave, lane, B_KC ? 0 : g.b_split);
-  FragReader<T, A_KC, A_PK> ra(wm * kWaveM, lane);
-  FragReader<T, B_KC> rb(wn * kWaveN, lane);
+  FragReader<T, A_KC, lds_packed(A_L)> ra(wm * kWaveM, lane);
+  FragReader<T, B_KC, lds_packed(B_L)> rb(wn * kWaveN, lane);
   f32x4 acc[kFragM][kFragN];
 #pragma unroll
   for (int i = 0; i < kFragM; ++i)
@@ -414,16 +429,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int nt = 0; nt < kFragN; ++nt) cur.b[nt] = rb.read(st[0] + kOperandBytes, nt);
   int kt = 0;
   for (; kt + kStages <= nk; kt += kStages) {
-    kstep<T, A_KC, B_KC, 0, A_PK>(st, da, db, ra, rb, acc, cur, kt, g.K, wave);
-    kstep<T, A_KC, B_KC, 1, A_PK>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave);
-    kstep<T, A_KC, B_KC, 2, A_PK>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave);
-    kstep<T, A_KC, B_KC, 3, A_PK>(st, da, db, ra, rb, acc, cur, kt + 3, g.K, wave);
+    kstep<T, A_KC, B_KC, 0, A_L, B_L>(st, da, db, ra, rb, acc, cur, kt, g.K, wave);
+    kstep<T, A_KC, B_KC, 1, A_L, B_L>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave);
+    kstep<T, A_KC, B_KC, 2, A_L, B_L>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave);
+    kstep<T, A_KC, B_KC, 3, A_L, B_L>(st, da, db, ra, rb, acc, cur, kt + 3, g.K, wave);
   }
   // ragged end: the remaining nk - kt < kStages tiles start again at stage 0
   const int rem = nk - kt;
-  if (rem > 0) kstep<T, A_KC, B_KC, 0, A_PK>(st, da, db, ra, rb, acc, cur, kt, g.K, wave);
-  if (rem > 1) kstep<T, A_KC, B_KC, 1, A_PK>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave);
-  if (rem > 2) kstep<T, A_KC, B_KC, 2, A_PK>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave);
+  if (rem > 0) kstep<T, A_KC, B_KC, 0, A_L, B_L>(st, da, db, ra, rb, acc, cur, kt, g.K, wave);
+  if (rem > 1) kstep<T, A_KC, B_KC, 1, A_L, B_L>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave);
+  if (rem > 2) kstep<T, A_KC, B_KC, 2, A_L, B_L>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave);
   drain_barrier();  // no direct load may land in the LDS the epilogue reuses
 
   // ---- epilogue ----

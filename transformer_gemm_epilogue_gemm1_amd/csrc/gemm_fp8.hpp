@@ -26,7 +26,7 @@ struct Elem<uint8_t> {  // OCP e4m3, stored as its 8-bit code
 };
 
 // 32-row fragment t of a contraction-contiguous operand tile; PK: the tile
-// holds a tile-packed operand (kp_offset in tile_map.hpp).
+// is in the packed LDS order (kp_offset in tile_map.hpp).
 template <bool PK = false>
 struct FragReader8 {
   int off0;  // lane's byte offset of fragment 0, first chunk
@@ -59,9 +59,10 @@ struct Frags8 {
 // its reload for tile kt + 1; the loads of tile kt + kStages - 1 go out
 // after the products of A fragment kDmaIssueAfter8 (4 products, 256
 // matrix-core cycles, as in the bf16 step).
-template <int S, bool PK = false>
-__device__ __forceinline__ void kstep8(char* const (&st)[kStages], const Dma<uint8_t, true, PK>& da,
-                                       const Dma<uint8_t, true, PK>& db, FragReader8<PK>& ra, FragReader8<PK>& rb,
+template <int S, int L = kLayKC>
+__device__ __forceinline__ void kstep8(char* const (&st)[kStages], const Dma<uint8_t, true, L>& da,
+                                       const Dma<uint8_t, true, L>& db, FragReader8<lds_packed(L)>& ra,
+                                       FragReader8<lds_packed(L)>& rb,
                                        f32x16 (&acc)[kFrag8M][kFrag8N], Frags8& cur, int kt, int K, int wave) {
   constexpr int SL = (S + kStages - 1) % kStages;
   constexpr int SN = (S + 1) % kStages;
@@ -90,8 +91,9 @@ __device__ __forceinline__ void kstep8(char* const (&st)[kStages], const Dma<uin
 // C = A B^T for fp8 A[M, K] (g.a, g.lda) and B[N, K] (g.b, g.ldb); the
 // epilogue interface is the bf16 kernel's (16-row slabs, apply / end_slab /
 // finish).
-// PK: both operands are tile-packed (kp_unit), g.lda / g.ldb counting 16-byte chunks per row.
-template <class Epi, bool PK = false>
+// L: OpLayout of both operands (kLayPacked: tile-packed, kp_unit, with g.lda /
+// g.ldb counting 16-byte chunks per row).
+template <class Epi, int L = kLayKC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_fp8_kernel(
     GemmArgs g, typename Epi::Params ep) {
   static_assert(kStages == 4, "the stage arrays and the unrolled steps below assume four stages");
@@ -108,10 +110,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   map_tile(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, &tm, &tn);
   const int m0 = tm * kTileM, n0 = tn * kTileN;
 
-  Dma<uint8_t, true, PK> da, db;
+  Dma<uint8_t, true, L> da, db;
   da.init(g.a, g.a_span, g.lda, m0, g.M, wave, lane);
   db.init(g.b, g.b_span, g.ldb, n0, g.N, wave, lane);
-  FragReader8<PK> ra(wm * kWaveM, lane), rb(wn * kWaveN, lane);
+  FragReader8<lds_packed(L)> ra(wm * kWaveM, lane), rb(wn * kWaveN, lane);
   f32x16 acc[kFrag8M][kFrag8N];
 #pragma unroll
   for (int i = 0; i < kFrag8M; ++i)
@@ -135,15 +137,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int nt = 0; nt < kFrag8N; ++nt) cur.b[nt] = rb.read(st[0] + kOperandBytes, nt);
   int kt = 0;
   for (; kt + kStages <= nk; kt += kStages) {
-    kstep8<0, PK>(st, da, db, ra, rb, acc, cur, kt, g.K, wave);
-    kstep8<1, PK>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave);
-    kstep8<2, PK>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave);
-    kstep8<3, PK>(st, da, db, ra, rb, acc, cur, kt + 3, g.K, wave);
+    kstep8<0, L>(st, da, db, ra, rb, acc, cur, kt, g.K, wave);
+    kstep8<1, L>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave);
+    kstep8<2, L>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave);
+    kstep8<3, L>(st, da, db, ra, rb, acc, cur, kt + 3, g.K, wave);
   }
   const int rem = nk - kt;
-  if (rem > 0) kstep8<0, PK>(st, da, db, ra, rb, acc, cur, kt, g.K, wave);
-  if (rem > 1) kstep8<1, PK>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave);
-  if (rem > 2) kstep8<2, PK>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave);
+  if (rem > 0) kstep8<0, L>(st, da, db, ra, rb, acc, cur, kt, g.K, wave);
+  if (rem > 1) kstep8<1, L>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave);
+  if (rem > 2) kstep8<2, L>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave);
   drain_barrier();  // no direct load may land in the LDS the epilogue reuses
 
   // ---- epilogue: slab s = rows 16 s .. 16 s + 15 of the wavefront's 128 =

@@ -41,9 +41,13 @@ constexpr int kPartialCols = kWaveN;                // columns per partial-RMS t
 
 // ---- contraction-contiguous ("KC") operand tile ---------------------------
 // 256 operand rows x 64 bytes (four 16-byte chunks).  Chunk c of row r is
-// stored at chunk position c ^ ((r >> 2) & 3): the 16 rows one MFMA fragment
-// read touches (r0..r0+15 at one chunk) then cover all 64 banks once.
-CODA_HD int kc_swizzle(int r) { return (r >> 2) & 3; }
+// stored at chunk position c ^ ((r ^ (r >> 2)) & 3).  A fragment read takes
+// one chunk of 16 consecutive rows; with this swizzle every 4, 8 and 16
+// consecutive lanes of it hit distinct 16-byte bank groups within a 64-,
+// 128- and 256-byte window, so the read is conflict-free however the LDS
+// groups the lanes of a 16-byte read.  (With (r >> 2) & 3 alone only the
+// 16-lane window is conflict-free; 8 consecutive lanes then meet 2-way.)
+CODA_HD int kc_swizzle(int r) { return (r ^ (r >> 2)) & 3; }
 CODA_HD int kc_offset(int r, int c) { return r * kKTBytes + ((c ^ kc_swizzle(r)) << 4); }
 
 // ---- tile-packed contraction-contiguous ("KP") operand -----------------
