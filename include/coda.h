@@ -388,6 +388,22 @@ int64_t coda_packed_bytes_e4m3(int64_t rows, int64_t cols);
 coda_status coda_quantize_cols_e4m3_packed(int64_t K, int64_t N, const void* W, int64_t ldw,
                                            void* Wt8p, float* scales, void* stream);
 
+/* coda_quantize_rows_e4m3 with the codes X8 [M,K] written tile-packed into
+ * X8p (coda_packed_bytes_e4m3(M, K) bytes, 16-byte aligned; the rows past M
+ * in the last 16-row block are not written).  Same recipe and scales.  The
+ * fp8 backward quantises dY, dH and the weights this way for its products. */
+coda_status coda_quantize_rows_e4m3_packed(int64_t M, int64_t K, const void* X, int64_t ldx,
+                                           void* X8p, float* scales, void* stream);
+
+/* coda_quantize_rows_cols_e4m3 with both code arrays tile-packed: X8p holds
+ * the row codes [M,N] (coda_packed_bytes_e4m3(M, N) bytes) and Xt8p the
+ * transposed column codes [N,M] (coda_packed_bytes_e4m3(N, M) bytes), both
+ * 16-byte aligned.  M a multiple of 16, M <= 4194240; scales as in
+ * coda_quantize_rows_cols_e4m3. */
+coda_status coda_quantize_rows_cols_e4m3_packed(int64_t M, int64_t N, const void* X, int64_t ldx,
+                                                void* X8p, float* row_scales, void* Xt8p,
+                                                float* col_scales, void* stream);
+
 /* coda_gemm_res_prms_fp8 with Hg8 written tile-packed into Hg8p
  * (coda_packed_bytes_e4m3(M, D) bytes, 16-byte aligned); A8 and W1t8 as in
  * coda_gemm_res_prms_fp8. */

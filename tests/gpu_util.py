@@ -34,3 +34,25 @@ def round_to(dtype: str, x: np.ndarray) -> np.ndarray:
     """Host rounding of float32 values to the storage dtype (RNE), as float32."""
     x = np.asarray(x, dtype=np.float32)
     return ci.bf16_bits_to_f32(ci.bf16_bits(x)) if dtype == "bf16" else x
+
+
+def whole_max_rel(oracle_rows, got, M: int, block: int = 2048, check=None):
+    """max|got - ref| / max|ref| over EVERY row of each tensor in `got`.
+
+    The oracle runs on row blocks (exact: no step of the chain mixes rows),
+    so the full-size tensors are compared without holding them in float64.
+    oracle_rows(rows) -> dict of float64 arrays for those rows; got: name ->
+    device tensor with M rows first; check(rows, ref, host) runs extra
+    per-block assertions."""
+    num = {k: 0.0 for k in got}
+    den = {k: 0.0 for k in got}
+    for s in range(0, M, block):
+        rows = np.arange(s, min(M, s + block))
+        ref = oracle_rows(rows)
+        host = {k: t[s:s + len(rows)].float().cpu().numpy().astype(np.float64) for k, t in got.items()}
+        for k in got:
+            num[k] = max(num[k], float(np.max(np.abs(host[k] - ref[k]))))
+            den[k] = max(den[k], float(np.max(np.abs(ref[k]))))
+        if check is not None:
+            check(rows, ref, host)
+    return {k: num[k] / den[k] for k in got}

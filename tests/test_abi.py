@@ -304,6 +304,27 @@ def test_quantize_validation(lib):
     assert rc(0, 256, None, 256, None, 256, None, None, 0, None, None) == OK
 
 
+def test_quantize_packed_validation(lib):
+    q = lib.coda_quantize_rows_e4m3_packed
+    assert q(512, 264, H_, 264, HG_, PART_, None) == SHAPE                 # K not a multiple of 16
+    assert q(512, 256, None, 256, HG_, PART_, None) == NULL
+    assert q(512, 256, H_, 256, HG_, None, None) == NULL
+    assert q(512, 256, H_, 260, HG_, PART_, None) == ALIGN                 # ldx not a multiple of 8
+    assert q(512, 256, H_, 256, HG_ + 8, PART_, None) == ALIGN
+    assert q(512, 256, H_, 256, H_ + 4096, PART_, None) == ALIAS           # codes over X
+    assert q(512, 256, H_, 256, HG_, HG_ + 512 * 256 - 64, None) == ALIAS  # scales over the codes
+    assert q(0, 256, None, 256, None, None, None) == OK
+    rc = lib.coda_quantize_rows_cols_e4m3_packed
+    assert rc(520, 256, H_, 256, HG_, PART_, Y_, R2_, None) == SHAPE        # M not a multiple of 16
+    assert rc(512, 264, H_, 264, HG_, PART_, Y_, R2_, None) == SHAPE        # N not a multiple of 16
+    assert rc(512, 256, H_, 256, HG_, PART_, None, R2_, None) == NULL
+    assert rc(512, 256, H_, 256, HG_, PART_, Y_, None, None) == NULL
+    assert rc(512, 256, H_, 256, HG_, PART_, Y_ + 4, R2_, None) == ALIGN
+    assert rc(512, 256, H_, 256, HG_, PART_, HG_ + 256, R2_, None) == ALIAS  # the two code arrays
+    assert rc(512, 256, H_, 256, HG_, PART_, Y_, PART_ + 64, None) == ALIAS  # the two scale arrays
+    assert rc(0, 256, None, 256, None, None, None, None, None) == OK
+
+
 def rope_call(lib, dt=BF16, M=512, D=256, N2=1536, X=H_, ldx=None, W=W2_, ldw=None, r=R2_, pos=DY_, cs=DG_,
               max_pos=2048, nq=512, nk=512, dh=128, Y=Y_, ldy=None):
     return lib.coda_gemm_rowscale_rope(dt, M, D, N2, X, ldx or D, W, ldw or N2, r, pos, cs, max_pos, nq, nk, dh, Y,

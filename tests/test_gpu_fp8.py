@@ -134,14 +134,41 @@ def test_fp8_float8_dtype_accepted():
 
 
 @pytest.mark.slow
-def test_full_size_7b_fp8_sampled_rows():
+def test_full_size_7b_fp8_whole_tensor():
+    # every row of the 7B fp8 chain, with the checks of _check per row block:
+    # Y and H against the oracle, Hg8 bit-exact on the GPU's own H and at
+    # most one code from the oracle's, only where H itself rounded differently
     wl = ci.WORKLOADS["7b-fp8"]
     x, d, o = _run(wl, seed=0)
-    rng = np.random.default_rng(13)
-    rows = np.unique(np.concatenate([[0, 255, 256, wl.M - 1], rng.integers(0, wl.M, 20)]))
-    err, frac = _check(wl, x, o, rows=rows)
-    print(f"7b-fp8 sampled-row Y error {err:.3e}, differing codes {frac:.2e}")
-    assert torch.isfinite(o["Y"].float()).all().item()
+    num = {"Y": 0.0, "H": 0.0}
+    den = {"Y": 0.0, "H": 0.0}
+    ndiff = nhdiff = 0
+    for s0 in range(0, wl.M, 4096):
+        rows = np.arange(s0, min(wl.M, s0 + 4096))
+        orc = oracle.forward_fp8(x["A8"], x["sa"], x["W1t8"], x["sw1"], x["R"].f32, x["g"].f32, x["W2t8"],
+                                 x["sw2"], wl.eps, rows=rows)
+        blk = slice(s0, s0 + len(rows))
+        H = o["H"][blk].float().cpu().numpy()
+        Y = o["Y"][blk].float().cpu().numpy()
+        codes = o["Hg8"][blk].cpu().numpy()
+        hg = (H.astype(np.float32) * x["g"].f32[None, :]).astype(np.float32)
+        np.testing.assert_array_equal(codes, oracle.e4m3_encode(hg))
+        diff = codes != orc["Hg8"]
+        hdiff = H != orc["Hb"]
+        assert np.all(hdiff[diff])
+        assert np.abs(_magnitude_rank(codes) - _magnitude_rank(orc["Hg8"])).max() <= 1
+        np.testing.assert_allclose(o["r"][blk].cpu().numpy(), orc["r"], rtol=2e-3)
+        for k, got in (("Y", Y), ("H", H)):
+            num[k] = max(num[k], float(np.max(np.abs(got.astype(np.float64) - orc[k]))))
+            den[k] = max(den[k], float(np.max(np.abs(orc[k]))))
+        ndiff += int(diff.sum())
+        nhdiff += int(hdiff.sum())
+    n = wl.M * wl.D
+    err, herr = num["Y"] / den["Y"], num["H"] / den["H"]
+    print(f"7b-fp8 whole-tensor Y error {err:.3e}, H error {herr:.3e}, H bits differ {nhdiff / n:.2e}, "
+          f"codes differ {ndiff / n:.2e}", file=sys.__stderr__, flush=True)
+    assert err <= 1e-2 and herr <= 2.0 ** -8
+    assert nhdiff / n <= 0.03 and ndiff / n <= 0.005
 
 
 def _bf16_dev(x32):
@@ -204,6 +231,48 @@ def test_quantize_rows_cols_bit_exact(shape):
     np.testing.assert_array_equal(Xt8.cpu().numpy(), c_codes)
 
 
+@pytest.mark.parametrize("shape", [(1, 16), (3, 48), (257, 272), (300, 4096), (16, 28672), (4, 40016)], ids=str)
+def test_quantize_rows_packed_bit_exact(shape):
+    # the tile-packed row codes (the fp8 backward's dY, dH and weight
+    # operands) unpack to the oracle's codes; scales identical
+    M, K = shape
+    rng = np.random.default_rng(M + K + 1)
+    x = rng.standard_normal((M, K)).astype(np.float32) * np.exp(rng.uniform(-8, 8, size=(M, 1))).astype(np.float32)
+    x[0, :] = 0.0
+    if M > 2:
+        x[2, K // 2] = -1e4
+        x[1, :] *= np.float32(1e-40) / np.abs(x[1]).max()
+    dx, xf = _bf16_dev(x)
+    X8p, sc = coda.quantize_rows_e4m3_packed(dx)
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.quantize_rows(xf)
+    np.testing.assert_array_equal(sc.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(coda.unpack_e4m3(X8p, M).cpu().numpy(), c_ref)
+
+
+@pytest.mark.parametrize("shape", [(16, 16), (48, 272), (272, 528), (1040, 4096), (64, 28672)], ids=str)
+def test_quantize_rows_cols_packed_bit_exact(shape):
+    # both code arrays tile-packed (dY and dH in the fp8 backward): each
+    # unpacks to the oracle's row codes and transposed column codes
+    M, N = shape
+    rng = np.random.default_rng(M * 3 + N + 1)
+    x = (rng.standard_normal((M, N)).astype(np.float32) * np.exp(rng.uniform(-6, 6, size=(M, 1))).astype(np.float32)
+         * np.exp(rng.uniform(-3, 3, size=(1, N))).astype(np.float32))
+    x[1, :] = 0.0
+    x[:, 2] = 0.0
+    x[M - 1, N - 1] = -3e4
+    x[3, :] *= np.float32(1e-40) / np.abs(x[3]).max()
+    dx, xf = _bf16_dev(x)
+    X8p, sr, Xt8p, sc = coda.quantize_rows_cols_e4m3_packed(dx)
+    torch.cuda.synchronize()
+    r_codes, r_scales = oracle.quantize_rows(xf)
+    c_codes, c_scales = oracle.quantize_cols_transposed(xf)
+    np.testing.assert_array_equal(sr.cpu().numpy(), r_scales)
+    np.testing.assert_array_equal(coda.unpack_e4m3(X8p, M).cpu().numpy(), r_codes)
+    np.testing.assert_array_equal(sc.cpu().numpy(), c_scales)
+    np.testing.assert_array_equal(coda.unpack_e4m3(Xt8p, N).cpu().numpy(), c_codes)
+
+
 def test_chain_from_bf16_activation():
     # A quantised on the device gives the same codes as the oracle's recipe,
     # and the chain on them meets the fp8 bars
@@ -232,43 +301,83 @@ BWD_SHAPES = [  # M, K, D, N2: multiples of 16, ragged against the 256 tiles
 ]
 
 
+def _bwd_inputs(wl, seed):
+    """The backward's inputs generated on the host: dY, A, W1, g, W2 from the
+    seeded recipe, and H, r as the forward stores them, taken from the oracle
+    (H = bf16 rounding of the exact H, r in float32 from the exact H).  The
+    GPU and the oracle get the same values; no GPU output feeds the oracle."""
+    x = ci.make_inputs(wl, seed=seed, with_dy=True)
+    ref = oracle.forward(x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps)
+    H_bits = ci.bf16_bits(ref["H"].astype(np.float32))
+    H = ci.bf16_bits_to_f32(H_bits).astype(np.float64)
+    r = ref["r"].astype(np.float32)
+    d = {k: dev(v) for k, v in x.items()}
+    d["H"] = torch.from_numpy(H_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    d["r"] = torch.from_numpy(r).cuda()
+    return x, d, H, r.astype(np.float64)
+
+
 @pytest.mark.parametrize("shape", BWD_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_fp8_backward_matches_oracle(shape):
     wl = ci.custom_workload(*shape, wl_id=510)
-    x = ci.make_inputs(wl, seed=6, with_dy=True)
-    d = {k: dev(v) for k, v in x.items()}
-    H, Hg, r, Y, P = coda.fused_forward(d["A"], d["W1"], d["R"], d["g"], d["W2"], wl.eps)
-    grads = coda.fused_backward_fp8(d["dY"], d["A"], d["W1"], d["g"], d["W2"], H, r)
+    x, d, H, r = _bwd_inputs(wl, seed=6)
+    grads = coda.fused_backward_fp8(d["dY"], d["A"], d["W1"], d["g"], d["W2"], d["H"], d["r"])
     torch.cuda.synchronize()
     out = dict(zip(GRADS8, grads))
     orc = oracle.backward_fp8(x["dY"].f32, x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps,
-                              H=host_f32(H).astype(np.float64), r=r.cpu().numpy().astype(np.float64))
-    # the oracle quantises its own (fp64-computed, bf16-stored) dH and X_n;
-    # where their last bit differs from the GPU's, a code moves one e4m3 step
-    # (up to 2^-3 of that element).  Contractions over many rows average
-    # that out below 1e-2; over the 16 rows of the smallest case it can
-    # reach 2^-3 / sqrt(16) of a term, hence the wider bar there.  The
-    # stage-wise checks below take the GPU's own stored operands.
-    bar = 1e-2 if wl.M >= 256 else 3e-2
+                              H=H, r=r)
+    # The stored dH (dR): its only source of difference is G, which the fp8
+    # products accumulate at less than float32 precision (as in the forward,
+    # where H misses the bf16 rounding of the exact value in ~1% of
+    # elements) and the oracle in float64.  dH = r P - c H with P = g G and
+    # c = r^3 s / D, s = sum_j P_j H_j: to first order a relative error e of
+    # G moves dH by r dP (with P's bf16 step) and by dc H, where
+    # |dc| <= (r^3 / D) e sum_j |P_j H_j| -- s cancels heavily (sum |P H|
+    # up to 1e5 |s| here), so c carries G's error much amplified.  Bound
+    # with e = 2^-7: a bf16 step of r P and of dH, plus that term; and at
+    # most 3% of the elements differ (measured 0.8-0.9%).
+    dH = host_f32(out["dR"]).astype(np.float64)
+    diff = dH != orc["dH"]
+    assert diff.mean() <= 0.03, f"{diff.mean():.2e} of dH differs"
+    P = orc["G"] * x["g"].f32[None, :].astype(np.float64)
+    s_abs = np.sum(np.abs(P * H), axis=1)
+    bound = 2.0 ** -7 * (np.abs(r[:, None] * P) + np.abs(orc["dH"]) + (r ** 3 * s_abs / wl.D)[:, None] * np.abs(H))
+    assert np.all(np.abs(dH - orc["dH"]) <= bound), f"dH deviation {np.max(np.abs(dH - orc['dH']) / bound):.2f} of the bound"
+    # Those few one-step differences can flip an e4m3 code (or a row or
+    # column scale) of dH, which moves the dA and dW1 products it feeds by
+    # up to one e4m3 step of a term; the end-to-end bar is 1e-2, and 3e-2
+    # for the 16-row case, whose dW1 contracts over 16 rows only (one term
+    # of 16, one step of 2^-3: derivation in the design notes).
+    bar = {k: 1e-2 for k in GRADS8}
+    if wl.M < 64:
+        bar["dA"] = bar["dW1"] = 3e-2
     errs = {}
     for k in GRADS8:
         errs[k] = max_rel(host_f32(out[k]), orc[k])
-        assert errs[k] <= bar, f"{k}: error {errs[k]:.3e}"
-    print("fp8 backward errors", {k: f"{v:.2e}" for k, v in errs.items()}, file=sys.__stderr__, flush=True)
+        assert errs[k] <= bar[k], f"{k}: error {errs[k]:.3e}"
+    print("fp8 backward errors", {k: f"{v:.2e}" for k, v in errs.items()}, f"dH differing {diff.mean():.1e}",
+          file=sys.__stderr__, flush=True)
+    # As accurate as the recipe: against the exact (unquantised) gradient the
+    # GPU's fp8 gradients are as close as the oracle's fp8 gradients are.
+    exact = oracle.backward(x["dY"].f32, x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps)
+    for k in ("dA", "dW1", "dW2", "dg"):
+        e_gpu = max_rel(host_f32(out[k]), exact[k])
+        e_orc = max_rel(orc[k], exact[k])
+        assert e_gpu <= 1.25 * e_orc + 1e-3, f"{k}: {e_gpu:.3e} from the exact gradient, oracle {e_orc:.3e}"
     # stage-wise: dA and dW1 on the GPU's own stored dH, quantised on the host
     # (one bf16 rounding of an fp32 accumulation)
-    dH = host_f32(out["dR"])
     deq = lambda c_s: oracle.e4m3_decode(c_s[0]) * c_s[1][:, None].astype(np.float64)
-    dA_host = deq(oracle.quantize_rows(dH)) @ deq(oracle.quantize_rows(x["W1"].f32)).T
+    dHf = host_f32(out["dR"])
+    dA_host = deq(oracle.quantize_rows(dHf)) @ deq(oracle.quantize_rows(x["W1"].f32)).T
     assert max_rel(host_f32(out["dA"]), dA_host) <= 2.0 ** -8
-    dW1_host = deq(oracle.quantize_cols_transposed(x["A"].f32)) @ deq(oracle.quantize_cols_transposed(dH)).T
+    dW1_host = deq(oracle.quantize_cols_transposed(x["A"].f32)) @ deq(oracle.quantize_cols_transposed(dHf)).T
     assert max_rel(host_f32(out["dW1"]), dW1_host) <= 2.0 ** -8
-    Hf, rf = host_f32(H), r.cpu().numpy().astype(np.float32)
-    xn = round_to("bf16", (Hf * rf[:, None]).astype(np.float32) * x["g"].f32[None, :])
+    xn = round_to("bf16", (H.astype(np.float32) * r.astype(np.float32)[:, None]).astype(np.float32)
+                  * x["g"].f32[None, :])
     dW2_host = deq(oracle.quantize_cols_transposed(xn)) @ deq(oracle.quantize_cols_transposed(x["dY"].f32)).T
     assert max_rel(host_f32(out["dW2"]), dW2_host) <= 2.0 ** -8
     # repeat calls are bit-identical
-    again = coda.fused_backward_fp8(d["dY"], d["A"], d["W1"], d["g"], d["W2"], H, r)
+    again = coda.fused_backward_fp8(d["dY"], d["A"], d["W1"], d["g"], d["W2"], d["H"], d["r"])
     torch.cuda.synchronize()
     for a, b in zip(grads, again):
         assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,

@@ -19,7 +19,7 @@ import torch
 import coda_inputs as ci
 import oracle
 import transformer_gemm_epilogue_gemm1_amd as coda
-from tests.gpu_util import dev, host_bits, host_f32, max_rel, tolerance
+from tests.gpu_util import dev, host_bits, host_f32, max_rel, tolerance, whole_max_rel
 
 pytestmark = pytest.mark.gpu
 
@@ -61,7 +61,19 @@ def _check_against_oracle(wl, o, rows=None):
         assert np.array_equal(host_bits(Hr), host_bits(o["H"])), "fused H differs from the unfused chain's H"
         ref_err = max_rel(host_f32(Yr)[sel], orc["Y"])
         assert ref_err <= tolerance(wl.dtype), f"unfused Y error {ref_err:.3e}"
+        _comparable(err, ref_err, wl.dtype)
     return err, ref_err
+
+
+def _comparable(err, ref_err, dtype):
+    """The fused chain is as accurate as the operator-by-operator chain (the
+    CODA news article, results section: error comparable to the PyTorch
+    reference, sometimes smaller): its error against the oracle is at most
+    1.25x the unfused chain's, up to 5% of the tolerance (both chains round
+    Y and one operand of the second product to the storage dtype, in
+    different places)."""
+    assert err <= 1.25 * ref_err + 0.05 * tolerance(dtype), f"fused error {err:.3e} vs unfused {ref_err:.3e}"
+    print(f"Y error against the oracle: fused {err:.3e}, unfused {ref_err:.3e}", file=sys.__stderr__, flush=True)
 
 
 def _check_stages(wl, o):
@@ -200,22 +212,37 @@ FULL = ["1b-bf16", "7b-bf16", "70b-bf16"]
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled_rows(name):
-    # the full workloads in the benchmark's launch configuration; the oracle
-    # recomputes a sample of rows exactly (rows are independent)
+def test_full_size_whole_tensor(name):
+    # the full workloads in the benchmark's launch configuration, fused and
+    # unfused, against the oracle over every row (computed in row blocks)
     wl = ci.WORKLOADS[name]
-    o = _run(wl, seed=0, ref=(name != "70b-bf16"))
-    rng = np.random.default_rng(7)
-    rows = np.unique(np.concatenate([[0, 1, 255, 256, wl.M - 1], rng.integers(0, wl.M, 27)]))
-    err, ref_err = _check_against_oracle(wl, o, rows=rows)
-    print(f"{name}: sampled-row fused error {err:.3e}, unfused {ref_err}")
-    # whole-tensor properties at full size: r * RMS(H_stored) == 1 up to eps
+    o = _run(wl, seed=0, ref=True)
+    x = o["x"]
+    Hr, rr, Yr = o["ref"]
+    assert torch.equal(Hr.view(torch.int16), o["H"].view(torch.int16)), "fused H differs from the unfused chain's H"
+
+    W1, g, W2 = x["W1"].f64(), x["g"].f64(), x["W2"].f64()   # converted once, not per block
+
+    def orc(rows):
+        ref = oracle.forward(x["A"].f32, W1, x["R"].f32, g, W2, wl.eps, rows=rows)
+        # the unfused chain's Y is compared with the same reference Y; r as a column
+        return {"Y": ref["Y"], "Yref": ref["Y"], "H": ref["H"], "r": ref["r"][:, None]}
+
+    def check(rows, ref, host):
+        np.testing.assert_allclose(host["H"], ref["H"], rtol=2.0 ** -8 * 1.01, atol=1e-5)
+        np.testing.assert_allclose(host["r"], ref["r"], rtol=2e-3)
+
+    errs = whole_max_rel(orc, {"Y": o["Y"], "Yref": Yr, "H": o["H"], "r": o["r"][:, None]}, wl.M, check=check)
+    print(f"{name}: whole-tensor Y error fused {errs['Y']:.3e}, unfused {errs['Yref']:.3e}",
+          file=sys.__stderr__, flush=True)
+    assert errs["Y"] <= 1e-2 and errs["Yref"] <= 1e-2
+    _comparable(errs["Y"], errs["Yref"], wl.dtype)
+    # whole-tensor property: r * RMS(H_stored) == 1 up to eps
     H = o["H"].float()
     ms = (H * H).mean(dim=1)
-    rr = o["r"] * torch.sqrt(ms)
+    rrms = o["r"] * torch.sqrt(ms)
     expect = torch.sqrt(ms / (ms + wl.eps))
-    assert torch.max(torch.abs(rr - expect)).item() < 1e-5
-    assert torch.isfinite(o["Y"].float()).all().item()
+    assert torch.max(torch.abs(rrms - expect)).item() < 1e-5
 
 
 @pytest.mark.slow
@@ -224,20 +251,19 @@ def test_largest_matrix_spans():
     # under the 2 GiB - 256 limit of one matrix: the direct loads address A
     # with 32-bit offsets up to the top of that range, and the contraction
     # (32760 = 1023 k-tiles + 24) and Y's columns (127 tiles + 248) both end
-    # ragged.  Sampled rows against the oracle.
+    # ragged.  Every row against the oracle.
     M, K, D, N2 = 32768, 32760, 256, 32760
     wl = ci.custom_workload(M, K, D, N2, wl_id=130)
     assert M * K * 2 <= 2 ** 31 - 256 and M * N2 * 2 <= 2 ** 31 - 256
     o = _run(wl, seed=3, ref=False)
-    rng = np.random.default_rng(13)
-    rows = np.unique(np.concatenate([[0, 1, 255, 256, M - 256, M - 1], rng.integers(0, M, 10)]))
     x = o["x"]
-    orc = oracle.forward(x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps, rows=rows)
-    tr = torch.from_numpy(rows).cuda()
-    Y = o["Y"].index_select(0, tr).float().cpu().numpy()
-    H = o["H"].index_select(0, tr).float().cpu().numpy()
-    np.testing.assert_allclose(H, orc["H"], rtol=2.0 ** -8 * 1.01, atol=1e-5)
-    err = max_rel(Y, orc["Y"])
-    print(f"largest spans: sampled-row Y error {err:.3e}")
-    assert err <= 1e-2
-    assert torch.isfinite(o["Y"][-1].float()).all().item()
+    W1, g, W2 = x["W1"].f64(), x["g"].f64(), x["W2"].f64()
+
+    def orc(rows):
+        ref = oracle.forward(x["A"].f32, W1, x["R"].f32, g, W2, wl.eps, rows=rows)
+        return {"Y": ref["Y"], "H": ref["H"]}
+
+    errs = whole_max_rel(orc, {"Y": o["Y"], "H": o["H"]}, M)
+    print(f"largest spans: whole-tensor Y error {errs['Y']:.3e}, H error {errs['H']:.3e}", file=sys.__stderr__,
+          flush=True)
+    assert errs["Y"] <= 1e-2 and errs["H"] <= 2.0 ** -8

@@ -19,7 +19,7 @@ import torch
 import coda_inputs as ci
 import oracle
 import transformer_gemm_epilogue_gemm1_amd as coda
-from tests.gpu_util import dev, host_bits, host_f32, max_rel, tolerance
+from tests.gpu_util import dev, host_bits, host_f32, max_rel, tolerance, whole_max_rel
 
 pytestmark = pytest.mark.gpu
 
@@ -120,15 +120,19 @@ def test_without_row_scale_and_strided():
 
 
 @pytest.mark.slow
-def test_full_size_7b_sampled_rows():
-    # the 7B shape (F = 14336) in the benchmark's launch configuration
+def test_full_size_7b_whole_tensor():
+    # the 7B shape (F = 14336) in the benchmark's launch configuration, Z
+    # against the oracle over every row
     wl = ci.WORKLOADS["7b-bf16"]
     x, d, o = _run(wl, seed=0, keep_y=False)
-    rng = np.random.default_rng(9)
-    rows = np.unique(np.concatenate([[0, 255, 256, wl.M - 1], rng.integers(0, wl.M, 20)]))
-    err = _check(wl, x, o, rows=rows)
-    print(f"7b-bf16 SwiGLU sampled-row error {err:.3e}")
-    assert torch.isfinite(o["Z"].float()).all().item()
+    W1, g, W2 = x["W1"].f64(), x["g"].f64(), x["W2"].f64()
+
+    def orc(rows):
+        return {"Z": oracle.forward_swiglu(x["A"].f32, W1, x["R"].f32, g, W2, wl.eps, rows=rows)["Z"]}
+
+    err = whole_max_rel(orc, {"Z": o["Z"]}, wl.M)["Z"]
+    print(f"7b-bf16 SwiGLU whole-tensor Z error {err:.3e}", file=sys.__stderr__, flush=True)
+    assert err <= 1e-2
 
 
 # ---- backward through the gate (coda_swiglu_bwd), then the chain's backward ----
@@ -164,18 +168,23 @@ def test_swiglu_backward_matches_oracle(shape, dtype):
 
 
 @pytest.mark.slow
-def test_swiglu_bwd_full_size_sampled_rows():
-    # the gate's backward at the 7B shape (M = 16384, F = 14336) on sampled rows
+def test_swiglu_bwd_full_size_whole_tensor():
+    # the gate's backward at the 7B shape (M = 16384, F = 14336), every row;
+    # Y and dZ drawn on the host (seeded) and uploaded
     wl = ci.WORKLOADS["7b-bf16"]
     F = wl.N2 // 2
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(11)
-    Y = (torch.randn((wl.M, 2 * F), device="cuda", generator=gen) * 2.0).bfloat16()
-    dZ = torch.randn((wl.M, F), device="cuda", generator=gen).bfloat16()
+    rng = np.random.default_rng(11)
+    y_bits = ci.bf16_bits((rng.standard_normal((wl.M, 2 * F), dtype=np.float32) * 2.0).astype(np.float32))
+    dz_bits = ci.bf16_bits(rng.standard_normal((wl.M, F), dtype=np.float32))
+    Y = torch.from_numpy(y_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    dZ = torch.from_numpy(dz_bits.view(np.int16)).cuda().view(torch.bfloat16)
     dY = torch.full_like(Y, float("nan"))
     coda.coda_swiglu_bwd(dZ, Y, dY)
     torch.cuda.synchronize()
-    rows = torch.tensor([0, 1, 4097, 9000, wl.M - 1], device="cuda")
-    ref = oracle.swiglu_dy(host_f32(dZ[rows]).astype(np.float64), host_f32(Y[rows]).astype(np.float64))
-    assert max_rel(host_f32(dY[rows]), ref) <= 2.0 ** -8
-    assert torch.isfinite(dY.float()).all().item()
+
+    def orc(rows):
+        return {"dY": oracle.swiglu_dy(ci.bf16_bits_to_f32(dz_bits[rows]), ci.bf16_bits_to_f32(y_bits[rows]))}
+
+    err = whole_max_rel(orc, {"dY": dY}, wl.M, block=1024)["dY"]
+    print(f"7b SwiGLU gate backward whole-tensor dY error {err:.3e}", file=sys.__stderr__, flush=True)
+    assert err <= 2.0 ** -8

@@ -286,3 +286,93 @@ def test_fp8_backward_quantisation_axes(which):
     else:
         np.testing.assert_array_equal(b[:, sel], 8 * a[:, sel])
         np.testing.assert_array_equal(np.delete(b, sel, axis=1), np.delete(a, sel, axis=1))
+
+
+# ---- the backward's bf16 storage (P, X_n, dH), pinned independently -------
+from tests import fp8_backward_brute as bb  # noqa: E402
+
+
+def _bwd_pin_case(seed, M=16, K=16, D=16, N2=32):
+    # the backward's inputs, with H and r as the forward stores them (H in
+    # bf16, r in float32)
+    c = _bwd_case(seed, M, K, D, N2)
+    H = oracle.bf16_round(c["A"].astype(np.float64) @ c["W1"].astype(np.float64) + c["R"])
+    r = (1.0 / np.sqrt(np.mean(H * H, axis=1) + 1e-5)).astype(np.float32).astype(np.float64)
+    return c, H, r
+
+
+def _listed(*arrays):
+    return [np.asarray(a, dtype=np.float64).tolist() for a in arrays]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_fp8_backward_matches_brute_force(seed):
+    c, H, r = _bwd_pin_case(seed)
+    got = oracle.backward_fp8(c["dY"], c["A"], c["W1"], c["R"], c["g"], c["W2"], 1e-5, H=H, r=r)
+    ref = bb.backward(*_listed(c["dY"], c["A"], c["W1"], c["g"], c["W2"], H, r))
+    for k in ("dA", "dR", "dW1", "dW2", "dg"):
+        np.testing.assert_allclose(got[k], np.array(ref[k]), rtol=1e-12, atol=1e-13, err_msg=k)
+
+
+def _bwd_fp8_mutant(kind, c, H, r):
+    """oracle.backward_fp8's steps with one planted mistake in where a value is
+    stored in bf16."""
+    from oracle.fp8 import _deq_cols, _deq_rows
+    rnd = oracle.bf16_round
+    g = np.asarray(c["g"], np.float64)
+    D = c["W1"].shape[1]
+    G = _deq_rows(c["dY"], True) @ _deq_rows(c["W2"], True).T
+    P = G * g[None, :]
+    s = np.sum((rnd(P) if kind == "s_from_stored_P" else P) * H, axis=1)
+    if kind == "Xn_not_stored":
+        Xn = (H * r[:, None]) * g[None, :]
+    elif kind == "Xn_rounded_before_g":
+        Xn = rnd(rnd(H * r[:, None]) * g[None, :])
+    else:
+        Xn = rnd((H * r[:, None]) * g[None, :])
+    cc = (r ** 3 * s / D)[:, None]
+    Pu = P if kind == "dH_from_unrounded_P" else rnd(P)
+    if kind == "dH_terms_rounded_first":
+        dH = rnd(rnd(r[:, None] * Pu) - rnd(cc * H))
+    elif kind == "dH_not_stored":
+        dH = r[:, None] * Pu - cc * H
+    else:
+        dH = rnd(r[:, None] * Pu - cc * H)
+    return {"dW2": _deq_cols(Xn, True).T @ _deq_cols(c["dY"], True),
+            "dA": _deq_rows(dH, True) @ _deq_rows(c["W1"], True).T,
+            "dW1": _deq_cols(c["A"], True).T @ _deq_cols(dH, True)}
+
+
+@pytest.mark.parametrize("kind", ["dH_from_unrounded_P", "dH_terms_rounded_first", "dH_not_stored",
+                                  "Xn_not_stored", "Xn_rounded_before_g", "s_from_stored_P"])
+def test_fp8_backward_storage_pin_rejects_planted_mistakes(kind):
+    # each misplaced bf16 rounding moves some stored value by an ulp, which
+    # flips e4m3 codes (or a row / column scale) of a quantised product: the
+    # products through those codes leave the brute force by far more than
+    # the brute force and the oracle differ (3e-16)
+    c, H, r = _bwd_pin_case(0)
+    ref = bb.backward(*_listed(c["dY"], c["A"], c["W1"], c["g"], c["W2"], H, r))
+    m = _bwd_fp8_mutant(kind, c, H, r)
+    worst = max(np.max(np.abs(m[k] - np.array(ref[k]))) / np.max(np.abs(np.array(ref[k]))) for k in m)
+    assert worst > 1e-3, f"{kind} not rejected ({worst:.1e})"
+
+
+def test_fp8_backward_quantises_the_stored_bf16_xn():
+    # Hand-worked: M = 2, K = D = N2 = 1, g = 1, dY = 1, H = (256, 1), r =
+    # (1, r1) with r1 = float32(0.60725) = 0.6072499752...  X_n = H r g is
+    # (256, r1); stored in bf16 the second is 0.60546875 (spacing 2^-8).
+    # X_n's column scale is s = float32(256 / 448); 256 / s rounds to the
+    # code 448, and 0.60546875 / s = 1.0596 to the code 1.0 -- while the
+    # unrounded r1 / s = 1.0627 would pass the midpoint 1.0625 to 1.125.
+    # dY's column codes are 448 with scale t = float32(1 / 448), so
+    # dW2 = (448 s)(448 t) + (1.0 s)(448 t).
+    r1 = float(np.float32(0.60725))
+    assert oracle.bf16_round(np.array([r1]))[0] == 0.60546875
+    s = float(np.float32(256.0) / np.float32(448.0))
+    t = float(np.float32(1.0) / np.float32(448.0))
+    one = np.ones((2, 1), np.float32)
+    out = oracle.backward_fp8(one, one, np.ones((1, 1), np.float32), np.zeros((2, 1)), np.ones(1, np.float32),
+                              np.ones((1, 1), np.float32), 0.0, H=np.array([[256.0], [1.0]]), r=np.array([1.0, r1]))
+    assert out["Xn"][1, 0] == 0.60546875
+    assert out["dW2"][0, 0] == pytest.approx((448 * s) * (448 * t) + (1.0 * s) * (448 * t), rel=1e-15)
+    assert out["dW2"][0, 0] != pytest.approx((448 * s) * (448 * t) + (1.125 * s) * (448 * t), rel=1e-6)

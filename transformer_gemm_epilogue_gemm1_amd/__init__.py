@@ -15,7 +15,8 @@ from .binding import (coda_ce_combine, coda_chain_bwd, coda_chain_bwd_workspace_
                       coda_gemm_rowscale_rope, coda_rope_bwd, fused_forward_rope, rope_cache,
                       coda_gemm_rowscale_ce_bwd, fused_backward_ce,
                       fused_forward_fp8_from_bf16, quantize_rows_e4m3, quantize_weight_e4m3,
-                      quantize_rows_cols_e4m3, fused_backward_fp8,
+                      quantize_rows_cols_e4m3, fused_backward_fp8, quantize_rows_e4m3_packed,
+                      quantize_rows_cols_e4m3_packed,
                       coda_packed_bytes, packed_empty, unpack, coda_gemm_res_prms_packed,
                       coda_gemm_rowscale_packed, fused_forward_packed,
                       packed_empty_e4m3, unpack_e4m3, quantize_weight_e4m3_packed,

@@ -37,6 +37,8 @@ SIGNATURES = {
     "coda_gemm_rowscale_packed": (c_int, [c_i64, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp]),
     "coda_packed_bytes_e4m3": (c_i64, [c_i64, c_i64]),
     "coda_quantize_cols_e4m3_packed": (c_int, [c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp]),
+    "coda_quantize_rows_e4m3_packed": (c_int, [c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp]),
+    "coda_quantize_rows_cols_e4m3_packed": (c_int, [c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "coda_gemm_res_prms_fp8_packed": (c_int, [c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp,
                                               c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp]),
     "coda_gemm_rowscale_fp8_packed": (c_int, [c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp]),

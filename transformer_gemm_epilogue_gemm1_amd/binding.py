@@ -686,6 +686,34 @@ def quantize_rows_cols_e4m3(X, stream=None):
     return X8, sr, Xt8, sc
 
 
+def quantize_rows_e4m3_packed(X, stream=None):
+    """quantize_rows_e4m3 with the codes [M, K] written tile-packed
+    (packed_empty_e4m3(M, K)); returns (X8p, scales)."""
+    M, K = X.shape
+    ldx = _mat(X, "X", torch.bfloat16, (M, K))
+    X8p = packed_empty_e4m3(M, K, X.device)
+    sc = torch.empty((M,), device=X.device, dtype=torch.float32)
+    st = _lib.load().coda_quantize_rows_e4m3_packed(M, K, X.data_ptr(), ldx, X8p.data_ptr(), sc.data_ptr(),
+                                                    _stream(stream))
+    _lib.check("coda_quantize_rows_e4m3_packed", st)
+    return X8p, sc
+
+
+def quantize_rows_cols_e4m3_packed(X, stream=None):
+    """quantize_rows_cols_e4m3 with both code arrays tile-packed: returns
+    (X8p [M, N] packed, row scales, Xt8p [N, M] packed, column scales)."""
+    M, N = X.shape
+    ldx = _mat(X, "X", torch.bfloat16, (M, N))
+    X8p = packed_empty_e4m3(M, N, X.device)
+    Xt8p = packed_empty_e4m3(N, M, X.device)
+    sr = torch.empty((M,), device=X.device, dtype=torch.float32)
+    sc = torch.empty((N,), device=X.device, dtype=torch.float32)
+    st = _lib.load().coda_quantize_rows_cols_e4m3_packed(M, N, X.data_ptr(), ldx, X8p.data_ptr(), sr.data_ptr(),
+                                                         Xt8p.data_ptr(), sc.data_ptr(), _stream(stream))
+    _lib.check("coda_quantize_rows_cols_e4m3_packed", st)
+    return X8p, sr, Xt8p, sc
+
+
 def fused_forward_fp8(A8, sa, W1t8, sw1, R, g, W2t8, sw2, eps: float, stream=None):
     """The fused chain with fp8 GEMM operands: returns (H, Hg8, r, Y, partials)."""
     M, D, N2 = A8.shape[0], W1t8.shape[0], W2t8.shape[0]

@@ -870,6 +870,44 @@ coda_status coda_quantize_cols_e4m3_packed(int64_t K, int64_t N, const void* W, 
   return launch_status("coda_quantize_cols_e4m3_packed");
 }
 
+coda_status coda_quantize_rows_e4m3_packed(int64_t M, int64_t K, const void* X, int64_t ldx, void* X8p,
+                                           float* scales, void* stream) {
+  coda_status st = check_dims_fp8(M, {{"K", K}});
+  if (st != CODA_OK) return st;
+  if (M == 0) return ok();
+  const int64_t x8_bytes = packed_bytes_e4m3(M, K);
+  const Mat mX{X, M, K, ldx, 2, "X"}, mX8{X8p, 1, x8_bytes, x8_bytes, 1, "X8"}, ms{scales, 1, M, M, 4, "scales"};
+  if ((st = check_mat(mX, 8)) != CODA_OK || (st = check_mat(mX8, 16)) != CODA_OK) return st;
+  if (scales == nullptr) return fail(CODA_ERR_NULL, "scales is NULL");
+  if (((uintptr_t)scales & 3) != 0) return fail(CODA_ERR_ALIGN, "scales is not 4-byte aligned");
+  const Mat outs[2] = {mX8, ms};
+  if ((st = check_alias(outs, 2, &mX, 1)) != CODA_OK) return st;
+  q_rows(X, ldx, (int)M, (int)K, X8p, K, scales, (hipStream_t)stream, K / 16);
+  return launch_status("coda_quantize_rows_e4m3_packed");
+}
+
+coda_status coda_quantize_rows_cols_e4m3_packed(int64_t M, int64_t N, const void* X, int64_t ldx, void* X8p,
+                                                float* row_scales, void* Xt8p, float* col_scales, void* stream) {
+  coda_status st = check_dims_fp8(M, {{"N", N}});
+  if (st != CODA_OK) return st;
+  if (M == 0) return ok();
+  if (M % 16 != 0) return fail(CODA_ERR_SHAPE, "M = %lld is not a multiple of 16", (long long)M);
+  if (M > kMaxColRows) return fail(CODA_ERR_SHAPE, "M = %lld exceeds %lld rows", (long long)M, (long long)kMaxColRows);
+  const int64_t x8_bytes = packed_bytes_e4m3(M, N), xt_bytes = packed_bytes_e4m3(N, M);
+  const Mat mX{X, M, N, ldx, 2, "X"}, mX8{X8p, 1, x8_bytes, x8_bytes, 1, "X8"}, mXt{Xt8p, 1, xt_bytes, xt_bytes, 1, "Xt8"};
+  const Mat msr{row_scales, 1, M, M, 4, "row_scales"}, msc{col_scales, 1, N, N, 4, "col_scales"};
+  if ((st = check_mat(mX, 8)) != CODA_OK || (st = check_mat(mX8, 16)) != CODA_OK ||
+      (st = check_mat(mXt, 16)) != CODA_OK)
+    return st;
+  if (row_scales == nullptr || col_scales == nullptr) return fail(CODA_ERR_NULL, "row_scales and col_scales must be set");
+  if ((((uintptr_t)row_scales | (uintptr_t)col_scales) & 3) != 0)
+    return fail(CODA_ERR_ALIGN, "row_scales / col_scales not 4-byte aligned");
+  const Mat outs[4] = {mX8, msr, mXt, msc};
+  if ((st = check_alias(outs, 4, &mX, 1)) != CODA_OK) return st;
+  q_rows_cols(X, ldx, (int)M, (int)N, X8p, N, row_scales, Xt8p, M, col_scales, (hipStream_t)stream, N / 16, M / 16);
+  return launch_status("coda_quantize_rows_cols_e4m3_packed");
+}
+
 coda_status coda_gemm_res_prms_fp8_packed(int64_t M, int64_t K, int64_t D, const void* A8, int64_t lda,
                                           const float* sa, const void* W1t8, int64_t ldw1t, const float* sw1,
                                           const void* R, int64_t ldr, const void* g, void* H, int64_t ldh,
