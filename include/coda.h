@@ -483,6 +483,34 @@ coda_status coda_chain_bwd(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64
                            void* dA, void* dR, void* dW1, void* dW2, float* dg,
                            void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of the scratch array coda_chain_bwd_noalloc keeps in device memory
+ * (one copy on each GPU the library runs on, held until the process ends). */
+#define CODA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* coda_chain_bwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving or training loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and errors as coda_chain_bwd, without
+ * the workspace: the call allocates nothing (no hipMalloc, no library
+ * allocation) and keeps X_n, the partial sums and c in the library's static
+ * scratch array instead.  G and dA read W2 and W1 in place (no transposed
+ * copies), which gives bit-identical results.
+ * Limit: the shape must need at most CODA_NOALLOC_SCRATCH_BYTES of scratch,
+ *   X_n M*D (dtype) + 4*T*M + 4*U*D + 4*M bytes, each part rounded up to a
+ *   multiple of 256, with T = 4*ceil(D/256) and U = ceil(M/128)
+ *   (bf16: M*D up to about 31M elements, e.g. M = 7680 at D = 4096).
+ * Larger shapes fail with CODA_ERR_WORKSPACE before anything is enqueued.
+ * The scratch is shared by every call on one GPU and keeps the last call's
+ * contents (nothing in it needs to start at zero): calls that overlap on
+ * one GPU -- on two streams, or from two host threads -- race on it, so
+ * the caller orders them.  The first call on each device looks up the
+ * array's device address (hipGetSymbolAddress); a failure there is
+ * CODA_ERR_HIP. */
+coda_status coda_chain_bwd_noalloc(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64_t N2,
+                                   const void* dY, const void* A, const void* W1, const void* g,
+                                   const void* W2, const void* H, const float* r,
+                                   void* dA, void* dR, void* dW1, void* dW2, float* dg,
+                                   void* stream);
+
 /* Backward of the chain with e4m3 products (the fp8 recipe above, carried to
  * the backward; the pages give none).  Every product takes e4m3 operands
  * quantised along its contraction, as coda_quantize_rows_e4m3 does:

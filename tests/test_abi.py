@@ -510,6 +510,45 @@ def test_chain_bwd_rejects(lib, kw, status):
     assert lib.coda_last_error().decode() != ""
 
 
+def chain_bwd_noalloc(lib, **kw):
+    a = dict(dt=BF16, M=512, K=256, D=256, N2=512, dY=DY_, A=A_, W1=W1_, g=G_, W2=W2_, H=H_, r=R2_, dA=DA_,
+             dR=DR_, dW1=DW1_, dW2=DW2_, dg=DG_)
+    a.update(kw)
+    return lib.coda_chain_bwd_noalloc(a["dt"], a["M"], a["K"], a["D"], a["N2"], a["dY"], a["A"], a["W1"], a["g"],
+                                      a["W2"], a["H"], a["r"], a["dA"], a["dR"], a["dW1"], a["dW2"], a["dg"], None)
+
+
+def _noalloc_need(M, D, es):
+    al = lambda x: (x + 255) // 256 * 256
+    T, U = 4 * ((D + 255) // 256), (M + 127) // 128
+    return al(al(al(al(M * D * es) + T * M * 4) + U * D * 4) + M * 4)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=2), DTYPE),
+    (dict(K=12), SHAPE),
+    (dict(dY=None), NULL),
+    (dict(dg=None), NULL),
+    (dict(r=R2_ + 1), ALIGN),
+    (dict(dR=H_), ALIAS),
+    (dict(dW1=DR_ + 4096), ALIAS),
+    (dict(M=7936, D=4096, K=256, N2=512), WS),    # X_n and the partial sums just over the 64 MiB scratch
+    (dict(M=16384, D=4096, K=4096, N2=28672), WS),  # the 7B backward needs a workspace
+])
+def test_chain_bwd_noalloc_rejects(lib, kw, status):
+    # validation happens before anything touches a device (so these run
+    # without a GPU); shapes whose scratch exceeds the static array fail
+    assert chain_bwd_noalloc(lib, **kw) == status
+    assert lib.coda_last_error().decode() != ""
+
+
+def test_chain_bwd_noalloc_limit():
+    # the header's limit and the scratch the two rejected shapes need
+    assert _noalloc_need(7680, 4096, 2) <= 64 << 20 < _noalloc_need(7936, 4096, 2)
+    hdr = open(HEADER).read()
+    assert "#define CODA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in hdr
+
+
 def test_chain_bwd_empty_still_checks_weights(lib):
     # with M = 0 the M-row arguments may be NULL, the weight gradients may not
     none = dict(dY=None, A=None, H=None, r=None, dA=None, dR=None)

@@ -7,6 +7,7 @@ if it has not been built.
 from . import _lib
 from ._lib import CodaError
 from .binding import (coda_ce_combine, coda_chain_bwd, coda_chain_bwd_workspace_bytes,  # noqa: F401
+                      coda_chain_bwd_noalloc,
                       coda_gemm_res_prms, coda_gemm_rowscale_lse, fused_forward_ce,
                       coda_gemm_res_prms_fp8, coda_gemm_rowscale, coda_gemm_rowscale_fp8,
                       coda_gemm_rowscale_swiglu, coda_prms_num_partials, coda_ref_chain,

@@ -81,6 +81,9 @@ SIGNATURES = {
     "coda_chain_bwd": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64,
                                c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "coda_chain_bwd_noalloc": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64,
+                                       c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                       c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "coda_status_string": (ctypes.c_char_p, [c_int]),
     "coda_last_error": (ctypes.c_char_p, []),
 }

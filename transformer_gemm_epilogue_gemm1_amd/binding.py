@@ -419,6 +419,28 @@ def coda_chain_bwd(dY, A, W1, g, W2, H, r, dA, dR, dW1, dW2, dg, ws, stream=None
     _lib.check("coda_chain_bwd", st)
 
 
+def coda_chain_bwd_noalloc(dY, A, W1, g, W2, H, r, dA, dR, dW1, dW2, dg, stream=None) -> None:
+    """coda_chain_bwd without a workspace: the library's static scratch holds
+    X_n, the partial sums and c (see coda.h for the size limit).  For callers
+    that cannot allocate; calls that overlap on one GPU race on the scratch."""
+    lib = _lib.load()
+    dt = A.dtype
+    M, K = A.shape
+    D = W1.shape[1]
+    N2 = W2.shape[1]
+    for t, n, dtp, shp in ((dY, "dY", dt, (M, N2)), (A, "A", dt, (M, K)), (W1, "W1", dt, (K, D)),
+                           (g, "g", dt, (D,)), (W2, "W2", dt, (D, N2)), (H, "H", dt, (M, D)),
+                           (r, "r", torch.float32, (M,)), (dA, "dA", dt, (M, K)), (dR, "dR", dt, (M, D)),
+                           (dW1, "dW1", dt, (K, D)), (dW2, "dW2", dt, (D, N2)),
+                           (dg, "dg", torch.float32, (D,))):
+        _mat(t, n, dtp, shp)
+        _dense(t, n)
+    st = lib.coda_chain_bwd_noalloc(_dtype_code(A), M, K, D, N2, dY.data_ptr(), A.data_ptr(), W1.data_ptr(),
+                                    g.data_ptr(), W2.data_ptr(), H.data_ptr(), r.data_ptr(), dA.data_ptr(),
+                                    dR.data_ptr(), dW1.data_ptr(), dW2.data_ptr(), dg.data_ptr(), _stream(stream))
+    _lib.check("coda_chain_bwd_noalloc", st)
+
+
 # ---- conveniences that allocate outputs with torch, then call the above ----
 
 def fused_forward(A, W1, R, g, W2, eps: float, stream=None):

@@ -9,7 +9,9 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/coda.h"
 #include "epilogues.hpp"
@@ -262,11 +264,16 @@ struct BwdWs {
   }
 };
 
-template <typename T>
+// IN_PLACE: G and dA read W2 and W1 where they lie, as contraction-contiguous
+// B operands, and the workspace holds no transposed weights (BwdWs with
+// K = N2 = 0).  The products see the same fragments either way, so the
+// results are bit-identical; the transposes make the whole backward about 1%
+// faster at 7B.
+template <typename T, bool IN_PLACE = false>
 coda_status chain_bwd_impl(int M, int K, int D, int N2, const void* dY, const void* A, const void* W1,
                            const void* g, const void* W2, const void* H, const float* r, void* dA, void* dR,
                            void* dW1, void* dW2, float* dg, char* ws, hipStream_t s) {
-  const BwdWs L(M, K, D, N2, sizeof(T));
+  const BwdWs L(M, IN_PLACE ? 0 : K, D, IN_PLACE ? 0 : N2, sizeof(T));
   T* Xn = (T*)(ws + L.xn);
   float* srow = (float*)(ws + L.srow);
   float* dgcol = (float*)(ws + L.dgcol);
@@ -276,18 +283,25 @@ coda_status chain_bwd_impl(int M, int K, int D, int N2, const void* dY, const vo
   const int Tn = (int)num_partials(D), U = (M + kWaveM - 1) / kWaveM;
   coda_status st;
   if (M > 0) {
-    // 0. W2^T and W1^T: the contraction of G and dA then runs across their
-    // rows (transposing LDS reads, no bank conflicts) instead of along them
-    hipLaunchKernelGGL(transpose_kernel<T>, dim3((unsigned)((N2 + 63) / 64), (unsigned)((D + 63) / 64)), dim3(256), 0,
-                       s, (const T*)W2, N2, D, N2, W2t, D);
-    hipLaunchKernelGGL(transpose_kernel<T>, dim3((unsigned)((D + 63) / 64), (unsigned)((K + 63) / 64)), dim3(256), 0,
-                       s, (const T*)W1, D, K, D, W1t, K);
-    if ((st = launch_status("coda_chain_bwd transpose")) != CODA_OK) return st;
-    // 1. G = dY W2^T with the P / X_n / partial-sum epilogue
     typename EpiBwdG<T>::Params ep{(const T*)H, (const T*)g, r, (T*)dR, Xn, D, srow, dgcol};
-    if ((st = launch_gemm<T, true, false, EpiBwdG<T>>("coda_chain_bwd G", M, D, N2, dY, N2, W2t, D, ep, s)) !=
-        CODA_OK)
-      return st;
+    if constexpr (IN_PLACE) {
+      // 1. G = dY W2^T with the P / X_n / partial-sum epilogue, W2 [D, N2] in place
+      if ((st = launch_gemm<T, true, true, EpiBwdG<T>>("coda_chain_bwd G", M, D, N2, dY, N2, W2, N2, ep, s)) !=
+          CODA_OK)
+        return st;
+    } else {
+      // 0. W2^T and W1^T: the contraction of G and dA then runs across their
+      // rows (transposing LDS reads, no bank conflicts) instead of along them
+      hipLaunchKernelGGL(transpose_kernel<T>, dim3((unsigned)((N2 + 63) / 64), (unsigned)((D + 63) / 64)), dim3(256),
+                         0, s, (const T*)W2, N2, D, N2, W2t, D);
+      hipLaunchKernelGGL(transpose_kernel<T>, dim3((unsigned)((D + 63) / 64), (unsigned)((K + 63) / 64)), dim3(256),
+                         0, s, (const T*)W1, D, K, D, W1t, K);
+      if ((st = launch_status("coda_chain_bwd transpose")) != CODA_OK) return st;
+      // 1. G = dY W2^T with the P / X_n / partial-sum epilogue
+      if ((st = launch_gemm<T, true, false, EpiBwdG<T>>("coda_chain_bwd G", M, D, N2, dY, N2, W2t, D, ep, s)) !=
+          CODA_OK)
+        return st;
+    }
   }
   // 2. c and dg (with M = 0 only the columns: dg = 0)
   hipLaunchKernelGGL(bwd_combine_kernel, dim3((unsigned)((M + 63) / 64 + (D + 63) / 64)), dim3(256), 0, s, srow,
@@ -299,11 +313,13 @@ coda_status chain_bwd_impl(int M, int K, int D, int N2, const void* dY, const vo
     const int blocks = (int)((nchunks + 255) / 256 < 16384 ? (nchunks + 255) / 256 : 16384);
     hipLaunchKernelGGL(dh_finalize_kernel<T>, dim3(blocks), dim3(256), 0, s, (T*)dR, (const T*)H, r, c, D, nchunks);
     if ((st = launch_status("coda_chain_bwd dH")) != CODA_OK) return st;
-    // 4. dA = dH W1^T  (W1^T [D, K] read row-contiguously)
-    if ((st = launch_gemm<T, true, false, EpiRowScale<T>>("coda_chain_bwd dA", M, K, D, dR, D, W1t, K,
-                                                          typename EpiRowScale<T>::Params{nullptr, (T*)dA, K}, s)) !=
-        CODA_OK)
-      return st;
+    // 4. dA = dH W1^T  (W1^T [D, K] read row-contiguously, or W1 [K, D] in place)
+    const typename EpiRowScale<T>::Params epa{nullptr, (T*)dA, K};
+    if constexpr (IN_PLACE)
+      st = launch_gemm<T, true, true, EpiRowScale<T>>("coda_chain_bwd dA", M, K, D, dR, D, W1, D, epa, s);
+    else
+      st = launch_gemm<T, true, false, EpiRowScale<T>>("coda_chain_bwd dA", M, K, D, dR, D, W1t, K, epa, s);
+    if (st != CODA_OK) return st;
   }
   // 5. dW1 = A^T dH  and  6. dW2 = X_n^T dY: contraction over the M rows.
   // With M = 0 the main loop runs no k-tile and writes zeros; the M-row
@@ -475,6 +491,79 @@ coda_status check_rope(int64_t M, int64_t N, const int32_t* positions, const flo
   *mpos = Mat{positions, 1, M, M, 4, "positions"};
   *mcs = Mat{cos_sin, max_pos, d_head, d_head, 4, "cos_sin"};
   if (mcs->span() > kMaxSpan) return fail(CODA_ERR_SHAPE, "cos_sin spans more than 2 GiB");
+  return CODA_OK;
+}
+
+// Argument checks of the backward shared by coda_chain_bwd and
+// coda_chain_bwd_noalloc (all but the workspace).  Matrices with M rows are
+// checked only when M > 0 (they may be NULL then).
+coda_status check_bwd_args(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64_t N2, const void* dY,
+                           const void* A, const void* W1, const void* g, const void* W2, const void* H,
+                           const float* r, void* dA, void* dR, void* dW1, void* dW2, float* dg) {
+  coda_status st = check_dims(dt, M, {{"K", K}, {"D", D}, {"N2", N2}});
+  if (st != CODA_OK) return st;
+  const int es = elem_size(dt), E = elems_per_chunk(dt);
+  const Mat mdY{dY, M, N2, N2, es, "dY"}, mA{A, M, K, K, es, "A"}, mH{H, M, D, D, es, "H"};
+  const Mat mdA{dA, M, K, K, es, "dA"}, mdR{dR, M, D, D, es, "dR"};
+  const Mat mW1{W1, K, D, D, es, "W1"}, mg{g, 1, D, D, es, "g"}, mW2{W2, D, N2, N2, es, "W2"};
+  const Mat mdW1{dW1, K, D, D, es, "dW1"}, mdW2{dW2, D, N2, N2, es, "dW2"};
+  for (const Mat* m : {&mW1, &mg, &mW2, &mdW1, &mdW2})
+    if ((st = check_mat(*m, E)) != CODA_OK) return st;
+  if (M > 0) {
+    for (const Mat* m : {&mdY, &mA, &mH, &mdA, &mdR})
+      if ((st = check_mat(*m, E)) != CODA_OK) return st;
+    if (r == nullptr) return fail(CODA_ERR_NULL, "r is NULL");
+    if (((uintptr_t)r & 3) != 0) return fail(CODA_ERR_ALIGN, "r is not 4-byte aligned");
+  }
+  if (dg == nullptr) return fail(CODA_ERR_NULL, "dg is NULL");
+  if (((uintptr_t)dg & 3) != 0) return fail(CODA_ERR_ALIGN, "dg is not 4-byte aligned");
+  return CODA_OK;
+}
+
+// Outputs (and the workspace, when ws names one) against the inputs and
+// each other.
+coda_status check_bwd_alias(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64_t N2, const void* dY,
+                            const void* A, const void* W1, const void* g, const void* W2, const void* H,
+                            const float* r, void* dA, void* dR, void* dW1, void* dW2, float* dg, const Mat& ws) {
+  const int es = elem_size(dt);
+  const Mat mdY{dY, M, N2, N2, es, "dY"}, mA{A, M, K, K, es, "A"}, mH{H, M, D, D, es, "H"};
+  const Mat mdA{dA, M, K, K, es, "dA"}, mdR{dR, M, D, D, es, "dR"};
+  const Mat mW1{W1, K, D, D, es, "W1"}, mg{g, 1, D, D, es, "g"}, mW2{W2, D, N2, N2, es, "W2"};
+  const Mat mdW1{dW1, K, D, D, es, "dW1"}, mdW2{dW2, D, N2, N2, es, "dW2"};
+  const Mat mr{r, 1, M, M, 4, "r"}, mdg{dg, 1, D, D, 4, "dg"};
+  const Mat none{nullptr, 0, 0, 0, es, ""};
+  const Mat outs[6] = {M > 0 ? mdA : none, M > 0 ? mdR : none, mdW1, mdW2, mdg, ws};
+  const Mat ins[7] = {M > 0 ? mdY : none, M > 0 ? mA : none, mW1, mg, mW2, M > 0 ? mH : none, M > 0 ? mr : none};
+  return check_alias(outs, 6, ins, 7);
+}
+
+// ---- scratch of coda_chain_bwd_noalloc ----------------------------------
+// A file-scope device array: every GPU the library runs on holds its own
+// copy from the time the library's code is loaded on it until the process
+// ends.  Host code never passes the array's name to a kernel or a copy (on
+// the host it is only a stand-in for the symbol): the device address comes
+// from hipGetSymbolAddress, taken once per device with that device current,
+// on the first call of coda_chain_bwd_noalloc there.
+constexpr size_t kNoAllocScratchBytes = CODA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<char*> g_scratch_ptr;  // per device ordinal, nullptr until looked up
+
+coda_status noalloc_scratch(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(CODA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(CODA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = (char*)p;
+  }
+  *out = g_scratch_ptr[dev];
   return CODA_OK;
 }
 
@@ -1194,25 +1283,9 @@ coda_status coda_chain_bwd(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64
                            const void* A, const void* W1, const void* g, const void* W2, const void* H,
                            const float* r, void* dA, void* dR, void* dW1, void* dW2, float* dg, void* ws,
                            size_t ws_bytes, void* stream) {
-  coda_status st = check_dims(dt, M, {{"K", K}, {"D", D}, {"N2", N2}});
+  coda_status st = check_bwd_args(dt, M, K, D, N2, dY, A, W1, g, W2, H, r, dA, dR, dW1, dW2, dg);
   if (st != CODA_OK) return st;
-  const int es = elem_size(dt), E = elems_per_chunk(dt);
-  // matrices with M rows are checked only when M > 0 (they may be NULL then)
-  const Mat mdY{dY, M, N2, N2, es, "dY"}, mA{A, M, K, K, es, "A"}, mH{H, M, D, D, es, "H"};
-  const Mat mdA{dA, M, K, K, es, "dA"}, mdR{dR, M, D, D, es, "dR"};
-  const Mat mW1{W1, K, D, D, es, "W1"}, mg{g, 1, D, D, es, "g"}, mW2{W2, D, N2, N2, es, "W2"};
-  const Mat mdW1{dW1, K, D, D, es, "dW1"}, mdW2{dW2, D, N2, N2, es, "dW2"};
-  const Mat mr{r, 1, M, M, 4, "r"}, mdg{dg, 1, D, D, 4, "dg"};
-  for (const Mat* m : {&mW1, &mg, &mW2, &mdW1, &mdW2})
-    if ((st = check_mat(*m, E)) != CODA_OK) return st;
-  if (M > 0) {
-    for (const Mat* m : {&mdY, &mA, &mH, &mdA, &mdR})
-      if ((st = check_mat(*m, E)) != CODA_OK) return st;
-    if (r == nullptr) return fail(CODA_ERR_NULL, "r is NULL");
-    if (((uintptr_t)r & 3) != 0) return fail(CODA_ERR_ALIGN, "r is not 4-byte aligned");
-  }
-  if (dg == nullptr) return fail(CODA_ERR_NULL, "dg is NULL");
-  if (((uintptr_t)dg & 3) != 0) return fail(CODA_ERR_ALIGN, "dg is not 4-byte aligned");
+  const int es = elem_size(dt);
   const BwdWs L(M, K, D, N2, es);
   if (ws == nullptr || ws_bytes < L.total)
     return fail(CODA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, ws ? ws_bytes : (size_t)0);
@@ -1220,16 +1293,38 @@ coda_status coda_chain_bwd(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64
   const Mat mws{ws, 1, (int64_t)L.total, (int64_t)L.total, 1, "workspace"};
   const Mat mXn{(char*)ws + L.xn, M, D, D, es, "workspace X_n"};
   if (mXn.span() > kMaxSpan) return fail(CODA_ERR_SHAPE, "workspace X_n spans more than 2 GiB");
-  const Mat none{nullptr, 0, 0, 0, es, ""};
-  const Mat outs[6] = {M > 0 ? mdA : none, M > 0 ? mdR : none, mdW1, mdW2, mdg, mws};
-  const Mat ins[7] = {M > 0 ? mdY : none, M > 0 ? mA : none, mW1, mg, mW2, M > 0 ? mH : none, M > 0 ? mr : none};
-  if ((st = check_alias(outs, 6, ins, 7)) != CODA_OK) return st;
+  if ((st = check_bwd_alias(dt, M, K, D, N2, dY, A, W1, g, W2, H, r, dA, dR, dW1, dW2, dg, mws)) != CODA_OK)
+    return st;
   hipStream_t s = (hipStream_t)stream;
   if (dt == CODA_BF16)
     return chain_bwd_impl<uint16_t>((int)M, (int)K, (int)D, (int)N2, dY, A, W1, g, W2, H, r, dA, dR, dW1, dW2, dg,
                                     (char*)ws, s);
   return chain_bwd_impl<float>((int)M, (int)K, (int)D, (int)N2, dY, A, W1, g, W2, H, r, dA, dR, dW1, dW2, dg,
                                (char*)ws, s);
+}
+
+coda_status coda_chain_bwd_noalloc(coda_dtype dt, int64_t M, int64_t K, int64_t D, int64_t N2, const void* dY,
+                                   const void* A, const void* W1, const void* g, const void* W2, const void* H,
+                                   const float* r, void* dA, void* dR, void* dW1, void* dW2, float* dg,
+                                   void* stream) {
+  coda_status st = check_bwd_args(dt, M, K, D, N2, dY, A, W1, g, W2, H, r, dA, dR, dW1, dW2, dg);
+  if (st != CODA_OK) return st;
+  const size_t need = BwdWs(M, 0, D, 0, elem_size(dt)).total;
+  if (need > kNoAllocScratchBytes)
+    return fail(CODA_ERR_WORKSPACE, "this shape needs %zu bytes of scratch; the static scratch holds %zu "
+                "(M * D elements of X_n dominate): use coda_chain_bwd with a workspace",
+                need, kNoAllocScratchBytes);
+  const Mat none{nullptr, 0, 0, 0, 1, ""};
+  if ((st = check_bwd_alias(dt, M, K, D, N2, dY, A, W1, g, W2, H, r, dA, dR, dW1, dW2, dg, none)) != CODA_OK)
+    return st;
+  char* ws = nullptr;
+  if ((st = noalloc_scratch(&ws)) != CODA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == CODA_BF16)
+    return chain_bwd_impl<uint16_t, true>((int)M, (int)K, (int)D, (int)N2, dY, A, W1, g, W2, H, r, dA, dR, dW1,
+                                          dW2, dg, ws, s);
+  return chain_bwd_impl<float, true>((int)M, (int)K, (int)D, (int)N2, dY, A, W1, g, W2, H, r, dA, dR, dW1, dW2, dg,
+                                     ws, s);
 }
 
 size_t coda_chain_bwd_fp8_workspace_bytes(int64_t M, int64_t K, int64_t D, int64_t N2) {
