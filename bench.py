@@ -110,8 +110,11 @@ def measured_traffic(workload: str):
     return rec["bytes_per_launch"] if ok else None
 
 
-def cpu_baseline(wl, x, budget_s: float):
-    """The fp64 oracle, as it stands, on a bounded sample of rows of the same workload."""
+def cpu_baseline(wl, x, budget_s: float, gpu_outputs=None):
+    """The fp64 oracle, as it stands, on a bounded sample of rows of the same workload.
+
+    gpu_outputs (name -> device tensor [M, N2]): each is compared with the
+    oracle's Y over the rows the oracle computed (max|Y - Y_ref| / max|Y_ref|)."""
     import threadpoolctl
 
     import oracle
@@ -128,13 +131,27 @@ def cpu_baseline(wl, x, budget_s: float):
     n = int(min(wl.M, max(probe, probe * budget_s / max(t_probe, 1e-3))))
     rows = np.arange(n)
     t0 = time.perf_counter()
-    oracle.forward(x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps, rows=rows)
+    ref = oracle.forward(x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps, rows=rows)
     dt = time.perf_counter() - t0
     out = {"value": round(n * row_flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores),
            "kind": "oracle", "seconds": round(dt, 3), "blas": blas,
            "affinity_cores": len(os.sched_getaffinity(0)),
            "sample": f"rows 0..{n - 1} of the {wl.M}-row {wl.name} forward chain (rows are independent), "
                      f"fp64 numpy, {dt:.2f} s, including the oracle's own fp64 weight conversion"}
+    if gpu_outputs:
+        den = float(np.max(np.abs(ref["Y"])))
+        errs = {}
+        for name, t in gpu_outputs.items():
+            num = 0.0
+            for s0 in range(0, n, 2048):
+                blk = t[s0:min(n, s0 + 2048)].float().cpu().numpy().astype(np.float64)
+                num = max(num, float(np.max(np.abs(blk - ref["Y"][s0:s0 + blk.shape[0]]))))
+            errs[name] = num / den
+        out["y_errors"] = {"rows": f"0..{n - 1} of {wl.M}", "metric": "max|Y - Y_oracle| / max|Y_oracle|",
+                           **{k: float(f"{v:.4e}") for k, v in errs.items()}}
+        if "fused" in errs and "ref_chain" in errs:
+            out["y_errors"]["fused_over_ref_chain"] = round(errs["fused"] / errs["ref_chain"], 4)
+    del ref
     # the backward on a row sample (the weight gradients are sums over rows,
     # so a row sample is a proportional share of the work): same dY recipe
     nb = int(min(wl.M, 2048))
@@ -892,7 +909,20 @@ def bench_backward(args, up, stream):
         t_ms = time_ms(torch_train, stream, n, w)
         out["torch_autograd_train_step_ms"] = round(t_ms, 4)
         out["train_step_speedup_vs_torch_autograd"] = round(t_ms / train_ms, 4)
-        del leaves
+        # the backward alone: autograd of one retained forward graph
+        Ht = torch.addmm(leaves["R"], leaves["A"], leaves["W1"])
+        Xn = torch.nn.functional.rms_norm(Ht.float(), (D,), leaves["g"].float(), wl.eps).to(tdt)
+        Yt = torch.matmul(Xn, leaves["W2"])
+
+        def torch_bwd():
+            for t in leaves.values():
+                t.grad = None
+            Yt.backward(d["dY"], retain_graph=True)
+
+        tb_ms = time_ms(torch_bwd, stream, n, w)
+        out["torch_autograd_backward_ms"] = round(tb_ms, 4)
+        out["backward_speedup_vs_torch_autograd"] = round(tb_ms / bwd_ms, 4)
+        del leaves, Ht, Xn, Yt
     return out
 
 
@@ -1058,6 +1088,13 @@ def main():
         out["hg_layout"] = {"tile_packed_ms": round(pk_ms, 4), "row_major_ms": round(rm_ms, 4),
                             "packed_speedup": round(rm_ms / pk_ms, 4)}
 
+    # the timed path's own output: one more step of it (the layout A/B above
+    # ended with the row-major pair), kept for the comparisons below
+    step()
+    torch.cuda.synchronize()
+    Y_timed = Y.clone()
+    H_timed = H.clone()
+    compare = {"fused": Y_timed}
     if not args.no_ref_chain:
         ws = torch.empty((coda.coda_ref_chain_workspace_bytes(tdt, M, D),), device=dev, dtype=torch.uint8)
         Hr = torch.empty_like(H)
@@ -1078,9 +1115,12 @@ def main():
         out["ref_chain_ms"] = round(ref_ms, 4)
         out["speedup_vs_ref_chain"] = round(ref_ms / ms_step, 4)
         out["h_bit_identical_to_ref_chain"] = bool(torch.equal(Hr.view(torch.int16) if tdt == torch.bfloat16
-                                                               else Hr, H.view(torch.int16)
-                                                               if tdt == torch.bfloat16 else H))
-        del ws, Hr, rr, Yr
+                                                               else Hr, H_timed.view(torch.int16)
+                                                               if tdt == torch.bfloat16 else H_timed))
+        yd = float((Y_timed.float() - Yr.float()).abs().max() / Yr.float().abs().max())
+        out["y_rel_diff_vs_ref_chain"] = float(f"{yd:.4e}")
+        compare["ref_chain"] = Yr
+        del ws, Hr, rr
 
     if args.flush_mib > 0:
         # sensitivity check: every step starts with cold caches (a write of
@@ -1128,6 +1168,7 @@ def main():
         t_ms = a.elapsed_time(b) / nt
         out["torch_chain_ms"] = round(t_ms, 4)
         out["speedup_vs_torch_chain"] = round(t_ms / ms_step, 4)
+        compare["torch_chain"] = torch_chain()
 
     if not args.no_other_workloads and wl.name == "7b-bf16":
         out["other_workloads"] = {
@@ -1150,7 +1191,9 @@ def main():
         out["rope"] = bench_rope(args, up, stream)
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds, compare)
+        if "y_errors" in out["cpu_baseline"]:
+            out["y_errors"] = out["cpu_baseline"].pop("y_errors")
 
     print(json.dumps(out), flush=True)
 

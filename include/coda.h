@@ -33,9 +33,17 @@
  *     ld >= row width and a multiple of 8 (bf16) or 4 (f32) elements; base
  *     pointers 16-byte aligned; each matrix spans less than 2 GiB.
  *   - Outputs must not overlap inputs (CODA_ERR_ALIAS), except where stated.
- *   - Deterministic: the same inputs give the same bits on every call (fixed
- *     reduction orders, no atomics).  Thread-safe: no mutable global state
- *     except the per-thread last-error string.
+ *   - Deterministic: the same inputs give the same bits on every call.  Every
+ *     sum runs in a fixed order; the only atomics are the fp8 quantisers'
+ *     row and column maxima (an atomic max on the float bits, whose result
+ *     does not depend on the order).  Thread-safe: the mutable global state
+ *     is the per-thread last-error string and, for coda_chain_bwd_noalloc,
+ *     a per-device table of its scratch address (filled once, under a
+ *     lock) and the scratch array itself (see that call).
+ *   - K, D, N2 multiples of 8 (16 for fp8) is a deliberate narrowing: the
+ *     kernels move 16-byte pieces of 8 bf16 (4 f32, 16 e4m3) along every
+ *     dimension except M, which may be any size.  LLaMA-shaped layers
+ *     satisfy it; other sizes return CODA_ERR_SHAPE.
  *   - Rounding: every float32 -> bfloat16 conversion is round-to-nearest-even.
  */
 #ifndef CODA_H
