@@ -12,10 +12,14 @@ Sources (the CODA news article by Synced / 机器之心, mirrored by KuCoin News
     3 mantissa bits; largest finite 448; no infinities; S.1111.111 is NaN)
     with float32 scales: A per row (sa), the weights per output channel
     (sw1, sw2), the weights stored transposed, [N, K];
-  * the first GEMM's epilogue keeps H in bf16 and quantises H g for the
-    second GEMM without a scale: Hg8 = e4m3(clamp(float(H_bf16) * g, +-448)),
-    the product taken in float32 and rounded to nearest-even, which is the
-    precision the kernel takes that decision in;
+  * the first GEMM's epilogue keeps H in bf16 and quantises x = H g for
+    the second GEMM with one power-of-two scale per row and block of 32
+    columns (the block scaling of the OCP microscaling formats, which
+    gfx950's scaled fp8 matrix products apply per 32 contraction elements):
+    x is the float32 product float(H_bf16) * g, the block's exponent E is
+    the smallest integer with max |x| over the block <= 448 * 2^E (clamped
+    to [-127, 127]; 0 for an all-zero block), so no value saturates, and
+    the codes are the nearest-even e4m3 of x * 2^-E;
   * r comes from the exact H, as in the bf16 chain;
   * quantising a bf16 operand (quantize_rows): per row, scale = amax / 448
     in float32 (1 for an all-zero row), codes = e4m3(float32(x) / scale),
@@ -32,8 +36,9 @@ Sources (the CODA news article by Synced / 机器之心, mirrored by KuCoin News
 
     A   = e4m3(A8) * sa[:, None]            W1 = (e4m3(W1t8) * sw1[:, None])^T
     H   = A W1 + R                          Hb = bf16(H)
-    Hg8 = e4m3_code(f32(Hb) * f32(g))       r  = 1 / sqrt(mean_j H_ij^2 + eps)
-    Y   = diag(r) e4m3(Hg8) (e4m3(W2t8) * sw2[:, None])^T
+    x   = f32(Hb) * f32(g)                  E_ib = block exponent of x over block b
+    Hg8 = e4m3_code(x * 2^-E)               r  = 1 / sqrt(mean_j H_ij^2 + eps)
+    Y   = diag(r) (e4m3(Hg8) * 2^E) (e4m3(W2t8) * sw2[:, None])^T
 """
 from __future__ import annotations
 
@@ -107,9 +112,33 @@ def bf16_round(x) -> np.ndarray:
     return (np.round(m * 256.0) / 256.0) * np.exp2(e)
 
 
+MX_BLOCK = 32
+
+
+def mx_exponents(x, block: int = MX_BLOCK) -> np.ndarray:
+    """Per row and block of `block` columns of x (the last block may be
+    short): the smallest integer E with max |x| over the block <= 448 * 2^E,
+    clamped to [-127, 127], and 0 for an all-zero block.  int32 [rows,
+    ceil(cols / block)]."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    rows, cols = a.shape
+    nb = -(-cols // block)
+    amax = np.zeros((rows, nb))
+    for b in range(nb):
+        amax[:, b] = np.max(a[:, b * block:(b + 1) * block], axis=1)
+    pos = amax > 0
+    E = np.zeros(amax.shape, dtype=np.int64)
+    E[pos] = np.ceil(np.log2(amax[pos] / 448.0)).astype(np.int64)
+    # settle the rounding of log2 exactly: 448 * 2^(E-1) < amax <= 448 * 2^E
+    E = np.where(pos & (amax > np.ldexp(448.0, E)), E + 1, E)
+    E = np.where(pos & (amax <= np.ldexp(448.0, E - 1)), E - 1, E)
+    return np.clip(E, -127, 127).astype(np.int32)
+
+
 def forward_fp8(A8, sa, W1t8, sw1, R, g, W2t8, sw2, eps: float,
                 rows: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
-    """Returns float64 H (exact), Hb (bf16-rounded H), r, Y and the uint8 Hg8 codes."""
+    """Returns float64 H (exact), Hb (bf16-rounded H), r, Y, the uint8 Hg8
+    codes and their int32 block exponents Hg8_exp [rows, ceil(D/32)]."""
     sa = np.asarray(sa, dtype=np.float64)
     W1 = (e4m3_decode(W1t8) * np.asarray(sw1, dtype=np.float64)[:, None]).T
     W2 = (e4m3_decode(W2t8) * np.asarray(sw2, dtype=np.float64)[:, None]).T
@@ -118,11 +147,13 @@ def forward_fp8(A8, sa, W1t8, sw1, R, g, W2t8, sw2, eps: float,
     H = A @ W1 + np.asarray(R, dtype=np.float64)[idx]
     Hb = bf16_round(H)
     prod = (Hb.astype(np.float32) * np.asarray(g, dtype=np.float32)[None, :]).astype(np.float32)
-    Hg8 = e4m3_encode(prod)
+    E = mx_exponents(prod)
+    Ecol = np.repeat(E, MX_BLOCK, axis=1)[:, :prod.shape[1]]
+    Hg8 = e4m3_encode(np.ldexp(prod.astype(np.float64), -Ecol))
     ms = np.mean(H * H, axis=1)
     r = 1.0 / np.sqrt(ms + eps)
-    Y = r[:, None] * (e4m3_decode(Hg8) @ W2)
-    return {"H": H, "Hb": Hb, "Hg8": Hg8, "r": r, "Y": Y}
+    Y = r[:, None] * (np.ldexp(e4m3_decode(Hg8), Ecol) @ W2)
+    return {"H": H, "Hb": Hb, "Hg8": Hg8, "Hg8_exp": E, "r": r, "Y": Y}
 
 
 def _deq_rows(x, on: bool) -> np.ndarray:

@@ -74,7 +74,8 @@ def _args(x):
 
 def _brute(A8, sa, W1t8, sw1, R, g, W2t8, sw2, eps):
     """Pure-Python fp8 chain: the code table from the format definition,
-    math.fsum sums, float32 product and nearest-even e4m3 by direct search."""
+    math.fsum sums, float32 product, the block exponent by direct search and
+    nearest-even e4m3 by direct search."""
     def val(c):
         s = -1.0 if c & 0x80 else 1.0
         e, m = (c >> 3) & 15, c & 7
@@ -86,25 +87,34 @@ def _brute(A8, sa, W1t8, sw1, R, g, W2t8, sw2, eps):
         best = min(range(0x7F), key=lambda c: (abs(pos[c] - a), c % 2))
         return best | (0x80 if math.copysign(1.0, x) < 0 else 0)
 
+    def block_exp(vals):   # smallest E in [-127, 127] with max |v| <= 448 * 2^E; 0 for a zero block
+        amax = max(abs(v) for v in vals)
+        if amax == 0:
+            return 0
+        return next((E for E in range(-127, 128) if amax <= math.ldexp(448.0, E)), 127)
+
     M, K = len(A8), len(A8[0])
     D, N2 = len(W1t8), len(W2t8)
     H = [[math.fsum([val(A8[i][k]) * float(sa[i]) * val(W1t8[j][k]) * float(sw1[j]) for k in range(K)]
                     + [float(R[i][j])]) for j in range(D)] for i in range(M)]
     Hb = [[float(torch.tensor(h, dtype=torch.float64).to(torch.bfloat16)) for h in row] for row in H]
-    Hg8 = [[enc(float(np.float32(np.float32(Hb[i][j]) * np.float32(g[j])))) for j in range(D)] for i in range(M)]
+    x = [[float(np.float32(np.float32(Hb[i][j]) * np.float32(g[j]))) for j in range(D)] for i in range(M)]
+    E = [[block_exp(x[i][b:b + 32]) for b in range(0, D, 32)] for i in range(M)]
+    Hg8 = [[enc(math.ldexp(x[i][j], -E[i][j // 32])) for j in range(D)] for i in range(M)]
     r = [1.0 / math.sqrt(math.fsum(h * h for h in H[i]) / D + eps) for i in range(M)]
-    Y = [[r[i] * math.fsum(val(Hg8[i][j]) * val(W2t8[n][j]) * float(sw2[n]) for j in range(D))
-          for n in range(N2)] for i in range(M)]
-    return np.array(H), np.array(Hg8, dtype=np.uint8), np.array(r), np.array(Y)
+    Y = [[r[i] * math.fsum(math.ldexp(val(Hg8[i][j]), E[i][j // 32]) * val(W2t8[n][j]) * float(sw2[n])
+                           for j in range(D)) for n in range(N2)] for i in range(M)]
+    return np.array(H), np.array(Hg8, dtype=np.uint8), np.array(E), np.array(r), np.array(Y)
 
 
-@pytest.mark.parametrize("shape", [(1, 16, 8, 8), (3, 32, 16, 8), (5, 16, 24, 16)])
+@pytest.mark.parametrize("shape", [(1, 16, 8, 8), (3, 32, 16, 8), (5, 16, 24, 16), (3, 16, 80, 8)])
 def test_brute_force(shape):
     wl, x = _case(40 + sum(shape), *shape)
     out = oracle.forward_fp8(*_args(x), wl.eps)
-    H, Hg8, r, Y = _brute(*(np.asarray(a).tolist() if np.asarray(a).ndim == 2 else np.asarray(a) for a in _args(x)),
-                          wl.eps)
+    H, Hg8, E, r, Y = _brute(*(np.asarray(a).tolist() if np.asarray(a).ndim == 2 else np.asarray(a)
+                               for a in _args(x)), wl.eps)
     np.testing.assert_allclose(out["H"], H, rtol=1e-13, atol=1e-14)
+    np.testing.assert_array_equal(out["Hg8_exp"], E)
     np.testing.assert_array_equal(out["Hg8"], Hg8)
     np.testing.assert_allclose(out["r"], r, rtol=1e-13)
     np.testing.assert_allclose(out["Y"], Y, rtol=1e-12, atol=1e-13)
@@ -133,8 +143,11 @@ def test_lossless_case_reduces_to_the_plain_chain():
 def _hand_case():
     # K = 1: A = 1.0 (code 0x38, sa 1), W1 = 2^-9 (code 0x01) with sw1 0.5,
     # R = 1.0625, g = 1: H = 1.0625 + 2^-10.  The stored bf16 H is 1.0625
-    # (spacing 2^-7 near 1), halfway between e4m3 1.0 and 1.125, so the
-    # even code 0x38 (1.0); the unrounded H would give 0x39 (1.125).
+    # (spacing 2^-7 near 1).  Its one-column block has max 1.0625, so the
+    # block exponent is -8 (448 * 2^-9 = 0.875 < 1.0625 <= 1.75); scaled,
+    # 1.0625 * 2^8 = 272 lies halfway between e4m3 256 and 288, so the even
+    # code 0x78 (256, i.e. 1.0 after the scale); the unrounded H would give
+    # 272.25, code 0x79 (288, i.e. 1.125).
     return (np.array([[0x38]], np.uint8), np.array([1.0], np.float32), np.array([[0x01]], np.uint8),
             np.array([0.5], np.float32), np.array([[1.0625]]), np.array([1.0]),
             np.array([[0x38]], np.uint8), np.array([1.0], np.float32))
@@ -144,7 +157,8 @@ def test_quantises_the_stored_bf16_h():
     out = oracle.forward_fp8(*_hand_case(), 0.0)
     assert out["H"][0, 0] == 1.0625 + 2.0 ** -10
     assert out["Hb"][0, 0] == 1.0625
-    assert out["Hg8"][0, 0] == 0x38
+    assert out["Hg8_exp"][0, 0] == -8
+    assert out["Hg8"][0, 0] == 0x78
     assert out["Y"][0, 0] == pytest.approx(1.0 / (1.0625 + 2.0 ** -10), rel=1e-15)   # r * 1.0 * 1.0
 
 
@@ -159,26 +173,80 @@ def _mutant_codes(kind, a, eps):
     H = A @ W1 + R
     prod = H if kind == "no_bf16_before_quantising" else oracle.bf16_round(H)
     prod = (np.asarray(prod, dtype=np.float32) * np.asarray(g, np.float32)).astype(np.float32)
-    codes = oracle.e4m3_encode(prod)
+    E = oracle.mx_exponents(prod, block=64 if kind == "blocks_of_64" else 32)
+    if kind == "exponent_rounded_down":     # saturating: max |x| * 2^-E may exceed 448
+        E = np.where(E != 0, E - 1, E)
+    Ecol = np.repeat(E, 64 if kind == "blocks_of_64" else 32, axis=1)[:, :prod.shape[1]]
+    scaled = np.ldexp(prod.astype(np.float64), -Ecol)
+    codes = oracle.e4m3_encode(scaled)
     if kind == "round_down":
         v = oracle.e4m3_decode(codes)
-        codes = np.where(np.abs(v) > np.abs(prod), np.where(codes & 0x7F, codes - 1, codes), codes).astype(np.uint8)
+        codes = np.where(np.abs(v) > np.abs(scaled), np.where(codes & 0x7F, codes - 1, codes), codes).astype(np.uint8)
     r = 1.0 / np.sqrt(np.mean(H * H, axis=1) + eps)
-    return codes, r[:, None] * (oracle.e4m3_decode(codes) @ (oracle.e4m3_decode(W2t8) * sw2[:, None]).T)
+    return codes, r[:, None] * (np.ldexp(oracle.e4m3_decode(codes), Ecol) @ (oracle.e4m3_decode(W2t8) * sw2[:, None]).T)
 
 
 @pytest.mark.parametrize("kind", ["no_bf16_before_quantising", "scale_columns_of_A", "weights_not_transposed",
-                                  "round_down"])
+                                  "round_down", "blocks_of_64", "exponent_rounded_down"])
 def test_pins_reject_planted_mistakes(kind):
     if kind == "no_bf16_before_quantising":
         codes, _ = _mutant_codes(kind, _hand_case(), 0.0)
-        assert codes[0, 0] != oracle.forward_fp8(*_hand_case(), 0.0)["Hg8"][0, 0] == 0x38
+        assert codes[0, 0] != oracle.forward_fp8(*_hand_case(), 0.0)["Hg8"][0, 0] == 0x78
         return
-    wl, x = _case(77, 3, 16, 16, 8)
+    if kind == "blocks_of_64":
+        # one row, A = 0 so H = R: columns 0..31 around 0.01, columns 32..63
+        # around 10.  Their 32-column blocks get exponents -15 and -5; a
+        # shared 64-column block would quantise the small half with -5 and
+        # lose most of its bits.
+        R = np.concatenate([np.linspace(0.004, 0.011, 32), np.linspace(3.0, 10.0, 32)])[None, :]
+        a = (np.zeros((1, 16), np.uint8), np.ones(1, np.float32), np.zeros((64, 16), np.uint8), np.ones(64, np.float32),
+             R, np.ones(64), np.full((8, 64), 0x38, np.uint8), np.ones(8, np.float32))
+        out = oracle.forward_fp8(*a, 1e-5)
+        assert list(out["Hg8_exp"][0]) == [-15, -5]
+        codes, _ = _mutant_codes(kind, a, 1e-5)
+        assert not np.array_equal(codes, out["Hg8"])
+        return
+    wl, x = _case(77, 3, 16, 80, 8)
     a = _args(x)
-    _, Hg8, _, Y = _brute(*(np.asarray(v).tolist() if np.asarray(v).ndim == 2 else np.asarray(v) for v in a), wl.eps)
+    _, Hg8, _, _, Y = _brute(*(np.asarray(v).tolist() if np.asarray(v).ndim == 2 else np.asarray(v) for v in a),
+                             wl.eps)
     codes, Ym = _mutant_codes(kind, a, wl.eps)
     assert (not np.array_equal(codes, Hg8)) or np.max(np.abs(Ym - Y)) > 1e-9
+
+
+def test_mx_exponents_closed_forms():
+    x = np.array([[448.0, 0, 0, 0], [449.0, 1, 0, 0], [1.0, 0.5, 0, 0], [1.75, -1.0, 0, 0], [0, 0, 0, 0],
+                  [-2.0 ** -140, 0, 0, 0], [3e38, 0, 0, 0], [-0.875, 0, 0, 0]], dtype=np.float32)
+    E = oracle.mx_exponents(x, block=4)[:, 0]
+    # 448 <= 448 * 2^0; 449 needs 2^1; 1.0 and 1.75 fit 448 * 2^-8 = 1.75; 0.875 = 448 * 2^-9
+    np.testing.assert_array_equal(E, [0, 1, -8, -8, 0, -127, 120, -9])
+    # the definition on random magnitudes: 448 * 2^(E-1) < amax <= 448 * 2^E
+    rng = np.random.default_rng(3)
+    a = np.exp(rng.uniform(-60, 60, size=(500, 32))).astype(np.float32) * rng.choice([-1, 1], size=(500, 32))
+    E = oracle.mx_exponents(a)[:, 0].astype(np.float64)
+    amax = np.max(np.abs(a.astype(np.float64)), axis=1)
+    assert np.all(amax <= np.ldexp(448.0, E.astype(int))) and np.all(amax > np.ldexp(448.0, E.astype(int) - 1))
+
+
+def test_large_residual_does_not_saturate():
+    # a residual stream 1000x larger than the recipe's N(0, 1): H g reaches
+    # ~4e3, far past e4m3's 448.  With the block exponents the fp8 chain's Y
+    # stays within the e4m3 rounding of the exact chain on the dequantised
+    # operands; the unscaled recipe (codes of clamp(H g, 448)) would be off
+    # by most of Y.
+    wl, x = _case(91, 64, 64, 128, 64)
+    R = x["R"].f32 * 1000.0
+    A8, sa, W1t8, sw1, _, g, W2t8, sw2 = _args(x)
+    out = oracle.forward_fp8(A8, sa, W1t8, sw1, R, g, W2t8, sw2, wl.eps)
+    W1 = (oracle.e4m3_decode(W1t8) * sw1[:, None]).T
+    W2 = (oracle.e4m3_decode(W2t8) * sw2[:, None]).T
+    exact = oracle.forward(oracle.e4m3_decode(A8) * sa[:, None], W1, R, g, W2, wl.eps)
+    assert np.max(np.abs(out["Hb"] * g[None, :])) > 2000
+    rel = np.max(np.abs(out["Y"] - exact["Y"])) / np.max(np.abs(exact["Y"]))
+    assert rel < 0.05, rel
+    prod = (out["Hb"].astype(np.float32) * g.astype(np.float32)[None, :]).astype(np.float32)
+    Yclamp = out["r"][:, None] * (oracle.e4m3_decode(oracle.e4m3_encode(prod)) @ W2)
+    assert np.max(np.abs(Yclamp - exact["Y"])) / np.max(np.abs(exact["Y"])) > 0.5
 
 
 def test_quantize_rows_pins():
