@@ -650,6 +650,7 @@ def bench_fp8(args, stream):
     # the chain's Hg8 and W2 codes tile-packed (the second GEMM's operands)
     W2t8p, sw2p = coda.quantize_weight_e4m3_packed(W2, stream)
     Hg8p = coda.packed_empty_e4m3(M, D, dev)
+    E = coda.mx_exp_empty(M, D, dev)    # Hg8's MX block exponents
     P = torch.empty((coda.coda_prms_num_partials(torch.bfloat16, D), M), device=dev, dtype=torch.float32)
     r = torch.empty((M,), device=dev, dtype=torch.float32)
     Y = torch.empty((M, N2), device=dev, dtype=torch.bfloat16)
@@ -658,14 +659,14 @@ def bench_fp8(args, stream):
         coda.quantize_rows_e4m3(A, stream, A8, sa)
 
     def chain():
-        coda.coda_gemm_res_prms_fp8_packed(A8, sa, W1t8, sw1, R, g, H, Hg8p, P, stream)
+        coda.coda_gemm_res_prms_fp8_packed(A8, sa, W1t8, sw1, R, g, H, Hg8p, E, P, stream)
         coda.coda_rms_combine(P, r, D, wl.eps, stream)
-        coda.coda_gemm_rowscale_fp8_packed(Hg8p, W2t8p, sw2p, r, Y, stream)
+        coda.coda_gemm_rowscale_fp8_packed(Hg8p, E, W2t8p, sw2p, r, Y, stream)
 
     def chain_row_major():
-        coda.coda_gemm_res_prms_fp8(A8, sa, W1t8, sw1, R, g, H, Hg8, P, stream)
+        coda.coda_gemm_res_prms_fp8(A8, sa, W1t8, sw1, R, g, H, Hg8, E, P, stream)
         coda.coda_rms_combine(P, r, D, wl.eps, stream)
-        coda.coda_gemm_rowscale_fp8(Hg8, W2t8, sw2, r, Y, stream)
+        coda.coda_gemm_rowscale_fp8(Hg8, E, W2t8, sw2, r, Y, stream)
 
     def step():
         quantize_a()
@@ -673,14 +674,16 @@ def bench_fp8(args, stream):
 
     n = max(5, args.steps // 2)
     w = max(2, args.warmup // 2)
-    ms, chain_ms, q_ms, g2_ms, rm_ms, g2rm_ms = time_ms_alternating(
-        [step, chain, quantize_a, lambda: coda.coda_gemm_rowscale_fp8_packed(Hg8p, W2t8p, sw2p, r, Y, stream),
-         chain_row_major, lambda: coda.coda_gemm_rowscale_fp8(Hg8, W2t8, sw2, r, Y, stream)], stream, n, w)
+    ms, chain_ms, q_ms, g2_ms, rm_ms, g2rm_ms, g2u_ms = time_ms_alternating(
+        [step, chain, quantize_a, lambda: coda.coda_gemm_rowscale_fp8_packed(Hg8p, E, W2t8p, sw2p, r, Y, stream),
+         chain_row_major, lambda: coda.coda_gemm_rowscale_fp8(Hg8, E, W2t8, sw2, r, Y, stream),
+         lambda: coda.coda_gemm_rowscale_fp8_packed(Hg8p, None, W2t8p, sw2p, r, Y, stream)], stream, n, w)
     tf = wl.fwd_flops / (ms * 1e-3) / 1e12
     g2_tf = 2.0 * M * D * N2 / (g2_ms * 1e-3) / 1e12
     out = {"workload": f"7b-fp8: M={M} K={K} D={D} N2={N2}, e4m3 operands with per-row / per-channel scales, "
-                       "bf16 A quantised on the device in every step; the second GEMM's operands (Hg8, W2 codes) "
-                       "tile-packed",
+                       "bf16 A quantised on the device in every step; H g quantised with MX block exponents "
+                       "(one per row and 32 columns) that the second GEMM's scaled products apply; the second "
+                       "GEMM's operands (Hg8, W2 codes) tile-packed",
            "ms_per_step": round(ms, 4), "tflops": round(tf, 2),
            "pct_of_fp8_peak": round(100.0 * tf / PEAK_FP8_TFLOPS, 2), "fp8_peak_tflops": round(PEAK_FP8_TFLOPS, 1),
            "quantize_a_ms": round(q_ms, 4),
@@ -690,6 +693,8 @@ def bench_fp8(args, stream):
            "coda_gemm_rowscale_fp8_packed_ms": round(g2_ms, 4),
            "coda_gemm_rowscale_fp8_packed_tflops": round(g2_tf, 2),
            "coda_gemm_rowscale_fp8_packed_frac": round(g2_tf / PEAK_FP8_TFLOPS, 4),
+           "second_gemm_without_block_exponents_ms": round(g2u_ms, 4),
+           "block_exponent_cost_pct": round(100.0 * (g2_ms / g2u_ms - 1.0), 2),
            "row_major": {"chain_on_quantised_a_ms": round(rm_ms, 4), "coda_gemm_rowscale_fp8_ms": round(g2rm_ms, 4),
                          "packed_chain_speedup": round(rm_ms / chain_ms, 4)}}
     if not args.no_ceiling:

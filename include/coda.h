@@ -323,23 +323,44 @@ coda_status coda_gemm_rowscale_ce_bwd_packed(int64_t M, int64_t D, int64_t V,
  * bias 7, 3 mantissa bits; largest finite 448; no infinities) with float32
  * dequantisation scales, A per row and the weights per output channel, the
  * weights stored transposed ([N, K], contraction contiguous).  H stays bf16;
- * the second GEMM's operand is H g quantised without a scale.  Products run
- * on v_mfma_f32_32x32x64_f8f6f4 with fp32 accumulation.  Sizes: K, D, N2
- * multiples of 16; e4m3 leading dimensions multiples of 16 elements, bf16
- * ones multiples of 8. */
+ * the second GEMM's operand x = H g is quantised with one power-of-two scale
+ * per row and block of 32 columns, the block scaling of the OCP microscaling
+ * (MX) formats: its exponent E is the smallest integer with
+ * max |x| over the block <= 448 * 2^E (clamped to [-127, 127], 0 for an
+ * all-zero block), so no code saturates, and the codes are e4m3_rne(x 2^-E).
+ * Products run on v_mfma_scale_f32_32x32x64_f8f6f4 with fp32 accumulation;
+ * the MX exponents ride along as the instruction's A-side scales.  Sizes:
+ * K, D, N2 multiples of 16; e4m3 leading dimensions multiples of 16
+ * elements, bf16 ones multiples of 8.
+ *
+ * Block-exponent arrays (hg_exp, x_exp): coda_mx_exp_bytes(M, D) bytes,
+ * 16-byte aligned; byte ((t / 4 * M + i) * 2 + h) * 4 + t % 4 is E + 127 (an
+ * E8M0 code) for row i and columns [64 t + 32 h, 64 t + 32 h + 32) of D
+ * (groups of 4 k-tiles of 64 columns outermost, so that the second GEMM's
+ * reads of one group for 32 rows are 256 contiguous bytes).  The first GEMM
+ * writes every byte, 127 (E = 0) for the blocks past D; the second GEMM
+ * reads the bytes of t < ceil(D / 64) only. */
+
+/* Bytes of the block-exponent array of a [rows, cols] MX operand:
+ * 8 * rows * ceil(cols / 256).  -1 for bad arguments. */
+int64_t coda_mx_exp_bytes(int64_t rows, int64_t cols);
 
 /* First GEMM, fp8 operands:
  *   H_ij   = round_bf16((acc_ij * sa_i) * sw1_j + R_ij)     acc = sum_k A8_ik W1t8_jk
- *   Hg8_ij = e4m3_rne(clamp(float(H_ij) * g_j, -448, 448))  (float32 product)
+ *   x_ij   = float(H_ij) * g_j                               (float32 product)
+ *   hg_exp = the MX block exponents E of x (layout above)
+ *   Hg8_ij = e4m3_rne(x_ij * 2^-E)                           (never saturates)
  *   partials as coda_gemm_res_prms (coda_prms_num_partials(CODA_BF16, D) rows)
  *   A8: e4m3 [M,K] (lda); sa: float[M]; W1t8: e4m3 [D,K] (ldw1t); sw1: float[D],
- *   16-byte aligned; R, g, H: bf16; Hg8: e4m3 [M,D] (ldhg). */
+ *   16-byte aligned; R, g, H: bf16; Hg8: e4m3 [M,D] (ldhg); hg_exp as above.
+ *   The block maximum is taken inside the epilogue (the 32 columns of a
+ *   block sit in 4 lanes of one row). */
 coda_status coda_gemm_res_prms_fp8(int64_t M, int64_t K, int64_t D,
                                    const void* A8, int64_t lda, const float* sa,
                                    const void* W1t8, int64_t ldw1t, const float* sw1,
                                    const void* R, int64_t ldr, const void* g,
                                    void* H, int64_t ldh, void* Hg8, int64_t ldhg,
-                                   float* partials, void* stream);
+                                   void* hg_exp, float* partials, void* stream);
 
 /* Quantisation of a bf16 operand for the fp8 GEMMs (the recipe above): per
  * row of X [M,K], scale = amax / 448 (1 for an all-zero row) and
@@ -371,11 +392,13 @@ coda_status coda_quantize_rows_cols_e4m3(int64_t M, int64_t N, const void* X, in
                                          void* stream);
 
 /* Second GEMM, fp8 operands, deferred row scale:
- *   Y_ik = round_bf16((acc_ik * r_i) * sw2_k)    acc = sum_j X8_ij W2t8_kj
- *   X8: e4m3 [M,D] (ldx), e.g. Hg8; W2t8: e4m3 [N2,D] (ldw2t); sw2: float[N2],
- *   16-byte aligned; r: float[M] or NULL; Y: bf16 [M,N2] (ldy). */
+ *   Y_ik = round_bf16((acc_ik * r_i) * sw2_k)
+ *   acc  = sum_j e4m3(X8_ij) 2^E(i, j) e4m3(W2t8_kj)
+ *   X8: e4m3 [M,D] (ldx), e.g. Hg8; x_exp: its MX block exponents E (layout
+ *   above, e.g. hg_exp), or NULL for E = 0; W2t8: e4m3 [N2,D] (ldw2t); sw2:
+ *   float[N2], 16-byte aligned; r: float[M] or NULL; Y: bf16 [M,N2] (ldy). */
 coda_status coda_gemm_rowscale_fp8(int64_t M, int64_t D, int64_t N2,
-                                   const void* X8, int64_t ldx,
+                                   const void* X8, int64_t ldx, const void* x_exp,
                                    const void* W2t8, int64_t ldw2t, const float* sw2,
                                    const float* r, void* Y, int64_t ldy, void* stream);
 
@@ -419,15 +442,16 @@ coda_status coda_gemm_res_prms_fp8_packed(int64_t M, int64_t K, int64_t D,
                                           const void* A8, int64_t lda, const float* sa,
                                           const void* W1t8, int64_t ldw1t, const float* sw1,
                                           const void* R, int64_t ldr, const void* g,
-                                          void* H, int64_t ldh, void* Hg8p,
+                                          void* H, int64_t ldh, void* Hg8p, void* hg_exp,
                                           float* partials, void* stream);
 
 /* coda_gemm_rowscale_fp8 with both operands tile-packed: X8p [M,D] (as
  * coda_gemm_res_prms_fp8_packed writes Hg8) and W2t8p [N2,D] (as
- * coda_quantize_cols_e4m3_packed writes it).  sw2, r, Y as in
- * coda_gemm_rowscale_fp8. */
+ * coda_quantize_cols_e4m3_packed writes it).  x_exp (row-major, never
+ * packed), sw2, r, Y as in coda_gemm_rowscale_fp8. */
 coda_status coda_gemm_rowscale_fp8_packed(int64_t M, int64_t D, int64_t N2,
-                                          const void* X8p, const void* W2t8p, const float* sw2,
+                                          const void* X8p, const void* x_exp,
+                                          const void* W2t8p, const float* sw2,
                                           const float* r, void* Y, int64_t ldy, void* stream);
 
 /* Bytes of workspace coda_ref_chain needs: float C[M,D] + X_n[M,D]. */

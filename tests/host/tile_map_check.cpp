@@ -269,9 +269,11 @@ static void check_swiglu_col() {
 }
 
 // fp8 fragments: 32-row fragments read as two 16-byte chunks per lane; the
-// lane gets operand row base + 32 t + l % 32 and k-bytes [32 (l/32), +32);
+// lane gets operand row base + 32 t + l % 32 and chunks l/32 and 2 + l/32
+// (each 32-byte scale block of the k-tile spread over both lane halves);
 // every 16-lane pass of a read hits each bank once; reads stay in the tile;
-// the second chunk is the first XOR 16 bytes, fragment t is 2 KiB further.
+// the second chunk is the first XOR 32 bytes, fragment t is 2 KiB further;
+// over a fragment every (row, chunk) of the 32 rows is read exactly once.
 static void check_kc8() {
   for (int base = 0; base < kTileM; base += kWaveM)
     for (int t = 0; t < kFrag8M && base + 32 * t < kTileM; ++t)
@@ -279,9 +281,15 @@ static void check_kc8() {
         for (int lane = 0; lane < 64; ++lane) {
           const int off = kc8_offset(base, t, half, lane);
           CHECK(off >= 0 && off + 16 <= kOperandBytes, "kc8 read out of tile");
-          CHECK(off == (kc8_offset(base, 0, 0, lane) ^ (16 * half)) + 2048 * t, "kc8 address shortcut");
-          const int row = base + 32 * t + (lane & 31), chunk = 2 * (lane >> 5) + half;
+          CHECK(off == (kc8_offset(base, 0, 0, lane) ^ (32 * half)) + 2048 * t, "kc8 address shortcut");
+          const int row = base + 32 * t + (lane & 31), chunk = (lane >> 5) + 2 * half;
           CHECK(off == kc_offset(row, chunk), "kc8 element");
+        }
+        if (half == 1) {
+          std::vector<int> seen(32 * 4, 0);
+          for (int lane = 0; lane < 64; ++lane)
+            for (int h = 0; h < 2; ++h) seen[(lane & 31) * 4 + (lane >> 5) + 2 * h]++;
+          for (int v : seen) CHECK(v == 1, "kc8: a (row, chunk) of the fragment read twice or never");
         }
         for (int g = 0; g < 4; ++g) {
           int used[64] = {0};
@@ -328,6 +336,38 @@ static void check_epilogue_slab() {
   }
 }
 
+// MX exponent bytes: every (row, k-tile, half) of an array for M rows and
+// G groups lands on its own byte inside 8 M G bytes; a group's dword of one
+// (row, half) holds its 4 k-tiles in order; the dwords the 64 lanes of a
+// 32-row fragment read for one group are 256 contiguous bytes.
+static void check_mx_byte() {
+  for (int M : {1, 3, 32, 37, 300})
+    for (int G : {1, 2, 5}) {
+      std::vector<int> hit(8 * M * G, 0);
+      for (int i = 0; i < M; ++i)
+        for (int t = 0; t < 4 * G; ++t)
+          for (int h = 0; h < 2; ++h) {
+            const int64_t o = mx_byte(i, t, h, M);
+            CHECK(o >= 0 && o < 8 * M * G, "mx_byte outside the array");
+            if (o >= 0 && o < 8 * M * G) hit[o]++;
+            CHECK(o == mx_byte(i, t & ~3, h, M) + (t & 3), "mx_byte: k-tiles of a group not consecutive");
+            CHECK(mx_byte(i, t & ~3, h, M) % 4 == 0, "mx_byte: group dword misaligned");
+          }
+      for (int v : hit) CHECK(v == 1, "mx_byte: a byte used twice or never");
+      for (int base = 0; base + 32 <= M; base += 32)
+        for (int g = 0; g < G; ++g) {
+          std::vector<int> w(64, 0);
+          const int64_t lo = mx_byte(base, 4 * g, 0, M);
+          for (int lane = 0; lane < 64; ++lane) {
+            const int64_t o = mx_byte(base + (lane & 31), 4 * g, lane >> 5, M) - lo;
+            CHECK(o >= 0 && o < 256 && o % 4 == 0, "mx_byte: fragment group read not in 256 contiguous bytes");
+            if (o >= 0 && o < 256) w[o / 4]++;
+          }
+          for (int v : w) CHECK(v == 1, "mx_byte: fragment group read does not cover its 256 bytes");
+        }
+    }
+}
+
 int main() {
   check_map_tile();
   check_kc();
@@ -337,6 +377,7 @@ int main() {
   check_epilogue_slab();
   check_swiglu_col();
   check_kc8();
+  check_mx_byte();
   if (failures) {
     fprintf(stderr, "%d failures\n", failures);
     return 1;

@@ -19,8 +19,8 @@ from transformer_gemm_epilogue_gemm1_amd import _lib  # noqa: E402
 OK, NULL, SHAPE, ALIGN, DTYPE, ALIAS, WS, HIP = range(8)
 BF16, F32 = 0, 1
 P = 0x7F0000000000  # fake device addresses, far apart
-A_, W1_, R_, G_, H_, HG_, PART_, W2_, Y_, R2_, WS_, DY_, DA_, DR_, DW1_, DW2_, DG_ = (
-    P + i * (1 << 36) for i in range(17))
+A_, W1_, R_, G_, H_, HG_, PART_, W2_, Y_, R2_, WS_, DY_, DA_, DR_, DW1_, DW2_, DG_, EX_ = (
+    P + i * (1 << 36) for i in range(18))
 
 
 def declared_functions():
@@ -379,9 +379,9 @@ def test_rope_bwd_validation(lib, args, status):
 
 
 def prms8(lib, M=512, K=256, D=512, A=A_, lda=None, sa=R2_, W=W1_, ldw=None, sw=G_ + 4096, R=R_, ldr=None, g=G_,
-           H=H_, ldh=None, Hg=HG_, ldhg=None, part=PART_):
+           H=H_, ldh=None, Hg=HG_, ldhg=None, ex=EX_, part=PART_):
     return lib.coda_gemm_res_prms_fp8(M, K, D, A, lda or K, sa, W, ldw or K, sw, R, ldr or D, g, H, ldh or D, Hg,
-                                      ldhg or D, part, None)
+                                      ldhg or D, ex, part, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -396,7 +396,10 @@ def prms8(lib, M=512, K=256, D=512, A=A_, lda=None, sa=R2_, W=W1_, ldw=None, sw=
     (dict(g=None), NULL),
     (dict(H=None), NULL),
     (dict(Hg=None), NULL),
+    (dict(ex=None), NULL),         # the block exponents are an output of the first GEMM
     (dict(part=None), NULL),
+    (dict(ex=EX_ + 4), ALIGN),
+    (dict(ex=HG_ + 512 * 512 - 64), ALIAS),   # overlaps Hg8's last row
     (dict(lda=264), ALIGN),        # e4m3 ld must be a multiple of 16 elements
     (dict(ldhg=520), ALIGN),
     (dict(ldr=516), ALIGN),        # bf16 ld a multiple of 8
@@ -412,8 +415,8 @@ def test_gemm_res_prms_fp8_rejects(lib, kw, status):
     assert lib.coda_last_error().decode() != ""
 
 
-def rowscale8(lib, M=512, D=256, N2=512, X=HG_, ldx=None, W=W2_, ldw=None, sw=G_, r=R2_, Y=Y_, ldy=None):
-    return lib.coda_gemm_rowscale_fp8(M, D, N2, X, ldx or D, W, ldw or D, sw, r, Y, ldy or N2, None)
+def rowscale8(lib, M=512, D=256, N2=512, X=HG_, ldx=None, ex=EX_, W=W2_, ldw=None, sw=G_, r=R2_, Y=Y_, ldy=None):
+    return lib.coda_gemm_rowscale_fp8(M, D, N2, X, ldx or D, ex, W, ldw or D, sw, r, Y, ldy or N2, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -426,14 +429,26 @@ def rowscale8(lib, M=512, D=256, N2=512, X=HG_, ldx=None, W=W2_, ldw=None, sw=G_
     (dict(sw=G_ + 8), ALIGN),
     (dict(Y=HG_), ALIAS),
     (dict(Y=G_ - 64), ALIAS),
+    (dict(ex=EX_ + 2), ALIGN),
+    (dict(Y=EX_ - 64), ALIAS),     # Y's last bytes over the exponents
 ])
 def test_gemm_rowscale_fp8_rejects(lib, kw, status):
     assert rowscale8(lib, **kw) == status
 
 
+def test_mx_exp_bytes(lib):
+    # 8 bytes per row and group of 4 k-tiles (2 halves x 4 k-tiles)
+    assert lib.coda_mx_exp_bytes(300, 512) == 300 * 2 * 8
+    assert lib.coda_mx_exp_bytes(3, 272) == 3 * 2 * 8
+    assert lib.coda_mx_exp_bytes(1, 16) == 8
+    assert lib.coda_mx_exp_bytes(0, 4096) == 0
+    assert lib.coda_mx_exp_bytes(-1, 16) == -1
+    assert lib.coda_mx_exp_bytes(4, 0) == -1
+
+
 def test_fp8_empty_is_noop(lib):
-    assert prms8(lib, M=0, A=None, sa=None, R=None, H=None, Hg=None, part=None) == OK
-    assert rowscale8(lib, M=0, X=None, Y=None, r=None) == OK
+    assert prms8(lib, M=0, A=None, sa=None, R=None, H=None, Hg=None, ex=None, part=None) == OK
+    assert rowscale8(lib, M=0, X=None, ex=None, Y=None, r=None) == OK
 
 
 def test_chain_bwd_workspace_bytes(lib):
@@ -681,12 +696,19 @@ def test_fp8_packed_validation(lib):
     assert lib.coda_quantize_cols_e4m3_packed(256, 512, W2_, 512, W2_ + 64, R2_, None) == ALIAS
     # first GEMM: Hg8 overlapping H
     assert lib.coda_gemm_res_prms_fp8_packed(300, 256, 512, A_, 256, R2_, W1_, 256, DG_, R_, 512, G_, H_, 512,
-                                             H_ + 64, PART_, None) == ALIAS
-    # second GEMM: D not a multiple of 16, NULL operand, Y overlapping X
-    assert lib.coda_gemm_rowscale_fp8_packed(300, 264, 512, HG_, W2_, DG_, R2_, Y_, 512, None) == SHAPE
-    assert lib.coda_gemm_rowscale_fp8_packed(300, 256, 512, None, W2_, DG_, R2_, Y_, 512, None) == NULL
-    assert lib.coda_gemm_rowscale_fp8_packed(300, 256, 512, HG_, W2_, DG_, R2_, HG_ + 16, 512, None) == ALIAS
-    assert lib.coda_gemm_rowscale_fp8_packed(0, 256, 512, None, None, None, None, None, 512, None) == OK
+                                             H_ + 64, EX_, PART_, None) == ALIAS
+    # first GEMM: exponents missing, or overlapping the packed Hg8
+    assert lib.coda_gemm_res_prms_fp8_packed(300, 256, 512, A_, 256, R2_, W1_, 256, DG_, R_, 512, G_, H_, 512,
+                                             HG_, None, PART_, None) == NULL
+    assert lib.coda_gemm_res_prms_fp8_packed(300, 256, 512, A_, 256, R2_, W1_, 256, DG_, R_, 512, G_, H_, 512,
+                                             HG_, HG_ + 1024, PART_, None) == ALIAS
+    # second GEMM: D not a multiple of 16, NULL operand, Y overlapping X or the exponents
+    assert lib.coda_gemm_rowscale_fp8_packed(300, 264, 512, HG_, EX_, W2_, DG_, R2_, Y_, 512, None) == SHAPE
+    assert lib.coda_gemm_rowscale_fp8_packed(300, 256, 512, None, EX_, W2_, DG_, R2_, Y_, 512, None) == NULL
+    assert lib.coda_gemm_rowscale_fp8_packed(300, 256, 512, HG_, EX_, W2_, DG_, R2_, HG_ + 16, 512, None) == ALIAS
+    assert lib.coda_gemm_rowscale_fp8_packed(300, 256, 512, HG_, EX_, W2_, DG_, R2_, EX_ + 16, 512, None) == ALIAS
+    assert lib.coda_gemm_rowscale_fp8_packed(300, 256, 512, HG_, EX_ + 8, W2_, DG_, R2_, Y_, 512, None) == ALIGN
+    assert lib.coda_gemm_rowscale_fp8_packed(0, 256, 512, None, None, None, None, None, None, 512, None) == OK
 
 
 def test_lse_ce_rope_packed_validation(lib):

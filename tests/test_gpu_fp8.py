@@ -5,10 +5,12 @@ Inputs are the seeded fp8 workloads (e4m3 codes with per-row / per-channel
 scales).  Compared with the fp64 oracle of the same chain (oracle/fp8.py):
   * Y: max|Y - Y_ref| / max|Y_ref| <= 1e-2;
   * H: max|H - H_ref| / max|H_ref| <= 2^-8 (a bf16 rounding);
-  * Hg8: bit-exact against host arithmetic on the GPU's own H (the
-    quantisation decision in the kernel's precision: e4m3 of the float32
-    product); against the oracle's codes, equal except where the GPU's H
-    differs from the bf16 rounding of the exact H, and then one code apart;
+  * Hg8 and its MX block exponents: bit-exact against host arithmetic on
+    the GPU's own H (the quantisation decision in the kernel's precision:
+    the block exponent of the float32 products, then e4m3 of the scaled
+    product); against the oracle's, equal except in blocks where the GPU's
+    H differs from the bf16 rounding of the exact H, and there within one
+    e4m3 step of the dequantised value;
   * r: as in the bf16 chain.
 """
 import sys
@@ -44,16 +46,64 @@ def _run(wl, seed):
     x = ci.make_inputs_fp8(wl, seed=seed)
     d = {"A8": _u8(x["A8"]), "sa": _f32(x["sa"]), "W1t8": _u8(x["W1t8"]), "sw1": _f32(x["sw1"]),
          "W2t8": _u8(x["W2t8"]), "sw2": _f32(x["sw2"]), "R": dev(x["R"]), "g": dev(x["g"])}
-    H, Hg8, r, Y, P = coda.fused_forward_fp8(d["A8"], d["sa"], d["W1t8"], d["sw1"], d["R"], d["g"], d["W2t8"],
-                                             d["sw2"], wl.eps)
+    H, Hg8, E, r, Y, P = coda.fused_forward_fp8(d["A8"], d["sa"], d["W1t8"], d["sw1"], d["R"], d["g"], d["W2t8"],
+                                                d["sw2"], wl.eps)
     torch.cuda.synchronize()
-    return x, d, {"H": H, "Hg8": Hg8, "r": r, "Y": Y, "P": P}
+    return x, d, {"H": H, "Hg8": Hg8, "E": E, "r": r, "Y": Y, "P": P}
 
 
-def _magnitude_rank(codes):
-    """Position of each code in increasing value order (sign-magnitude)."""
-    c = codes.astype(np.int64)
-    return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+def _blk(Eb, b):
+    """The bytes [rows] of block b (32 columns) in an exponent array
+    [G, rows, 2, 4]: half b % 2 of k-tile t = b // 2, at [t // 4, :, h, t % 4]."""
+    t = b // 2
+    return Eb[t // 4, :, b % 2, t % 4]
+
+
+def _block_exponents(Eb, D):
+    """int exponents [rows, ceil(D/32)] from the byte array."""
+    return np.stack([_blk(Eb, b) for b in range(-(-D // 32))], axis=1).astype(np.int64) - 127
+
+
+def _check_codes(H, g32, codes, Eb, orc=None):
+    """Hg8 codes and exponents against host arithmetic on the GPU's own H,
+    then (orc given) against the oracle's; returns (codes differ, blocks
+    differ) as fractions."""
+    D = H.shape[1]
+    # the quantisation decision, in the kernel's precision, on the GPU's own H
+    hg = (H.astype(np.float32) * g32[None, :]).astype(np.float32)
+    E_host = oracle.mx_exponents(hg)
+    E_gpu = _block_exponents(Eb, D)
+    np.testing.assert_array_equal(E_gpu, E_host)
+    # every block past D, up to the array's end, holds exponent 0 (byte 127)
+    for b in range(-(-D // 32), 8 * Eb.shape[0]):
+        assert np.all(_blk(Eb, b) == 127)
+    Ecol = np.repeat(E_host, 32, axis=1)[:, :D]
+    np.testing.assert_array_equal(codes, oracle.e4m3_encode(np.ldexp(hg.astype(np.float64), -Ecol)))
+    if orc is None:
+        return 0.0, 0.0
+    # against the oracle: the exponent differs only in blocks where H itself
+    # rounded differently, and a code only in such blocks or where its own H
+    # differs; the dequantised values differ by at most the difference of
+    # the products plus one e4m3 step (the block scale makes the step at a
+    # small value far finer than H's own deviation there)
+    hdiff = H != orc["Hb"]
+    nb = E_host.shape[1]
+    hblk = np.zeros(E_host.shape, dtype=bool)
+    for b in range(nb):
+        hblk[:, b] = hdiff[:, 32 * b:32 * b + 32].any(axis=1)
+    ediff = E_host != orc["Hg8_exp"]
+    assert np.all(hblk[ediff])
+    diff = codes != orc["Hg8"]
+    blkcol = np.repeat(ediff, 32, axis=1)[:, :D]
+    assert np.all((hdiff | blkcol)[diff])
+    v_gpu = np.ldexp(oracle.e4m3_decode(codes), Ecol)
+    Eo = np.repeat(orc["Hg8_exp"], 32, axis=1)[:, :D]
+    v_orc = np.ldexp(oracle.e4m3_decode(orc["Hg8"]), Eo)
+    # half an e4m3 spacing each side, subnormals included, at the coarser exponent
+    step = np.ldexp(np.maximum(np.abs(v_orc), np.ldexp(1.0, np.maximum(Ecol, Eo) - 6)), -3)
+    hg_orc = (orc["Hb"].astype(np.float32) * g32[None, :]).astype(np.float32)
+    assert np.all(np.abs(v_gpu - v_orc) <= np.abs(hg.astype(np.float64) - hg_orc) + step)
+    return float(diff.mean()), float(ediff.mean())
 
 
 def _check(wl, x, o, rows=None):
@@ -62,27 +112,21 @@ def _check(wl, x, o, rows=None):
     sel = slice(None) if rows is None else np.asarray(rows)
     H = host_f32(o["H"])[sel]
     herr = max_rel(H, orc["H"])
-    # the quantisation decision, in the kernel's precision, on the GPU's own H
-    hg = (H.astype(np.float32) * x["g"].f32[None, :]).astype(np.float32)
-    gpu_codes = o["Hg8"].cpu().numpy()[sel]
-    np.testing.assert_array_equal(gpu_codes, oracle.e4m3_encode(hg))
-    # against the oracle's codes: differences only where H itself rounded differently
-    diff = gpu_codes != orc["Hg8"]
+    codes = o["Hg8"].cpu().numpy()[sel]
+    Eb = o["E"].cpu().numpy()[:, sel]
+    cdiff, ediff = _check_codes(H, x["g"].f32, codes, Eb, orc)
     hdiff = H != orc["Hb"]
-    dist = np.abs(_magnitude_rank(gpu_codes) - _magnitude_rank(orc["Hg8"]))
-    print(f"H max_rel {herr:.2e}, H bits differ {hdiff.mean():.2e}, codes differ {diff.mean():.2e}, "
-          f"max code distance {dist.max()}", file=sys.__stderr__, flush=True)
+    print(f"H max_rel {herr:.2e}, H bits differ {hdiff.mean():.2e}, codes differ {cdiff:.2e}, "
+          f"block exponents differ {ediff:.2e}", file=sys.__stderr__, flush=True)
     assert herr <= 2.0 ** -8, f"H error {herr:.3e}"
     # H from the fp8 products misses the bf16 rounding of the exact value in
     # up to ~1% of elements (measured 0.4-0.95%; small |H|, absolute deviation
-    # ~3e-4); a code differs only there, and by one step at most, because that
-    # deviation is below the smallest e4m3 spacing (2^-9)
-    assert np.all(hdiff[diff])
-    assert hdiff.mean() <= 0.03 and diff.mean() <= 0.005 and dist.max() <= 1
+    # ~3e-4)
+    assert hdiff.mean() <= 0.03 and cdiff <= 0.005 and ediff <= 0.005
     np.testing.assert_allclose(o["r"].cpu().numpy()[sel], orc["r"], rtol=2e-3)
     err = max_rel(host_f32(o["Y"])[sel], orc["Y"])
     assert err <= 1e-2, f"Y error {err:.3e}"
-    return err, diff.mean()
+    return err, cdiff
 
 
 SHAPES = [  # M, K, D, N2 (multiples of 16, ragged against the 256 tiles)
@@ -109,14 +153,113 @@ def test_fp8_repeatable_and_unscaled_second_gemm():
     wl = ci.custom_workload(300, 256, 512, 768, dtype="fp8", wl_id=501)
     x, d, o = _run(wl, seed=2)
     Y2 = torch.full_like(o["Y"], float("nan"))
-    coda.coda_gemm_rowscale_fp8(o["Hg8"], d["W2t8"], d["sw2"], o["r"], Y2)
+    coda.coda_gemm_rowscale_fp8(o["Hg8"], o["E"], d["W2t8"], d["sw2"], o["r"], Y2)
     Y3 = torch.empty_like(o["Y"])
-    coda.coda_gemm_rowscale_fp8(o["Hg8"], d["W2t8"], d["sw2"], None, Y3)   # r = NULL: no row scale
+    coda.coda_gemm_rowscale_fp8(o["Hg8"], None, d["W2t8"], d["sw2"], None, Y3)   # no exponents, no row scale
+    Y4 = torch.empty_like(o["Y"])
+    coda.coda_gemm_rowscale_fp8(o["Hg8"], o["E"], d["W2t8"], d["sw2"], None, Y4)  # exponents, no row scale
     torch.cuda.synchronize()
     assert torch.equal(Y2.view(torch.int16), o["Y"].view(torch.int16))
     xq = oracle.e4m3_decode(o["Hg8"].cpu().numpy())
-    ref = xq @ (oracle.e4m3_decode(x["W2t8"]) * x["sw2"][:, None].astype(np.float64)).T
-    assert max_rel(host_f32(Y3), ref) <= 2.0 ** -8
+    W2 = (oracle.e4m3_decode(x["W2t8"]) * x["sw2"][:, None].astype(np.float64)).T
+    assert max_rel(host_f32(Y3), xq @ W2) <= 2.0 ** -8
+    Ecol = np.repeat(_block_exponents(o["E"].cpu().numpy(), wl.D), 32, axis=1)[:, :wl.D]
+    assert max_rel(host_f32(Y4), np.ldexp(xq, Ecol) @ W2) <= 2.0 ** -8
+
+
+def _mx_case(M, D, N2, seed):
+    """Random codes, block exponents in [-6, 6] and weights for the MX
+    second GEMM; the exponent bytes of blocks past D are random finite codes
+    (their columns are zero) and the bytes of k-tiles past D are 0xFF (never
+    read)."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=(M, D), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C                     # no NaN codes
+    nb, nk, G = -(-D // 32), -(-D // 64), -(-D // 256)
+    E = rng.integers(-6, 7, size=(M, nb))
+    Eb = np.full((G, M, 2, 4), 0xFF, dtype=np.uint8)
+    for b in range(2 * nk):
+        t = b // 2
+        Eb[t // 4, :, b % 2, t % 4] = (E[:, b] + 127) if b < nb else rng.integers(0, 255, size=M)
+    W2t8 = rng.integers(0, 256, size=(N2, D), dtype=np.uint8)
+    W2t8[(W2t8 & 0x7F) == 0x7F] = 0x38
+    sw2 = np.exp2(rng.integers(-8, 1, size=N2)).astype(np.float32)
+    X = np.ldexp(oracle.e4m3_decode(codes), np.repeat(E, 32, axis=1)[:, :D])
+    terms = np.abs(X) @ np.abs(oracle.e4m3_decode(W2t8) * sw2[:, None].astype(np.float64)).T
+    ref = X @ (oracle.e4m3_decode(W2t8) * sw2[:, None].astype(np.float64)).T
+    return codes, Eb, W2t8, sw2, ref, terms
+
+
+@pytest.mark.parametrize("shape", [(1, 16, 256), (5, 96, 16), (64, 176, 272), (37, 272, 528), (300, 384, 256),
+                                   (260, 448, 784), (300, 528, 256), (260, 1040, 784), (513, 4096, 512)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("packed", [False, True], ids=["row_major", "packed"])
+def test_mx_second_gemm_random_exponents(shape, packed):
+    # random codes with a random exponent per block of every row, against
+    # the fp64 product of the dequantised operands; D covers 1 to 64 k-tiles
+    # with 0 to 3 of them after the last whole group
+    M, D, N2 = shape
+    codes, Eb, W2t8, sw2, ref, terms = _mx_case(M, D, N2, seed=M + D + N2)
+    Y = torch.full((M, N2), float("nan"), device="cuda", dtype=torch.bfloat16)
+    if packed:
+        coda.coda_gemm_rowscale_fp8_packed(_pack8(codes).cuda(), _u8(Eb), _pack8(W2t8).cuda(), _f32(sw2), None, Y)
+    else:
+        coda.coda_gemm_rowscale_fp8(_u8(codes), _u8(Eb), _u8(W2t8), _f32(sw2), None, Y)
+    torch.cuda.synchronize()
+    got = host_f32(Y).astype(np.float64)
+    # bf16 rounding of the result plus the accumulation over D terms: the
+    # matrix core sums e4m3 products below float32 precision (measured up to
+    # 2^-14 of sum |terms| when the block exponents span 2^+-24), so the
+    # bound allows 2^-12 of it; one block with a wrong exponent moves a
+    # result by about 2^-10 of sum |terms| even at D = 4096
+    bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -12 * terms
+    assert np.all(np.abs(got - ref) <= bound), float(np.max(np.abs(got - ref) / np.maximum(bound, 1e-300)))
+
+
+@pytest.mark.parametrize("MD", [(1, 16), (37, 96), (40, 176), (33, 272), (37, 448)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("packed", [False, True], ids=["row_major", "packed"])
+def test_mx_block_exponent_map(MD, packed):
+    # exact: with ones in block b only and a distinct exponent in every byte
+    # (varying with the row too), each output is 2^E(row, b) times the
+    # unscaled one, so the byte the products take for block b is read off
+    M, D = MD
+    N2 = 32
+    nb, G = -(-D // 32), -(-D // 256)
+    Eb = np.zeros((G, M, 2, 4), dtype=np.uint8)
+    for i in range(M):
+        for h in range(2):
+            for t in range(4 * G):
+                Eb[t // 4, i, h, t % 4] = 127 + (8 * G * h + t + 3 * i) % 41 - 20
+    W = np.full((N2, D), 0x38, dtype=np.uint8)             # e4m3 1.0
+    sw = _f32(np.ones(N2, dtype=np.float32))
+    Ed = _u8(Eb)
+    for b in range(nb):
+        X = np.zeros((M, D), dtype=np.uint8)
+        X[:, 32 * b:32 * b + 32] = 0x38
+        Y = torch.empty((M, N2), device="cuda", dtype=torch.bfloat16)
+        Yu = torch.empty((M, N2), device="cuda", dtype=torch.bfloat16)
+        if packed:
+            Xp, Wp = _pack8(X).cuda(), _pack8(W).cuda()
+            coda.coda_gemm_rowscale_fp8_packed(Xp, Ed, Wp, sw, None, Y)
+            coda.coda_gemm_rowscale_fp8_packed(Xp, None, Wp, sw, None, Yu)
+        else:
+            coda.coda_gemm_rowscale_fp8(_u8(X), Ed, _u8(W), sw, None, Y)
+            coda.coda_gemm_rowscale_fp8(_u8(X), None, _u8(W), sw, None, Yu)
+        torch.cuda.synchronize()
+        want = _blk(Eb, b).astype(np.float64) - 127
+        ratio = host_f32(Y).astype(np.float64) / host_f32(Yu).astype(np.float64)
+        np.testing.assert_array_equal(ratio, np.repeat(np.exp2(want)[:, None], N2, axis=1),
+                                      err_msg=f"block {b}")
+
+
+def _pack8(a):
+    """A row-major e4m3 matrix [rows, cols] in the tile-packed layout (host)."""
+    rows, cols = a.shape
+    rp = -(-rows // 16) * 16
+    buf = np.zeros((rp, cols), dtype=np.uint8)
+    buf[:rows] = a
+    return torch.from_numpy(np.ascontiguousarray(buf.reshape(rp // 16, 16, cols // 16, 16).transpose(0, 2, 1, 3)))
 
 
 def test_fp8_float8_dtype_accepted():
@@ -126,11 +269,39 @@ def test_fp8_float8_dtype_accepted():
     wl = ci.custom_workload(64, 128, 256, 256, dtype="fp8", wl_id=502)
     x, d, o = _run(wl, seed=3)
     f8 = {k: d[k].view(torch.float8_e4m3fn) for k in ("A8", "W1t8", "W2t8")}
-    H, Hg8, r, Y, P = coda.fused_forward_fp8(f8["A8"], d["sa"], f8["W1t8"], d["sw1"], d["R"], d["g"], f8["W2t8"],
-                                             d["sw2"], wl.eps)
+    H, Hg8, E, r, Y, P = coda.fused_forward_fp8(f8["A8"], d["sa"], f8["W1t8"], d["sw1"], d["R"], d["g"],
+                                                f8["W2t8"], d["sw2"], wl.eps)
     torch.cuda.synchronize()
     assert torch.equal(Y.view(torch.int16), o["Y"].view(torch.int16))
     assert torch.equal(Hg8.view(torch.uint8), o["Hg8"])
+    assert torch.equal(E, o["E"])
+
+
+def test_large_residual_does_not_saturate():
+    # R scaled by 1e3 pushes H g far past e4m3's largest finite value 448: the
+    # block exponents absorb it, so Y stays as close to the exact fp64 chain
+    # (no quantisation of H g at all) as at the ordinary scale
+    wl = ci.custom_workload(300, 256, 512, 768, dtype="fp8", wl_id=504)
+    x = ci.make_inputs_fp8(wl, seed=6)
+    R_big = x["R"].f32 * np.float32(1e3)
+    Rb = ci.bf16_bits(R_big)
+    Rd = torch.from_numpy(Rb.view(np.int16)).cuda().view(torch.bfloat16)
+    Rf = ci.bf16_bits_to_f32(Rb)
+    H, Hg8, E, r, Y, P = coda.fused_forward_fp8(_u8(x["A8"]), _f32(x["sa"]), _u8(x["W1t8"]), _f32(x["sw1"]), Rd,
+                                                dev(x["g"]), _u8(x["W2t8"]), _f32(x["sw2"]), wl.eps)
+    torch.cuda.synchronize()
+    orc = oracle.forward_fp8(x["A8"], x["sa"], x["W1t8"], x["sw1"], Rf, x["g"].f32, x["W2t8"], x["sw2"], wl.eps)
+    # the exact chain: H and H g in fp64, no bf16 or e4m3 rounding between the GEMMs
+    W2 = (oracle.e4m3_decode(x["W2t8"]) * x["sw2"][:, None].astype(np.float64)).T
+    Y_exact = orc["r"][:, None] * ((orc["H"] * x["g"].f32[None, :].astype(np.float64)) @ W2)
+    hg = host_f32(H) * x["g"].f32[None, :]
+    assert np.abs(hg).max() > 448 * 8                       # far past e4m3's range without a scale
+    assert _block_exponents(E.cpu().numpy(), wl.D).max() >= 3
+    err = max_rel(host_f32(Y), Y_exact)
+    err_orc = max_rel(host_f32(Y), orc["Y"])
+    print(f"R x 1e3: Y error vs exact chain {err:.3e}, vs oracle {err_orc:.3e}", file=sys.__stderr__, flush=True)
+    assert err_orc <= 1e-2
+    assert err <= 0.05
 
 
 @pytest.mark.slow
@@ -151,17 +322,14 @@ def test_full_size_7b_fp8_whole_tensor():
         H = o["H"][blk].float().cpu().numpy()
         Y = o["Y"][blk].float().cpu().numpy()
         codes = o["Hg8"][blk].cpu().numpy()
-        hg = (H.astype(np.float32) * x["g"].f32[None, :]).astype(np.float32)
-        np.testing.assert_array_equal(codes, oracle.e4m3_encode(hg))
-        diff = codes != orc["Hg8"]
+        cdiff, _ = _check_codes(H, x["g"].f32, codes, o["E"][:, blk].cpu().numpy(), orc)
+        diff_n = int(round(cdiff * codes.size))
         hdiff = H != orc["Hb"]
-        assert np.all(hdiff[diff])
-        assert np.abs(_magnitude_rank(codes) - _magnitude_rank(orc["Hg8"])).max() <= 1
         np.testing.assert_allclose(o["r"][blk].cpu().numpy(), orc["r"], rtol=2e-3)
         for k, got in (("Y", Y), ("H", H)):
             num[k] = max(num[k], float(np.max(np.abs(got.astype(np.float64) - orc[k]))))
             den[k] = max(den[k], float(np.max(np.abs(orc[k]))))
-        ndiff += int(diff.sum())
+        ndiff += diff_n
         nhdiff += int(hdiff.sum())
     n = wl.M * wl.D
     err, herr = num["Y"] / den["Y"], num["H"] / den["H"]
@@ -283,13 +451,13 @@ def test_chain_from_bf16_activation():
     A8_ref, sa_ref = oracle.quantize_rows(Af)
     d = {"W1t8": _u8(x["W1t8"]), "sw1": _f32(x["sw1"]), "W2t8": _u8(x["W2t8"]), "sw2": _f32(x["sw2"]),
          "R": dev(x["R"]), "g": dev(x["g"])}
-    H, Hg8, r, Y, P, A8, sa = coda.fused_forward_fp8_from_bf16(dA, d["W1t8"], d["sw1"], d["R"], d["g"], d["W2t8"],
-                                                               d["sw2"], wl.eps)
+    H, Hg8, E, r, Y, P, A8, sa = coda.fused_forward_fp8_from_bf16(dA, d["W1t8"], d["sw1"], d["R"], d["g"],
+                                                                  d["W2t8"], d["sw2"], wl.eps)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(A8.cpu().numpy(), A8_ref)
     np.testing.assert_array_equal(sa.cpu().numpy(), sa_ref)
     x2 = dict(x, A8=A8_ref, sa=sa_ref)
-    _check(wl, x2, {"H": H, "Hg8": Hg8, "r": r, "Y": Y})
+    _check(wl, x2, {"H": H, "Hg8": Hg8, "E": E, "r": r, "Y": Y})
 
 
 GRADS8 = ("dA", "dR", "dW1", "dW2", "dg")

@@ -90,10 +90,10 @@ def test_fp8_training_step_graph():
     def step():
         Wt8, sw1 = coda.quantize_weight_e4m3(d["W1"])
         W2t8, sw2 = coda.quantize_weight_e4m3(d["W2"])
-        H, Hg8, r, Y, P, A8, sa = coda.fused_forward_fp8_from_bf16(d["A"], Wt8, sw1, d["R"], d["g"], W2t8, sw2,
-                                                                   wl.eps)
+        H, Hg8, E, r, Y, P, A8, sa = coda.fused_forward_fp8_from_bf16(d["A"], Wt8, sw1, d["R"], d["g"], W2t8, sw2,
+                                                                      wl.eps)
         grads = coda.fused_backward_fp8(d["dY"], d["A"], d["W1"], d["g"], d["W2"], H, r)
-        return (H, Hg8, r, Y, A8, sa) + tuple(grads)
+        return (H, Hg8, E, r, Y, A8, sa) + tuple(grads)
 
     def refill(rnd):
         gen.manual_seed(200 + rnd)

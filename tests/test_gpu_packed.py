@@ -161,16 +161,17 @@ def test_fp8_packed_chain_matches_row_major_and_oracle(shape):
     x = ci.make_inputs_fp8(wl, seed=3)
     d = {"A8": _u8(x["A8"]), "sa": _f32(x["sa"]), "W1t8": _u8(x["W1t8"]), "sw1": _f32(x["sw1"]),
          "W2t8": _u8(x["W2t8"]), "sw2": _f32(x["sw2"]), "R": dev(x["R"]), "g": dev(x["g"])}
-    H, Hg8, r, Y, P = coda.fused_forward_fp8(d["A8"], d["sa"], d["W1t8"], d["sw1"], d["R"], d["g"], d["W2t8"],
-                                             d["sw2"], wl.eps)
+    H, Hg8, E, r, Y, P = coda.fused_forward_fp8(d["A8"], d["sa"], d["W1t8"], d["sw1"], d["R"], d["g"], d["W2t8"],
+                                                d["sw2"], wl.eps)
     # the packed weight codes: the row-major codes permuted
     W2p = coda.packed_empty_e4m3(N2, D, "cuda")
     W2p.copy_(torch.nn.functional.pad(d["W2t8"], (0, 0, 0, (-N2) % 16)).reshape(-1, 16, D // 16, 16)
               .permute(0, 2, 1, 3))
-    Hp, Hg8p, rp, Yp, Pp = coda.fused_forward_fp8_packed(d["A8"], d["sa"], d["W1t8"], d["sw1"], d["R"], d["g"], W2p,
-                                                         d["sw2"], wl.eps)
+    Hp, Hg8p, Ep, rp, Yp, Pp = coda.fused_forward_fp8_packed(d["A8"], d["sa"], d["W1t8"], d["sw1"], d["R"], d["g"],
+                                                             W2p, d["sw2"], wl.eps)
     torch.cuda.synchronize()
     assert torch.equal(coda.unpack_e4m3(Hg8p, M), Hg8)
+    assert torch.equal(Ep, E)
     _same(H, Hp, "H")
     _same(P, Pp, "partials")
     _same(r, rp, "r")
@@ -211,11 +212,12 @@ def test_full_size_7b_fp8_packed():
     W1t8, sw1 = coda.quantize_weight_e4m3(W1)
     W2t8, sw2 = coda.quantize_weight_e4m3(W2)
     W2t8p, sw2p = coda.quantize_weight_e4m3_packed(W2)
-    H, Hg8, r, Y, P = coda.fused_forward_fp8(A8, sa, W1t8, sw1, R, gg, W2t8, sw2, 1e-5)
-    Hp, Hg8p, rp, Yp, Pp = coda.fused_forward_fp8_packed(A8, sa, W1t8, sw1, R, gg, W2t8p, sw2p, 1e-5)
+    H, Hg8, E, r, Y, P = coda.fused_forward_fp8(A8, sa, W1t8, sw1, R, gg, W2t8, sw2, 1e-5)
+    Hp, Hg8p, Ep, rp, Yp, Pp = coda.fused_forward_fp8_packed(A8, sa, W1t8, sw1, R, gg, W2t8p, sw2p, 1e-5)
     torch.cuda.synchronize()
     assert torch.equal(coda.unpack_e4m3(W2t8p, N2), W2t8)
     assert torch.equal(coda.unpack_e4m3(Hg8p, M), Hg8)
+    assert torch.equal(Ep, E)
     _same(Y, Yp, "Y")
 
 

@@ -40,8 +40,10 @@ SIGNATURES = {
     "coda_quantize_rows_e4m3_packed": (c_int, [c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp]),
     "coda_quantize_rows_cols_e4m3_packed": (c_int, [c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "coda_gemm_res_prms_fp8_packed": (c_int, [c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp,
-                                              c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp]),
-    "coda_gemm_rowscale_fp8_packed": (c_int, [c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp]),
+                                              c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp]),
+    "coda_gemm_rowscale_fp8_packed": (c_int, [c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,
+                                              c_vp]),
+    "coda_mx_exp_bytes": (c_i64, [c_i64, c_i64]),
     "coda_gemm_rowscale_swiglu_packed": (c_int, [c_i64, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp,
                                                  c_i64, c_vp]),
     "coda_gemm_rowscale_lse_packed": (c_int, [c_i64, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp,
@@ -71,9 +73,9 @@ SIGNATURES = {
     "coda_rope_bwd": (c_int, [c_int, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp,
                               c_i64, c_vp]),
     "coda_gemm_res_prms_fp8": (c_int, [c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_i64,
-                                       c_vp, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp]),
-    "coda_gemm_rowscale_fp8": (c_int, [c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_i64,
-                                       c_vp]),
+                                       c_vp, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp]),
+    "coda_gemm_rowscale_fp8": (c_int, [c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp,
+                                       c_i64, c_vp]),
     "coda_ref_chain_workspace_bytes": (c_size, [c_int, c_i64, c_i64]),
     "coda_ref_chain": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64, c_float, c_vp, c_vp, c_vp, c_vp,
                                c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),

@@ -329,8 +329,33 @@ def _mat8(t: torch.Tensor, name: str, shape) -> int:
     return _mat(t, name, t.dtype, shape)
 
 
-def coda_gemm_res_prms_fp8(A8, sa, W1t8, sw1, R, g, H, Hg8, partials, stream=None) -> None:
-    """fp8 first GEMM: H = bf16(acc sa sw1 + R), Hg8 = e4m3(H g), partial sums of squares."""
+def mx_exp_empty(rows: int, cols: int, device) -> torch.Tensor:
+    """A block-exponent array for a [rows, cols] MX operand: uint8
+    [G, rows, 2, 4] with G = ceil(cols / 256); byte [t // 4, i, h, t % 4] is
+    the E8M0 exponent of columns [64 t + 32 h, + 32) of row i."""
+    return torch.empty(((cols + 255) // 256, rows, 2, 4), device=device, dtype=torch.uint8)
+
+
+def mx_exponents_of(E: torch.Tensor, cols: int) -> torch.Tensor:
+    """The int32 exponents [rows, ceil(cols / 32)] an exponent array holds
+    (E8M0 codes minus 127); block b of a row is half b % 2 of k-tile b // 2."""
+    nb = (cols + 31) // 32
+    b = torch.arange(nb, device=E.device)
+    t = b // 2
+    return E[t // 4, :, b % 2, t % 4].T.to(torch.int32) - 127
+
+
+def _mx(E: torch.Tensor, name: str, rows: int, cols: int) -> None:
+    shape = ((cols + 255) // 256, rows, 2, 4)
+    if E.dtype != torch.uint8 or tuple(E.shape) != shape or not E.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous uint8 tensor of shape {shape}, got {E.dtype} {tuple(E.shape)}")
+    if E.data_ptr() % 16 != 0:
+        raise ValueError(f"{name} is not 16-byte aligned")
+
+
+def coda_gemm_res_prms_fp8(A8, sa, W1t8, sw1, R, g, H, Hg8, Hg8_exp, partials, stream=None) -> None:
+    """fp8 first GEMM: H = bf16(acc sa sw1 + R), Hg8 = e4m3(H g 2^-E) with the
+    MX block exponents E in Hg8_exp (mx_exp_empty(M, D)), partial sums of squares."""
     lib = _lib.load()
     M, K = A8.shape
     D = W1t8.shape[0]
@@ -338,6 +363,7 @@ def coda_gemm_res_prms_fp8(A8, sa, W1t8, sw1, R, g, H, Hg8, partials, stream=Non
     lda = _mat8(A8, "A8", (M, K))
     ldw = _mat8(W1t8, "W1t8", (D, K))
     ldhg = _mat8(Hg8, "Hg8", (M, D))
+    _mx(Hg8_exp, "Hg8_exp", M, D)
     _mat(sa, "sa", torch.float32, (M,))
     _mat(sw1, "sw1", torch.float32, (D,))
     ldr = _mat(R, "R", torch.bfloat16, (M, D))
@@ -347,22 +373,27 @@ def coda_gemm_res_prms_fp8(A8, sa, W1t8, sw1, R, g, H, Hg8, partials, stream=Non
     _dense(partials, "partials")
     st = lib.coda_gemm_res_prms_fp8(M, K, D, A8.data_ptr(), lda, sa.data_ptr(), W1t8.data_ptr(), ldw,
                                     sw1.data_ptr(), R.data_ptr(), ldr, g.data_ptr(), H.data_ptr(), ldh,
-                                    Hg8.data_ptr(), ldhg, partials.data_ptr(), _stream(stream))
+                                    Hg8.data_ptr(), ldhg, Hg8_exp.data_ptr(), partials.data_ptr(), _stream(stream))
     _lib.check("coda_gemm_res_prms_fp8", st)
 
 
-def coda_gemm_rowscale_fp8(X8, W2t8, sw2, r: Optional[torch.Tensor], Y, stream=None) -> None:
-    """fp8 second GEMM: Y = bf16(acc r sw2), W2 given transposed ([N2, D])."""
+def coda_gemm_rowscale_fp8(X8, X8_exp: Optional[torch.Tensor], W2t8, sw2, r: Optional[torch.Tensor], Y,
+                           stream=None) -> None:
+    """fp8 second GEMM: Y = bf16(acc r sw2), acc over X8's codes times 2^E
+    (X8_exp, or E = 0 when None), W2 given transposed ([N2, D])."""
     lib = _lib.load()
     M, D = X8.shape
     N2 = W2t8.shape[0]
     ldx = _mat8(X8, "X8", (M, D))
     ldw = _mat8(W2t8, "W2t8", (N2, D))
+    if X8_exp is not None:
+        _mx(X8_exp, "X8_exp", M, D)
     _mat(sw2, "sw2", torch.float32, (N2,))
     ldy = _mat(Y, "Y", torch.bfloat16, (M, N2))
     if r is not None:
         _mat(r, "r", torch.float32, (M,))
-    st = lib.coda_gemm_rowscale_fp8(M, D, N2, X8.data_ptr(), ldx, W2t8.data_ptr(), ldw, sw2.data_ptr(),
+    st = lib.coda_gemm_rowscale_fp8(M, D, N2, X8.data_ptr(), ldx, X8_exp.data_ptr() if X8_exp is not None else None,
+                                    W2t8.data_ptr(), ldw, sw2.data_ptr(),
                                     r.data_ptr() if r is not None else None, Y.data_ptr(), ldy, _stream(stream))
     _lib.check("coda_gemm_rowscale_fp8", st)
 
@@ -632,7 +663,7 @@ def quantize_weight_e4m3_packed(W, stream=None, Wt8p=None, scales=None):
     return Wt8p, scales
 
 
-def coda_gemm_res_prms_fp8_packed(A8, sa, W1t8, sw1, R, g, H, Hg8p, partials, stream=None) -> None:
+def coda_gemm_res_prms_fp8_packed(A8, sa, W1t8, sw1, R, g, H, Hg8p, Hg8_exp, partials, stream=None) -> None:
     """coda_gemm_res_prms_fp8 with Hg8 written tile-packed into Hg8p."""
     lib = _lib.load()
     M, K = A8.shape
@@ -641,6 +672,7 @@ def coda_gemm_res_prms_fp8_packed(A8, sa, W1t8, sw1, R, g, H, Hg8p, partials, st
     lda = _mat8(A8, "A8", (M, K))
     ldw = _mat8(W1t8, "W1t8", (D, K))
     _packed8(Hg8p, "Hg8", M, D)
+    _mx(Hg8_exp, "Hg8_exp", M, D)
     _mat(sa, "sa", torch.float32, (M,))
     _mat(sw1, "sw1", torch.float32, (D,))
     ldr = _mat(R, "R", torch.bfloat16, (M, D))
@@ -650,22 +682,28 @@ def coda_gemm_res_prms_fp8_packed(A8, sa, W1t8, sw1, R, g, H, Hg8p, partials, st
     _dense(partials, "partials")
     st = lib.coda_gemm_res_prms_fp8_packed(M, K, D, A8.data_ptr(), lda, sa.data_ptr(), W1t8.data_ptr(), ldw,
                                            sw1.data_ptr(), R.data_ptr(), ldr, g.data_ptr(), H.data_ptr(), ldh,
-                                           Hg8p.data_ptr(), partials.data_ptr(), _stream(stream))
+                                           Hg8p.data_ptr(), Hg8_exp.data_ptr(), partials.data_ptr(),
+                                           _stream(stream))
     _lib.check("coda_gemm_res_prms_fp8_packed", st)
 
 
-def coda_gemm_rowscale_fp8_packed(X8p, W2t8p, sw2, r: Optional[torch.Tensor], Y, stream=None) -> None:
-    """coda_gemm_rowscale_fp8 with both operands tile-packed."""
+def coda_gemm_rowscale_fp8_packed(X8p, X8_exp: Optional[torch.Tensor], W2t8p, sw2, r: Optional[torch.Tensor], Y,
+                                  stream=None) -> None:
+    """coda_gemm_rowscale_fp8 with both operands tile-packed (X8_exp row-major)."""
     lib = _lib.load()
     M, N2 = Y.shape
     D = X8p.shape[1] * 16
     _packed8(X8p, "X8", M, D)
     _packed8(W2t8p, "W2t8", N2, D)
+    if X8_exp is not None:
+        _mx(X8_exp, "X8_exp", M, D)
     _mat(sw2, "sw2", torch.float32, (N2,))
     ldy = _mat(Y, "Y", torch.bfloat16, (M, N2))
     if r is not None:
         _mat(r, "r", torch.float32, (M,))
-    st = lib.coda_gemm_rowscale_fp8_packed(M, D, N2, X8p.data_ptr(), W2t8p.data_ptr(), sw2.data_ptr(),
+    st = lib.coda_gemm_rowscale_fp8_packed(M, D, N2, X8p.data_ptr(),
+                                           X8_exp.data_ptr() if X8_exp is not None else None,
+                                           W2t8p.data_ptr(), sw2.data_ptr(),
                                            r.data_ptr() if r is not None else None, Y.data_ptr(), ldy,
                                            _stream(stream))
     _lib.check("coda_gemm_rowscale_fp8_packed", st)
@@ -678,18 +716,19 @@ def unpack_e4m3(Xp: torch.Tensor, rows: int) -> torch.Tensor:
 
 
 def fused_forward_fp8_packed(A8, sa, W1t8, sw1, R, g, W2t8p, sw2, eps: float, stream=None):
-    """The fp8 chain with Hg8 and W2t8 tile-packed: returns (H, Hg8p, r, Y, partials)."""
+    """The fp8 chain with Hg8 and W2t8 tile-packed: returns (H, Hg8p, Hg8_exp, r, Y, partials)."""
     M, D, N2 = A8.shape[0], W1t8.shape[0], sw2.shape[0]
     dev = A8.device
     H = torch.empty((M, D), device=dev, dtype=torch.bfloat16)
     Hg8p = packed_empty_e4m3(M, D, dev)
+    E = mx_exp_empty(M, D, dev)
     P = torch.empty((coda_prms_num_partials(torch.bfloat16, D), M), device=dev, dtype=torch.float32)
     r = torch.empty((M,), device=dev, dtype=torch.float32)
     Y = torch.empty((M, N2), device=dev, dtype=torch.bfloat16)
-    coda_gemm_res_prms_fp8_packed(A8, sa, W1t8, sw1, R, g, H, Hg8p, P, stream)
+    coda_gemm_res_prms_fp8_packed(A8, sa, W1t8, sw1, R, g, H, Hg8p, E, P, stream)
     coda_rms_combine(P, r, D, eps, stream)
-    coda_gemm_rowscale_fp8_packed(Hg8p, W2t8p, sw2, r, Y, stream)
-    return H, Hg8p, r, Y, P
+    coda_gemm_rowscale_fp8_packed(Hg8p, E, W2t8p, sw2, r, Y, stream)
+    return H, Hg8p, E, r, Y, P
 
 
 def quantize_rows_cols_e4m3(X, stream=None):
@@ -737,18 +776,20 @@ def quantize_rows_cols_e4m3_packed(X, stream=None):
 
 
 def fused_forward_fp8(A8, sa, W1t8, sw1, R, g, W2t8, sw2, eps: float, stream=None):
-    """The fused chain with fp8 GEMM operands: returns (H, Hg8, r, Y, partials)."""
+    """The fused chain with fp8 GEMM operands: returns (H, Hg8, Hg8_exp, r, Y,
+    partials), Hg8_exp the MX block exponents of Hg8 (mx_exp_empty layout)."""
     M, D, N2 = A8.shape[0], W1t8.shape[0], W2t8.shape[0]
     dev = A8.device
     H = torch.empty((M, D), device=dev, dtype=torch.bfloat16)
     Hg8 = torch.empty((M, D), device=dev, dtype=A8.dtype)
+    E = mx_exp_empty(M, D, dev)
     P = torch.empty((coda_prms_num_partials(torch.bfloat16, D), M), device=dev, dtype=torch.float32)
     r = torch.empty((M,), device=dev, dtype=torch.float32)
     Y = torch.empty((M, N2), device=dev, dtype=torch.bfloat16)
-    coda_gemm_res_prms_fp8(A8, sa, W1t8, sw1, R, g, H, Hg8, P, stream)
+    coda_gemm_res_prms_fp8(A8, sa, W1t8, sw1, R, g, H, Hg8, E, P, stream)
     coda_rms_combine(P, r, D, eps, stream)
-    coda_gemm_rowscale_fp8(Hg8, W2t8, sw2, r, Y, stream)
-    return H, Hg8, r, Y, P
+    coda_gemm_rowscale_fp8(Hg8, E, W2t8, sw2, r, Y, stream)
+    return H, Hg8, E, r, Y, P
 
 
 def fused_forward_ce(A, W1, R, g, Wv, eps: float, targets, stream=None):
@@ -909,7 +950,7 @@ def fused_forward_rope_packed(A, W1, R, g, Wqkv, eps: float, positions, cos_sin,
 
 def fused_forward_fp8_from_bf16(A, W1t8, sw1, R, g, W2t8, sw2, eps: float, stream=None):
     """The fp8 chain fed with a bf16 activation A: A quantised per row on the
-    device, then the fp8 chain; returns (H, Hg8, r, Y, partials, A8, sa)."""
+    device, then the fp8 chain; returns (H, Hg8, Hg8_exp, r, Y, partials, A8, sa)."""
     A8, sa = quantize_rows_e4m3(A, stream)
     return fused_forward_fp8(A8, sa, W1t8, sw1, R, g, W2t8, sw2, eps, stream) + (A8, sa)
 

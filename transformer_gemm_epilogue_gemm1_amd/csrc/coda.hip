@@ -141,11 +141,17 @@ coda_status launch_gemm(const char* what, int M, int N, int K, const void* a, in
 // Bytes of a tile-packed e4m3 matrix (kp_unit): rows padded to 16, cols / 16 chunks.
 int64_t packed_bytes_e4m3(int64_t rows, int64_t cols) { return (rows + 15) / 16 * 16 * cols; }
 
+// Bytes of a block-exponent array (mx_byte layout) for `rows` rows and
+// `cols` contraction columns: 8 bytes per row and group of 4 k-tiles.
+int64_t mx_exp_bytes(int64_t rows, int64_t cols) { return 8 * rows * ((cols + 255) / 256); }
+
 // L: OpLayout of both operands (kLayPacked: lda / ldb counting 16-byte chunks
-// per row).
-template <class Epi, int L = kLayKC>
+// per row).  MX: a_exp holds the block exponents of A (mx_byte layout,
+// mx_exp_bytes(M, K) bytes).
+template <class Epi, int L = kLayKC, bool MX = false>
 coda_status launch_gemm_fp8(const char* what, int M, int N, int K, const void* a, int64_t lda, const void* b,
-                            int64_t ldb, const typename Epi::Params& ep, hipStream_t s) {
+                            int64_t ldb, const typename Epi::Params& ep, hipStream_t s,
+                            const void* a_exp = nullptr) {
   GemmArgs g;
   g.M = M;
   g.N = N;
@@ -160,7 +166,8 @@ coda_status launch_gemm_fp8(const char* what, int M, int N, int K, const void* a
   g.ldb = ldb;
   g.b_span = L == kLayPacked ? (uint32_t)packed_bytes_e4m3(N, 16 * ldb) : span_bytes(N, K, ldb, 1);
   g.b_split = 0;
-  hipLaunchKernelGGL((gemm_fp8_kernel<Epi, L>), dim3(g.tiles_m * g.tiles_n), dim3(kThreads), 0, s, g, ep);
+  const MxArgs mx{(const uint8_t*)a_exp, M, (uint32_t)mx_exp_bytes(M, K)};
+  hipLaunchKernelGGL((gemm_fp8_kernel<Epi, L, MX>), dim3(g.tiles_m * g.tiles_n), dim3(kThreads), 0, s, g, ep, mx);
   return launch_status(what);
 }
 
@@ -835,28 +842,31 @@ coda_status coda_rope_bwd(coda_dtype dt, int64_t M, int64_t N2, const void* dYr,
 
 coda_status coda_gemm_res_prms_fp8(int64_t M, int64_t K, int64_t D, const void* A8, int64_t lda, const float* sa,
                                    const void* W1t8, int64_t ldw1t, const float* sw1, const void* R, int64_t ldr,
-                                   const void* g, void* H, int64_t ldh, void* Hg8, int64_t ldhg, float* partials,
-                                   void* stream) {
+                                   const void* g, void* H, int64_t ldh, void* Hg8, int64_t ldhg, void* hg_exp,
+                                   float* partials, void* stream) {
   coda_status st = check_dims_fp8(M, {{"K", K}, {"D", D}});
   if (st != CODA_OK) return st;
   if (M == 0) return ok();
   const int64_t T = num_partials(D);
+  const int64_t eb = mx_exp_bytes(M, D);
   const Mat mA{A8, M, K, lda, 1, "A8"}, mW{W1t8, D, K, ldw1t, 1, "W1t8"}, mR{R, M, D, ldr, 2, "R"};
   const Mat mg{g, 1, D, D, 2, "g"}, mH{H, M, D, ldh, 2, "H"}, mHg{Hg8, M, D, ldhg, 1, "Hg8"};
   const Mat mP{partials, T, M, M, 4, "partials"}, msa{sa, 1, M, M, 4, "sa"}, msw{sw1, 1, D, D, 4, "sw1"};
+  const Mat mE{hg_exp, 1, eb, eb, 1, "hg_exp"};
   for (const Mat* m : {&mA, &mW, &mHg})
     if ((st = check_mat(*m, 16)) != CODA_OK) return st;
   for (const Mat* m : {&mR, &mg, &mH})
     if ((st = check_mat(*m, 8)) != CODA_OK) return st;
+  if ((st = check_mat(mE, 4)) != CODA_OK) return st;
   if ((st = check_vec(sa, M, 4, "sa")) != CODA_OK || (st = check_vec(sw1, D, 16, "sw1")) != CODA_OK) return st;
   if (partials == nullptr) return fail(CODA_ERR_NULL, "partials is NULL");
   if (((uintptr_t)partials & 3) != 0) return fail(CODA_ERR_ALIGN, "partials is not 4-byte aligned");
   if (mP.span() > kMaxSpan) return fail(CODA_ERR_SHAPE, "partials span too large");
-  const Mat outs[3] = {mH, mHg, mP};
+  const Mat outs[4] = {mH, mHg, mP, mE};
   const Mat ins[6] = {mA, mW, mR, mg, msa, msw};
-  if ((st = check_alias(outs, 3, ins, 6)) != CODA_OK) return st;
+  if ((st = check_alias(outs, 4, ins, 6)) != CODA_OK) return st;
   EpiResPrmsFp8::Params ep{sa, sw1, (const uint16_t*)R, ldr, (const uint16_t*)g, (uint16_t*)H, ldh,
-                           (uint8_t*)Hg8, ldhg, partials};
+                           (uint8_t*)Hg8, ldhg, partials, 0, (uint8_t*)hg_exp};
   return launch_gemm_fp8<EpiResPrmsFp8>("coda_gemm_res_prms_fp8", (int)M, (int)D, (int)K, A8, lda, W1t8, ldw1t,
                                         ep, (hipStream_t)stream);
 }
@@ -915,23 +925,28 @@ coda_status coda_quantize_rows_cols_e4m3(int64_t M, int64_t N, const void* X, in
   return launch_status("coda_quantize_rows_cols_e4m3");
 }
 
-coda_status coda_gemm_rowscale_fp8(int64_t M, int64_t D, int64_t N2, const void* X8, int64_t ldx, const void* W2t8,
-                                   int64_t ldw2t, const float* sw2, const float* r, void* Y, int64_t ldy,
-                                   void* stream) {
+coda_status coda_gemm_rowscale_fp8(int64_t M, int64_t D, int64_t N2, const void* X8, int64_t ldx,
+                                   const void* x_exp, const void* W2t8, int64_t ldw2t, const float* sw2,
+                                   const float* r, void* Y, int64_t ldy, void* stream) {
   coda_status st = check_dims_fp8(M, {{"D", D}, {"N2", N2}});
   if (st != CODA_OK) return st;
   if (M == 0) return ok();
+  const int64_t eb = mx_exp_bytes(M, D);
   const Mat mX{X8, M, D, ldx, 1, "X8"}, mW{W2t8, N2, D, ldw2t, 1, "W2t8"}, mY{Y, M, N2, ldy, 2, "Y"};
-  const Mat mr{r, 1, M, M, 4, "r"}, msw{sw2, 1, N2, N2, 4, "sw2"};
+  const Mat mr{r, 1, M, M, 4, "r"}, msw{sw2, 1, N2, N2, 4, "sw2"}, mE{x_exp, 1, eb, eb, 1, "x_exp"};
   for (const Mat* m : {&mX, &mW})
     if ((st = check_mat(*m, 16)) != CODA_OK) return st;
   if ((st = check_mat(mY, 8)) != CODA_OK) return st;
+  if (x_exp != nullptr && (st = check_mat(mE, 4)) != CODA_OK) return st;
   if ((st = check_vec(sw2, N2, 16, "sw2")) != CODA_OK) return st;
   if (r != nullptr && ((uintptr_t)r & 3) != 0) return fail(CODA_ERR_ALIGN, "r is not 4-byte aligned");
   const Mat none{nullptr, 0, 0, 0, 4, ""};
-  const Mat ins[4] = {mX, mW, msw, r ? mr : none};
-  if ((st = check_alias(&mY, 1, ins, 4)) != CODA_OK) return st;
+  const Mat ins[5] = {mX, mW, msw, r ? mr : none, x_exp ? mE : none};
+  if ((st = check_alias(&mY, 1, ins, 5)) != CODA_OK) return st;
   EpiRowScaleFp8::Params ep{r, sw2, (uint16_t*)Y, ldy};
+  if (x_exp != nullptr)
+    return launch_gemm_fp8<EpiRowScaleFp8, kLayKC, true>("coda_gemm_rowscale_fp8", (int)M, (int)N2, (int)D, X8, ldx,
+                                                         W2t8, ldw2t, ep, (hipStream_t)stream, x_exp);
   return launch_gemm_fp8<EpiRowScaleFp8>("coda_gemm_rowscale_fp8", (int)M, (int)N2, (int)D, X8, ldx, W2t8, ldw2t,
                                          ep, (hipStream_t)stream);
 }
@@ -1000,51 +1015,65 @@ coda_status coda_quantize_rows_cols_e4m3_packed(int64_t M, int64_t N, const void
 coda_status coda_gemm_res_prms_fp8_packed(int64_t M, int64_t K, int64_t D, const void* A8, int64_t lda,
                                           const float* sa, const void* W1t8, int64_t ldw1t, const float* sw1,
                                           const void* R, int64_t ldr, const void* g, void* H, int64_t ldh,
-                                          void* Hg8p, float* partials, void* stream) {
+                                          void* Hg8p, void* hg_exp, float* partials, void* stream) {
   coda_status st = check_dims_fp8(M, {{"K", K}, {"D", D}});
   if (st != CODA_OK) return st;
   if (M == 0) return ok();
   const int64_t T = num_partials(D);
-  const int64_t hg_bytes = packed_bytes_e4m3(M, D);
+  const int64_t hg_bytes = packed_bytes_e4m3(M, D), eb = mx_exp_bytes(M, D);
   const Mat mA{A8, M, K, lda, 1, "A8"}, mW{W1t8, D, K, ldw1t, 1, "W1t8"}, mR{R, M, D, ldr, 2, "R"};
   const Mat mg{g, 1, D, D, 2, "g"}, mH{H, M, D, ldh, 2, "H"}, mHg{Hg8p, 1, hg_bytes, hg_bytes, 1, "Hg8"};
   const Mat mP{partials, T, M, M, 4, "partials"}, msa{sa, 1, M, M, 4, "sa"}, msw{sw1, 1, D, D, 4, "sw1"};
+  const Mat mE{hg_exp, 1, eb, eb, 1, "hg_exp"};
   for (const Mat* m : {&mA, &mW, &mHg})
     if ((st = check_mat(*m, 16)) != CODA_OK) return st;
   for (const Mat* m : {&mR, &mg, &mH})
     if ((st = check_mat(*m, 8)) != CODA_OK) return st;
+  if ((st = check_mat(mE, 4)) != CODA_OK) return st;
   if ((st = check_vec(sa, M, 4, "sa")) != CODA_OK || (st = check_vec(sw1, D, 16, "sw1")) != CODA_OK) return st;
   if (partials == nullptr) return fail(CODA_ERR_NULL, "partials is NULL");
   if (((uintptr_t)partials & 3) != 0) return fail(CODA_ERR_ALIGN, "partials is not 4-byte aligned");
   if (mP.span() > kMaxSpan) return fail(CODA_ERR_SHAPE, "partials span too large");
-  const Mat outs[3] = {mH, mHg, mP};
+  const Mat outs[4] = {mH, mHg, mP, mE};
   const Mat ins[6] = {mA, mW, mR, mg, msa, msw};
-  if ((st = check_alias(outs, 3, ins, 6)) != CODA_OK) return st;
+  if ((st = check_alias(outs, 4, ins, 6)) != CODA_OK) return st;
   EpiResPrmsFp8::Params ep{sa, sw1, (const uint16_t*)R, ldr, (const uint16_t*)g, (uint16_t*)H, ldh,
-                           (uint8_t*)Hg8p, 0, partials, D / 16};
+                           (uint8_t*)Hg8p, 0, partials, D / 16, (uint8_t*)hg_exp};
   return launch_gemm_fp8<EpiResPrmsFp8>("coda_gemm_res_prms_fp8_packed", (int)M, (int)D, (int)K, A8, lda, W1t8,
                                         ldw1t, ep, (hipStream_t)stream);
 }
 
-coda_status coda_gemm_rowscale_fp8_packed(int64_t M, int64_t D, int64_t N2, const void* X8p, const void* W2t8p,
-                                          const float* sw2, const float* r, void* Y, int64_t ldy, void* stream) {
+coda_status coda_gemm_rowscale_fp8_packed(int64_t M, int64_t D, int64_t N2, const void* X8p, const void* x_exp,
+                                          const void* W2t8p, const float* sw2, const float* r, void* Y, int64_t ldy,
+                                          void* stream) {
   coda_status st = check_dims_fp8(M, {{"D", D}, {"N2", N2}});
   if (st != CODA_OK) return st;
   if (M == 0) return ok();
-  const int64_t x_bytes = packed_bytes_e4m3(M, D), w_bytes = packed_bytes_e4m3(N2, D);
+  const int64_t x_bytes = packed_bytes_e4m3(M, D), w_bytes = packed_bytes_e4m3(N2, D), eb = mx_exp_bytes(M, D);
   const Mat mX{X8p, 1, x_bytes, x_bytes, 1, "X8"}, mW{W2t8p, 1, w_bytes, w_bytes, 1, "W2t8"};
   const Mat mY{Y, M, N2, ldy, 2, "Y"}, mr{r, 1, M, M, 4, "r"}, msw{sw2, 1, N2, N2, 4, "sw2"};
+  const Mat mE{x_exp, 1, eb, eb, 1, "x_exp"};
   for (const Mat* m : {&mX, &mW})
     if ((st = check_mat(*m, 16)) != CODA_OK) return st;
   if ((st = check_mat(mY, 8)) != CODA_OK) return st;
+  if (x_exp != nullptr && (st = check_mat(mE, 4)) != CODA_OK) return st;
   if ((st = check_vec(sw2, N2, 16, "sw2")) != CODA_OK) return st;
   if (r != nullptr && ((uintptr_t)r & 3) != 0) return fail(CODA_ERR_ALIGN, "r is not 4-byte aligned");
   const Mat none{nullptr, 0, 0, 0, 4, ""};
-  const Mat ins[4] = {mX, mW, msw, r ? mr : none};
-  if ((st = check_alias(&mY, 1, ins, 4)) != CODA_OK) return st;
+  const Mat ins[5] = {mX, mW, msw, r ? mr : none, x_exp ? mE : none};
+  if ((st = check_alias(&mY, 1, ins, 5)) != CODA_OK) return st;
   EpiRowScaleFp8::Params ep{r, sw2, (uint16_t*)Y, ldy};
+  if (x_exp != nullptr)
+    return launch_gemm_fp8<EpiRowScaleFp8, kLayPacked, true>("coda_gemm_rowscale_fp8_packed", (int)M, (int)N2,
+                                                             (int)D, X8p, D / 16, W2t8p, D / 16, ep,
+                                                             (hipStream_t)stream, x_exp);
   return launch_gemm_fp8<EpiRowScaleFp8, kLayPacked>("coda_gemm_rowscale_fp8_packed", (int)M, (int)N2, (int)D, X8p,
-                                               D / 16, W2t8p, D / 16, ep, (hipStream_t)stream);
+                                                     D / 16, W2t8p, D / 16, ep, (hipStream_t)stream);
+}
+
+int64_t coda_mx_exp_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || rows > kMaxDim || cols < 1 || cols > kMaxDim) return -1;
+  return mx_exp_bytes(rows, cols);
 }
 
 coda_status coda_gemm_rowscale_lse(coda_dtype dt, int64_t M, int64_t D, int64_t V, const void* X, int64_t ldx,

@@ -26,6 +26,19 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
   return (uint32_t)w;
 }
 
+// Block exponent of the OCP microscaling formats for a block whose largest
+// magnitude is amax: the smallest integer E with amax <= 448 * 2^E, so that
+// amax * 2^-E fits e4m3 without saturating, clamped to the E8M0 range
+// [-127, 127]; 0 for an all-zero block.  With amax = m 2^e, m in [0.5, 1),
+// and 448 = 0.875 * 2^9: E = e - 9, or e - 8 when m > 0.875.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int e;
+  const float m = frexpf(amax, &e);
+  const int E = e - 9 + (m > 0.875f ? 1 : 0);
+  return E < -127 ? -127 : (E > 127 ? 127 : E);
+}
+
 // Column scales of a lane's 8 columns.
 __device__ __forceinline__ void load_col_scales(const float* sw, int col, int N, float out[8]) {
 #pragma unroll
@@ -42,8 +55,18 @@ __device__ __forceinline__ void load_col_scales(const float* sw, int col, int N,
 
 // First GEMM, fp8 operands:
 //   H   = round_bf16((acc * sa_i) * sw_j + R_ij)                 bf16 [M, D]
-//   Hg8 = e4m3(clamp(float(H_ij) * g_j, +-448))                  e4m3 [M, D]
+//   x   = float(H_ij) * g_j                                      float32
+//   E_ib = mx_exponent(max |x| over block b = columns [32b, 32b + 32) of row i)
+//   Hg8 = e4m3(x * 2^-E_ib)                                      e4m3 [M, D]
+//   hg_exp[mx_byte(i, b / 2, b % 2, M)] = E_ib + 127            E8M0 bytes
 //   partials[t][row] = sum over partial tile t of float(H)^2    (as in EpiResPrms)
+// A block's 32 columns are 4 lanes of a row group (lanes l with equal l / 4),
+// so the block maximum is two lane exchanges (a tile reduction of the CODA
+// news article's building blocks).  apply() keeps x; end_slab(), which
+// every lane runs, takes the block maxima and writes codes and exponents.
+// Every byte of the exponent array is written: its groups of 4 k-tiles
+// cover exactly the 256-column tiles, and a block past D (all x = 0) gets
+// exponent 0.  The second GEMM reads whole groups of them.
 struct EpiResPrmsFp8 {
   struct Params {
     const float* sa;    // [M]
@@ -57,42 +80,43 @@ struct EpiResPrmsFp8 {
     int64_t ldhg;
     float* partials;    // [T][M]
     int64_t hg_nck;     // > 0: Hg8 is tile-packed (kp_unit) with hg_nck 16-byte chunks per row
+    uint8_t* hg_exp;    // block exponents (mx_byte layout), 8 M ceil(D / 256) bytes
   };
   Params p;
   RowChunks<uint16_t> rc;
   RowScalars sa;
   float sw[8], gv[8];
   float ss[2];
-  int lane, t, M;
+  float xg[2][8];  // x of the lane's two rows of the current slab (0 where not applied)
+  int lane, t, M, N, col;
 
   __device__ __forceinline__ EpiResPrmsFp8(const Params& p_, int lane_, int wm, int wn, int m0, int n0, int tn,
-                                           int M_, int N)
-      : p(p_), lane(lane_), t(4 * tn + wn), M(M_) {
-    const int col = n0 + wn * kWaveN + (lane & 7) * 8;
-    rc.prefetch(p.R, p.ldr, m0 + wm * kWaveM, col, lane, M_, N);
+                                           int M_, int N_)
+      : p(p_), lane(lane_), t(4 * tn + wn), M(M_), N(N_) {
+    col = n0 + wn * kWaveN + (lane & 7) * 8;
+    rc.prefetch(p.R, p.ldr, m0 + wm * kWaveM, col, lane, M_, N_);
     sa.prefetch(p.sa, m0 + wm * kWaveM, lane, M_);
-    load_col_scales(p.sw, col, N, sw);
+    load_col_scales(p.sw, col, N_, sw);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) gv[i] = 0.f;
-    if (col < N) Chunk8<uint16_t>::load(p.g + col, gv);
+    for (int i = 0; i < 8; ++i) {
+      gv[i] = 0.f;
+      xg[0][i] = xg[1][i] = 0.f;
+    }
+    if (col < N_) Chunk8<uint16_t>::load(p.g + col, gv);
     ss[0] = ss[1] = 0.f;
   }
 
-  __device__ __forceinline__ void apply(int mt, int q, int row, int col, float v[8]) {
+  __device__ __forceinline__ void apply(int mt, int q, int row, int col_, float v[8]) {
     float rv[8], h[8];
-    rc.get(p.R, p.ldr, mt, q, row, col, rv);
+    rc.get(p.R, p.ldr, mt, q, row, col_, rv);
     const float s = sa.v[mt][q];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       h[i] = Chunk8<uint16_t>::round((v[i] * s) * sw[i] + rv[i]);
       ss[q] += h[i] * h[i];
+      xg[q][i] = h[i] * gv[i];
     }
-    Chunk8<uint16_t>::store(p.H + (int64_t)row * p.ldh + col, h);
-    const uint32_t lo = pack_e4m3x4(h[0] * gv[0], h[1] * gv[1], h[2] * gv[2], h[3] * gv[3]);
-    const uint32_t hi = pack_e4m3x4(h[4] * gv[4], h[5] * gv[5], h[6] * gv[6], h[7] * gv[7]);
-    uint8_t* dst = p.hg_nck > 0 ? p.Hg8 + kp_unit(row, col >> 4, p.hg_nck) * 16 + (col & 15)
-                                : p.Hg8 + (int64_t)row * p.ldhg + col;
-    *(u32x2*)dst = u32x2{lo, hi};
+    Chunk8<uint16_t>::store(p.H + (int64_t)row * p.ldh + col_, h);
   }
 
   __device__ __forceinline__ void end_slab(int, int slab_row0) {
@@ -105,6 +129,26 @@ struct EpiResPrmsFp8 {
       const int row = slab_row0 + (lane >> 3) + 8 * q;
       if ((lane & 7) == 0 && row < M) p.partials[(int64_t)t * M + row] = s;
       ss[q] = 0.f;
+      // the block of 32 columns: its maximum over the 4 lanes holding it
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(xg[q][i]));
+      a = fmaxf(a, __shfl_xor(a, 1));
+      a = fmaxf(a, __shfl_xor(a, 2));
+      const int E = mx_exponent(a);
+      if (row < M && col < N) {
+        const uint32_t lo = pack_e4m3x4(ldexpf(xg[q][0], -E), ldexpf(xg[q][1], -E), ldexpf(xg[q][2], -E),
+                                        ldexpf(xg[q][3], -E));
+        const uint32_t hi = pack_e4m3x4(ldexpf(xg[q][4], -E), ldexpf(xg[q][5], -E), ldexpf(xg[q][6], -E),
+                                        ldexpf(xg[q][7], -E));
+        uint8_t* dst = p.hg_nck > 0 ? p.Hg8 + kp_unit(row, col >> 4, p.hg_nck) * 16 + (col & 15)
+                                    : p.Hg8 + (int64_t)row * p.ldhg + col;
+        *(u32x2*)dst = u32x2{lo, hi};
+      }
+      if ((lane & 3) == 0 && row < M)
+        p.hg_exp[mx_byte(row, col >> 6, (col >> 5) & 1, M)] = (uint8_t)(E + 127);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xg[q][i] = 0.f;
     }
   }
   __device__ __forceinline__ void finish() {}

@@ -280,6 +280,15 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
+// The same with N loads of the wavefront allowed in flight (the k-tile's
+// direct loads issued last, plus N - kLoadsPerTile loads issued after them).
+template <int N>
+__device__ __forceinline__ void stage_barrier_n() {
+  static_assert(N >= kLoadsPerTile && N < 64, "vmcnt holds 0..63");
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 __device__ __forceinline__ void drain_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");

@@ -25,20 +25,22 @@ struct Elem<uint8_t> {  // OCP e4m3, stored as its 8-bit code
   static constexpr int E = 16;
 };
 
-// 32-row fragment t of a contraction-contiguous operand tile; PK: the tile
-// is in the packed LDS order (kp_offset in tile_map.hpp).
+// 32-row fragment t of a contraction-contiguous operand tile (chunks g and
+// 2 + g of the lane's row, kc8_offset); PK: the tile is in the packed LDS
+// order (kp_offset in tile_map.hpp).
 template <bool PK = false>
 struct FragReader8 {
   int off0;  // lane's byte offset of fragment 0, first chunk
   __device__ __forceinline__ FragReader8(int base, int lane)
-      : off0(PK ? kp_offset(base + (lane & 31), 2 * (lane >> 5)) : kc8_offset(base, 0, 0, lane)) {}
+      : off0(PK ? kp_offset(base + (lane & 31), lane >> 5) : kc8_offset(base, 0, 0, lane)) {}
   __device__ __forceinline__ void refresh() { opaque(off0); }
   __device__ __forceinline__ i32x8 read(const char* tile, int t) const {
-    // KC: second chunk = the first XOR 16 bytes (the swizzle only moves whole
-    // chunk pairs); packed: the next chunk of the row block, 256 bytes on.
-    // Fragment t lies 32 rows (2 KiB) further in both layouts.
+    // KC: the second chunk (chunk index + 2) is the first XOR 32 bytes (the
+    // swizzle XORs the chunk index); packed: two chunks of the row block
+    // further, 512 bytes on.  Fragment t lies 32 rows (2 KiB) further in
+    // both layouts.
     const u32x4 lo = *(const u32x4*)(tile + off0 + 2048 * t);
-    const u32x4 hi = *(const u32x4*)(tile + (PK ? off0 + 256 : (off0 ^ 16)) + 2048 * t);
+    const u32x4 hi = *(const u32x4*)(tile + (PK ? off0 + 512 : (off0 ^ 32)) + 2048 * t);
     return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   }
 };
@@ -47,6 +49,54 @@ __device__ __forceinline__ void mac8(f32x16& acc, const i32x8& a, const i32x8& b
   // formats 0, 0: both operands e4m3; zero scale selectors: unscaled
   acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
 }
+
+// The same product with a block scale on A: contraction block h of row i
+// (k-tile bytes [32 h, 32 h + 32), the half-h registers of lanes i and
+// 32 + i) is multiplied by 2^(b - 127), b the byte SEL of lane 32 h + i's
+// sc (an E8M0 exponent); B is unscaled (127 = 2^0).
+template <int SEL>
+__device__ __forceinline__ void mac8_mx(f32x16& acc, const i32x8& a, const i32x8& b, uint32_t sc) {
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, SEL, (int)sc, 0, 127);
+}
+
+// Block exponents of an A operand (E8M0 bytes in the mx_byte layout of
+// tile_map.hpp, as the first GEMM's fp8 epilogue writes them): one dword per
+// (row, half) and group of 4 k-tiles.  Lane l supplies, per A fragment mt,
+// the scales of row base + 32 mt + l % 32 for block l / 32, so it reads the
+// dword of that row and half: 256 contiguous bytes per fragment and group.
+// Rows past M read 0 through the buffer descriptor's range check.
+struct MxArgs {
+  const uint8_t* e;  // null: the operand is unscaled
+  int64_t M;         // rows of the array (the GEMM's M)
+  uint32_t span;     // bytes of the array
+};
+
+struct MxReader {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t off[kFrag8M];  // byte offset of group 0, or kOutOfRange
+  uint32_t gstep;         // bytes between groups
+  __device__ __forceinline__ void init(const MxArgs& mx, int row0, int M, int lane) {
+    rsrc = make_rsrc(mx.e, mx.span);
+    gstep = (uint32_t)(8 * mx.M);
+#pragma unroll
+    for (int mt = 0; mt < kFrag8M; ++mt) {
+      const int row = row0 + 32 * mt + (lane & 31);
+      off[mt] = row < M ? (uint32_t)mx_byte(row, 0, lane >> 5, mx.M) : kOutOfRange;
+    }
+  }
+  // group grp's dwords; a group past the last one reads 0 (past the array)
+  __device__ __forceinline__ void load(int grp, uint32_t (&out)[kFrag8M]) const {
+#pragma unroll
+    for (int mt = 0; mt < kFrag8M; ++mt)
+      out[mt] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)(off[mt] + gstep * (uint32_t)grp), 0, 0);
+  }
+};
+
+// Block exponents held across a group of 4 k-tiles: cur for the group being
+// multiplied, nxt for the next one, loaded during the group's first step.
+struct MxRegs {
+  uint32_t cur[kFrag8M], nxt[kFrag8M];
+};
 
 constexpr int kDmaIssueAfter8 = 1;
 
@@ -59,13 +109,26 @@ struct Frags8 {
 // its reload for tile kt + 1; the loads of tile kt + kStages - 1 go out
 // after the products of A fragment kDmaIssueAfter8 (4 products, 256
 // matrix-core cycles, as in the bf16 step).
-template <int S, int L = kLayKC>
+//
+// MX (A block-scaled): k-tile kt uses byte kt % 4 = S of the group's
+// exponent dwords.  The first step of a group moves the prefetched dwords
+// into use and, behind the direct loads, loads the next group's (NEXT: the
+// steps after the main loop belong to the last group and load none); its
+// barrier then allows those kFrag8M loads in flight as well (they have a
+// whole group of steps to land).
+template <int S, int L = kLayKC, bool MX = false, bool NEXT = true>
 __device__ __forceinline__ void kstep8(char* const (&st)[kStages], const Dma<uint8_t, true, L>& da,
                                        const Dma<uint8_t, true, L>& db, FragReader8<lds_packed(L)>& ra,
                                        FragReader8<lds_packed(L)>& rb,
-                                       f32x16 (&acc)[kFrag8M][kFrag8N], Frags8& cur, int kt, int K, int wave) {
+                                       f32x16 (&acc)[kFrag8M][kFrag8N], Frags8& cur, int kt, int K, int wave,
+                                       const MxReader& mr, MxRegs& ms) {
   constexpr int SL = (S + kStages - 1) % kStages;
   constexpr int SN = (S + 1) % kStages;
+  static_assert(!MX || kStages == 4, "a group of exponent bytes is one pass over the four stages");
+  if constexpr (MX && S == 0) {
+#pragma unroll
+    for (int mt = 0; mt < kFrag8M; ++mt) ms.cur[mt] = ms.nxt[mt];
+  }
   ra.refresh();
   rb.refresh();
   i32x8 nb[kFrag8N];
@@ -75,17 +138,26 @@ __device__ __forceinline__ void kstep8(char* const (&st)[kStages], const Dma<uin
 #pragma unroll
   for (int mt = 0; mt < kFrag8M; ++mt) {
 #pragma unroll
-    for (int nt = 0; nt < kFrag8N; ++nt) mac8(acc[mt][nt], cur.a[mt], cur.b[nt]);
+    for (int nt = 0; nt < kFrag8N; ++nt) {
+      if constexpr (MX)
+        mac8_mx<S>(acc[mt][nt], cur.a[mt], cur.b[nt], ms.cur[mt]);
+      else
+        mac8(acc[mt][nt], cur.a[mt], cur.b[nt]);
+    }
     cur.a[mt] = ra.read(st[SN], mt);
     if (mt == kDmaIssueAfter8) {
       da.issue(st[SL], kt + kStages - 1, K, wave);
       db.issue(st[SL] + kOperandBytes, kt + kStages - 1, K, wave);
+      if constexpr (MX && S == 0 && NEXT) mr.load(kt / 4 + 1, ms.nxt);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int nt = 0; nt < kFrag8N; ++nt) cur.b[nt] = nb[nt];
-  stage_barrier();
+  if constexpr (MX && S == 0 && NEXT)
+    stage_barrier_n<kLoadsPerTile + kFrag8M>();
+  else
+    stage_barrier();
 }
 
 // C = A B^T for fp8 A[M, K] (g.a, g.lda) and B[N, K] (g.b, g.ldb); the
@@ -93,9 +165,11 @@ __device__ __forceinline__ void kstep8(char* const (&st)[kStages], const Dma<uin
 // finish).
 // L: OpLayout of both operands (kLayPacked: tile-packed, kp_unit, with g.lda /
 // g.ldb counting 16-byte chunks per row).
-template <class Epi, int L = kLayKC>
+// MX: A carries block exponents (mx, MxReader's layout) that the products
+// apply; otherwise mx is unused.
+template <class Epi, int L = kLayKC, bool MX = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_fp8_kernel(
-    GemmArgs g, typename Epi::Params ep) {
+    GemmArgs g, typename Epi::Params ep, MxArgs mx) {
   static_assert(kStages == 4, "the stage arrays and the unrolled steps below assume four stages");
   __shared__ __attribute__((aligned(1024))) char st0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char st1[kStageBytes];
@@ -123,6 +197,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int nk = (g.K + KTE - 1) / KTE;
+  MxReader mr;
+  MxRegs ms;
+  if constexpr (MX) {
+    mr.init(mx, m0 + wm * kWaveM, g.M, lane);
+    mr.load(0, ms.nxt);  // landed by the prologue's wait below
+  }
 #pragma unroll
   for (int t = 0; t < kStages - 1; ++t) {
     da.issue(st[t], t, g.K, wave);
@@ -137,15 +217,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int nt = 0; nt < kFrag8N; ++nt) cur.b[nt] = rb.read(st[0] + kOperandBytes, nt);
   int kt = 0;
   for (; kt + kStages <= nk; kt += kStages) {
-    kstep8<0, L>(st, da, db, ra, rb, acc, cur, kt, g.K, wave);
-    kstep8<1, L>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave);
-    kstep8<2, L>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave);
-    kstep8<3, L>(st, da, db, ra, rb, acc, cur, kt + 3, g.K, wave);
+    kstep8<0, L, MX>(st, da, db, ra, rb, acc, cur, kt, g.K, wave, mr, ms);
+    kstep8<1, L, MX>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave, mr, ms);
+    kstep8<2, L, MX>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave, mr, ms);
+    kstep8<3, L, MX>(st, da, db, ra, rb, acc, cur, kt + 3, g.K, wave, mr, ms);
   }
   const int rem = nk - kt;
-  if (rem > 0) kstep8<0, L>(st, da, db, ra, rb, acc, cur, kt, g.K, wave);
-  if (rem > 1) kstep8<1, L>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave);
-  if (rem > 2) kstep8<2, L>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave);
+  if (rem > 0) kstep8<0, L, MX, false>(st, da, db, ra, rb, acc, cur, kt, g.K, wave, mr, ms);
+  if (rem > 1) kstep8<1, L, MX, false>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave, mr, ms);
+  if (rem > 2) kstep8<2, L, MX, false>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave, mr, ms);
   drain_barrier();  // no direct load may land in the LDS the epilogue reuses
 
   // ---- epilogue: slab s = rows 16 s .. 16 s + 15 of the wavefront's 128 =

@@ -165,14 +165,29 @@ constexpr int kSwiGLUPartner = kSwiGLURun / 8;
 // One k-tile is 64 bytes = 64 fp8 elements per operand row, so both operands
 // use the contraction-contiguous layout above unchanged.  A wavefront's
 // 128 x 64 sub-tile is 4 x 2 products of 32 x 32.  Lane l = 32 g + i of a
-// 32-row fragment t supplies operand row base + 32 t + i and contraction
-// bytes [32 g, 32 g + 32) of the k-tile: chunks 2 g and 2 g + 1, read with
-// two 16-byte reads.  The same (lane, byte) -> k assignment on both operands
-// makes the product independent of how the hardware orders k.
+// 32-row fragment t supplies operand row base + 32 t + i and two 16-byte
+// chunks of the k-tile: chunk g in its first four registers (half 0) and
+// chunk 2 + g in its last four (half 1).  The matrix core takes the first
+// registers of both lane halves as contraction block 0 and the last as block
+// 1, with block 0's scale from lane i and block 1's from lane 32 + i (a GPU
+// probe with a different exponent per block showed this), so the k-tile's
+// bytes [0, 32) and [32, 64) are exactly its two scale blocks, as the
+// microscaling formats need.  Unscaled products only need the same
+// (lane, byte) -> k assignment on both operands.
 constexpr int kFrag8M = kWaveM / 32;  // 4 fragments of 32 A rows
 constexpr int kFrag8N = kWaveN / 32;  // 2 fragments of 32 B rows
 CODA_HD int kc8_offset(int base, int t, int half, int lane) {
-  return kc_offset(base + 32 * t + (lane & 31), 2 * (lane >> 5) + half);
+  return kc_offset(base + 32 * t + (lane & 31), (lane >> 5) + 2 * half);
+}
+// MX block exponents (one E8M0 byte per row and 32 contraction columns):
+// row i's exponent for half h of k-tile t lies at byte mx_byte(i, t, h, M)
+// of an array for M rows: groups of 4 k-tiles outermost, then the rows, the
+// two halves, and the k-tile within its group.  A group's dword of one
+// (row, half) then holds 4 consecutive k-tiles, and the dwords a 32-row
+// fragment's 64 lanes read for a group (row i + lane % 32, half lane / 32)
+// are 256 contiguous bytes.  The array spans 8 M ceil(cols / 256) bytes.
+CODA_HD int64_t mx_byte(int64_t i, int t, int h, int64_t M) {
+  return (((int64_t)(t >> 2) * M + i) * 2 + h) * 4 + (t & 3);
 }
 // Accumulator element e (0..15) of lane l in a 32 x 32 product is output
 // row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32 (established by a GPU
