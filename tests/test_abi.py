@@ -739,3 +739,28 @@ def test_lse_ce_rope_packed_validation(lib):
     assert rope(cs=None) == NULL
     assert rope(Xp=HG_ + 8) == ALIGN
     assert rope(Y=HG_ + 512) == ALIAS
+
+
+@pytest.mark.parametrize("dim", ["K", "D", "N2"])
+@pytest.mark.parametrize("dt", [BF16, F32])
+def test_sizes_narrowed_to_multiples_of_8(lib, dim, dt):
+    # The boundary takes K, D and N2 in multiples of 8 only (the kernels move
+    # 16-byte pieces of 8 bf16 along every one of them, the fp32 path keeps
+    # the same rule); any other size is refused with CODA_ERR_SHAPE before
+    # anything is enqueued, by the forward pair, the reference chain and the
+    # backward alike, and the message names the size.
+    base = dict(M=512, K=256, D=256, N2=512)
+    bad = dict(base, **{dim: base[dim] + 4})
+    calls = []
+    if dim in ("K", "D"):
+        calls.append(lambda: prms(lib, dt=dt, M=bad["M"], K=bad["K"], D=bad["D"], lda=bad["K"] + 4,
+                                  ldw1=bad["D"] + 4, ldr=bad["D"] + 4, ldh=bad["D"] + 4, ldhg=bad["D"] + 4))
+    if dim in ("D", "N2"):
+        calls.append(lambda: rowscale(lib, dt=dt, M=bad["M"], D=bad["D"], N2=bad["N2"], ldx=bad["D"] + 4,
+                                      ldw2=bad["N2"] + 4, ldy=bad["N2"] + 4))
+    calls.append(lambda: chain_bwd(lib, dt=dt, ws_bytes=1 << 40, **bad))
+    for call in calls:
+        assert call() == SHAPE
+        assert f"{dim} = {bad[dim]} is not a multiple of 8" in lib.coda_last_error().decode()
+    # the same call at the multiple of 8 just below gets past the size check
+    assert chain_bwd(lib, dt=dt, ws=None, **dict(base, **{dim: base[dim] - 8})) == WS
