@@ -313,10 +313,8 @@ struct GemmArgs {
 };
 
 // A fragment index after whose products a k-step issues its direct loads
-// (see kstep).  With both operands row-contiguous (the weight-gradient
-// products) the loads go out first (-1): any later point spills registers.
+// (see kstep), for every operand layout.
 constexpr int kDmaIssueAfter = 3;
-constexpr int kDmaIssueAfterRR = -1;
 
 // Fragments of one k-tile held in registers.
 struct Frags {
@@ -329,8 +327,7 @@ struct Frags {
 //   for each A fragment mt: run its 4 products of tile kt, then read tile
 //   kt + 1's fragment mt into the same registers, so each read has about a
 //   whole step to land before its products in the next step;
-//   after the products of A fragment kDmaIssueAfter (at the start of the
-//   step for the weight-gradient products), issue the direct loads of tile
+//   after the products of A fragment kDmaIssueAfter, issue the direct loads of tile
 //   kt + kStages - 1 into stage (S - 1) mod kStages, which held tile kt - 1
 //   (read in step kt - 2, used before the barrier of step kt - 1);
 //   stage_barrier: at most tile kt + 3 is still in flight, so tile kt + 2,
@@ -346,6 +343,9 @@ struct Frags {
 // the addressing overlaps them; measured at the 7B second-GEMM shape under
 // the power cap, 1.7-2.4% faster than issuing first (after 1 fragment: 1.2%,
 // after 4-7: 0.3-0.8%; the A and B loads split over two points: 0.6-1.7%).
+// The weight-gradient products (both operands row-contiguous) gain more: the
+// 7B backward is 4.3% faster with their loads after fragment 3 than first
+// (after 2: 3.9%, 4: 2.8%, 5: 2.3%).
 template <typename T, bool A_KC, bool B_KC, int S, int A_L = kLayKC, int B_L = kLayKC>
 __device__ __forceinline__ void kstep(char* const (&st)[kStages], const Dma<T, A_KC, A_L>& da,
                                       const Dma<T, B_KC, B_L>& db, FragReader<T, A_KC, lds_packed(A_L)>& ra,
@@ -353,11 +353,7 @@ __device__ __forceinline__ void kstep(char* const (&st)[kStages], const Dma<T, A
                                       f32x4 (&acc)[kFragM][kFragN], Frags& cur, int kt, int K, int wave) {
   constexpr int SL = (S + kStages - 1) % kStages;
   constexpr int SN = (S + 1) % kStages;
-  constexpr int issue_at = A_KC || B_KC ? kDmaIssueAfter : kDmaIssueAfterRR;
-  if constexpr (issue_at < 0) {
-    da.issue(st[SL], kt + kStages - 1, K, wave);
-    db.issue(st[SL] + kOperandBytes, kt + kStages - 1, K, wave);
-  }
+  constexpr int issue_at = kDmaIssueAfter;
   ra.refresh();
   rb.refresh();
   u32x4 nb[kFragN];
