@@ -354,7 +354,8 @@ int64_t coda_mx_exp_bytes(int64_t rows, int64_t cols);
  *   A8: e4m3 [M,K] (lda); sa: float[M]; W1t8: e4m3 [D,K] (ldw1t); sw1: float[D],
  *   16-byte aligned; R, g, H: bf16; Hg8: e4m3 [M,D] (ldhg); hg_exp as above.
  *   The block maximum is taken inside the epilogue (the 32 columns of a
- *   block sit in 4 lanes of one row). */
+ *   block sit in 4 lanes of one row).  x must be finite: a NaN is left out
+ *   of its block's maximum and coded as -448, an infinity as +-448. */
 coda_status coda_gemm_res_prms_fp8(int64_t M, int64_t K, int64_t D,
                                    const void* A8, int64_t lda, const float* sa,
                                    const void* W1t8, int64_t ldw1t, const float* sw1,
