@@ -334,15 +334,17 @@ coda_status coda_gemm_rowscale_ce_bwd_packed(int64_t M, int64_t D, int64_t V,
  * elements, bf16 ones multiples of 8.
  *
  * Block-exponent arrays (hg_exp, x_exp): coda_mx_exp_bytes(M, D) bytes,
- * 16-byte aligned; byte ((t / 4 * M + i) * 2 + h) * 4 + t % 4 is E + 127 (an
- * E8M0 code) for row i and columns [64 t + 32 h, 64 t + 32 h + 32) of D
- * (groups of 4 k-tiles of 64 columns outermost, so that the second GEMM's
- * reads of one group for 32 rows are 256 contiguous bytes).  The first GEMM
- * writes every byte, 127 (E = 0) for the blocks past D; the second GEMM
+ * 16-byte aligned.  E + 127 (an E8M0 code) for row i and columns
+ * [64 t + 32 h, 64 t + 32 h + 32) of D lies at byte
+ *   ((t/4 * ceil(M/128) + i/128) * 64 + 32 h + i%32) * 16 + ((i/32)%4) * 4 + t%4
+ * (groups of 4 k-tiles of 64 columns, then blocks of 128 rows: each lane of
+ * the second GEMM finds the 4 exponents it needs per k-tile group in 16
+ * consecutive bytes).  The first GEMM writes every byte, 127 (E = 0) for
+ * the blocks past D and the rows past M in the last block; the second GEMM
  * reads the bytes of t < ceil(D / 64) only. */
 
 /* Bytes of the block-exponent array of a [rows, cols] MX operand:
- * 8 * rows * ceil(cols / 256).  -1 for bad arguments. */
+ * 1024 * ceil(rows / 128) * ceil(cols / 256).  -1 for bad arguments. */
 int64_t coda_mx_exp_bytes(int64_t rows, int64_t cols);
 
 /* First GEMM, fp8 operands:

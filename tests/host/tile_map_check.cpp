@@ -341,29 +341,39 @@ static void check_epilogue_slab() {
 // (row, half) holds its 4 k-tiles in order; the dwords the 64 lanes of a
 // 32-row fragment read for one group are 256 contiguous bytes.
 static void check_mx_byte() {
-  for (int M : {1, 3, 32, 37, 300})
+  for (int M : {1, 3, 32, 37, 128, 300})
     for (int G : {1, 2, 5}) {
-      std::vector<int> hit(8 * M * G, 0);
-      for (int i = 0; i < M; ++i)
+      const int64_t RB = mx_row_blocks(M), bytes = 1024 * RB * G;
+      CHECK(RB == (M + 127) / 128, "mx_row_blocks");
+      std::vector<int> hit(bytes, 0);
+      // every (row up to M rounded up to 128, k-tile, half) owns one byte
+      for (int i = 0; i < 128 * RB; ++i)
         for (int t = 0; t < 4 * G; ++t)
           for (int h = 0; h < 2; ++h) {
             const int64_t o = mx_byte(i, t, h, M);
-            CHECK(o >= 0 && o < 8 * M * G, "mx_byte outside the array");
-            if (o >= 0 && o < 8 * M * G) hit[o]++;
-            CHECK(o == mx_byte(i, t & ~3, h, M) + (t & 3), "mx_byte: k-tiles of a group not consecutive");
-            CHECK(mx_byte(i, t & ~3, h, M) % 4 == 0, "mx_byte: group dword misaligned");
+            CHECK(o >= 0 && o < bytes, "mx_byte outside the array");
+            if (o >= 0 && o < bytes) hit[o]++;
           }
       for (int v : hit) CHECK(v == 1, "mx_byte: a byte used twice or never");
-      for (int base = 0; base + 32 <= M; base += 32)
+      // a wave's read of group g for its 128 rows: lane l takes the 16 bytes
+      // at mx_byte(row0 + l % 32, 4g, l / 32); dword f of them holds the 4
+      // k-tiles of fragment f's row row0 + 32f + l % 32, and the 64 lanes'
+      // reads tile 1 KiB
+      for (int row0 = 0; row0 < 128 * RB; row0 += 128)
         for (int g = 0; g < G; ++g) {
           std::vector<int> w(64, 0);
-          const int64_t lo = mx_byte(base, 4 * g, 0, M);
+          const int64_t lo = mx_byte(row0, 4 * g, 0, M);
+          CHECK(lo % 1024 == 0, "mx_byte: wave read not 1 KiB aligned");
           for (int lane = 0; lane < 64; ++lane) {
-            const int64_t o = mx_byte(base + (lane & 31), 4 * g, lane >> 5, M) - lo;
-            CHECK(o >= 0 && o < 256 && o % 4 == 0, "mx_byte: fragment group read not in 256 contiguous bytes");
-            if (o >= 0 && o < 256) w[o / 4]++;
+            const int64_t off = mx_byte(row0 + (lane & 31), 4 * g, lane >> 5, M);
+            CHECK(off % 16 == 0 && off - lo >= 0 && off - lo < 1024, "mx_byte: lane read misplaced");
+            if (off - lo >= 0 && off - lo < 1024) w[(off - lo) / 16]++;
+            for (int f = 0; f < 4; ++f)
+              for (int tt = 0; tt < 4; ++tt)
+                CHECK(mx_byte(row0 + 32 * f + (lane & 31), 4 * g + tt, lane >> 5, M) == off + 4 * f + tt,
+                      "mx_byte: lane's 16 bytes not its fragments' k-tiles");
           }
-          for (int v : w) CHECK(v == 1, "mx_byte: fragment group read does not cover its 256 bytes");
+          for (int v : w) CHECK(v == 1, "mx_byte: wave read does not cover its 1 KiB");
         }
     }
 }

@@ -437,10 +437,12 @@ def test_gemm_rowscale_fp8_rejects(lib, kw, status):
 
 
 def test_mx_exp_bytes(lib):
-    # 8 bytes per row and group of 4 k-tiles (2 halves x 4 k-tiles)
-    assert lib.coda_mx_exp_bytes(300, 512) == 300 * 2 * 8
-    assert lib.coda_mx_exp_bytes(3, 272) == 3 * 2 * 8
-    assert lib.coda_mx_exp_bytes(1, 16) == 8
+    # 1 KiB per 128-row block and group of 4 k-tiles (256 columns)
+    assert lib.coda_mx_exp_bytes(300, 512) == 1024 * 3 * 2
+    assert lib.coda_mx_exp_bytes(3, 272) == 1024 * 1 * 2
+    assert lib.coda_mx_exp_bytes(128, 256) == 1024
+    assert lib.coda_mx_exp_bytes(129, 256) == 2048
+    assert lib.coda_mx_exp_bytes(1, 16) == 1024
     assert lib.coda_mx_exp_bytes(0, 4096) == 0
     assert lib.coda_mx_exp_bytes(-1, 16) == -1
     assert lib.coda_mx_exp_bytes(4, 0) == -1

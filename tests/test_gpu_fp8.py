@@ -52,31 +52,40 @@ def _run(wl, seed):
     return x, d, {"H": H, "Hg8": Hg8, "E": E, "r": r, "Y": Y, "P": P}
 
 
-def _blk(Eb, b):
-    """The bytes [rows] of block b (32 columns) in an exponent array
-    [G, rows, 2, 4]: half b % 2 of k-tile t = b // 2, at [t // 4, :, h, t % 4]."""
-    t = b // 2
-    return Eb[t // 4, :, b % 2, t % 4]
+def _pos(M, b):
+    """Index tuples into an exponent array [G, B, 2, 32, 4, 4] of rows 0..M-1,
+    block b (32 columns): half b % 2 of k-tile t = b // 2."""
+    t, i = b // 2, np.arange(M)
+    return (t // 4, i // 128, b % 2, i % 32, (i // 32) % 4, t % 4)
 
 
-def _block_exponents(Eb, D):
-    """int exponents [rows, ceil(D/32)] from the byte array."""
-    return np.stack([_blk(Eb, b) for b in range(-(-D // 32))], axis=1).astype(np.int64) - 127
+def _all_exponents(Eb, M):
+    """int exponents [M, 8 G] of every block a row's bytes describe (the
+    blocks past D included)."""
+    return np.stack([Eb[_pos(M, b)] for b in range(8 * Eb.shape[0])], axis=1).astype(np.int64) - 127
 
 
-def _check_codes(H, g32, codes, Eb, orc=None):
-    """Hg8 codes and exponents against host arithmetic on the GPU's own H,
-    then (orc given) against the oracle's; returns (codes differ, blocks
-    differ) as fractions."""
+def _block_exponents(Eb, M, D):
+    """int exponents [M, ceil(D/32)] from the byte array."""
+    return _all_exponents(Eb, M)[:, :-(-D // 32)]
+
+
+def _put(Eb, M, b, vals):
+    Eb[_pos(M, b)] = vals
+
+
+def _check_codes(H, g32, codes, Eall, orc=None):
+    """Hg8 codes and exponents (Eall: _all_exponents of the same rows)
+    against host arithmetic on the GPU's own H, then (orc given) against the
+    oracle's; returns (codes differ, blocks differ) as fractions."""
     D = H.shape[1]
     # the quantisation decision, in the kernel's precision, on the GPU's own H
     hg = (H.astype(np.float32) * g32[None, :]).astype(np.float32)
     E_host = oracle.mx_exponents(hg)
-    E_gpu = _block_exponents(Eb, D)
-    np.testing.assert_array_equal(E_gpu, E_host)
+    nb = -(-D // 32)
+    np.testing.assert_array_equal(Eall[:, :nb], E_host)
     # every block past D, up to the array's end, holds exponent 0 (byte 127)
-    for b in range(-(-D // 32), 8 * Eb.shape[0]):
-        assert np.all(_blk(Eb, b) == 127)
+    assert np.all(Eall[:, nb:] == 0)
     Ecol = np.repeat(E_host, 32, axis=1)[:, :D]
     np.testing.assert_array_equal(codes, oracle.e4m3_encode(np.ldexp(hg.astype(np.float64), -Ecol)))
     if orc is None:
@@ -113,8 +122,17 @@ def _check(wl, x, o, rows=None):
     H = host_f32(o["H"])[sel]
     herr = max_rel(H, orc["H"])
     codes = o["Hg8"].cpu().numpy()[sel]
-    Eb = o["E"].cpu().numpy()[:, sel]
-    cdiff, ediff = _check_codes(H, x["g"].f32, codes, Eb, orc)
+    Eb = o["E"].cpu().numpy()
+    Eall = _all_exponents(Eb, wl.M)
+    # the padding rows of the last 128-row block hold exponent 0 too
+    pad = np.arange(wl.M, 128 * Eb.shape[1])
+    for bb in range(8 * Eb.shape[0]):
+        t = bb // 2
+        assert np.all(Eb[t // 4, pad // 128, bb % 2, pad % 32, (pad // 32) % 4, t % 4] == 127)
+    # the binding's reader of the layout agrees with this file's
+    np.testing.assert_array_equal(coda.mx_exponents_of(o["E"], wl.M, wl.D).cpu().numpy(),
+                                  Eall[:, :-(-wl.D // 32)])
+    cdiff, ediff = _check_codes(H, x["g"].f32, codes, Eall[sel], orc)
     hdiff = H != orc["Hb"]
     print(f"H max_rel {herr:.2e}, H bits differ {hdiff.mean():.2e}, codes differ {cdiff:.2e}, "
           f"block exponents differ {ediff:.2e}", file=sys.__stderr__, flush=True)
@@ -163,7 +181,7 @@ def test_fp8_repeatable_and_unscaled_second_gemm():
     xq = oracle.e4m3_decode(o["Hg8"].cpu().numpy())
     W2 = (oracle.e4m3_decode(x["W2t8"]) * x["sw2"][:, None].astype(np.float64)).T
     assert max_rel(host_f32(Y3), xq @ W2) <= 2.0 ** -8
-    Ecol = np.repeat(_block_exponents(o["E"].cpu().numpy(), wl.D), 32, axis=1)[:, :wl.D]
+    Ecol = np.repeat(_block_exponents(o["E"].cpu().numpy(), wl.M, wl.D), 32, axis=1)[:, :wl.D]
     assert max_rel(host_f32(Y4), np.ldexp(xq, Ecol) @ W2) <= 2.0 ** -8
 
 
@@ -177,10 +195,9 @@ def _mx_case(M, D, N2, seed):
     codes[(codes & 0x7F) == 0x7F] = 0x3C                     # no NaN codes
     nb, nk, G = -(-D // 32), -(-D // 64), -(-D // 256)
     E = rng.integers(-6, 7, size=(M, nb))
-    Eb = np.full((G, M, 2, 4), 0xFF, dtype=np.uint8)
+    Eb = np.full((G, -(-M // 128), 2, 32, 4, 4), 0xFF, dtype=np.uint8)   # padding rows: 0xFF (never used)
     for b in range(2 * nk):
-        t = b // 2
-        Eb[t // 4, :, b % 2, t % 4] = (E[:, b] + 127) if b < nb else rng.integers(0, 255, size=M)
+        _put(Eb, M, b, (E[:, b] + 127) if b < nb else rng.integers(0, 255, size=M))
     W2t8 = rng.integers(0, 256, size=(N2, D), dtype=np.uint8)
     W2t8[(W2t8 & 0x7F) == 0x7F] = 0x38
     sw2 = np.exp2(rng.integers(-8, 1, size=N2)).astype(np.float32)
@@ -226,11 +243,10 @@ def test_mx_block_exponent_map(MD, packed):
     M, D = MD
     N2 = 32
     nb, G = -(-D // 32), -(-D // 256)
-    Eb = np.zeros((G, M, 2, 4), dtype=np.uint8)
-    for i in range(M):
-        for h in range(2):
-            for t in range(4 * G):
-                Eb[t // 4, i, h, t % 4] = 127 + (8 * G * h + t + 3 * i) % 41 - 20
+    Eb = np.zeros((G, -(-M // 128), 2, 32, 4, 4), dtype=np.uint8)
+    for b in range(8 * G):
+        h, t = b % 2, b // 2
+        _put(Eb, M, b, 127 + (8 * G * h + t + 3 * np.arange(M)) % 41 - 20)
     W = np.full((N2, D), 0x38, dtype=np.uint8)             # e4m3 1.0
     sw = _f32(np.ones(N2, dtype=np.float32))
     Ed = _u8(Eb)
@@ -247,7 +263,7 @@ def test_mx_block_exponent_map(MD, packed):
             coda.coda_gemm_rowscale_fp8(_u8(X), Ed, _u8(W), sw, None, Y)
             coda.coda_gemm_rowscale_fp8(_u8(X), None, _u8(W), sw, None, Yu)
         torch.cuda.synchronize()
-        want = _blk(Eb, b).astype(np.float64) - 127
+        want = Eb[_pos(M, b)].astype(np.float64) - 127
         ratio = host_f32(Y).astype(np.float64) / host_f32(Yu).astype(np.float64)
         np.testing.assert_array_equal(ratio, np.repeat(np.exp2(want)[:, None], N2, axis=1),
                                       err_msg=f"block {b}")
@@ -296,7 +312,7 @@ def test_large_residual_does_not_saturate():
     Y_exact = orc["r"][:, None] * ((orc["H"] * x["g"].f32[None, :].astype(np.float64)) @ W2)
     hg = host_f32(H) * x["g"].f32[None, :]
     assert np.abs(hg).max() > 448 * 8                       # far past e4m3's range without a scale
-    assert _block_exponents(E.cpu().numpy(), wl.D).max() >= 3
+    assert _block_exponents(E.cpu().numpy(), wl.M, wl.D).max() >= 3
     err = max_rel(host_f32(Y), Y_exact)
     err_orc = max_rel(host_f32(Y), orc["Y"])
     print(f"R x 1e3: Y error vs exact chain {err:.3e}, vs oracle {err_orc:.3e}", file=sys.__stderr__, flush=True)
@@ -314,6 +330,7 @@ def test_full_size_7b_fp8_whole_tensor():
     num = {"Y": 0.0, "H": 0.0}
     den = {"Y": 0.0, "H": 0.0}
     ndiff = nhdiff = 0
+    Eall = _all_exponents(o["E"].cpu().numpy(), wl.M)
     for s0 in range(0, wl.M, 4096):
         rows = np.arange(s0, min(wl.M, s0 + 4096))
         orc = oracle.forward_fp8(x["A8"], x["sa"], x["W1t8"], x["sw1"], x["R"].f32, x["g"].f32, x["W2t8"],
@@ -322,7 +339,7 @@ def test_full_size_7b_fp8_whole_tensor():
         H = o["H"][blk].float().cpu().numpy()
         Y = o["Y"][blk].float().cpu().numpy()
         codes = o["Hg8"][blk].cpu().numpy()
-        cdiff, _ = _check_codes(H, x["g"].f32, codes, o["E"][:, blk].cpu().numpy(), orc)
+        cdiff, _ = _check_codes(H, x["g"].f32, codes, Eall[blk], orc)
         diff_n = int(round(cdiff * codes.size))
         hdiff = H != orc["Hb"]
         np.testing.assert_allclose(o["r"][blk].cpu().numpy(), orc["r"], rtol=2e-3)

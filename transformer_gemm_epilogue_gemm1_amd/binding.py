@@ -329,24 +329,32 @@ def _mat8(t: torch.Tensor, name: str, shape) -> int:
     return _mat(t, name, t.dtype, shape)
 
 
+def _mx_shape(rows: int, cols: int):
+    return ((cols + 255) // 256, (rows + 127) // 128, 2, 32, 4, 4)
+
+
 def mx_exp_empty(rows: int, cols: int, device) -> torch.Tensor:
     """A block-exponent array for a [rows, cols] MX operand: uint8
-    [G, rows, 2, 4] with G = ceil(cols / 256); byte [t // 4, i, h, t % 4] is
-    the E8M0 exponent of columns [64 t + 32 h, + 32) of row i."""
-    return torch.empty(((cols + 255) // 256, rows, 2, 4), device=device, dtype=torch.uint8)
+    [G, B, 2, 32, 4, 4] with G = ceil(cols / 256) groups of 4 k-tiles and
+    B = ceil(rows / 128) row blocks; byte [t // 4, i // 128, h, i % 32,
+    (i // 32) % 4, t % 4] is the E8M0 exponent of columns [64 t + 32 h, + 32)
+    of row i (the rows past `rows` in the last block are padding)."""
+    return torch.empty(_mx_shape(rows, cols), device=device, dtype=torch.uint8)
 
 
-def mx_exponents_of(E: torch.Tensor, cols: int) -> torch.Tensor:
+def mx_exponents_of(E: torch.Tensor, rows: int, cols: int) -> torch.Tensor:
     """The int32 exponents [rows, ceil(cols / 32)] an exponent array holds
     (E8M0 codes minus 127); block b of a row is half b % 2 of k-tile b // 2."""
     nb = (cols + 31) // 32
     b = torch.arange(nb, device=E.device)
     t = b // 2
-    return E[t // 4, :, b % 2, t % 4].T.to(torch.int32) - 127
+    i = torch.arange(rows, device=E.device)
+    return E[(t // 4)[None, :], (i // 128)[:, None], (b % 2)[None, :], (i % 32)[:, None], ((i // 32) % 4)[:, None],
+             (t % 4)[None, :]].to(torch.int32) - 127
 
 
 def _mx(E: torch.Tensor, name: str, rows: int, cols: int) -> None:
-    shape = ((cols + 255) // 256, rows, 2, 4)
+    shape = _mx_shape(rows, cols)
     if E.dtype != torch.uint8 or tuple(E.shape) != shape or not E.is_contiguous():
         raise ValueError(f"{name}: expected a contiguous uint8 tensor of shape {shape}, got {E.dtype} {tuple(E.shape)}")
     if E.data_ptr() % 16 != 0:

@@ -142,8 +142,8 @@ coda_status launch_gemm(const char* what, int M, int N, int K, const void* a, in
 int64_t packed_bytes_e4m3(int64_t rows, int64_t cols) { return (rows + 15) / 16 * 16 * cols; }
 
 // Bytes of a block-exponent array (mx_byte layout) for `rows` rows and
-// `cols` contraction columns: 8 bytes per row and group of 4 k-tiles.
-int64_t mx_exp_bytes(int64_t rows, int64_t cols) { return 8 * rows * ((cols + 255) / 256); }
+// `cols` contraction columns: 1 KiB per 128-row block and group of 4 k-tiles.
+int64_t mx_exp_bytes(int64_t rows, int64_t cols) { return 1024 * mx_row_blocks(rows) * ((cols + 255) / 256); }
 
 // L: OpLayout of both operands (kLayPacked: lda / ldb counting 16-byte chunks
 // per row).  MX: a_exp holds the block exponents of A (mx_byte layout,

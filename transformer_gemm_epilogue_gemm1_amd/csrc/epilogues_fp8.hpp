@@ -65,8 +65,9 @@ __device__ __forceinline__ void load_col_scales(const float* sw, int col, int N,
 // news article's building blocks).  apply() keeps x; end_slab(), which
 // every lane runs, takes the block maxima and writes codes and exponents.
 // Every byte of the exponent array is written: its groups of 4 k-tiles
-// cover exactly the 256-column tiles, and a block past D (all x = 0) gets
-// exponent 0.  The second GEMM reads whole groups of them.
+// cover exactly the 256-column tiles, its row blocks the rows up to M
+// rounded up to 128 (whose lanes run end_slab with x = 0), and a block past
+// D or a padding row gets exponent 0.  The second GEMM reads whole groups.
 struct EpiResPrmsFp8 {
   struct Params {
     const float* sa;    // [M]
@@ -80,7 +81,7 @@ struct EpiResPrmsFp8 {
     int64_t ldhg;
     float* partials;    // [T][M]
     int64_t hg_nck;     // > 0: Hg8 is tile-packed (kp_unit) with hg_nck 16-byte chunks per row
-    uint8_t* hg_exp;    // block exponents (mx_byte layout), 8 M ceil(D / 256) bytes
+    uint8_t* hg_exp;    // block exponents (mx_byte layout), 1024 ceil(M / 128) ceil(D / 256) bytes
   };
   Params p;
   RowChunks<uint16_t> rc;
@@ -145,7 +146,7 @@ struct EpiResPrmsFp8 {
                                     : p.Hg8 + (int64_t)row * p.ldhg + col;
         *(u32x2*)dst = u32x2{lo, hi};
       }
-      if ((lane & 3) == 0 && row < M)
+      if ((lane & 3) == 0 && row < 128 * mx_row_blocks(M))
         p.hg_exp[mx_byte(row, col >> 6, (col >> 5) & 1, M)] = (uint8_t)(E + 127);
 #pragma unroll
       for (int i = 0; i < 8; ++i) xg[q][i] = 0.f;

@@ -179,15 +179,21 @@ constexpr int kFrag8N = kWaveN / 32;  // 2 fragments of 32 B rows
 CODA_HD int kc8_offset(int base, int t, int half, int lane) {
   return kc_offset(base + 32 * t + (lane & 31), (lane >> 5) + 2 * half);
 }
-// MX block exponents (one E8M0 byte per row and 32 contraction columns):
-// row i's exponent for half h of k-tile t lies at byte mx_byte(i, t, h, M)
-// of an array for M rows: groups of 4 k-tiles outermost, then the rows, the
-// two halves, and the k-tile within its group.  A group's dword of one
-// (row, half) then holds 4 consecutive k-tiles, and the dwords a 32-row
-// fragment's 64 lanes read for a group (row i + lane % 32, half lane / 32)
-// are 256 contiguous bytes.  The array spans 8 M ceil(cols / 256) bytes.
+// MX block exponents (one E8M0 byte per row and 32 contraction columns), in
+// the order the second GEMM's lanes take them.  Rows come in blocks of 128
+// (a wavefront's A rows); within a block, row 32 mt + l of k-tile t, half h
+// is the scale that lane 32 h + l supplies for A fragment mt (tile_map's
+// 32-row fragments).  Byte mx_byte(i, t, h, M) of an array for M rows:
+//   ((t / 4 * ceil(M / 128) + i / 128) * 64 + 32 h + i % 32) * 16
+//     + ((i / 32) % 4) * 4 + t % 4
+// so a lane's 16 bytes hold, for one group of 4 k-tiles, its 4 fragments'
+// dwords (one k-tile per byte), and a wavefront's 64 lanes read one 1 KiB
+// block per group.  The array spans 1024 ceil(M / 128) ceil(cols / 256)
+// bytes; the rows past M in the last block are padding.
+CODA_HD int64_t mx_row_blocks(int64_t M) { return (M + 127) / 128; }
 CODA_HD int64_t mx_byte(int64_t i, int t, int h, int64_t M) {
-  return (((int64_t)(t >> 2) * M + i) * 2 + h) * 4 + (t & 3);
+  return (((int64_t)(t >> 2) * mx_row_blocks(M) + (i >> 7)) * 64 + 32 * h + (i & 31)) * 16 + ((i >> 5) & 3) * 4 +
+         (t & 3);
 }
 // Accumulator element e (0..15) of lane l in a 32 x 32 product is output
 // row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32 (established by a GPU
