@@ -20,6 +20,7 @@
 #pragma once
 
 #include "gemm.hpp"
+#include "lanes.hpp"
 
 namespace coda {
 
@@ -126,10 +127,7 @@ struct EpiResPrms {
   __device__ __forceinline__ void end_slab(int, int slab_row0) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      float s = ss[q];
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
+      const float s = sum8(ss[q]);
       const int row = slab_row0 + (lane >> 3) + 8 * q;
       if ((lane & 7) == 0 && row < M) p.partials[(int64_t)t * M + row] = s;
       ss[q] = 0.f;
@@ -177,6 +175,8 @@ struct EpiRowScale {
 // inline tens of instructions per value into an epilogue that runs once per
 // tile and is fetched cold.  Large |x| behave: e^-x -> inf gives 0, -> 0
 // gives x.
+static_assert(kSwiGLUPartner == 4, "the SwiGLU epilogue pairs lanes l and l ^ 4");
+
 template <typename T>
 struct EpiSwiGLU {
   struct Params {
@@ -202,7 +202,7 @@ struct EpiSwiGLU {
     if (p.Y != nullptr) Chunk8<T>::store(p.Y + (int64_t)row * p.ldy + (up ? p.F : 0) + oc, v);
     float o[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = __shfl_xor(v[i], kSwiGLUPartner);
+    for (int i = 0; i < 8; ++i) o[i] = lane_xor4(v[i]);  // the partner lane (kSwiGLUPartner = 4)
     if (!up) {
       float z[8];
 #pragma unroll
@@ -291,8 +291,9 @@ struct EpiLSE {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       float m = mx[q], s = sm[q];
-#pragma unroll
-      for (int x = 1; x < 8; x <<= 1) lse_merge(m, s, __shfl_xor(m, x), __shfl_xor(s, x));
+      lse_merge(m, s, lane_xor1(m), lane_xor1(s));
+      lse_merge(m, s, lane_xor2(m), lane_xor2(s));
+      lse_merge(m, s, lane_xor4(m), lane_xor4(s));
       const int row = slab_row0 + (lane >> 3) + 8 * q;
       if ((lane & 7) == 0 && row < M) {
         p.pmax[(int64_t)t * M + row] = m;
@@ -387,10 +388,7 @@ struct EpiBwdG {
   __device__ __forceinline__ void end_slab(int, int slab_row0) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      float s = ss[q];
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
+      const float s = sum8(ss[q]);
       const int row = slab_row0 + (lane >> 3) + 8 * q;
       if ((lane & 7) == 0 && row < M) p.srow[(int64_t)t * M + row] = s;
       ss[q] = 0.f;

@@ -123,10 +123,7 @@ struct EpiResPrmsFp8 {
   __device__ __forceinline__ void end_slab(int, int slab_row0) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      float s = ss[q];
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
+      const float s = sum8(ss[q]);
       const int row = slab_row0 + (lane >> 3) + 8 * q;
       if ((lane & 7) == 0 && row < M) p.partials[(int64_t)t * M + row] = s;
       ss[q] = 0.f;
@@ -134,8 +131,7 @@ struct EpiResPrmsFp8 {
       float a = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(xg[q][i]));
-      a = fmaxf(a, __shfl_xor(a, 1));
-      a = fmaxf(a, __shfl_xor(a, 2));
+      a = max4(a);
       const int E = mx_exponent(a);
       if (row < M && col < N) {
         const uint32_t lo = pack_e4m3x4(ldexpf(xg[q][0], -E), ldexpf(xg[q][1], -E), ldexpf(xg[q][2], -E),
