@@ -26,13 +26,16 @@ Sources (the CODA news article by Synced / 机器之心, mirrored by KuCoin News
     the division correctly rounded in float32; a column-wise variant gives
     the transposed weight codes with per-output-channel scales;
   * backward (backward_fp8): every product of the chain's backward takes
-    e4m3 operands quantised along its contraction: G = dY W2^T with dY and
-    W2 [D, N2] per row; dW2 = Xn^T dY with Xn and dY per column (their
-    contraction runs over the M rows); dA = dH W1^T with dH and W1 [K, D]
-    per row; dW1 = A^T dH with A and dH per column.  The quantisers are
-    treated as the identity when differentiating (straight-through); the
-    rest is the bf16 chain's backward: P = g G, s = sum_j P H,
-    dg = sum_i r H G, Xn = (H r) g, dH = r P - (r^3 s / D) H, dR = dH.
+    e4m3 operands with MX block exponents along its contraction (mx_quantize:
+    one exponent per 32 contraction elements, chosen as for H g above, so
+    no value saturates): G = dY W2^T with dY and W2 [D, N2] in blocks along
+    their rows; dW2 = Xn^T dY with Xn and dY in blocks along their columns
+    (their contraction runs over the M rows); dA = dH W1^T with dH and
+    W1 [K, D] along their rows; dW1 = A^T dH with A and dH along their
+    columns.  The quantisers are treated as the identity when
+    differentiating (straight-through); the rest is the bf16 chain's
+    backward: P = g G, s = sum_j P H, dg = sum_i r H G, Xn = (H r) g,
+    dH = r P - (r^3 s / D) H, dR = dH.
 
     A   = e4m3(A8) * sa[:, None]            W1 = (e4m3(W1t8) * sw1[:, None])^T
     H   = A W1 + R                          Hb = bf16(H)
@@ -135,6 +138,24 @@ def mx_exponents(x, block: int = MX_BLOCK) -> np.ndarray:
     return np.clip(E, -127, 127).astype(np.int32)
 
 
+def mx_quantize(x):
+    """MX e4m3 quantisation of a float32 matrix along its rows: per row and
+    block of 32 columns the exponent E of mx_exponents, and the codes
+    e4m3(x 2^-E) (nearest, ties to the even code).  Returns (codes uint8
+    [rows, cols], E int32 [rows, ceil(cols / 32)])."""
+    x = np.asarray(x, dtype=np.float32)
+    E = mx_exponents(x)
+    Ecol = np.repeat(E, MX_BLOCK, axis=1)[:, :x.shape[1]]
+    return e4m3_encode(np.ldexp(x.astype(np.float64), -Ecol)), E
+
+
+def mx_dequantize(codes, E) -> np.ndarray:
+    """The values MX codes and their block exponents stand for (float64)."""
+    codes = np.asarray(codes)
+    Ecol = np.repeat(np.asarray(E, dtype=np.int64), MX_BLOCK, axis=1)[:, :codes.shape[1]]
+    return np.ldexp(e4m3_decode(codes), Ecol)
+
+
 def forward_fp8(A8, sa, W1t8, sw1, R, g, W2t8, sw2, eps: float,
                 rows: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
     """Returns float64 H (exact), Hb (bf16-rounded H), r, Y, the uint8 Hg8
@@ -157,15 +178,16 @@ def forward_fp8(A8, sa, W1t8, sw1, R, g, W2t8, sw2, eps: float,
 
 
 def _deq_rows(x, on: bool) -> np.ndarray:
-    """x after per-row quantisation and dequantisation (x itself when off)."""
+    """x (float32) after MX quantisation along its rows and dequantisation
+    (x itself when off)."""
     if not on:
         return np.asarray(x, dtype=np.float64)
-    codes, scale = quantize_rows(x)
-    return e4m3_decode(codes) * scale[:, None].astype(np.float64)
+    return mx_dequantize(*mx_quantize(x))
 
 
 def _deq_cols(x, on: bool) -> np.ndarray:
-    """x after per-column quantisation and dequantisation."""
+    """x after MX quantisation along its columns (blocks of 32 rows) and
+    dequantisation."""
     if not on:
         return np.asarray(x, dtype=np.float64)
     return _deq_rows(np.ascontiguousarray(np.asarray(x, dtype=np.float32).T), True).T

@@ -2,9 +2,11 @@
 
 A second, independent implementation of the reading that oracle/fp8.py
 documents for the backward: every product takes e4m3 operands quantised along
-its contraction (per row or per column, scale = amax / 448 in float32, codes
-= nearest-even e4m3 of the float32 quotient, magnitudes clamped to 448), the
-quantisers count as the identity when differentiating, and the three values
+its contraction with MX block exponents (per row or per column, in blocks of
+32 contraction elements, the last one short: E the smallest integer with the
+block's largest float32 magnitude <= 448 2^E, clamped to [-127, 127], 0 for
+an all-zero block; codes the nearest-even e4m3 of x 2^-E), the quantisers
+count as the identity when differentiating, and the three values
 the recipe keeps in bf16 -- P = g G, X_n = (H r) g and dH = r P - (r^3 s / D) H
 -- are rounded to bf16 at the point they are stored, from their float32 value
 (a value the kernels hold in float32 is stored as bf16), with dH taking the
@@ -46,11 +48,25 @@ def e4m3_nearest(x: float) -> int:
     return best | (0x80 if math.copysign(1.0, x) < 0 else 0)
 
 
-def quant_vec(v):
-    """Dequantised values of one vector quantised with its own scale."""
-    amax = max(abs(f32(x)) for x in v)
-    scale = f32(amax / 448.0) if amax > 0 else 1.0
-    return [e4m3_value(e4m3_nearest(f32(f32(x) / scale))) * scale for x in v]
+def block_exponent(amax: float) -> int:
+    """The smallest integer E in [-127, 127] with amax <= 448 2^E, found by
+    counting up (127 if none; 0 for an all-zero block)."""
+    if amax == 0:
+        return 0
+    E = -127
+    while E < 127 and amax > 448.0 * 2.0 ** E:
+        E += 1
+    return E
+
+
+def quant_vec(v, block=32):
+    """Dequantised values of one vector quantised in blocks of `block`."""
+    out = []
+    for b0 in range(0, len(v), block):
+        blk = [f32(x) for x in v[b0:b0 + block]]
+        E = block_exponent(max(abs(x) for x in blk))
+        out += [e4m3_value(e4m3_nearest(x * 2.0 ** -E)) * 2.0 ** E for x in blk]
+    return out
 
 
 def quant_rows(X):

@@ -360,7 +360,9 @@ def test_fp8_backward_quantisation_axes(which):
 from tests import fp8_backward_brute as bb  # noqa: E402
 
 
-def _bwd_pin_case(seed, M=16, K=16, D=16, N2=32):
+def _bwd_pin_case(seed, M=40, K=16, D=48, N2=72):
+    # every contraction spans more than one block of 32 and ends in a short
+    # block (N2 = 72, D = 48, M = 40): per-vector scales would not match
     # the backward's inputs, with H and r as the forward stores them (H in
     # bf16, r in float32)
     c = _bwd_case(seed, M, K, D, N2)
@@ -426,21 +428,95 @@ def test_fp8_backward_storage_pin_rejects_planted_mistakes(kind):
 
 
 def test_fp8_backward_quantises_the_stored_bf16_xn():
-    # Hand-worked: M = 2, K = D = N2 = 1, g = 1, dY = 1, H = (256, 1), r =
-    # (1, r1) with r1 = float32(0.60725) = 0.6072499752...  X_n = H r g is
-    # (256, r1); stored in bf16 the second is 0.60546875 (spacing 2^-8).
-    # X_n's column scale is s = float32(256 / 448); 256 / s rounds to the
-    # code 448, and 0.60546875 / s = 1.0596 to the code 1.0 -- while the
-    # unrounded r1 / s = 1.0627 would pass the midpoint 1.0625 to 1.125.
-    # dY's column codes are 448 with scale t = float32(1 / 448), so
-    # dW2 = (448 s)(448 t) + (1.0 s)(448 t).
-    r1 = float(np.float32(0.60725))
-    assert oracle.bf16_round(np.array([r1]))[0] == 0.60546875
-    s = float(np.float32(256.0) / np.float32(448.0))
-    t = float(np.float32(1.0) / np.float32(448.0))
+    # Hand-worked: M = 2, K = D = N2 = 1, g = 1, dY = 1, H = (256, 1),
+    # r = (1, r1) with r1 = float32(1.0627) = 1.06270003...  X_n = H r g is
+    # (256, r1); stored in bf16 the second is 1.0625 (spacing 2^-7), exactly
+    # halfway between the e4m3 values 1.0 and 1.125, so its code is the even
+    # one, 1.0 -- while the unrounded r1 is past the midpoint: 1.125.
+    # X_n's column is one block with largest magnitude 256: exponent 0
+    # (224 < 256 <= 448), codes 256 and 1.0.  dY's column (1, 1) has exponent
+    # -8 (1 <= 448 / 256 = 1.75) and codes 256, i.e. exactly 1.  So
+    # dW2 = 256 + 1.0 = 257, not 257.125.
+    r1 = float(np.float32(1.0627))
+    assert oracle.bf16_round(np.array([r1]))[0] == 1.0625
     one = np.ones((2, 1), np.float32)
     out = oracle.backward_fp8(one, one, np.ones((1, 1), np.float32), np.zeros((2, 1)), np.ones(1, np.float32),
                               np.ones((1, 1), np.float32), 0.0, H=np.array([[256.0], [1.0]]), r=np.array([1.0, r1]))
-    assert out["Xn"][1, 0] == 0.60546875
-    assert out["dW2"][0, 0] == pytest.approx((448 * s) * (448 * t) + (1.0 * s) * (448 * t), rel=1e-15)
-    assert out["dW2"][0, 0] != pytest.approx((448 * s) * (448 * t) + (1.125 * s) * (448 * t), rel=1e-6)
+    assert out["Xn"][1, 0] == 1.0625
+    assert out["dW2"][0, 0] == 257.0
+
+
+def test_mx_quantize_hand_values():
+    # one row, blocks of 32 (the second one short):
+    #   block 0: 448 and 1.0 -> E = 0, codes exact (448 = 0x7E, 1.0 = 0x38);
+    #   block 1: 449 -> E = 1: 224.5 lies between the e4m3 values 224 and 240,
+    #   nearer 224 (0x76), which stands for 448; 3.0 -> 1.5 (0x3C), i.e. 3.0.
+    x = np.zeros((1, 40), np.float32)
+    x[0, 0], x[0, 1], x[0, 32], x[0, 33] = 448.0, 1.0, 449.0, 3.0
+    codes, E = oracle.mx_quantize(x)
+    assert E.tolist() == [[0, 1]]
+    assert codes[0, :2].tolist() == [0x7E, 0x38] and codes[0, 32:34].tolist() == [0x76, 0x3C]
+    assert np.all(codes[0, 2:32] == 0) and np.all(codes[0, 34:] == 0)
+    deq = oracle.mx_dequantize(codes, E)
+    assert deq[0, 0] == 448.0 and deq[0, 1] == 1.0 and deq[0, 32] == 448.0 and deq[0, 33] == 3.0
+
+
+def test_fp8_backward_blocks_are_independent():
+    # MX quantisation is block-local: scaling the 32 contraction elements of
+    # one block by 8 multiplies that block's dequantised values by 8 exactly
+    # and leaves every other block's alone.  So scaling dY[i, 32:64] by 8 adds
+    # exactly 7 times that block's contribution to row i of G (the contribution
+    # computed from dY with everything else zeroed), and changes no other row.
+    # With one scale per row (or blocks of 64) the rest of row i would move.
+    c = _bwd_case(34, M=8, K=16, D=16, N2=96)
+    H = c["A"].astype(np.float64) @ c["W1"].astype(np.float64) + c["R"]
+    r = 1.0 / np.sqrt(np.mean(H * H, axis=1) + 1e-5)
+    args = (c["A"], c["W1"], c["R"], c["g"], c["W2"], 1e-5)
+    base = oracle.backward_fp8(c["dY"], *args, H=H, r=r)["G"]
+    dY2 = c["dY"].copy()
+    dY2[3, 32:64] *= 8
+    new = oracle.backward_fp8(dY2, *args, H=H, r=r)["G"]
+    only = np.zeros_like(c["dY"])
+    only[3, 32:64] = c["dY"][3, 32:64]
+    part = oracle.backward_fp8(only, *args, H=H, r=r)["G"]
+    np.testing.assert_allclose(new[3], base[3] + 7 * part[3], rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(np.delete(new, 3, axis=0), np.delete(base, 3, axis=0))
+    # the same along the contraction over M: dW2 with a block of dY's column 5
+    # (rows 32..63 of that column) scaled
+    c = _bwd_case(35, M=96, K=16, D=16, N2=24)
+    H = c["A"].astype(np.float64) @ c["W1"].astype(np.float64) + c["R"]
+    r = 1.0 / np.sqrt(np.mean(H * H, axis=1) + 1e-5)
+    args = (c["A"], c["W1"], c["R"], c["g"], c["W2"], 1e-5)
+    base = oracle.backward_fp8(c["dY"], *args, H=H, r=r)["dW2"]
+    dY2 = c["dY"].copy()
+    dY2[32:64, 5] *= 8
+    new = oracle.backward_fp8(dY2, *args, H=H, r=r)["dW2"]
+    only = np.zeros_like(c["dY"])
+    only[32:64, 5] = c["dY"][32:64, 5]
+    part = oracle.backward_fp8(only, *args, H=H, r=r)["dW2"]
+    np.testing.assert_allclose(new[:, 5], base[:, 5] + 7 * part[:, 5], rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(np.delete(new, 5, axis=1), np.delete(base, 5, axis=1))
+
+
+def _deq_per_row_scale(x, on):
+    codes, scale = oracle.quantize_rows(x)
+    return oracle.e4m3_decode(codes) * scale[:, None].astype(np.float64)
+
+
+def _deq_blocks_of_64(x, on):
+    from oracle.fp8 import mx_exponents
+    x = np.asarray(x, np.float32)
+    E = np.repeat(mx_exponents(x, 64), 64, axis=1)[:, :x.shape[1]]
+    return np.ldexp(oracle.e4m3_decode(oracle.e4m3_encode(np.ldexp(x.astype(np.float64), -E))), E)
+
+
+@pytest.mark.parametrize("mutant", [_deq_per_row_scale, _deq_blocks_of_64], ids=["per_row_scale", "blocks_of_64"])
+def test_block_pin_rejects_planted_granularity(mutant, monkeypatch):
+    # the backward's quantiser replaced by one with the wrong granularity (the
+    # brute force alone cannot tell blocks of 64 from blocks of 32 on Gaussian
+    # data: their exponents nearly always agree); the block-independence pin
+    # must fail
+    import oracle.fp8 as f
+    monkeypatch.setattr(f, "_deq_rows", mutant)
+    with pytest.raises(AssertionError):
+        test_fp8_backward_blocks_are_independent()
