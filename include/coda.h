@@ -546,20 +546,42 @@ coda_status coda_chain_bwd_noalloc(coda_dtype dt, int64_t M, int64_t K, int64_t 
                                    void* dA, void* dR, void* dW1, void* dW2, float* dg,
                                    void* stream);
 
+/* MX (OCP microscaling) e4m3 quantisation of a bf16 matrix X [M, N] (row-
+ * major, ldx) along its rows and/or its columns, as the fp8 backward takes
+ * its operands; one read of X serves both.  Each block of 32 consecutive
+ * elements along the quantised direction gets its own exponent E, the
+ * smallest integer with the block's largest magnitude <= 448 2^E (clamped to
+ * [-127, 127], 0 for an all-zero block; the rule of the fp8 first GEMM's
+ * block exponents), stored as the E8M0 byte E + 127, and its elements the
+ * codes e4m3(x 2^-E), nearest-even (no value saturates).
+ *   Xr8p, Er: the row codes [M, N] tile-packed (coda_packed_bytes_e4m3(M, N)
+ *     bytes) and their exponents, one per row and 32 columns, in the layout
+ *     of coda_mx_exp_bytes (rows M, cols N: coda_mx_exp_bytes(M, N) bytes);
+ *   Xc8p, Ec: the codes of X^T [N, M] tile-packed (coda_packed_bytes_e4m3(N,
+ *     M) bytes), one exponent per column of X and 32 rows (rows N, cols M:
+ *     coda_mx_exp_bytes(N, M) bytes).
+ * Either pair may be NULL (not both; a pair is both set or both NULL).  Every
+ * byte of an exponent array is written, those of padding rows and of blocks
+ * past the end as 127.  M, N multiples of 16, N <= 16776960; M = 0 is a
+ * no-op.  All outputs 16-byte aligned; none may overlap X or another. */
+coda_status coda_quantize_mx_e4m3_packed(int64_t M, int64_t N, const void* X, int64_t ldx,
+                                         void* Xr8p, void* Er, void* Xc8p, void* Ec, void* stream);
+
 /* Backward of the chain with e4m3 products (the fp8 recipe above, carried to
  * the backward; the pages give none).  Every product takes e4m3 operands
- * quantised along its contraction, as coda_quantize_rows_e4m3 does:
- *   G = dY W2^T       dY per row, W2 [D,N2] per row
- *   dW2 = X_n^T dY    X_n and dY per column (contraction over the M rows)
- *   dA = dH W1^T      dH per row, W1 [K,D] per row
- *   dW1 = A^T dH      A and dH per column
- * with fp32 accumulation and dequantisation in the epilogues; everything
- * else (P, X_n, the partial sums, c, dg, dH = r P - c H, dR = dH) is the
- * bf16 backward's.  The quantisers count as the identity when
- * differentiating (straight-through).  Arguments as coda_chain_bwd, all
- * bf16 (r, dg float); M, K, D, N2 multiples of 16, M <= 4194240; ws of
- * coda_chain_bwd_fp8_workspace_bytes() (the bf16 backward's workspace plus
- * the e4m3 operands and their scales). */
+ * with MX block exponents along its contraction, as
+ * coda_quantize_mx_e4m3_packed makes them, and the matrix core applies the
+ * exponents of both operands:
+ *   G = dY W2^T       dY along its rows, W2 [D,N2] along its rows
+ *   dW2 = X_n^T dY    X_n and dY along their columns (contraction over M)
+ *   dA = dH W1^T      dH along its rows, W1 [K,D] along its rows
+ *   dW1 = A^T dH      A and dH along their columns
+ * with fp32 accumulation; everything else (P, X_n, the partial sums, c, dg,
+ * dH = r P - c H, dR = dH) is the bf16 backward's.  The quantisers count as
+ * the identity when differentiating (straight-through).  Arguments as
+ * coda_chain_bwd, all bf16 (r, dg float); M, K, D, N2 multiples of 16,
+ * M <= 4194240; ws of coda_chain_bwd_fp8_workspace_bytes() (the bf16
+ * backward's workspace plus the e4m3 operands and their exponents). */
 size_t coda_chain_bwd_fp8_workspace_bytes(int64_t M, int64_t K, int64_t D, int64_t N2);
 coda_status coda_chain_bwd_fp8(int64_t M, int64_t K, int64_t D, int64_t N2,
                                const void* dY, const void* A, const void* W1, const void* g,

@@ -325,6 +325,28 @@ def test_quantize_packed_validation(lib):
     assert rc(0, 256, None, 256, None, None, None, None, None) == OK
 
 
+def test_quantize_mx_validation(lib):
+    q = lib.coda_quantize_mx_e4m3_packed
+    M, N = 512, 256
+    assert q(520, N, H_, N, HG_, EX_, Y_, DG_, None) == SHAPE           # M not a multiple of 16
+    assert q(M, 264, H_, 264, HG_, EX_, Y_, DG_, None) == SHAPE         # N not a multiple of 16
+    assert q(M, 65536 * 256, H_, 65536 * 256, HG_, EX_, None, None, None) == SHAPE  # N past the grid
+    assert q(M, N, H_, N, HG_, None, Y_, DG_, None) == NULL             # row codes without exponents
+    assert q(M, N, H_, N, HG_, EX_, None, DG_, None) == NULL            # column exponents without codes
+    assert q(M, N, H_, N, None, None, None, None, None) == NULL         # no output at all
+    assert q(M, N, None, N, HG_, EX_, None, None, None) == NULL
+    assert q(M, N, H_, 260, HG_, EX_, None, None, None) == ALIGN        # ldx not a multiple of 8
+    assert q(M, N, H_, N, HG_, EX_ + 8, None, None, None) == ALIGN
+    assert q(M, N, H_, N, None, None, Y_ + 4, DG_, None) == ALIGN
+    assert q(M, N, H_, N, H_ + 4096, EX_, None, None, None) == ALIAS    # codes over X
+    assert q(M, N, H_, N, HG_, HG_ + 256, None, None, None) == ALIAS    # exponents over the codes
+    assert q(M, N, H_, N, HG_, EX_, HG_ + 4096, DG_, None) == ALIAS     # the two code arrays
+    assert q(M, N, H_, N, HG_, EX_, Y_, EX_ + 1024, None) == ALIAS      # the two exponent arrays
+    assert q(0, N, None, N, HG_, EX_, None, None, None) == OK           # M = 0: nothing to do
+    # the exponent arrays the call fills: 1 KiB per 128 rows and 256 columns
+    assert lib.coda_mx_exp_bytes(M, N) == 4096 and lib.coda_mx_exp_bytes(N, M) == 4096
+
+
 def rope_call(lib, dt=BF16, M=512, D=256, N2=1536, X=H_, ldx=None, W=W2_, ldw=None, r=R2_, pos=DY_, cs=DG_,
               max_pos=2048, nq=512, nk=512, dh=128, Y=Y_, ldy=None):
     return lib.coda_gemm_rowscale_rope(dt, M, D, N2, X, ldx or D, W, ldw or N2, r, pos, cs, max_pos, nq, nk, dh, Y,

@@ -512,24 +512,26 @@ def test_fp8_backward_matches_oracle(shape):
     orc = oracle.backward_fp8(x["dY"].f32, x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps,
                               H=H, r=r)
     # The stored dH (dR): its only source of difference is G, which the fp8
-    # products accumulate at less than float32 precision (as in the forward,
-    # where H misses the bf16 rounding of the exact value in ~1% of
-    # elements) and the oracle in float64.  dH = r P - c H with P = g G and
-    # c = r^3 s / D, s = sum_j P_j H_j: to first order a relative error e of
-    # G moves dH by r dP (with P's bf16 step) and by dc H, where
-    # |dc| <= (r^3 / D) e sum_j |P_j H_j| -- s cancels heavily (sum |P H|
-    # up to 1e5 |s| here), so c carries G's error much amplified.  Bound
-    # with e = 2^-7: a bf16 step of r P and of dH, plus that term; and at
-    # most 3% of the elements differ (measured 0.8-0.9%).
+    # products accumulate at less than float32 precision and the oracle in
+    # float64.  Their error model (the one the scaled second GEMM's tests
+    # establish): |dG| <= 2^-8 |G| + 2^-12 T, T = sum_n |dY_n W2_n| over the
+    # dequantised operands.  dH = r P - c H with P = g G and c = r^3 s / D,
+    # s = sum_j P_j H_j, so |d dH| <= r |g| dG + (r^3 / D) sum_j |g_j| dG_j
+    # |H_j| |H| plus the bf16 steps of r P and of dH; s cancels heavily (sum
+    # |P H| up to 1e5 |s| here), which is where c carries G's error much
+    # amplified.  At most 3% of the elements differ (measured 0.8-0.9%).
     dH = host_f32(out["dR"]).astype(np.float64)
     diff = dH != orc["dH"]
     assert diff.mean() <= 0.03, f"{diff.mean():.2e} of dH differs"
+    deq = lambda v: oracle.mx_dequantize(*oracle.mx_quantize(v))
     P = orc["G"] * x["g"].f32[None, :].astype(np.float64)
-    s_abs = np.sum(np.abs(P * H), axis=1)
-    bound = 2.0 ** -7 * (np.abs(r[:, None] * P) + np.abs(orc["dH"]) + (r ** 3 * s_abs / wl.D)[:, None] * np.abs(H))
+    T = np.abs(deq(x["dY"].f32)) @ np.abs(deq(x["W2"].f32)).T
+    dP = np.abs(x["g"].f32.astype(np.float64))[None, :] * (2.0 ** -8 * np.abs(orc["G"]) + 2.0 ** -12 * T)
+    dc = (r ** 3 / wl.D) * np.sum(dP * np.abs(H), axis=1)
+    bound = 2.0 ** -8 * (np.abs(r[:, None] * P) + np.abs(orc["dH"])) + r[:, None] * dP + dc[:, None] * np.abs(H)
     assert np.all(np.abs(dH - orc["dH"]) <= bound), f"dH deviation {np.max(np.abs(dH - orc['dH']) / bound):.2f} of the bound"
-    # Those few one-step differences can flip an e4m3 code (or a row or
-    # column scale) of dH, which moves the dA and dW1 products it feeds by
+    # Those few one-step differences can flip an e4m3 code (or a block
+    # exponent) of dH, which moves the dA and dW1 products it feeds by
     # up to one e4m3 step of a term; the end-to-end bar is 1e-2, and 3e-2
     # for the 16-row case, whose dW1 contracts over 16 rows only (one term
     # of 16, one step of 2^-3: derivation in the design notes).
@@ -550,16 +552,16 @@ def test_fp8_backward_matches_oracle(shape):
         e_orc = max_rel(orc[k], exact[k])
         assert e_gpu <= 1.25 * e_orc + 1e-3, f"{k}: {e_gpu:.3e} from the exact gradient, oracle {e_orc:.3e}"
     # stage-wise: dA and dW1 on the GPU's own stored dH, quantised on the host
-    # (one bf16 rounding of an fp32 accumulation)
-    deq = lambda c_s: oracle.e4m3_decode(c_s[0]) * c_s[1][:, None].astype(np.float64)
+    # (one bf16 rounding of an fp32 accumulation); deq(x) quantises x's rows
+    deq = lambda v: oracle.mx_dequantize(*oracle.mx_quantize(v))
     dHf = host_f32(out["dR"])
-    dA_host = deq(oracle.quantize_rows(dHf)) @ deq(oracle.quantize_rows(x["W1"].f32)).T
+    dA_host = deq(dHf) @ deq(x["W1"].f32).T
     assert max_rel(host_f32(out["dA"]), dA_host) <= 2.0 ** -8
-    dW1_host = deq(oracle.quantize_cols_transposed(x["A"].f32)) @ deq(oracle.quantize_cols_transposed(dHf)).T
+    dW1_host = deq(x["A"].f32.T) @ deq(dHf.T).T
     assert max_rel(host_f32(out["dW1"]), dW1_host) <= 2.0 ** -8
     xn = round_to("bf16", (H.astype(np.float32) * r.astype(np.float32)[:, None]).astype(np.float32)
                   * x["g"].f32[None, :])
-    dW2_host = deq(oracle.quantize_cols_transposed(xn)) @ deq(oracle.quantize_cols_transposed(x["dY"].f32)).T
+    dW2_host = deq(xn.T) @ deq(x["dY"].f32.T).T
     assert max_rel(host_f32(out["dW2"]), dW2_host) <= 2.0 ** -8
     # repeat calls are bit-identical
     again = coda.fused_backward_fp8(d["dY"], d["A"], d["W1"], d["g"], d["W2"], d["H"], d["r"])
@@ -583,3 +585,85 @@ def test_fp8_backward_empty_batch():
     torch.cuda.synchronize()
     assert torch.count_nonzero(dW1).item() == 0 and torch.count_nonzero(dW2).item() == 0
     assert torch.count_nonzero(dg).item() == 0
+
+
+
+def _mx_expected_bytes(E, rows, cols):
+    """The whole exponent array (uint8 [G, B, 2, 32, 4, 4]) the quantiser
+    writes for block exponents E [rows, ceil(cols / 32)]: 127 everywhere a
+    block lies past the end or a row is padding."""
+    Eb = np.full((-(-cols // 256), -(-rows // 128), 2, 32, 4, 4), 127, dtype=np.uint8)
+    for b in range(E.shape[1]):
+        _put(Eb, rows, b, E[:, b] + 127)
+    return Eb
+
+
+@pytest.mark.parametrize("shape", [(16, 16), (48, 272), (272, 528), (528, 48), (1040, 4096), (64, 28672)], ids=str)
+def test_quantize_mx_bit_exact(shape):
+    # the MX quantiser, both ways from one read, against the oracle's
+    # mx_quantize of X (row codes) and of X^T (column codes), every exponent
+    # byte included; one-way calls give the same arrays
+    M, N = shape
+    rng = np.random.default_rng(M * 7 + N)
+    x = (rng.standard_normal((M, N)).astype(np.float32) * np.exp(rng.uniform(-9, 9, size=(M, 1))).astype(np.float32)
+         * np.exp(rng.uniform(-5, 5, size=(1, N))).astype(np.float32))
+    x[1, :] = 0.0                                   # all-zero blocks: E = 0
+    x[:, 2] = 0.0
+    x[M - 1, N - 1] = -3e4
+    x[3, :] *= np.float32(1e-40) / np.abs(x[3]).max()   # subnormal blocks
+    x[0, :17] = 448.0                               # exactly 448: E = 0, code 0x7E
+    dx, xf = _bf16_dev(x)
+    Xr8p, Er, Xc8p, Ec = coda.quantize_mx_e4m3_packed(dx)
+    torch.cuda.synchronize()
+    r_codes, r_E = oracle.mx_quantize(xf)
+    c_codes, c_E = oracle.mx_quantize(np.ascontiguousarray(xf.T))
+    np.testing.assert_array_equal(coda.unpack_e4m3(Xr8p, M).cpu().numpy(), r_codes)
+    np.testing.assert_array_equal(Er.cpu().numpy(), _mx_expected_bytes(r_E, M, N))
+    np.testing.assert_array_equal(coda.unpack_e4m3(Xc8p, N).cpu().numpy(), c_codes)
+    np.testing.assert_array_equal(Ec.cpu().numpy(), _mx_expected_bytes(c_E, N, M))
+    np.testing.assert_array_equal(coda.mx_exponents_of(Er, M, N).cpu().numpy(), r_E)
+    R8, E1, none1, none2 = coda.quantize_mx_e4m3_packed(dx, cols=False)
+    none3, none4, C8, E2 = coda.quantize_mx_e4m3_packed(dx, rows=False)
+    torch.cuda.synchronize()
+    assert none1 is None and none2 is None and none3 is None and none4 is None
+    assert torch.equal(R8, Xr8p) and torch.equal(E1, Er) and torch.equal(C8, Xc8p) and torch.equal(E2, Ec)
+
+
+def test_fp8_backward_block_scaled_inputs():
+    # dY, A, W1 and W2 multiplied by 2^k, k fixed on each 32 x 32 block and
+    # varying from block to block over [-8, 8]: every block exponent of every
+    # product operand differs from its neighbours' along both directions, so
+    # an exponent applied to the wrong block (of A or of B, along the
+    # contraction or across the rows) moves results by powers of two.  The
+    # oracle sees the same scaled values.
+    wl = ci.custom_workload(272, 160, 272, 528, wl_id=512)
+    x = ci.make_inputs(wl, seed=7, with_dy=True)
+    rng = np.random.default_rng(12)
+    for k in ("dY", "A", "W1", "W2"):
+        v = x[k].f32
+        kr = rng.integers(-4, 5, size=-(-v.shape[0] // 32))
+        kc = rng.integers(-4, 5, size=-(-v.shape[1] // 32))
+        f = np.ldexp(np.float32(1.0), (kr[:, None] + kc[None, :])).astype(np.float32)
+        f = np.repeat(np.repeat(f, 32, axis=0), 32, axis=1)[:v.shape[0], :v.shape[1]]
+        x[k] = ci.HostTensor(v * f, "bf16")          # exact: a power of two times a bf16 value
+    ref = oracle.forward(x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps)
+    H_bits = ci.bf16_bits(ref["H"].astype(np.float32))
+    H = ci.bf16_bits_to_f32(H_bits).astype(np.float64)
+    r = ref["r"].astype(np.float32)
+    d = {k: dev(v) for k, v in x.items()}
+    dH_ = torch.from_numpy(H_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    grads = coda.fused_backward_fp8(d["dY"], d["A"], d["W1"], d["g"], d["W2"], dH_, torch.from_numpy(r).cuda())
+    torch.cuda.synchronize()
+    out = dict(zip(GRADS8, grads))
+    orc = oracle.backward_fp8(x["dY"].f32, x["A"].f32, x["W1"].f32, x["R"].f32, x["g"].f32, x["W2"].f32, wl.eps,
+                              H=H, r=r.astype(np.float64))
+    errs = {k: max_rel(host_f32(out[k]), orc[k]) for k in GRADS8}
+    print("fp8 backward, block-scaled inputs:", {k: f"{v:.2e}" for k, v in errs.items()}, file=sys.__stderr__,
+          flush=True)
+    for k in GRADS8:
+        assert errs[k] <= 1e-2, f"{k}: error {errs[k]:.3e}"
+    # the stage-wise products on the GPU's own dH, as in the test above
+    deq = lambda v: oracle.mx_dequantize(*oracle.mx_quantize(v))
+    dHf = host_f32(out["dR"])
+    assert max_rel(host_f32(out["dA"]), deq(dHf) @ deq(x["W1"].f32).T) <= 2.0 ** -8
+    assert max_rel(host_f32(out["dW1"]), deq(x["A"].f32.T) @ deq(dHf.T).T) <= 2.0 ** -8

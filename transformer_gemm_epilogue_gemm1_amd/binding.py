@@ -783,6 +783,26 @@ def quantize_rows_cols_e4m3_packed(X, stream=None):
     return X8p, sr, Xt8p, sc
 
 
+def quantize_mx_e4m3_packed(X, rows: bool = True, cols: bool = True, stream=None):
+    """MX e4m3 codes of a bf16 X [M, N] with one block exponent per 32
+    elements: along the rows (Xr8p [M, N] tile-packed, Er = mx_exp_empty(M,
+    N)) and / or along the columns (the codes of X^T, Xc8p [N, M] tile-packed,
+    Ec = mx_exp_empty(N, M)).  Returns (Xr8p, Er, Xc8p, Ec), None for a pair
+    not asked for."""
+    if not (rows or cols):
+        raise ValueError("ask for the row codes, the column codes or both")
+    M, N = X.shape
+    ldx = _mat(X, "X", torch.bfloat16, (M, N))
+    dev = X.device
+    Xr8p, Er = (packed_empty_e4m3(M, N, dev), mx_exp_empty(M, N, dev)) if rows else (None, None)
+    Xc8p, Ec = (packed_empty_e4m3(N, M, dev), mx_exp_empty(N, M, dev)) if cols else (None, None)
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    st = _lib.load().coda_quantize_mx_e4m3_packed(M, N, X.data_ptr(), ldx, ptr(Xr8p), ptr(Er), ptr(Xc8p), ptr(Ec),
+                                                  _stream(stream))
+    _lib.check("coda_quantize_mx_e4m3_packed", st)
+    return Xr8p, Er, Xc8p, Ec
+
+
 def fused_forward_fp8(A8, sa, W1t8, sw1, R, g, W2t8, sw2, eps: float, stream=None):
     """The fused chain with fp8 GEMM operands: returns (H, Hg8, Hg8_exp, r, Y,
     partials), Hg8_exp the MX block exponents of Hg8 (mx_exp_empty layout)."""

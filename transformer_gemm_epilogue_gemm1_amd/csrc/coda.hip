@@ -146,12 +146,13 @@ int64_t packed_bytes_e4m3(int64_t rows, int64_t cols) { return (rows + 15) / 16 
 int64_t mx_exp_bytes(int64_t rows, int64_t cols) { return 1024 * mx_row_blocks(rows) * ((cols + 255) / 256); }
 
 // L: OpLayout of both operands (kLayPacked: lda / ldb counting 16-byte chunks
-// per row).  MX: a_exp holds the block exponents of A (mx_byte layout,
-// mx_exp_bytes(M, K) bytes).
-template <class Epi, int L = kLayKC, bool MX = false>
+// per row).  MX: a mask of kMxA (a_exp holds the block exponents of A,
+// mx_byte layout, mx_exp_bytes(M, K) bytes) and kMxB (b_exp those of B,
+// mx_exp_bytes(N, K) bytes).
+template <class Epi, int L = kLayKC, int MX = 0>
 coda_status launch_gemm_fp8(const char* what, int M, int N, int K, const void* a, int64_t lda, const void* b,
                             int64_t ldb, const typename Epi::Params& ep, hipStream_t s,
-                            const void* a_exp = nullptr) {
+                            const void* a_exp = nullptr, const void* b_exp = nullptr) {
   GemmArgs g;
   g.M = M;
   g.N = N;
@@ -166,8 +167,10 @@ coda_status launch_gemm_fp8(const char* what, int M, int N, int K, const void* a
   g.ldb = ldb;
   g.b_span = L == kLayPacked ? (uint32_t)packed_bytes_e4m3(N, 16 * ldb) : span_bytes(N, K, ldb, 1);
   g.b_split = 0;
-  const MxArgs mx{(const uint8_t*)a_exp, M, (uint32_t)mx_exp_bytes(M, K)};
-  hipLaunchKernelGGL((gemm_fp8_kernel<Epi, L, MX>), dim3(g.tiles_m * g.tiles_n), dim3(kThreads), 0, s, g, ep, mx);
+  const MxArgs mxa{(const uint8_t*)a_exp, M, (uint32_t)mx_exp_bytes(M, K)};
+  const MxArgs mxb{(const uint8_t*)b_exp, N, (uint32_t)mx_exp_bytes(N, K)};
+  hipLaunchKernelGGL((gemm_fp8_kernel<Epi, L, MX>), dim3(g.tiles_m * g.tiles_n), dim3(kThreads), 0, s, g, ep, mxa,
+                     mxb);
   return launch_status(what);
 }
 
@@ -344,10 +347,11 @@ coda_status chain_bwd_impl(int M, int K, int D, int N2, const void* dY, const vo
 }
 
 // Workspace of the fp8 backward: the bf16 backward's (X_n, partial sums, c)
-// followed by the e4m3 operands of the four products and their scales.
+// followed by the e4m3 operands of the four products (tile-packed codes) and
+// their block exponents (mx_byte layout).
 struct Bwd8Ws {
   BwdWs b;
-  size_t dy8, sdy, dyt8, sdyt, w2q, sw2, w1q, sw1, dh8, sdh, dht8, sdht, xnt8, sxn, at8, sat, total;
+  size_t dy8, edy, dyt8, edyt, w2q, ew2, w1q, ew1, dh8, edh, dht8, edht, xnt8, exn, at8, eat, total;
   Bwd8Ws(int64_t M, int64_t K, int64_t D, int64_t N2) : b(M, 0, D, 0, 2) {
     size_t o = b.total;
     auto take = [&o](int64_t bytes) {
@@ -355,22 +359,22 @@ struct Bwd8Ws {
       o = align_up(o + (size_t)bytes);
       return at;
     };
-    dy8 = take(M * N2);
-    sdy = take(M * 4);
-    dyt8 = take(N2 * M);
-    sdyt = take(N2 * 4);
-    w2q = take(D * N2);
-    sw2 = take(D * 4);
-    w1q = take(K * D);
-    sw1 = take(K * 4);
-    dh8 = take(M * D);
-    sdh = take(M * 4);
-    dht8 = take(D * M);
-    sdht = take(D * 4);
-    xnt8 = take(D * M);
-    sxn = take(D * 4);
-    at8 = take(K * M);
-    sat = take(K * 4);
+    dy8 = take(M * N2);                  // dY, rows (G's A)
+    edy = take(mx_exp_bytes(M, N2));
+    dyt8 = take(N2 * M);                 // dY^T (dW2's B)
+    edyt = take(mx_exp_bytes(N2, M));
+    w2q = take(D * N2);                  // W2 [D, N2], rows (G's B)
+    ew2 = take(mx_exp_bytes(D, N2));
+    w1q = take(K * D);                   // W1 [K, D], rows (dA's B)
+    ew1 = take(mx_exp_bytes(K, D));
+    dh8 = take(M * D);                   // dH, rows (dA's A)
+    edh = take(mx_exp_bytes(M, D));
+    dht8 = take(D * M);                  // dH^T (dW1's B)
+    edht = take(mx_exp_bytes(D, M));
+    xnt8 = take(D * M);                  // X_n^T (dW2's A)
+    exn = take(mx_exp_bytes(D, M));
+    at8 = take(K * M);                   // A^T (dW1's A)
+    eat = take(mx_exp_bytes(K, M));
     total = o;
   }
 };
@@ -424,8 +428,24 @@ void q_rows_cols(const void* X, int64_t ldx, int M, int N, void* X8, int64_t ldx
   hipLaunchKernelGGL(amax_to_scale_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, sc, N);
 }
 
-// The chain's backward with every product on e4m3 operands quantised along
-// its contraction (bf16 tensors in and out); the per-element steps are the
+// MX quantisation of X [M, N] (bf16) along its rows (Xr8, Er) and/or along
+// its columns (Xc8 = the codes of X^T, Ec), tile-packed; a pair left null is
+// not produced.  M % 16 == 0, N % 16 == 0, ceil(N / 256) <= 65535.
+void q_mx(const void* X, int64_t ldx, int M, int N, void* Xr8, void* Er, void* Xc8, void* Ec, hipStream_t s) {
+  const dim3 grid((unsigned)((256 / kMxTileRows) * ((M + 255) / 256)), (unsigned)((N + 255) / 256)), block(256);
+  const uint16_t* x = (const uint16_t*)X;
+  uint8_t *r8 = (uint8_t*)Xr8, *er = (uint8_t*)Er, *c8 = (uint8_t*)Xc8, *ec = (uint8_t*)Ec;
+  if (Xr8 != nullptr && Xc8 != nullptr)
+    hipLaunchKernelGGL((mx_quantize_kernel<true, true>), grid, block, 0, s, x, ldx, M, N, r8, er, c8, ec);
+  else if (Xr8 != nullptr)
+    hipLaunchKernelGGL((mx_quantize_kernel<true, false>), grid, block, 0, s, x, ldx, M, N, r8, er, c8, ec);
+  else
+    hipLaunchKernelGGL((mx_quantize_kernel<false, true>), grid, block, 0, s, x, ldx, M, N, r8, er, c8, ec);
+}
+
+// The chain's backward with every product on e4m3 operands with MX block
+// exponents along its contraction (bf16 tensors in and out); the products
+// apply the exponents of both operands, and the per-element steps are the
 // bf16 backward's.  M > 0, all sizes multiples of 16.  Every code array is
 // written tile-packed (no padding rows, since all row counts are multiples of
 // 16), so all four products read both operands in the packed layout.
@@ -437,20 +457,19 @@ coda_status chain_bwd_fp8_impl(int M, int K, int D, int N2, const void* dY, cons
   float* srow = (float*)(ws + L.b.srow);
   float* dgcol = (float*)(ws + L.b.dgcol);
   float* c = (float*)(ws + L.b.c);
-  auto f = [ws](size_t o) { return (float*)(ws + o); };
   const int Tn = (int)num_partials(D), U = (M + kWaveM - 1) / kWaveM;
   coda_status st;
+  char* const w = ws;
   // operands of G = dY W2^T (rows) and dW2 = X_n^T dY (dY's columns)
-  q_rows_cols(dY, N2, M, N2, ws + L.dy8, N2, f(L.sdy), ws + L.dyt8, M, f(L.sdyt), s, N2 / 16, M / 16);
-  q_rows(W2, N2, D, N2, ws + L.w2q, N2, f(L.sw2), s, N2 / 16);
-  q_rows(W1, D, K, D, ws + L.w1q, D, f(L.sw1), s, D / 16);
+  q_mx(dY, N2, M, N2, w + L.dy8, w + L.edy, w + L.dyt8, w + L.edyt, s);
+  q_mx(W2, N2, D, N2, w + L.w2q, w + L.ew2, nullptr, nullptr, s);
+  q_mx(W1, D, K, D, w + L.w1q, w + L.ew1, nullptr, nullptr, s);
   if ((st = launch_status("coda_chain_bwd_fp8 quantise dY, W1, W2")) != CODA_OK) return st;
-  // 1. G with the P / X_n / partial-sum epilogue, after dequantisation
-  using EpiG = EpiDequant<EpiBwdG<uint16_t>>;
-  typename EpiG::Params eg{f(L.sdy), f(L.sw2), {(const uint16_t*)H, (const uint16_t*)g, r, (uint16_t*)dR, Xn, D,
-                                                srow, dgcol}};
-  if ((st = launch_gemm_fp8<EpiG, kLayPacked>("coda_chain_bwd_fp8 G", M, D, N2, ws + L.dy8, N2 / 16, ws + L.w2q, N2 / 16,
-                                        eg, s)) !=
+  // 1. G with the P / X_n / partial-sum epilogue
+  using EpiG = EpiBwdG<uint16_t>;
+  const typename EpiG::Params eg{(const uint16_t*)H, (const uint16_t*)g, r, (uint16_t*)dR, Xn, D, srow, dgcol};
+  if ((st = launch_gemm_fp8<EpiG, kLayPacked, kMxA | kMxB>("coda_chain_bwd_fp8 G", M, D, N2, w + L.dy8, N2 / 16,
+                                                           w + L.w2q, N2 / 16, eg, s, w + L.edy, w + L.ew2)) !=
       CODA_OK)
     return st;
   // 2. c and dg;  3. dH in place in dR
@@ -461,23 +480,24 @@ coda_status chain_bwd_fp8_impl(int M, int K, int D, int N2, const void* dY, cons
   hipLaunchKernelGGL(dh_finalize_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, (uint16_t*)dR, (const uint16_t*)H,
                      r, c, D, nchunks);
   // operands of dA = dH W1^T (dH rows), dW1 = A^T dH and dW2 = X_n^T dY (columns)
-  q_rows_cols(dR, D, M, D, ws + L.dh8, D, f(L.sdh), ws + L.dht8, M, f(L.sdht), s, D / 16, M / 16);
-  q_cols(Xn, D, M, D, ws + L.xnt8, M, f(L.sxn), s, M / 16);
-  q_cols(A, K, M, K, ws + L.at8, M, f(L.sat), s, M / 16);
+  q_mx(dR, D, M, D, w + L.dh8, w + L.edh, w + L.dht8, w + L.edht, s);
+  q_mx(Xn, D, M, D, nullptr, nullptr, w + L.xnt8, w + L.exn, s);
+  q_mx(A, K, M, K, nullptr, nullptr, w + L.at8, w + L.eat, s);
   if ((st = launch_status("coda_chain_bwd_fp8 combine, dH, quantise")) != CODA_OK) return st;
-  using EpiO = EpiDequant<EpiRowScale<uint16_t>>;
+  using EpiO = EpiRowScale<uint16_t>;
   // 4. dA = dH W1^T
-  if ((st = launch_gemm_fp8<EpiO, kLayPacked>("coda_chain_bwd_fp8 dA", M, K, D, ws + L.dh8, D / 16, ws + L.w1q, D / 16,
-                                  typename EpiO::Params{f(L.sdh), f(L.sw1), {nullptr, (uint16_t*)dA, K}}, s)) !=
-      CODA_OK)
+  if ((st = launch_gemm_fp8<EpiO, kLayPacked, kMxA | kMxB>("coda_chain_bwd_fp8 dA", M, K, D, w + L.dh8, D / 16,
+                                                           w + L.w1q, D / 16, typename EpiO::Params{nullptr, (uint16_t*)dA, K},
+                                                           s, w + L.edh, w + L.ew1)) != CODA_OK)
     return st;
   // 5. dW1 = A^T dH;  6. dW2 = X_n^T dY  (contraction over the M rows)
-  if ((st = launch_gemm_fp8<EpiO, kLayPacked>("coda_chain_bwd_fp8 dW1", K, D, M, ws + L.at8, M / 16, ws + L.dht8, M / 16,
-                                  typename EpiO::Params{f(L.sat), f(L.sdht), {nullptr, (uint16_t*)dW1, D}}, s)) !=
-      CODA_OK)
+  if ((st = launch_gemm_fp8<EpiO, kLayPacked, kMxA | kMxB>("coda_chain_bwd_fp8 dW1", K, D, M, w + L.at8, M / 16,
+                                                           w + L.dht8, M / 16, typename EpiO::Params{nullptr, (uint16_t*)dW1, D},
+                                                           s, w + L.eat, w + L.edht)) != CODA_OK)
     return st;
-  return launch_gemm_fp8<EpiO, kLayPacked>("coda_chain_bwd_fp8 dW2", D, N2, M, ws + L.xnt8, M / 16, ws + L.dyt8, M / 16,
-                               typename EpiO::Params{f(L.sxn), f(L.sdyt), {nullptr, (uint16_t*)dW2, N2}}, s);
+  return launch_gemm_fp8<EpiO, kLayPacked, kMxA | kMxB>("coda_chain_bwd_fp8 dW2", D, N2, M, w + L.xnt8, M / 16,
+                                                        w + L.dyt8, M / 16, typename EpiO::Params{nullptr, (uint16_t*)dW2, N2},
+                                                        s, w + L.exn, w + L.edyt);
 }
 
 // Shared checks of the RoPE entry points: head layout, positions, table.
@@ -945,7 +965,7 @@ coda_status coda_gemm_rowscale_fp8(int64_t M, int64_t D, int64_t N2, const void*
   if ((st = check_alias(&mY, 1, ins, 5)) != CODA_OK) return st;
   EpiRowScaleFp8::Params ep{r, sw2, (uint16_t*)Y, ldy};
   if (x_exp != nullptr)
-    return launch_gemm_fp8<EpiRowScaleFp8, kLayKC, true>("coda_gemm_rowscale_fp8", (int)M, (int)N2, (int)D, X8, ldx,
+    return launch_gemm_fp8<EpiRowScaleFp8, kLayKC, kMxA>("coda_gemm_rowscale_fp8", (int)M, (int)N2, (int)D, X8, ldx,
                                                          W2t8, ldw2t, ep, (hipStream_t)stream, x_exp);
   return launch_gemm_fp8<EpiRowScaleFp8>("coda_gemm_rowscale_fp8", (int)M, (int)N2, (int)D, X8, ldx, W2t8, ldw2t,
                                          ep, (hipStream_t)stream);
@@ -1012,6 +1032,38 @@ coda_status coda_quantize_rows_cols_e4m3_packed(int64_t M, int64_t N, const void
   return launch_status("coda_quantize_rows_cols_e4m3_packed");
 }
 
+coda_status coda_quantize_mx_e4m3_packed(int64_t M, int64_t N, const void* X, int64_t ldx, void* Xr8p, void* Er,
+                                         void* Xc8p, void* Ec, void* stream) {
+  coda_status st = check_dims_fp8(M, {{"N", N}});
+  if (st != CODA_OK) return st;
+  if (M % 16 != 0) return fail(CODA_ERR_SHAPE, "M = %lld is not a multiple of 16", (long long)M);
+  if ((N + 255) / 256 > 65535) return fail(CODA_ERR_SHAPE, "N = %lld exceeds %d columns", (long long)N, 65535 * 256);
+  if ((Xr8p == nullptr) != (Er == nullptr) || (Xc8p == nullptr) != (Ec == nullptr))
+    return fail(CODA_ERR_NULL, "codes and exponents come in pairs: Xr8p with Er, Xc8p with Ec");
+  if (Xr8p == nullptr && Xc8p == nullptr) return fail(CODA_ERR_NULL, "no output: set Xr8p / Er or Xc8p / Ec");
+  if (M == 0) return ok();
+  const int64_t cb = packed_bytes_e4m3(M, N), erb = mx_exp_bytes(M, N), ecb = mx_exp_bytes(N, M);
+  const Mat mX{X, M, N, ldx, 2, "X"};
+  const Mat mr{Xr8p, 1, cb, cb, 1, "Xr8p"}, mer{Er, 1, erb, erb, 1, "Er"};
+  const Mat mc{Xc8p, 1, cb, cb, 1, "Xc8p"}, mec{Ec, 1, ecb, ecb, 1, "Ec"};
+  if ((st = check_mat(mX, 8)) != CODA_OK) return st;
+  const Mat none{nullptr, 0, 0, 0, 1, ""};
+  Mat outs[4] = {none, none, none, none};
+  if (Xr8p != nullptr) {
+    if ((st = check_mat(mr, 16)) != CODA_OK || (st = check_mat(mer, 16)) != CODA_OK) return st;
+    outs[0] = mr;
+    outs[1] = mer;
+  }
+  if (Xc8p != nullptr) {
+    if ((st = check_mat(mc, 16)) != CODA_OK || (st = check_mat(mec, 16)) != CODA_OK) return st;
+    outs[2] = mc;
+    outs[3] = mec;
+  }
+  if ((st = check_alias(outs, 4, &mX, 1)) != CODA_OK) return st;
+  q_mx(X, ldx, (int)M, (int)N, Xr8p, Er, Xc8p, Ec, (hipStream_t)stream);
+  return launch_status("coda_quantize_mx_e4m3_packed");
+}
+
 coda_status coda_gemm_res_prms_fp8_packed(int64_t M, int64_t K, int64_t D, const void* A8, int64_t lda,
                                           const float* sa, const void* W1t8, int64_t ldw1t, const float* sw1,
                                           const void* R, int64_t ldr, const void* g, void* H, int64_t ldh,
@@ -1064,7 +1116,7 @@ coda_status coda_gemm_rowscale_fp8_packed(int64_t M, int64_t D, int64_t N2, cons
   if ((st = check_alias(&mY, 1, ins, 5)) != CODA_OK) return st;
   EpiRowScaleFp8::Params ep{r, sw2, (uint16_t*)Y, ldy};
   if (x_exp != nullptr)
-    return launch_gemm_fp8<EpiRowScaleFp8, kLayPacked, true>("coda_gemm_rowscale_fp8_packed", (int)M, (int)N2,
+    return launch_gemm_fp8<EpiRowScaleFp8, kLayPacked, kMxA>("coda_gemm_rowscale_fp8_packed", (int)M, (int)N2,
                                                              (int)D, X8p, D / 16, W2t8p, D / 16, ep,
                                                              (hipStream_t)stream, x_exp);
   return launch_gemm_fp8<EpiRowScaleFp8, kLayPacked>("coda_gemm_rowscale_fp8_packed", (int)M, (int)N2, (int)D, X8p,
@@ -1369,6 +1421,9 @@ coda_status coda_chain_bwd_fp8(int64_t M, int64_t K, int64_t D, int64_t N2, cons
   if (st != CODA_OK) return st;
   if (M % 16 != 0) return fail(CODA_ERR_SHAPE, "M = %lld is not a multiple of 16", (long long)M);
   if (M > kMaxColRows) return fail(CODA_ERR_SHAPE, "M = %lld exceeds %lld rows", (long long)M, (long long)kMaxColRows);
+  for (const auto& d : {std::make_pair("K", K), std::make_pair("D", D), std::make_pair("N2", N2)})
+    if ((d.second + 255) / 256 > 65535)  // the MX quantiser's grid of 256-column tiles
+      return fail(CODA_ERR_SHAPE, "%s = %lld exceeds %d", d.first, (long long)d.second, 65535 * 256);
   const Mat mdY{dY, M, N2, N2, 2, "dY"}, mA{A, M, K, K, 2, "A"}, mH{H, M, D, D, 2, "H"};
   const Mat mdA{dA, M, K, K, 2, "dA"}, mdR{dR, M, D, D, 2, "dR"};
   const Mat mW1{W1, K, D, D, 2, "W1"}, mg{g, 1, D, D, 2, "g"}, mW2{W2, D, N2, N2, 2, "W2"};

@@ -50,55 +50,82 @@ __device__ __forceinline__ void mac8(f32x16& acc, const i32x8& a, const i32x8& b
   acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
 }
 
-// The same product with a block scale on A: contraction block h of row i
-// (k-tile bytes [32 h, 32 h + 32), the half-h registers of lanes i and
-// 32 + i) is multiplied by 2^(b - 127), b the byte SEL of lane 32 h + i's
-// sc (an E8M0 exponent); B is unscaled (127 = 2^0).
-template <int SEL>
-__device__ __forceinline__ void mac8_mx(f32x16& acc, const i32x8& a, const i32x8& b, uint32_t sc) {
-  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, SEL, (int)sc, 0, 127);
-}
+// Which operands carry block exponents (MX): a mask of these bits.
+constexpr int kMxA = 1, kMxB = 2;
 
-// Block exponents of an A operand (E8M0 bytes in the mx_byte layout of
-// tile_map.hpp, as the first GEMM's fp8 epilogue writes them).  Lane l
-// supplies, per A fragment mt, the scales of row base + 32 mt + l % 32 for
-// block l / 32; the layout puts the 4 fragments' dwords of a lane (one byte
-// per k-tile of a group) in 16 consecutive bytes, so a group costs the lane
-// one 16-byte load, and the wavefront reads 1 KiB of consecutive memory.
-// (With one dword load per fragment the scaled GEMM ran 3.5% slower than
-// with the exponents recycled in registers, wherever the dwords lay.)
-// Wavefronts whose rows all lie past M read 0 through the buffer
-// descriptor's range check.
+// The same product with block scales: contraction block h of A's row i (the
+// k-tile's bytes [32 h, 32 h + 32), the half-h registers of lanes i and
+// 32 + i) is multiplied by 2^(a - 127), a the byte SEL of lane 32 h + i's
+// sa; block h of B's row j (output column j) likewise by the byte SEL of
+// lane 32 h + j's sb.  An unscaled operand passes 0x7F7F7F7F (2^0 in every
+// byte).
+template <int SEL>
+__device__ __forceinline__ void mac8_mx(f32x16& acc, const i32x8& a, const i32x8& b, uint32_t sa, uint32_t sb) {
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, SEL, (int)sa, SEL, (int)sb);
+}
+constexpr uint32_t kMxUnit = 0x7F7F7F7Fu;
+
+// Block exponents of an operand (E8M0 bytes in the mx_byte layout of
+// tile_map.hpp, as the first GEMM's fp8 epilogue and the MX quantiser write
+// them).  Lane l supplies, per fragment f of the wavefront's rows, the
+// scales of row row0 + 32 f + l % 32 for block l / 32.  The layout puts the
+// dwords of the 4 fragments of a 128-row block in a lane's 16 consecutive
+// bytes (one byte per k-tile of a group of 4): an A wavefront (128 rows, 4
+// fragments) loads all 16, a B wavefront (64 rows, 2 fragments, half of a
+// 128-row block) the 8 of its half.  A group costs the lane one load; the
+// wavefront reads 1 KiB (A) or 512 bytes (B) of consecutive memory.  (With
+// one dword load per fragment the scaled GEMM ran 3.5% slower than with the
+// exponents recycled in registers, wherever the dwords lay.)  Wavefronts
+// whose rows all lie past the operand's end read 0 through the buffer
+// descriptor's range check; their products are never stored.
 struct MxArgs {
   const uint8_t* e;  // null: the operand is unscaled
-  int64_t M;         // rows of the array (the GEMM's M)
+  int64_t M;         // rows of the array (the operand's rows: the GEMM's M for A, N for B)
   uint32_t span;     // bytes of the array
 };
 
+template <int NF>
 struct MxReader {
+  static_assert(NF == 4 || NF == 2, "a wavefront's operand rows are 4 or 2 fragments");
   static constexpr int kLoads = 1;  // vector memory instructions per load() (the barrier counts them)
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t off;    // byte offset of the lane's 16 bytes of group 0, or kOutOfRange
+  uint32_t off;    // byte offset of the lane's dwords of group 0, or kOutOfRange
   uint32_t gstep;  // bytes between groups
-  __device__ __forceinline__ void init(const MxArgs& mx, int row0, int M, int lane) {
+  // row0: the wavefront's first operand row (a multiple of 32 NF)
+  __device__ __forceinline__ void init(const MxArgs& mx, int row0, int lane) {
     rsrc = make_rsrc(mx.e, mx.span);
     gstep = (uint32_t)(1024 * mx_row_blocks(mx.M));
-    off = row0 < M ? (uint32_t)mx_byte(row0 + (lane & 31), 0, lane >> 5, mx.M) : kOutOfRange;
+    off = row0 < mx.M ? (uint32_t)mx_byte(row0 + (lane & 31), 0, lane >> 5, mx.M) : kOutOfRange;
   }
   // group grp's dwords; a group past the last one reads 0 (past the array)
-  __device__ __forceinline__ void load(int grp, uint32_t (&out)[kFrag8M]) const {
-    static_assert(kFrag8M == 4, "one 16-byte load holds the 4 fragments' dwords");
-    const u32x4 v = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(off + gstep * (uint32_t)grp), 0, 0));
+  __device__ __forceinline__ void load(int grp, uint32_t (&out)[NF]) const {
+    const int o = (int)(off + gstep * (uint32_t)grp);
+    if constexpr (NF == 4) {
+      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, o, 0, 0));
 #pragma unroll
-    for (int mt = 0; mt < kFrag8M; ++mt) out[mt] = v[mt];
+      for (int f = 0; f < 4; ++f) out[f] = v[f];
+    } else {
+      const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsrc, o, 0, 0));
+      out[0] = v[0];
+      out[1] = v[1];
+    }
   }
 };
 
 // Block exponents held across a group of 4 k-tiles: cur for the group being
 // multiplied, nxt for the next one, loaded during the group's first step.
+template <int NF>
 struct MxRegs {
-  uint32_t cur[kFrag8M], nxt[kFrag8M];
+  uint32_t cur[NF], nxt[NF];
+};
+
+// The exponent readers and registers of both operands (those not scaled stay
+// unused).
+struct MxState {
+  MxReader<kFrag8M> ra;
+  MxReader<kFrag8N> rb;
+  MxRegs<kFrag8M> a;
+  MxRegs<kFrag8N> b;
 };
 
 constexpr int kDmaIssueAfter8 = 1;
@@ -113,26 +140,32 @@ struct Frags8 {
 // after the products of A fragment kDmaIssueAfter8 (4 products, 256
 // matrix-core cycles, as in the bf16 step).
 //
-// MX (A block-scaled): k-tile kt uses byte kt % 4 = S of the group's
-// exponent dwords.  The first step of a group moves the prefetched dwords
-// into use and, behind the direct loads, loads the next group's (NEXT: the
-// steps after the main loop belong to the last group and load none); its
-// barrier then allows that load in flight as well (it has a whole group of
-// steps to land).  The barrier's count must equal the instructions issued
-// after the direct loads: a larger one lets the oldest tile's loads through
-// unlanded.
-template <int S, int L = kLayKC, bool MX = false, bool NEXT = true>
+// MX (a mask of kMxA, kMxB: the operands that are block-scaled): k-tile kt
+// uses byte kt % 4 = S of the group's exponent dwords.  The first step of a
+// group moves the prefetched dwords into use and, behind the direct loads,
+// loads the next group's (NEXT: the steps after the main loop belong to the
+// last group and load none); its barrier then allows those loads in flight
+// as well (they have a whole group of steps to land).  The barrier's count
+// must equal the instructions issued after the direct loads: a larger one
+// lets the oldest tile's loads through unlanded.
+template <int S, int L = kLayKC, int MX = 0, bool NEXT = true>
 __device__ __forceinline__ void kstep8(char* const (&st)[kStages], const Dma<uint8_t, true, L>& da,
                                        const Dma<uint8_t, true, L>& db, FragReader8<lds_packed(L)>& ra,
                                        FragReader8<lds_packed(L)>& rb,
                                        f32x16 (&acc)[kFrag8M][kFrag8N], Frags8& cur, int kt, int K, int wave,
-                                       const MxReader& mr, MxRegs& ms) {
+                                       MxState& ms) {
+  constexpr bool MA = (MX & kMxA) != 0, MB = (MX & kMxB) != 0;
+  constexpr int kMxLoads = (MA ? MxReader<kFrag8M>::kLoads : 0) + (MB ? MxReader<kFrag8N>::kLoads : 0);
   constexpr int SL = (S + kStages - 1) % kStages;
   constexpr int SN = (S + 1) % kStages;
-  static_assert(!MX || kStages == 4, "a group of exponent bytes is one pass over the four stages");
-  if constexpr (MX && S == 0) {
+  static_assert(MX == 0 || kStages == 4, "a group of exponent bytes is one pass over the four stages");
+  if constexpr (MA && S == 0) {
 #pragma unroll
-    for (int mt = 0; mt < kFrag8M; ++mt) ms.cur[mt] = ms.nxt[mt];
+    for (int mt = 0; mt < kFrag8M; ++mt) ms.a.cur[mt] = ms.a.nxt[mt];
+  }
+  if constexpr (MB && S == 0) {
+#pragma unroll
+    for (int nt = 0; nt < kFrag8N; ++nt) ms.b.cur[nt] = ms.b.nxt[nt];
   }
   ra.refresh();
   rb.refresh();
@@ -144,8 +177,8 @@ __device__ __forceinline__ void kstep8(char* const (&st)[kStages], const Dma<uin
   for (int mt = 0; mt < kFrag8M; ++mt) {
 #pragma unroll
     for (int nt = 0; nt < kFrag8N; ++nt) {
-      if constexpr (MX)
-        mac8_mx<S>(acc[mt][nt], cur.a[mt], cur.b[nt], ms.cur[mt]);
+      if constexpr (MX != 0)
+        mac8_mx<S>(acc[mt][nt], cur.a[mt], cur.b[nt], MA ? ms.a.cur[mt] : kMxUnit, MB ? ms.b.cur[nt] : kMxUnit);
       else
         mac8(acc[mt][nt], cur.a[mt], cur.b[nt]);
     }
@@ -153,14 +186,15 @@ __device__ __forceinline__ void kstep8(char* const (&st)[kStages], const Dma<uin
     if (mt == kDmaIssueAfter8) {
       da.issue(st[SL], kt + kStages - 1, K, wave);
       db.issue(st[SL] + kOperandBytes, kt + kStages - 1, K, wave);
-      if constexpr (MX && S == 0 && NEXT) mr.load(kt / 4 + 1, ms.nxt);
+      if constexpr (MA && S == 0 && NEXT) ms.ra.load(kt / 4 + 1, ms.a.nxt);
+      if constexpr (MB && S == 0 && NEXT) ms.rb.load(kt / 4 + 1, ms.b.nxt);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int nt = 0; nt < kFrag8N; ++nt) cur.b[nt] = nb[nt];
-  if constexpr (MX && S == 0 && NEXT)
-    stage_barrier_n<kLoadsPerTile + MxReader::kLoads>();
+  if constexpr (MX != 0 && S == 0 && NEXT)
+    stage_barrier_n<kLoadsPerTile + kMxLoads>();
   else
     stage_barrier();
 }
@@ -170,11 +204,12 @@ __device__ __forceinline__ void kstep8(char* const (&st)[kStages], const Dma<uin
 // finish).
 // L: OpLayout of both operands (kLayPacked: tile-packed, kp_unit, with g.lda /
 // g.ldb counting 16-byte chunks per row).
-// MX: A carries block exponents (mx, MxReader's layout) that the products
-// apply; otherwise mx is unused.
-template <class Epi, int L = kLayKC, bool MX = false>
+// MX: a mask of kMxA, kMxB, the operands that carry block exponents (mxa,
+// mxb, MxReader's layout) that the products apply; the others' MxArgs are
+// unused.
+template <class Epi, int L = kLayKC, int MX = 0>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_fp8_kernel(
-    GemmArgs g, typename Epi::Params ep, MxArgs mx) {
+    GemmArgs g, typename Epi::Params ep, MxArgs mxa, MxArgs mxb) {
   static_assert(kStages == 4, "the stage arrays and the unrolled steps below assume four stages");
   __shared__ __attribute__((aligned(1024))) char st0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char st1[kStageBytes];
@@ -202,11 +237,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int nk = (g.K + KTE - 1) / KTE;
-  MxReader mr;
-  MxRegs ms;
-  if constexpr (MX) {
-    mr.init(mx, m0 + wm * kWaveM, g.M, lane);
-    mr.load(0, ms.nxt);  // landed by the prologue's wait below
+  MxState ms;
+  if constexpr ((MX & kMxA) != 0) {
+    ms.ra.init(mxa, m0 + wm * kWaveM, lane);
+    ms.ra.load(0, ms.a.nxt);  // landed by the prologue's wait below
+  }
+  if constexpr ((MX & kMxB) != 0) {
+    ms.rb.init(mxb, n0 + wn * kWaveN, lane);
+    ms.rb.load(0, ms.b.nxt);
   }
 #pragma unroll
   for (int t = 0; t < kStages - 1; ++t) {
@@ -222,15 +260,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int nt = 0; nt < kFrag8N; ++nt) cur.b[nt] = rb.read(st[0] + kOperandBytes, nt);
   int kt = 0;
   for (; kt + kStages <= nk; kt += kStages) {
-    kstep8<0, L, MX>(st, da, db, ra, rb, acc, cur, kt, g.K, wave, mr, ms);
-    kstep8<1, L, MX>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave, mr, ms);
-    kstep8<2, L, MX>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave, mr, ms);
-    kstep8<3, L, MX>(st, da, db, ra, rb, acc, cur, kt + 3, g.K, wave, mr, ms);
+    kstep8<0, L, MX>(st, da, db, ra, rb, acc, cur, kt, g.K, wave, ms);
+    kstep8<1, L, MX>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave, ms);
+    kstep8<2, L, MX>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave, ms);
+    kstep8<3, L, MX>(st, da, db, ra, rb, acc, cur, kt + 3, g.K, wave, ms);
   }
   const int rem = nk - kt;
-  if (rem > 0) kstep8<0, L, MX, false>(st, da, db, ra, rb, acc, cur, kt, g.K, wave, mr, ms);
-  if (rem > 1) kstep8<1, L, MX, false>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave, mr, ms);
-  if (rem > 2) kstep8<2, L, MX, false>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave, mr, ms);
+  if (rem > 0) kstep8<0, L, MX, false>(st, da, db, ra, rb, acc, cur, kt, g.K, wave, ms);
+  if (rem > 1) kstep8<1, L, MX, false>(st, da, db, ra, rb, acc, cur, kt + 1, g.K, wave, ms);
+  if (rem > 2) kstep8<2, L, MX, false>(st, da, db, ra, rb, acc, cur, kt + 2, g.K, wave, ms);
   drain_barrier();  // no direct load may land in the LDS the epilogue reuses
 
   // ---- epilogue: slab s = rows 16 s .. 16 s + 15 of the wavefront's 128 =

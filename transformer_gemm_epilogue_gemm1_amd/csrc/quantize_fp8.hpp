@@ -314,4 +314,114 @@ __global__ __launch_bounds__(256) void amax_to_scale_kernel(float* __restrict__ 
   if (i < n) scales[i] = e4m3_scale(scales[i]);
 }
 
+// ---- MX quantisation (OCP microscaling: one E8M0 exponent per 32 elements) --
+//
+// X [M, N] (bf16) quantised along its rows and/or along its columns, each
+// 32-element block with its own exponent (mx_exponent of the block's largest
+// float32 magnitude, as the first fp8 GEMM's epilogue takes it) and the codes
+// e4m3(x 2^-E):
+//   ROWS: Xr8 [M, N] tile-packed (kp_unit, N / 16 units per row), exponents
+//         Er per row and block of 32 columns (mx_byte layout, rows M, cols N);
+//   COLS: the codes of X^T, Xc8 [N, M] tile-packed (M / 16 units per row),
+//         exponents Ec per column of X and block of 32 rows (rows N, cols M).
+// One read of X serves both.  A workgroup takes 32 rows x 256 columns; thread
+// t holds row t / 8's 32 columns 32 (t % 8) .. +31, the block of its row
+// codes.  For the column codes the tile goes through LDS, where thread t
+// then reads column t: element (r, 32 b + k) sits at word
+// r * kMxPitch + 32 b + (k + 4 b) % 32, which spreads both the writes of a
+// row's 8 blocks and the reads of 64 consecutive columns over the banks.
+// Each workgroup takes kMxHalves such 32-row tiles in turn, with the loads of
+// all of them in flight first.  The grid covers 256 ceil(M / 256) rows and
+// 256 ceil(N / 256) columns, so
+// that every exponent byte of both arrays is written, those of padding rows
+// and of blocks past the end as 127 (E = 0, their values read as 0); codes
+// are written only inside X.  M % 16 == 0, N % 16 == 0.
+constexpr int kMxPitch = 257;
+
+template <bool ROWS, bool COLS>
+__device__ __forceinline__ void mx_quantize_tile(const float (&v)[32], int i0, int j0, int M, int N,
+                                                 uint8_t* __restrict__ Xr8, uint8_t* __restrict__ Er,
+                                                 uint8_t* __restrict__ Xc8, uint8_t* __restrict__ Ec, float* tile) {
+  const int t = threadIdx.x;
+  const int rr = t >> 3, cb = t & 7;
+  const int row = i0 + rr, col = j0 + 32 * cb;
+  if constexpr (ROWS) {
+    float a = 0.f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) a = fmaxf(a, fabsf(v[k]));
+    const int E = mx_exponent(a);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (row < M && col + 16 * h < N) {
+        const float* x = v + 16 * h;
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          w[q] = pack_e4m3x4(ldexpf(x[4 * q], -E), ldexpf(x[4 * q + 1], -E), ldexpf(x[4 * q + 2], -E),
+                             ldexpf(x[4 * q + 3], -E));
+        *(u32x4*)(Xr8 + kp_unit(row, (col >> 4) + h, N >> 4) * 16) = w;
+      }
+    }
+    if (row < 128 * mx_row_blocks(M)) Er[mx_byte(row, col >> 6, (col >> 5) & 1, M)] = (uint8_t)(E + 127);
+  }
+  if constexpr (COLS) {
+    __syncthreads();  // the tile's previous reads are done
+#pragma unroll
+    for (int k = 0; k < 32; ++k) tile[rr * kMxPitch + 32 * cb + ((k + 4 * cb) & 31)] = v[k];
+    __syncthreads();
+    const int pc = 32 * (t >> 5) + (((t & 31) + 4 * (t >> 5)) & 31);
+    float w[32];
+    float a = 0.f;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      w[r] = tile[r * kMxPitch + pc];
+      a = fmaxf(a, fabsf(w[r]));
+    }
+    const int E = mx_exponent(a);
+    const int crow = j0 + t;  // the row of X^T
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (crow < N && i0 + 16 * h < M) {
+        const float* x = w + 16 * h;
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          o[q] = pack_e4m3x4(ldexpf(x[4 * q], -E), ldexpf(x[4 * q + 1], -E), ldexpf(x[4 * q + 2], -E),
+                             ldexpf(x[4 * q + 3], -E));
+        *(u32x4*)(Xc8 + kp_unit(crow, (i0 >> 4) + h, M >> 4) * 16) = o;
+      }
+    }
+    if (crow < 128 * mx_row_blocks(N)) Ec[mx_byte(crow, i0 >> 6, (i0 >> 5) & 1, N)] = (uint8_t)(E + 127);
+  }
+}
+
+// A workgroup takes kMxTileRows = 32 kMxHalves rows as kMxHalves 32-row
+// tiles, all of whose loads go out first.
+constexpr int kMxHalves = 2, kMxTileRows = 32 * kMxHalves;
+
+template <bool ROWS, bool COLS>
+__global__ __launch_bounds__(256) void mx_quantize_kernel(const uint16_t* __restrict__ X, int64_t ldx, int M, int N,
+                                                          uint8_t* __restrict__ Xr8, uint8_t* __restrict__ Er,
+                                                          uint8_t* __restrict__ Xc8, uint8_t* __restrict__ Ec) {
+  __shared__ float tile[COLS ? 32 * kMxPitch : 1];
+  const int t = threadIdx.x;
+  const int j0 = blockIdx.y * 256;  // row tiles along x: the longer grid dimension
+  const int rr = t >> 3, cb = t & 7;
+  const int col = j0 + 32 * cb;
+  float v[kMxHalves][32];
+#pragma unroll
+  for (int u = 0; u < kMxHalves; ++u) {
+    const int row = blockIdx.x * kMxTileRows + 32 * u + rr;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bool in = row < M && col + 8 * c < N;
+      const u32x4 raw = in ? Chunk8<uint16_t>::load_raw(X + (int64_t)row * ldx + col + 8 * c) : u32x4{0, 0, 0, 0};
+      Chunk8<uint16_t>::unpack(raw, v[u] + 8 * c);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kMxHalves; ++u)
+    mx_quantize_tile<ROWS, COLS>(v[u], blockIdx.x * kMxTileRows + 32 * u, j0, M, N, Xr8, Er, Xc8, Ec, tile);
+}
+
 }  // namespace coda
