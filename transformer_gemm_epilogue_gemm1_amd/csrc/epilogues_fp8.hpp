@@ -179,34 +179,4 @@ struct EpiRowScaleFp8 {
   __device__ __forceinline__ void finish() {}
 };
 
-// Dequantisation in front of another epilogue: the accumulator of a product
-// of e4m3 operands quantised with row scales sa (A's rows) and sb (B's rows,
-// the output columns) is v = (acc * sa[row]) * sb[col]; Inner then sees v as
-// if the product had been taken in full precision.
-template <class Inner>
-struct EpiDequant {
-  struct Params {
-    const float* sa;  // [M]
-    const float* sb;  // [N]
-    typename Inner::Params inner;
-  };
-  Inner in;
-  RowScalars rs;
-  float sb[8];
-  __device__ __forceinline__ EpiDequant(const Params& p, int lane, int wm, int wn, int m0, int n0, int tn, int M,
-                                        int N)
-      : in(p.inner, lane, wm, wn, m0, n0, tn, M, N) {
-    rs.prefetch(p.sa, m0 + wm * kWaveM, lane, M);
-    load_col_scales(p.sb, n0 + wn * kWaveN + (lane & 7) * 8, N, sb);
-  }
-  __device__ __forceinline__ void apply(int mt, int q, int row, int col, float v[8]) {
-    const float s = rs.v[mt][q];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = (v[i] * s) * sb[i];
-    in.apply(mt, q, row, col, v);
-  }
-  __device__ __forceinline__ void end_slab(int mt, int slab_row0) { in.end_slab(mt, slab_row0); }
-  __device__ __forceinline__ void finish() { in.finish(); }
-};
-
 }  // namespace coda
