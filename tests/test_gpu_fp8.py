@@ -12,6 +12,10 @@ scales).  Compared with the fp64 oracle of the same chain (oracle/fp8.py):
     H differs from the bf16 rounding of the exact H, and there within one
     e4m3 step of the dequantised value;
   * r: as in the bf16 chain.
+Also here: the quantisers (per-row / per-channel scales, and the MX
+quantiser: codes and every exponent byte bit-exact against the oracle), the
+second GEMM's block-exponent map, and the fp8 backward (coda_chain_bwd_fp8,
+MX operands on both sides of every product) against oracle.backward_fp8.
 """
 import sys
 
