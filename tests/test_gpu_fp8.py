@@ -671,3 +671,19 @@ def test_fp8_backward_block_scaled_inputs():
     dHf = host_f32(out["dR"])
     assert max_rel(host_f32(out["dA"]), deq(dHf) @ deq(x["W1"].f32).T) <= 2.0 ** -8
     assert max_rel(host_f32(out["dW1"]), deq(x["A"].f32.T) @ deq(dHf.T).T) <= 2.0 ** -8
+
+
+def test_quantize_mx_strided_input():
+    # X as a view with a leading dimension past its width: the same arrays as
+    # from a contiguous copy
+    M, N, ld = 96, 272, 336
+    rng = np.random.default_rng(41)
+    full = rng.standard_normal((M, ld)).astype(np.float32)
+    dfull, _ = _bf16_dev(full)
+    view = dfull[:, :N]
+    assert view.stride(0) == ld
+    a = coda.quantize_mx_e4m3_packed(view)
+    b = coda.quantize_mx_e4m3_packed(view.contiguous())
+    torch.cuda.synchronize()
+    for p, q in zip(a, b):
+        assert torch.equal(p, q)
