@@ -83,8 +83,9 @@ def parse():
 
 
 # The second GEMM (gemm_kernel with the EpiRowScale epilogue) is compiled from
-# these files alone, with the build's compiler flags.
-SECOND_GEMM_SOURCES = ("csrc/gemm.hpp", "csrc/tile_map.hpp", "csrc/epilogues.hpp")
+# these files alone (epilogues.hpp includes the others), with the build's
+# compiler flags.
+SECOND_GEMM_SOURCES = ("csrc/gemm.hpp", "csrc/tile_map.hpp", "csrc/epilogues.hpp", "csrc/lanes.hpp")
 
 
 def second_gemm_sources_sha256() -> str:
