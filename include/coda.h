@@ -580,8 +580,10 @@ coda_status coda_quantize_mx_e4m3_packed(int64_t M, int64_t N, const void* X, in
  * dH = r P - c H, dR = dH) is the bf16 backward's.  The quantisers count as
  * the identity when differentiating (straight-through).  Arguments as
  * coda_chain_bwd, all bf16 (r, dg float); M, K, D, N2 multiples of 16,
- * M <= 4194240; ws of coda_chain_bwd_fp8_workspace_bytes() (the bf16
- * backward's workspace plus the e4m3 operands and their exponents). */
+ * M <= 4194240; ws of coda_chain_bwd_fp8_workspace_bytes(): the bf16
+ * backward's partial sums and c, and the e4m3 operands with their
+ * exponents (X_n is never held in bf16: G's epilogue writes its column
+ * codes and exponents directly). */
 size_t coda_chain_bwd_fp8_workspace_bytes(int64_t M, int64_t K, int64_t D, int64_t N2);
 coda_status coda_chain_bwd_fp8(int64_t M, int64_t K, int64_t D, int64_t N2,
                                const void* dY, const void* A, const void* W1, const void* g,

@@ -261,10 +261,11 @@ size_t align_up(size_t x) { return (x + kWsAlign - 1) & ~(kWsAlign - 1); }
 // backward at 7B than transposing first.)
 struct BwdWs {
   size_t xn, srow, dgcol, c, w2t, w1t, total;
-  BwdWs(int64_t M, int64_t K, int64_t D, int64_t N2, int es) {
+  // with_xn false: no room for X_n (the fp8 backward codes it in G's epilogue)
+  BwdWs(int64_t M, int64_t K, int64_t D, int64_t N2, int es, bool with_xn = true) {
     const int64_t T = num_partials(D), U = (M + kWaveM - 1) / kWaveM;
     xn = 0;
-    srow = align_up(xn + (size_t)M * D * es);
+    srow = align_up(xn + (with_xn ? (size_t)M * D * es : 0));
     dgcol = align_up(srow + (size_t)T * M * 4);
     c = align_up(dgcol + (size_t)U * D * 4);
     w2t = align_up(c + (size_t)M * 4);
@@ -352,7 +353,7 @@ coda_status chain_bwd_impl(int M, int K, int D, int N2, const void* dY, const vo
 struct Bwd8Ws {
   BwdWs b;
   size_t dy8, edy, dyt8, edyt, w2q, ew2, w1q, ew1, dh8, edh, dht8, edht, xnt8, exn, at8, eat, total;
-  Bwd8Ws(int64_t M, int64_t K, int64_t D, int64_t N2) : b(M, 0, D, 0, 2) {
+  Bwd8Ws(int64_t M, int64_t K, int64_t D, int64_t N2) : b(M, 0, D, 0, 2, false) {
     size_t o = b.total;
     auto take = [&o](int64_t bytes) {
       const size_t at = o;
@@ -453,7 +454,6 @@ coda_status chain_bwd_fp8_impl(int M, int K, int D, int N2, const void* dY, cons
                                const void* g, const void* W2, const void* H, const float* r, void* dA, void* dR,
                                void* dW1, void* dW2, float* dg, char* ws, hipStream_t s) {
   const Bwd8Ws L(M, K, D, N2);
-  uint16_t* Xn = (uint16_t*)(ws + L.b.xn);
   float* srow = (float*)(ws + L.b.srow);
   float* dgcol = (float*)(ws + L.b.dgcol);
   float* c = (float*)(ws + L.b.c);
@@ -465,9 +465,11 @@ coda_status chain_bwd_fp8_impl(int M, int K, int D, int N2, const void* dY, cons
   q_mx(W2, N2, D, N2, w + L.w2q, w + L.ew2, nullptr, nullptr, s);
   q_mx(W1, D, K, D, w + L.w1q, w + L.ew1, nullptr, nullptr, s);
   if ((st = launch_status("coda_chain_bwd_fp8 quantise dY, W1, W2")) != CODA_OK) return st;
-  // 1. G with the P / X_n / partial-sum epilogue
-  using EpiG = EpiBwdG<uint16_t>;
-  const typename EpiG::Params eg{(const uint16_t*)H, (const uint16_t*)g, r, (uint16_t*)dR, Xn, D, srow, dgcol};
+  // 1. G with the P / partial-sum epilogue, X_n leaving as dW2's operand (its
+  // column codes and exponents)
+  using EpiG = EpiBwdGMx;
+  const typename EpiG::Params eg{{(const uint16_t*)H, (const uint16_t*)g, r, (uint16_t*)dR, nullptr, D, srow, dgcol},
+                                 (uint8_t*)(w + L.xnt8), (uint8_t*)(w + L.exn)};
   if ((st = launch_gemm_fp8<EpiG, kLayPacked, kMxA | kMxB>("coda_chain_bwd_fp8 G", M, D, N2, w + L.dy8, N2 / 16,
                                                            w + L.w2q, N2 / 16, eg, s, w + L.edy, w + L.ew2)) !=
       CODA_OK)
@@ -479,9 +481,8 @@ coda_status chain_bwd_fp8_impl(int M, int K, int D, int N2, const void* dY, cons
   const int blocks = (int)((nchunks + 255) / 256 < 16384 ? (nchunks + 255) / 256 : 16384);
   hipLaunchKernelGGL(dh_finalize_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, (uint16_t*)dR, (const uint16_t*)H,
                      r, c, D, nchunks);
-  // operands of dA = dH W1^T (dH rows), dW1 = A^T dH and dW2 = X_n^T dY (columns)
+  // operands of dA = dH W1^T (dH rows) and dW1 = A^T dH (columns)
   q_mx(dR, D, M, D, w + L.dh8, w + L.edh, w + L.dht8, w + L.edht, s);
-  q_mx(Xn, D, M, D, nullptr, nullptr, w + L.xnt8, w + L.exn, s);
   q_mx(A, K, M, K, nullptr, nullptr, w + L.at8, w + L.eat, s);
   if ((st = launch_status("coda_chain_bwd_fp8 combine, dH, quantise")) != CODA_OK) return st;
   using EpiO = EpiRowScale<uint16_t>;

@@ -370,8 +370,14 @@ struct EpiBwdG {
   }
 
   __device__ __forceinline__ void apply(int mt, int q, int row, int col_, float v[8]) {
-    float hv[8], pv[8], xv[8];
-    const int64_t o = (int64_t)row * p.ld + col_;
+    float xv[8];
+    apply_p(mt, q, row, col_, v, xv);
+    Chunk8<T>::store(p.Xn + (int64_t)row * p.ld + col_, xv);
+  }
+
+  // P and the sums; xv gets X_n's 8 values before their rounding to T
+  __device__ __forceinline__ void apply_p(int mt, int q, int row, int col_, const float v[8], float xv[8]) {
+    float hv[8], pv[8];
     hc.get(p.H, p.ld, mt, q, row, col_, hv);
     const float rr = rs.v[mt][q];
 #pragma unroll
@@ -381,8 +387,7 @@ struct EpiBwdG {
       colsum[i] += (rr * hv[i]) * v[i];
       xv[i] = (hv[i] * rr) * gv[i];
     }
-    Chunk8<T>::store(p.P + o, pv);
-    Chunk8<T>::store(p.Xn + o, xv);
+    Chunk8<T>::store(p.P + (int64_t)row * p.ld + col_, pv);
   }
 
   __device__ __forceinline__ void end_slab(int, int slab_row0) {

@@ -179,4 +179,95 @@ struct EpiRowScaleFp8 {
   __device__ __forceinline__ void finish() {}
 };
 
+// Backward, first product G = dY W2^T on e4m3 operands (the fp8 backward):
+// EpiBwdG's P, row sums and column sums, with X_n leaving as the operand the
+// weight gradient dW2 = X_n^T dY reads, instead of as bf16.  X_n is rounded
+// to bf16 first (the stored value the recipe quantises) and then coded along
+// its columns with MX block exponents, as the MX quantiser codes a matrix's
+// columns: per column j and block of 32 rows b, E = mx_exponent(max |X_n|),
+// byte E + 127 at mx_byte(j, b / 2, b % 2, D) of exn, and the codes
+// e4m3(X_n 2^-E) as the rows of X_n^T [D, M], tile-packed (kp_unit with M / 16
+// units per row) in xnt8.  A block is two epilogue slabs: the wavefront keeps
+// its 32 x 64 values in LDS, and after the second slab lane l takes column l
+// of the wavefront's 64 (one read pass for the maximum, one per 16-row unit
+// for the codes).  Values outside X (rows >= M, columns >= D) read as 0, so
+// every exponent byte the array holds is written: 127 for padding rows and
+// for blocks past M, as the quantiser writes them.
+struct EpiBwdGMx : EpiBwdG<uint16_t> {
+  using Base = EpiBwdG<uint16_t>;
+  struct Params {
+    Base::Params b;  // b.Xn is not used
+    uint8_t* xnt8;
+    uint8_t* exn;
+  };
+  static constexpr int kLdsBytes = 32 * kWaveN * 4;
+  uint8_t* xnt8;
+  uint8_t* exn;
+  float* xs;  // [32][kWaveN] X_n values of the current block
+  int row0, col0;
+
+  __device__ __forceinline__ EpiBwdGMx(const Params& p_, int lane_, int wm, int wn, int m0, int n0, int tn, int M_,
+                                       int N_)
+      : Base(p_.b, lane_, wm, wn, m0, n0, tn, M_, N_), xnt8(p_.xnt8), exn(p_.exn), xs(nullptr) {
+    row0 = m0 + wm * kWaveM;
+    col0 = n0 + wn * kWaveN;
+  }
+
+  // the lane's own positions of a block: rows 16 s + l / 8 + 8 q, columns
+  // 8 (l % 8) .. + 7
+  __device__ __forceinline__ void zero_own() {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        float* d = xs + (16 * s + (lane >> 3) + 8 * q) * kWaveN + 8 * (lane & 7);
+        *(f32x4*)d = f32x4{0.f, 0.f, 0.f, 0.f};
+        *(f32x4*)(d + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+  }
+  __device__ __forceinline__ void set_lds(char* lds) {
+    xs = (float*)lds;
+    zero_own();
+  }
+
+  __device__ __forceinline__ void apply(int mt, int q, int row, int col_, float v[8]) {
+    float xv[8];
+    apply_p(mt, q, row, col_, v, xv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xv[i] = Chunk8<uint16_t>::round(xv[i]);
+    float* d = xs + (16 * (mt & 1) + (lane >> 3) + 8 * q) * kWaveN + 8 * (lane & 7);
+    *(f32x4*)d = f32x4{xv[0], xv[1], xv[2], xv[3]};
+    *(f32x4*)(d + 4) = f32x4{xv[4], xv[5], xv[6], xv[7]};
+  }
+
+  __device__ __forceinline__ void end_slab(int mt, int slab_row0) {
+    Base::end_slab(mt, slab_row0);
+    if (mt & 1) {
+      const int br = slab_row0 - 16;  // the block's first row
+      wave_lds_fence();
+      float a = 0.f;
+#pragma unroll
+      for (int r = 0; r < 32; ++r) a = fmaxf(a, fabsf(xs[r * kWaveN + lane]));
+      const int E = mx_exponent(a);
+      const int crow = col0 + lane;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (crow < N && br + 16 * h < M) {
+          u32x4 o;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float* x = xs + (16 * h + 4 * k) * kWaveN + lane;
+            o[k] = pack_e4m3x4(ldexpf(x[0], -E), ldexpf(x[kWaveN], -E), ldexpf(x[2 * kWaveN], -E),
+                               ldexpf(x[3 * kWaveN], -E));
+          }
+          *(u32x4*)(xnt8 + kp_unit(crow, (br >> 4) + h, M >> 4) * 16) = o;
+        }
+      }
+      if (crow < 128 * mx_row_blocks(N)) exn[mx_byte(crow, br >> 6, (br >> 5) & 1, N)] = (uint8_t)(E + 127);
+      wave_lds_fence();  // the block's reads are done before the next block's writes
+      zero_own();
+    }
+  }
+};
+
 }  // namespace coda

@@ -36,6 +36,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "tile_map.hpp"
 
 namespace coda {
@@ -386,13 +388,25 @@ __device__ __forceinline__ void kstep(char* const (&st)[kStages], const Dma<T, A
 //                              (epi_row), v[8] the accumulators
 //   end_slab(mt, slab_row0)    after all lanes applied 16-row slab mt
 //   finish()                   on every lane after the last slab
+// An epilogue that stages data of its own in LDS declares kLdsBytes (per
+// wavefront) and set_lds(char*); only the fp8 kernel hands out such room.
 // A_L, B_L: OpLayout of a contraction-contiguous operand.
+template <class E, class = void>
+struct epi_lds_bytes {
+  static constexpr int value = 0;
+};
+template <class E>
+struct epi_lds_bytes<E, std::void_t<decltype(E::kLdsBytes)>> {
+  static constexpr int value = E::kLdsBytes;
+};
+
 template <typename T, bool A_KC, bool B_KC, class Epi, int A_L = kLayKC, int B_L = kLayKC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(
     GemmArgs g, typename Epi::Params ep) {
   static_assert(kStages == 4, "the stage arrays and the unrolled steps below assume four stages");
   static_assert((A_L == kLayKC || A_KC) && (B_L == kLayKC || B_KC), "only contraction-contiguous operands are packed");
   static_assert((A_L != kLayPacked && B_L != kLayPacked) || sizeof(T) == 2, "tile-packed operands are bf16");
+  static_assert(epi_lds_bytes<Epi>::value == 0, "this kernel gives its epilogues no LDS of their own");
   __shared__ __attribute__((aligned(1024))) char st0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char st1[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char st2[kStageBytes];

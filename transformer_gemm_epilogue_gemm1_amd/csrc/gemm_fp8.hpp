@@ -201,7 +201,8 @@ __device__ __forceinline__ void kstep8(char* const (&st)[kStages], const Dma<uin
 
 // C = A B^T for fp8 A[M, K] (g.a, g.lda) and B[N, K] (g.b, g.ldb); the
 // epilogue interface is the bf16 kernel's (16-row slabs, apply / end_slab /
-// finish).
+// finish), and an epilogue that declares kLdsBytes gets that much LDS per
+// wavefront through set_lds, in the stage that holds its slab.
 // L: OpLayout of both operands (kLayPacked: tile-packed, kp_unit, with g.lda /
 // g.ldb counting 16-byte chunks per row).
 // MX: a mask of kMxA, kMxB, the operands that carry block exponents (mxa,
@@ -274,8 +275,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // ---- epilogue: slab s = rows 16 s .. 16 s + 15 of the wavefront's 128 =
   // half s % 2 of row fragment s / 2 (acc32_row) ----
   Epi epi(ep, lane, wm, wn, m0, n0, tn, g.M, g.N);
-  float* slab = (float*)(((wave & 3) == 0 ? st0 : (wave & 3) == 1 ? st1 : (wave & 3) == 2 ? st2 : st3) +
-                         (wave >> 2) * kEpiSlabBytes);
+  char* const stw = (wave & 3) == 0 ? st0 : (wave & 3) == 1 ? st1 : (wave & 3) == 2 ? st2 : st3;
+  float* slab = (float*)(stw + (wave >> 2) * kEpiSlabBytes);
+  if constexpr (epi_lds_bytes<Epi>::value > 0) {
+    // the two wavefronts of a stage: their slabs, then the epilogue's own room
+    static_assert(2 * kEpiSlabBytes + 2 * epi_lds_bytes<Epi>::value <= kStageBytes, "epilogue LDS exceeds a stage");
+    static_assert(kEpiSlabBytes % 16 == 0 && epi_lds_bytes<Epi>::value % 16 == 0, "16-byte LDS alignment");
+    epi.set_lds(stw + 2 * kEpiSlabBytes + (wave >> 2) * epi_lds_bytes<Epi>::value);
+  }
   const int row_base = m0 + wm * kWaveM;
   const int col = n0 + wn * kWaveN + (lane & 7) * 8;
 #pragma unroll
