@@ -687,3 +687,36 @@ def test_quantize_mx_strided_input():
     torch.cuda.synchronize()
     for p, q in zip(a, b):
         assert torch.equal(p, q)
+
+
+@pytest.mark.parametrize("shape", [(48, 96, 272, 160), (272, 144, 528, 304)], ids=lambda s: "x".join(map(str, s)))
+def test_fp8_backward_poisoned_workspace(shape):
+    # The workspace filled with 0xFF before the call: an exponent byte that no
+    # kernel writes would then read as E8M0 NaN and spread into the gradient
+    # it scales, and a code byte as e4m3 NaN.  M and D are ragged against the
+    # 256-row / 256-column tiles, so the exponents of blocks past M and of
+    # padding columns, which the products read as scales of zero codes, are
+    # covered (the first product's epilogue writes X_n's).  The gradients must
+    # be finite and bit-identical to a call on a fresh workspace; the outputs
+    # start as bf16 NaN.
+    M, K, D, N2 = shape
+    wl = ci.custom_workload(M, K, D, N2, wl_id=513)
+    x = ci.make_inputs(wl, seed=5, with_dy=True)
+    d = {k: dev(v) for k, v in x.items()}
+    H, _, r, _, _ = coda.fused_forward(d["A"], d["W1"], d["R"], d["g"], d["W2"], wl.eps)
+    ref = coda.fused_backward_fp8(d["dY"], d["A"], d["W1"], d["g"], d["W2"], H, r)
+    lib = coda._lib.load()
+    nbytes = int(lib.coda_chain_bwd_fp8_workspace_bytes(M, K, D, N2))
+    ws = torch.full((nbytes,), 0xFF, device="cuda", dtype=torch.uint8)
+    bf = torch.bfloat16
+    nan = lambda *s: torch.full(s, -1, device="cuda", dtype=torch.int16).view(bf)
+    out = [nan(M, K), nan(M, D), nan(K, D), nan(D, N2), torch.full((D,), float("nan"), device="cuda")]
+    st = lib.coda_chain_bwd_fp8(M, K, D, N2, d["dY"].data_ptr(), d["A"].data_ptr(), d["W1"].data_ptr(),
+                                d["g"].data_ptr(), d["W2"].data_ptr(), H.data_ptr(), r.data_ptr(),
+                                *[t.data_ptr() for t in out], ws.data_ptr(), nbytes,
+                                torch.cuda.current_stream().cuda_stream)
+    assert st == 0, st
+    torch.cuda.synchronize()
+    for name, a, b in zip(GRADS8, ref, out):
+        assert bool(torch.isfinite(b.float()).all()), f"{name} has non-finite values"
+        assert torch.equal(a.view(torch.int16) if a.dtype == bf else a, b.view(torch.int16) if b.dtype == bf else b), name

@@ -483,7 +483,7 @@ def coda_chain_bwd_noalloc(dY, A, W1, g, W2, H, r, dA, dR, dW1, dW2, dg, stream=
 # ---- conveniences that allocate outputs with torch, then call the above ----
 
 def fused_forward(A, W1, R, g, W2, eps: float, stream=None):
-    """The fused chain: three launches, returns (H, Hg, r, Y)."""
+    """The fused chain: three launches, returns (H, Hg, r, Y, partials)."""
     M, D, N2 = A.shape[0], W1.shape[1], W2.shape[1]
     dev, dt = A.device, A.dtype
     H = torch.empty((M, D), device=dev, dtype=dt)
