@@ -347,9 +347,10 @@ coda_status chain_bwd_impl(int M, int K, int D, int N2, const void* dY, const vo
                                                       typename EpiRowScale<T>::Params{nullptr, (T*)dW2, N2}, s);
 }
 
-// Workspace of the fp8 backward: the bf16 backward's (X_n, partial sums, c)
-// followed by the e4m3 operands of the four products (tile-packed codes) and
-// their block exponents (mx_byte layout).
+// Workspace of the fp8 backward: the bf16 backward's partial sums and c (no
+// X_n: G's epilogue writes its codes) followed by the e4m3 operands of the
+// four products (tile-packed codes) and their block exponents (mx_byte
+// layout).
 struct Bwd8Ws {
   BwdWs b;
   size_t dy8, edy, dyt8, edyt, w2q, ew2, w1q, ew1, dh8, edh, dht8, edht, xnt8, exn, at8, eat, total;
