@@ -622,10 +622,11 @@ def mfma_ceiling(kind: str, stream, reps: int = 3):
 
 def bench_fp8(args, stream):
     """The fused chain with fp8 (OCP e4m3) GEMM operands at the 7B shape:
-    the weights quantised once per output channel (coda_quantize_cols_e4m3),
-    a bf16 activation A quantised per row in every step
-    (coda_quantize_rows_e4m3), H and Y bf16; also the chain on an A that
-    arrives quantised, and the second GEMM alone."""
+    the weights quantised once per output channel
+    (coda_quantize_cols_e4m3_packed), a bf16 activation A quantised per row
+    in every step (coda_quantize_rows_e4m3_packed), every e4m3 operand
+    tile-packed, H and Y bf16; also the chain on an A that arrives quantised,
+    each GEMM alone, and the same chain on row-major operands."""
     import torch
 
     import coda_inputs as ci
@@ -644,11 +645,14 @@ def bench_fp8(args, stream):
     W2t8, sw2 = coda.quantize_weight_e4m3(W2, stream)
     A8 = torch.empty((M, K), device=dev, dtype=torch.uint8)
     sa = torch.empty((M,), device=dev, dtype=torch.float32)
+    # every e4m3 operand tile-packed: A8 and W1's codes (the first GEMM's),
+    # Hg8 and W2's codes (the second GEMM's)
+    A8p = coda.packed_empty_e4m3(M, K, dev)
+    W1t8p, sw1p = coda.quantize_weight_e4m3_packed(W1, stream)
     R = torch.randn((M, D), device=dev, generator=gen).to(torch.bfloat16)
     g = (1.0 + 0.1 * torch.randn((D,), device=dev, generator=gen)).to(torch.bfloat16)
     H = torch.empty((M, D), device=dev, dtype=torch.bfloat16)
     Hg8 = torch.empty((M, D), device=dev, dtype=torch.uint8)
-    # the chain's Hg8 and W2 codes tile-packed (the second GEMM's operands)
     W2t8p, sw2p = coda.quantize_weight_e4m3_packed(W2, stream)
     Hg8p = coda.packed_empty_e4m3(M, D, dev)
     E = coda.mx_exp_empty(M, D, dev)    # Hg8's MX block exponents
@@ -657,12 +661,17 @@ def bench_fp8(args, stream):
     Y = torch.empty((M, N2), device=dev, dtype=torch.bfloat16)
 
     def quantize_a():
-        coda.quantize_rows_e4m3(A, stream, A8, sa)
+        coda.quantize_rows_e4m3_packed(A, stream, A8p, sa)
+
+    def first_gemm():
+        coda.coda_gemm_res_prms_fp8_all_packed(A8p, sa, W1t8p, sw1p, R, g, H, Hg8p, E, P, stream)
 
     def chain():
-        coda.coda_gemm_res_prms_fp8_packed(A8, sa, W1t8, sw1, R, g, H, Hg8p, E, P, stream)
+        first_gemm()
         coda.coda_rms_combine(P, r, D, wl.eps, stream)
         coda.coda_gemm_rowscale_fp8_packed(Hg8p, E, W2t8p, sw2p, r, Y, stream)
+
+    coda.quantize_rows_e4m3(A, stream, A8)   # the row-major codes (same scales) for the row-major chain
 
     def chain_row_major():
         coda.coda_gemm_res_prms_fp8(A8, sa, W1t8, sw1, R, g, H, Hg8, E, P, stream)
@@ -675,20 +684,27 @@ def bench_fp8(args, stream):
 
     n = max(5, args.steps // 2)
     w = max(2, args.warmup // 2)
-    ms, chain_ms, q_ms, g2_ms, rm_ms, g2rm_ms, g2u_ms = time_ms_alternating(
+    ms, chain_ms, q_ms, g2_ms, rm_ms, g2rm_ms, g2u_ms, g1_ms, g1rm_ms = time_ms_alternating(
         [step, chain, quantize_a, lambda: coda.coda_gemm_rowscale_fp8_packed(Hg8p, E, W2t8p, sw2p, r, Y, stream),
          chain_row_major, lambda: coda.coda_gemm_rowscale_fp8(Hg8, E, W2t8, sw2, r, Y, stream),
-         lambda: coda.coda_gemm_rowscale_fp8_packed(Hg8p, None, W2t8p, sw2p, r, Y, stream)], stream, n, w)
+         lambda: coda.coda_gemm_rowscale_fp8_packed(Hg8p, None, W2t8p, sw2p, r, Y, stream), first_gemm,
+         lambda: coda.coda_gemm_res_prms_fp8_packed(A8, sa, W1t8, sw1, R, g, H, Hg8p, E, P, stream)],
+        stream, n, w)
+    g1_flops = 2.0 * M * K * D
     tf = wl.fwd_flops / (ms * 1e-3) / 1e12
     g2_tf = 2.0 * M * D * N2 / (g2_ms * 1e-3) / 1e12
     out = {"workload": f"7b-fp8: M={M} K={K} D={D} N2={N2}, e4m3 operands with per-row / per-channel scales, "
                        "bf16 A quantised on the device in every step; H g quantised with MX block exponents "
-                       "(one per row and 32 columns) that the second GEMM's scaled products apply; the second "
-                       "GEMM's operands (Hg8, W2 codes) tile-packed",
+                       "(one per row and 32 columns) that the second GEMM's scaled products apply; every e4m3 "
+                       "operand (A8, W1 codes, Hg8, W2 codes) tile-packed",
            "ms_per_step": round(ms, 4), "tflops": round(tf, 2),
            "pct_of_fp8_peak": round(100.0 * tf / PEAK_FP8_TFLOPS, 2), "fp8_peak_tflops": round(PEAK_FP8_TFLOPS, 1),
            "quantize_a_ms": round(q_ms, 4),
            "quantize_a_gbps": round((M * K * 3 + M * 4) / (q_ms * 1e-3) / 1e9, 1),
+           "coda_gemm_res_prms_fp8_all_packed_ms": round(g1_ms, 4),
+           "coda_gemm_res_prms_fp8_all_packed_tflops": round(g1_flops / (g1_ms * 1e-3) / 1e12, 2),
+           "first_gemm_row_major_operands_ms": round(g1rm_ms, 4),
+           "first_gemm_packed_operands_speedup": round(g1rm_ms / g1_ms, 4),
            "chain_on_quantised_a_ms": round(chain_ms, 4),
            "chain_on_quantised_a_tflops": round(wl.fwd_flops / (chain_ms * 1e-3) / 1e12, 2),
            "coda_gemm_rowscale_fp8_packed_ms": round(g2_ms, 4),
@@ -731,7 +747,7 @@ def bench_fp8(args, stream):
             coda._lib.check("coda_chain_bwd_fp8", st)
 
         def train8():
-            coda.quantize_weight_e4m3(W1, stream, W1t8, sw1)
+            coda.quantize_weight_e4m3_packed(W1, stream, W1t8p, sw1p)
             coda.quantize_weight_e4m3_packed(W2, stream, W2t8p, sw2p)
             step()
             bwd8()

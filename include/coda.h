@@ -424,8 +424,8 @@ coda_status coda_quantize_cols_e4m3_packed(int64_t K, int64_t N, const void* W, 
 
 /* coda_quantize_rows_e4m3 with the codes X8 [M,K] written tile-packed into
  * X8p (coda_packed_bytes_e4m3(M, K) bytes, 16-byte aligned; the rows past M
- * in the last 16-row block are not written).  Same recipe and scales.  The
- * fp8 backward quantises dY, dH and the weights this way for its products. */
+ * in the last 16-row block are not written).  Same recipe, scales and codes.
+ * coda_gemm_res_prms_fp8_all_packed takes A's codes in this layout. */
 coda_status coda_quantize_rows_e4m3_packed(int64_t M, int64_t K, const void* X, int64_t ldx,
                                            void* X8p, float* scales, void* stream);
 
@@ -447,6 +447,22 @@ coda_status coda_gemm_res_prms_fp8_packed(int64_t M, int64_t K, int64_t D,
                                           const void* R, int64_t ldr, const void* g,
                                           void* H, int64_t ldh, void* Hg8p, void* hg_exp,
                                           float* partials, void* stream);
+
+/* coda_gemm_res_prms_fp8_packed with both operands tile-packed as well:
+ * A8p [M,K] as coda_quantize_rows_e4m3_packed writes it
+ * (coda_packed_bytes_e4m3(M, K) bytes) and W1t8p [D,K] as
+ * coda_quantize_cols_e4m3_packed writes W1's transposed codes
+ * (coda_packed_bytes_e4m3(D, K) bytes), both 16-byte aligned; sa, sw1, R,
+ * g, H, Hg8p, hg_exp and partials as in coda_gemm_res_prms_fp8_packed.  The
+ * same arithmetic on the same codes as with row-major operands, so the
+ * outputs are bit-identical; the packed operands let the kernel's LDS reads
+ * take whole 16-byte fragments. */
+coda_status coda_gemm_res_prms_fp8_all_packed(int64_t M, int64_t K, int64_t D,
+                                              const void* A8p, const float* sa,
+                                              const void* W1t8p, const float* sw1,
+                                              const void* R, int64_t ldr, const void* g,
+                                              void* H, int64_t ldh, void* Hg8p, void* hg_exp,
+                                              float* partials, void* stream);
 
 /* coda_gemm_rowscale_fp8 with both operands tile-packed: X8p [M,D] (as
  * coda_gemm_res_prms_fp8_packed writes Hg8) and W2t8p [N2,D] (as

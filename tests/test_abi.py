@@ -735,6 +735,24 @@ def test_fp8_packed_validation(lib):
     assert lib.coda_gemm_rowscale_fp8_packed(0, 256, 512, None, None, None, None, None, None, 512, None) == OK
 
 
+def test_fp8_all_packed_first_gemm_validation(lib):
+    def call(M=300, K=256, D=512, A8p=A_, sa=R2_, W1t8p=W1_, sw1=DG_, R=R_, ldr=512, H=H_, Hg8p=HG_, ex=EX_,
+             part=PART_):
+        return lib.coda_gemm_res_prms_fp8_all_packed(M, K, D, A8p, sa, W1t8p, sw1, R, ldr, G_, H, 512, Hg8p, ex,
+                                                     part, None)
+    assert call(K=264) == SHAPE            # K not a multiple of 16
+    assert call(D=520) == SHAPE
+    assert call(ldr=256) == SHAPE          # R's leading dimension below D
+    assert call(A8p=None) == NULL
+    assert call(W1t8p=None) == NULL
+    assert call(ex=None) == NULL
+    assert call(A8p=A_ + 8) == ALIGN       # packed codes 16-byte aligned
+    assert call(sw1=DG_ + 4) == ALIGN
+    assert call(Hg8p=A_ + 64) == ALIAS     # output inside the packed A8p
+    assert call(H=W1_ + 1024) == ALIAS     # output inside the packed W1t8p
+    assert call(M=0, A8p=None, W1t8p=None, R=None, H=None, Hg8p=None, ex=None, part=None) == OK
+
+
 def test_lse_ce_rope_packed_validation(lib):
     # LM head with the cross-entropy statistics: M=300, D=512, V=1000
     lse = lambda **k: lib.coda_gemm_rowscale_lse_packed(

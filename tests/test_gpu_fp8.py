@@ -420,10 +420,13 @@ def test_quantize_rows_cols_bit_exact(shape):
     np.testing.assert_array_equal(Xt8.cpu().numpy(), c_codes)
 
 
-@pytest.mark.parametrize("shape", [(1, 16), (3, 48), (257, 272), (300, 4096), (16, 28672), (4, 40016)], ids=str)
+@pytest.mark.parametrize("shape", [(1, 16), (3, 48), (18, 1040), (5, 2064), (257, 272), (300, 4096), (301, 8192),
+                                   (16, 28672), (4, 40016)], ids=str)
 def test_quantize_rows_packed_bit_exact(shape):
-    # the tile-packed row codes (the fp8 backward's dY, dH and weight
-    # operands) unpack to the oracle's codes; scales identical
+    # the tile-packed row codes (the all-packed first GEMM's A) unpack to the
+    # oracle's codes; scales identical.  Up to K = 8192 a workgroup takes 4
+    # rows (1, 2, 4 or 8 units per lane; M not a multiple of 4 here), longer
+    # rows one row per workgroup.
     M, K = shape
     rng = np.random.default_rng(M + K + 1)
     x = rng.standard_normal((M, K)).astype(np.float32) * np.exp(rng.uniform(-8, 8, size=(M, 1))).astype(np.float32)
@@ -673,6 +676,21 @@ def test_fp8_backward_block_scaled_inputs():
     assert max_rel(host_f32(out["dW1"]), deq(x["A"].f32.T) @ deq(dHf.T).T) <= 2.0 ** -8
 
 
+def test_quantize_rows_packed_strided_input():
+    # X with a leading dimension past its width: the same codes and scales as
+    # a contiguous copy
+    M, K, ld = 37, 1040, 1104
+    rng = np.random.default_rng(43)
+    full = rng.standard_normal((M, ld)).astype(np.float32)
+    dfull, _ = _bf16_dev(full)
+    view = dfull[:, :K]
+    a = coda.quantize_rows_e4m3_packed(view)
+    b = coda.quantize_rows_e4m3_packed(view.contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(a[1], b[1])
+    assert torch.equal(coda.unpack_e4m3(a[0], M), coda.unpack_e4m3(b[0], M))
+
+
 def test_quantize_mx_strided_input():
     # X as a view with a leading dimension past its width: the same arrays as
     # from a contiguous copy
@@ -720,3 +738,68 @@ def test_fp8_backward_poisoned_workspace(shape):
     for name, a, b in zip(GRADS8, ref, out):
         assert bool(torch.isfinite(b.float()).all()), f"{name} has non-finite values"
         assert torch.equal(a.view(torch.int16) if a.dtype == bf else a, b.view(torch.int16) if b.dtype == bf else b), name
+
+
+def _pack8(a):
+    """Host tile-packing of e4m3 codes [rows, cols] (cols % 16 == 0) into the
+    packed_empty_e4m3 layout: [row block of 16, 16-code run, row in block,
+    code], rows past the end zero."""
+    rows, cols = a.shape
+    nb = -(-rows // 16)
+    p = np.zeros((nb * 16, cols), dtype=np.uint8)
+    p[:rows] = a
+    return np.ascontiguousarray(p.reshape(nb, 16, cols // 16, 16).transpose(0, 2, 1, 3))
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_all_packed_chain(shape):
+    # A8 and W1t8 tile-packed (coda_gemm_res_prms_fp8_all_packed), then the
+    # packed second GEMM: the oracle's bars, and every output bit-identical to
+    # the chain on row-major operands (the same codes, the same arithmetic)
+    wl = ci.custom_workload(*shape, dtype="fp8", wl_id=514)
+    x, d, o = _run(wl, seed=6)
+    A8p, W1t8p = _u8(_pack8(x["A8"])), _u8(_pack8(x["W1t8"]))
+    W2t8p = _u8(_pack8(x["W2t8"]))
+    H, Hg8p, E, r, Y, P = coda.fused_forward_fp8_all_packed(A8p, d["sa"], W1t8p, d["sw1"], d["R"], d["g"], W2t8p,
+                                                            d["sw2"], wl.eps)
+    torch.cuda.synchronize()
+    Hg8 = coda.unpack_e4m3(Hg8p, wl.M)
+    for name, a, b in (("H", o["H"], H), ("Hg8", o["Hg8"], Hg8), ("E", o["E"], E), ("r", o["r"], r),
+                       ("Y", o["Y"], Y), ("partials", o["P"], P)):
+        assert torch.equal(a.view(torch.uint8) if a.dtype != torch.float32 else a,
+                           b.view(torch.uint8) if b.dtype != torch.float32 else b), name
+    _check(wl, x, {"H": H, "Hg8": Hg8, "E": E, "r": r, "Y": Y})
+
+
+def test_all_packed_from_bf16_quantisers():
+    # the packed quantisers feed the all-packed first GEMM: the same H, Hg8,
+    # exponents and partials as the row-major quantisers and first GEMM
+    M, K, D = 300, 528, 784
+    rng = np.random.default_rng(21)
+    A, _ = _bf16_dev(rng.standard_normal((M, K)).astype(np.float32))
+    W1, _ = _bf16_dev((rng.standard_normal((K, D)) * K ** -0.5).astype(np.float32))
+    R, _ = _bf16_dev(rng.standard_normal((M, D)).astype(np.float32))
+    g, _ = _bf16_dev((1 + 0.1 * rng.standard_normal(D)).astype(np.float32))
+    A8, sa = coda.quantize_rows_e4m3(A)
+    W1t8, sw1 = coda.quantize_weight_e4m3(W1)
+    A8p, sa2 = coda.quantize_rows_e4m3_packed(A)
+    W1t8p, sw12 = coda.quantize_weight_e4m3_packed(W1)
+    bf = torch.bfloat16
+    T = coda.coda_prms_num_partials(bf, D)
+    outs = []
+    for packed in (False, True):
+        H = torch.empty((M, D), device="cuda", dtype=bf)
+        Hg8p = coda.packed_empty_e4m3(M, D, "cuda")
+        E = coda.mx_exp_empty(M, D, "cuda")
+        P = torch.empty((T, M), device="cuda", dtype=torch.float32)
+        if packed:
+            coda.coda_gemm_res_prms_fp8_all_packed(A8p, sa2, W1t8p, sw12, R, g, H, Hg8p, E, P)
+        else:
+            coda.coda_gemm_res_prms_fp8_packed(A8, sa, W1t8, sw1, R, g, H, Hg8p, E, P)
+        outs.append((H, Hg8p, E, P))   # Hg8p compared on its M rows (the padding rows are not written)
+    torch.cuda.synchronize()
+    assert torch.equal(sa, sa2) and torch.equal(sw1, sw12)
+    outs = [(H, coda.unpack_e4m3(Hg8p, M), E, P) for H, Hg8p, E, P in outs]
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.uint8) if a.dtype != torch.float32 else a,
+                           b.view(torch.uint8) if b.dtype != torch.float32 else b)

@@ -25,6 +25,7 @@ from .binding import (coda_ce_combine, coda_chain_bwd, coda_chain_bwd_workspace_
                       coda_gemm_rowscale_swiglu_packed, fused_forward_swiglu_packed,
                       coda_gemm_rowscale_lse_packed, coda_gemm_rowscale_ce_bwd_packed, coda_gemm_rowscale_rope_packed,
                       fused_forward_ce_packed, fused_backward_ce_packed, fused_forward_rope_packed,
-                      mx_exp_empty, mx_exponents_of, quantize_mx_e4m3_packed)
+                      mx_exp_empty, mx_exponents_of, quantize_mx_e4m3_packed,
+                      coda_gemm_res_prms_fp8_all_packed, fused_forward_fp8_all_packed)
 
 _lib.load()

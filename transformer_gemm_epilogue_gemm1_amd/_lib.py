@@ -42,6 +42,8 @@ SIGNATURES = {
     "coda_quantize_mx_e4m3_packed": (c_int, [c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "coda_gemm_res_prms_fp8_packed": (c_int, [c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp,
                                               c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp]),
+    "coda_gemm_res_prms_fp8_all_packed": (c_int, [c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp,
+                                                  c_vp, c_i64, c_vp, c_vp, c_vp, c_vp]),
     "coda_gemm_rowscale_fp8_packed": (c_int, [c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,
                                               c_vp]),
     "coda_mx_exp_bytes": (c_i64, [c_i64, c_i64]),

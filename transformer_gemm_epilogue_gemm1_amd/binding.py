@@ -695,6 +695,32 @@ def coda_gemm_res_prms_fp8_packed(A8, sa, W1t8, sw1, R, g, H, Hg8p, Hg8_exp, par
     _lib.check("coda_gemm_res_prms_fp8_packed", st)
 
 
+def coda_gemm_res_prms_fp8_all_packed(A8p, sa, W1t8p, sw1, R, g, H, Hg8p, Hg8_exp, partials, stream=None) -> None:
+    """coda_gemm_res_prms_fp8_packed with A8p (packed_empty_e4m3(M, K), as
+    quantize_rows_e4m3_packed writes it) and W1t8p (packed_empty_e4m3(D, K), as
+    quantize_weight_e4m3_packed writes it) tile-packed too; M and D from R."""
+    lib = _lib.load()
+    M, D = R.shape
+    K = 16 * A8p.shape[1]
+    T = coda_prms_num_partials(torch.bfloat16, D)
+    _packed8(A8p, "A8p", M, K)
+    _packed8(W1t8p, "W1t8p", D, K)
+    _packed8(Hg8p, "Hg8", M, D)
+    _mx(Hg8_exp, "Hg8_exp", M, D)
+    _mat(sa, "sa", torch.float32, (M,))
+    _mat(sw1, "sw1", torch.float32, (D,))
+    ldr = _mat(R, "R", torch.bfloat16, (M, D))
+    _mat(g, "g", torch.bfloat16, (D,))
+    ldh = _mat(H, "H", torch.bfloat16, (M, D))
+    _mat(partials, "partials", torch.float32, (T, M))
+    _dense(partials, "partials")
+    st = lib.coda_gemm_res_prms_fp8_all_packed(M, K, D, A8p.data_ptr(), sa.data_ptr(), W1t8p.data_ptr(),
+                                               sw1.data_ptr(), R.data_ptr(), ldr, g.data_ptr(), H.data_ptr(), ldh,
+                                               Hg8p.data_ptr(), Hg8_exp.data_ptr(), partials.data_ptr(),
+                                               _stream(stream))
+    _lib.check("coda_gemm_res_prms_fp8_all_packed", st)
+
+
 def coda_gemm_rowscale_fp8_packed(X8p, X8_exp: Optional[torch.Tensor], W2t8p, sw2, r: Optional[torch.Tensor], Y,
                                   stream=None) -> None:
     """coda_gemm_rowscale_fp8 with both operands tile-packed (X8_exp row-major)."""
@@ -739,6 +765,24 @@ def fused_forward_fp8_packed(A8, sa, W1t8, sw1, R, g, W2t8p, sw2, eps: float, st
     return H, Hg8p, E, r, Y, P
 
 
+def fused_forward_fp8_all_packed(A8p, sa, W1t8p, sw1, R, g, W2t8p, sw2, eps: float, stream=None):
+    """The fp8 chain with every e4m3 operand tile-packed (A8p, W1t8p, Hg8,
+    W2t8p): returns (H, Hg8p, Hg8_exp, r, Y, partials)."""
+    M, D = R.shape
+    N2 = sw2.shape[0]
+    dev = R.device
+    H = torch.empty((M, D), device=dev, dtype=torch.bfloat16)
+    Hg8p = packed_empty_e4m3(M, D, dev)
+    E = mx_exp_empty(M, D, dev)
+    P = torch.empty((coda_prms_num_partials(torch.bfloat16, D), M), device=dev, dtype=torch.float32)
+    r = torch.empty((M,), device=dev, dtype=torch.float32)
+    Y = torch.empty((M, N2), device=dev, dtype=torch.bfloat16)
+    coda_gemm_res_prms_fp8_all_packed(A8p, sa, W1t8p, sw1, R, g, H, Hg8p, E, P, stream)
+    coda_rms_combine(P, r, D, eps, stream)
+    coda_gemm_rowscale_fp8_packed(Hg8p, E, W2t8p, sw2, r, Y, stream)
+    return H, Hg8p, E, r, Y, P
+
+
 def quantize_rows_cols_e4m3(X, stream=None):
     """Both e4m3 quantisations of a bf16 activation X [M, N]: the row codes
     (uint8 [M, N]) with their scales [M], and the transposed column codes
@@ -755,13 +799,17 @@ def quantize_rows_cols_e4m3(X, stream=None):
     return X8, sr, Xt8, sc
 
 
-def quantize_rows_e4m3_packed(X, stream=None):
+def quantize_rows_e4m3_packed(X, stream=None, X8p=None, scales=None):
     """quantize_rows_e4m3 with the codes [M, K] written tile-packed
-    (packed_empty_e4m3(M, K)); returns (X8p, scales)."""
+    (packed_empty_e4m3(M, K)), into X8p / scales when given; returns
+    (X8p, scales)."""
     M, K = X.shape
     ldx = _mat(X, "X", torch.bfloat16, (M, K))
-    X8p = packed_empty_e4m3(M, K, X.device)
-    sc = torch.empty((M,), device=X.device, dtype=torch.float32)
+    if X8p is None:
+        X8p = packed_empty_e4m3(M, K, X.device)
+    _packed8(X8p, "X8p", M, K)
+    sc = torch.empty((M,), device=X.device, dtype=torch.float32) if scales is None else scales
+    _mat(sc, "scales", torch.float32, (M,))
     st = _lib.load().coda_quantize_rows_e4m3_packed(M, K, X.data_ptr(), ldx, X8p.data_ptr(), sc.data_ptr(),
                                                     _stream(stream))
     _lib.check("coda_quantize_rows_e4m3_packed", st)

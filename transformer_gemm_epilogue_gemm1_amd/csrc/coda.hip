@@ -390,6 +390,20 @@ void q_rows(const void* X, int64_t ldx, int M, int K, void* X8, int64_t ldx8, fl
   const uint16_t* x = (const uint16_t*)X;
   uint8_t* x8 = (uint8_t*)X8;
   const int chunks = (K / 8 + 255) / 256;  // 16-byte chunks per thread
+  if (x8_nck > 0 && K <= 8 * 1024) {
+    // tile-packed codes: 4 rows per workgroup, up to UPL units per lane
+    const dim3 g4((unsigned)((M + 3) / 4));
+    const int upl = (K / 16 + 63) / 64;
+    if (upl <= 1)
+      hipLaunchKernelGGL(quantize_rows_packed_e4m3_kernel<1>, g4, block, 0, s, x, ldx, M, K, x8, sc, x8_nck);
+    else if (upl <= 2)
+      hipLaunchKernelGGL(quantize_rows_packed_e4m3_kernel<2>, g4, block, 0, s, x, ldx, M, K, x8, sc, x8_nck);
+    else if (upl <= 4)
+      hipLaunchKernelGGL(quantize_rows_packed_e4m3_kernel<4>, g4, block, 0, s, x, ldx, M, K, x8, sc, x8_nck);
+    else
+      hipLaunchKernelGGL(quantize_rows_packed_e4m3_kernel<8>, g4, block, 0, s, x, ldx, M, K, x8, sc, x8_nck);
+    return;
+  }
   if (chunks <= 1)
     hipLaunchKernelGGL(quantize_rows_e4m3_kernel<1>, grid, block, 0, s, x, ldx, K, x8, ldx8, sc, x8_nck);
   else if (chunks <= 2)
@@ -1095,6 +1109,38 @@ coda_status coda_gemm_res_prms_fp8_packed(int64_t M, int64_t K, int64_t D, const
                            (uint8_t*)Hg8p, 0, partials, D / 16, (uint8_t*)hg_exp};
   return launch_gemm_fp8<EpiResPrmsFp8>("coda_gemm_res_prms_fp8_packed", (int)M, (int)D, (int)K, A8, lda, W1t8,
                                         ldw1t, ep, (hipStream_t)stream);
+}
+
+coda_status coda_gemm_res_prms_fp8_all_packed(int64_t M, int64_t K, int64_t D, const void* A8p, const float* sa,
+                                              const void* W1t8p, const float* sw1, const void* R, int64_t ldr,
+                                              const void* g, void* H, int64_t ldh, void* Hg8p, void* hg_exp,
+                                              float* partials, void* stream) {
+  coda_status st = check_dims_fp8(M, {{"K", K}, {"D", D}});
+  if (st != CODA_OK) return st;
+  if (M == 0) return ok();
+  const int64_t T = num_partials(D);
+  const int64_t a_bytes = packed_bytes_e4m3(M, K), w_bytes = packed_bytes_e4m3(D, K);
+  const int64_t hg_bytes = packed_bytes_e4m3(M, D), eb = mx_exp_bytes(M, D);
+  const Mat mA{A8p, 1, a_bytes, a_bytes, 1, "A8p"}, mW{W1t8p, 1, w_bytes, w_bytes, 1, "W1t8p"};
+  const Mat mR{R, M, D, ldr, 2, "R"}, mg{g, 1, D, D, 2, "g"}, mH{H, M, D, ldh, 2, "H"};
+  const Mat mHg{Hg8p, 1, hg_bytes, hg_bytes, 1, "Hg8"}, mE{hg_exp, 1, eb, eb, 1, "hg_exp"};
+  const Mat mP{partials, T, M, M, 4, "partials"}, msa{sa, 1, M, M, 4, "sa"}, msw{sw1, 1, D, D, 4, "sw1"};
+  for (const Mat* m : {&mA, &mW, &mHg})
+    if ((st = check_mat(*m, 16)) != CODA_OK) return st;
+  for (const Mat* m : {&mR, &mg, &mH})
+    if ((st = check_mat(*m, 8)) != CODA_OK) return st;
+  if ((st = check_mat(mE, 4)) != CODA_OK) return st;
+  if ((st = check_vec(sa, M, 4, "sa")) != CODA_OK || (st = check_vec(sw1, D, 16, "sw1")) != CODA_OK) return st;
+  if (partials == nullptr) return fail(CODA_ERR_NULL, "partials is NULL");
+  if (((uintptr_t)partials & 3) != 0) return fail(CODA_ERR_ALIGN, "partials is not 4-byte aligned");
+  if (mP.span() > kMaxSpan) return fail(CODA_ERR_SHAPE, "partials span too large");
+  const Mat outs[4] = {mH, mHg, mP, mE};
+  const Mat ins[6] = {mA, mW, mR, mg, msa, msw};
+  if ((st = check_alias(outs, 4, ins, 6)) != CODA_OK) return st;
+  EpiResPrmsFp8::Params ep{sa, sw1, (const uint16_t*)R, ldr, (const uint16_t*)g, (uint16_t*)H, ldh,
+                           (uint8_t*)Hg8p, 0, partials, D / 16, (uint8_t*)hg_exp};
+  return launch_gemm_fp8<EpiResPrmsFp8, kLayPacked>("coda_gemm_res_prms_fp8_all_packed", (int)M, (int)D, (int)K,
+                                                    A8p, K / 16, W1t8p, K / 16, ep, (hipStream_t)stream);
 }
 
 coda_status coda_gemm_rowscale_fp8_packed(int64_t M, int64_t D, int64_t N2, const void* X8p, const void* x_exp,

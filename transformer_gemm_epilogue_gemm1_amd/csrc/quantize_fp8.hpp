@@ -107,6 +107,67 @@ __global__ __launch_bounds__(256) void quantize_rows_e4m3_kernel(const uint16_t*
   }
 }
 
+// The row quantisation with the codes tile-packed (kp_unit, nck = K / 16
+// units per row), laid out for that layout's stores; the same scales and
+// codes as quantize_rows_e4m3_kernel.  In the packed layout the 16-code units
+// of one row lie 256 bytes apart and the 16 rows of a unit column are
+// contiguous, so a workgroup takes 4 rows: lane l of wavefront w holds row
+// 4 blockIdx.x + (l & 3) and its units u = 16 (UPL w + j) + (l >> 2),
+// j < UPL (two 16-byte loads of bf16 each, 512 contiguous bytes per row and
+// instruction pair).  Each store instruction then writes 4 rows of 16 unit
+// columns, 64 contiguous bytes each.  The row maximum reduces over the 16
+// lanes of a row, then over the 4 wavefronts through LDS.  K <= 1024 UPL;
+// the launcher takes it up to K = 8192 (UPL = 8, 160 VGPRs), longer rows
+// take the one-row kernels.
+template <int UPL>
+__global__ __launch_bounds__(256) void quantize_rows_packed_e4m3_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+                                                                        int M, int K, uint8_t* __restrict__ X8,
+                                                                        float* __restrict__ scales, int64_t nck) {
+  __shared__ float red[4][4];
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t row = 4 * (int64_t)blockIdx.x + (l & 3);
+  const int q = l >> 2, nu = K / 16;
+  const bool rin = row < M;
+  const uint16_t* x = X + (rin ? row : 0) * ldx;
+  u32x4 raw[UPL][2];
+#pragma unroll
+  for (int j = 0; j < UPL; ++j) {
+    const int u = 16 * (UPL * w + j) + q;
+    const bool in = rin && u < nu;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) raw[j][h] = in ? Chunk8<uint16_t>::load_raw(x + 16 * u + 8 * h) : u32x4{0, 0, 0, 0};
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < UPL; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float v[8];
+      Chunk8<uint16_t>::unpack(raw[j][h], v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    }
+#pragma unroll
+  for (int d = 4; d < 64; d *= 2) m = fmaxf(m, __shfl_xor(m, d));
+  if (q == 0) red[w][l & 3] = m;
+  __syncthreads();
+  const int r = l & 3;
+  const float s = e4m3_scale(fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r])));
+  if (w == 0 && q == 0 && rin) scales[row] = s;
+  const E4m3Divider enc = E4m3Divider::of(s);
+#pragma unroll
+  for (int j = 0; j < UPL; ++j) {
+    const int u = 16 * (UPL * w + j) + q;
+    if (rin && u < nu) {
+      float v0[8], v1[8];
+      Chunk8<uint16_t>::unpack(raw[j][0], v0);
+      Chunk8<uint16_t>::unpack(raw[j][1], v1);
+      const u32x2 lo = encode8(v0, enc), hi = encode8(v1, enc);
+      *(u32x4*)(X8 + kp_unit(row, u, nck) * 16) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+  }
+}
+
 // Rows longer than 32768 elements: the same result in two passes over the
 // row, the second from cache.
 __global__ __launch_bounds__(256) void quantize_long_rows_e4m3_kernel(const uint16_t* __restrict__ X, int64_t ldx,
