@@ -740,17 +740,6 @@ def test_fp8_backward_poisoned_workspace(shape):
         assert torch.equal(a.view(torch.int16) if a.dtype == bf else a, b.view(torch.int16) if b.dtype == bf else b), name
 
 
-def _pack8(a):
-    """Host tile-packing of e4m3 codes [rows, cols] (cols % 16 == 0) into the
-    packed_empty_e4m3 layout: [row block of 16, 16-code run, row in block,
-    code], rows past the end zero."""
-    rows, cols = a.shape
-    nb = -(-rows // 16)
-    p = np.zeros((nb * 16, cols), dtype=np.uint8)
-    p[:rows] = a
-    return np.ascontiguousarray(p.reshape(nb, 16, cols // 16, 16).transpose(0, 2, 1, 3))
-
-
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_all_packed_chain(shape):
     # A8 and W1t8 tile-packed (coda_gemm_res_prms_fp8_all_packed), then the
@@ -758,8 +747,7 @@ def test_all_packed_chain(shape):
     # the chain on row-major operands (the same codes, the same arithmetic)
     wl = ci.custom_workload(*shape, dtype="fp8", wl_id=514)
     x, d, o = _run(wl, seed=6)
-    A8p, W1t8p = _u8(_pack8(x["A8"])), _u8(_pack8(x["W1t8"]))
-    W2t8p = _u8(_pack8(x["W2t8"]))
+    A8p, W1t8p, W2t8p = (_pack8(x[k]).cuda() for k in ("A8", "W1t8", "W2t8"))
     H, Hg8p, E, r, Y, P = coda.fused_forward_fp8_all_packed(A8p, d["sa"], W1t8p, d["sw1"], d["R"], d["g"], W2t8p,
                                                             d["sw2"], wl.eps)
     torch.cuda.synchronize()
