@@ -358,6 +358,16 @@ def test_full_size_7b_fp8_whole_tensor():
           f"codes differ {ndiff / n:.2e}", file=sys.__stderr__, flush=True)
     assert err <= 1e-2 and herr <= 2.0 ** -8
     assert nhdiff / n <= 0.03 and ndiff / n <= 0.005
+    # the benchmark's layout: every e4m3 operand tile-packed, the whole 7B
+    # outputs bit-identical to the row-major chain's checked above
+    A8p, W1t8p, W2t8p = (_pack8(x[k]).cuda() for k in ("A8", "W1t8", "W2t8"))
+    H, Hg8p, E, r, Y, P = coda.fused_forward_fp8_all_packed(A8p, d["sa"], W1t8p, d["sw1"], d["R"], d["g"], W2t8p,
+                                                            d["sw2"], wl.eps)
+    torch.cuda.synchronize()
+    for name, a, b in (("H", o["H"], H), ("Hg8", o["Hg8"], coda.unpack_e4m3(Hg8p, wl.M)), ("E", o["E"], E),
+                       ("r", o["r"], r), ("Y", o["Y"], Y), ("partials", o["P"], P)):
+        assert torch.equal(a.view(torch.uint8) if a.dtype != torch.float32 else a,
+                           b.view(torch.uint8) if b.dtype != torch.float32 else b), name
 
 
 def _bf16_dev(x32):
